@@ -1,0 +1,123 @@
+"""Philox4x64-10 counter-based generator, written from its published definition.
+
+TEST INFRASTRUCTURE ONLY: part of the CPU oracle.  Only tests, the smoke check
+and the benchmark's CPU-baseline leg may import this package.
+
+Source of the generator: J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
+"Parallel Random Numbers: As Easy as 1, 2, 3", SC'11 -- the Philox family,
+instance N=4 words of W=64 bits, R=10 rounds.  One round maps the counter
+(x0, x1, x2, x3) under the round key (k0, k1) to
+
+    (hi(M1*x2) ^ x1 ^ k0,  lo(M1*x2),  hi(M0*x0) ^ x3 ^ k1,  lo(M0*x0))
+
+where hi/lo are the upper/lower 64 bits of the 128-bit product; between
+rounds the key advances by the Weyl constants (golden ratio and sqrt(3)-1 in
+64-bit fixed point).  The result is pinned bit-for-bit against numpy's
+independent ``numpy.random.Philox`` (also 4x64-10) in the tests.
+
+The pages fix only that the projection is regenerated "from its seed and
+metadata" (LoGRA paper text, paperpeel.com, §2.2 "Memory and
+synchronization").  Which generator and which bits is this library's choice;
+the layout is stated here and in ``include/logra.h``:
+
+* key of a projection: ``(seed, (step << 32) | matrix_id)``;
+* sign bits of A: one block per (row j, 256-column group b = l >> 8) with
+  counter ``(j, b, 0, 0)``; column l uses bit ``l & 63`` of output word
+  ``(l & 255) >> 6``; bit 1 means sigma = -1, bit 0 means sigma = +1;
+* stochastic-rounding draws: key ``(sr_seed, (step << 32) | matrix_id)``;
+  element e = (row0 + i) * k + l (logical index) uses counter
+  ``(e >> 4, 0, 1, 0)`` and the 16 bits ``[16*(e & 3), +16)`` of output word
+  ``(e & 15) >> 2``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK32 = np.uint64(0xFFFFFFFF)
+SHIFT32 = np.uint64(32)
+
+# Multipliers and Weyl increments of Philox4x64 (Salmon et al., SC'11).
+PHILOX_M0 = np.uint64(0xD2E7470EE14C6C93)
+PHILOX_M1 = np.uint64(0xCA5A826395121157)
+PHILOX_W0 = np.uint64(0x9E3779B97F4A7C15)
+PHILOX_W1 = np.uint64(0xBB67AE8584CAA73B)
+ROUNDS = 10
+
+
+def _mulhilo64(a: np.ndarray, m: np.uint64):
+    """128-bit product of uint64 array ``a`` and constant ``m`` as (hi, lo)."""
+    a = np.asarray(a, dtype=np.uint64)
+    m = np.uint64(m)
+    a_lo, a_hi = a & MASK32, a >> SHIFT32
+    m_lo, m_hi = m & MASK32, m >> SHIFT32
+    with np.errstate(over="ignore"):
+        p00 = a_lo * m_lo
+        p01 = a_lo * m_hi
+        p10 = a_hi * m_lo
+        p11 = a_hi * m_hi
+        mid = (p00 >> SHIFT32) + (p01 & MASK32) + (p10 & MASK32)
+        lo = (p00 & MASK32) | ((mid & MASK32) << SHIFT32)
+        hi = p11 + (p01 >> SHIFT32) + (p10 >> SHIFT32) + (mid >> SHIFT32)
+    return hi, lo
+
+
+def philox4x64_10(ctr, key):
+    """Apply Philox4x64-10 to counters ``ctr`` (shape [..., 4]) under ``key``.
+
+    ``key`` is a pair (k0, k1) of uint64 scalars or arrays broadcastable to the
+    counter batch.  Returns an array of the same shape as ``ctr`` (uint64).
+    """
+    x = np.array(ctr, dtype=np.uint64, copy=True)
+    if x.shape[-1] != 4:
+        raise ValueError("counter must have 4 words")
+    k0 = np.asarray(key[0], dtype=np.uint64)
+    k1 = np.asarray(key[1], dtype=np.uint64)
+    x0, x1, x2, x3 = x[..., 0], x[..., 1], x[..., 2], x[..., 3]
+    with np.errstate(over="ignore"):
+        for rnd in range(ROUNDS):
+            if rnd:
+                k0 = k0 + PHILOX_W0
+                k1 = k1 + PHILOX_W1
+            hi0, lo0 = _mulhilo64(x0, PHILOX_M0)
+            hi1, lo1 = _mulhilo64(x2, PHILOX_M1)
+            x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
+    return np.stack([x0, x1, x2, x3], axis=-1)
+
+
+def projection_key(seed: int, matrix_id: int, step: int):
+    """Key words of one projection matrix A: (seed, step<<32 | matrix_id)."""
+    if not (0 <= matrix_id < 2**32 and 0 <= step < 2**32 and 0 <= seed < 2**64):
+        raise ValueError("seed must fit 64 bits, matrix_id and step 32 bits")
+    return np.uint64(seed), np.uint64((int(step) << 32) | int(matrix_id))
+
+
+def sign_bits(seed: int, matrix_id: int, step: int, r: int, k: int) -> np.ndarray:
+    """Sign bits of A as a uint8 array [r, k]: 1 means sigma = -1."""
+    key = projection_key(seed, matrix_id, step)
+    nblk = (k + 255) // 256
+    j = np.arange(r, dtype=np.uint64)[:, None]
+    b = np.arange(nblk, dtype=np.uint64)[None, :]
+    ctr = np.zeros((r, nblk, 4), dtype=np.uint64)
+    ctr[..., 0] = j
+    ctr[..., 1] = b
+    words = philox4x64_10(ctr, key)                     # [r, nblk, 4]
+    l = np.arange(k)
+    w = words[:, l >> 8, (l & 255) >> 6]                # [r, k]
+    return ((w >> (l & 63).astype(np.uint64)) & np.uint64(1)).astype(np.uint8)
+
+
+def sr_draws(sr_seed: int, matrix_id: int, step: int, d: int, k: int,
+             row0: int = 0) -> np.ndarray:
+    """16-bit stochastic-rounding draws u as uint32 array [d, k]."""
+    key = projection_key(sr_seed, matrix_id, step)
+    e = ((np.arange(d, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(k)
+         + np.arange(k, dtype=np.uint64)[None, :])
+    blocks, inv = np.unique(e >> np.uint64(4), return_inverse=True)
+    ctr = np.zeros((blocks.size, 4), dtype=np.uint64)
+    ctr[:, 0] = blocks
+    ctr[:, 2] = 1
+    words = philox4x64_10(ctr, key)                     # [nblocks, 4]
+    inv = inv.reshape(e.shape)
+    lane = (e & np.uint64(15)).astype(np.int64)
+    w = words[inv, lane >> 2]
+    return ((w >> (np.uint64(16) * (e & np.uint64(3)))) & np.uint64(0xFFFF)).astype(np.uint32)
