@@ -1,0 +1,231 @@
+"""Benchmark of the LoGRA sketch hot path on one MI355X.
+
+One step = one update over the whole layer set of the workload:
+  A. project every selected matrix's input, every microbatch (XAt = X A^T)
+  B. accumulate every sketch, every microbatch (grouped: the seven matrices
+     of one layer and one microbatch per launch)
+  C. RowAdam for every sketch, predicted-KL q over the context set, alpha on
+     the device
+  D. merge every matrix, W <- round(W - eta*alpha U A)
+Inputs are synthetic and resident in HBM before timing starts (distinct
+buffers for every layer and microbatch, so the 256 MB Infinity Cache cannot
+serve them).  The metric is HBM GB/s of phases B + D: their algorithmic bytes
+(accumulate 2Td + 4Tr + 8dr per call, merge 4dk + 4dr per matrix) divided by
+their HIP-event time on the stream the kernels run on.
+
+Prints one JSON line.  --gpus above 1 is refused (one-GPU build).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen2.5-7b-set-r64")
+    ap.add_argument("--rounding", default=None, choices=[None, "nearest", "stochastic"])
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None, help="use fewer layers (profiling runs only)")
+    return ap.parse_args()
+
+
+def acc_bytes(T, d, r):
+    return 2 * T * d + 4 * T * r + 8 * d * r
+
+
+def merge_bytes(d, k, r):
+    return 4 * d * k + 4 * d * r
+
+
+def project_bytes(T, k, r):
+    return 2 * T * k + 4 * T * r
+
+
+def cpu_baseline(w, rounding):
+    """The oracle, untuned, on a bounded sample: layer 0's seven accumulates for one
+    microbatch and its seven merges.  Returns the sample's algorithmic GB/s."""
+    import numpy as np
+    import oracle
+    from oracle import philox
+    from rank_gradient_sketching_logra_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    mats = w.matrices(layers=[0])
+    inputs = []
+    for (layer, kind, mid, d, k) in mats:
+        inputs.append((mid, d, k, synth.output_grad(w, layer, kind, 0),
+                       synth.fp32_matrix((w.T, w.r), 7.5, (w.index, mid, 0, 0, 0)),
+                       synth.weight(w, layer, kind),
+                       synth.fp32_matrix((d, w.r), 1.0, (w.index, mid, 0, 0, 7))))
+    nbytes = 0
+    t0 = time.perf_counter()
+    for (mid, d, k, db, XAt, wb, U) in inputs:
+        S = oracle.accumulate(np.zeros((d, w.r)), oracle.bf16_bits_to_f64(db), XAt.astype(np.float64))
+        A = oracle.regen_A(w.seed, mid, w.step, w.r, k)
+        u = philox.sr_draws(w.sr_seed, mid, w.step, d, k) if rounding == "stochastic" else None
+        oracle.merge(oracle.bf16_bits_to_f64(wb), U.astype(np.float64), A, w.eta, w_dtype="bf16",
+                     mode=rounding, u_draws=u)
+        nbytes += acc_bytes(w.T, d, w.r) + merge_bytes(d, k, w.r)
+        del S
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 of {w.name}: 7 accumulates (1 microbatch, T={w.T}) + 7 merges ({rounding}),"
+                      f" numpy fp64, {nbytes / 1e9:.2f} GB algorithmic in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design in DESIGN.md, not a run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_gradient_sketching_logra_amd import binding as B
+    from rank_gradient_sketching_logra_amd import synth
+
+    w = synth.BY_NAME[args.workload]
+    rounding = args.rounding or w.rounding
+    layers = args.layers or w.layers
+    T, r, M = w.T, w.r, w.microbatches
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+
+    def randn(shape, std, dtype=torch.bfloat16):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        t.normal_(0.0, std, generator=g)
+        return t
+
+    mats = w.matrices(layers=range(layers))
+    # Inputs X: q/k/v share the attention input, gate/up the MLP input.
+    shared = {"q": "att", "k": "att", "v": "att", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+    xw = {"att": w.shapes["q"][1], "o": w.shapes["o"][1], "mlp": w.shapes["gate"][1], "down": w.shapes["down"][1]}
+    X = {(l, mb, s): randn((T, xw[s]), 1.0) for l in range(layers) for mb in range(M) for s in xw}
+    D = {(l, mb, kind): randn((T, d), 1e-3) for (l, kind, mid, d, k) in mats for mb in range(M)}
+    XAt = {(l, mb, kind): torch.empty((T, r), dtype=torch.float32, device=dev)
+           for (l, kind, mid, d, k) in mats for mb in range(M)}
+    W = {(l, kind): randn((d, k), 0.02) for (l, kind, mid, d, k) in mats}
+    S = {(l, kind): torch.zeros((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
+    U = {(l, kind): torch.empty((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
+    V = {(l, kind): torch.zeros((d,), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
+    keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
+    maxd = max(d for (_, _, _, d, _) in mats)
+    acc_ws = B.workspace(7 * B.accumulate_ws_bytes(T, r), dev)
+    ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
+    P, Vv = (w.P or 64), (w.V or 152064)
+    z = randn((P, Vv), 4.0)
+    zd = randn((P, Vv), 1.0)
+    kl_ws = B.workspace(B.predicted_kl_q_ws_bytes(P, Vv), dev)
+    q = torch.empty((1,), dtype=torch.float32, device=dev)
+    alpha = torch.empty((1,), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    by_layer = {}
+    for (l, kind, mid, d, k) in mats:
+        by_layer.setdefault(l, []).append((kind, d, k))
+    acc_total = sum(acc_bytes(T, d, r) for (_, _, _, d, _) in mats) * M
+    merge_total = sum(merge_bytes(d, k, r) for (_, _, _, d, k) in mats)
+    proj_total = sum(project_bytes(T, k, r) for (_, _, _, d, k) in mats) * M
+    n_acc_launch = layers * M
+    t_step = 0
+
+    def step(ev):
+        nonlocal t_step
+        t_step += 1
+        for s in S.values():
+            s.zero_()
+        ev[0].record()
+        for mb in range(M):                          # A: forward-side projections
+            for l in range(layers):
+                for (kind, d, k) in by_layer[l]:
+                    B.project_input(keys[(l, kind)], X[(l, mb, shared[kind])], r, out=XAt[(l, mb, kind)])
+        ev[1].record()
+        for mb in range(M):                          # B: backward-side sketch accumulation
+            for l in reversed(range(layers)):
+                B.sketch_accumulate_grouped([(D[(l, mb, kind)], XAt[(l, mb, kind)], S[(l, kind)])
+                                             for (kind, d, k) in by_layer[l]], ws=acc_ws)
+        ev[2].record()
+        for key_ in S:                               # C: optimiser and step control
+            B.rowadam(S[key_], V[key_], t_step, w.beta, w.eps, U=U[key_], ws=ra_ws)
+        B.predicted_kl_q(z, zd, w.tau, out=q, ws=kl_ws)
+        B.step_alpha_dev(q, w.delta, w.alpha_max, out=alpha)
+        ev[3].record()
+        for key_ in S:                               # D: merge
+            B.merge(keys[key_], W[key_], U[key_], w.eta, scale_dev=alpha, mode=rounding,
+                    sr_seed=w.sr_seed)
+        ev[4].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(4)]   # ms per phase per step
+    tot = [sum(p) for p in ph]
+    K = args.steps
+    acc_ms, merge_ms = tot[1] / K, tot[3] / K
+    value = (acc_total + merge_total) / ((acc_ms + merge_ms) * 1e-3) / 1e9
+    acc_gbs = acc_total / (acc_ms * 1e-3) / 1e9
+    merge_gbs = merge_total / (merge_ms * 1e-3) / 1e9
+    proj_gbs = proj_total / (tot[0] / K * 1e-3) / 1e9
+    out = {
+        "metric": "sketch-accumulate + merge HBM GB/s (% of peak), Qwen-7B layer set, r=64",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs of the workload's shapes, resident in HBM)",
+        "config": {"workload": w.name, "layers": layers, "matrices": len(mats), "r": r, "T": T,
+                   "microbatches": M, "rounding": rounding, "optimizer": w.optimizer,
+                   "contexts": P, "vocab": Vv, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2)},
+        "roofline": {"bound": "hbm", "kernel": "sketch_accumulate (grouped: pack + acc_bf16 kernels)",
+                     "achieved": round(acc_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(acc_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": acc_total // n_acc_launch,
+                     "avg_launch_us": round(acc_ms * 1e3 / n_acc_launch, 3)},
+        "phases_ms": {"project": round(tot[0] / K, 3), "accumulate": round(acc_ms, 3),
+                      "rowadam_q_alpha": round(tot[2] / K, 3), "merge": round(merge_ms, 3)},
+        "kernels_gbs": {"accumulate": round(acc_gbs, 1), "merge": round(merge_gbs, 1),
+                        "project": round(proj_gbs, 1)},
+        "algorithmic_gb": {"accumulate": round(acc_total / 1e9, 3), "merge": round(merge_total / 1e9, 3),
+                           "project": round(proj_total / 1e9, 3)},
+    }
+    if not args.skip_cpu_baseline and layers == w.layers:
+        out["cpu_baseline"] = cpu_baseline(w, rounding)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+/*
+ * logra.h -- C ABI of the LoGRA low-rank gradient-sketch library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [paper]   "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
+ *             Sketches", paper text on paperpeel.com.
+ *   [zh]      Chinese review of the paper (shibing624.github.io ai-paper-analysis).
+ *   [ko]      Korean summary of the paper (onedev.kr).
+ *   [rgc]     "Randomized Gradient Compression" blog (iluvatarlabs), "How it works"
+ *             (a different method; used for the orientation of the contraction
+ *             and the meaning of stochastic rounding only).
+ *   [summary] paperlayer.ai section summary of the paper ("B. RowAdam", "D.1").
+ *
+ * For one selected linear weight W in R^{d x k} (out x in, row-major), with
+ * layer input X [T x k] and backward derivative D [T x d] of a microbatch of
+ * T tokens, the library computes
+ *
+ *   A      = sigma / sqrt(r), sigma in {+1,-1}^{r x k} from a counter-based
+ *            generator keyed by (seed, matrix_id, step)       [paper] §2.1-2.2
+ *   XAt    = X A^T                        [T x r]  fp32       [paper] §2.1
+ *   S     += D^T XAt                      [d x r]  fp32       [paper] §2.1 (Eq. 2)
+ *   U      = RowAdam(S) or S (SGD)        [d x r]  fp32       [summary] B
+ *   q      = 1/(2|P| tau^2) sum_s Var_{p_s}[zdot_s]           [paper] §2.3 (Eq. 6)
+ *   alpha  = min(alpha_max, sqrt(delta/q))                    [paper] §2.3, App. A.2
+ *   W     <- round(W - scale * U A)       in place, bf16/fp32 [paper] §2.1-2.2
+ *
+ * Conventions (every entry point):
+ *   - Matrices are row-major.  Device pointers are caller-owned device memory;
+ *     the library never allocates or frees device memory except where an entry
+ *     point says so.  Workspace arguments are caller-allocated device memory
+ *     of at least the size the matching *_ws_bytes() query returns.
+ *   - Every device call is asynchronous on the caller's stream (NULL = the
+ *     default stream); outputs are valid once that stream has synchronised.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation failure nothing is launched and a status other than
+ *     LOGRA_OK is returned.  logra_last_error() gives a message for the
+ *     calling thread's most recent failure.  No C++ exception crosses the ABI.
+ *   - Alignment: X, D and W base pointers must be 16-byte aligned and their
+ *     leading dimensions (in elements) must make every row start 16-byte
+ *     aligned; XAt, S, U, v, z and zdot must be 16-byte aligned.
+ *   - Results are deterministic: the same input bits and shapes give the same
+ *     output bits, run after run; no floating-point atomics are used.
+ *
+ * Generator (this library's choice -- the pages fix only that A is
+ * regenerated from a seed and metadata, [paper] §2.2 "Memory and
+ * synchronization"): Philox4x64-10 (Salmon et al., SC'11).
+ *   key of a projection      = (seed, (step << 32) | matrix_id)
+ *   sign of A[j, l]          = bit (l & 63) of word ((l & 255) >> 6) of
+ *                              Philox(counter = (j, l >> 8, 0, 0)); 1 -> -1
+ *   stochastic-rounding draw = for element e = (row0 + i) * k + l of W, the
+ *                              16 bits [16*(e & 3), +16) of word ((e & 15) >> 2)
+ *                              of Philox(counter = (e >> 4, 0, 1, 0)) under key
+ *                              (sr_seed, (step << 32) | matrix_id)
+ */
+#ifndef LOGRA_H_
+#define LOGRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOGRA_API __attribute__((visibility("default")))
+
+/* Opaque stream handle: a hipStream_t (NULL = default stream). */
+typedef void* logra_stream;
+
+typedef enum logra_status {
+  LOGRA_OK = 0,
+  LOGRA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  LOGRA_ERR_SHAPE = 2,     /* a size is out of range or inconsistent             */
+  LOGRA_ERR_DTYPE = 3,     /* unsupported element type or type combination       */
+  LOGRA_ERR_ALIGN = 4,     /* pointer or leading dimension breaks 16-B alignment */
+  LOGRA_ERR_ALIAS = 5,     /* output overlaps an input it must not overlap      */
+  LOGRA_ERR_DOMAIN = 6,    /* scalar out of its domain (q<0, NaN, delta<=0, ...) */
+  LOGRA_ERR_HIP = 7,       /* the HIP runtime reported an error                  */
+  LOGRA_ERR_WORKSPACE = 8  /* workspace missing or too small                     */
+} logra_status;
+
+typedef enum logra_dtype {
+  LOGRA_F32 = 0,   /* IEEE binary32                           */
+  LOGRA_BF16 = 1,  /* bfloat16 (top half of a binary32)       */
+  LOGRA_I8 = 2     /* int8, used only for the signs of A      */
+} logra_dtype;
+
+typedef enum logra_round {
+  LOGRA_ROUND_NEAREST = 0,    /* round to nearest, ties to even               */
+  LOGRA_ROUND_STOCHASTIC = 1  /* deterministic stochastic rounding (bf16 W)   */
+} logra_round;
+
+/* Identifies one projection A: [paper] §2.2 -- each matrix has its own A,
+ * refreshed every update; a fixed basis keeps `step` constant. */
+typedef struct logra_key {
+  uint64_t seed;
+  uint32_t matrix_id;
+  uint32_t step;
+} logra_key;
+
+/* Largest supported rank r (register-resident accumulators). */
+#define LOGRA_MAX_RANK 256
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Library version string (static storage). */
+LOGRA_API const char* logra_version(void);
+
+/* Message for the calling thread's last failed call ("" if none). */
+LOGRA_API const char* logra_last_error(void);
+
+/* Bytes of one fp32 sketch, 4*d*r: [paper] §2.2 "Memory and synchronization"
+ * (d = k = 4096, r = 64 gives 1 MiB against 64 MiB dense).  Returns -1 for
+ * negative sizes. */
+LOGRA_API int64_t logra_sketch_bytes(int64_t d, int64_t r);
+
+/* ------------------------------------------------------------- projection */
+
+/* Materialise A [r x k] (row-major, contiguous) for `key`.
+ * out = LOGRA_I8: A[j,l] = sigma (+1/-1, int8).
+ * out = LOGRA_F32: A[j,l] = sigma * fl32(1/sqrt(r)).
+ * Bit-identical to the A used inside logra_project_input and logra_merge.
+ * Sources: [paper] §2.1 (A in R^{r x k}), §2.2 (regenerated from its seed);
+ * [zh], [ko] (entries +-1/sqrt(r)).
+ * Errors: NULL key/A; r < 1, r > LOGRA_MAX_RANK, k < 1; out not I8/F32. */
+LOGRA_API int logra_regen_A(const logra_key* key, int64_t r, int64_t k,
+                            logra_dtype out, void* A, logra_stream stream);
+
+/* XAt [T x r] = X [T x k] A^T, overwritten (fp32, contiguous, ld = r).
+ * X is bf16 or fp32 with leading dimension ldx >= k.  [paper] §2.1: the
+ * inputs of the weight-gradient product are projected before they meet the
+ * backward derivatives; [rgc] the layer keeps X A^T instead of X.
+ * Errors: NULL pointers; T < 1, k < 1, r < 1, r > LOGRA_MAX_RANK, ldx < k;
+ * alignment; XAt overlapping X. */
+LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, int64_t r,
+                                  const void* X, logra_dtype x_dtype, int64_t ldx,
+                                  float* XAt, logra_stream stream);
+
+/* ---------------------------------------------------------------- sketch */
+
+/* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a
+ * grouped call) needs for bf16 D: XAt repacked as two bf16 planes (hi, lo)
+ * of XAt^T, rank padded to 32 and tokens to 256.  0 for invalid sizes. */
+LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r);
+
+/* S [d x r] += D^T XAt for one microbatch (fp32 accumulate; G = D^T X is
+ * never formed).  D [T x d] is bf16 or fp32 with leading dimension ldd >= d;
+ * XAt [T x r] fp32 contiguous; S [d x r] fp32 contiguous, read and written.
+ * The caller zeroes S at the start of each update.  [paper] §2.1 (S = G A^T,
+ * accumulated per microbatch in fp32), [rgc] "How it works" (C += D^T (X P)).
+ * bf16 D runs on bf16 MFMA with XAt split into two bf16 terms (hi + lo), which
+ * needs the workspace above (ignored for fp32 D, may be NULL then).  Each
+ * element of S sums tokens in ascending 16-token steps, so results do not
+ * depend on the launch shape or on grouping.
+ * Errors: NULL pointers; T < 1, d < 1, r < 1, r > LOGRA_MAX_RANK, ldd < d;
+ * alignment; S or the workspace overlapping an operand; workspace too small. */
+LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r,
+                                      const void* D, logra_dtype d_dtype, int64_t ldd,
+                                      const float* XAt, float* S, void* ws, size_t ws_bytes,
+                                      logra_stream stream);
+
+/* One matrix of a grouped accumulate. */
+typedef struct logra_acc_desc {
+  const void* D;       /* [T x d], row-major, leading dimension ldd */
+  const float* XAt;    /* [T x r] fp32 contiguous                    */
+  float* S;            /* [d x r] fp32 contiguous                    */
+  int64_t d;
+  int64_t ldd;
+} logra_acc_desc;
+
+#define LOGRA_MAX_GROUP 16
+
+/* Grouped form: n <= LOGRA_MAX_GROUP accumulates that share T, r and the
+ * dtype of D, in one launch (e.g. the seven projections of one layer for one
+ * microbatch).  Same result bits as n separate logra_sketch_accumulate calls.
+ * The descriptor array is read on the host during the call.  For bf16 D the
+ * workspace holds n consecutive per-descriptor workspaces of
+ * logra_sketch_accumulate_ws_bytes(T, r) bytes each.
+ * Errors: as logra_sketch_accumulate for each descriptor; n < 1 or
+ * n > LOGRA_MAX_GROUP; two descriptors writing overlapping S. */
+LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype d_dtype,
+                                              const logra_acc_desc* descs, int n,
+                                              void* ws, size_t ws_bytes,
+                                              logra_stream stream);
+
+/* ------------------------------------------------------------- optimiser */
+
+/* Workspace bytes logra_rowadam needs for d rows. */
+LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d);
+
+/* RowAdam ([summary] B; [paper] App. D.1 Table 4: beta2, no first moment,
+ * relative eps).  With t the 1-based index of this update:
+ *   m_i = sum_j S_ij^2;  v_i <- beta v_i + (1-beta) m_i;  vh_i = v_i/(1-beta^t)
+ *   rho = sqrt(mean_i vh_i);  Ut_ij = S_ij / (sqrt(vh_i) + eps*rho)
+ *   U = Ut * ||S||_F / ||Ut||_F   (U = 0 when Ut = 0)
+ * S [d x r], U [d x r] fp32 contiguous (U may equal S: in place); v [d]
+ * fp32, read and written.  Reductions run in fp64 in a fixed order.
+ * Errors: NULL pointers; d < 1, r < 1; t < 1; beta not in [0,1); eps < 0 or
+ * non-finite; workspace too small; U partially overlapping S. */
+LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                            float beta, float eps, float* U, void* ws, size_t ws_bytes,
+                            logra_stream stream);
+
+/* -------------------------------------------------------- step control */
+
+/* Workspace bytes logra_predicted_kl_q needs for P contexts of V logits. */
+LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V);
+
+/* q = 1/(2 P tau^2) * sum_s Var_{v ~ softmax(z_s/tau)}[zdot_s,v], written to
+ * q_dev (one float on the device).  z, zdot [P x V] row-major contiguous,
+ * bf16 or fp32 (same dtype).  [paper] §2.3 (Eq. 6), App. A.1.
+ * Errors: NULL pointers; P < 1, V < 1; tau not finite and > 0; workspace too
+ * small. */
+LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zdot,
+                                   logra_dtype dtype, float tau, float* q_dev,
+                                   void* ws, size_t ws_bytes, logra_stream stream);
+
+/* alpha = min(alpha_max, sqrt(delta / q)) on the host (fp64); q = 0 gives
+ * alpha_max.  [paper] §2.3 and App. A.2 (root restored from alpha^2 q <= delta;
+ * [zh], [ko]).  Errors: NULL alpha; q < 0 or NaN, delta <= 0, alpha_max <= 0
+ * (LOGRA_ERR_DOMAIN). */
+LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double* alpha);
+
+/* Device form: *alpha_dev = min(alpha_max, sqrt(delta / *q_dev)) in fp32;
+ * q = 0 gives alpha_max; q < 0 or NaN gives NaN (checked on the host by the
+ * caller if needed).  Errors: NULL pointers; delta <= 0 or alpha_max <= 0. */
+LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_max,
+                                   float* alpha_dev, logra_stream stream);
+
+/* -------------------------------------------------------------- merge */
+
+/* W [d x k] <- round(W - s * U A) in place, A regenerated from `key`.
+ * s = scale * (*scale_dev if scale_dev != NULL else 1): on the trainer
+ * scale = alpha*eta (or eta with alpha on the device); on the rollout side U
+ * is the received alpha*eta*U and scale = 1 ([paper] §2.2 "Memory and
+ * synchronization").  W is bf16 (mode NEAREST or STOCHASTIC) or fp32 (NEAREST
+ * only), leading dimension ldw >= k.  U [d x r] fp32 contiguous.  The update
+ * is formed in fp32 and rounded once to W's type.  row0 is the global index
+ * of W's first row (for row-sharded merges: stochastic-rounding draws are
+ * indexed by (row0 + i) * k + l, so a merge of a row block equals the same
+ * rows of a whole-matrix merge).  Two merges of equal W with equal
+ * (U, key, s, mode, sr_seed, row0) give identical bits -- the rollout-sync
+ * invariant.  [paper] §2.1-2.2, [rgc] "How it works" (stochastic rounding).
+ * Errors: NULL pointers; d < 1, k < 1, r < 1, r > LOGRA_MAX_RANK, ldw < k,
+ * row0 < 0; fp32 W with STOCHASTIC; non-finite scale; W overlapping U. */
+LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r,
+                          void* W, logra_dtype w_dtype, int64_t ldw, const float* U,
+                          double scale, const float* scale_dev, logra_round mode,
+                          uint64_t sr_seed, int64_t row0, logra_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGRA_H_ */

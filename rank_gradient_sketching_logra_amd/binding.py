@@ -1,0 +1,226 @@
+"""ctypes binding of liblogra.so: the C ABI declared in include/logra.h.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+liblogra.so; torch is used for device memory (output and workspace tensors)
+and for the current stream.  There is no fallback: if the library is not
+built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_double, c_float, c_int, c_int64, c_size_t, \
+    c_uint32, c_uint64, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogra.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_ALIAS, ERR_DOMAIN, ERR_HIP, ERR_WORKSPACE = range(9)
+F32, BF16, I8 = 0, 1, 2
+ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
+MAX_RANK = 256
+MAX_GROUP = 16
+
+# Every symbol the header exports, with (restype, argtypes).
+class Key(Structure):
+    _fields_ = [("seed", c_uint64), ("matrix_id", c_uint32), ("step", c_uint32)]
+
+
+class AccDesc(Structure):
+    _fields_ = [("D", c_void_p), ("XAt", c_void_p), ("S", c_void_p), ("d", c_int64), ("ldd", c_int64)]
+
+
+SIGNATURES = {
+    "logra_version": (c_char_p, []),
+    "logra_last_error": (c_char_p, []),
+    "logra_sketch_bytes": (c_int64, [c_int64, c_int64]),
+    "logra_regen_A": (c_int, [POINTER(Key), c_int64, c_int64, c_int, c_void_p, c_void_p]),
+    "logra_project_input": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
+                                    c_int64, c_void_p, c_void_p]),
+    "logra_sketch_accumulate_ws_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_sketch_accumulate": (c_int, [c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_sketch_accumulate_grouped": (c_int, [c_int64, c_int64, c_int, POINTER(AccDesc), c_int,
+                                                c_void_p, c_size_t, c_void_p]),
+    "logra_rowadam_ws_bytes": (c_size_t, [c_int64]),
+    "logra_rowadam": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_float, c_float,
+                              c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_predicted_kl_q_ws_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_predicted_kl_q": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int, c_float,
+                                     c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_step_alpha": (c_int, [c_double, c_double, c_double, POINTER(c_double)]),
+    "logra_step_alpha_dev": (c_int, [c_void_p, c_float, c_float, c_void_p, c_void_p]),
+    "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
+                            c_void_p, c_double, c_void_p, c_int, c_uint64, c_int64, c_void_p]),
+}
+
+_lib_handle = None
+
+
+class LograError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"logra status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load liblogra.so once; raise if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m rank_gradient_sketching_logra_amd.build` (hipcc, gfx950)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status: int):
+    if status != OK:
+        raise LograError(status, lib().logra_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t: torch.Tensor, stream=None):
+    if stream is not None:
+        return c_void_p(stream.cuda_stream)
+    return c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def key(seed: int, matrix_id: int, step: int) -> Key:
+    return Key(seed, matrix_id, step)
+
+
+def version() -> str:
+    return lib().logra_version().decode()
+
+
+def sketch_bytes(d: int, r: int) -> int:
+    return lib().logra_sketch_bytes(d, r)
+
+
+def regen_A(k_: Key, r: int, k: int, out_dtype=torch.int8, device="cuda", stream=None):
+    """Materialise A [r x k]: int8 signs or fp32 sigma * fl32(1/sqrt(r))."""
+    A = torch.empty((r, k), dtype=out_dtype, device=device)
+    code = I8 if out_dtype == torch.int8 else F32 if out_dtype == torch.float32 else -1
+    _check(lib().logra_regen_A(ctypes.byref(k_), r, k, code, _ptr(A), _stream(A, stream)))
+    return A
+
+
+def project_input(k_: Key, X: torch.Tensor, r: int, out=None, stream=None):
+    """XAt = X A^T, [T x r] fp32."""
+    T, k = X.shape
+    XAt = out if out is not None else torch.empty((T, r), dtype=torch.float32, device=X.device)
+    _check(lib().logra_project_input(ctypes.byref(k_), T, k, r, _ptr(X), _dtype_code(X), _ld(X),
+                                     _ptr(XAt), _stream(X, stream)))
+    return XAt
+
+
+def accumulate_ws_bytes(T: int, r: int) -> int:
+    return lib().logra_sketch_accumulate_ws_bytes(T, r)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=device)
+
+
+def sketch_accumulate(D: torch.Tensor, XAt: torch.Tensor, S: torch.Tensor, ws=None, stream=None):
+    """S += D^T XAt (in place)."""
+    T, d = D.shape
+    r = S.shape[1]
+    if ws is None:
+        ws = workspace(accumulate_ws_bytes(T, r), D.device)
+    _check(lib().logra_sketch_accumulate(T, d, r, _ptr(D), _dtype_code(D), _ld(D), _ptr(XAt),
+                                         _ptr(S), _ptr(ws), ws.numel(), _stream(D, stream)))
+    return S
+
+
+def sketch_accumulate_grouped(items, ws=None, stream=None):
+    """items: sequence of (D, XAt, S) sharing T, r and D's dtype; one launch."""
+    n = len(items)
+    T = items[0][0].shape[0]
+    r = items[0][2].shape[1]
+    descs = (AccDesc * n)()
+    for i, (D, XAt, S) in enumerate(items):
+        descs[i] = AccDesc(D.data_ptr(), XAt.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
+    if ws is None:
+        ws = workspace(n * accumulate_ws_bytes(T, r), items[0][0].device)
+    _check(lib().logra_sketch_accumulate_grouped(T, r, _dtype_code(items[0][0]), descs, n, _ptr(ws),
+                                                 ws.numel(), _stream(items[0][0], stream)))
+
+
+def rowadam_ws_bytes(d: int) -> int:
+    return lib().logra_rowadam_ws_bytes(d)
+
+
+def rowadam(S: torch.Tensor, v: torch.Tensor, t: int, beta: float, eps: float, U=None, ws=None,
+            stream=None):
+    """U = RowAdam(S) with v updated in place; U may be S."""
+    d, r = S.shape
+    U = U if U is not None else torch.empty_like(S)
+    if ws is None:
+        ws = workspace(rowadam_ws_bytes(d), S.device)
+    _check(lib().logra_rowadam(d, r, _ptr(S), _ptr(v), t, beta, eps, _ptr(U), _ptr(ws), ws.numel(),
+                               _stream(S, stream)))
+    return U
+
+
+def predicted_kl_q_ws_bytes(P: int, V: int) -> int:
+    return lib().logra_predicted_kl_q_ws_bytes(P, V)
+
+
+def predicted_kl_q(z: torch.Tensor, zdot: torch.Tensor, tau: float, out=None, ws=None, stream=None):
+    """q on the device (one-element fp32 tensor)."""
+    P, V = z.shape
+    q = out if out is not None else torch.empty((1,), dtype=torch.float32, device=z.device)
+    if ws is None:
+        ws = workspace(predicted_kl_q_ws_bytes(P, V), z.device)
+    _check(lib().logra_predicted_kl_q(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), tau, _ptr(q),
+                                      _ptr(ws), ws.numel(), _stream(z, stream)))
+    return q
+
+
+def step_alpha(q: float, delta: float, alpha_max: float) -> float:
+    out = c_double(0.0)
+    _check(lib().logra_step_alpha(q, delta, alpha_max, ctypes.byref(out)))
+    return out.value
+
+
+def step_alpha_dev(q_dev: torch.Tensor, delta: float, alpha_max: float, out=None, stream=None):
+    a = out if out is not None else torch.empty((1,), dtype=torch.float32, device=q_dev.device)
+    _check(lib().logra_step_alpha_dev(_ptr(q_dev), delta, alpha_max, _ptr(a), _stream(q_dev, stream)))
+    return a
+
+
+def merge(k_: Key, W: torch.Tensor, U: torch.Tensor, scale: float, scale_dev=None,
+          mode: str = "nearest", sr_seed: int = 0, row0: int = 0, stream=None):
+    """W <- round(W - s U A) in place."""
+    d, kk = W.shape
+    r = U.shape[1]
+    m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
+    _check(lib().logra_merge(ctypes.byref(k_), d, kk, r, _ptr(W), _dtype_code(W), _ld(W), _ptr(U),
+                             float(scale), _ptr(scale_dev), m, sr_seed, row0, _stream(W, stream)))
+    return W

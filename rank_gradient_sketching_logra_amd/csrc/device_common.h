@@ -1,0 +1,119 @@
+// Device-side building blocks shared by the LoGRA kernels (gfx950 / CDNA4).
+//
+// - Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+//   Easy as 1, 2, 3", SC'11): the counter-based generator that regenerates
+//   the Rademacher projection and the stochastic-rounding draws.
+// - bf16 rounding: nearest-even and deterministic stochastic rounding of an
+//   fp32 value.  Stochastic rounding moves to the far bf16 neighbour with
+//   probability equal to the fraction of the gap ("Randomized Gradient
+//   Compression" blog, "How it works"); with a 16-bit draw u this is "add u
+//   to the 16 discarded bits and truncate".
+// - MFMA operand vector types for v_mfma_f32_32x32x16_bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logra {
+
+// ----------------------------------------------------------------- Philox
+
+// Multipliers and Weyl key increments of Philox4x64 (SC'11).
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+struct Philox4 {
+  uint64_t w[4];
+};
+
+// Ten rounds.  Each round multiplies words 0 and 2 by the two constants,
+// and the new counter is (hi(M1*x2)^x1^k0, lo(M1*x2), hi(M0*x0)^x3^k1,
+// lo(M0*x0)); the key advances by the Weyl constants between rounds.
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                 uint64_t c3, uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t lo0 = c0 * kPhiloxM0;
+    const uint64_t hi0 = __umul64hi(c0, kPhiloxM0);
+    const uint64_t lo1 = c2 * kPhiloxM1;
+    const uint64_t hi1 = __umul64hi(c2, kPhiloxM1);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  Philox4 out;
+  out.w[0] = c0;
+  out.w[1] = c1;
+  out.w[2] = c2;
+  out.w[3] = c3;
+  return out;
+}
+
+// Key words of a projection: (seed, step << 32 | matrix_id).
+struct KeyWords {
+  uint64_t k0, k1;
+};
+
+// 256 sign bits of row j, columns [256*b, 256*b + 256) of sigma.
+// Bit l & 255 of the result (word (l & 255) >> 6, bit l & 63) set means -1.
+__device__ __forceinline__ Philox4 sigma_block(KeyWords key, uint64_t j, uint64_t b) {
+  return philox4x64_10(j, b, 0, 0, key.k0, key.k1);
+}
+
+// 16 stochastic-rounding draws for flat elements [16*g, 16*g + 16): draw of
+// element e is bits [16*(e & 3), +16) of word (e & 15) >> 2.
+__device__ __forceinline__ Philox4 sr_block(KeyWords key, uint64_t g) {
+  return philox4x64_10(g, 0, 1, 0, key.k0, key.k1);
+}
+
+// ------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Nearest-even rounding of an fp32 value to bf16 (bit pattern in the low 16
+// bits).  Adding 0x7FFF plus the lowest kept bit to the pattern carries into
+// the kept bits exactly when the discarded part is above half, or exactly
+// half with an odd kept part.  Overflow lands on infinity.  NaN maps to a
+// quiet NaN of the same sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Stochastic rounding with a 16-bit draw u: the discarded 16 bits are the
+// position inside the gap in units of 2^-16, so adding u and truncating
+// moves away from zero exactly when floor(fraction * 2^16) + u >= 2^16.
+// Infinity and NaN round to nearest.
+__device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t u16) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return f32_to_bf16_rne(f);
+  return (u + u16) >> 16;
+}
+
+// --------------------------------------------------------------- MFMA types
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Split an fp32 value into bf16 hi + bf16 lo with hi = RNE(x) and
+// lo = RNE(x - hi); hi + lo carries ~16 significant bits.
+__device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - bf16_bits_to_f32(hi));
+}
+
+}  // namespace logra

@@ -1,0 +1,53 @@
+// Internal launcher interface between the C ABI layer and the HIP kernels.
+// Launchers assume validated arguments (checked in logra_abi.cpp) and only
+// enqueue work on `stream`; they return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logra {
+
+struct KeyArg {
+  uint64_t k0, k1;
+};
+
+constexpr int kMaxGroup = 16;
+constexpr int kMaxRank = 256;
+
+struct AccItem {
+  const void* D;   // [T x d] bf16 or fp32
+  const float* XAt;
+  float* S;
+  int64_t d;
+  int64_t ldd;
+  void* ws;        // packed projected input of this item
+};
+
+// Rank padded to whole 32-wide MFMA blocks and tokens padded to whole chunks.
+int64_t acc_rank_pad(int64_t r);
+int64_t acc_token_pad(int64_t T);
+size_t acc_ws_bytes_per_item(int64_t T, int64_t r);
+
+hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void* A,
+                          hipStream_t s);
+hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const void* X,
+                          bool bf16, int64_t ldx, float* XAt, hipStream_t s);
+hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
+                             hipStream_t s);
+
+size_t rowadam_ws_bytes(int64_t d);
+hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                          float beta, float eps, float* U, void* ws, hipStream_t s);
+
+size_t klq_ws_bytes(int64_t P, int64_t V);
+hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,
+                                 bool bf16, float tau, float* q, void* ws, hipStream_t s);
+hipError_t launch_step_alpha(const float* q, float delta, float amax, float* alpha,
+                             hipStream_t s);
+
+hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
+                        int64_t ldw, const float* U, double scale, const float* scale_dev,
+                        bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s);
+
+}  // namespace logra

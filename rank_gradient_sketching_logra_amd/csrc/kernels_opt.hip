@@ -1,0 +1,312 @@
+// RowAdam scaling of the sketch, predicted-KL coefficient q and step rule.
+//
+// Sources: paperlayer.ai summary of the LoGRA paper, "B. RowAdam" (row-wise
+// running squared magnitude, Frobenius norm restored, d statistics that
+// persist across projection refreshes); "LoGRA: Scaling LLM Reinforcement
+// Learning with Low-Rank Gradient Sketches" (paperpeel.com) App. D.1 Table 4
+// (beta2, no first moment, relative epsilon), §2.3 and App. A.1 (q as the
+// softmax-weighted variance of the logit change rates), App. A.2 (alpha).
+//
+// All reductions are fixed-order trees (no atomics), so results are
+// bit-reproducible.  RowAdam reduces in fp64; q accumulates per thread in
+// fp32 and combines partial results in fp64.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace logra {
+
+namespace {
+
+// ------------------------------------------------------------- RowAdam
+
+constexpr int kRowsPerBlock = 16;
+
+struct RowAdamWs {
+  double* m;        // [d] row energy sum_j S_ij^2
+  double* vh;       // [d] bias-corrected second moment
+  double* partial;  // [2 * nblocks]: per block (sum m, sum vh)
+  double* scalars;  // [4]: eps*rho, norm ratio, -, -
+};
+
+__device__ __forceinline__ double wave_sum(double x) {
+  // Butterfly over the 64 lanes (fixed pattern, every lane gets the total).
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(256) void rowadam_rows_kernel(int64_t d, int64_t r,
+                                                           const float* __restrict__ S,
+                                                           float* __restrict__ v, double beta,
+                                                           double bias_corr, RowAdamWs ws) {
+  __shared__ double sm[kRowsPerBlock], svh[kRowsPerBlock];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
+  for (int q = wave; q < kRowsPerBlock; q += 4) {
+    const int64_t i = base + q;
+    double m = 0.0, vh = 0.0;
+    if (i < d) {
+      double acc = 0.0;
+      for (int64_t j = lane; j < r; j += 64) {
+        const double x = (double)S[i * r + j];
+        acc += x * x;
+      }
+      m = wave_sum(acc);
+      const double vn = beta * (double)v[i] + (1.0 - beta) * m;
+      vh = vn / bias_corr;
+      if (lane == 0) {
+        v[i] = (float)vn;
+        ws.m[i] = m;
+        ws.vh[i] = vh;
+      }
+    }
+    if (lane == 0) {
+      sm[q] = m;
+      svh[q] = vh;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = 0.0, b = 0.0;
+    for (int q = 0; q < kRowsPerBlock; ++q) {
+      a += sm[q];
+      b += svh[q];
+    }
+    ws.partial[2 * blockIdx.x] = a;
+    ws.partial[2 * blockIdx.x + 1] = b;
+  }
+}
+
+// One block: rho, then ||Ut||_F^2 = sum_i m_i / (sqrt(vh_i) + eps rho)^2 and
+// the norm-restoring ratio ||S||_F / ||Ut||_F.
+__global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nblocks,
+                                                           double eps, RowAdamWs ws) {
+  __shared__ double red[256];
+  __shared__ double tot[2];
+  if (threadIdx.x == 0) {
+    double a = 0.0, b = 0.0;
+    for (int64_t q = 0; q < nblocks; ++q) {
+      a += ws.partial[2 * q];
+      b += ws.partial[2 * q + 1];
+    }
+    tot[0] = a;  // ||S||_F^2
+    tot[1] = b;  // sum vh
+  }
+  __syncthreads();
+  const double erho = eps * sqrt(tot[1] / (double)d);
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < d; i += 256) {
+    const double den = sqrt(ws.vh[i]) + erho;
+    if (den > 0.0) acc += ws.m[i] / (den * den);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double nu2 = red[0];
+    ws.scalars[0] = erho;
+    ws.scalars[1] = nu2 > 0.0 ? sqrt(tot[0] / nu2) : 0.0;
+  }
+}
+
+__global__ __launch_bounds__(256) void rowadam_apply_kernel(int64_t d, int64_t r,
+                                                            const float* S, float* U,
+                                                            RowAdamWs ws) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= d * r) return;
+  const int64_t i = idx / r;
+  const double den = sqrt(ws.vh[i]) + ws.scalars[0];
+  const double f = den > 0.0 ? ws.scalars[1] / den : 0.0;
+  U[idx] = (float)((double)S[idx] * f);
+}
+
+// -------------------------------------------------------- predicted KL q
+
+// Partial softmax moments of one chunk of one context, relative to the
+// running maximum m of z/tau and to a per-context shift c of zdot:
+//   w = sum exp(l - m), s1 = sum exp(l - m)(zd - c), s2 = sum exp(l - m)(zd - c)^2.
+struct Moments {
+  float m, w, s1, s2;
+};
+
+__device__ __forceinline__ Moments combine(Moments a, Moments b) {
+  if (b.w == 0.f && b.m == -INFINITY) return a;
+  if (a.w == 0.f && a.m == -INFINITY) return b;
+  const float m = fmaxf(a.m, b.m);
+  const float fa = __expf(a.m - m), fb = __expf(b.m - m);
+  return Moments{m, a.w * fa + b.w * fb, a.s1 * fa + b.s1 * fb, a.s2 * fa + b.s2 * fb};
+}
+
+constexpr int kKlqThreads = 256;
+constexpr int kKlqChunks = 16;  // chunks of V per context
+
+template <bool BF16>
+__device__ __forceinline__ float load_val(const void* p, int64_t i) {
+  if (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kKlqThreads) void klq_partial_kernel(int64_t V, const void* z,
+                                                                  const void* zd, float inv_tau,
+                                                                  double* __restrict__ part) {
+  __shared__ Moments red[kKlqThreads];
+  const int64_t s = blockIdx.y;
+  const int64_t chunk = (V + kKlqChunks - 1) / kKlqChunks;
+  const int64_t lo = blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < V ? lo + chunk : V;
+  const int64_t row = s * V;
+  const float c = load_val<BF16>(zd, row);  // shift: zdot of the first vocabulary entry
+  Moments mo{-INFINITY, 0.f, 0.f, 0.f};
+  for (int64_t v0 = lo + (int64_t)threadIdx.x * 8; v0 < hi; v0 += (int64_t)kKlqThreads * 8) {
+    float l[8], y[8];
+    float gm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = v0 + e < hi;
+      l[e] = ok ? load_val<BF16>(z, row + v0 + e) * inv_tau : -INFINITY;
+      y[e] = ok ? load_val<BF16>(zd, row + v0 + e) - c : 0.f;
+      gm = fmaxf(gm, l[e]);
+    }
+    if (gm > mo.m) {
+      const float f = __expf(mo.m - gm);
+      mo.w *= f;
+      mo.s1 *= f;
+      mo.s2 *= f;
+      mo.m = gm;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __expf(l[e] - mo.m);
+      mo.w += p;
+      mo.s1 += p * y[e];
+      mo.s2 += p * y[e] * y[e];
+    }
+  }
+  red[threadIdx.x] = mo;
+  __syncthreads();
+  for (int w = kKlqThreads / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = combine(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double* o = part + (s * kKlqChunks + blockIdx.x) * 4;
+    o[0] = red[0].m;
+    o[1] = red[0].w;
+    o[2] = red[0].s1;
+    o[3] = red[0].s2;
+  }
+}
+
+// Combine the chunk partials of each context in order (fp64), form the
+// centred variance, and sum over contexts in a fixed tree.
+__global__ __launch_bounds__(256) void klq_final_kernel(int64_t P, const double* __restrict__ part,
+                                                        double scale, float* __restrict__ q) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int64_t s = threadIdx.x; s < P; s += 256) {
+    double m = -INFINITY, w = 0.0, s1 = 0.0, s2 = 0.0;
+    for (int c = 0; c < kKlqChunks; ++c) {
+      const double* o = part + (s * kKlqChunks + c) * 4;
+      if (o[1] == 0.0 && o[0] == -INFINITY) continue;
+      const double mm = o[0] > m ? o[0] : m;
+      const double fa = exp(m - mm), fb = exp(o[0] - mm);
+      w = w * fa + o[1] * fb;
+      s1 = s1 * fa + o[2] * fb;
+      s2 = s2 * fa + o[3] * fb;
+      m = mm;
+    }
+    const double mean = s1 / w;
+    double var = s2 / w - mean * mean;
+    if (var < 0.0) var = 0.0;
+    acc += var;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) q[0] = (float)(red[0] * scale);
+}
+
+__global__ void step_alpha_kernel(const float* q, float delta, float amax, float* alpha) {
+  const float qq = *q;
+  float a;
+  if (!(qq >= 0.f)) a = __int_as_float(0x7FC00000);
+  else if (qq == 0.f) a = amax;
+  else a = fminf(amax, sqrtf(delta / qq));
+  *alpha = a;
+}
+
+RowAdamWs rowadam_ws_layout(void* ws, int64_t d) {
+  const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
+  double* p = static_cast<double*>(ws);
+  RowAdamWs w;
+  w.m = p;
+  w.vh = p + d;
+  w.partial = p + 2 * d;
+  w.scalars = p + 2 * d + 2 * nb;
+  return w;
+}
+
+}  // namespace
+
+size_t rowadam_ws_bytes(int64_t d) {
+  const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
+  return (size_t)(2 * d + 2 * nb + 4) * sizeof(double);
+}
+
+hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                          float beta, float eps, float* U, void* ws, hipStream_t s) {
+  const RowAdamWs w = rowadam_ws_layout(ws, d);
+  const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
+  const double b = (double)beta;
+  const double bias = 1.0 - std::pow(b, (double)t);
+  hipLaunchKernelGGL(rowadam_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, d, r, S, v, b,
+                     bias, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rowadam_norm_kernel, dim3(1), dim3(256), 0, s, d, nb, (double)eps, w);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = d * r;
+  hipLaunchKernelGGL(rowadam_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     d, r, S, U, w);
+  return hipGetLastError();
+}
+
+size_t klq_ws_bytes(int64_t P, int64_t V) {
+  (void)V;
+  return (size_t)(P * kKlqChunks * 4) * sizeof(double);
+}
+
+hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,
+                                 bool bf16, float tau, float* q, void* ws, hipStream_t s) {
+  double* part = static_cast<double*>(ws);
+  const dim3 grid(kKlqChunks, (unsigned)P);
+  const float inv_tau = (float)(1.0 / (double)tau);
+  if (bf16)
+    hipLaunchKernelGGL(klq_partial_kernel<true>, grid, dim3(kKlqThreads), 0, s, V, z, zd,
+                       inv_tau, part);
+  else
+    hipLaunchKernelGGL(klq_partial_kernel<false>, grid, dim3(kKlqThreads), 0, s, V, z, zd,
+                       inv_tau, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const double scale = 1.0 / (2.0 * (double)P * (double)tau * (double)tau);
+  hipLaunchKernelGGL(klq_final_kernel, dim3(1), dim3(256), 0, s, P, part, scale, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_alpha(const float* q, float delta, float amax, float* alpha,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(step_alpha_kernel, dim3(1), dim3(1), 0, s, q, delta, amax, alpha);
+  return hipGetLastError();
+}
+
+}  // namespace logra

@@ -1,0 +1,260 @@
+// C ABI entry points: host-side validation, then launches on the caller's
+// stream.  Nothing is launched when validation fails.  See include/logra.h
+// for the contract of every call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/logra.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return LOGRA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LOGRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [p, p + n).
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range(const void* p, size_t n) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + n};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+size_t elem_size(logra_dtype t) { return t == LOGRA_F32 ? 4 : t == LOGRA_BF16 ? 2 : 1; }
+
+// Extent in bytes of a [rows x cols] matrix with leading dimension ld.
+size_t extent(int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  return (size_t)((rows - 1) * ld + cols) * es;
+}
+
+bool bad_rank(int64_t r) { return r < 1 || r > LOGRA_MAX_RANK; }
+
+logra::KeyArg key_words(uint64_t seed, const logra_key* key) {
+  return logra::KeyArg{seed, ((uint64_t)key->step << 32) | (uint64_t)key->matrix_id};
+}
+
+// A matrix operand (X, D or W): dtype, alignment of base and rows.
+int check_matrix(const char* name, const void* p, logra_dtype t, int64_t ld, int64_t cols) {
+  if (t != LOGRA_F32 && t != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "%s: dtype must be F32 or BF16", name);
+  if (ld < cols) return fail(LOGRA_ERR_SHAPE, "%s: leading dimension %lld < %lld", name, (long long)ld, (long long)cols);
+  if (!aligned16(p)) return fail(LOGRA_ERR_ALIGN, "%s: base pointer not 16-byte aligned", name);
+  if ((ld * (int64_t)elem_size(t)) % 16 != 0)
+    return fail(LOGRA_ERR_ALIGN, "%s: rows not 16-byte aligned (leading dimension %lld)", name, (long long)ld);
+  return LOGRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LOGRA_API const char* logra_version(void) { return "logra-mi355x 0.1.0 (gfx950)"; }
+
+LOGRA_API const char* logra_last_error(void) { return g_last_error.c_str(); }
+
+LOGRA_API int64_t logra_sketch_bytes(int64_t d, int64_t r) {
+  if (d < 0 || r < 0) return -1;
+  return 4 * d * r;
+}
+
+LOGRA_API int logra_regen_A(const logra_key* key, int64_t r, int64_t k, logra_dtype out,
+                            void* A, logra_stream stream) {
+  if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A: NULL key or output");
+  if (bad_rank(r) || k < 1) return fail(LOGRA_ERR_SHAPE, "regen_A: need 1 <= r <= %d and k >= 1", LOGRA_MAX_RANK);
+  if (out != LOGRA_I8 && out != LOGRA_F32) return fail(LOGRA_ERR_DTYPE, "regen_A: output must be I8 or F32");
+  return hip_status(logra::launch_regen_A(key_words(key->seed, key), r, k, out == LOGRA_I8, A,
+                                          static_cast<hipStream_t>(stream)),
+                    "regen_A launch");
+}
+
+LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, int64_t r,
+                                  const void* X, logra_dtype x_dtype, int64_t ldx, float* XAt,
+                                  logra_stream stream) {
+  if (!key || !X || !XAt) return fail(LOGRA_ERR_NULL, "project_input: NULL pointer");
+  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  int st = check_matrix("project_input X", X, x_dtype, ldx, k);
+  if (st) return st;
+  if (!aligned16(XAt)) return fail(LOGRA_ERR_ALIGN, "project_input: XAt not 16-byte aligned");
+  if (overlap(range(X, extent(T, k, ldx, elem_size(x_dtype))), range(XAt, (size_t)(T * r) * 4)))
+    return fail(LOGRA_ERR_ALIAS, "project_input: XAt overlaps X");
+  return hip_status(logra::launch_project(key_words(key->seed, key), T, k, r, X, x_dtype == LOGRA_BF16,
+                                          ldx, XAt, static_cast<hipStream_t>(stream)),
+                    "project_input launch");
+}
+
+LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r) {
+  if (T < 1 || bad_rank(r)) return 0;
+  return logra::acc_ws_bytes_per_item(T, r);
+}
+
+static int check_acc_item(const char* name, int64_t T, int64_t r, logra_dtype dt, const void* D,
+                          int64_t d, int64_t ldd, const float* XAt, const float* S, void* ws,
+                          size_t ws_bytes) {
+  if (!D || !XAt || !S) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
+  if (d < 1) return fail(LOGRA_ERR_SHAPE, "%s: d must be >= 1", name);
+  int st = check_matrix(name, D, dt, ldd, d);
+  if (st) return st;
+  if (!aligned16(XAt) || !aligned16(S)) return fail(LOGRA_ERR_ALIGN, "%s: XAt and S must be 16-byte aligned", name);
+  const Range rs = range(S, (size_t)(d * r) * 4);
+  if (overlap(rs, range(D, extent(T, d, ldd, elem_size(dt)))) || overlap(rs, range(XAt, (size_t)(T * r) * 4)))
+    return fail(LOGRA_ERR_ALIAS, "%s: S overlaps D or XAt", name);
+  if (dt == LOGRA_BF16) {
+    const size_t need = logra::acc_ws_bytes_per_item(T, r);
+    if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
+    if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "%s: workspace not 16-byte aligned", name);
+    const Range rw = range(ws, need);
+    if (overlap(rw, rs) || overlap(rw, range(D, extent(T, d, ldd, elem_size(dt)))) ||
+        overlap(rw, range(XAt, (size_t)(T * r) * 4)))
+      return fail(LOGRA_ERR_ALIAS, "%s: workspace overlaps an operand", name);
+  }
+  return LOGRA_OK;
+}
+
+LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r, const void* D,
+                                      logra_dtype d_dtype, int64_t ldd, const float* XAt,
+                                      float* S, void* ws, size_t ws_bytes, logra_stream stream) {
+  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  int st = check_acc_item("sketch_accumulate", T, r, d_dtype, D, d, ldd, XAt, S, ws, ws_bytes);
+  if (st) return st;
+  logra::AccItem it{D, XAt, S, d, ldd, ws};
+  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, &it, 1,
+                                             static_cast<hipStream_t>(stream)),
+                    "sketch_accumulate launch");
+}
+
+LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype d_dtype,
+                                              const logra_acc_desc* descs, int n, void* ws,
+                                              size_t ws_bytes, logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t per = logra::acc_ws_bytes_per_item(T, r);
+  if (d_dtype == LOGRA_BF16 && (!ws || ws_bytes < per * (size_t)n))
+    return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_grouped: workspace of %zu bytes needed", per * (size_t)n);
+  logra::AccItem items[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    void* wsi = d_dtype == LOGRA_BF16 ? static_cast<char*>(ws) + per * (size_t)i : nullptr;
+    int st = check_acc_item("sketch_accumulate_grouped", T, r, d_dtype, descs[i].D, descs[i].d, descs[i].ldd,
+                            descs[i].XAt, descs[i].S, wsi, per);
+    if (st) return st;
+    for (int j = 0; j < i; ++j)
+      if (overlap(range(descs[i].S, (size_t)(descs[i].d * r) * 4), range(descs[j].S, (size_t)(descs[j].d * r) * 4)))
+        return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_grouped: sketches %d and %d overlap", j, i);
+    items[i] = logra::AccItem{descs[i].D, descs[i].XAt, descs[i].S, descs[i].d, descs[i].ldd, wsi};
+  }
+  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, items, n,
+                                             static_cast<hipStream_t>(stream)),
+                    "sketch_accumulate_grouped launch");
+}
+
+LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {
+  if (d < 1) return 0;
+  return logra::rowadam_ws_bytes(d);
+}
+
+LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                            float beta, float eps, float* U, void* ws, size_t ws_bytes,
+                            logra_stream stream) {
+  if (!S || !v || !U) return fail(LOGRA_ERR_NULL, "rowadam: NULL pointer");
+  if (d < 1 || r < 1) return fail(LOGRA_ERR_SHAPE, "rowadam: need d, r >= 1");
+  if (t < 1) return fail(LOGRA_ERR_DOMAIN, "rowadam: t counts updates from 1");
+  if (!(beta >= 0.f && beta < 1.f)) return fail(LOGRA_ERR_DOMAIN, "rowadam: beta must be in [0, 1)");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "rowadam: eps must be finite and >= 0");
+  const size_t need = logra::rowadam_ws_bytes(d);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "rowadam: workspace of %zu bytes needed", need);
+  if (!aligned16(S) || !aligned16(U) || !aligned16(v) || !aligned16(ws))
+    return fail(LOGRA_ERR_ALIGN, "rowadam: S, U, v and workspace must be 16-byte aligned");
+  const Range rs = range(S, (size_t)(d * r) * 4), ru = range(U, (size_t)(d * r) * 4);
+  if (overlap(rs, ru) && rs.lo != ru.lo) return fail(LOGRA_ERR_ALIAS, "rowadam: U partially overlaps S");
+  const Range rv = range(v, (size_t)d * 4), rw = range(ws, need);
+  if (overlap(rv, rs) || overlap(rv, ru) || overlap(rw, rs) || overlap(rw, ru) || overlap(rw, rv))
+    return fail(LOGRA_ERR_ALIAS, "rowadam: v or workspace overlaps an operand");
+  return hip_status(logra::launch_rowadam(d, r, S, v, t, beta, eps, U, ws, static_cast<hipStream_t>(stream)),
+                    "rowadam launch");
+}
+
+LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V) {
+  if (P < 1 || V < 1) return 0;
+  return logra::klq_ws_bytes(P, V);
+}
+
+LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zdot,
+                                   logra_dtype dtype, float tau, float* q_dev, void* ws,
+                                   size_t ws_bytes, logra_stream stream) {
+  if (!z || !zdot || !q_dev) return fail(LOGRA_ERR_NULL, "predicted_kl_q: NULL pointer");
+  if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: need P, V >= 1");
+  if (P > 65535) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: at most 65535 contexts per call");
+  if (dtype != LOGRA_F32 && dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "predicted_kl_q: dtype must be F32 or BF16");
+  if (!(tau > 0.f) || !std::isfinite(tau)) return fail(LOGRA_ERR_DOMAIN, "predicted_kl_q: tau must be finite and > 0");
+  const size_t need = logra::klq_ws_bytes(P, V);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "predicted_kl_q: workspace of %zu bytes needed", need);
+  if (!aligned16(z) || !aligned16(zdot) || !aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "predicted_kl_q: z, zdot and workspace must be 16-byte aligned");
+  return hip_status(logra::launch_predicted_kl_q(P, V, z, zdot, dtype == LOGRA_BF16, tau, q_dev, ws,
+                                                 static_cast<hipStream_t>(stream)),
+                    "predicted_kl_q launch");
+}
+
+LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double* alpha) {
+  if (!alpha) return fail(LOGRA_ERR_NULL, "step_alpha: NULL output");
+  if (!(delta > 0.0) || !(alpha_max > 0.0)) return fail(LOGRA_ERR_DOMAIN, "step_alpha: delta and alpha_max must be > 0");
+  if (std::isnan(q) || q < 0.0) return fail(LOGRA_ERR_DOMAIN, "step_alpha: q must be >= 0");
+  *alpha = q == 0.0 ? alpha_max : std::fmin(alpha_max, std::sqrt(delta / q));
+  return ok();
+}
+
+LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_max,
+                                   float* alpha_dev, logra_stream stream) {
+  if (!q_dev || !alpha_dev) return fail(LOGRA_ERR_NULL, "step_alpha_dev: NULL pointer");
+  if (!(delta > 0.f) || !(alpha_max > 0.f)) return fail(LOGRA_ERR_DOMAIN, "step_alpha_dev: delta and alpha_max must be > 0");
+  return hip_status(logra::launch_step_alpha(q_dev, delta, alpha_max, alpha_dev, static_cast<hipStream_t>(stream)),
+                    "step_alpha_dev launch");
+}
+
+LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r, void* W,
+                          logra_dtype w_dtype, int64_t ldw, const float* U, double scale,
+                          const float* scale_dev, logra_round mode, uint64_t sr_seed,
+                          int64_t row0, logra_stream stream) {
+  if (!key || !W || !U) return fail(LOGRA_ERR_NULL, "merge: NULL pointer");
+  if (d < 1 || k < 1 || bad_rank(r) || row0 < 0) return fail(LOGRA_ERR_SHAPE, "merge: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
+  int st = check_matrix("merge W", W, w_dtype, ldw, k);
+  if (st) return st;
+  if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "merge: unknown rounding mode");
+  if (w_dtype == LOGRA_F32 && mode == LOGRA_ROUND_STOCHASTIC)
+    return fail(LOGRA_ERR_DTYPE, "merge: stochastic rounding is defined for bf16 weights only");
+  if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "merge: scale must be finite");
+  if (!aligned16(U)) return fail(LOGRA_ERR_ALIGN, "merge: U not 16-byte aligned");
+  const Range rw = range(W, extent(d, k, ldw, elem_size(w_dtype)));
+  if (overlap(rw, range(U, (size_t)(d * r) * 4))) return fail(LOGRA_ERR_ALIAS, "merge: W overlaps U");
+  if (scale_dev && overlap(rw, range(scale_dev, 4))) return fail(LOGRA_ERR_ALIAS, "merge: W overlaps the device scale");
+  return hip_status(logra::launch_merge(key_words(key->seed, key), d, k, r, W, w_dtype == LOGRA_BF16, ldw, U,
+                                        scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
+                                        key_words(sr_seed, key), row0, static_cast<hipStream_t>(stream)),
+                    "merge launch");
+}
+
+}  // extern "C"

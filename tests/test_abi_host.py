@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything.
+
+No call here reaches a kernel launch (validation fails first), so these run
+without a GPU.  Device pointers are fake addresses: validation never
+dereferences them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_gradient_sketching_logra_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logra.h")
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LOGRA_API\s+[\w\s\*]+?\b(logra_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        import rank_gradient_sketching_logra_amd.build as build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) >= 15
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_sizes(lib):
+    assert "gfx950" in B.version()
+    assert B.sketch_bytes(4096, 64) == 1 << 20          # 1 MiB, paper §2.2
+    assert lib.logra_sketch_bytes(-1, 3) == -1
+    assert B.accumulate_ws_bytes(4096, 64) == 2 * 64 * 4096 * 2
+    assert B.accumulate_ws_bytes(1000, 33) == 2 * 64 * 1024 * 2
+    assert B.accumulate_ws_bytes(0, 8) == 0
+    assert B.rowadam_ws_bytes(0) == 0
+    assert B.predicted_kl_q_ws_bytes(64, 152064) > 0
+
+
+def test_step_alpha_host(lib):
+    assert B.step_alpha(8e-3, 2e-3, 4.0) == pytest.approx(0.5, rel=1e-15)
+    assert B.step_alpha(0.0, 2e-3, 4.0) == 4.0
+    assert B.step_alpha(1e-9, 2e-3, 4.0) == 4.0
+    for q, dl, am in ((-1.0, 1e-3, 1.0), (float("nan"), 1e-3, 1.0), (1.0, 0.0, 1.0), (1.0, 1e-3, -1.0)):
+        with pytest.raises(B.LograError) as e:
+            B.step_alpha(q, dl, am)
+        assert e.value.status == B.ERR_DOMAIN
+
+
+A = 0x10000          # fake, 16-byte aligned device addresses
+Bp = 0x4000000
+C = 0x8000000
+Dp = 0xC000000
+
+
+def key():
+    return B.Key(1, 0, 0)
+
+
+def err(fn, *args):
+    st = fn(*args)
+    assert st != B.OK
+    return st
+
+
+def test_regen_validation(lib):
+    assert err(lib.logra_regen_A, None, 8, 16, B.I8, A, None) == B.ERR_NULL
+    assert err(lib.logra_regen_A, ctypes.byref(key()), 0, 16, B.I8, A, None) == B.ERR_SHAPE
+    assert err(lib.logra_regen_A, ctypes.byref(key()), 257, 16, B.I8, A, None) == B.ERR_SHAPE
+    assert err(lib.logra_regen_A, ctypes.byref(key()), 8, 16, B.BF16, A, None) == B.ERR_DTYPE
+    assert "regen_A" in lib.logra_last_error().decode()
+
+
+def test_project_validation(lib):
+    k = ctypes.byref(key())
+    f = lib.logra_project_input
+    assert err(f, k, 16, 64, 8, None, B.BF16, 64, Bp, None) == B.ERR_NULL
+    assert err(f, k, 0, 64, 8, A, B.BF16, 64, Bp, None) == B.ERR_SHAPE
+    assert err(f, k, 16, 64, 8, A, B.BF16, 32, Bp, None) == B.ERR_SHAPE        # ldx < k
+    assert err(f, k, 16, 64, 8, A, B.I8, 64, Bp, None) == B.ERR_DTYPE
+    assert err(f, k, 16, 64, 8, A + 2, B.BF16, 64, Bp, None) == B.ERR_ALIGN
+    assert err(f, k, 16, 60, 8, A, B.BF16, 60, Bp, None) == B.ERR_ALIGN      # 120-byte rows
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, A + 64, None) == B.ERR_ALIAS
+
+
+def test_accumulate_validation(lib):
+    f = lib.logra_sketch_accumulate
+    ws = B.accumulate_ws_bytes(128, 64)
+    assert err(f, 128, 64, 64, None, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_NULL
+    assert err(f, 128, 64, 300, A, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 0, 64, 64, A, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 128, 64, 64, A, B.BF16, 64, Bp, C, None, 0, None) == B.ERR_WORKSPACE
+    assert err(f, 128, 64, 64, A, B.BF16, 64, Bp, C, Dp, ws - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 128, 64, 64, A, B.BF16, 64, Bp, A + 128, Dp, ws, None) == B.ERR_ALIAS   # S in D
+    assert err(f, 128, 64, 64, A, B.BF16, 64, Bp, C, C + 256, ws, None) == B.ERR_ALIAS    # ws in S
+    assert err(f, 128, 64, 64, A, B.BF16, 64, Bp + 4, C, Dp, ws, None) == B.ERR_ALIGN
+
+
+def test_grouped_validation(lib):
+    f = lib.logra_sketch_accumulate_grouped
+    ws = 2 * B.accumulate_ws_bytes(128, 64)
+    descs = (B.AccDesc * 2)(B.AccDesc(A, Bp, C, 64, 64), B.AccDesc(A + 65536, Bp + 65536, C + 64, 64, 64))
+    assert err(f, 128, 64, B.BF16, descs, 2, Dp, ws, None) == B.ERR_ALIAS     # sketches overlap
+    assert err(f, 128, 64, B.BF16, descs, 0, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 128, 64, B.BF16, descs, 17, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 128, 64, B.BF16, descs, 2, Dp, ws // 2, None) == B.ERR_WORKSPACE
+    assert err(f, 128, 64, B.BF16, None, 2, Dp, ws, None) == B.ERR_NULL
+
+
+def test_rowadam_validation(lib):
+    f = lib.logra_rowadam
+    ws = B.rowadam_ws_bytes(64)
+    assert err(f, 64, 8, None, Bp, 1, 0.95, 1e-8, C, Dp, ws, None) == B.ERR_NULL
+    assert err(f, 64, 8, A, Bp, 0, 0.95, 1e-8, C, Dp, ws, None) == B.ERR_DOMAIN       # t < 1
+    assert err(f, 64, 8, A, Bp, 1, 1.0, 1e-8, C, Dp, ws, None) == B.ERR_DOMAIN        # beta
+    assert err(f, 64, 8, A, Bp, 1, 0.95, -1.0, C, Dp, ws, None) == B.ERR_DOMAIN       # eps
+    assert err(f, 64, 8, A, Bp, 1, 0.95, 1e-8, C, Dp, ws - 8, None) == B.ERR_WORKSPACE
+    assert err(f, 64, 8, A, Bp, 1, 0.95, 1e-8, A + 16, Dp, ws, None) == B.ERR_ALIAS    # partial overlap
+    assert err(f, 64, 8, A, A + 64, 1, 0.95, 1e-8, C, Dp, ws, None) == B.ERR_ALIAS     # v inside S
+
+
+def test_predicted_kl_validation(lib):
+    f = lib.logra_predicted_kl_q
+    ws = B.predicted_kl_q_ws_bytes(4, 512)
+    assert err(f, 4, 512, None, Bp, B.BF16, 1.0, C, Dp, ws, None) == B.ERR_NULL
+    assert err(f, 0, 512, A, Bp, B.BF16, 1.0, C, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 4, 512, A, Bp, B.I8, 1.0, C, Dp, ws, None) == B.ERR_DTYPE
+    assert err(f, 4, 512, A, Bp, B.BF16, 0.0, C, Dp, ws, None) == B.ERR_DOMAIN
+    assert err(f, 4, 512, A, Bp, B.BF16, float("inf"), C, Dp, ws, None) == B.ERR_DOMAIN
+    assert err(f, 4, 512, A, Bp, B.BF16, 1.0, C, Dp, 0, None) == B.ERR_WORKSPACE
+    assert err(lib.logra_step_alpha_dev, None, 1e-3, 4.0, C, None) == B.ERR_NULL
+    assert err(lib.logra_step_alpha_dev, A, 0.0, 4.0, C, None) == B.ERR_DOMAIN
+
+
+def test_merge_validation(lib):
+    f = lib.logra_merge
+    k = ctypes.byref(key())
+    assert err(f, None, 64, 64, 8, A, B.BF16, 64, Bp, 1.0, None, 0, 0, 0, None) == B.ERR_NULL
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp, 1.0, None, 0, 0, -1, None) == B.ERR_SHAPE
+    assert err(f, k, 64, 64, 0, A, B.BF16, 64, Bp, 1.0, None, 0, 0, 0, None) == B.ERR_SHAPE
+    assert err(f, k, 64, 64, 8, A, B.F32, 64, Bp, 1.0, None, 1, 0, 0, None) == B.ERR_DTYPE   # SR on fp32
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp, float("nan"), None, 0, 0, 0, None) == B.ERR_DOMAIN
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp, 1.0, None, 7, 0, 0, None) == B.ERR_DOMAIN
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, A + 1024, 1.0, None, 0, 0, 0, None) == B.ERR_ALIAS
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp + 8, 1.0, None, 0, 0, 0, None) == B.ERR_ALIGN

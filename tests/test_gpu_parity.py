@@ -1,0 +1,425 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Tolerances (the contract): S and U relative Frobenius error <= 2e-3; q and
+alpha <= 1e-4 relative; merged W within 1 bf16 ulp of the oracle on >= 99.99%
+of elements; A bit-exact; repeated merges bit-identical.  Tighter bounds
+derived from the arithmetic are asserted as well, so that a dropped term
+(e.g. the lo half of the bf16 split, worth ~1.7e-3) cannot hide under the
+contract's 2e-3:
+  - XAt from bf16 X: exact products, fp32 accumulation -> <= 1e-5;
+  - S from bf16 D: XAt carried as bf16 hi + lo (~2^-17 relative) and fp32
+    accumulation -> <= 5e-5;
+  - U from the same S: fp64 reductions -> <= 1e-6.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import philox
+from rank_gradient_sketching_logra_amd import binding as B
+from rank_gradient_sketching_logra_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the parity tests need an MI355X")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def relfro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def bf16_inputs(shape, std, words):
+    bits = synth.normal(shape, std, words, "bf16")
+    return bits, oracle.bf16_bits_to_f64(bits)
+
+
+# ------------------------------------------------------------ regen A
+
+
+@pytest.mark.parametrize("r,k", [(1, 1), (8, 256), (64, 3584), (33, 700), (256, 5120), (7, 1000)])
+def test_regen_A_bit_exact(r, k):
+    say(f"regen_A r={r} k={k}")
+    kk = B.key(0x1234ABCD, 17, 3)
+    A8 = B.regen_A(kk, r, k, torch.int8, DEV).cpu().numpy()
+    A32 = B.regen_A(kk, r, k, torch.float32, DEV).cpu().numpy()
+    assert np.array_equal(A8, oracle.regen_A(0x1234ABCD, 17, 3, r, k, kind="i8"))
+    assert np.array_equal(A32.view(np.uint32), oracle.regen_A(0x1234ABCD, 17, 3, r, k, kind="f32").view(np.uint32))
+
+
+# ------------------------------------------------------------ project
+
+
+@pytest.mark.parametrize("T,k,r,ldx", [(64, 256, 64, 256), (1000, 712, 33, 720), (96, 3584, 256, 3584),
+                                       (37, 40, 1, 48), (512, 1536, 64, 1536)])
+def test_project_bf16(T, k, r, ldx):
+    say(f"project bf16 T={T} k={k} r={r} ldx={ldx}")
+    bits, X = bf16_inputs((T, ldx), 1.0, (9, T, k, r, 0))
+    Xd = bf16_dev(bits)[:, :k]
+    kk = B.key(5, 2, 1)
+    XAt = B.project_input(kk, Xd, r).cpu().numpy()
+    want = oracle.project(X[:, :k], oracle.regen_A(5, 2, 1, r, k))
+    assert relfro(XAt, want) <= 1e-5
+
+
+def test_project_identity_gives_projection_transpose():
+    """X = I_k (bf16, exact) gives X A^T = A^T bit for bit against regen_A's fp32 A."""
+    k, r = 512, 64
+    say("project identity")
+    Xd = torch.eye(k, dtype=torch.bfloat16, device=DEV)
+    kk = B.key(11, 4, 9)
+    XAt = B.project_input(kk, Xd, r).cpu().numpy()
+    A32 = B.regen_A(kk, r, k, torch.float32, DEV).cpu().numpy()
+    assert np.array_equal(XAt.view(np.uint32), A32.T.copy().view(np.uint32))
+
+
+@pytest.mark.parametrize("T,k,r", [(512, 256, 8), (33, 300, 5)])
+def test_project_f32(T, k, r):
+    say(f"project f32 T={T} k={k} r={r}")
+    X = synth.normal((T, k), 1.0, (10, T, k, r, 0), "f32")
+    kk = B.key(1, 0, 0)
+    XAt = B.project_input(kk, torch.from_numpy(X).to(DEV), r).cpu().numpy()
+    want = oracle.project(X.astype(np.float64), oracle.regen_A(1, 0, 0, r, k))
+    assert relfro(XAt, want) <= 1e-6
+
+
+# ------------------------------------------------------------ accumulate
+
+
+@pytest.mark.parametrize("T,d,r,ldd", [(1000, 300, 64, 304), (512, 256, 8, 256), (4096, 512, 64, 512),
+                                       (300, 1000, 256, 1000), (77, 24, 33, 24), (2048, 1536, 100, 1536),
+                                       (16, 8, 1, 8)])
+def test_accumulate_bf16(T, d, r, ldd):
+    say(f"accumulate bf16 T={T} d={d} r={r} ldd={ldd}")
+    S0 = synth.fp32_matrix((d, r), 0.1, (12, d, r, 0, 5))
+    S = torch.from_numpy(S0.copy()).to(DEV)
+    want = S0.astype(np.float64)
+    for mb in range(2):
+        bits, Dm = bf16_inputs((T, ldd), 1e-3, (12, T, d, mb, 1))
+        XAt = synth.fp32_matrix((T, r), 3.0, (12, T, r, mb, 0))
+        B.sketch_accumulate(bf16_dev(bits)[:, :d], torch.from_numpy(XAt).to(DEV), S)
+        want = oracle.accumulate(want, Dm[:, :d], XAt.astype(np.float64))
+    got = S.cpu().numpy()
+    err = relfro(got, want)
+    say(f"  rel-Fro {err:.3e}")
+    assert err <= 2e-3
+    assert err <= 5e-5
+
+
+@pytest.mark.parametrize("T,d,r", [(512, 256, 8), (100, 37, 3)])
+def test_accumulate_f32(T, d, r):
+    say(f"accumulate f32 T={T} d={d} r={r}")
+    ld = (d + 3) // 4 * 4
+    D = synth.normal((T, ld), 1e-3, (13, T, d, 0, 1), "f32")
+    XAt = synth.fp32_matrix((T, r), 2.0, (13, T, r, 0, 0))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    B.sketch_accumulate(torch.from_numpy(D).to(DEV)[:, :d], torch.from_numpy(XAt).to(DEV), S)
+    want = oracle.accumulate(np.zeros((d, r)), D[:, :d].astype(np.float64), XAt.astype(np.float64))
+    assert relfro(S.cpu().numpy(), want) <= 1e-6
+
+
+def test_accumulate_grouped_is_bit_identical_to_single_calls():
+    T, r = 1024, 64
+    shapes = [(3584, 0), (512, 1), (512, 2), (1000, 3), (2048, 4)]
+    say("accumulate grouped vs single")
+    items, singles = [], []
+    for d, i in shapes:
+        bits, _ = bf16_inputs((T, d), 1e-3, (14, d, i, 0, 1))
+        D = bf16_dev(bits)
+        XAt = torch.from_numpy(synth.fp32_matrix((T, r), 3.0, (14, d, i, 0, 0))).to(DEV)
+        S1 = torch.from_numpy(synth.fp32_matrix((d, r), 0.1, (14, d, i, 0, 5))).to(DEV)
+        S2 = S1.clone()
+        items.append((D, XAt, S1))
+        singles.append((D, XAt, S2))
+    B.sketch_accumulate_grouped(items)
+    for D, XAt, S2 in singles:
+        B.sketch_accumulate(D, XAt, S2)
+    for (_, _, S1), (_, _, S2) in zip(items, singles):
+        assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+
+
+def test_accumulate_deterministic_and_zero_d_is_noop():
+    T, d, r = 2048, 2000, 64
+    say("accumulate determinism")
+    bits, _ = bf16_inputs((T, d), 1e-3, (15, 0, 0, 0, 1))
+    D = bf16_dev(bits)
+    XAt = torch.from_numpy(synth.fp32_matrix((T, r), 3.0, (15, 0, 0, 0, 0))).to(DEV)
+    S0 = torch.from_numpy(synth.fp32_matrix((d, r), 0.1, (15, 0, 0, 0, 5))).to(DEV)
+    a, b = S0.clone(), S0.clone()
+    B.sketch_accumulate(D, XAt, a)
+    B.sketch_accumulate(D, XAt, b)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    c = S0.clone()
+    B.sketch_accumulate(torch.zeros_like(D), XAt, c)
+    assert torch.equal(c.view(torch.int32), S0.view(torch.int32))
+
+
+def test_project_then_accumulate_equals_dense_gradient_projection():
+    """End to end on the smallest workload's shapes with bf16 data: S from the
+    library vs (D^T X) A^T from the oracle's dense gradient."""
+    T, d, k, r = 512, 256, 256, 8
+    say("project+accumulate vs dense gradient")
+    kk = B.key(1, 0, 0)
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    G = np.zeros((d, k))
+    for mb in range(2):
+        xb, X = bf16_inputs((T, k), 1.0, (16, mb, 0, 0, 0))
+        db, Dm = bf16_inputs((T, d), 1e-3, (16, mb, 0, 0, 1))
+        XAt = B.project_input(kk, bf16_dev(xb), r)
+        B.sketch_accumulate(bf16_dev(db), XAt, S)
+        G += oracle.dense_gradient(Dm, X)
+    want = G @ oracle.regen_A(1, 0, 0, r, k).T
+    assert relfro(S.cpu().numpy(), want) <= 5e-5
+
+
+# ------------------------------------------------------------ RowAdam
+
+
+@pytest.mark.parametrize("d,r,t,beta", [(4096, 64, 1, 0.999), (18944, 64, 3, 0.95), (300, 7, 2, 0.9),
+                                        (1, 1, 1, 0.95), (513, 256, 5, 0.0)])
+def test_rowadam(d, r, t, beta):
+    say(f"rowadam d={d} r={r} t={t} beta={beta}")
+    S0 = synth.fp32_matrix((d, r), 0.5, (17, d, r, t, 5))
+    S0 *= synth.fp32_matrix((d, 1), 1.0, (17, d, r, t, 6)) ** 2 + np.float32(0.05)
+    if d > 10:
+        S0[5] = 0
+    v0 = np.abs(synth.fp32_matrix((d,), 0.2, (17, d, r, t, 7))) if t > 1 else np.zeros(d, np.float32)
+    S = torch.from_numpy(S0).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    U = B.rowadam(S, v, t, beta, 1e-8)
+    Uw, vw = oracle.rowadam(S0.astype(np.float64), v0.astype(np.float64), t, beta, 1e-8)
+    assert relfro(U.cpu().numpy(), Uw) <= 1e-6
+    assert relfro(v.cpu().numpy(), vw) <= 1e-6
+    nu, ns = np.linalg.norm(U.cpu().numpy().astype(np.float64)), np.linalg.norm(S0.astype(np.float64))
+    assert abs(nu - ns) <= 1e-6 * ns
+
+
+def test_rowadam_in_place_and_zero():
+    d, r = 1000, 64
+    say("rowadam in place / zero")
+    S0 = synth.fp32_matrix((d, r), 1.0, (18, 0, 0, 0, 5))
+    v0 = np.zeros(d, np.float32)
+    S = torch.from_numpy(S0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    B.rowadam(S, v, 1, 0.95, 1e-8, U=S)
+    Uw, _ = oracle.rowadam(S0.astype(np.float64), v0.astype(np.float64), 1, 0.95, 1e-8)
+    assert relfro(S.cpu().numpy(), Uw) <= 1e-6
+    Z = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    U = B.rowadam(Z, torch.ones(d, device=DEV), 4, 0.95, 1e-8)
+    assert torch.count_nonzero(U).item() == 0
+
+
+# ------------------------------------------------------------ predicted KL
+
+
+@pytest.mark.parametrize("P,V,dtype,tau", [(4, 512, "f32", 1.0), (64, 152064, "bf16", 1.0), (3, 1000, "bf16", 0.7),
+                                           (1, 7, "f32", 2.0), (128, 4099, "bf16", 1.0)])
+def test_predicted_kl_q(P, V, dtype, tau):
+    say(f"predicted_kl_q P={P} V={V} {dtype} tau={tau}")
+    z = synth.normal((P, V), 4.0, (19, P, V, 0, 3), dtype)
+    zd = synth.normal((P, V), 1.0, (19, P, V, 0, 4), dtype)
+    if dtype == "bf16":
+        zt, zdt = bf16_dev(z), bf16_dev(zd)
+        z64, zd64 = oracle.bf16_bits_to_f64(z), oracle.bf16_bits_to_f64(zd)
+    else:
+        zt, zdt = torch.from_numpy(z).to(DEV), torch.from_numpy(zd).to(DEV)
+        z64, zd64 = z.astype(np.float64), zd.astype(np.float64)
+    q = B.predicted_kl_q(zt, zdt, tau).item()
+    qw = oracle.predicted_kl_q(z64, zd64, tau)
+    assert abs(q - qw) <= 1e-4 * qw
+    a = B.step_alpha_dev(torch.tensor([q], device=DEV), 2e-3, 4.0).item()
+    aw = oracle.step_alpha(qw, 2e-3, 4.0)
+    assert abs(a - aw) <= 1e-4 * aw
+
+
+def test_predicted_kl_special_cases():
+    say("predicted_kl_q special cases")
+    P, V = 5, 3000
+    z = torch.from_numpy(synth.normal((P, V), 4.0, (20, 0, 0, 0, 3), "f32")).to(DEV)
+    q0 = B.predicted_kl_q(z, torch.full((P, V), 3.25, device=DEV), 1.0).item()
+    assert abs(q0) <= 1e-7
+    zd = synth.normal((1, V), 1.0, (20, 0, 0, 0, 4), "f32")
+    qu = B.predicted_kl_q(torch.zeros((1, V), device=DEV), torch.from_numpy(zd).to(DEV), 2.0).item()
+    assert abs(qu - zd.astype(np.float64).var() / 8.0) <= 1e-5 * qu
+
+
+def test_step_alpha_device_edges():
+    say("step_alpha_dev edges")
+    q = torch.tensor([0.0, 8e-3, -1.0], device=DEV)
+    assert B.step_alpha_dev(q[0:1], 2e-3, 4.0).item() == 4.0
+    assert B.step_alpha_dev(q[1:2], 2e-3, 4.0).item() == pytest.approx(0.5, rel=1e-6)
+    assert math.isnan(B.step_alpha_dev(q[2:3], 2e-3, 4.0).item())
+
+
+# ------------------------------------------------------------ merge
+
+
+def merge_case(d, k, r, mode, scale, seed_words, ldw=None, row0=0, sr_seed=2, mid=3, step=1):
+    ldw = ldw or k
+    wbits = synth.normal((d, ldw), 0.02, seed_words + (2,), "bf16")
+    U = synth.fp32_matrix((d, r), 1.0, seed_words + (7,))
+    W = bf16_dev(wbits)[:, :k]
+    Ut = torch.from_numpy(U).to(DEV)
+    kk = B.key(1, mid, step)
+    B.merge(kk, W, Ut, scale, mode=mode, sr_seed=sr_seed, row0=row0)
+    got = bf16_host(W)
+    A = oracle.regen_A(1, mid, step, r, k)
+    u = philox.sr_draws(sr_seed, mid, step, d, k, row0=row0) if mode == "stochastic" else None
+    want = oracle.merge(oracle.bf16_bits_to_f64(wbits[:, :k]), U.astype(np.float64), A, scale,
+                        w_dtype="bf16", mode=mode, u_draws=u)
+    return got, want, wbits
+
+
+def ulp_check(got_bits, want_bits):
+    g = oracle.bf16_bits_to_f64(got_bits)
+    w = oracle.bf16_bits_to_f64(want_bits)
+    within = np.abs(g - w) <= oracle.ulp_bf16(w)
+    return within.mean(), (got_bits == want_bits).mean()
+
+
+@pytest.mark.parametrize("d,k,r,mode", [(256, 256, 8, "nearest"), (300, 712, 64, "nearest"),
+                                        (300, 712, 64, "stochastic"), (1000, 3584, 64, "stochastic"),
+                                        (130, 5120, 256, "stochastic"), (64, 100, 33, "nearest"),
+                                        (17, 37 * 8, 1, "stochastic")])
+def test_merge_bf16(d, k, r, mode):
+    say(f"merge bf16 d={d} k={k} r={r} {mode}")
+    # scale chosen so the update is a few bf16 ulps of W (W ~ 0.02, ulp ~ 1e-4)
+    got, want, _ = merge_case(d, k, r, mode, 2e-4, (21, d, k, r))
+    frac, exact = ulp_check(got, want)
+    say(f"  within 1 ulp {frac:.6f}, identical {exact:.6f}")
+    assert frac >= 0.9999
+    assert exact >= 0.999
+
+
+def test_merge_rollout_sync_invariant_and_row_blocks():
+    """Two merges of equal W with equal (U, key, scale, mode, sr_seed) are bit-identical;
+    merging a row block with its global row offset equals the same rows of the whole merge."""
+    d, k, r = 700, 1024, 64
+    say("merge determinism / row blocks")
+    wbits = synth.normal((d, k), 0.02, (22, 0, 0, 0, 2), "bf16")
+    U = torch.from_numpy(synth.fp32_matrix((d, r), 1.0, (22, 0, 0, 0, 7))).to(DEV)
+    kk = B.key(9, 5, 2)
+    outs = []
+    for mode in ("nearest", "stochastic"):
+        W1, W2 = bf16_dev(wbits), bf16_dev(wbits)
+        B.merge(kk, W1, U, 3e-4, mode=mode, sr_seed=77)
+        B.merge(kk, W2, U, 3e-4, mode=mode, sr_seed=77)
+        assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+        W3 = bf16_dev(wbits)
+        for a, b in ((0, 100), (100, 333), (333, 700)):
+            B.merge(kk, W3[a:b], U[a:b], 3e-4, mode=mode, sr_seed=77, row0=a)
+        assert torch.equal(W1.view(torch.int16), W3.view(torch.int16))
+        outs.append(W1)
+    assert not torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_merge_zero_update_and_device_scale():
+    d, k, r = 200, 512, 64
+    say("merge zero update / device scale")
+    wbits = synth.normal((d, k), 0.02, (23, 0, 0, 0, 2), "bf16")
+    kk = B.key(3, 1, 0)
+    for mode in ("nearest", "stochastic"):
+        W = bf16_dev(wbits)
+        B.merge(kk, W, torch.zeros((d, r), device=DEV), 1.0, mode=mode, sr_seed=5)
+        assert np.array_equal(bf16_host(W), wbits)
+        W = bf16_dev(wbits)
+        B.merge(kk, W, torch.ones((d, r), device=DEV), 0.0, mode=mode, sr_seed=5)
+        assert np.array_equal(bf16_host(W), wbits)
+    U = torch.from_numpy(synth.fp32_matrix((d, r), 1.0, (23, 0, 0, 0, 7))).to(DEV)
+    W1, W2 = bf16_dev(wbits), bf16_dev(wbits)
+    B.merge(kk, W1, U, 2.5e-4, mode="stochastic", sr_seed=5)
+    B.merge(kk, W2, U, 1e-3, scale_dev=torch.tensor([0.25], device=DEV), mode="stochastic", sr_seed=5)
+    assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+
+
+def test_merge_fp32_unit_factor_and_values():
+    """fp32 W: U = e_i e_j^T, scale = -1 on W = 0 writes row j of A into row i;
+    general values match the oracle's fp32 rounding."""
+    d, k, r = 6, 600, 8
+    say("merge fp32")
+    kk = B.key(5, 9, 2)
+    A32 = B.regen_A(kk, r, k, torch.float32, DEV)
+    for i, j in ((0, 0), (4, 7), (5, 3)):
+        W = torch.zeros((d, k), dtype=torch.float32, device=DEV)
+        U = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+        U[i, j] = 1.0
+        B.merge(kk, W, U, -1.0)
+        assert torch.equal(W[i].view(torch.int32), A32[j].view(torch.int32))
+        assert torch.count_nonzero(W).item() == torch.count_nonzero(A32[j]).item()
+    d, k, r = 256, 256, 8
+    W0 = synth.normal((d, k), 0.02, (24, 0, 0, 0, 2), "f32")
+    U0 = synth.fp32_matrix((d, r), 1.0, (24, 0, 0, 0, 7))
+    W = torch.from_numpy(W0.copy()).to(DEV)
+    B.merge(B.key(1, 0, 0), W, torch.from_numpy(U0).to(DEV), 1e-3)
+    want = oracle.merge(W0.astype(np.float64), U0.astype(np.float64), oracle.regen_A(1, 0, 0, r, k), 1e-3,
+                        w_dtype="f32")
+    got = W.cpu().numpy()
+    assert (got == want).mean() >= 0.999
+    assert np.max(np.abs(got.astype(np.float64) - want) / np.spacing(np.abs(want))) <= 1.0
+
+
+# --------------------------------------------- full-size shapes (sampled)
+
+
+def test_full_size_layer_sampled():
+    """One 7B-shaped layer (q, k, v, o, gate, up, down; r = 64; T = 4096) through the
+    grouped accumulate the benchmark times, checked on sampled rows of every S, and
+    the merge of the gate matrix checked on sampled rows."""
+    w = synth.BY_NAME["qwen2.5-7b-set-r64"]
+    T, r = w.T, w.r
+    say("full-size 7B layer, sampled")
+    rs = np.random.default_rng(25)
+    items, host = [], []
+    for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
+        db = synth.output_grad(w, layer, kind, 0)
+        XAt = synth.fp32_matrix((T, r), 7.5, (25, mid, 0, 0, 0))
+        S0 = synth.fp32_matrix((d, r), 0.3, (25, mid, 0, 0, 5))
+        items.append((bf16_dev(db), torch.from_numpy(XAt).to(DEV), torch.from_numpy(S0.copy()).to(DEV)))
+        host.append((db, XAt, S0, d))
+    B.sketch_accumulate_grouped(items)
+    for (db, XAt, S0, d), (_, _, S) in zip(host, items):
+        rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 48)]))
+        Dc = oracle.bf16_bits_to_f64(db[:, rows])
+        want = S0[rows].astype(np.float64) + Dc.T @ XAt.astype(np.float64)
+        assert relfro(S.cpu().numpy()[rows], want) <= 5e-5
+    # merge of the gate matrix, sampled rows
+    d, k = w.shapes["gate"]
+    wbits = synth.weight(w, 0, "gate")
+    U = synth.fp32_matrix((d, r), 1.0, (25, 4, 0, 0, 7))
+    W = bf16_dev(wbits)
+    kk = B.key(w.seed, 4, w.step)
+    B.merge(kk, W, torch.from_numpy(U).to(DEV), 1e-3 * 0.5, mode="stochastic", sr_seed=w.sr_seed)
+    rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 32)]))
+    A = oracle.regen_A(w.seed, 4, w.step, r, k)
+    got = bf16_host(W)[rows]
+    u = np.concatenate([philox.sr_draws(w.sr_seed, 4, w.step, 1, k, row0=int(i)) for i in rows])
+    want = oracle.merge(oracle.bf16_bits_to_f64(wbits[rows]), U[rows].astype(np.float64), A, 5e-4,
+                        w_dtype="bf16", mode="stochastic", u_draws=u)
+    frac, exact = ulp_check(got, want)
+    assert frac >= 0.9999 and exact >= 0.999
