@@ -195,11 +195,12 @@ LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d);
  *   rho = sqrt(mean_i vh_i);  Ut_ij = S_ij / (sqrt(vh_i) + eps*rho)
  *   U = Ut * ||S||_F / ||Ut||_F   (U = 0 when Ut = 0)
  * S [d x r], U [d x r] fp32 contiguous (U may equal S: in place); v [d]
- * fp32, read and written.  Reductions run in fp64 in a fixed order.
+ * fp32, read and written.  beta and eps are taken in fp64 (0.999 in fp32
+ * would move 1 - beta by 1.3e-5).  Reductions run in fp64 in a fixed order.
  * Errors: NULL pointers; d < 1, r < 1; t < 1; beta not in [0,1); eps < 0 or
  * non-finite; workspace too small; U partially overlapping S. */
 LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                            float beta, float eps, float* U, void* ws, size_t ws_bytes,
+                            double beta, double eps, float* U, void* ws, size_t ws_bytes,
                             logra_stream stream);
 
 /* -------------------------------------------------------- step control */

@@ -44,7 +44,7 @@ SIGNATURES = {
     "logra_sketch_accumulate_grouped": (c_int, [c_int64, c_int64, c_int, POINTER(AccDesc), c_int,
                                                 c_void_p, c_size_t, c_void_p]),
     "logra_rowadam_ws_bytes": (c_size_t, [c_int64]),
-    "logra_rowadam": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_float, c_float,
+    "logra_rowadam": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_double, c_double,
                               c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_predicted_kl_q_ws_bytes": (c_size_t, [c_int64, c_int64]),
     "logra_predicted_kl_q": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int, c_float,

@@ -38,7 +38,7 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
 
 size_t rowadam_ws_bytes(int64_t d);
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                          float beta, float eps, float* U, void* ws, hipStream_t s);
+                          double beta, double eps, float* U, void* ws, hipStream_t s);
 
 size_t klq_ws_bytes(int64_t P, int64_t V);
 hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,

@@ -262,16 +262,16 @@ size_t rowadam_ws_bytes(int64_t d) {
 }
 
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                          float beta, float eps, float* U, void* ws, hipStream_t s) {
+                          double beta, double eps, float* U, void* ws, hipStream_t s) {
   const RowAdamWs w = rowadam_ws_layout(ws, d);
   const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
-  const double b = (double)beta;
+  const double b = beta;
   const double bias = 1.0 - std::pow(b, (double)t);
   hipLaunchKernelGGL(rowadam_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, d, r, S, v, b,
                      bias, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rowadam_norm_kernel, dim3(1), dim3(256), 0, s, d, nb, (double)eps, w);
+  hipLaunchKernelGGL(rowadam_norm_kernel, dim3(1), dim3(256), 0, s, d, nb, eps, w);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = d * r;

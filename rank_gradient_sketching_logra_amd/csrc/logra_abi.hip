@@ -178,13 +178,13 @@ LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {
 }
 
 LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                            float beta, float eps, float* U, void* ws, size_t ws_bytes,
+                            double beta, double eps, float* U, void* ws, size_t ws_bytes,
                             logra_stream stream) {
   if (!S || !v || !U) return fail(LOGRA_ERR_NULL, "rowadam: NULL pointer");
   if (d < 1 || r < 1) return fail(LOGRA_ERR_SHAPE, "rowadam: need d, r >= 1");
   if (t < 1) return fail(LOGRA_ERR_DOMAIN, "rowadam: t counts updates from 1");
-  if (!(beta >= 0.f && beta < 1.f)) return fail(LOGRA_ERR_DOMAIN, "rowadam: beta must be in [0, 1)");
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "rowadam: eps must be finite and >= 0");
+  if (!(beta >= 0.0 && beta < 1.0)) return fail(LOGRA_ERR_DOMAIN, "rowadam: beta must be in [0, 1)");
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "rowadam: eps must be finite and >= 0");
   const size_t need = logra::rowadam_ws_bytes(d);
   if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "rowadam: workspace of %zu bytes needed", need);
   if (!aligned16(S) || !aligned16(U) || !aligned16(v) || !aligned16(ws))

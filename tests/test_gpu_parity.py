@@ -303,14 +303,14 @@ def ulp_check(got_bits, want_bits):
     return within.mean(), (got_bits == want_bits).mean()
 
 
-@pytest.mark.parametrize("d,k,r,mode", [(256, 256, 8, "nearest"), (300, 712, 64, "nearest"),
-                                        (300, 712, 64, "stochastic"), (1000, 3584, 64, "stochastic"),
-                                        (130, 5120, 256, "stochastic"), (64, 100, 33, "nearest"),
-                                        (17, 37 * 8, 1, "stochastic")])
-def test_merge_bf16(d, k, r, mode):
-    say(f"merge bf16 d={d} k={k} r={r} {mode}")
+@pytest.mark.parametrize("d,k,r,mode,ldw", [(256, 256, 8, "nearest", 256), (300, 712, 64, "nearest", 712),
+                                            (300, 712, 64, "stochastic", 712), (1000, 3584, 64, "stochastic", 3584),
+                                            (130, 5120, 256, "stochastic", 5120), (64, 100, 33, "nearest", 104),
+                                            (64, 100, 33, "stochastic", 104), (17, 37 * 8, 1, "stochastic", 296)])
+def test_merge_bf16(d, k, r, mode, ldw):
+    say(f"merge bf16 d={d} k={k} r={r} {mode} ldw={ldw}")
     # scale chosen so the update is a few bf16 ulps of W (W ~ 0.02, ulp ~ 1e-4)
-    got, want, _ = merge_case(d, k, r, mode, 2e-4, (21, d, k, r))
+    got, want, _ = merge_case(d, k, r, mode, 2e-4, (21, d, k, r), ldw=ldw)
     frac, exact = ulp_check(got, want)
     say(f"  within 1 ulp {frac:.6f}, identical {exact:.6f}")
     assert frac >= 0.9999
