@@ -140,8 +140,9 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
 /* ---------------------------------------------------------------- sketch */
 
 /* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a
- * grouped call) needs for bf16 D: XAt repacked as two bf16 planes (hi, lo)
- * of XAt^T, rank padded to 32 and tokens to 256.  0 for invalid sizes. */
+ * grouped call) needs for bf16 D: XAt repacked as two bf16 terms (hi, lo)
+ * in matrix-core operand order, ranks padded to 16 and tokens to 32
+ * (4 * ceil(r/16)*16 * ceil(T/32)*32 bytes).  0 for invalid sizes. */
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r);
 
 /* S [d x r] += D^T XAt for one microbatch (fp32 accumulate; G = D^T X is
@@ -150,9 +151,11 @@ LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r);
  * The caller zeroes S at the start of each update.  [paper] §2.1 (S = G A^T,
  * accumulated per microbatch in fp32), [rgc] "How it works" (C += D^T (X P)).
  * bf16 D runs on bf16 MFMA with XAt split into two bf16 terms (hi + lo), which
- * needs the workspace above (ignored for fp32 D, may be NULL then).  Each
- * element of S sums tokens in ascending 16-token steps, so results do not
- * depend on the launch shape or on grouping.
+ * needs the workspace above (ignored for fp32 D, may be NULL then).  The
+ * summation order is a function of T alone: the 32-token steps are cut into
+ * four contiguous slices, each slice is summed in ascending step order, the
+ * slice sums are combined as s0 + (s1 + (s2 + s3)) and added to S -- so a
+ * grouped call gives the same bits as single calls.
  * Errors: NULL pointers; T < 1, d < 1, r < 1, r > LOGRA_MAX_RANK, ldd < d;
  * alignment; S or the workspace overlapping an operand; workspace too small. */
 LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r,

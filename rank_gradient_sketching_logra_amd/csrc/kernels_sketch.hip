@@ -194,10 +194,16 @@ __global__ void project_f32_kernel(KeyArg key, int64_t T, int64_t k, int64_t r,
 
 // ---------------------------------------------------------- accumulate
 
-// Packed projected input: two bf16 planes (hi, lo) of XAt^T, [RP x TP] each,
-// zero-padded to whole 32-rank blocks and 256-token chunks, so one 16-byte
-// load is one MFMA B operand (8 consecutive tokens of one rank).
-constexpr int kTokPad = 256;
+// Packed projected input.  XAt is split into two bf16 terms, hi = RNE(x) and
+// lo = RNE(x - hi), laid out in MFMA B-operand order for
+// v_mfma_f32_16x16x32_bf16: for 32-token step s and 16-rank block b, two
+// 1 KiB operands (hi then lo) in which lane l holds tokens 32s + 8(l>>4) + i
+// (i = 0..7) of rank 16b + (l & 15).  One wave reads one operand with one
+// fully contiguous 16-byte-per-lane load.  Tokens >= T and ranks >= r are 0.
+constexpr int kAccStep = 32;       // tokens per MFMA step
+constexpr int kAccCols = 128;      // columns of D per block: 16 lanes x 8
+constexpr int kAccSlices = 4;      // token slices per block, one per wave
+constexpr int kAccGroupRB = 4;     // 16-rank blocks per rank group (64 ranks)
 
 struct AccGroupArgs {
   const void* D[kMaxGroup];
@@ -208,145 +214,272 @@ struct AccGroupArgs {
   int64_t ldd[kMaxGroup];
   int64_t tile_begin[kMaxGroup + 1];
   int n;
-  int64_t T, TP, r, RP;
+  int64_t T, r;
+  int nsteps;   // ceil(T / 32)
+  int nrb;      // 16-rank blocks packed: ceil(r / 16), rounded up to a
+                // multiple of 4 when there is more than one rank group
+  int ngroups;  // nrb / RB rank groups (RB = min(nrb, 4))
 };
 
-__global__ void acc_pack_kernel(AccGroupArgs g) {
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// One wave per (step, rank block) of one item.
+__global__ __launch_bounds__(256) void acc_pack_kernel(AccGroupArgs g) {
   const int item = blockIdx.y;
-  const int64_t ntg = g.TP >> 3;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= ntg * g.RP) return;
-  const int64_t tg = idx / g.RP;
-  const int64_t j = idx - tg * g.RP;
+  const int64_t chunk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (chunk >= (int64_t)g.nsteps * g.nrb) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t s = chunk / g.nrb;
+  const int64_t b = chunk - s * g.nrb;
+  const int64_t j = 16 * b + (lane & 15);
+  const int64_t t0 = kAccStep * s + 8 * (lane >> 4);
   const float* __restrict__ x = g.XAt[item];
-  uint32_t h[8], l[8];
+  float h[8], l[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t t = tg * 8 + i;
-    const float v = (t < g.T && j < g.r) ? x[t * g.r + j] : 0.f;
-    split_hi_lo(v, h[i], l[i]);
+    const float v = (t0 + i < g.T && j < g.r) ? x[(t0 + i) * g.r + j] : 0.f;
+    const __bf16 hb = (__bf16)v;
+    h[i] = (float)hb;
+    l[i] = v - h[i];
   }
-  uint16_t* hi = g.planes[item] + j * g.TP + tg * 8;
-  uint16_t* lo = hi + g.RP * g.TP;
   u32x4 vh, vl;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    vh[p] = h[2 * p] | (h[2 * p + 1] << 16);
-    vl[p] = l[2 * p] | (l[2 * p + 1] << 16);
+    vh[p] = pack_bf16x2(h[2 * p], h[2 * p + 1]);
+    vl[p] = pack_bf16x2(l[2 * p], l[2 * p + 1]);
   }
-  *reinterpret_cast<u32x4*>(hi) = vh;
-  *reinterpret_cast<u32x4*>(lo) = vl;
+  uint16_t* dst = g.planes[item] + chunk * 1024 + lane * 8;
+  *reinterpret_cast<u32x4*>(dst) = vh;
+  *reinterpret_cast<u32x4*>(dst + 512) = vl;
 }
 
-// bf16 D.  One block = MC = 32*WM columns of D (rows of S) x all ranks x all
-// tokens; waves form a WM x (4/WM) grid over (column block, rank blocks).
-// D is staged through LDS in row-major chunks of TC tokens (prefetched one
-// chunk ahead in registers); the MFMA A operand (8 tokens of one column) is
-// read from LDS as 16-bit values.  The B operand (8 tokens of one rank) is
-// one 16-byte load from the packed planes.  Each output element accumulates
-// over tokens in ascending 16-token steps, hi term then lo term, whatever
-// the tiling -- so single and grouped calls give identical bits.
-template <int WM, int NBW, int TC>
-__global__ __launch_bounds__(256) void acc_bf16_kernel(AccGroupArgs g) {
-  constexpr int WN = 4 / WM;
-  constexpr int MC = 32 * WM;
-  constexpr int PITCH = MC + 4;            // 16-bit elements per LDS row
-  constexpr int VPR = MC / 8;              // 16-byte vectors per chunk row
-  constexpr int NV = TC * VPR / 256;       // vectors per thread per chunk
-  static_assert(NV >= 1 && TC * VPR % 256 == 0, "chunk must split evenly");
-  __shared__ __align__(16) uint16_t Ds[TC * PITCH];
+// Eight bf16 of row t of D from column col; zero outside the matrix.
+__device__ __forceinline__ u32x4 load_drow(const uint16_t* __restrict__ D, int64_t ldd,
+                                           int64_t t, int64_t T, int64_t col, int64_t d,
+                                           bool full) {
+  if (t >= T) return u32x4{0u, 0u, 0u, 0u};
+  const uint16_t* p = D + t * ldd + col;
+  if (full) return *reinterpret_cast<const u32x4*>(p);
+  uint32_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = (col + i < d) ? p[i] : 0u;
+  return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+               e[6] | (e[7] << 16)};
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their
+// maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt lgkmcnt(0) with the other counters unconstrained.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Transpose a lane's 8 x 8 block of bf16 (row[i] = eight columns of token
+// i): a[e] = the eight tokens of column e, as one MFMA operand.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&row)[8], u32x4 (&a)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = e >> 1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t x0 = row[2 * p][q], x1 = row[2 * p + 1][q];
+      a[e][p] = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+    }
+  }
+}
+
+// acc[e][b] += A_e B_b over one 32-token step, hi term then lo term.
+template <int RB>
+__device__ __forceinline__ void acc_mfma_step(f32x4 (&acc)[8][RB], const u32x4 (&a)[8],
+                                              const u32x4 (&bh)[RB], const u32x4 (&bl)[RB]) {
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bh[b]),
+                                                          acc[e][b], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bl[b]),
+                                                          acc[e][b], 0, 0, 0);
+  }
+}
+
+// Direct global->LDS loads of one step into a wave's stage: eight 1 KiB row
+// loads (rows prow, prow + ldd, ...) and the 2 RB B operands at pb.  Lane
+// l's 16 bytes land at byte 16 l of each 1 KiB slab.
+template <int RB>
+__device__ __forceinline__ void acc_issue_step(u32x4 (*slabs)[64], const uint16_t* prow,
+                                               int64_t ldd, const uint16_t* pb) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(prow + i * ldd, &slabs[i][0], 16, 0, 0);
+#pragma unroll
+  for (int h = 0; h < 2 * RB; ++h)
+    __builtin_amdgcn_global_load_lds(pb + h * 512, &slabs[8 + h][0], 16, 0, 0);
+}
+
+// bf16 D.  A block owns 128 columns of D (rows of S) and one group of up to
+// 64 ranks; its four waves take four contiguous slices of the 32-token steps.
+// Lane l covers D rows 32s + 8(l>>4) + i (i = 0..7), columns c0 + 8(l&15) ..
+// +7 -- sixteen lanes cover 256 contiguous bytes of a row.  Each wave stages
+// one step at a time in a private 16 KiB LDS area filled by direct
+// global->LDS loads (eight 1 KiB row loads, lane l's 16 bytes at offset
+// 16 l, and the step's B operands, i.e. the packed XAt above).  A step is
+// read back into registers completely before the next step's loads are
+// issued, so the next step is in flight while this one computes, without
+// holding registers.  The lane's 8 x 8 block is transposed in registers:
+// for e = 0..7, operand A_e holds the eight tokens of column c0 + 8(l&15) +
+// e, which is MFMA row m = l & 15 of instance e; the B operand has the same
+// token for each (lane, element), so each 16x16x32 MFMA adds 32 tokens.
+// Instance e, rank block b gives C[m][n] = S[c0 + 8m + e][16b + n], lane l
+// holding m = 4(l>>4) + i, n = l & 15.  Each wave sums its slice in
+// ascending step order (hi term then lo term per step), the slices are
+// combined as w0 + (w1 + (w2 + w3)) through LDS and the total is added to S.
+// The slicing depends on T alone, so the result bits do not depend on
+// grouping.  A strip that reaches past column d of D, and the last step
+// when T is not a multiple of 32, take guarded loads instead.
+template <int RB>
+__global__ __launch_bounds__(256, 2) void acc_bf16_kernel(AccGroupArgs g) {
+  constexpr int kStage = 8 + 2 * RB;  // 1 KiB slabs per wave: rows, then B hi/lo
+  __shared__ __align__(16) u32x4 stage[4][kStage][64];  // 64 KiB at RB = 4
+  static_assert(sizeof(stage) >= sizeof(float) * RB * 32 * 64, "reduction fits in the stage");
+  float* red = reinterpret_cast<float*>(&stage[0][0][0]);
 
   const int64_t logical = xcd_logical_block();
   if (logical >= g.tile_begin[g.n]) return;
   int item = 0;
   while (logical >= g.tile_begin[item + 1]) ++item;
-  const int64_t c0 = (logical - g.tile_begin[item]) * MC;
+  const int64_t local = logical - g.tile_begin[item];
+  const int rg = (int)(local % g.ngroups);
+  const int64_t c0 = (local / g.ngroups) * kAccCols;
   const uint16_t* __restrict__ D = static_cast<const uint16_t*>(g.D[item]);
   const int64_t ldd = g.ldd[item];
   const int64_t d = g.d[item];
-  const uint16_t* __restrict__ planes = g.planes[item];
-  const int64_t T = g.T, TP = g.TP, RP = g.RP;
-  const int NBT = (int)(RP >> 5);
+  const int64_t T = g.T;
+  const int rb0 = rg * RB;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-  const int half = lane >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+  const int per = (g.nsteps + kAccSlices - 1) / kAccSlices;
+  const int s_begin = wave * per;
+  const int s_end = (s_begin + per) < g.nsteps ? (s_begin + per) : g.nsteps;
 
-  u32x4 pre[NV];
-  auto load_chunk = [&](int64_t tbase) {
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int v = tid + 256 * p;
-      const int row = v / VPR;
-      const int cv = v - row * VPR;
-      pre[p] = load_bf16x8(D, ldd, tbase + row, c0 + cv * 8, T, d);
-    }
-  };
+  const int64_t col = c0 + 8 * n;
+  const bool col_full = col + 8 <= d;
+  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb0 * 1024;
 
-  f32x16 acc[NBW];
+  f32x4 acc[8][RB];
 #pragma unroll
-  for (int q = 0; q < NBW; ++q)
+  for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
+    for (int b = 0; b < RB; ++b) acc[e][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t nch = (T + TC - 1) / TC;
-  load_chunk(0);
-  for (int64_t ch = 0; ch < nch; ++ch) {
-    __syncthreads();
+  // Steps whose 32 rows all lie inside D: [s_begin, s_full).
+  const int s_full = (int)((int64_t)s_end * kAccStep <= T ? s_end : T / kAccStep);
+  int s_rest = s_begin;
+  if (s_begin < s_full && c0 + kAccCols <= d) {
+    // Interior strip: every lane's 16 bytes lie inside a row of D.
+    const int64_t rstride = (int64_t)kAccStep * ldd;
+    const int64_t bstride = (int64_t)g.nrb * 1024;
+    const uint16_t* prow = D + ((int64_t)kAccStep * s_begin + 8 * grp) * ldd + col;
+    const uint16_t* pb = planes + (int64_t)s_begin * bstride + lane * 8;
+    acc_issue_step<RB>(stage[wave], prow, ldd, pb);
+    for (int s = s_begin; s < s_full; ++s) {
+      wait_vmcnt<0>();  // step s has landed in the stage
+      u32x4 row[8], a[8], bh[RB], bl[RB];
 #pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int v = tid + 256 * p;
-      const int row = v / VPR;
-      const int cv = v - row * VPR;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&Ds[row * PITCH + cv * 8]);
-      dst[0] = pre[p][0];
-      dst[1] = pre[p][1];
-      dst[2] = pre[p][2];
-      dst[3] = pre[p][3];
-    }
-    __syncthreads();
-    const int64_t tbase = ch * TC;
-    if (ch + 1 < nch) load_chunk(tbase + TC);
-
+      for (int i = 0; i < 8; ++i) row[i] = stage[wave][i][lane];
 #pragma unroll
-    for (int s = 0; s < TC / 16; ++s) {
-      u32x4 a;
-      const uint16_t* col = &Ds[(16 * s + 8 * half) * PITCH + 32 * wm + (lane & 31)];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        a[ii] = (uint32_t)col[(2 * ii) * PITCH] | ((uint32_t)col[(2 * ii + 1) * PITCH] << 16);
-#pragma unroll
-      for (int q = 0; q < NBW; ++q) {
-        const int nb = wn + WN * q;
-        if (nb < NBT) {
-          const uint16_t* ph =
-              planes + (int64_t)(nb * 32 + (lane & 31)) * TP + tbase + 16 * s + 8 * half;
-          const u32x4 bh = *reinterpret_cast<const u32x4*>(ph);
-          const u32x4 bl = *reinterpret_cast<const u32x4*>(ph + RP * TP);
-          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bh), acc[q],
-                                                           0, 0, 0);
-          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bl), acc[q],
-                                                           0, 0, 0);
-        }
+      for (int b = 0; b < RB; ++b) {
+        bh[b] = stage[wave][8 + 2 * b][lane];
+        bl[b] = stage[wave][9 + 2 * b][lane];
       }
+      wait_lgkmcnt0();  // the stage has been read; it may be refilled
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < s_full) {
+        prow += rstride;
+        pb += bstride;
+        acc_issue_step<RB>(stage[wave], prow, ldd, pb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      transpose8x8(row, a);
+      acc_mfma_step<RB>(acc, a, bh, bl);
+    }
+    s_rest = s_full;
+  }
+  if (s_rest < s_end) {
+    // Edge strips and the partial last step: guarded loads, no prefetch.
+    for (int s = s_rest; s < s_end; ++s) {
+      const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
+      u32x4 row[8], a[8], bh[RB], bl[RB];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) row[i] = load_drow(D, ldd, t0 + i, T, col, d, col_full);
+      const uint16_t* pb = planes + (int64_t)s * g.nrb * 1024 + lane * 8;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        bh[b] = *reinterpret_cast<const u32x4*>(pb + 1024 * b);
+        bl[b] = *reinterpret_cast<const u32x4*>(pb + 1024 * b + 512);
+      }
+      transpose8x8(row, a);
+      acc_mfma_step<RB>(acc, a, bh, bl);
     }
   }
+  __syncthreads();  // every wave is done with its stage
 
-  float* __restrict__ S = g.S[item];
-  const int64_t r = g.r;
+  // Fixed-order combination of the four slices, w0 + (w1 + (w2 + w3)), in
+  // the accumulator layout (element (e, b, i) of lane l at [(e RB + b) 4 + i][l]).
+  for (int w = kAccSlices - 1; w >= 1; --w) {
+    if (wave == w) {
 #pragma unroll
-  for (int q = 0; q < NBW; ++q) {
-    const int nb = wn + WN * q;
-    if (nb >= NBT) continue;
-    const int64_t j = nb * 32 + (lane & 31);
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int reg = 0; reg < 16; ++reg) {
-      const int64_t c = c0 + 32 * wm + 8 * (reg >> 2) + 4 * half + (reg & 3);
-      if (c < d && j < r) S[c * r + j] += acc[q][reg];
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* p = &red[((e * RB + b) * 4 + i) * 64 + lane];
+            *p = (w == kAccSlices - 1) ? acc[e][b][i] : acc[e][b][i] + *p;
+          }
     }
+    __syncthreads();
+  }
+  // Wave 0 forms the total and stores it as a row-major tile [c][j] in the
+  // second half of the stage.
+  constexpr int TJ = 16 * RB;               // ranks per tile row
+  constexpr int PER = kAccCols * TJ / 256;  // tile elements per thread
+  float* tile = red + RB * 32 * 64;
+  static_assert(sizeof(stage) >= 2 * sizeof(float) * RB * 32 * 64, "tile fits in the stage");
+  if (wave == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cl = 8 * (4 * grp + i) + e;
+          tile[cl * TJ + 16 * b + n] = acc[e][b][i] + red[((e * RB + b) * 4 + i) * 64 + lane];
+        }
+  }
+  __syncthreads();
+  // S += tile over the block's rows c0 .. c0 + 127 and ranks 16 rb0 ..
+  // + 16 RB, consecutive threads on consecutive ranks of a row.
+  const int64_t r = g.r;
+  float* __restrict__ S = g.S[item];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    const int64_t c = c0 + idx / TJ;
+    const int64_t j = 16 * rb0 + idx % TJ;
+    if (c < d && j < r) S[c * r + j] += tile[idx];
   }
 }
 
@@ -370,8 +503,11 @@ __global__ void acc_f32_kernel(AccGroupArgs g) {
 
 // ------------------------------------------------------------ launchers
 
-int64_t acc_rank_pad(int64_t r) { return (r + 31) / 32 * 32; }
-int64_t acc_token_pad(int64_t T) { return (T + kTokPad - 1) / kTokPad * kTokPad; }
+int64_t acc_rank_pad(int64_t r) {
+  const int64_t nrb = (r + 15) / 16;
+  return 16 * (nrb <= kAccGroupRB ? nrb : (nrb + kAccGroupRB - 1) / kAccGroupRB * kAccGroupRB);
+}
+int64_t acc_token_pad(int64_t T) { return (T + kAccStep - 1) / kAccStep * kAccStep; }
 size_t acc_ws_bytes_per_item(int64_t T, int64_t r) {
   return (size_t)(2 * acc_rank_pad(r) * acc_token_pad(T) * sizeof(uint16_t));
 }
@@ -425,8 +561,10 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   g.n = n;
   g.T = T;
   g.r = r;
-  g.TP = acc_token_pad(T);
-  g.RP = acc_rank_pad(r);
+  g.nsteps = (int)(acc_token_pad(T) / kAccStep);
+  g.nrb = (int)(acc_rank_pad(r) / 16);
+  const int rb = g.nrb < kAccGroupRB ? g.nrb : kAccGroupRB;
+  g.ngroups = g.nrb / rb;
   for (int i = 0; i < n; ++i) {
     g.D[i] = items[i].D;
     g.XAt[i] = items[i].XAt;
@@ -442,40 +580,24 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
                        dim3(256), 0, s, g);
     return hipGetLastError();
   }
-  // Pack XAt into hi/lo planes.
   {
-    const int64_t m = (g.TP / 8) * g.RP;
-    hipLaunchKernelGGL(acc_pack_kernel, dim3((unsigned)((m + 255) / 256), (unsigned)n),
+    const int64_t chunks = (int64_t)g.nsteps * g.nrb;
+    hipLaunchKernelGGL(acc_pack_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)n),
                        dim3(256), 0, s, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nbt = (int)(g.RP / 32);
-  const int wm = (nbt == 1) ? 4 : 2;
-  const int mc = 32 * wm;
   g.tile_begin[0] = 0;
-  for (int i = 0; i < n; ++i) g.tile_begin[i + 1] = g.tile_begin[i] + (g.d[i] + mc - 1) / mc;
+  for (int i = 0; i < n; ++i)
+    g.tile_begin[i + 1] = g.tile_begin[i] + (g.d[i] + kAccCols - 1) / kAccCols * g.ngroups;
   const int64_t tiles = g.tile_begin[n];
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  if (nbt == 1) {
-    hipLaunchKernelGGL((acc_bf16_kernel<4, 1, 128>), grid, dim3(256), 0, s, g);
-  } else {
-    switch ((nbt + 1) / 2) {
-      case 1:
-        hipLaunchKernelGGL((acc_bf16_kernel<2, 1, 128>), grid, dim3(256), 0, s, g);
-        break;
-      case 2:
-        hipLaunchKernelGGL((acc_bf16_kernel<2, 2, 128>), grid, dim3(256), 0, s, g);
-        break;
-      case 3:
-        hipLaunchKernelGGL((acc_bf16_kernel<2, 3, 64>), grid, dim3(256), 0, s, g);
-        break;
-      case 4:
-        hipLaunchKernelGGL((acc_bf16_kernel<2, 4, 64>), grid, dim3(256), 0, s, g);
-        break;
-      default:
-        return hipErrorInvalidValue;
-    }
+  switch (rb) {
+    case 1: hipLaunchKernelGGL(acc_bf16_kernel<1>, grid, dim3(256), 0, s, g); break;
+    case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(256), 0, s, g); break;
+    case 3: hipLaunchKernelGGL(acc_bf16_kernel<3>, grid, dim3(256), 0, s, g); break;
+    case 4: hipLaunchKernelGGL(acc_bf16_kernel<4>, grid, dim3(256), 0, s, g); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -43,7 +43,7 @@ def test_version_and_sizes(lib):
     assert B.sketch_bytes(4096, 64) == 1 << 20          # 1 MiB, paper §2.2
     assert lib.logra_sketch_bytes(-1, 3) == -1
     assert B.accumulate_ws_bytes(4096, 64) == 2 * 64 * 4096 * 2
-    assert B.accumulate_ws_bytes(1000, 33) == 2 * 64 * 1024 * 2
+    assert B.accumulate_ws_bytes(1000, 33) == 2 * 48 * 1024 * 2
     assert B.accumulate_ws_bytes(0, 8) == 0
     assert B.rowadam_ws_bytes(0) == 0
     assert B.predicted_kl_q_ws_bytes(64, 152064) > 0
