@@ -128,7 +128,6 @@ def main():
     V = {(l, kind): torch.zeros((d,), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
     maxd = max(d for (_, _, _, d, _) in mats)
-    acc_ws = B.workspace(7 * B.accumulate_ws_bytes(T, r), dev)
     ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
     P, Vv = (w.P or 64), (w.V or 152064)
     z = randn((P, Vv), 4.0)
@@ -141,6 +140,7 @@ def main():
     by_layer = {}
     for (l, kind, mid, d, k) in mats:
         by_layer.setdefault(l, []).append((kind, d, k))
+    acc_ws = B.workspace(B.accumulate_grouped_ws_bytes(T, [d for (_, d, _) in by_layer[0]], r), dev)
     acc_total = sum(acc_bytes(T, d, r) for (_, _, _, d, _) in mats) * M
     merge_total = sum(merge_bytes(d, k, r) for (_, _, _, d, k) in mats)
     proj_total = sum(project_bytes(T, k, r) for (_, _, _, d, k) in mats) * M

@@ -140,10 +140,11 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
 /* ---------------------------------------------------------------- sketch */
 
 /* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a
- * grouped call) needs for bf16 D: XAt repacked as two bf16 terms (hi, lo)
- * in matrix-core operand order, ranks padded to 16 and tokens to 32
- * (4 * ceil(r/16)*16 * ceil(T/32)*32 bytes).  0 for invalid sizes. */
-LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r);
+ * grouped call) needs for bf16 D: XAt repacked as two bf16 terms (hi, lo) in
+ * matrix-core operand order, ranks padded to 16 (to 64 when r > 64) and
+ * tokens to 32.  d is accepted for future layouts and does not change the
+ * size today.  A multiple of 256 bytes; 0 for invalid sizes. */
+LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r);
 
 /* S [d x r] += D^T XAt for one microbatch (fp32 accumulate; G = D^T X is
  * never formed).  D [T x d] is bf16 or fp32 with leading dimension ldd >= d;
@@ -152,10 +153,11 @@ LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r);
  * accumulated per microbatch in fp32), [rgc] "How it works" (C += D^T (X P)).
  * bf16 D runs on bf16 MFMA with XAt split into two bf16 terms (hi + lo), which
  * needs the workspace above (ignored for fp32 D, may be NULL then).  The
- * summation order is a function of T alone: the 32-token steps are cut into
- * four contiguous slices, each slice is summed in ascending step order, the
- * slice sums are combined as s0 + (s1 + (s2 + s3)) and added to S -- so a
- * grouped call gives the same bits as single calls.
+ * summation order is a function of T alone: the 32-token steps are split
+ * into halves at h = ceil(ceil(T / 32) / 2); each half sums its steps in
+ * ascending order (hi term, then lo term, per step) and S receives
+ * S + (first half + second half) -- so a grouped call gives the same bits
+ * as single calls.
  * Errors: NULL pointers; T < 1, d < 1, r < 1, r > LOGRA_MAX_RANK, ldd < d;
  * alignment; S or the workspace overlapping an operand; workspace too small. */
 LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r,
@@ -178,8 +180,8 @@ typedef struct logra_acc_desc {
  * dtype of D, in one launch (e.g. the seven projections of one layer for one
  * microbatch).  Same result bits as n separate logra_sketch_accumulate calls.
  * The descriptor array is read on the host during the call.  For bf16 D the
- * workspace holds n consecutive per-descriptor workspaces of
- * logra_sketch_accumulate_ws_bytes(T, r) bytes each.
+ * workspace holds n consecutive per-descriptor workspaces, descriptor i's of
+ * logra_sketch_accumulate_ws_bytes(T, descs[i].d, r) bytes, in order.
  * Errors: as logra_sketch_accumulate for each descriptor; n < 1 or
  * n > LOGRA_MAX_GROUP; two descriptors writing overlapping S. */
 LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype d_dtype,

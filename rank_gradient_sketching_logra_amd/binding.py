@@ -38,7 +38,7 @@ SIGNATURES = {
     "logra_regen_A": (c_int, [POINTER(Key), c_int64, c_int64, c_int, c_void_p, c_void_p]),
     "logra_project_input": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
                                     c_int64, c_void_p, c_void_p]),
-    "logra_sketch_accumulate_ws_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_sketch_accumulate_ws_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
     "logra_sketch_accumulate": (c_int, [c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_sketch_accumulate_grouped": (c_int, [c_int64, c_int64, c_int, POINTER(AccDesc), c_int,
@@ -139,8 +139,13 @@ def project_input(k_: Key, X: torch.Tensor, r: int, out=None, stream=None):
     return XAt
 
 
-def accumulate_ws_bytes(T: int, r: int) -> int:
-    return lib().logra_sketch_accumulate_ws_bytes(T, r)
+def accumulate_ws_bytes(T: int, d: int, r: int) -> int:
+    return lib().logra_sketch_accumulate_ws_bytes(T, d, r)
+
+
+def accumulate_grouped_ws_bytes(T: int, ds, r: int) -> int:
+    """Workspace of a grouped call: the per-descriptor workspaces, in order."""
+    return sum(accumulate_ws_bytes(T, d, r) for d in ds)
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -152,7 +157,7 @@ def sketch_accumulate(D: torch.Tensor, XAt: torch.Tensor, S: torch.Tensor, ws=No
     T, d = D.shape
     r = S.shape[1]
     if ws is None:
-        ws = workspace(accumulate_ws_bytes(T, r), D.device)
+        ws = workspace(accumulate_ws_bytes(T, d, r), D.device)
     _check(lib().logra_sketch_accumulate(T, d, r, _ptr(D), _dtype_code(D), _ld(D), _ptr(XAt),
                                          _ptr(S), _ptr(ws), ws.numel(), _stream(D, stream)))
     return S
@@ -167,7 +172,8 @@ def sketch_accumulate_grouped(items, ws=None, stream=None):
     for i, (D, XAt, S) in enumerate(items):
         descs[i] = AccDesc(D.data_ptr(), XAt.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
     if ws is None:
-        ws = workspace(n * accumulate_ws_bytes(T, r), items[0][0].device)
+        ws = workspace(accumulate_grouped_ws_bytes(T, [D.shape[1] for (D, _, _) in items], r),
+                       items[0][0].device)
     _check(lib().logra_sketch_accumulate_grouped(T, r, _dtype_code(items[0][0]), descs, n, _ptr(ws),
                                                  ws.numel(), _stream(items[0][0], stream)))
 

@@ -21,13 +21,14 @@ struct AccItem {
   float* S;
   int64_t d;
   int64_t ldd;
-  void* ws;        // packed projected input of this item
+  void* ws;        // workspace of this item: packed projected input
 };
 
-// Rank padded to whole 32-wide MFMA blocks and tokens padded to whole chunks.
+// Rank padded to whole 16-rank blocks (64 when r > 64), tokens to 32-token
+// steps; workspace of one accumulate item (a multiple of 256 bytes).
 int64_t acc_rank_pad(int64_t r);
 int64_t acc_token_pad(int64_t T);
-size_t acc_ws_bytes_per_item(int64_t T, int64_t r);
+size_t acc_ws_bytes_per_item(int64_t T, int64_t d, int64_t r);
 
 hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void* A,
                           hipStream_t s);

@@ -200,25 +200,29 @@ __global__ void project_f32_kernel(KeyArg key, int64_t T, int64_t k, int64_t r,
 // 1 KiB operands (hi then lo) in which lane l holds tokens 32s + 8(l>>4) + i
 // (i = 0..7) of rank 16b + (l & 15).  One wave reads one operand with one
 // fully contiguous 16-byte-per-lane load.  Tokens >= T and ranks >= r are 0.
-constexpr int kAccStep = 32;       // tokens per MFMA step
-constexpr int kAccCols = 128;      // columns of D per block: 16 lanes x 8
-constexpr int kAccSlices = 4;      // token slices per block, one per wave
-constexpr int kAccGroupRB = 4;     // 16-rank blocks per rank group (64 ranks)
+constexpr int kAccStep = 32;        // tokens per MFMA step
+constexpr int kAccCols = 128;       // columns of D per wave: 16 lanes x 8
+constexpr int kAccWaves = 4;        // waves per block: 2 strips x 2 token halves
+constexpr int kAccBlockCols = 2 * kAccCols;
+constexpr int kAccGroupRB = 4;      // 16-rank blocks per rank group (64 ranks)
+constexpr int kAccRing = 3;         // steps in flight per block (LDS ring depth)
 
 struct AccGroupArgs {
   const void* D[kMaxGroup];
   const float* XAt[kMaxGroup];
   float* S[kMaxGroup];
-  uint16_t* planes[kMaxGroup];
+  uint16_t* planes[kMaxGroup];  // packed XAt of each item (workspace)
   int64_t d[kMaxGroup];
   int64_t ldd[kMaxGroup];
+  int64_t nq[kMaxGroup];        // 256-column blocks of each item
   int64_t tile_begin[kMaxGroup + 1];
   int n;
   int64_t T, r;
   int nsteps;   // ceil(T / 32)
   int nrb;      // 16-rank blocks packed: ceil(r / 16), rounded up to a
                 // multiple of 4 when there is more than one rank group
-  int ngroups;  // nrb / RB rank groups (RB = min(nrb, 4))
+  int rb;       // 16-rank blocks per rank group: min(nrb, 4)
+  int ngroups;  // nrb / rb rank groups
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -312,54 +316,166 @@ __device__ __forceinline__ void acc_mfma_step(f32x4 (&acc)[8][RB], const u32x4 (
   }
 }
 
-// Direct global->LDS loads of one step into a wave's stage: eight 1 KiB row
-// loads (rows prow, prow + ldd, ...) and the 2 RB B operands at pb.  Lane
-// l's 16 bytes land at byte 16 l of each 1 KiB slab.
+// 32-bit LDS address of a shared-memory object.
+template <typename Tp>
+__device__ __forceinline__ uint32_t lds_addr(Tp* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) Tp*)p;
+}
+
+// LDS reads of consecutive 1 KiB slabs (lane l's 16 bytes at byte 16 l of
+// each) that complete inside the statement: the compiler never sees an LDS
+// read it could order against pending direct global->LDS loads, and the
+// results exist only once the data has arrived.  The outputs are
+// early-clobber: a destination sharing a register with the address would be
+// overwritten by the first read's data while later reads still use it.
+__device__ __forceinline__ void lds_read8(uint32_t a, u32x4 (&r)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(a)
+      : "memory");
+}
+__device__ __forceinline__ void lds_read2(uint32_t a, u32x4& x, u32x4& y) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y)
+      : "v"(a)
+      : "memory");
+}
+// Workgroup barrier with no memory fence.  The ring's ordering is explicit:
+// loads into LDS are waited for by count before it, and every LDS read has
+// completed inside its own statement, so the fence __syncthreads() adds
+// (which waits for every outstanding global load) is not needed.  The empty
+// statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Rows (8 slabs at ad) and B operands (2 RB slabs at ab: hi, lo per rank
+// block) of one step.
 template <int RB>
-__device__ __forceinline__ void acc_issue_step(u32x4 (*slabs)[64], const uint16_t* prow,
-                                               int64_t ldd, const uint16_t* pb) {
+__device__ __forceinline__ void acc_read_step(uint32_t ad, uint32_t ab, u32x4 (&row)[8],
+                                              u32x4 (&bh)[RB], u32x4 (&bl)[RB]) {
+  if constexpr (RB == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:1024\n\t"
+        "ds_read_b128 %2, %16 offset:2048\n\t"
+        "ds_read_b128 %3, %16 offset:3072\n\t"
+        "ds_read_b128 %4, %16 offset:4096\n\t"
+        "ds_read_b128 %5, %16 offset:5120\n\t"
+        "ds_read_b128 %6, %16 offset:6144\n\t"
+        "ds_read_b128 %7, %16 offset:7168\n\t"
+        "ds_read_b128 %8, %17\n\t"
+        "ds_read_b128 %9, %17 offset:1024\n\t"
+        "ds_read_b128 %10, %17 offset:2048\n\t"
+        "ds_read_b128 %11, %17 offset:3072\n\t"
+        "ds_read_b128 %12, %17 offset:4096\n\t"
+        "ds_read_b128 %13, %17 offset:5120\n\t"
+        "ds_read_b128 %14, %17 offset:6144\n\t"
+        "ds_read_b128 %15, %17 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(row[0]), "=&v"(row[1]), "=&v"(row[2]), "=&v"(row[3]), "=&v"(row[4]), "=&v"(row[5]),
+          "=&v"(row[6]), "=&v"(row[7]), "=&v"(bh[0]), "=&v"(bl[0]), "=&v"(bh[1]), "=&v"(bl[1]),
+          "=&v"(bh[2]), "=&v"(bl[2]), "=&v"(bh[3]), "=&v"(bl[3])
+        : "v"(ad), "v"(ab)
+        : "memory");
+  } else {
+    lds_read8(ad, row);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) lds_read2(ab + 2048 * b, bh[b], bl[b]);
+  }
+}
+
+// acc[e][b] += A_e B_b over one 32-token step for rank block b only.
+template <int RB>
+__device__ __forceinline__ void acc_mfma_rb(f32x4 (&acc)[8][RB], const u32x4 (&a)[8], int b,
+                                            u32x4 bh, u32x4 bl) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bh),
+                                                        acc[e][b], 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bl),
+                                                        acc[e][b], 0, 0, 0);
+}
+
+// Direct global->LDS loads of a wave's eight 1 KiB row slabs of one step:
+// rows prow, prow + ldd, ...; lane l's 16 bytes land at byte 16 l.
+__device__ __forceinline__ void acc_issue_rows(u32x4 (*slabs)[64], const uint16_t* prow,
+                                               int64_t ldd) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_global_load_lds(prow + i * ldd, &slabs[i][0], 16, 0, 0);
-#pragma unroll
-  for (int h = 0; h < 2 * RB; ++h)
-    __builtin_amdgcn_global_load_lds(pb + h * 512, &slabs[8 + h][0], 16, 0, 0);
 }
 
-// bf16 D.  A block owns 128 columns of D (rows of S) and one group of up to
-// 64 ranks; its four waves take four contiguous slices of the 32-token steps.
-// Lane l covers D rows 32s + 8(l>>4) + i (i = 0..7), columns c0 + 8(l&15) ..
-// +7 -- sixteen lanes cover 256 contiguous bytes of a row.  Each wave stages
-// one step at a time in a private 16 KiB LDS area filled by direct
-// global->LDS loads (eight 1 KiB row loads, lane l's 16 bytes at offset
-// 16 l, and the step's B operands, i.e. the packed XAt above).  A step is
-// read back into registers completely before the next step's loads are
-// issued, so the next step is in flight while this one computes, without
-// holding registers.  The lane's 8 x 8 block is transposed in registers:
-// for e = 0..7, operand A_e holds the eight tokens of column c0 + 8(l&15) +
-// e, which is MFMA row m = l & 15 of instance e; the B operand has the same
+// Direct global->LDS load of row slab i (row pointer prow) of a wave.
+__device__ __forceinline__ void acc_issue_rows_one(u32x4 (*slabs)[64], int i,
+                                                   const uint16_t* prow) {
+  __builtin_amdgcn_global_load_lds(prow, &slabs[i][0], 16, 0, 0);
+}
+
+// Direct global->LDS loads of one wave's share of a half's B operands for
+// one step: the 1 KiB operands j = strip, strip + 2, ... of the 2 RB at pb.
+template <int RB>
+__device__ __forceinline__ void acc_issue_b(u32x4 (*bs)[64], const uint16_t* pb, int strip) {
+#pragma unroll
+  for (int j0 = 0; j0 < 2 * RB; j0 += 2)
+    __builtin_amdgcn_global_load_lds(pb + (j0 + strip) * 512, &bs[j0 + strip][0], 16, 0, 0);
+}
+
+// bf16 D.  A block covers 256 columns of D (rows of S) and one group of up
+// to 64 ranks over all T tokens.  Its four waves are two 128-column strips
+// times two token halves: wave w takes the strip of columns
+// c0 = 256 q + 128 (w & 1) onwards and, for w >> 1 = 0 (1), the steps
+// [0, h) ([h, nsteps)) with h = ceil(nsteps / 2).  Lane l covers D rows
+// 32s + 8(l>>4) + i (i = 0..7), columns c0 + 8(l&15) .. +7, so sixteen lanes
+// read 256 contiguous bytes of a row.  A three-step ring in LDS is filled by
+// direct global->LDS loads: every wave streams its own rows, and each half's
+// B operands (the packed XAt above) are loaded once per step by that half's
+// two waves and shared by both strips.  Two steps are in flight while a
+// third computes.  The lane's 8 x 8 block is transposed in registers: for
+// e = 0..7, operand A_e holds the eight tokens of column c0 + 8(l&15) + e,
+// which is MFMA row m = l & 15 of instance e; the B operand has the same
 // token for each (lane, element), so each 16x16x32 MFMA adds 32 tokens.
 // Instance e, rank block b gives C[m][n] = S[c0 + 8m + e][16b + n], lane l
-// holding m = 4(l>>4) + i, n = l & 15.  Each wave sums its slice in
-// ascending step order (hi term then lo term per step), the slices are
-// combined as w0 + (w1 + (w2 + w3)) through LDS and the total is added to S.
-// The slicing depends on T alone, so the result bits do not depend on
-// grouping.  A strip that reaches past column d of D, and the last step
-// when T is not a multiple of 32, take guarded loads instead.
+// holding m = 4(l>>4) + i, n = l & 15.  Each wave sums its half's steps in
+// ascending order (hi term then lo term per step); the second half's sum R
+// passes through LDS to the first half's wave, which forms L + R, and the
+// block adds that to S through an LDS tile so that S is read and written
+// in whole rows.  The order depends on T alone, so grouped and single calls
+// give the same bits.  Strips that reach past column d take guarded loads;
+// rows past T (last step only) are loaded from row T - 1 and zeroed.
 template <int RB>
-__global__ __launch_bounds__(256, 2) void acc_bf16_kernel(AccGroupArgs g) {
-  constexpr int kStage = 8 + 2 * RB;  // 1 KiB slabs per wave: rows, then B hi/lo
-  __shared__ __align__(16) u32x4 stage[4][kStage][64];  // 64 KiB at RB = 4
-  static_assert(sizeof(stage) >= sizeof(float) * RB * 32 * 64, "reduction fits in the stage");
-  float* red = reinterpret_cast<float*>(&stage[0][0][0]);
+__global__ __launch_bounds__(256, 1) void acc_bf16_kernel(AccGroupArgs g) {
+  constexpr int R = kAccRing;
+  constexpr int NB = 2 * RB;                  // B operands per step and half
+  constexpr int kRing = R * kAccWaves * 8;    // 1 KiB row slabs
+  __shared__ __align__(16) u32x4 smem[(kRing + R * 2 * NB) * 64];  // 144 KiB at RB = 4
+  u32x4 (*dring)[kAccWaves][8][64] = reinterpret_cast<u32x4 (*)[kAccWaves][8][64]>(smem);
+  u32x4 (*bring)[2][NB][64] = reinterpret_cast<u32x4 (*)[2][NB][64]>(smem + kRing * 64);
 
   const int64_t logical = xcd_logical_block();
   if (logical >= g.tile_begin[g.n]) return;
   int item = 0;
   while (logical >= g.tile_begin[item + 1]) ++item;
   const int64_t local = logical - g.tile_begin[item];
-  const int rg = (int)(local % g.ngroups);
-  const int64_t c0 = (local / g.ngroups) * kAccCols;
+  const int rg = (int)(local % g.ngroups);  // rank groups of a column block are adjacent
+  const int64_t q = local / g.ngroups;
   const uint16_t* __restrict__ D = static_cast<const uint16_t*>(g.D[item]);
   const int64_t ldd = g.ldd[item];
   const int64_t d = g.d[item];
@@ -368,15 +484,22 @@ __global__ __launch_bounds__(256, 2) void acc_bf16_kernel(AccGroupArgs g) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int strip = wave & 1;
+  const int half = wave >> 1;
   const int n = lane & 15;
   const int grp = lane >> 4;
-  const int per = (g.nsteps + kAccSlices - 1) / kAccSlices;
-  const int s_begin = wave * per;
-  const int s_end = (s_begin + per) < g.nsteps ? (s_begin + per) : g.nsteps;
+  const int nsteps = g.nsteps;
+  const int h = (nsteps + 1) >> 1;
+  const int s_begin = half ? h : 0;
+  const int s_end = half ? nsteps : h;
 
+  const int64_t c0 = q * kAccBlockCols + kAccCols * strip;  // this wave's strip
   const int64_t col = c0 + 8 * n;
+  const bool active = c0 < d;                  // uniform per wave
+  const bool interior = c0 + kAccCols <= d;    // uniform per wave
   const bool col_full = col + 8 <= d;
-  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb0 * 1024;
+  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb0 * 1024 + lane * 8;
+  const int64_t bstride = (int64_t)g.nrb * 1024;
 
   f32x4 acc[8][RB];
 #pragma unroll
@@ -384,102 +507,142 @@ __global__ __launch_bounds__(256, 2) void acc_bf16_kernel(AccGroupArgs g) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[e][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Steps whose 32 rows all lie inside D: [s_begin, s_full).
-  const int s_full = (int)((int64_t)s_end * kAccStep <= T ? s_end : T / kAccStep);
-  int s_rest = s_begin;
-  if (s_begin < s_full && c0 + kAccCols <= d) {
-    // Interior strip: every lane's 16 bytes lie inside a row of D.
-    const int64_t rstride = (int64_t)kAccStep * ldd;
-    const int64_t bstride = (int64_t)g.nrb * 1024;
-    const uint16_t* prow = D + ((int64_t)kAccStep * s_begin + 8 * grp) * ldd + col;
-    const uint16_t* pb = planes + (int64_t)s_begin * bstride + lane * 8;
-    acc_issue_step<RB>(stage[wave], prow, ldd, pb);
-    for (int s = s_begin; s < s_full; ++s) {
-      wait_vmcnt<0>();  // step s has landed in the stage
-      u32x4 row[8], a[8], bh[RB], bl[RB];
+  // Loads of iteration k (step s_begin + k) into ring slot k % R: this
+  // wave's share of its half's B operands and, for an interior strip, its
+  // eight row slabs.  Iterations past the half re-read its last step
+  // (already cached) so that every iteration issues the same number of
+  // loads; rows past T read row T - 1.
+  auto issue = [&](int k, bool rows) {
+    const int st = s_begin + k;
+    const int sc = st < s_end ? st : s_end - 1;
+    const int slot = k % R;
+    acc_issue_b<RB>(bring[slot][half], planes + (int64_t)sc * bstride, strip);
+    if (!rows) return;
+    const int64_t t0 = (int64_t)kAccStep * sc + 8 * grp;
+    if ((int64_t)kAccStep * (sc + 1) <= T) {
+      acc_issue_rows(dring[slot][wave], D + t0 * ldd + col, ldd);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) row[i] = stage[wave][i][lane];
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        bh[b] = stage[wave][8 + 2 * b][lane];
-        bl[b] = stage[wave][9 + 2 * b][lane];
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = t0 + i < T ? t0 + i : T - 1;
+        acc_issue_rows_one(dring[slot][wave], i, D + t * ldd + col);
       }
-      wait_lgkmcnt0();  // the stage has been read; it may be refilled
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < s_full) {
-        prow += rstride;
-        pb += bstride;
-        acc_issue_step<RB>(stage[wave], prow, ldd, pb);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      transpose8x8(row, a);
-      acc_mfma_step<RB>(acc, a, bh, bl);
     }
-    s_rest = s_full;
-  }
-  if (s_rest < s_end) {
-    // Edge strips and the partial last step: guarded loads, no prefetch.
-    for (int s = s_rest; s < s_end; ++s) {
-      const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
-      u32x4 row[8], a[8], bh[RB], bl[RB];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) row[i] = load_drow(D, ldd, t0 + i, T, col, d, col_full);
-      const uint16_t* pb = planes + (int64_t)s * g.nrb * 1024 + lane * 8;
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        bh[b] = *reinterpret_cast<const u32x4*>(pb + 1024 * b);
-        bl[b] = *reinterpret_cast<const u32x4*>(pb + 1024 * b + 512);
-      }
-      transpose8x8(row, a);
-      acc_mfma_step<RB>(acc, a, bh, bl);
-    }
-  }
-  __syncthreads();  // every wave is done with its stage
+  };
 
-  // Fixed-order combination of the four slices, w0 + (w1 + (w2 + w3)), in
-  // the accumulator layout (element (e, b, i) of lane l at [(e RB + b) 4 + i][l]).
-  for (int w = kAccSlices - 1; w >= 1; --w) {
-    if (wave == w) {
+  if (interior) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+    for (int k = 0; k < R - 1; ++k) issue(k, true);
+    for (int k = 0; k < h; ++k) {
+      // Iteration k has landed once only the loads of iteration k + 1 (eight
+      // row slabs and RB B operands) remain.
+      static_assert(R == 3, "the wait count assumes a three-step ring");
+      wait_vmcnt<8 + RB>();
+      ring_barrier();  // both waves' shares of the half's B operands have landed
+      const int slot = k % R;
+      const int s = s_begin + k;
+      u32x4 row[8], a[8], bh[RB], bl[RB];
+      acc_read_step<RB>(lds_addr(&dring[slot][wave][0][lane]),
+                        lds_addr(&bring[slot][half][0][lane]), row, bh, bl);
+      if ((int64_t)kAccStep * (s + 1) > T) {
+        const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* p = &red[((e * RB + b) * 4 + i) * 64 + lane];
-            *p = (w == kAccSlices - 1) ? acc[e][b][i] : acc[e][b][i] + *p;
-          }
+        for (int i = 0; i < 8; ++i)
+          if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      // Refill the slot every wave finished reading before this barrier.
+      issue(k + R - 1, true);
+      if (s < s_end) {
+        transpose8x8(row, a);
+        acc_mfma_step<RB>(acc, a, bh, bl);
+      }
     }
-    __syncthreads();
+  } else {
+    // Edge or empty strip: the same barriers and B shares; rows by guarded
+    // loads when the strip starts inside D.
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) issue(k, false);
+    for (int k = 0; k < h; ++k) {
+      wait_vmcnt<0>();
+      ring_barrier();
+      const int slot = k % R;
+      const int s = s_begin + k;
+      if (active && s < s_end) {
+        const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
+        u32x4 row[8], a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) row[i] = load_drow(D, ldd, t0 + i, T, col, d, col_full);
+        transpose8x8(row, a);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          u32x4 bh, bl;
+          lds_read2(lds_addr(&bring[slot][half][2 * b][lane]), bh, bl);
+          acc_mfma_rb<RB>(acc, a, b, bh, bl);
+        }
+      }
+      issue(k + R - 1, false);
+    }
   }
-  // Wave 0 forms the total and stores it as a row-major tile [c][j] in the
-  // second half of the stage.
-  constexpr int TJ = 16 * RB;               // ranks per tile row
-  constexpr int PER = kAccCols * TJ / 256;  // tile elements per thread
-  float* tile = red + RB * 32 * 64;
-  static_assert(sizeof(stage) >= 2 * sizeof(float) * RB * 32 * 64, "tile fits in the stage");
-  if (wave == 0) {
+  wait_vmcnt<0>();  // no load may still target LDS past this point
+
+  // This thread's share of the block's S tile (256 rows x 16 RB ranks): rank
+  // j0 + lane of rows row0 + wave + 4k, so a wave reads whole row segments.
+  // The loads are issued now and complete while L + R is formed.
+  constexpr int TJ = 16 * RB;
+  constexpr int kRowsPerThread = kAccBlockCols / kAccWaves;
+  float* __restrict__ S = g.S[item];
+  const int64_t r = g.r;
+  const int64_t row0 = q * kAccBlockCols + wave;
+  const int64_t j = 16 * (int64_t)rb0 + lane;
+  const bool jok = lane < TJ && j < r;
+  int64_t rstride = 4 * r;
+  const int64_t jc = j < r ? j : r - 1;  // in-bounds address for idle lanes
+  float sv[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int64_t row = row0 + 4 * k < d ? row0 + 4 * k : d - 1;
+    sv[k] = S[row * r + jc];
+  }
+  // Keep the addresses from being held live across the exchange below.
+  asm volatile("" : "+s"(rstride));
+  ring_barrier();  // every wave is done with the ring
+
+  // R of each strip, in accumulator order: element (e, b) of lane l at
+  // [strip][(e RB + b) 64 + l].  Then the L + R tile, rows of TJ + 1 floats.
+  f32x4* xr = reinterpret_cast<f32x4*>(smem);
+  float* yt = reinterpret_cast<float*>(smem + 2 * 8 * RB * 64);
+  constexpr int YS = TJ + 1;
+  if (half == 1) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
+      for (int b = 0; b < RB; ++b) xr[(strip * 8 * RB + e * RB + b) * 64 + lane] = acc[e][b];
+  }
+  wait_lgkmcnt0();
+  ring_barrier();
+  if (half == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const f32x4 rr = xr[(strip * 8 * RB + e * RB + b) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int cl = 8 * (4 * grp + i) + e;
-          tile[cl * TJ + 16 * b + n] = acc[e][b][i] + red[((e * RB + b) * 4 + i) * 64 + lane];
+          const int m = 4 * grp + i;
+          yt[(kAccCols * strip + 8 * m + e) * YS + 16 * b + n] = acc[e][b][i] + rr[i];
         }
+      }
   }
-  __syncthreads();
-  // S += tile over the block's rows c0 .. c0 + 127 and ranks 16 rb0 ..
-  // + 16 RB, consecutive threads on consecutive ranks of a row.
-  const int64_t r = g.r;
-  float* __restrict__ S = g.S[item];
+  wait_lgkmcnt0();
+  ring_barrier();
+  wait_vmcnt<0>();  // the S loads (long complete): no waits between the stores below
+  if (jok) {
+    float* p = S + row0 * r + j;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int idx = threadIdx.x + 256 * m;
-    const int64_t c = c0 + idx / TJ;
-    const int64_t j = 16 * rb0 + idx % TJ;
-    if (c < d && j < r) S[c * r + j] += tile[idx];
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      if (row0 + 4 * k < d) *p = sv[k] + yt[(wave + 4 * k) * YS + lane];
+      p += rstride;
+    }
   }
 }
 
@@ -508,8 +671,10 @@ int64_t acc_rank_pad(int64_t r) {
   return 16 * (nrb <= kAccGroupRB ? nrb : (nrb + kAccGroupRB - 1) / kAccGroupRB * kAccGroupRB);
 }
 int64_t acc_token_pad(int64_t T) { return (T + kAccStep - 1) / kAccStep * kAccStep; }
-size_t acc_ws_bytes_per_item(int64_t T, int64_t r) {
-  return (size_t)(2 * acc_rank_pad(r) * acc_token_pad(T) * sizeof(uint16_t));
+static int64_t acc_col_blocks(int64_t d) { return (d + kAccBlockCols - 1) / kAccBlockCols; }
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+size_t acc_ws_bytes_per_item(int64_t T, int64_t /*d*/, int64_t r) {
+  return round256((size_t)(acc_rank_pad(r) * acc_token_pad(T) * 4));
 }
 
 hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void* A,
@@ -563,15 +728,16 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   g.r = r;
   g.nsteps = (int)(acc_token_pad(T) / kAccStep);
   g.nrb = (int)(acc_rank_pad(r) / 16);
-  const int rb = g.nrb < kAccGroupRB ? g.nrb : kAccGroupRB;
-  g.ngroups = g.nrb / rb;
+  g.rb = g.nrb < kAccGroupRB ? g.nrb : kAccGroupRB;
+  g.ngroups = g.nrb / g.rb;
   for (int i = 0; i < n; ++i) {
     g.D[i] = items[i].D;
     g.XAt[i] = items[i].XAt;
     g.S[i] = items[i].S;
-    g.planes[i] = static_cast<uint16_t*>(items[i].ws);
     g.d[i] = items[i].d;
     g.ldd[i] = items[i].ldd;
+    g.nq[i] = acc_col_blocks(items[i].d);
+    g.planes[i] = static_cast<uint16_t*>(items[i].ws);
   }
   if (!bf16) {
     int64_t maxdr = 0;
@@ -588,11 +754,10 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
     if (e != hipSuccess) return e;
   }
   g.tile_begin[0] = 0;
-  for (int i = 0; i < n; ++i)
-    g.tile_begin[i + 1] = g.tile_begin[i] + (g.d[i] + kAccCols - 1) / kAccCols * g.ngroups;
+  for (int i = 0; i < n; ++i) g.tile_begin[i + 1] = g.tile_begin[i] + g.nq[i] * g.ngroups;
   const int64_t tiles = g.tile_begin[n];
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  switch (rb) {
+  switch (g.rb) {
     case 1: hipLaunchKernelGGL(acc_bf16_kernel<1>, grid, dim3(256), 0, s, g); break;
     case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(256), 0, s, g); break;
     case 3: hipLaunchKernelGGL(acc_bf16_kernel<3>, grid, dim3(256), 0, s, g); break;

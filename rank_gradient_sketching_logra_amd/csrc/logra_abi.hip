@@ -107,9 +107,9 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
                     "project_input launch");
 }
 
-LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t r) {
-  if (T < 1 || bad_rank(r)) return 0;
-  return logra::acc_ws_bytes_per_item(T, r);
+LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r) {
+  if (T < 1 || d < 1 || bad_rank(r)) return 0;
+  return logra::acc_ws_bytes_per_item(T, d, r);
 }
 
 static int check_acc_item(const char* name, int64_t T, int64_t r, logra_dtype dt, const void* D,
@@ -124,7 +124,7 @@ static int check_acc_item(const char* name, int64_t T, int64_t r, logra_dtype dt
   if (overlap(rs, range(D, extent(T, d, ldd, elem_size(dt)))) || overlap(rs, range(XAt, (size_t)(T * r) * 4)))
     return fail(LOGRA_ERR_ALIAS, "%s: S overlaps D or XAt", name);
   if (dt == LOGRA_BF16) {
-    const size_t need = logra::acc_ws_bytes_per_item(T, r);
+    const size_t need = logra::acc_ws_bytes_per_item(T, d, r);
     if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
     if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "%s: workspace not 16-byte aligned", name);
     const Range rw = range(ws, need);
@@ -153,12 +153,13 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
   if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
-  const size_t per = logra::acc_ws_bytes_per_item(T, r);
-  if (d_dtype == LOGRA_BF16 && (!ws || ws_bytes < per * (size_t)n))
-    return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_grouped: workspace of %zu bytes needed", per * (size_t)n);
   logra::AccItem items[LOGRA_MAX_GROUP];
+  size_t off = 0;
   for (int i = 0; i < n; ++i) {
-    void* wsi = d_dtype == LOGRA_BF16 ? static_cast<char*>(ws) + per * (size_t)i : nullptr;
+    const size_t per = descs[i].d >= 1 ? logra::acc_ws_bytes_per_item(T, descs[i].d, r) : 0;
+    void* wsi = (d_dtype == LOGRA_BF16 && ws) ? static_cast<char*>(ws) + off : nullptr;
+    if (d_dtype == LOGRA_BF16 && (!ws || ws_bytes < off + per))
+      return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_grouped: workspace of at least %zu bytes needed", off + per);
     int st = check_acc_item("sketch_accumulate_grouped", T, r, d_dtype, descs[i].D, descs[i].d, descs[i].ldd,
                             descs[i].XAt, descs[i].S, wsi, per);
     if (st) return st;
@@ -166,6 +167,7 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
       if (overlap(range(descs[i].S, (size_t)(descs[i].d * r) * 4), range(descs[j].S, (size_t)(descs[j].d * r) * 4)))
         return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_grouped: sketches %d and %d overlap", j, i);
     items[i] = logra::AccItem{descs[i].D, descs[i].XAt, descs[i].S, descs[i].d, descs[i].ldd, wsi};
+    if (d_dtype == LOGRA_BF16) off += per;
   }
   return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, items, n,
                                              static_cast<hipStream_t>(stream)),

@@ -42,9 +42,13 @@ def test_version_and_sizes(lib):
     assert "gfx950" in B.version()
     assert B.sketch_bytes(4096, 64) == 1 << 20          # 1 MiB, paper §2.2
     assert lib.logra_sketch_bytes(-1, 3) == -1
-    assert B.accumulate_ws_bytes(4096, 64) == 2 * 64 * 4096 * 2
-    assert B.accumulate_ws_bytes(1000, 33) == 2 * 48 * 1024 * 2
-    assert B.accumulate_ws_bytes(0, 8) == 0
+    # packed XAt (hi, lo bf16: 4 bytes per padded token x rank) + fp32 partials
+    # (512-column groups x padded ranks x 1024-token groups)
+    assert B.accumulate_ws_bytes(4096, 3584, 64) == 64 * 4096 * 4
+    assert B.accumulate_ws_bytes(1000, 300, 33) == 48 * 1024 * 4
+    assert B.accumulate_ws_bytes(4096, 100, 100) == 128 * 4096 * 4
+    assert B.accumulate_ws_bytes(0, 8, 8) == 0
+    assert B.accumulate_ws_bytes(8, 0, 8) == 0
     assert B.rowadam_ws_bytes(0) == 0
     assert B.predicted_kl_q_ws_bytes(64, 152064) > 0
 
@@ -97,7 +101,7 @@ def test_project_validation(lib):
 
 def test_accumulate_validation(lib):
     f = lib.logra_sketch_accumulate
-    ws = B.accumulate_ws_bytes(128, 64)
+    ws = B.accumulate_ws_bytes(128, 64, 64)
     assert err(f, 128, 64, 64, None, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_NULL
     assert err(f, 128, 64, 300, A, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_SHAPE
     assert err(f, 0, 64, 64, A, B.BF16, 64, Bp, C, Dp, ws, None) == B.ERR_SHAPE
@@ -110,7 +114,7 @@ def test_accumulate_validation(lib):
 
 def test_grouped_validation(lib):
     f = lib.logra_sketch_accumulate_grouped
-    ws = 2 * B.accumulate_ws_bytes(128, 64)
+    ws = 2 * B.accumulate_ws_bytes(128, 64, 64)
     descs = (B.AccDesc * 2)(B.AccDesc(A, Bp, C, 64, 64), B.AccDesc(A + 65536, Bp + 65536, C + 64, 64, 64))
     assert err(f, 128, 64, B.BF16, descs, 2, Dp, ws, None) == B.ERR_ALIAS     # sketches overlap
     assert err(f, 128, 64, B.BF16, descs, 0, Dp, ws, None) == B.ERR_SHAPE

@@ -114,7 +114,7 @@ def test_project_f32(T, k, r):
 
 @pytest.mark.parametrize("T,d,r,ldd", [(1000, 300, 64, 304), (512, 256, 8, 256), (4096, 512, 64, 512),
                                        (300, 1000, 256, 1000), (77, 24, 33, 24), (2048, 1536, 100, 1536),
-                                       (16, 8, 1, 8)])
+                                       (16, 8, 1, 8), (4500, 700, 40, 704), (32, 300, 64, 304)])
 def test_accumulate_bf16(T, d, r, ldd):
     say(f"accumulate bf16 T={T} d={d} r={r} ldd={ldd}")
     S0 = synth.fp32_matrix((d, r), 0.1, (12, d, r, 0, 5))
@@ -128,7 +128,6 @@ def test_accumulate_bf16(T, d, r, ldd):
     got = S.cpu().numpy()
     err = relfro(got, want)
     say(f"  rel-Fro {err:.3e}")
-    assert err <= 2e-3
     assert err <= 5e-5
 
 
@@ -144,10 +143,11 @@ def test_accumulate_f32(T, d, r):
     assert relfro(S.cpu().numpy(), want) <= 1e-6
 
 
-def test_accumulate_grouped_is_bit_identical_to_single_calls():
-    T, r = 1024, 64
+@pytest.mark.parametrize("T", [1024, 4200])
+def test_accumulate_grouped_is_bit_identical_to_single_calls(T):
+    r = 64
     shapes = [(3584, 0), (512, 1), (512, 2), (1000, 3), (2048, 4)]
-    say("accumulate grouped vs single")
+    say(f"accumulate grouped vs single T={T}")
     items, singles = [], []
     for d, i in shapes:
         bits, _ = bf16_inputs((T, d), 1e-3, (14, d, i, 0, 1))
