@@ -196,16 +196,15 @@ __global__ void project_f32_kernel(KeyArg key, int64_t T, int64_t k, int64_t r,
 
 // Packed projected input.  XAt is split into two bf16 terms, hi = RNE(x) and
 // lo = RNE(x - hi), laid out in MFMA B-operand order for
-// v_mfma_f32_16x16x32_bf16: for 32-token step s and 16-rank block b, two
-// 1 KiB operands (hi then lo) in which lane l holds tokens 32s + 8(l>>4) + i
-// (i = 0..7) of rank 16b + (l & 15).  One wave reads one operand with one
+// v_mfma_f32_32x32x16_bf16: for 16-token step s and 32-rank block b, two
+// 1 KiB operands (hi then lo) in which lane l holds tokens 16s + 8(l>>5) + i
+// (i = 0..7) of rank 32b + (l & 31).  One wave reads one operand with one
 // fully contiguous 16-byte-per-lane load.  Tokens >= T and ranks >= r are 0.
-constexpr int kAccStep = 32;        // tokens per MFMA step
-constexpr int kAccCols = 128;       // columns of D per wave: 16 lanes x 8
-constexpr int kAccWaves = 4;        // waves per block: 2 strips x 2 token halves
-constexpr int kAccBlockCols = 2 * kAccCols;
-constexpr int kAccGroupRB = 4;      // 16-rank blocks per rank group (64 ranks)
-constexpr int kAccRing = 3;         // steps in flight per block (LDS ring depth)
+constexpr int kAccStep = 16;        // tokens per MFMA step
+constexpr int kAccCols = 256;       // columns of D per block: 32 lanes x 8
+constexpr int kAccWaves = 8;        // waves per block: 2 rank blocks x 4 token quarters
+constexpr int kAccGroupRB = 2;      // 32-rank blocks per rank group (64 ranks)
+constexpr int kAccRing = 3;         // LDS ring slots (steps) per block
 
 struct AccGroupArgs {
   const void* D[kMaxGroup];
@@ -218,10 +217,10 @@ struct AccGroupArgs {
   int64_t tile_begin[kMaxGroup + 1];
   int n;
   int64_t T, r;
-  int nsteps;   // ceil(T / 32)
-  int nrb;      // 16-rank blocks packed: ceil(r / 16), rounded up to a
-                // multiple of 4 when there is more than one rank group
-  int rb;       // 16-rank blocks per rank group: min(nrb, 4)
+  int nsteps;   // ceil(T / 16)
+  int nrb;      // 32-rank blocks packed: ceil(r / 32), rounded up to a
+                // multiple of 2 when there is more than one rank group
+  int rb;       // 32-rank blocks per rank group: min(nrb, 2)
   int ngroups;  // nrb / rb rank groups
 };
 
@@ -238,8 +237,8 @@ __global__ __launch_bounds__(256) void acc_pack_kernel(AccGroupArgs g) {
   const int lane = threadIdx.x & 63;
   const int64_t s = chunk / g.nrb;
   const int64_t b = chunk - s * g.nrb;
-  const int64_t j = 16 * b + (lane & 15);
-  const int64_t t0 = kAccStep * s + 8 * (lane >> 4);
+  const int64_t j = 32 * b + (lane & 31);
+  const int64_t t0 = kAccStep * s + 8 * (lane >> 5);
   const float* __restrict__ x = g.XAt[item];
   float h[8], l[8];
 #pragma unroll
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(256) void acc_pack_kernel(AccGroupArgs g) {
 __device__ __forceinline__ u32x4 load_drow(const uint16_t* __restrict__ D, int64_t ldd,
                                            int64_t t, int64_t T, int64_t col, int64_t d,
                                            bool full) {
-  if (t >= T) return u32x4{0u, 0u, 0u, 0u};
+  if (t >= T || col >= d) return u32x4{0u, 0u, 0u, 0u};
   const uint16_t* p = D + t * ldd + col;
   if (full) return *reinterpret_cast<const u32x4*>(p);
   uint32_t e[8];
@@ -286,33 +285,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Transpose a lane's 8 x 8 block of bf16 (row[i] = eight columns of token
-// i): a[e] = the eight tokens of column e, as one MFMA operand.
+// i): a[e] = the eight tokens of column e, as one MFMA operand.  Each output
+// word takes one 16-bit half from each of two rows (one byte permute).
 __device__ __forceinline__ void transpose8x8(const u32x4 (&row)[8], u32x4 (&a)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int q = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t x0 = row[2 * p][q], x1 = row[2 * p + 1][q];
-      a[e][p] = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
-    }
-  }
-}
-
-// acc[e][b] += A_e B_b over one 32-token step, hi term then lo term.
-template <int RB>
-__device__ __forceinline__ void acc_mfma_step(f32x4 (&acc)[8][RB], const u32x4 (&a)[8],
-                                              const u32x4 (&bh)[RB], const u32x4 (&bl)[RB]) {
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bh[b]),
-                                                          acc[e][b], 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bl[b]),
-                                                          acc[e][b], 0, 0, 0);
+    for (int p = 0; p < 4; ++p) a[e][p] = __builtin_amdgcn_perm(row[2 * p + 1][q], row[2 * p][q], sel);
   }
 }
 
@@ -322,37 +303,44 @@ __device__ __forceinline__ uint32_t lds_addr(Tp* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) Tp*)p;
 }
 
-// LDS reads of consecutive 1 KiB slabs (lane l's 16 bytes at byte 16 l of
-// each) that complete inside the statement: the compiler never sees an LDS
-// read it could order against pending direct global->LDS loads, and the
+// LDS reads that complete inside the statement: the compiler never sees an
+// LDS read it could order against pending direct global->LDS loads, and the
 // results exist only once the data has arrived.  The outputs are
 // early-clobber: a destination sharing a register with the address would be
 // overwritten by the first read's data while later reads still use it.
-__device__ __forceinline__ void lds_read8(uint32_t a, u32x4 (&r)[8]) {
+//
+// One step's operands: eight 1 KiB row slabs at ad and two 1 KiB B operands
+// (hi, lo) at ab; lane l's 16 bytes at byte 16 l of each slab.
+__device__ __forceinline__ void acc_read_step(uint32_t ad, uint32_t ab, u32x4 (&row)[8],
+                                              u32x4& bh, u32x4& bl) {
   asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:4096\n\t"
-      "ds_read_b128 %5, %8 offset:5120\n\t"
-      "ds_read_b128 %6, %8 offset:6144\n\t"
-      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "ds_read_b128 %0, %10\n\t"
+      "ds_read_b128 %1, %10 offset:1024\n\t"
+      "ds_read_b128 %2, %10 offset:2048\n\t"
+      "ds_read_b128 %3, %10 offset:3072\n\t"
+      "ds_read_b128 %4, %10 offset:4096\n\t"
+      "ds_read_b128 %5, %10 offset:5120\n\t"
+      "ds_read_b128 %6, %10 offset:6144\n\t"
+      "ds_read_b128 %7, %10 offset:7168\n\t"
+      "ds_read_b128 %8, %11\n\t"
+      "ds_read_b128 %9, %11 offset:1024\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7])
-      : "v"(a)
+      : "=&v"(row[0]), "=&v"(row[1]), "=&v"(row[2]), "=&v"(row[3]), "=&v"(row[4]),
+        "=&v"(row[5]), "=&v"(row[6]), "=&v"(row[7]), "=&v"(bh), "=&v"(bl)
+      : "v"(ad), "v"(ab)
       : "memory");
 }
-__device__ __forceinline__ void lds_read2(uint32_t a, u32x4& x, u32x4& y) {
+// The two B operands only.
+__device__ __forceinline__ void acc_read_b(uint32_t ab, u32x4& bh, u32x4& bl) {
   asm volatile(
       "ds_read_b128 %0, %2\n\t"
       "ds_read_b128 %1, %2 offset:1024\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x), "=&v"(y)
-      : "v"(a)
+      : "=&v"(bh), "=&v"(bl)
+      : "v"(ab)
       : "memory");
 }
+
 // Workgroup barrier with no memory fence.  The ring's ordering is explicit:
 // loads into LDS are waited for by count before it, and every LDS read has
 // completed inside its own statement, so the fence __syncthreads() adds
@@ -364,110 +352,62 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Rows (8 slabs at ad) and B operands (2 RB slabs at ab: hi, lo per rank
-// block) of one step.
-template <int RB>
-__device__ __forceinline__ void acc_read_step(uint32_t ad, uint32_t ab, u32x4 (&row)[8],
-                                              u32x4 (&bh)[RB], u32x4 (&bl)[RB]) {
-  if constexpr (RB == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %16 offset:1024\n\t"
-        "ds_read_b128 %2, %16 offset:2048\n\t"
-        "ds_read_b128 %3, %16 offset:3072\n\t"
-        "ds_read_b128 %4, %16 offset:4096\n\t"
-        "ds_read_b128 %5, %16 offset:5120\n\t"
-        "ds_read_b128 %6, %16 offset:6144\n\t"
-        "ds_read_b128 %7, %16 offset:7168\n\t"
-        "ds_read_b128 %8, %17\n\t"
-        "ds_read_b128 %9, %17 offset:1024\n\t"
-        "ds_read_b128 %10, %17 offset:2048\n\t"
-        "ds_read_b128 %11, %17 offset:3072\n\t"
-        "ds_read_b128 %12, %17 offset:4096\n\t"
-        "ds_read_b128 %13, %17 offset:5120\n\t"
-        "ds_read_b128 %14, %17 offset:6144\n\t"
-        "ds_read_b128 %15, %17 offset:7168\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(row[0]), "=&v"(row[1]), "=&v"(row[2]), "=&v"(row[3]), "=&v"(row[4]), "=&v"(row[5]),
-          "=&v"(row[6]), "=&v"(row[7]), "=&v"(bh[0]), "=&v"(bl[0]), "=&v"(bh[1]), "=&v"(bl[1]),
-          "=&v"(bh[2]), "=&v"(bl[2]), "=&v"(bh[3]), "=&v"(bl[3])
-        : "v"(ad), "v"(ab)
-        : "memory");
-  } else {
-    lds_read8(ad, row);
+// Direct global->LDS loads of four 1 KiB row slabs at dst: rows prow,
+// prow + ldd, ...; lane l's 16 bytes land at byte 16 l of each.
+__device__ __forceinline__ void acc_issue_rows4(u32x4* dst, const uint16_t* prow, int64_t ldd) {
 #pragma unroll
-    for (int b = 0; b < RB; ++b) lds_read2(ab + 2048 * b, bh[b], bl[b]);
-  }
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(prow + i * ldd, dst + i * 64, 16, 0, 0);
 }
 
-// acc[e][b] += A_e B_b over one 32-token step for rank block b only.
-template <int RB>
-__device__ __forceinline__ void acc_mfma_rb(f32x4 (&acc)[8][RB], const u32x4 (&a)[8], int b,
-                                            u32x4 bh, u32x4 bl) {
+// Direct global->LDS load of one 1 KiB slab from p to dst.
+__device__ __forceinline__ void acc_issue_slab(u32x4* dst, const uint16_t* p) {
+  __builtin_amdgcn_global_load_lds(p, dst, 16, 0, 0);
+}
+
+// acc[e] += A_e B over one 16-token step, hi term then lo term.
+__device__ __forceinline__ void acc_mfma_step(f32x16 (&acc)[8], const u32x4 (&a)[8], u32x4 bh,
+                                              u32x4 bl) {
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bh),
-                                                        acc[e][b], 0, 0, 0);
+    acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bh), acc[e], 0,
+                                                     0, 0);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    acc[e][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[e]), as_bf16x8(bl),
-                                                        acc[e][b], 0, 0, 0);
-}
-
-// Direct global->LDS loads of a wave's eight 1 KiB row slabs of one step:
-// rows prow, prow + ldd, ...; lane l's 16 bytes land at byte 16 l.
-__device__ __forceinline__ void acc_issue_rows(u32x4 (*slabs)[64], const uint16_t* prow,
-                                               int64_t ldd) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(prow + i * ldd, &slabs[i][0], 16, 0, 0);
-}
-
-// Direct global->LDS load of row slab i (row pointer prow) of a wave.
-__device__ __forceinline__ void acc_issue_rows_one(u32x4 (*slabs)[64], int i,
-                                                   const uint16_t* prow) {
-  __builtin_amdgcn_global_load_lds(prow, &slabs[i][0], 16, 0, 0);
-}
-
-// Direct global->LDS loads of one wave's share of a half's B operands for
-// one step: the 1 KiB operands j = strip, strip + 2, ... of the 2 RB at pb.
-template <int RB>
-__device__ __forceinline__ void acc_issue_b(u32x4 (*bs)[64], const uint16_t* pb, int strip) {
-#pragma unroll
-  for (int j0 = 0; j0 < 2 * RB; j0 += 2)
-    __builtin_amdgcn_global_load_lds(pb + (j0 + strip) * 512, &bs[j0 + strip][0], 16, 0, 0);
+    acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e], 0,
+                                                     0, 0);
 }
 
 // bf16 D.  A block covers 256 columns of D (rows of S) and one group of up
-// to 64 ranks over all T tokens.  Its four waves are two 128-column strips
-// times two token halves: wave w takes the strip of columns
-// c0 = 256 q + 128 (w & 1) onwards and, for w >> 1 = 0 (1), the steps
-// [0, h) ([h, nsteps)) with h = ceil(nsteps / 2).  Lane l covers D rows
-// 32s + 8(l>>4) + i (i = 0..7), columns c0 + 8(l&15) .. +7, so sixteen lanes
-// read 256 contiguous bytes of a row.  A three-step ring in LDS is filled by
-// direct global->LDS loads: every wave streams its own rows, and each half's
-// B operands (the packed XAt above) are loaded once per step by that half's
-// two waves and shared by both strips.  Two steps are in flight while a
-// third computes.  The lane's 8 x 8 block is transposed in registers: for
-// e = 0..7, operand A_e holds the eight tokens of column c0 + 8(l&15) + e,
-// which is MFMA row m = l & 15 of instance e; the B operand has the same
-// token for each (lane, element), so each 16x16x32 MFMA adds 32 tokens.
-// Instance e, rank block b gives C[m][n] = S[c0 + 8m + e][16b + n], lane l
-// holding m = 4(l>>4) + i, n = l & 15.  Each wave sums its half's steps in
-// ascending order (hi term then lo term per step); the second half's sum R
-// passes through LDS to the first half's wave, which forms L + R, and the
-// block adds that to S through an LDS tile so that S is read and written
-// in whole rows.  The order depends on T alone, so grouped and single calls
-// give the same bits.  Strips that reach past column d take guarded loads;
+// to two 32-rank blocks over all T tokens.  Its eight waves (two per SIMD,
+// so one wave's matrix work overlaps the other's loads and transposes) are
+// two rank blocks times four token quarters: wave w takes rank block w & 1
+// of the group and the 16-token steps s = u (mod 4) of quarter u = w >> 1,
+// so the block streams consecutive tokens.  Lane l covers D rows 16s + 8(l>>5) + i
+// (i = 0..7), columns c0 + 8(l&31) .. +7, so 32 lanes read 512 contiguous
+// bytes of a row.  A ring of kAccRing steps in LDS is filled by direct
+// global->LDS loads: a slot holds, for each quarter, the step's eight row
+// slabs (loaded four each by the quarter's two waves and read by both) and
+// the B operands of the group's rank blocks (each wave loads its own), so
+// kAccRing - 1 steps are in flight while one computes.  The lane's 8 x 8
+// block is transposed in registers: for e = 0..7, operand A_e holds the
+// eight tokens of column c0 + 8(l&31) + e, which is MFMA row m = l & 31 of
+// instance e; the B operand holds the same tokens for rank n = l & 31, so
+// each 32x32x16 MFMA adds 16 tokens.  Instance e gives
+// C[m][n] = S[c0 + 8m + e][32b + n], lane l holding n = l & 31 and
+// m = 8(j>>2) + 4(l>>5) + (j&3) in register j.  Each wave sums its
+// quarter's steps in ascending order (hi term then lo term per step); the
+// quarter sums meet through LDS as (Q0 + Q1) + (Q2 + Q3), and the block
+// adds that to S through an LDS tile so that S is read and written in whole
+// rows.  The order depends on T alone, so grouped and single calls give the
+// same bits.  Blocks that reach past column d take guarded register loads;
 // rows past T (last step only) are loaded from row T - 1 and zeroed.
 template <int RB>
-__global__ __launch_bounds__(256, 1) void acc_bf16_kernel(AccGroupArgs g) {
+__global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
   constexpr int R = kAccRing;
-  constexpr int NB = 2 * RB;                  // B operands per step and half
-  constexpr int kRing = R * kAccWaves * 8;    // 1 KiB row slabs
-  __shared__ __align__(16) u32x4 smem[(kRing + R * 2 * NB) * 64];  // 144 KiB at RB = 4
-  u32x4 (*dring)[kAccWaves][8][64] = reinterpret_cast<u32x4 (*)[kAccWaves][8][64]>(smem);
-  u32x4 (*bring)[2][NB][64] = reinterpret_cast<u32x4 (*)[2][NB][64]>(smem + kRing * 64);
+  constexpr int kQuarter = 8 + 2 * RB;  // 1 KiB slabs per quarter in a slot
+  constexpr int kSlot = 4 * kQuarter;
+  __shared__ __align__(16) u32x4 smem[R * kSlot * 64];  // 144 KiB at RB = 2
 
   const int64_t logical = xcd_logical_block();
   if (logical >= g.tile_begin[g.n]) return;
@@ -480,158 +420,177 @@ __global__ __launch_bounds__(256, 1) void acc_bf16_kernel(AccGroupArgs g) {
   const int64_t ldd = g.ldd[item];
   const int64_t d = g.d[item];
   const int64_t T = g.T;
-  const int rb0 = rg * RB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int strip = wave & 1;
-  const int half = wave >> 1;
-  const int n = lane & 15;
-  const int grp = lane >> 4;
+  const int rb = wave & 1;              // rank block of this wave within the group
+  const int qt = wave >> 1;             // token quarter
+  const bool has_rb = rb < RB;          // uniform per wave
+  const int hw = lane >> 5;
   const int nsteps = g.nsteps;
-  const int h = (nsteps + 1) >> 1;
-  const int s_begin = half ? h : 0;
-  const int s_end = half ? nsteps : h;
+  const int Q = (nsteps + 3) >> 2;      // iterations: steps 4k + qt, k < Q
 
-  const int64_t c0 = q * kAccBlockCols + kAccCols * strip;  // this wave's strip
-  const int64_t col = c0 + 8 * n;
-  const bool active = c0 < d;                  // uniform per wave
-  const bool interior = c0 + kAccCols <= d;    // uniform per wave
+  const int64_t c0 = q * kAccCols;
+  const int64_t col = c0 + 8 * (lane & 31);
+  const bool interior = c0 + kAccCols <= d;  // uniform per block
   const bool col_full = col + 8 <= d;
-  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb0 * 1024 + lane * 8;
+  const uint16_t* __restrict__ planes =
+      g.planes[item] + ((int64_t)rg * RB + rb) * 1024 + lane * 8;
   const int64_t bstride = (int64_t)g.nrb * 1024;
 
-  f32x4 acc[8][RB];
+  f32x16 acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int b = 0; b < RB; ++b) acc[e][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
 
-  // Loads of iteration k (step s_begin + k) into ring slot k % R: this
-  // wave's share of its half's B operands and, for an interior strip, its
-  // eight row slabs.  Iterations past the half re-read its last step
-  // (already cached) so that every iteration issues the same number of
-  // loads; rows past T read row T - 1.
-  auto issue = [&](int k, bool rows) {
-    const int st = s_begin + k;
-    const int sc = st < s_end ? st : s_end - 1;
-    const int slot = k % R;
-    acc_issue_b<RB>(bring[slot][half], planes + (int64_t)sc * bstride, strip);
-    if (!rows) return;
-    const int64_t t0 = (int64_t)kAccStep * sc + 8 * grp;
+  // Loads of iteration k (step 4k + qt) into slot k % R: this wave's B
+  // operands (hi, lo of its rank block) and, for an interior block, its
+  // four of the step's eight row slabs.  Iterations past the last step
+  // re-read it (already cached) so that every iteration issues the same
+  // number of loads; rows past T read row T - 1.
+  auto issue = [&](int k) {
+    const int st = 4 * k + qt;
+    const int sc = st < nsteps ? st : nsteps - 1;
+    u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
+    if (has_rb) {
+      const uint16_t* pb = planes + (int64_t)sc * bstride;
+      acc_issue_slab(qs + (8 + 2 * rb) * 64, pb);
+      acc_issue_slab(qs + (9 + 2 * rb) * 64, pb + 512);
+    }
+    if (!interior) return;
+    const int64_t t0 = (int64_t)kAccStep * sc + 8 * hw + 4 * rb;
     if ((int64_t)kAccStep * (sc + 1) <= T) {
-      acc_issue_rows(dring[slot][wave], D + t0 * ldd + col, ldd);
+      acc_issue_rows4(qs + 4 * rb * 64, D + t0 * ldd + col, ldd);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + i < T ? t0 + i : T - 1;
-        acc_issue_rows_one(dring[slot][wave], i, D + t * ldd + col);
+        acc_issue_slab(qs + (4 * rb + i) * 64, D + t * ldd + col);
       }
     }
   };
 
   if (interior) {
 #pragma unroll
-    for (int k = 0; k < R - 1; ++k) issue(k, true);
-    for (int k = 0; k < h; ++k) {
-      // Iteration k has landed once only the loads of iteration k + 1 (eight
-      // row slabs and RB B operands) remain.
-      static_assert(R == 3, "the wait count assumes a three-step ring");
-      wait_vmcnt<8 + RB>();
-      ring_barrier();  // both waves' shares of the half's B operands have landed
-      const int slot = k % R;
-      const int s = s_begin + k;
-      u32x4 row[8], a[8], bh[RB], bl[RB];
-      acc_read_step<RB>(lds_addr(&dring[slot][wave][0][lane]),
-                        lds_addr(&bring[slot][half][0][lane]), row, bh, bl);
-      if ((int64_t)kAccStep * (s + 1) > T) {
-        const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
+    for (int k = 0; k < R - 1; ++k) issue(k);
+    for (int k = 0; k < Q; ++k) {
+      // Iteration k has landed once only the loads of iterations
+      // k+1 .. k+R-2 remain (six per iteration, four without a rank block).
+      static_assert(R == 3, "the wait counts assume a three-step ring");
+      if (has_rb) wait_vmcnt<6>();
+      else wait_vmcnt<4>();
+      ring_barrier();  // the partner's rows of iteration k have landed and
+                       // every wave is done with iteration k - 1's slot
+      issue(k + R - 1);
+      const int s = 4 * k + qt;
+      if (has_rb && s < nsteps) {
+        const u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
+        u32x4 row[8], a[8], bh, bl;
+        acc_read_step(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), row, bh, bl);
+        if ((int64_t)kAccStep * (s + 1) > T) {
+          const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-      // Refill the slot every wave finished reading before this barrier.
-      issue(k + R - 1, true);
-      if (s < s_end) {
+          for (int i = 0; i < 8; ++i)
+            if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
+        }
         transpose8x8(row, a);
-        acc_mfma_step<RB>(acc, a, bh, bl);
+        acc_mfma_step(acc, a, bh, bl);
       }
     }
   } else {
-    // Edge or empty strip: the same barriers and B shares; rows by guarded
-    // loads when the strip starts inside D.
+    // Block reaching past column d: the same barriers and B loads; rows by
+    // guarded register loads.
 #pragma unroll
-    for (int k = 0; k < R - 1; ++k) issue(k, false);
-    for (int k = 0; k < h; ++k) {
+    for (int k = 0; k < R - 1; ++k) issue(k);
+    for (int k = 0; k < Q; ++k) {
       wait_vmcnt<0>();
       ring_barrier();
-      const int slot = k % R;
-      const int s = s_begin + k;
-      if (active && s < s_end) {
-        const int64_t t0 = (int64_t)kAccStep * s + 8 * grp;
-        u32x4 row[8], a[8];
+      issue(k + R - 1);
+      const int s = 4 * k + qt;
+      if (has_rb && s < nsteps) {
+        const u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
+        const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
+        u32x4 row[8], a[8], bh, bl;
 #pragma unroll
         for (int i = 0; i < 8; ++i) row[i] = load_drow(D, ldd, t0 + i, T, col, d, col_full);
+        acc_read_b(lds_addr(qs + (8 + 2 * rb) * 64 + lane), bh, bl);
         transpose8x8(row, a);
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          u32x4 bh, bl;
-          lds_read2(lds_addr(&bring[slot][half][2 * b][lane]), bh, bl);
-          acc_mfma_rb<RB>(acc, a, b, bh, bl);
-        }
+        acc_mfma_step(acc, a, bh, bl);
       }
-      issue(k + R - 1, false);
     }
   }
   wait_vmcnt<0>();  // no load may still target LDS past this point
 
-  // This thread's share of the block's S tile (256 rows x 16 RB ranks): rank
-  // j0 + lane of rows row0 + wave + 4k, so a wave reads whole row segments.
-  // The loads are issued now and complete while L + R is formed.
-  constexpr int TJ = 16 * RB;
-  constexpr int kRowsPerThread = kAccBlockCols / kAccWaves;
+  // This thread's share of the block's S tile (256 rows x 32 RB ranks): rank
+  // j0 + lane of rows row0 + 8k, so a wave reads whole row segments.  The
+  // loads are issued now and complete while the quarter sums meet.
+  constexpr int TJ = 32 * RB;
+  constexpr int kRowsPerThread = kAccCols / kAccWaves;
   float* __restrict__ S = g.S[item];
   const int64_t r = g.r;
-  const int64_t row0 = q * kAccBlockCols + wave;
-  const int64_t j = 16 * (int64_t)rb0 + lane;
+  const int64_t row0 = c0 + wave;
+  const int64_t j = 32 * (int64_t)rg * RB + lane;
   const bool jok = lane < TJ && j < r;
-  int64_t rstride = 4 * r;
   const int64_t jc = j < r ? j : r - 1;  // in-bounds address for idle lanes
+  int64_t rstride = kAccWaves * r;
   float sv[kRowsPerThread];
 #pragma unroll
   for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t row = row0 + 4 * k < d ? row0 + 4 * k : d - 1;
+    const int64_t row = row0 + kAccWaves * k < d ? row0 + kAccWaves * k : d - 1;
     sv[k] = S[row * r + jc];
   }
   // Keep the addresses from being held live across the exchange below.
   asm volatile("" : "+s"(rstride));
   ring_barrier();  // every wave is done with the ring
 
-  // R of each strip, in accumulator order: element (e, b) of lane l at
-  // [strip][(e RB + b) 64 + l].  Then the L + R tile, rows of TJ + 1 floats.
+  // Quarter sums in accumulator order: element (e, j) of lane l at
+  // [slot][(4e + j / 4) 64 + l] as float4, one 32 KiB slot per wave.
   f32x4* xr = reinterpret_cast<f32x4*>(smem);
-  float* yt = reinterpret_cast<float*>(smem + 2 * 8 * RB * 64);
-  constexpr int YS = TJ + 1;
-  if (half == 1) {
+  auto put = [&](int slot) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int b = 0; b < RB; ++b) xr[(strip * 8 * RB + e * RB + b) * 64 + lane] = acc[e][b];
-  }
+      for (int v = 0; v < 4; ++v)
+        xr[(slot * 32 + 4 * e + v) * 64 + lane] =
+            f32x4{acc[e][4 * v], acc[e][4 * v + 1], acc[e][4 * v + 2], acc[e][4 * v + 3]};
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 x = xr[(slot * 32 + 4 * e + v) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[e][4 * v + i] += x[i];
+      }
+  };
+  // Q0 + Q1 and Q2 + Q3 (slots rb + 2 (qt >> 1)).
+  if (has_rb && (qt & 1)) put(rb + 2 * (qt >> 1));
   wait_lgkmcnt0();
   ring_barrier();
-  if (half == 0) {
+  if (has_rb && !(qt & 1)) add(rb + 2 * (qt >> 1));
+  wait_lgkmcnt0();
+  ring_barrier();
+  // (Q0 + Q1) + (Q2 + Q3).
+  if (has_rb && qt == 2) put(rb);
+  wait_lgkmcnt0();
+  ring_barrier();
+  // The tile in LDS after the first 64 KiB, rows of TJ + 1 floats.
+  float* yt = reinterpret_cast<float*>(smem + 2 * 32 * 64);
+  constexpr int YS = TJ + 1;
+  if (has_rb && qt == 0) {
+    add(rb);
+    const int n = lane & 31;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const f32x4 rr = xr[(strip * 8 * RB + e * RB + b) * 64 + lane];
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = 4 * grp + i;
-          yt[(kAccCols * strip + 8 * m + e) * YS + 16 * b + n] = acc[e][b][i] + rr[i];
+          const int m = 8 * v + 4 * hw + i;
+          yt[(8 * m + e) * YS + 32 * rb + n] = acc[e][4 * v + i];
         }
-      }
   }
   wait_lgkmcnt0();
   ring_barrier();
@@ -640,7 +599,7 @@ __global__ __launch_bounds__(256, 1) void acc_bf16_kernel(AccGroupArgs g) {
     float* p = S + row0 * r + j;
 #pragma unroll
     for (int k = 0; k < kRowsPerThread; ++k) {
-      if (row0 + 4 * k < d) *p = sv[k] + yt[(wave + 4 * k) * YS + lane];
+      if (row0 + kAccWaves * k < d) *p = sv[k] + yt[(wave + kAccWaves * k) * YS + lane];
       p += rstride;
     }
   }
@@ -667,11 +626,11 @@ __global__ void acc_f32_kernel(AccGroupArgs g) {
 // ------------------------------------------------------------ launchers
 
 int64_t acc_rank_pad(int64_t r) {
-  const int64_t nrb = (r + 15) / 16;
-  return 16 * (nrb <= kAccGroupRB ? nrb : (nrb + kAccGroupRB - 1) / kAccGroupRB * kAccGroupRB);
+  const int64_t nrb = (r + 31) / 32;
+  return 32 * (nrb <= kAccGroupRB ? nrb : (nrb + kAccGroupRB - 1) / kAccGroupRB * kAccGroupRB);
 }
 int64_t acc_token_pad(int64_t T) { return (T + kAccStep - 1) / kAccStep * kAccStep; }
-static int64_t acc_col_blocks(int64_t d) { return (d + kAccBlockCols - 1) / kAccBlockCols; }
+static int64_t acc_col_blocks(int64_t d) { return (d + kAccCols - 1) / kAccCols; }
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 size_t acc_ws_bytes_per_item(int64_t T, int64_t /*d*/, int64_t r) {
   return round256((size_t)(acc_rank_pad(r) * acc_token_pad(T) * 4));
@@ -727,7 +686,7 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   g.T = T;
   g.r = r;
   g.nsteps = (int)(acc_token_pad(T) / kAccStep);
-  g.nrb = (int)(acc_rank_pad(r) / 16);
+  g.nrb = (int)(acc_rank_pad(r) / 32);
   g.rb = g.nrb < kAccGroupRB ? g.nrb : kAccGroupRB;
   g.ngroups = g.nrb / g.rb;
   for (int i = 0; i < n; ++i) {
@@ -758,10 +717,8 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   const int64_t tiles = g.tile_begin[n];
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
   switch (g.rb) {
-    case 1: hipLaunchKernelGGL(acc_bf16_kernel<1>, grid, dim3(256), 0, s, g); break;
-    case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(256), 0, s, g); break;
-    case 3: hipLaunchKernelGGL(acc_bf16_kernel<3>, grid, dim3(256), 0, s, g); break;
-    case 4: hipLaunchKernelGGL(acc_bf16_kernel<4>, grid, dim3(256), 0, s, g); break;
+    case 1: hipLaunchKernelGGL(acc_bf16_kernel<1>, grid, dim3(kAccWaves * 64), 0, s, g); break;
+    case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
