@@ -1,25 +1,36 @@
 """Benchmark of the LoGRA sketch hot path on one MI355X.
 
 One step = one update over the whole layer set of the workload:
-  A. project every selected matrix's input, every microbatch (XAt = X A^T)
+  A. project every selected matrix's input, every microbatch, straight into
+     the packed operand form the accumulate reads (XAt = X A^T)
   B. accumulate every sketch, every microbatch (grouped: the seven matrices
-     of one layer and one microbatch per launch)
+     of one layer and one microbatch per launch -- one kernel per launch)
   C. RowAdam for every sketch, predicted-KL q over the context set, alpha on
      the device
   D. merge every matrix, W <- round(W - eta*alpha U A)
 Inputs are synthetic and resident in HBM before timing starts (distinct
 buffers for every layer and microbatch, so the 256 MB Infinity Cache cannot
 serve them).  The metric is HBM GB/s of phases B + D: their algorithmic bytes
-(accumulate 2Td + 4Tr + 8dr per call, merge 4dk + 4dr per matrix) divided by
-their HIP-event time on the stream the kernels run on.
+(accumulate 2Td + 4Tr + 8dr per matrix and microbatch, merge 4dk + 4dr per
+matrix) divided by their HIP-event time on the stream the kernels run on.
 
-Prints one JSON line.  --gpus above 1 is refused (one-GPU build).
+Modes:
+  (default)              the benchmark; prints one JSON line
+  --counter-run          a short run for rocprofv3 --pmc: a plain copy of known
+                         size (the calibration) and two steps of two layers
+  --summarize-traffic F W  read the FETCH_SIZE (F) and WRITE_SIZE (W) counter
+                         CSVs of two --counter-run passes and print the
+                         calibrated HBM bytes per accumulate launch
+--gpus above 1 is refused: this measures one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +38,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+CALIB_BYTES = 1 << 30   # plain copy used to calibrate the byte counters
+ACC_KERNEL = "acc_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "acc_bf16_kernel.qwen2.5-7b-set-r64.traffic.md")
+KERNEL_SOURCES = ["rank_gradient_sketching_logra_amd/csrc/kernels_sketch.hip",
+                  "rank_gradient_sketching_logra_amd/csrc/kernels.h",
+                  "rank_gradient_sketching_logra_amd/csrc/device_common.h"]
 
 
 def parse():
@@ -38,6 +55,8 @@ def parse():
     ap.add_argument("--rounding", default=None, choices=[None, "nearest", "stochastic"])
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="use fewer layers (profiling runs only)")
+    ap.add_argument("--counter-run", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
 
 
@@ -51,6 +70,60 @@ def merge_bytes(d, k, r):
 
 def project_bytes(T, k, r):
     return 2 * T * k + 4 * T * r
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Calibrated HBM bytes per accumulate launch from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    t = json.loads(line[len("traffic-json: "):])
+                    if t.get("kernel_sources") == kernel_source_hash():
+                        return t
+    except OSError:
+        pass
+    return None
+
+
+def summarize_traffic(fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the copy and of the accumulate kernel;
+    scale each counter by bytes-moved / counter-reading of the copy."""
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = "acc" if ACC_KERNEL in name else "copy" if re.search(r"copy", name) else None
+            if key is None:
+                continue
+            vals.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
+            vals[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        return {k: sorted(v.values()) for k, v in vals.items()}
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    # the calibration copy is the largest copy dispatch
+    fcopy, wcopy = max(f["copy"]), max(w["copy"])
+    ffac = CALIB_BYTES / (fcopy * 1024.0)
+    wfac = CALIB_BYTES / (wcopy * 1024.0)
+    facc = sum(f["acc"]) / len(f["acc"]) * 1024.0 * ffac
+    wacc = sum(w["acc"]) / len(w["acc"]) * 1024.0 * wfac
+    return {"kernel": ACC_KERNEL, "workload": "qwen2.5-7b-set-r64",
+            "fetch_bytes_per_launch": round(facc), "write_bytes_per_launch": round(wacc),
+            "traffic_bytes_per_launch": round(facc + wacc),
+            "fetch_calibration": round(ffac, 4), "write_calibration": round(wfac, 4),
+            "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
+            "acc_dispatches": len(f["acc"]), "kernel_sources": kernel_source_hash()}
 
 
 def cpu_baseline(w, rounding):
@@ -90,9 +163,12 @@ def cpu_baseline(w, rounding):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        t = summarize_traffic(*args.summarize_traffic)
+        print("traffic-json: " + json.dumps(t))
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design in DESIGN.md, not a run)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -102,6 +178,9 @@ def main():
     w = synth.BY_NAME[args.workload]
     rounding = args.rounding or w.rounding
     layers = args.layers or w.layers
+    if args.counter_run:
+        layers = min(layers, 2)
+        args.steps, args.warmup = 2, 0
     T, r, M = w.T, w.r, w.microbatches
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -114,14 +193,23 @@ def main():
         t.normal_(0.0, std, generator=g)
         return t
 
+    if args.counter_run:
+        # the calibration: a plain copy of CALIB_BYTES
+        src = torch.empty((CALIB_BYTES // 2,), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     mats = w.matrices(layers=range(layers))
     # Inputs X: q/k/v share the attention input, gate/up the MLP input.
     shared = {"q": "att", "k": "att", "v": "att", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
     xw = {"att": w.shapes["q"][1], "o": w.shapes["o"][1], "mlp": w.shapes["gate"][1], "down": w.shapes["down"][1]}
     X = {(l, mb, s): randn((T, xw[s]), 1.0) for l in range(layers) for mb in range(M) for s in xw}
     D = {(l, mb, kind): randn((T, d), 1e-3) for (l, kind, mid, d, k) in mats for mb in range(M)}
-    XAt = {(l, mb, kind): torch.empty((T, r), dtype=torch.float32, device=dev)
-           for (l, kind, mid, d, k) in mats for mb in range(M)}
+    pbytes = B.packed_input_bytes(T, r)
+    PL = {(l, mb, kind): torch.empty((pbytes,), dtype=torch.uint8, device=dev)
+          for (l, kind, mid, d, k) in mats for mb in range(M)}
     W = {(l, kind): randn((d, k), 0.02) for (l, kind, mid, d, k) in mats}
     S = {(l, kind): torch.zeros((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     U = {(l, kind): torch.empty((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
@@ -140,11 +228,11 @@ def main():
     by_layer = {}
     for (l, kind, mid, d, k) in mats:
         by_layer.setdefault(l, []).append((kind, d, k))
-    acc_ws = B.workspace(B.accumulate_grouped_ws_bytes(T, [d for (_, d, _) in by_layer[0]], r), dev)
     acc_total = sum(acc_bytes(T, d, r) for (_, _, _, d, _) in mats) * M
     merge_total = sum(merge_bytes(d, k, r) for (_, _, _, d, k) in mats)
     proj_total = sum(project_bytes(T, k, r) for (_, _, _, d, k) in mats) * M
     n_acc_launch = layers * M
+    acc_per_launch = acc_total // n_acc_launch
     t_step = 0
 
     def step(ev):
@@ -156,12 +244,13 @@ def main():
         for mb in range(M):                          # A: forward-side projections
             for l in range(layers):
                 for (kind, d, k) in by_layer[l]:
-                    B.project_input(keys[(l, kind)], X[(l, mb, shared[kind])], r, out=XAt[(l, mb, kind)])
+                    B.project_input_packed(keys[(l, kind)], X[(l, mb, shared[kind])], r,
+                                           planes=PL[(l, mb, kind)])
         ev[1].record()
         for mb in range(M):                          # B: backward-side sketch accumulation
             for l in reversed(range(layers)):
-                B.sketch_accumulate_grouped([(D[(l, mb, kind)], XAt[(l, mb, kind)], S[(l, kind)])
-                                             for (kind, d, k) in by_layer[l]], ws=acc_ws)
+                B.sketch_accumulate_grouped_packed([(D[(l, mb, kind)], PL[(l, mb, kind)], S[(l, kind)])
+                                                    for (kind, d, k) in by_layer[l]], r)
         ev[2].record()
         for key_ in S:                               # C: optimiser and step control
             B.rowadam(S[key_], V[key_], t_step, w.beta, w.eps, U=U[key_], ws=ra_ws)
@@ -186,6 +275,9 @@ def main():
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.counter_run:
+        print("counter run done", flush=True)
+        return
     ph = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(4)]   # ms per phase per step
     tot = [sum(p) for p in ph]
     K = args.steps
@@ -194,6 +286,8 @@ def main():
     acc_gbs = acc_total / (acc_ms * 1e-3) / 1e9
     merge_gbs = merge_total / (merge_ms * 1e-3) / 1e9
     proj_gbs = proj_total / (tot[0] / K * 1e-3) / 1e9
+    avg_launch_us = acc_ms * 1e3 / n_acc_launch
+    traffic = read_traffic() if w.name == "qwen2.5-7b-set-r64" else None
     out = {
         "metric": "sketch-accumulate + merge HBM GB/s (% of peak), Qwen-7B layer set, r=64",
         "value": round(value, 2),
@@ -210,11 +304,13 @@ def main():
         "config": {"workload": w.name, "layers": layers, "matrices": len(mats), "r": r, "T": T,
                    "microbatches": M, "rounding": rounding, "optimizer": w.optimizer,
                    "contexts": P, "vocab": Vv, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": "sketch_accumulate (grouped: pack + acc_bf16 kernels)",
-                     "achieved": round(acc_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(acc_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": acc_total // n_acc_launch,
-                     "avg_launch_us": round(acc_ms * 1e3 / n_acc_launch, 3)},
+        "roofline": {"bound": "hbm", "kernel": ACC_KERNEL,
+                     "achieved": round(acc_per_launch / (avg_launch_us * 1e-6) / 1e9, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(acc_per_launch / (avg_launch_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "bytes_per_launch": acc_per_launch, "launches": n_acc_launch * K,
+                     "avg_launch_us": round(avg_launch_us, 3)},
         "phases_ms": {"project": round(tot[0] / K, 3), "accumulate": round(acc_ms, 3),
                       "rowadam_q_alpha": round(tot[2] / K, 3), "merge": round(merge_ms, 3)},
         "kernels_gbs": {"accumulate": round(acc_gbs, 1), "merge": round(merge_gbs, 1),

@@ -189,6 +189,45 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
                                               void* ws, size_t ws_bytes,
                                               logra_stream stream);
 
+/* ------------------------------------------------- packed projected input */
+
+/* Bytes of the packed projected input for T tokens and rank r: XAt as two
+ * bf16 terms (hi = RNE(x), lo = RNE(x - hi)) in the matrix-core operand
+ * order the accumulate reads -- for each 16-token step and 32-rank block, a
+ * 1 KiB hi operand and a 1 KiB lo operand in which 16-byte lane l holds
+ * tokens 8(l>>5) .. +7 of the step for rank 32b + (l & 31); ranks padded as
+ * for logra_sketch_accumulate_ws_bytes, padding zero.  0 for invalid sizes. */
+LOGRA_API size_t logra_packed_input_bytes(int64_t T, int64_t r);
+
+/* logra_project_input writing its result straight in the packed form above
+ * (and, when XAt is not NULL, also as fp32 [T x r]), so the accumulate
+ * needs no repacking pass.  Same projection as logra_project_input ([paper]
+ * §2.1, §2.2); X must be bf16.  planes needs logra_packed_input_bytes(T, r)
+ * bytes, 16-byte aligned.
+ * Errors: as logra_project_input; X not bf16; planes NULL, too small,
+ * misaligned or overlapping X or XAt. */
+LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_t k, int64_t r,
+                                         const void* X, logra_dtype x_dtype, int64_t ldx,
+                                         float* XAt, void* planes, size_t planes_bytes,
+                                         logra_stream stream);
+
+typedef struct logra_acc_packed_desc {
+  const void* D;            /* [T x d] bf16, row-major, leading dimension ldd */
+  const uint16_t* planes;   /* packed projected input of this matrix          */
+  float* S;                 /* [d x r] fp32 contiguous                         */
+  int64_t d;
+  int64_t ldd;
+} logra_acc_packed_desc;
+
+/* logra_sketch_accumulate_grouped for bf16 D with the projected inputs
+ * already packed (by logra_project_input_packed): the same result bits, one
+ * kernel, no workspace.  Several descriptors may share one packed input.
+ * Errors: NULL pointers; T < 1, d < 1, r out of range, ldd < d; alignment;
+ * S overlapping D, a packed input or another S; n out of range. */
+LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
+                                                     const logra_acc_packed_desc* descs, int n,
+                                                     logra_stream stream);
+
 /* ------------------------------------------------------------- optimiser */
 
 /* Workspace bytes logra_rowadam needs for d rows. */

@@ -31,6 +31,11 @@ class AccDesc(Structure):
     _fields_ = [("D", c_void_p), ("XAt", c_void_p), ("S", c_void_p), ("d", c_int64), ("ldd", c_int64)]
 
 
+class AccPackedDesc(Structure):
+    _fields_ = [("D", c_void_p), ("planes", c_void_p), ("S", c_void_p), ("d", c_int64),
+                ("ldd", c_int64)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -38,6 +43,11 @@ SIGNATURES = {
     "logra_regen_A": (c_int, [POINTER(Key), c_int64, c_int64, c_int, c_void_p, c_void_p]),
     "logra_project_input": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
                                     c_int64, c_void_p, c_void_p]),
+    "logra_packed_input_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_project_input_packed": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
+                                           c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_sketch_accumulate_grouped_packed": (c_int, [c_int64, c_int64, POINTER(AccPackedDesc),
+                                                       c_int, c_void_p]),
     "logra_sketch_accumulate_ws_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
     "logra_sketch_accumulate": (c_int, [c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -137,6 +147,33 @@ def project_input(k_: Key, X: torch.Tensor, r: int, out=None, stream=None):
     _check(lib().logra_project_input(ctypes.byref(k_), T, k, r, _ptr(X), _dtype_code(X), _ld(X),
                                      _ptr(XAt), _stream(X, stream)))
     return XAt
+
+
+def packed_input_bytes(T: int, r: int) -> int:
+    return lib().logra_packed_input_bytes(T, r)
+
+
+def project_input_packed(k_: Key, X: torch.Tensor, r: int, planes=None, out=None, stream=None):
+    """Packed projected input (uint8 tensor of packed_input_bytes(T, r) bytes) and, if out is
+    given, also XAt = X A^T [T x r] fp32 in out.  Returns planes."""
+    T, k = X.shape
+    nb = packed_input_bytes(T, r)
+    planes = planes if planes is not None else torch.empty((nb,), dtype=torch.uint8, device=X.device)
+    _check(lib().logra_project_input_packed(ctypes.byref(k_), T, k, r, _ptr(X), _dtype_code(X), _ld(X),
+                                            _ptr(out), _ptr(planes), planes.numel(), _stream(X, stream)))
+    return planes
+
+
+def sketch_accumulate_grouped_packed(items, r: int, stream=None):
+    """items: sequence of (D, planes, S) with bf16 D sharing T and r; one launch."""
+    n = len(items)
+    T = items[0][0].shape[0]
+    descs = (AccPackedDesc * n)()
+    for i, (D, planes, S) in enumerate(items):
+        if S.shape[1] != r:
+            raise ValueError("S must be [d x r]")
+        descs[i] = AccPackedDesc(D.data_ptr(), planes.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
+    _check(lib().logra_sketch_accumulate_grouped_packed(T, r, descs, n, _stream(items[0][0], stream)))
 
 
 def accumulate_ws_bytes(T: int, d: int, r: int) -> int:

@@ -24,18 +24,22 @@ struct AccItem {
   void* ws;        // workspace of this item: packed projected input
 };
 
-// Rank padded to whole 16-rank blocks (64 when r > 64), tokens to 32-token
-// steps; workspace of one accumulate item (a multiple of 256 bytes).
+// Rank padded to whole 32-rank blocks (64 when r > 64), tokens to 16-token
+// steps; size of the packed projected input of one accumulate item (a
+// multiple of 256 bytes).
 int64_t acc_rank_pad(int64_t r);
 int64_t acc_token_pad(int64_t T);
 size_t acc_ws_bytes_per_item(int64_t T, int64_t d, int64_t r);
 
 hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void* A,
                           hipStream_t s);
+// XAt may be null when planes is given (bf16 X only); planes, when not
+// null, receives the packed projected input the accumulate reads.
 hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const void* X,
-                          bool bf16, int64_t ldx, float* XAt, hipStream_t s);
+                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s);
+// packed: items' ws already hold the packed projected input (XAt unused).
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
-                             hipStream_t s);
+                             bool packed, hipStream_t s);
 
 size_t rowadam_ws_bytes(int64_t d);
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,

@@ -96,7 +96,9 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(KeyArg key, int64_t T
                                                            int64_t r,
                                                            const uint16_t* __restrict__ X,
                                                            int64_t ldx, float cr,
-                                                           float* __restrict__ XAt) {
+                                                           float* __restrict__ XAt,
+                                                           uint16_t* __restrict__ planes,
+                                                           int nrb, int nsteps) {
   constexpr int NQ = (NBT + 1) / 2;
   constexpr int RP = NBT * 32;
   __shared__ __align__(16) float red[32][RP + 1];
@@ -159,11 +161,44 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(KeyArg key, int64_t T
     }
     __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
-    const int m = idx / (int)r;
-    const int j = idx - m * (int)r;
-    const int64_t t = t0 + m;
-    if (t < T) XAt[t * r + j] = red[m][j] * cr;
+  if (XAt) {
+    for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
+      const int m = idx / (int)r;
+      const int j = idx - m * (int)r;
+      const int64_t t = t0 + m;
+      if (t < T) XAt[t * r + j] = red[m][j] * cr;
+    }
+  }
+  if (planes) {
+    // The block's two 16-token steps in the accumulate's operand order: one
+    // wave per (step, 32-rank block), lane l holding tokens 8(l>>5) + i of
+    // rank 32b + (l & 31) as hi and lo bf16 terms.  Rows past T are zero
+    // (X reads past T are zero); ranks past r are written as zero.
+    for (int c = wave; c < 2 * nrb; c += 4) {
+      const int sl = c / nrb;
+      const int b = c - sl * nrb;
+      const int64_t s = 2 * (int64_t)blockIdx.x + sl;
+      if (s >= nsteps) continue;
+      const int j = 32 * b + (lane & 31);
+      float hv[8], lv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = j < r ? red[16 * sl + 8 * half + i][j] * cr : 0.f;
+        hv[i] = (float)(__bf16)v;
+        lv[i] = v - hv[i];
+      }
+      u32x4 vh, vl;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        vh[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p + 1]) << 16);
+        vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
+      }
+      uint16_t* dst = planes + (s * nrb + b) * 1024 + lane * 8;
+      *reinterpret_cast<u32x4*>(dst) = vh;
+      *reinterpret_cast<u32x4*>(dst + 512) = vl;
+    }
   }
 }
 
@@ -211,6 +246,7 @@ struct AccGroupArgs {
   const float* XAt[kMaxGroup];
   float* S[kMaxGroup];
   uint16_t* planes[kMaxGroup];  // packed XAt of each item (workspace)
+  int pack[kMaxGroup];          // 0: item shares an earlier item's XAt and planes
   int64_t d[kMaxGroup];
   int64_t ldd[kMaxGroup];
   int64_t nq[kMaxGroup];        // 256-column blocks of each item
@@ -232,6 +268,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // One wave per (step, rank block) of one item.
 __global__ __launch_bounds__(256) void acc_pack_kernel(AccGroupArgs g) {
   const int item = blockIdx.y;
+  if (!g.pack[item]) return;
   const int64_t chunk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (chunk >= (int64_t)g.nsteps * g.nrb) return;
   const int lane = threadIdx.x & 63;
@@ -646,9 +683,12 @@ hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void*
 }
 
 hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const void* X,
-                          bool bf16, int64_t ldx, float* XAt, hipStream_t s) {
+                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s) {
   const double crd = 1.0 / std::sqrt((double)r);
+  const int nrb = (int)(acc_rank_pad(r) / 32);
+  const int nsteps = (int)(acc_token_pad(T) / kAccStep);
   if (!bf16) {
+    if (planes) return hipErrorInvalidValue;
     const int64_t n = T * r;
     hipLaunchKernelGGL(project_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        key, T, k, r, static_cast<const float*>(X), ldx, crd, XAt);
@@ -661,7 +701,7 @@ hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const voi
 #define LOGRA_PROJ_CASE(NB)                                                                   \
   case NB:                                                                                    \
     hipLaunchKernelGGL(project_bf16_kernel<NB>, grid, dim3(256), 0, s, key, T, k, r, Xb, ldx, \
-                       cr, XAt);                                                              \
+                       cr, XAt, planes, nrb, nsteps);                                         \
     break;
     LOGRA_PROJ_CASE(1)
     LOGRA_PROJ_CASE(2)
@@ -679,7 +719,7 @@ hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const voi
 }
 
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
-                             hipStream_t s) {
+                             bool packed, hipStream_t s) {
   if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
   AccGroupArgs g{};
   g.n = n;
@@ -697,6 +737,15 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
     g.ldd[i] = items[i].ldd;
     g.nq[i] = acc_col_blocks(items[i].d);
     g.planes[i] = static_cast<uint16_t*>(items[i].ws);
+    g.pack[i] = packed ? 0 : 1;
+    // Items that read the same projected input share one packed copy: it is
+    // packed once, into the first such item's space.
+    for (int j = 0; j < i && !packed; ++j)
+      if (items[j].XAt == items[i].XAt) {
+        g.planes[i] = g.planes[j];
+        g.pack[i] = 0;
+        break;
+      }
   }
   if (!bf16) {
     int64_t maxdr = 0;
@@ -705,7 +754,7 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
                        dim3(256), 0, s, g);
     return hipGetLastError();
   }
-  {
+  if (!packed) {
     const int64_t chunks = (int64_t)g.nsteps * g.nrb;
     hipLaunchKernelGGL(acc_pack_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)n),
                        dim3(256), 0, s, g);

@@ -103,8 +103,34 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
   if (overlap(range(X, extent(T, k, ldx, elem_size(x_dtype))), range(XAt, (size_t)(T * r) * 4)))
     return fail(LOGRA_ERR_ALIAS, "project_input: XAt overlaps X");
   return hip_status(logra::launch_project(key_words(key->seed, key), T, k, r, X, x_dtype == LOGRA_BF16,
-                                          ldx, XAt, static_cast<hipStream_t>(stream)),
+                                          ldx, XAt, nullptr, static_cast<hipStream_t>(stream)),
                     "project_input launch");
+}
+
+LOGRA_API size_t logra_packed_input_bytes(int64_t T, int64_t r) {
+  if (T < 1 || bad_rank(r)) return 0;
+  return logra::acc_ws_bytes_per_item(T, 1, r);
+}
+
+LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_t k, int64_t r,
+                                         const void* X, logra_dtype x_dtype, int64_t ldx,
+                                         float* XAt, void* planes, size_t planes_bytes,
+                                         logra_stream stream) {
+  if (!key || !X || !planes) return fail(LOGRA_ERR_NULL, "project_input_packed: NULL pointer");
+  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_packed: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_packed: X must be bf16");
+  int st = check_matrix("project_input_packed X", X, x_dtype, ldx, k);
+  if (st) return st;
+  const size_t need = logra::acc_ws_bytes_per_item(T, 1, r);
+  if (planes_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "project_input_packed: %zu bytes of packed output needed", need);
+  if (!aligned16(planes) || (XAt && !aligned16(XAt))) return fail(LOGRA_ERR_ALIGN, "project_input_packed: outputs must be 16-byte aligned");
+  const Range rx = range(X, extent(T, k, ldx, elem_size(x_dtype)));
+  const Range rp = range(planes, need);
+  if (overlap(rx, rp) || (XAt && (overlap(rx, range(XAt, (size_t)(T * r) * 4)) || overlap(rp, range(XAt, (size_t)(T * r) * 4)))))
+    return fail(LOGRA_ERR_ALIAS, "project_input_packed: outputs overlap X or each other");
+  return hip_status(logra::launch_project(key_words(key->seed, key), T, k, r, X, true, ldx, XAt,
+                                          static_cast<uint16_t*>(planes), static_cast<hipStream_t>(stream)),
+                    "project_input_packed launch");
 }
 
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r) {
@@ -142,7 +168,7 @@ LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r, const voi
   int st = check_acc_item("sketch_accumulate", T, r, d_dtype, D, d, ldd, XAt, S, ws, ws_bytes);
   if (st) return st;
   logra::AccItem it{D, XAt, S, d, ldd, ws};
-  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, &it, 1,
+  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, &it, 1, false,
                                              static_cast<hipStream_t>(stream)),
                     "sketch_accumulate launch");
 }
@@ -169,9 +195,36 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
     items[i] = logra::AccItem{descs[i].D, descs[i].XAt, descs[i].S, descs[i].d, descs[i].ldd, wsi};
     if (d_dtype == LOGRA_BF16) off += per;
   }
-  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, items, n,
+  return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, items, n, false,
                                              static_cast<hipStream_t>(stream)),
                     "sketch_accumulate_grouped launch");
+}
+
+LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
+                                                     const logra_acc_packed_desc* descs, int n,
+                                                     logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t need = logra::acc_ws_bytes_per_item(T, 1, r);
+  logra::AccItem items[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    const logra_acc_packed_desc& e = descs[i];
+    if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL pointer in descriptor %d", i);
+    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: d must be >= 1");
+    int st = check_matrix("sketch_accumulate_grouped_packed D", e.D, LOGRA_BF16, e.ldd, e.d);
+    if (st) return st;
+    if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_grouped_packed: planes and S must be 16-byte aligned");
+    const Range rs = range(e.S, (size_t)(e.d * r) * 4);
+    if (overlap(rs, range(e.D, extent(T, e.d, e.ldd, 2))) || overlap(rs, range(e.planes, need)))
+      return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_grouped_packed: S overlaps D or the packed input");
+    for (int j = 0; j < i; ++j)
+      if (overlap(rs, range(descs[j].S, (size_t)(descs[j].d * r) * 4)) || overlap(rs, range(descs[j].planes, need)))
+        return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_grouped_packed: sketch %d overlaps an operand of %d", i, j);
+    items[i] = logra::AccItem{e.D, nullptr, e.S, e.d, e.ldd, const_cast<uint16_t*>(e.planes)};
+  }
+  return hip_status(logra::launch_accumulate(T, r, true, items, n, true, static_cast<hipStream_t>(stream)),
+                    "sketch_accumulate_grouped_packed launch");
 }
 
 LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {

@@ -123,6 +123,32 @@ def test_grouped_validation(lib):
     assert err(f, 128, 64, B.BF16, None, 2, Dp, ws, None) == B.ERR_NULL
 
 
+def test_packed_sizes_and_validation(lib):
+    assert B.packed_input_bytes(4096, 64) == 64 * 4096 * 4
+    assert B.packed_input_bytes(1000, 33) == 64 * 1008 * 4
+    assert B.packed_input_bytes(4096, 256) == 256 * 4096 * 4
+    assert B.packed_input_bytes(0, 64) == 0 and B.packed_input_bytes(16, 0) == 0
+    k = ctypes.byref(key())
+    f = lib.logra_project_input_packed
+    nb = B.packed_input_bytes(16, 8)
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, None, None, nb, None) == B.ERR_NULL
+    assert err(f, k, 16, 64, 8, A, B.F32, 64, None, Bp, nb, None) == B.ERR_DTYPE
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, None, Bp, nb - 1, None) == B.ERR_WORKSPACE
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, None, Bp + 8, nb, None) == B.ERR_ALIGN
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, None, A + 256, nb, None) == B.ERR_ALIAS     # planes in X
+    assert err(f, k, 16, 64, 8, A, B.BF16, 64, Bp + 16, Bp, nb, None) == B.ERR_ALIAS       # XAt in planes
+    g = lib.logra_sketch_accumulate_grouped_packed
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64))
+    assert err(g, 128, 64, d2, 2, None) == B.ERR_ALIAS                                     # sketches overlap
+    assert err(g, 128, 64, d2, 0, None) == B.ERR_SHAPE
+    assert err(g, 128, 300, d2, 1, None) == B.ERR_SHAPE
+    assert err(g, 128, 64, None, 1, None) == B.ERR_NULL
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, Bp + 64, 64, 64))
+    assert err(g, 128, 64, d1, 1, None) == B.ERR_ALIAS                                     # S in planes
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp + 4, C, 64, 64))
+    assert err(g, 128, 64, d1, 1, None) == B.ERR_ALIGN
+
+
 def test_rowadam_validation(lib):
     f = lib.logra_rowadam
     ws = B.rowadam_ws_bytes(64)

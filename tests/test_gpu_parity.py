@@ -148,11 +148,15 @@ def test_accumulate_grouped_is_bit_identical_to_single_calls(T):
     r = 64
     shapes = [(3584, 0), (512, 1), (512, 2), (1000, 3), (2048, 4)]
     say(f"accumulate grouped vs single T={T}")
-    items, singles = [], []
+    items, singles, xat = [], [], {}
     for d, i in shapes:
         bits, _ = bf16_inputs((T, d), 1e-3, (14, d, i, 0, 1))
         D = bf16_dev(bits)
-        XAt = torch.from_numpy(synth.fp32_matrix((T, r), 3.0, (14, d, i, 0, 0))).to(DEV)
+        # items 0-2 read one projected input (one tensor), as q, k and v do
+        if i <= 2 and 0 in xat:
+            XAt = xat[0]
+        else:
+            XAt = xat[i] = torch.from_numpy(synth.fp32_matrix((T, r), 3.0, (14, d, i, 0, 0))).to(DEV)
         S1 = torch.from_numpy(synth.fp32_matrix((d, r), 0.1, (14, d, i, 0, 5))).to(DEV)
         S2 = S1.clone()
         items.append((D, XAt, S1))
@@ -162,6 +166,37 @@ def test_accumulate_grouped_is_bit_identical_to_single_calls(T):
         B.sketch_accumulate(D, XAt, S2)
     for (_, _, S1), (_, _, S2) in zip(items, singles):
         assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+
+
+@pytest.mark.parametrize("T,r", [(1000, 64), (4096, 33), (48, 256)])
+def test_packed_projection_feeds_accumulate(T, r):
+    """project_input_packed + accumulate_grouped_packed: the same XAt bits as project_input,
+    the same S bits as the unpacked grouped accumulate, and S within tolerance of the oracle's
+    (D^T X) A^T."""
+    k, ds = 320, [640, 300, 256]
+    say(f"packed projection T={T} r={r}")
+    kk = B.key(3, 7, 1)
+    xb, X = bf16_inputs((T, k), 1.0, (17, T, r, 0, 0))
+    Xd = bf16_dev(xb)
+    XAt_ref = B.project_input(kk, Xd, r)
+    XAt = torch.empty_like(XAt_ref)
+    planes = B.project_input_packed(kk, Xd, r, out=XAt)
+    assert torch.equal(XAt.view(torch.int32), XAt_ref.view(torch.int32))
+    items_p, items_u, wants = [], [], []
+    A = oracle.regen_A(3, 7, 1, r, k)
+    for i, d in enumerate(ds):
+        ld = (d + 7) // 8 * 8
+        db, Dm = bf16_inputs((T, ld), 1e-3, (17, T, d, i, 1))
+        D = bf16_dev(db)[:, :d]
+        S0 = synth.fp32_matrix((d, r), 0.1, (17, d, r, i, 5))
+        items_p.append((D, planes, torch.from_numpy(S0.copy()).to(DEV)))
+        items_u.append((D, XAt_ref, torch.from_numpy(S0.copy()).to(DEV)))
+        wants.append(S0.astype(np.float64) + oracle.dense_gradient(Dm[:, :d], X) @ A.T)
+    B.sketch_accumulate_grouped_packed(items_p, r)
+    B.sketch_accumulate_grouped(items_u)
+    for (_, _, Sp), (_, _, Su), want in zip(items_p, items_u, wants):
+        assert torch.equal(Sp.view(torch.int32), Su.view(torch.int32))
+        assert relfro(Sp.cpu().numpy(), want) <= 5e-5
 
 
 def test_accumulate_deterministic_and_zero_d_is_noop():
