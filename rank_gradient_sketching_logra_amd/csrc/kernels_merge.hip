@@ -8,25 +8,27 @@
 // stochastic rounding, the update rebuilt a block of rows at a time and never
 // held whole.
 //
-// bf16 W runs on v_mfma_f32_16x16x32_bf16 with the product transposed: for
-// a 16-row band of W, instance e of a wave computes C[m][n] = sum over ranks
-// of sigma[rank][col(m, e)] * U[row n][rank], with U split into bf16 hi + lo
-// (two MFMAs per rank step) and sigma exact in bf16.  Lane l holds
-// C[m = 4(l>>4) + i][n = l & 15], and the columns are assigned so that lane
-// l owns 16 consecutive columns of one W row per 64-column group: W is read,
-// updated and written straight from registers with 16-byte accesses, and the
-// 16 stochastic-rounding draws of those elements come from one Philox block
-// when k is a multiple of 16.  Every element's sum runs over rank steps in
-// ascending order, hi then lo, whatever the row or block position, so a merge
-// of a row block equals the same rows of a whole-matrix merge.
+// bf16 W runs on v_mfma_f32_32x32x16_bf16 with the product transposed:
+// for a 32-row band of W, instance e of a wave computes
+// C[m][n] = sum over ranks of sigma[rank][col(m, e)] * U[row n][rank], with
+// U split into bf16 hi + lo (two MFMAs per 16-rank step) and sigma exact in
+// bf16.  Lane l holds C[m][n = l & 31] for m = 8(j>>2) + 4(l>>5) + (j&3),
+// j = 0..15, and the columns are assigned so that those sixteen values are
+// sixteen consecutive columns of one W row.  Interior tiles of W pass
+// through LDS: each 32-row band is loaded with direct global->LDS copies of
+// whole row segments (the lane-to-chunk order permuted so that the LDS tile
+// is swizzled and the matrix-side reads do not collide in banks), updated in
+// place in LDS, and written back with whole-row stores.  Every element's sum
+// runs over rank steps in ascending order, hi then lo, whatever the row or
+// block position, so a merge of a row block equals the same rows of a
+// whole-matrix merge; the sixteen stochastic-rounding draws of a lane's
+// elements come from one Philox block when k is a multiple of 16.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace logra {
 
 namespace {
-
-constexpr int kMergeBand = 16;  // rows per band: one MFMA n-block
 
 __device__ __forceinline__ uint64_t pick_word_m(const Philox4& p, int i) {
   const uint64_t a = (i & 1) ? p.w[1] : p.w[0];
@@ -43,24 +45,8 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// Eight consecutive fp32 of U row `row` from rank j0, split into bf16 hi/lo
-// B operands; zero for rows >= d or ranks >= r.
-__device__ __forceinline__ void load_u8(const float* __restrict__ U, int64_t d, int64_t r,
-                                        int64_t row, int64_t j0, bool r_vec, u32x4& hi,
-                                        u32x4& lo) {
-  float x[8];
-  if (row < d && r_vec && j0 + 8 <= r) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(U + row * r + j0);
-    const f32x4 x0 = p[0], x1 = p[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = x0[e];
-      x[4 + e] = x1[e];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (row < d && j0 + e < r) ? U[row * r + j0 + e] : 0.f;
-  }
+// bf16 hi/lo terms of eight fp32 values.
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
   float h[8], l[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -95,177 +81,406 @@ __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t
   }
 }
 
-// A block = 4 waves x NG 64-column groups: columns [cb * 256 NG, +256 NG),
-// row bands [band_begin, band_end) shared by the four waves.  KS = 32-rank
+// Sixteen updated bf16 of one lane: W values w (two words), products
+// acc[0..15] of consecutive columns, element index e0 of the first (for the
+// stochastic-rounding draws).
+template <bool STOCH>
+__device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const f32x16& acc,
+                                         float sc, KeyWords srk, uint64_t e0, u32x4& o0,
+                                         u32x4& o1) {
+  Philox4 p0, p1;
+  if constexpr (STOCH) {
+    p0 = sr_block(srk, e0 >> 4);
+    p1 = (((e0 + 15) >> 4) != (e0 >> 4)) ? sr_block(srk, (e0 + 15) >> 4) : p0;
+  }
+  uint32_t out[8];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
+    const uint32_t wbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
+    const float x = __builtin_fmaf(-sc, acc[t], bf16_bits_to_f32(wbits));
+    uint32_t o;
+    if constexpr (STOCH) {
+      const uint64_t ee = e0 + t;
+      const uint32_t u = ((ee >> 4) == (e0 >> 4)) ? sr_draw(p0, ee) : sr_draw(p1, ee);
+      o = f32_to_bf16_sr(x, u);
+    } else {
+      o = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+    if (t & 1)
+      out[t >> 1] |= o << 16;
+    else
+      out[t >> 1] = o;
+  }
+  o0 = u32x4{out[0], out[1], out[2], out[3]};
+  o1 = u32x4{out[4], out[5], out[6], out[7]};
+}
+
+// s_waitcnt with only the vector-memory counter constrained.
+template <int N>
+__device__ __forceinline__ void merge_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Direct global->LDS copy of one 16-byte chunk per lane.
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// LDS accesses of the streamed tiles are written as statements the compiler
+// cannot order against the direct loads still in flight (it would otherwise
+// wait for all of them before any LDS access): reads complete inside the
+// statement; writes are complete once lgkmcnt reaches zero.  Outputs are
+// early-clobber so that no destination shares a register with an address.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+// N 16-byte reads at a + 1024 i.
+template <int N>
+__device__ __forceinline__ void lds_read_slabs(uint32_t a, u32x4 (&x)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "slab count");
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x[0]) : "v"(a) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(x[0]), "=&v"(x[1]) : "v"(a) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(a) : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7])
+        : "v"(a)
+        : "memory");
+  }
+}
+// 16-byte reads at two or four arbitrary addresses.
+__device__ __forceinline__ void lds_read_at(const uint32_t (&a)[2], u32x4 (&x)[2]) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x[0]), "=&v"(x[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+}
+__device__ __forceinline__ void lds_read_at(const uint32_t (&a)[4], u32x4 (&x)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+__device__ __forceinline__ void lds_write16(uint32_t a, const u32x4& v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Workgroup barrier without the memory fence of __syncthreads (which waits
+// for every outstanding global access, the loads in flight included).
+__device__ __forceinline__ void merge_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A block = 8 waves (two per SIMD) x E 32-column instances: columns
+// [cb BC, cb BC + BC), BC = 256 E, row bands [band_begin, band_end) of 32
+// rows.  KS = 16-rank
 // steps.  The signs of A for the block's columns are generated once into LDS
-// as bits; each wave expands its A operands into registers, then streams its
-// bands: U band as B operands, W straight into registers, 2 KS MFMAs per
-// instance, update, round, store -- with the next band's loads in flight
-// when PREFETCH.
-template <int KS, int NG, bool PREFETCH>
-__global__ __launch_bounds__(256, KS >= 8 ? 1 : 2) void merge_bf16_kernel(
+// as bits and expanded into per-lane A operands; then each band computes
+// C = sigma^T U^T, updates and rounds.  Interior bands of column-interior
+// blocks stream through LDS (two band buffers for W, two for U, the next
+// band's loads in flight while one computes); the others take guarded
+// register loads and stores.
+constexpr int kMergeWaves = 8;
+
+template <int KS, int E, bool STOCH>
+__global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
     KeyArg key, int64_t d, int64_t k, int64_t r, uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ U, float scale_cr, const float* __restrict__ scale_dev,
-    int stochastic, KeyArg sr_key, int64_t row0, int64_t ncb, int64_t bands_per_block) {
-  constexpr int BC = 256 * NG;  // columns per block
-  constexpr int NW = BC / 32;   // sign words per rank
-  constexpr int NI = 4 * NG;    // MFMA instances per wave and band
-  __shared__ uint32_t sbits[KS * 32 * NW];
+    KeyArg sr_key, int64_t row0, int64_t ncb, int64_t bands_per_block) {
+  constexpr int NWV = kMergeWaves;
+  constexpr int BC = 32 * NWV * E;        // columns per block
+  constexpr int NWd = BC / 32;            // sign words per rank
+  constexpr int CH = BC / 8;              // 16-byte chunks per tile row
+  constexpr int WT = 32 * BC / 8;         // 16-byte chunks per W tile (32 rows)
+  constexpr int UT = 32 * KS * 4;         // 16-byte chunks per U band (operand order)
+  // LDS: two W tiles, then two U bands; the sign bits live in the second W
+  // tile until the A operands are built.
+  __shared__ __align__(16) u32x4 lds[2 * WT + 2 * UT];
+  static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;     // W row within the band (B and C layouts)
+  const int hw = lane >> 5;
   const int64_t cb = blockIdx.x % ncb;
   const int64_t bg = blockIdx.x / ncb;
   const int64_t cblk = cb * BC;
-  const int64_t nbands = (d + kMergeBand - 1) / kMergeBand;
+  const int64_t nbands = (d + 31) / 32;
   const int64_t band_begin = bg * bands_per_block;
   const int64_t band_end =
       band_begin + bands_per_block < nbands ? band_begin + bands_per_block : nbands;
   if (band_begin >= band_end) return;
 
-  // Sign bits of ranks [0, 32 KS) for the block's columns: word w of rank j
+  // Sign bits of ranks [0, 16 KS) for the block's columns: word w of rank j
   // holds columns cblk + 32w + (0..31), bit set meaning -1.
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(lds + WT);
   {
     const KeyWords kw{key.k0, key.k1};
-    for (int task = tid; task < KS * 32 * NG; task += 256) {
-      const int j = task / NG;
-      const int pb = task - j * NG;
-      const int64_t cbase = cblk + 256 * pb;
-      uint32_t* dst = &sbits[j * NW + 8 * pb];
-      if (j < r && cbase < k) {
-        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)(cbase >> 8));
+    constexpr int NP = (BC + 255) / 256;  // Philox blocks per rank
+    for (int task = tid; task < 16 * KS * NP; task += NWV * 64) {
+      const int j = task / NP;
+      const int pb = task - j * NP;
+      const int64_t c256 = (cblk >> 8) + pb;
+      uint32_t words[8];
+      if (j < r && c256 * 256 < k) {
+        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)c256);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          dst[2 * w] = (uint32_t)p.w[w];
-          dst[2 * w + 1] = (uint32_t)(p.w[w] >> 32);
+          words[2 * w] = (uint32_t)p.w[w];
+          words[2 * w + 1] = (uint32_t)(p.w[w] >> 32);
         }
       } else {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) dst[w] = 0u;
+        for (int w = 0; w < 8; ++w) words[w] = 0u;
+      }
+      if constexpr (BC >= 256) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) sbits[j * NWd + 8 * pb + w] = words[w];
+      } else {
+        const int off = (int)((cblk & 255) >> 5);  // 128-column block: half of the 256 bits
+#pragma unroll
+        for (int w = 0; w < NWd; ++w) sbits[j * NWd + w] = words[off + w];
       }
     }
   }
   __syncthreads();
 
-  // A operands: instance e = 4G + jj holds, for MFMA row m = l & 15, column
-  // 64(NG wave + G) + 16(m >> 2) + 4jj + (m & 3) of the block and ranks
-  // 32s + 8(l >> 4) + i, i = 0..7.  Ranks >= r read as +1; their U terms
-  // are zero.
-  const int m = lane & 15;
-  const int kg = lane >> 4;
-  u32x4 afrag[NI][KS];
+  // A operands: instance e holds, for MFMA row m = l & 31, column
+  // 32(E wave + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3) of the block and
+  // ranks 16s + 8(l >> 5) + i, i = 0..7.  Ranks >= r read as +1; their U
+  // terms are zero.
+  u32x4 afrag[E][KS];
+  {
+    const int m = lane & 31;
+    const int cm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
-  for (int e = 0; e < NI; ++e) {
-    const int G = e >> 2, jj = e & 3;
-    const int cl = 64 * (NG * wave + G) + 16 * (m >> 2) + 4 * jj + (m & 3);
+    for (int e = 0; e < E; ++e) {
+      const int cl = 32 * (E * wave + e) + cm;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint32_t byte = 0;
+      for (int s = 0; s < KS; ++s) {
+        uint32_t byte = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        byte |= ((sbits[(32 * s + 8 * kg + i) * NW + (cl >> 5)] >> (cl & 31)) & 1u) << i;
-      afrag[e][s] = u32x4{
-          0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
-          0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
-          0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
-          0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+        for (int i = 0; i < 8; ++i)
+          byte |= ((sbits[(16 * s + 8 * hw + i) * NWd + (cl >> 5)] >> (cl & 31)) & 1u) << i;
+        afrag[e][s] = u32x4{
+            0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
+            0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
+            0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
+            0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+        if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
+  __syncthreads();  // the sign bits are dead; their tile may be loaded
 
   float sc = scale_cr;
   if (scale_dev != nullptr) sc *= *scale_dev;
   const KeyWords srk{sr_key.k0, sr_key.k1};
-  const bool r_vec = (r & 3) == 0;
-  const int n = lane & 15;  // W row within the band (B and C layouts)
-  const int q = lane >> 4;  // 16-column slot within a 64-column group
-  const int64_t cwave = cblk + 64 * NG * wave;
+  const int64_t cw = cblk + 32 * E * wave;   // this wave's first column
+  const bool col_interior = cblk + BC <= k;
+  const bool u_dma = (r & 3) == 0;
+  const bool r_full = (r & 15) == 0;
 
-  u32x4 wv[NG][2], uh[KS], ul[KS];
-  u32x4 wn[NG][2], nh[KS], nl[KS];
-  auto load_band = [&](int64_t band, u32x4(&w)[NG][2], u32x4(&h)[KS], u32x4(&l)[KS]) {
-    const int64_t row = band * kMergeBand + n;
+  // C of one band: acc[e] over all rank steps, B operands from bfrag(s).
+  auto mfma_band = [&](f32x16 (&acc)[E], auto&& bfrag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) load_u8(U, d, r, row, 32 * s + 8 * kg, r_vec, h[s], l[s]);
+    for (int e = 0; e < E; ++e)
 #pragma unroll
-    for (int G = 0; G < NG; ++G)
-      load_w16(W, ldw, d, k, row, cwave + 64 * G + 16 * q, w[G][0], w[G][1]);
+      for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 bh, bl;
+      bfrag(s, bh, bl);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bh),
+                                                         acc[e], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bl),
+                                                         acc[e], 0, 0, 0);
+      // With many rank steps, keep each step's operand loads next to their
+      // use: hoisting them all would exceed the register file.
+      if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  load_band(band_begin, wv, uh, ul);
-  for (int64_t band = band_begin; band < band_end; ++band) {
-    const bool more = band + 1 < band_end;
-    if (PREFETCH && more) load_band(band + 1, wn, nh, nl);
-    const int64_t row = band * kMergeBand + n;
+  // Guarded register path for one band (row or column edge).
+  auto edge_band = [&](int64_t band) __attribute__((always_inline)) {
+    const int64_t row = band * 32 + n;
+    // An opaque copy of r: the rank bounds below are then not hoisted out of
+    // the band loop (all steps' bounds at once would not fit in registers).
+    int64_t rr = r;
+    asm volatile("" : "+s"(rr));
+    f32x16 acc[E];
+    mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+      float x[8];
+      const int64_t j0 = 16 * s + 8 * hw;
 #pragma unroll
-    for (int G = 0; G < NG; ++G) {
-      f32x4 acc[4];
+      for (int i = 0; i < 8; ++i) x[i] = (row < d && j0 + i < rr) ? U[row * rr + j0 + i] : 0.f;
+      split8(x, bh, bl);
+    });
+    if (row >= d) return;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(afrag[4 * G + jj][s]), as_bf16x8(uh[s]), acc[jj], 0, 0, 0);
-          acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(afrag[4 * G + jj][s]), as_bf16x8(ul[s]), acc[jj], 0, 0, 0);
-        }
-      }
-      const int64_t c = cwave + 64 * G + 16 * q;
-      if (row >= d || c >= k) continue;
-      // Element t of the lane's 16 columns is C[m = 4q + (t & 3)] of
-      // instance jj = t >> 2: acc[t >> 2][t & 3].
-      const uint64_t e0 = (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)c;
-      Philox4 p0, p1;
-      if (stochastic) {
-        p0 = sr_block(srk, e0 >> 4);
-        p1 = (((e0 + 15) >> 4) != (e0 >> 4)) ? sr_block(srk, (e0 + 15) >> 4) : p0;
-      }
-      uint32_t out[8];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const uint32_t word = wv[G][t >> 3][(t & 7) >> 1];
-        const uint32_t wbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
-        const float x = __builtin_fmaf(-sc, acc[t >> 2][t & 3], bf16_bits_to_f32(wbits));
-        uint32_t o;
-        if (stochastic) {
-          const uint64_t ee = e0 + t;
-          const uint32_t u = ((ee >> 4) == (e0 >> 4)) ? sr_draw(p0, ee) : sr_draw(p1, ee);
-          o = f32_to_bf16_sr(x, u);
-        } else {
-          o = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
-        }
-        if (t & 1)
-          out[t >> 1] |= o << 16;
-        else
-          out[t >> 1] = o;
-      }
+    for (int e = 0; e < E; ++e) {
+      const int64_t c = cw + 32 * e + 16 * hw;
+      if (c >= k) continue;
+      u32x4 w0, w1, o0, o1;
+      load_w16(W, ldw, d, k, row, c, w0, w1);
+      update16<STOCH>(w0, w1, acc[e], sc, srk,
+                      (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)c, o0, o1);
       if (c + 16 <= k) {
         u32x4* dst = reinterpret_cast<u32x4*>(W + row * ldw + c);
-        dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-        dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+        dst[0] = o0;
+        dst[1] = o1;
       } else {
-        for (int t = 0; t < 16 && c + t < k; ++t)
-          W[row * ldw + c + t] = (uint16_t)((out[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+        for (int t = 0; t < 16 && c + t < k; ++t) {
+          const uint32_t word = (t < 8) ? o0[t >> 1] : o1[(t - 8) >> 1];
+          W[row * ldw + c + t] = (uint16_t)((t & 1) ? (word >> 16) : (word & 0xFFFFu));
+        }
       }
     }
-    if (more) {
-      if (PREFETCH) {
-#pragma unroll
-        for (int G = 0; G < NG; ++G) {
-          wv[G][0] = wn[G][0];
-          wv[G][1] = wn[G][1];
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          uh[s] = nh[s];
-          ul[s] = nl[s];
-        }
-      } else {
-        load_band(band + 1, wv, uh, ul);
-      }
-    }
+  };
+
+  // Interior bands: [band_begin, fast_end) when the block is column-interior
+  // and U rows are 16-byte aligned; the rest take the guarded path.
+  int64_t fast_end = band_begin;
+  if (col_interior && u_dma) {
+    fast_end = band_end;
+    if (fast_end * 32 > d) --fast_end;  // the partial last band of W
   }
+
+  if (fast_end > band_begin) {
+    // Loads of band b into buffer b & 1: W rows as whole 16E-chunk segments
+    // (lane L of a load covers row a = a0 + L / CH, LDS position L % CH,
+    // global chunk (L % CH) ^ (a & (CH - 1))), then U in operand order
+    // (load (s, q) gives lane L row L & 31, ranks 16s + 8(L>>5) + 4q ..+3).
+    constexpr int RPL = 64 / CH;              // W rows per 1 KiB load
+    constexpr int WL = 32 / RPL / NWV;        // W loads per wave per band
+    constexpr int UL = (2 * KS + NWV - 1) / NWV;  // U loads per wave per band
+    static_assert(WL * RPL * NWV == 32, "W loads must cover the band");
+    auto issue = [&](int64_t band) __attribute__((always_inline)) {
+      u32x4* wt = lds + (band & 1) * WT;
+      u32x4* ut = lds + 2 * WT + (band & 1) * UT;
+#pragma unroll
+      for (int t = 0; t < WL; ++t) {
+        const int a = (wave * WL + t) * RPL + lane / CH;
+        const int pos = lane % CH;
+        const int chunk = pos ^ (a & (CH - 1));
+        dma16(W + (band * 32 + a) * ldw + cblk + 8 * chunk, wt + (wave * WL + t) * 64);
+      }
+#pragma unroll
+      for (int t = 0; t < UL; ++t) {
+        int li = wave + NWV * t;
+        if (li > 2 * KS - 1) li = 2 * KS - 1;   // repeat a load: same bytes, same place
+        const int s = li >> 1, q = li & 1;
+        int64_t j = 16 * s + 8 * hw + 4 * q;
+        if (j + 4 > r) j = r - 4;                // ranks past r: any in-bounds chunk, zeroed later
+        const int64_t row = band * 32 + n;
+        dma16(U + row * r + j, ut + li * 64);
+      }
+    };
+    constexpr int UR = 2 * KS < 8 ? 2 * KS : 8;   // U slabs per read statement
+    issue(band_begin);
+    for (int64_t band = band_begin; band < fast_end; ++band) {
+      // Wait for this band's loads (the previous band's stores, issued after
+      // them, may still be in flight); then every wave's share has landed.
+      if (band == band_begin)
+        merge_wait_vmcnt<0>();
+      else
+        merge_wait_vmcnt<WL>();
+      merge_barrier();
+      const u32x4* wt = lds + (band & 1) * WT;
+      const u32x4* ut = lds + 2 * WT + (band & 1) * UT;
+      // This lane's W chunks: columns 32e + 16hw .. +15 of row n are chunks
+      // cc, cc + 1 with cc = 4(E wave + e) + 2hw.
+      uint32_t wa[2 * E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int cc = 4 * (E * wave + e) + 2 * hw;
+        wa[2 * e] = lds_u32(wt + n * CH + (cc ^ (n & (CH - 1))));
+        wa[2 * e + 1] = lds_u32(wt + n * CH + ((cc + 1) ^ (n & (CH - 1))));
+      }
+      u32x4 wx[2 * E];
+      lds_read_at(wa, wx);
+      u32x4 ux[2 * KS];
+#pragma unroll
+      for (int g0 = 0; g0 < 2 * KS; g0 += UR) {
+        u32x4 part[UR];
+        lds_read_slabs<UR>(lds_u32(ut + g0 * 64 + lane), part);
+#pragma unroll
+        for (int i = 0; i < UR; ++i) ux[g0 + i] = part[i];
+      }
+      // The other buffer is free (its stores' reads finished before the last
+      // barrier): start the next band's loads.
+      if (band + 1 < fast_end) issue(band + 1);
+      int rr = (int)r;  // opaque per band: the rank bounds are not hoisted
+      asm volatile("" : "+s"(rr));
+      f32x16 acc[E];
+      mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+        float x[8];
+        // (Copy each component to a scalar before the bit cast: a bit cast of
+        // a vector-element lvalue is not compiled as the element here.)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t b0 = ux[2 * s][i], b1 = ux[2 * s + 1][i];
+          x[i] = __builtin_bit_cast(float, b0);
+          x[4 + i] = __builtin_bit_cast(float, b1);
+        }
+        if (!r_full) {
+          const int j0 = 16 * s + 8 * hw;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (j0 + i >= rr) x[i] = 0.f;
+        }
+        split8(x, bh, bl);
+      });
+      const int64_t row = band * 32 + n;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        u32x4 o0, o1;
+        update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk,
+                        (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw),
+                        o0, o1);
+        lds_write16(wa[2 * e], o0);
+        lds_write16(wa[2 * e + 1], o1);
+      }
+      lds_wait();
+      merge_barrier();  // the whole tile is updated
+      // Whole-row stores, in the load's lane order.
+      u32x4 ov[WL];
+      lds_read_slabs<WL>(lds_u32(wt + (wave * WL) * 64 + lane), ov);
+#pragma unroll
+      for (int t = 0; t < WL; ++t) {
+        const int a = (wave * WL + t) * RPL + lane / CH;
+        const int pos = lane % CH;
+        const int chunk = pos ^ (a & (CH - 1));
+        *reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk) = ov[t];
+      }
+      merge_barrier();  // every wave has read the tile before it is reloaded
+    }
+    merge_wait_vmcnt<0>();
+  }
+  for (int64_t band = fast_end; band < band_end; ++band) edge_band(band);
 }
 
 // fp32 W: a block owns 16 rows x one 256-column Philox block; signs in LDS
@@ -314,30 +529,34 @@ hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bo
                        static_cast<float*>(W), ldw, U, scale * cr, scale_dev);
     return hipGetLastError();
   }
-  const int64_t ksteps = (r + 31) / 32;
-  const int ks = ksteps <= 1 ? 1 : ksteps <= 2 ? 2 : ksteps <= 4 ? 4 : 8;
-  const int ng = ks <= 2 ? 2 : 1;
-  const int64_t bc = 256 * ng;
+  const int64_t ksteps = (r + 15) / 16;
+  const int ks = ksteps <= 1 ? 1 : ksteps <= 2 ? 2 : ksteps <= 4 ? 4 : ksteps <= 8 ? 8 : 16;
+  const int e = ks <= 4 ? 2 : 1;
+  const int64_t bc = 32 * kMergeWaves * e;
   const int64_t ncb = (k + bc - 1) / bc;
-  const int64_t nbands = (d + kMergeBand - 1) / kMergeBand;
+  const int64_t nbands = (d + 31) / 32;
   // Enough blocks to fill the chip several times over, each with a few bands
   // to amortise the sign setup.
-  int64_t per = (nbands * ncb + 2047) / 2048;
+  int64_t per = (nbands * ncb + 1023) / 1024;
   if (per < 4) per = 4;
   if (per > nbands) per = nbands;
   const int64_t groups = (nbands + per - 1) / per;
   const dim3 grid((unsigned)(ncb * groups));
   uint16_t* Wb = static_cast<uint16_t*>(W);
   const float scf = (float)(scale * cr);
-  const int st = stochastic ? 1 : 0;
-#define LOGRA_MERGE_LAUNCH(KS, NG, PF)                                                      \
-  hipLaunchKernelGGL((merge_bf16_kernel<KS, NG, PF>), grid, dim3(256), 0, s, key, d, k, r, \
-                     Wb, ldw, U, scf, scale_dev, st, sr_key, row0, ncb, per)
+#define LOGRA_MERGE_LAUNCH(KS, E)                                                               \
+  if (stochastic)                                                                               \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true>), grid, dim3(kMergeWaves * 64), 0, s, key, \
+                       d, k, r, Wb, ldw, U, scf, scale_dev, sr_key, row0, ncb, per);            \
+  else                                                                                          \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false>), grid, dim3(kMergeWaves * 64), 0, s,     \
+                       key, d, k, r, Wb, ldw, U, scf, scale_dev, sr_key, row0, ncb, per);
   switch (ks) {
-    case 1: LOGRA_MERGE_LAUNCH(1, 2, true); break;
-    case 2: LOGRA_MERGE_LAUNCH(2, 2, true); break;
-    case 4: LOGRA_MERGE_LAUNCH(4, 1, true); break;
-    case 8: LOGRA_MERGE_LAUNCH(8, 1, false); break;
+    case 1: LOGRA_MERGE_LAUNCH(1, 2) break;
+    case 2: LOGRA_MERGE_LAUNCH(2, 2) break;
+    case 4: LOGRA_MERGE_LAUNCH(4, 2) break;
+    case 8: LOGRA_MERGE_LAUNCH(8, 1) break;
+    case 16: LOGRA_MERGE_LAUNCH(16, 1) break;
     default: return hipErrorInvalidValue;
   }
 #undef LOGRA_MERGE_LAUNCH
