@@ -7,7 +7,8 @@ One step = one update over the whole layer set of the workload:
      of one layer and one microbatch per launch -- one kernel per launch)
   C. RowAdam for every sketch, predicted-KL q over the context set, alpha on
      the device
-  D. merge every matrix, W <- round(W - eta*alpha U A)
+  D. merge every matrix, W <- round(W - eta*alpha U A) (grouped: the seven
+     matrices of one layer per launch)
 Inputs are synthetic and resident in HBM before timing starts (distinct
 buffers for every layer and microbatch, so the 256 MB Infinity Cache cannot
 serve them).  The metric is HBM GB/s of phases B + D: their algorithmic bytes
@@ -257,9 +258,9 @@ def main():
         B.predicted_kl_q(z, zd, w.tau, out=q, ws=kl_ws)
         B.step_alpha_dev(q, w.delta, w.alpha_max, out=alpha)
         ev[3].record()
-        for key_ in S:                               # D: merge
-            B.merge(keys[key_], W[key_], U[key_], w.eta, scale_dev=alpha, mode=rounding,
-                    sr_seed=w.sr_seed)
+        for l in range(layers):                      # D: merge (one launch per layer)
+            B.merge_grouped([(keys[(l, kind)], W[(l, kind)], U[(l, kind)]) for (kind, d, k) in by_layer[l]],
+                            w.eta, scale_dev=alpha, mode=rounding, sr_seed=w.sr_seed)
         ev[4].record()
 
     def events():

@@ -294,6 +294,27 @@ LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r,
                           double scale, const float* scale_dev, logra_round mode,
                           uint64_t sr_seed, int64_t row0, logra_stream stream);
 
+typedef struct logra_merge_desc {
+  logra_key key;       /* key of this matrix's A                        */
+  void* W;             /* [d x k] bf16, row-major, leading dimension ldw */
+  int64_t d;
+  int64_t k;
+  int64_t ldw;
+  const float* U;      /* [d x r] fp32 contiguous                        */
+  int64_t row0;        /* global index of W's first row                  */
+} logra_merge_desc;
+
+/* Grouped form of logra_merge for bf16 W: n <= LOGRA_MAX_GROUP merges that
+ * share r, the scale (scale, scale_dev), the rounding mode and sr_seed, in
+ * one launch (e.g. the seven projections of one layer).  Each descriptor's
+ * result has the same bits as the single call with its key, W, d, k, ldw,
+ * U and row0.  The descriptor array is read on the host during the call.
+ * Errors: as logra_merge for each descriptor; n < 1 or n > LOGRA_MAX_GROUP;
+ * a W overlapping another descriptor's W or any U. */
+LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int n, double scale,
+                                  const float* scale_dev, logra_round mode, uint64_t sr_seed,
+                                  logra_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

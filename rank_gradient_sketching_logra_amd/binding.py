@@ -36,6 +36,11 @@ class AccPackedDesc(Structure):
                 ("ldd", c_int64)]
 
 
+class MergeDesc(Structure):
+    _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
+                ("U", c_void_p), ("row0", c_int64)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -61,6 +66,8 @@ SIGNATURES = {
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_step_alpha": (c_int, [c_double, c_double, c_double, POINTER(c_double)]),
     "logra_step_alpha_dev": (c_int, [c_void_p, c_float, c_float, c_void_p, c_void_p]),
+    "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
+                                    c_uint64, c_void_p]),
     "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                             c_void_p, c_double, c_void_p, c_int, c_uint64, c_int64, c_void_p]),
 }
@@ -267,3 +274,20 @@ def merge(k_: Key, W: torch.Tensor, U: torch.Tensor, scale: float, scale_dev=Non
     _check(lib().logra_merge(ctypes.byref(k_), d, kk, r, _ptr(W), _dtype_code(W), _ld(W), _ptr(U),
                              float(scale), _ptr(scale_dev), m, sr_seed, row0, _stream(W, stream)))
     return W
+
+
+def merge_grouped(items, scale: float, scale_dev=None, mode: str = "nearest", sr_seed: int = 0,
+                  stream=None):
+    """items: sequence of (key, W, U) or (key, W, U, row0) with bf16 W sharing r; one launch."""
+    n = len(items)
+    r = items[0][2].shape[1]
+    descs = (MergeDesc * n)()
+    for i, it in enumerate(items):
+        k_, W, U = it[0], it[1], it[2]
+        row0 = it[3] if len(it) > 3 else 0
+        if U.shape[1] != r:
+            raise ValueError("every U must be [d x r] with the same r")
+        descs[i] = MergeDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), U.data_ptr(), row0)
+    m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
+    _check(lib().logra_merge_grouped(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
+                                     _stream(items[0][1], stream)))

@@ -51,6 +51,17 @@ hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void
 hipError_t launch_step_alpha(const float* q, float delta, float amax, float* alpha,
                              hipStream_t s);
 
+struct MergeItem {
+  KeyArg key;      // sign key of the matrix
+  KeyArg sr_key;   // stochastic-rounding key of the matrix
+  void* W;         // [d x k] bf16, leading dimension ldw
+  int64_t d, k, ldw;
+  const float* U;  // [d x r] fp32
+  int64_t row0;
+};
+// Several bf16 merges sharing r, the scale and the rounding mode in one launch.
+hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,
+                                const float* scale_dev, bool stochastic, hipStream_t s);
 hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
                         int64_t ldw, const float* U, double scale, const float* scale_dev,
                         bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s);

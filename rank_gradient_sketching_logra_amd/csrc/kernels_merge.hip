@@ -200,20 +200,53 @@ __device__ __forceinline__ void merge_barrier() {
 // register loads and stores.
 constexpr int kMergeWaves = 8;
 
+struct MergeGroupArgs {
+  KeyArg key[kMaxGroup];
+  KeyArg sr_key[kMaxGroup];
+  uint16_t* W[kMaxGroup];
+  const float* U[kMaxGroup];
+  int64_t d[kMaxGroup];
+  int64_t k[kMaxGroup];
+  int64_t ldw[kMaxGroup];
+  int64_t row0[kMaxGroup];
+  int64_t ncb[kMaxGroup];                 // column blocks of each matrix
+  int64_t block_begin[kMaxGroup + 1];     // first block of each matrix
+  int n;
+  int64_t r;
+  int64_t per;                            // bands per block
+  float scale_cr;
+  const float* scale_dev;
+};
+
 template <int KS, int E, bool STOCH>
-__global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
-    KeyArg key, int64_t d, int64_t k, int64_t r, uint16_t* __restrict__ W, int64_t ldw,
-    const float* __restrict__ U, float scale_cr, const float* __restrict__ scale_dev,
-    KeyArg sr_key, int64_t row0, int64_t ncb, int64_t bands_per_block) {
+__global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGroupArgs g) {
+  // The matrix of this block (several share one launch).
+  if ((int64_t)blockIdx.x >= g.block_begin[g.n]) return;
+  int item = 0;
+  while ((int64_t)blockIdx.x >= g.block_begin[item + 1]) ++item;
+  const KeyArg key = g.key[item];
+  const KeyArg sr_key = g.sr_key[item];
+  uint16_t* __restrict__ W = g.W[item];
+  const float* __restrict__ U = g.U[item];
+  const int64_t d = g.d[item], k = g.k[item], ldw = g.ldw[item], row0 = g.row0[item];
+  const int64_t ncb = g.ncb[item];
+  const int64_t r = g.r;
+  const int64_t bands_per_block = g.per;
+  const float scale_cr = g.scale_cr;
+  const float* __restrict__ scale_dev = g.scale_dev;
+  const int64_t local = (int64_t)blockIdx.x - g.block_begin[item];
   constexpr int NWV = kMergeWaves;
   constexpr int BC = 32 * NWV * E;        // columns per block
   constexpr int NWd = BC / 32;            // sign words per rank
   constexpr int CH = BC / 8;              // 16-byte chunks per tile row
   constexpr int WT = 32 * BC / 8;         // 16-byte chunks per W tile (32 rows)
   constexpr int UT = 32 * KS * 4;         // 16-byte chunks per U band (operand order)
-  // LDS: two W tiles, then two U bands; the sign bits live in the second W
-  // tile until the A operands are built.
-  __shared__ __align__(16) u32x4 lds[2 * WT + 2 * UT];
+  constexpr int NR = KS >= 16 ? 2 : 3;    // bands in the LDS ring
+  constexpr int SLOT = WT + UT;           // one band: W tile, then fp32 U
+  // LDS: a ring of NR bands, then the band's U as bf16 hi/lo operands (KS
+  // hi slabs, KS lo slabs).  The sign bits live in the ring until the A
+  // operands are built.
+  __shared__ __align__(16) u32x4 lds[NR * SLOT + UT];
   static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
@@ -221,8 +254,8 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;     // W row within the band (B and C layouts)
   const int hw = lane >> 5;
-  const int64_t cb = blockIdx.x % ncb;
-  const int64_t bg = blockIdx.x / ncb;
+  const int64_t cb = local % ncb;
+  const int64_t bg = local / ncb;
   const int64_t cblk = cb * BC;
   const int64_t nbands = (d + 31) / 32;
   const int64_t band_begin = bg * bands_per_block;
@@ -232,7 +265,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
 
   // Sign bits of ranks [0, 16 KS) for the block's columns: word w of rank j
   // holds columns cblk + 32w + (0..31), bit set meaning -1.
-  uint32_t* sbits = reinterpret_cast<uint32_t*>(lds + WT);
+  uint32_t* sbits = reinterpret_cast<uint32_t*>(lds);
   {
     const KeyWords kw{key.k0, key.k1};
     constexpr int NP = (BC + 255) / 256;  // Philox blocks per rank
@@ -290,7 +323,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
       }
     }
   }
-  __syncthreads();  // the sign bits are dead; their tile may be loaded
+  __syncthreads();  // the sign bits are dead; the ring may be loaded
 
   float sc = scale_cr;
   if (scale_dev != nullptr) sc *= *scale_dev;
@@ -370,17 +403,22 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
   }
 
   if (fast_end > band_begin) {
-    // Loads of band b into buffer b & 1: W rows as whole 16E-chunk segments
-    // (lane L of a load covers row a = a0 + L / CH, LDS position L % CH,
-    // global chunk (L % CH) ^ (a & (CH - 1))), then U in operand order
-    // (load (s, q) gives lane L row L & 31, ranks 16s + 8(L>>5) + 4q ..+3).
+    // Loads of band b into ring slot b % NR: W rows as whole 16E-chunk
+    // segments (lane L of a load covers row a = a0 + L / CH, LDS position
+    // L % CH, global chunk (L % CH) ^ (a & (CH - 1))), then U in operand
+    // order (load (s, q) gives lane L row L & 31, ranks 16s + 8(L>>5) + 4q
+    // .. +3).  Two bands are in flight while one computes.
     constexpr int RPL = 64 / CH;              // W rows per 1 KiB load
-    constexpr int WL = 32 / RPL / NWV;        // W loads per wave per band
+    constexpr int WL = 32 / RPL / NWV;        // W loads (and stores) per wave per band
     constexpr int UL = (2 * KS + NWV - 1) / NWV;  // U loads per wave per band
+    constexpr int LB = WL + UL;               // loads per wave per band
     static_assert(WL * RPL * NWV == 32, "W loads must cover the band");
+    auto slot_of = [&](int64_t band) __attribute__((always_inline)) {
+      return lds + (int)((band - band_begin) % NR) * SLOT;
+    };
     auto issue = [&](int64_t band) __attribute__((always_inline)) {
-      u32x4* wt = lds + (band & 1) * WT;
-      u32x4* ut = lds + 2 * WT + (band & 1) * UT;
+      u32x4* wt = slot_of(band);
+      u32x4* ut = wt + WT;
 #pragma unroll
       for (int t = 0; t < WL; ++t) {
         const int a = (wave * WL + t) * RPL + lane / CH;
@@ -399,18 +437,68 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
         dma16(U + row * r + j, ut + li * 64);
       }
     };
-    constexpr int UR = 2 * KS < 8 ? 2 * KS : 8;   // U slabs per read statement
-    issue(band_begin);
+    // Wait until this wave's loads of band b have landed, given how many
+    // vector-memory operations it issued after them (see the loop).
+    auto wait_band = [&](int64_t band) __attribute__((always_inline)) {
+      const int64_t i = band - band_begin;
+      if constexpr (NR == 3) {
+        const bool more1 = band + 1 < fast_end;
+        if (i == 0) {
+          if (more1) merge_wait_vmcnt<LB>(); else merge_wait_vmcnt<0>();
+        } else if (i == 1) {
+          if (more1) merge_wait_vmcnt<LB + WL>(); else merge_wait_vmcnt<WL>();
+        } else {
+          if (more1) merge_wait_vmcnt<2 * WL + LB>(); else merge_wait_vmcnt<2 * WL>();
+        }
+      } else {
+        if (i == 0) merge_wait_vmcnt<0>(); else merge_wait_vmcnt<WL>();
+      }
+    };
+    u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
+#pragma unroll
+    for (int t = 0; t < NR - 1; ++t)
+      if (band_begin + t < fast_end) issue(band_begin + t);
     for (int64_t band = band_begin; band < fast_end; ++band) {
-      // Wait for this band's loads (the previous band's stores, issued after
-      // them, may still be in flight); then every wave's share has landed.
-      if (band == band_begin)
-        merge_wait_vmcnt<0>();
-      else
-        merge_wait_vmcnt<WL>();
-      merge_barrier();
-      const u32x4* wt = lds + (band & 1) * WT;
-      const u32x4* ut = lds + 2 * WT + (band & 1) * UT;
+      // Issue order per wave: loads(b0) .. loads(b0 + NR - 2), then per band
+      // j: loads(j + NR - 1), stores(j).
+      wait_band(band);
+      merge_barrier();  // every wave's loads of this band have landed, and the
+                        // slot of band - 1 is no longer read
+      if (band + NR - 1 < fast_end) issue(band + NR - 1);
+      u32x4* wt = slot_of(band);
+      const u32x4* ut = wt + WT;
+      // Split U once per band: wave w converts fp32 slabs w, w + NWV, ...
+      // (step s, half q) into halves of the hi and lo operands of step s.
+      {
+        int rr = (int)r;  // opaque: the rank bounds are not hoisted
+        asm volatile("" : "+s"(rr));
+        for (int li = wave; li < 2 * KS; li += NWV) {
+          u32x4 xv[1];
+          lds_read_slabs<1>(lds_u32(ut + li * 64 + lane), xv);
+          const int s = li >> 1, q = li & 1;
+          const int j0 = 16 * s + 8 * hw + 4 * q;
+          float h[4], l[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t bits = xv[0][i];
+            float x = __builtin_bit_cast(float, bits);
+            if (!r_full && j0 + i >= rr) x = 0.f;
+            h[i] = (float)(__bf16)x;
+            l[i] = x - h[i];
+          }
+          const uint32_t hi0 = bf16_pair(h[0], h[1]), hi1 = bf16_pair(h[2], h[3]);
+          const uint32_t lo0 = bf16_pair(l[0], l[1]), lo1 = bf16_pair(l[2], l[3]);
+          const uint32_t ah = lds_u32(bs + s * 64 + lane) + 8 * q;
+          const uint32_t al = lds_u32(bs + (KS + s) * 64 + lane) + 8 * q;
+          asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3"
+                       :
+                       : "v"(ah), "v"(hi0 | ((uint64_t)hi1 << 32)), "v"(al),
+                         "v"(lo0 | ((uint64_t)lo1 << 32))
+                       : "memory");
+        }
+      }
+      lds_wait();
+      merge_barrier();  // the band's operands are split
       // This lane's W chunks: columns 32e + 16hw .. +15 of row n are chunks
       // cc, cc + 1 with cc = 4(E wave + e) + 2hw.
       uint32_t wa[2 * E];
@@ -422,37 +510,13 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
       }
       u32x4 wx[2 * E];
       lds_read_at(wa, wx);
-      u32x4 ux[2 * KS];
-#pragma unroll
-      for (int g0 = 0; g0 < 2 * KS; g0 += UR) {
-        u32x4 part[UR];
-        lds_read_slabs<UR>(lds_u32(ut + g0 * 64 + lane), part);
-#pragma unroll
-        for (int i = 0; i < UR; ++i) ux[g0 + i] = part[i];
-      }
-      // The other buffer is free (its stores' reads finished before the last
-      // barrier): start the next band's loads.
-      if (band + 1 < fast_end) issue(band + 1);
-      int rr = (int)r;  // opaque per band: the rank bounds are not hoisted
-      asm volatile("" : "+s"(rr));
       f32x16 acc[E];
       mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
-        float x[8];
-        // (Copy each component to a scalar before the bit cast: a bit cast of
-        // a vector-element lvalue is not compiled as the element here.)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t b0 = ux[2 * s][i], b1 = ux[2 * s + 1][i];
-          x[i] = __builtin_bit_cast(float, b0);
-          x[4 + i] = __builtin_bit_cast(float, b1);
-        }
-        if (!r_full) {
-          const int j0 = 16 * s + 8 * hw;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (j0 + i >= rr) x[i] = 0.f;
-        }
-        split8(x, bh, bl);
+        u32x4 hl[1];
+        lds_read_slabs<1>(lds_u32(bs + s * 64 + lane), hl);
+        bh = hl[0];
+        lds_read_slabs<1>(lds_u32(bs + (KS + s) * 64 + lane), hl);
+        bl = hl[0];
       });
       const int64_t row = band * 32 + n;
 #pragma unroll
@@ -476,7 +540,6 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(
         const int chunk = pos ^ (a & (CH - 1));
         *reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk) = ov[t];
       }
-      merge_barrier();  // every wave has read the tile before it is reloaded
     }
     merge_wait_vmcnt<0>();
   }
@@ -519,38 +582,74 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(KeyArg key, int64_t d, i
 
 }  // namespace
 
-hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
-                        int64_t ldw, const float* U, double scale, const float* scale_dev,
-                        bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s) {
-  const double cr = 1.0 / std::sqrt((double)r);
-  if (!bf16) {
-    const dim3 grid((unsigned)((k + 255) / 256), (unsigned)((d + 15) / 16));
-    hipLaunchKernelGGL(merge_f32_kernel, grid, dim3(256), 0, s, key, d, k, r,
-                       static_cast<float*>(W), ldw, U, scale * cr, scale_dev);
-    return hipGetLastError();
+// Compute units of the current device (queried once per device).
+static int64_t compute_units() {
+  static int64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cached[dev] = n;
   }
+  return cached[dev];
+}
+
+hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,
+                                const float* scale_dev, bool stochastic, hipStream_t s) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  const double cr = 1.0 / std::sqrt((double)r);
   const int64_t ksteps = (r + 15) / 16;
   const int ks = ksteps <= 1 ? 1 : ksteps <= 2 ? 2 : ksteps <= 4 ? 4 : ksteps <= 8 ? 8 : 16;
   const int e = ks <= 4 ? 2 : 1;
   const int64_t bc = 32 * kMergeWaves * e;
-  const int64_t ncb = (k + bc - 1) / bc;
-  const int64_t nbands = (d + 31) / 32;
-  // Enough blocks to fill the chip several times over, each with a few bands
-  // to amortise the sign setup.
-  int64_t per = (nbands * ncb + 1023) / 1024;
+  MergeGroupArgs g{};
+  g.n = n;
+  g.r = r;
+  g.scale_cr = (float)(scale * cr);
+  g.scale_dev = scale_dev;
+  int64_t units = 0, maxbands = 1;
+  for (int i = 0; i < n; ++i) {
+    g.key[i] = items[i].key;
+    g.sr_key[i] = items[i].sr_key;
+    g.W[i] = static_cast<uint16_t*>(items[i].W);
+    g.U[i] = items[i].U;
+    g.d[i] = items[i].d;
+    g.k[i] = items[i].k;
+    g.ldw[i] = items[i].ldw;
+    g.row0[i] = items[i].row0;
+    g.ncb[i] = (items[i].k + bc - 1) / bc;
+    const int64_t nb = (items[i].d + 31) / 32;
+    units += nb * g.ncb[i];
+    maxbands = std::max(maxbands, nb);
+  }
+  // At most one block per compute unit over the whole group (a second round
+  // of blocks would double the time of the matrices it holds), each a run of
+  // bands of one column block: the sign setup is amortised and the band ring
+  // stays full.
+  const int64_t cus = compute_units();
+  auto blocks_for = [&](int64_t p) {
+    int64_t b = 0;
+    for (int i = 0; i < n; ++i) b += g.ncb[i] * (((items[i].d + 31) / 32 + p - 1) / p);
+    return b;
+  };
+  int64_t per = (units + cus - 1) / cus;
   if (per < 4) per = 4;
-  if (per > nbands) per = nbands;
-  const int64_t groups = (nbands + per - 1) / per;
-  const dim3 grid((unsigned)(ncb * groups));
-  uint16_t* Wb = static_cast<uint16_t*>(W);
-  const float scf = (float)(scale * cr);
+  while (per < maxbands && blocks_for(per) > cus) ++per;
+  if (per > maxbands) per = maxbands;
+  g.per = per;
+  g.block_begin[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nb = (items[i].d + 31) / 32;
+    g.block_begin[i + 1] = g.block_begin[i] + g.ncb[i] * ((nb + per - 1) / per);
+  }
+  const dim3 grid((unsigned)g.block_begin[n]);
 #define LOGRA_MERGE_LAUNCH(KS, E)                                                               \
   if (stochastic)                                                                               \
-    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true>), grid, dim3(kMergeWaves * 64), 0, s, key, \
-                       d, k, r, Wb, ldw, U, scf, scale_dev, sr_key, row0, ncb, per);            \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true>), grid, dim3(kMergeWaves * 64), 0, s, g); \
   else                                                                                          \
-    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false>), grid, dim3(kMergeWaves * 64), 0, s,     \
-                       key, d, k, r, Wb, ldw, U, scf, scale_dev, sr_key, row0, ncb, per);
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false>), grid, dim3(kMergeWaves * 64), 0, s, g);
   switch (ks) {
     case 1: LOGRA_MERGE_LAUNCH(1, 2) break;
     case 2: LOGRA_MERGE_LAUNCH(2, 2) break;
@@ -561,6 +660,20 @@ hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bo
   }
 #undef LOGRA_MERGE_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
+                        int64_t ldw, const float* U, double scale, const float* scale_dev,
+                        bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s) {
+  if (!bf16) {
+    const double cr = 1.0 / std::sqrt((double)r);
+    const dim3 grid((unsigned)((k + 255) / 256), (unsigned)((d + 15) / 16));
+    hipLaunchKernelGGL(merge_f32_kernel, grid, dim3(256), 0, s, key, d, k, r,
+                       static_cast<float*>(W), ldw, U, scale * cr, scale_dev);
+    return hipGetLastError();
+  }
+  const MergeItem it{key, sr_key, W, d, k, ldw, U, row0};
+  return launch_merge_grouped(&it, 1, r, scale, scale_dev, stochastic, s);
 }
 
 }  // namespace logra

@@ -290,6 +290,39 @@ LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_
                     "step_alpha_dev launch");
 }
 
+LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int n, double scale,
+                                  const float* scale_dev, logra_round mode, uint64_t sr_seed,
+                                  logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  if (bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "merge_grouped: unknown rounding mode");
+  if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "merge_grouped: scale must be finite");
+  logra::MergeItem items[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    const logra_merge_desc& e = descs[i];
+    if (!e.W || !e.U) return fail(LOGRA_ERR_NULL, "merge_grouped: NULL pointer in descriptor %d", i);
+    if (e.d < 1 || e.k < 1 || e.row0 < 0) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need d, k >= 1 and row0 >= 0");
+    int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.k);
+    if (st) return st;
+    if (!aligned16(e.U)) return fail(LOGRA_ERR_ALIGN, "merge_grouped: U not 16-byte aligned");
+    const Range rw = range(e.W, extent(e.d, e.k, e.ldw, 2));
+    if (scale_dev && overlap(rw, range(scale_dev, 4))) return fail(LOGRA_ERR_ALIAS, "merge_grouped: W overlaps the device scale");
+    for (int j = 0; j <= i; ++j) {
+      if (overlap(rw, range(descs[j].U, (size_t)(descs[j].d * r) * 4)) ||
+          (j < i && overlap(rw, range(descs[j].W, extent(descs[j].d, descs[j].k, descs[j].ldw, 2)))))
+        return fail(LOGRA_ERR_ALIAS, "merge_grouped: W of descriptor %d overlaps an operand of %d", i, j);
+      if (j < i && overlap(range(e.U, (size_t)(e.d * r) * 4), range(descs[j].W, extent(descs[j].d, descs[j].k, descs[j].ldw, 2))))
+        return fail(LOGRA_ERR_ALIAS, "merge_grouped: U of descriptor %d overlaps W of %d", i, j);
+    }
+    items[i] = logra::MergeItem{key_words(e.key.seed, &e.key), key_words(sr_seed, &e.key), e.W, e.d, e.k,
+                                e.ldw, e.U, e.row0};
+  }
+  return hip_status(logra::launch_merge_grouped(items, n, r, scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
+                                                static_cast<hipStream_t>(stream)),
+                    "merge_grouped launch");
+}
+
 LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r, void* W,
                           logra_dtype w_dtype, int64_t ldw, const float* U, double scale,
                           const float* scale_dev, logra_round mode, uint64_t sr_seed,

@@ -149,6 +149,24 @@ def test_packed_sizes_and_validation(lib):
     assert err(g, 128, 64, d1, 1, None) == B.ERR_ALIGN
 
 
+def test_merge_grouped_validation(lib):
+    f = lib.logra_merge_grouped
+    d2 = (B.MergeDesc * 2)(B.MergeDesc(key(), A, 64, 64, 64, Bp, 0), B.MergeDesc(key(), A + 4096, 64, 64, 64, C, 0))
+    assert err(f, 64, d2, 2, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # W overlap
+    assert err(f, 64, d2, 0, 1.0, None, 0, 0, None) == B.ERR_SHAPE
+    assert err(f, 64, d2, 17, 1.0, None, 0, 0, None) == B.ERR_SHAPE
+    assert err(f, 300, d2, 1, 1.0, None, 0, 0, None) == B.ERR_SHAPE
+    assert err(f, 64, d2, 1, float("inf"), None, 0, 0, None) == B.ERR_DOMAIN
+    assert err(f, 64, d2, 1, 1.0, None, 5, 0, None) == B.ERR_DOMAIN
+    assert err(f, 64, None, 1, 1.0, None, 0, 0, None) == B.ERR_NULL
+    d1 = (B.MergeDesc * 1)(B.MergeDesc(key(), A, 64, 64, 64, A + 512, 0))
+    assert err(f, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # U inside W
+    d1 = (B.MergeDesc * 1)(B.MergeDesc(key(), A, 64, 64, 64, Bp + 8, 0))
+    assert err(f, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
+    d2 = (B.MergeDesc * 2)(B.MergeDesc(key(), A, 64, 64, 64, Bp, 0), B.MergeDesc(key(), C, 64, 64, 64, A + 256, 0))
+    assert err(f, 64, d2, 2, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # U of 1 inside W of 0
+
+
 def test_rowadam_validation(lib):
     f = lib.logra_rowadam
     ws = B.rowadam_ws_bytes(64)

@@ -352,6 +352,35 @@ def test_merge_bf16(d, k, r, mode, ldw):
     assert exact >= 0.999
 
 
+@pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "nearest"), (256, "stochastic")])
+def test_merge_grouped_equals_single_merges(r, mode):
+    """One grouped launch over matrices of mixed shapes (full, ragged column and row edges, small)
+    gives the bits of separate merges, and each matches the oracle to the merge bar."""
+    shapes = [(320, 1024), (100, 712), (64, 3584), (96, 512)]
+    say(f"merge grouped r={r} {mode}")
+    items, singles, wants = [], [], []
+    for i, (d, k) in enumerate(shapes):
+        wb, W64 = bf16_inputs((d, k), 0.02, (19, d, k, i, 2))
+        U = synth.fp32_matrix((d, r), 1.0, (19, d, r, i, 7))
+        kk = B.key(11, 40 + i, 3)
+        W1 = bf16_dev(wb)
+        W2 = W1.clone()
+        Ud = torch.from_numpy(U).to(DEV)
+        items.append((kk, W1, Ud))
+        singles.append((kk, W2, Ud))
+        A = oracle.regen_A(11, 40 + i, 3, r, k)
+        u = philox.sr_draws(5, 40 + i, 3, d, k) if mode == "stochastic" else None
+        wants.append(oracle.merge(W64, U.astype(np.float64), A, 2e-4, w_dtype="bf16", mode=mode,
+                                  u_draws=u))
+    B.merge_grouped(items, 2e-4, mode=mode, sr_seed=5)
+    for kk, W2, Ud in singles:
+        B.merge(kk, W2, Ud, 2e-4, mode=mode, sr_seed=5)
+    for (_, W1, _), (_, W2, _), want in zip(items, singles, wants):
+        assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+        frac, exact = ulp_check(bf16_host(W1), want)
+        assert frac >= 0.9999 and exact >= 0.999
+
+
 def test_merge_rollout_sync_invariant_and_row_blocks():
     """Two merges of equal W with equal (U, key, scale, mode, sr_seed) are bit-identical;
     merging a row block with its global row offset equals the same rows of the whole merge."""
