@@ -452,38 +452,51 @@ def test_merge_fp32_unit_factor_and_values():
 
 
 def test_full_size_layer_sampled():
-    """One 7B-shaped layer (q, k, v, o, gate, up, down; r = 64; T = 4096) through the
-    grouped accumulate the benchmark times, checked on sampled rows of every S, and
-    the merge of the gate matrix checked on sampled rows."""
+    """One 7B-shaped layer (q, k, v, o, gate, up, down; r = 64; T = 4096) through the entry
+    points and launch configuration the benchmark times: projections straight into packed
+    operands, one grouped packed accumulate, one grouped merge with the step size on the
+    device.  S is checked on sampled rows of every matrix against the oracle's X A^T and
+    D^T (X A^T); W on sampled rows of every matrix."""
     w = synth.BY_NAME["qwen2.5-7b-set-r64"]
     T, r = w.T, w.r
-    say("full-size 7B layer, sampled")
+    say("full-size 7B layer, sampled (bench configuration)")
     rs = np.random.default_rng(25)
     items, host = [], []
     for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
+        xb = synth.layer_input(w, layer, kind, 0)
         db = synth.output_grad(w, layer, kind, 0)
-        XAt = synth.fp32_matrix((T, r), 7.5, (25, mid, 0, 0, 0))
         S0 = synth.fp32_matrix((d, r), 0.3, (25, mid, 0, 0, 5))
-        items.append((bf16_dev(db), torch.from_numpy(XAt).to(DEV), torch.from_numpy(S0.copy()).to(DEV)))
+        kk = B.key(w.seed, mid, w.step)
+        planes = B.project_input_packed(kk, bf16_dev(xb), r)
+        A = oracle.regen_A(w.seed, mid, w.step, r, k)
+        XAt = oracle.project(oracle.bf16_bits_to_f64(xb), A)
+        items.append((bf16_dev(db), planes, torch.from_numpy(S0.copy()).to(DEV)))
         host.append((db, XAt, S0, d))
-    B.sketch_accumulate_grouped(items)
+    B.sketch_accumulate_grouped_packed(items, r)
     for (db, XAt, S0, d), (_, _, S) in zip(host, items):
         rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 48)]))
         Dc = oracle.bf16_bits_to_f64(db[:, rows])
-        want = S0[rows].astype(np.float64) + Dc.T @ XAt.astype(np.float64)
+        want = S0[rows].astype(np.float64) + Dc.T @ XAt
         assert relfro(S.cpu().numpy()[rows], want) <= 5e-5
-    # merge of the gate matrix, sampled rows
-    d, k = w.shapes["gate"]
-    wbits = synth.weight(w, 0, "gate")
-    U = synth.fp32_matrix((d, r), 1.0, (25, 4, 0, 0, 7))
-    W = bf16_dev(wbits)
-    kk = B.key(w.seed, 4, w.step)
-    B.merge(kk, W, torch.from_numpy(U).to(DEV), 1e-3 * 0.5, mode="stochastic", sr_seed=w.sr_seed)
-    rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 32)]))
-    A = oracle.regen_A(w.seed, 4, w.step, r, k)
-    got = bf16_host(W)[rows]
-    u = np.concatenate([philox.sr_draws(w.sr_seed, 4, w.step, 1, k, row0=int(i)) for i in rows])
-    want = oracle.merge(oracle.bf16_bits_to_f64(wbits[rows]), U[rows].astype(np.float64), A, 5e-4,
-                        w_dtype="bf16", mode="stochastic", u_draws=u)
-    frac, exact = ulp_check(got, want)
-    assert frac >= 0.9999 and exact >= 0.999
+    del items
+    # the layer's grouped merge, step size on the device
+    alpha = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+    mitems, mhost = [], []
+    for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
+        wbits = synth.weight(w, layer, kind)
+        U = synth.fp32_matrix((d, r), 1.0, (25, mid, 0, 0, 7))
+        mitems.append((B.key(w.seed, mid, w.step), bf16_dev(wbits), torch.from_numpy(U).to(DEV)))
+        mhost.append((mid, d, k, wbits, U))
+    for mode in ("nearest", "stochastic"):
+        Ws = [W.clone() for (_, W, _) in mitems]
+        B.merge_grouped([(kk, W2, U) for (kk, _, U), W2 in zip(mitems, Ws)], 1e-3, scale_dev=alpha,
+                        mode=mode, sr_seed=w.sr_seed)
+        for (mid, d, k, wbits, U), W2 in zip(mhost, Ws):
+            rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 16)]))
+            A = oracle.regen_A(w.seed, mid, w.step, r, k)
+            u = (np.concatenate([philox.sr_draws(w.sr_seed, mid, w.step, 1, k, row0=int(i)) for i in rows])
+                 if mode == "stochastic" else None)
+            want = oracle.merge(oracle.bf16_bits_to_f64(wbits[rows]), U[rows].astype(np.float64), A, 5e-4,
+                                w_dtype="bf16", mode=mode, u_draws=u)
+            frac, exact = ulp_check(bf16_host(W2)[rows], want)
+            assert frac >= 0.9999 and exact >= 0.999
