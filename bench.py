@@ -39,7 +39,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+PEAK_MFMA_BF16_TFS = 2500.0   # MI355X dense bf16 matrix peak, published
 CALIB_BYTES = 1 << 30   # plain copy used to calibrate the byte counters
+POOL_LIMIT_BYTES = 160e9  # distinct input sets up to this size, else a pool
+POOL_SETS = 17            # input sets in a pool (27B set: 17 x 0.74 GB)
+BALLAST_BYTES = {"dense-27b-set-r256": 10 * 10**9}
+DEFAULT_WORKLOAD = "qwen2.5-7b-set-r64"
 ACC_KERNEL = "acc_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "acc_bf16_kernel.qwen2.5-7b-set-r64.traffic.md")
 KERNEL_SOURCES = ["rank_gradient_sketching_logra_amd/csrc/kernels_sketch.hip",
@@ -52,7 +57,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="qwen2.5-7b-set-r64")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rounding", default=None, choices=[None, "nearest", "stochastic"])
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="use fewer layers (profiling runs only)")
@@ -206,11 +211,18 @@ def main():
     # Inputs X: q/k/v share the attention input, gate/up the MLP input.
     shared = {"q": "att", "k": "att", "v": "att", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
     xw = {"att": w.shapes["q"][1], "o": w.shapes["o"][1], "mlp": w.shapes["gate"][1], "down": w.shapes["down"][1]}
-    X = {(l, mb, s): randn((T, xw[s]), 1.0) for l in range(layers) for mb in range(M) for s in xw}
-    D = {(l, mb, kind): randn((T, d), 1e-3) for (l, kind, mid, d, k) in mats for mb in range(M)}
     pbytes = B.packed_input_bytes(T, r)
-    PL = {(l, mb, kind): torch.empty((pbytes,), dtype=torch.uint8, device=dev)
-          for (l, kind, mid, d, k) in mats for mb in range(M)}
+    # One input set (X, D and packed planes of every matrix) per (layer, microbatch).  When
+    # the distinct sets would not fit beside the weights, the step rotates through a pool of
+    # sets, consecutive launches on consecutive sets, the pool far larger than the 256 MB
+    # Infinity Cache.
+    set_bytes = T * 2 * (sum(xw.values()) + sum(d for (_, d) in w.shapes.values())) + len(w.shapes) * pbytes
+    nsets = layers * M if layers * M * set_bytes <= POOL_LIMIT_BYTES else POOL_SETS
+    sid = {(l, mb): (mb * layers + l) % nsets for l in range(layers) for mb in range(M)}
+    X = {(i, s): randn((T, xw[s]), 1.0) for i in range(nsets) for s in xw}
+    D = {(i, kind): randn((T, d), 1e-3) for i in range(nsets) for kind, (d, k) in w.shapes.items()}
+    PL = {(i, kind): torch.empty((pbytes,), dtype=torch.uint8, device=dev)
+          for i in range(nsets) for kind in w.shapes}
     W = {(l, kind): randn((d, k), 0.02) for (l, kind, mid, d, k) in mats}
     S = {(l, kind): torch.zeros((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     U = {(l, kind): torch.empty((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
@@ -218,6 +230,9 @@ def main():
     keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
     maxd = max(d for (_, _, _, d, _) in mats)
     ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
+    # the rest of the model's weights, resident but untouched (27B set: the projections are
+    # 43.6 GB of the model's ~54 GB)
+    ballast = torch.empty((BALLAST_BYTES.get(w.name, 0),), dtype=torch.uint8, device=dev)
     P, Vv = (w.P or 64), (w.V or 152064)
     z = randn((P, Vv), 4.0)
     zd = randn((P, Vv), 1.0)
@@ -245,12 +260,13 @@ def main():
         for mb in range(M):                          # A: forward-side projections
             for l in range(layers):
                 for (kind, d, k) in by_layer[l]:
-                    B.project_input_packed(keys[(l, kind)], X[(l, mb, shared[kind])], r,
-                                           planes=PL[(l, mb, kind)])
+                    B.project_input_packed(keys[(l, kind)], X[(sid[(l, mb)], shared[kind])], r,
+                                           planes=PL[(sid[(l, mb)], kind)])
         ev[1].record()
         for mb in range(M):                          # B: backward-side sketch accumulation
             for l in reversed(range(layers)):
-                B.sketch_accumulate_grouped_packed([(D[(l, mb, kind)], PL[(l, mb, kind)], S[(l, kind)])
+                i = sid[(l, mb)]
+                B.sketch_accumulate_grouped_packed([(D[(i, kind)], PL[(i, kind)], S[(l, kind)])
                                                     for (kind, d, k) in by_layer[l]], r)
         ev[2].record()
         for key_ in S:                               # C: optimiser and step control
@@ -288,9 +304,12 @@ def main():
     merge_gbs = merge_total / (merge_ms * 1e-3) / 1e9
     proj_gbs = proj_total / (tot[0] / K * 1e-3) / 1e9
     avg_launch_us = acc_ms * 1e3 / n_acc_launch
-    traffic = read_traffic() if w.name == "qwen2.5-7b-set-r64" else None
+    traffic = read_traffic() if w.name == DEFAULT_WORKLOAD else None
+    metric = ("sketch-accumulate + merge HBM GB/s (% of peak), Qwen-7B layer set, r=64"
+              if w.name == DEFAULT_WORKLOAD else
+              f"sketch-accumulate + merge HBM GB/s (% of peak), {w.name}")
     out = {
-        "metric": "sketch-accumulate + merge HBM GB/s (% of peak), Qwen-7B layer set, r=64",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -319,7 +338,25 @@ def main():
         "algorithmic_gb": {"accumulate": round(acc_total / 1e9, 3), "merge": round(merge_total / 1e9, 3),
                            "project": round(proj_total / 1e9, 3)},
     }
-    if not args.skip_cpu_baseline and layers == w.layers:
+    # Time bound of each phase: the larger of its HBM time at 8 TB/s and its matrix time at
+    # the dense bf16 peak, the matrix work counted twice (XAt and U enter as bf16 hi + lo).
+    acc_flops = sum(2 * T * d * r for (_, _, _, d, _) in mats) * M
+    merge_flops = sum(2 * d * k * r for (_, _, _, d, k) in mats)
+    acc_bound = max(acc_total / PEAK_HBM_GBS / 1e6, 2 * acc_flops / PEAK_MFMA_BF16_TFS / 1e9)
+    merge_bound = max(merge_total / PEAK_HBM_GBS / 1e6, 2 * merge_flops / PEAK_MFMA_BF16_TFS / 1e9)
+    out["bound_ms"] = {"accumulate": round(acc_bound, 3), "merge": round(merge_bound, 3),
+                       "accumulate_frac": round(acc_bound / acc_ms, 4),
+                       "merge_frac": round(merge_bound / merge_ms, 4),
+                       "accumulate_mfma_tflops_executed": round(2 * acc_flops / (acc_ms * 1e-3) / 1e12, 1)}
+    if w.name != DEFAULT_WORKLOAD and 2 * acc_flops / PEAK_MFMA_BF16_TFS / 1e9 > acc_total / PEAK_HBM_GBS / 1e6:
+        # matrix-bound accumulate (r = 256): its roofline is the matrix peak, in the
+        # algorithmic flops 2Tdr per matrix
+        fl = acc_flops // n_acc_launch
+        out["roofline"].update({"bound": "mfma", "achieved": round(fl / (avg_launch_us * 1e-6) / 1e12, 2),
+                                "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
+                                "frac": round(fl / (avg_launch_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFS, 4),
+                                "flops_per_launch": fl})
+    if not args.skip_cpu_baseline and layers == w.layers and w.name == DEFAULT_WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(w, rounding)
     print(json.dumps(out), flush=True)
 

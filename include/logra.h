@@ -141,8 +141,8 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
 
 /* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a
  * grouped call) needs for bf16 D: XAt repacked as two bf16 terms (hi, lo) in
- * matrix-core operand order, ranks padded to 32 (to 64 when r > 64) and
- * tokens to 16.  d is accepted for future layouts and does not change the
+ * matrix-core operand order, ranks padded to 32, 64, 128 or 256 and tokens
+ * to 16.  d is accepted for future layouts and does not change the
  * size today.  A multiple of 256 bytes; 0 for invalid sizes. */
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r);
 
@@ -153,11 +153,11 @@ LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t 
  * accumulated per microbatch in fp32), [rgc] "How it works" (C += D^T (X P)).
  * bf16 D runs on bf16 MFMA with XAt split into two bf16 terms (hi + lo), which
  * needs the workspace above (ignored for fp32 D, may be NULL then).  The
- * summation order is a function of T alone: the 16-token steps s are dealt
- * to four quarters by s mod 4; each quarter sums its steps in ascending
- * order (hi term, then lo term, per step) and S receives
- * S + ((Q0 + Q1) + (Q2 + Q3)) -- so a grouped call gives the same bits as
- * single calls.
+ * summation order is a function of T and r alone: the 16-token steps s are
+ * dealt to classes by s mod c (c = 4 for r <= 64, 2 for r <= 128, else 1);
+ * each class sums its steps in ascending order (hi term, then lo term, per
+ * step) and S receives S + ((Q0 + Q1) + (Q2 + Q3)), S + (Q0 + Q1) or
+ * S + Q0 -- so a grouped call gives the same bits as single calls.
  * Errors: NULL pointers; T < 1, d < 1, r < 1, r > LOGRA_MAX_RANK, ldd < d;
  * alignment; S or the workspace overlapping an operand; workspace too small. */
 LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r,

@@ -24,7 +24,7 @@ struct AccItem {
   void* ws;        // workspace of this item: packed projected input
 };
 
-// Rank padded to whole 32-rank blocks (64 when r > 64), tokens to 16-token
+// Rank padded to 1, 2, 4 or 8 whole 32-rank blocks, tokens to 16-token
 // steps; size of the packed projected input of one accumulate item (a
 // multiple of 256 bytes).
 int64_t acc_rank_pad(int64_t r);

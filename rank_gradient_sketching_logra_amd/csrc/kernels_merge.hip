@@ -45,21 +45,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// bf16 hi/lo terms of eight fp32 values.
-__device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
-  float h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = (float)(__bf16)x[e];
-    l[e] = x[e] - h[e];
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    hi[p] = bf16_pair(h[2 * p], h[2 * p + 1]);
-    lo[p] = bf16_pair(l[2 * p], l[2 * p + 1]);
-  }
-}
-
 // Sixteen bf16 of W row `row` from column c (two 16-byte words); zero
 // outside the matrix.
 __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t ldw,
@@ -357,21 +342,61 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     }
   };
 
-  // Guarded register path for one band (row or column edge).
+  u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
+  // Four fp32 U values of rank slab li (step s = li >> 1, half q = li & 1)
+  // into the hi and lo operands of step s in bs; ranks >= r count as zero.
+  auto split_to_bs = [&](int li, const float (&xin)[4], int rr) __attribute__((always_inline)) {
+    const int s = li >> 1, q = li & 1;
+    const int j0 = 16 * s + 8 * hw + 4 * q;
+    float h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = xin[i];
+      if (!r_full && j0 + i >= rr) x = 0.f;
+      h[i] = (float)(__bf16)x;
+      l[i] = x - h[i];
+    }
+    const uint32_t hi0 = bf16_pair(h[0], h[1]), hi1 = bf16_pair(h[2], h[3]);
+    const uint32_t lo0 = bf16_pair(l[0], l[1]), lo1 = bf16_pair(l[2], l[3]);
+    const uint32_t ah = lds_u32(bs + s * 64 + lane) + 8 * q;
+    const uint32_t al = lds_u32(bs + (KS + s) * 64 + lane) + 8 * q;
+    asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3"
+                 :
+                 : "v"(ah), "v"(hi0 | ((uint64_t)hi1 << 32)), "v"(al),
+                   "v"(lo0 | ((uint64_t)lo1 << 32))
+                 : "memory");
+  };
+  // The band's hi and lo B operands of step s from bs.
+  auto bfrag_lds = [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+    u32x4 hl[1];
+    lds_read_slabs<1>(lds_u32(bs + s * 64 + lane), hl);
+    bh = hl[0];
+    lds_read_slabs<1>(lds_u32(bs + (KS + s) * 64 + lane), hl);
+    bl = hl[0];
+  };
+
+  // Guarded path for one band (row or column edge): U through bs as in the
+  // streamed path, W by guarded register loads and stores.
   auto edge_band = [&](int64_t band) __attribute__((always_inline)) {
     const int64_t row = band * 32 + n;
-    // An opaque copy of r: the rank bounds below are then not hoisted out of
-    // the band loop (all steps' bounds at once would not fit in registers).
-    int64_t rr = r;
-    asm volatile("" : "+s"(rr));
-    f32x16 acc[E];
-    mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
-      float x[8];
-      const int64_t j0 = 16 * s + 8 * hw;
+    merge_barrier();  // no wave still reads bs
+    {
+      // An opaque copy of r: the rank bounds are not hoisted out of the loop.
+      int rr = (int)r;
+      asm volatile("" : "+s"(rr));
+      for (int li = wave; li < 2 * KS; li += NWV) {
+        const int j0 = 16 * (li >> 1) + 8 * hw + 4 * (li & 1);
+        float x[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (row < d && j0 + i < rr) ? U[row * rr + j0 + i] : 0.f;
-      split8(x, bh, bl);
-    });
+        for (int i = 0; i < 4; ++i)
+          x[i] = (row < d && j0 + i < rr) ? U[row * r + j0 + i] : 0.f;
+        split_to_bs(li, x, rr);
+      }
+    }
+    lds_wait();
+    merge_barrier();  // the band's operands are split
+    f32x16 acc[E];
+    mfma_band(acc, bfrag_lds);
     if (row >= d) return;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -454,7 +479,6 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         if (i == 0) merge_wait_vmcnt<0>(); else merge_wait_vmcnt<WL>();
       }
     };
-    u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
 #pragma unroll
     for (int t = 0; t < NR - 1; ++t)
       if (band_begin + t < fast_end) issue(band_begin + t);
@@ -475,26 +499,13 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         for (int li = wave; li < 2 * KS; li += NWV) {
           u32x4 xv[1];
           lds_read_slabs<1>(lds_u32(ut + li * 64 + lane), xv);
-          const int s = li >> 1, q = li & 1;
-          const int j0 = 16 * s + 8 * hw + 4 * q;
-          float h[4], l[4];
+          float x[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t bits = xv[0][i];
-            float x = __builtin_bit_cast(float, bits);
-            if (!r_full && j0 + i >= rr) x = 0.f;
-            h[i] = (float)(__bf16)x;
-            l[i] = x - h[i];
+            x[i] = __builtin_bit_cast(float, bits);
           }
-          const uint32_t hi0 = bf16_pair(h[0], h[1]), hi1 = bf16_pair(h[2], h[3]);
-          const uint32_t lo0 = bf16_pair(l[0], l[1]), lo1 = bf16_pair(l[2], l[3]);
-          const uint32_t ah = lds_u32(bs + s * 64 + lane) + 8 * q;
-          const uint32_t al = lds_u32(bs + (KS + s) * 64 + lane) + 8 * q;
-          asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3"
-                       :
-                       : "v"(ah), "v"(hi0 | ((uint64_t)hi1 << 32)), "v"(al),
-                         "v"(lo0 | ((uint64_t)lo1 << 32))
-                       : "memory");
+          split_to_bs(li, x, rr);
         }
       }
       lds_wait();
@@ -511,13 +522,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       u32x4 wx[2 * E];
       lds_read_at(wa, wx);
       f32x16 acc[E];
-      mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
-        u32x4 hl[1];
-        lds_read_slabs<1>(lds_u32(bs + s * 64 + lane), hl);
-        bh = hl[0];
-        lds_read_slabs<1>(lds_u32(bs + (KS + s) * 64 + lane), hl);
-        bl = hl[0];
-      });
+      mfma_band(acc, bfrag_lds);
       const int64_t row = band * 32 + n;
 #pragma unroll
       for (int e = 0; e < E; ++e) {

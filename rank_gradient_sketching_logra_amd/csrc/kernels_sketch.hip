@@ -237,9 +237,7 @@ __global__ void project_f32_kernel(KeyArg key, int64_t T, int64_t k, int64_t r,
 // fully contiguous 16-byte-per-lane load.  Tokens >= T and ranks >= r are 0.
 constexpr int kAccStep = 16;        // tokens per MFMA step
 constexpr int kAccCols = 256;       // columns of D per block: 32 lanes x 8
-constexpr int kAccWaves = 8;        // waves per block: 2 rank blocks x 4 token quarters
-constexpr int kAccGroupRB = 2;      // 32-rank blocks per rank group (64 ranks)
-constexpr int kAccRing = 3;         // LDS ring slots (steps) per block
+constexpr int kAccWaves = 8;        // waves per block: rank blocks x token classes
 
 struct AccGroupArgs {
   const void* D[kMaxGroup];
@@ -254,10 +252,7 @@ struct AccGroupArgs {
   int n;
   int64_t T, r;
   int nsteps;   // ceil(T / 16)
-  int nrb;      // 32-rank blocks packed: ceil(r / 32), rounded up to a
-                // multiple of 2 when there is more than one rank group
-  int rb;       // 32-rank blocks per rank group: min(nrb, 2)
-  int ngroups;  // nrb / rb rank groups
+  int nrb;      // 32-rank blocks packed: ceil(r / 32) rounded up to 1, 2, 4 or 8
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -367,6 +362,34 @@ __device__ __forceinline__ void acc_read_step(uint32_t ad, uint32_t ab, u32x4 (&
       : "v"(ad), "v"(ab)
       : "memory");
 }
+// The same ten reads, issued only: the destinations are not valid until
+// acc_read_wait() (which names them, so nothing reads them before it).
+__device__ __forceinline__ void acc_read_issue(uint32_t ad, uint32_t ab, u32x4 (&row)[8],
+                                               u32x4& bh, u32x4& bl) {
+  asm volatile(
+      "ds_read_b128 %0, %10\n\t"
+      "ds_read_b128 %1, %10 offset:1024\n\t"
+      "ds_read_b128 %2, %10 offset:2048\n\t"
+      "ds_read_b128 %3, %10 offset:3072\n\t"
+      "ds_read_b128 %4, %10 offset:4096\n\t"
+      "ds_read_b128 %5, %10 offset:5120\n\t"
+      "ds_read_b128 %6, %10 offset:6144\n\t"
+      "ds_read_b128 %7, %10 offset:7168\n\t"
+      "ds_read_b128 %8, %11\n\t"
+      "ds_read_b128 %9, %11 offset:1024"
+      : "=&v"(row[0]), "=&v"(row[1]), "=&v"(row[2]), "=&v"(row[3]), "=&v"(row[4]),
+        "=&v"(row[5]), "=&v"(row[6]), "=&v"(row[7]), "=&v"(bh), "=&v"(bl)
+      : "v"(ad), "v"(ab)
+      : "memory");
+}
+__device__ __forceinline__ void acc_read_wait(u32x4 (&row)[8], u32x4& bh, u32x4& bl) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(row[0]), "+v"(row[1]), "+v"(row[2]), "+v"(row[3]), "+v"(row[4]),
+                 "+v"(row[5]), "+v"(row[6]), "+v"(row[7]), "+v"(bh), "+v"(bl)
+               :
+               : "memory");
+}
+
 // The two B operands only.
 __device__ __forceinline__ void acc_read_b(uint32_t ab, u32x4& bh, u32x4& bl) {
   asm volatile(
@@ -389,11 +412,12 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Direct global->LDS loads of four 1 KiB row slabs at dst: rows prow,
+// Direct global->LDS loads of N 1 KiB row slabs at dst: rows prow,
 // prow + ldd, ...; lane l's 16 bytes land at byte 16 l of each.
-__device__ __forceinline__ void acc_issue_rows4(u32x4* dst, const uint16_t* prow, int64_t ldd) {
+template <int N>
+__device__ __forceinline__ void acc_issue_rows(u32x4* dst, const uint16_t* prow, int64_t ldd) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < N; ++i)
     __builtin_amdgcn_global_load_lds(prow + i * ldd, dst + i * 64, 16, 0, 0);
 }
 
@@ -415,44 +439,59 @@ __device__ __forceinline__ void acc_mfma_step(f32x16 (&acc)[8], const u32x4 (&a)
                                                      0, 0);
 }
 
-// bf16 D.  A block covers 256 columns of D (rows of S) and one group of up
-// to two 32-rank blocks over all T tokens.  Its eight waves (two per SIMD,
-// so one wave's matrix work overlaps the other's loads and transposes) are
-// two rank blocks times four token quarters: wave w takes rank block w & 1
-// of the group and the 16-token steps s = u (mod 4) of quarter u = w >> 1,
-// so the block streams consecutive tokens.  Lane l covers D rows 16s + 8(l>>5) + i
-// (i = 0..7), columns c0 + 8(l&31) .. +7, so 32 lanes read 512 contiguous
-// bytes of a row.  A ring of kAccRing steps in LDS is filled by direct
-// global->LDS loads: a slot holds, for each quarter, the step's eight row
-// slabs (loaded four each by the quarter's two waves and read by both) and
-// the B operands of the group's rank blocks (each wave loads its own), so
-// kAccRing - 1 steps are in flight while one computes.  The lane's 8 x 8
-// block is transposed in registers: for e = 0..7, operand A_e holds the
-// eight tokens of column c0 + 8(l&31) + e, which is MFMA row m = l & 31 of
-// instance e; the B operand holds the same tokens for rank n = l & 31, so
-// each 32x32x16 MFMA adds 16 tokens.  Instance e gives
-// C[m][n] = S[c0 + 8m + e][32b + n], lane l holding n = l & 31 and
-// m = 8(j>>2) + 4(l>>5) + (j&3) in register j.  Each wave sums its
-// quarter's steps in ascending order (hi term then lo term per step); the
-// quarter sums meet through LDS as (Q0 + Q1) + (Q2 + Q3), and the block
-// adds that to S through an LDS tile so that S is read and written in whole
-// rows.  The order depends on T alone, so grouped and single calls give the
-// same bits.  Blocks that reach past column d take guarded register loads;
-// rows past T (last step only) are loaded from row T - 1 and zeroed.
+// Shape of the accumulate block for RB 32-rank blocks (RB = 1, 2, 4, 8: all
+// ranks in one block, so D is read once).  The eight waves are RBW rank
+// slots times NQ token classes; class u takes the 16-token steps s = u
+// (mod NQ).  A ring slot holds, per class, the step's eight row slabs and
+// the B operands of its RB rank blocks.
+template <int RB>
+struct AccShape {
+  static constexpr int RBW = RB < 2 ? 2 : RB;           // waves per token class
+  static constexpr int NQ = kAccWaves / RBW;            // token classes: 4, 4, 2, 1
+  static constexpr int NS = 8 / RBW;                    // row slabs each wave loads per step
+  static constexpr int kClass = 8 + 2 * RB;             // 1 KiB slabs per class in a slot
+  static constexpr int kSlot = NQ * kClass;             // 1 KiB slabs per slot
+  static constexpr int R = RB <= 2 ? 3 : (RB == 4 ? 4 : 6);  // ring slots
+  static constexpr int kSmemKiB = R * kSlot > 128 ? R * kSlot : 128;  // exchange needs 128
+};
+
+// bf16 D.  A block covers 256 columns of D (rows of S) and all ranks (RB
+// 32-rank blocks) over all T tokens.  Its eight waves (two per SIMD, so one
+// wave's matrix work overlaps the other's loads and transposes) are RBW rank
+// slots times NQ token classes: wave w takes rank block w % RBW (idle for
+// compute when that is >= RB) and the 16-token steps s = u (mod NQ) of class
+// u = w / RBW, so the block streams consecutive tokens.  Lane l covers D rows
+// 16s + 8(l>>5) + i (i = 0..7), columns c0 + 8(l&31) .. +7, so 32 lanes read
+// 512 contiguous bytes of a row.  A ring of R steps in LDS is filled by
+// direct global->LDS loads: a slot holds, for each class, the step's eight
+// row slabs (loaded 8 / RBW each by the class's waves and read by all of
+// them) and the B operands of the rank blocks (each wave loads its own), so
+// R - 1 steps are in flight while one computes.  The lane's 8 x 8 block is
+// transposed in registers: for e = 0..7, operand A_e holds the eight tokens
+// of column c0 + 8(l&31) + e, which is MFMA row m = l & 31 of instance e; the
+// B operand holds the same tokens for rank n = l & 31, so each 32x32x16 MFMA
+// adds 16 tokens.  Instance e gives C[m][n] = S[c0 + 8m + e][32b + n], lane l
+// holding n = l & 31 and m = 8(j>>2) + 4(l>>5) + (j&3) in register j.  Each
+// wave sums its class's steps in ascending order (hi term then lo term per
+// step); the class sums meet through LDS as (Q0 + Q1) + (Q2 + Q3) (NQ = 4)
+// or H0 + H1 (NQ = 2), and the result is added to S -- through an LDS tile
+// in whole rows for NQ = 4, straight from the accumulators (128-byte row
+// segments) otherwise.  The order depends on T and r alone, so grouped and
+// single calls give the same bits.  Blocks that reach past column d take
+// guarded register loads; rows past T (last step only) are loaded from row
+// T - 1 and zeroed.
 template <int RB>
 __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
-  constexpr int R = kAccRing;
-  constexpr int kQuarter = 8 + 2 * RB;  // 1 KiB slabs per quarter in a slot
-  constexpr int kSlot = 4 * kQuarter;
-  __shared__ __align__(16) u32x4 smem[R * kSlot * 64];  // 144 KiB at RB = 2
+  using Sh = AccShape<RB>;
+  constexpr int R = Sh::R, NQ = Sh::NQ, NS = Sh::NS, RBW = Sh::RBW;
+  constexpr int kClass = Sh::kClass, kSlot = Sh::kSlot;
+  __shared__ __align__(16) u32x4 smem[Sh::kSmemKiB * 64];
 
   const int64_t logical = xcd_logical_block();
   if (logical >= g.tile_begin[g.n]) return;
   int item = 0;
   while (logical >= g.tile_begin[item + 1]) ++item;
-  const int64_t local = logical - g.tile_begin[item];
-  const int rg = (int)(local % g.ngroups);  // rank groups of a column block are adjacent
-  const int64_t q = local / g.ngroups;
+  const int64_t q = logical - g.tile_begin[item];
   const uint16_t* __restrict__ D = static_cast<const uint16_t*>(g.D[item]);
   const int64_t ldd = g.ldd[item];
   const int64_t d = g.d[item];
@@ -460,19 +499,18 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rb = wave & 1;              // rank block of this wave within the group
-  const int qt = wave >> 1;             // token quarter
+  const int rb = wave % RBW;            // rank block of this wave
+  const int qt = wave / RBW;            // token class
   const bool has_rb = rb < RB;          // uniform per wave
   const int hw = lane >> 5;
   const int nsteps = g.nsteps;
-  const int Q = (nsteps + 3) >> 2;      // iterations: steps 4k + qt, k < Q
+  const int Q = (nsteps + NQ - 1) / NQ;  // iterations: steps NQ k + qt, k < Q
 
   const int64_t c0 = q * kAccCols;
   const int64_t col = c0 + 8 * (lane & 31);
   const bool interior = c0 + kAccCols <= d;  // uniform per block
   const bool col_full = col + 8 <= d;
-  const uint16_t* __restrict__ planes =
-      g.planes[item] + ((int64_t)rg * RB + rb) * 1024 + lane * 8;
+  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb * 1024 + lane * 8;
   const int64_t bstride = (int64_t)g.nrb * 1024;
 
   f32x16 acc[8];
@@ -481,59 +519,93 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
 
-  // Loads of iteration k (step 4k + qt) into slot k % R: this wave's B
-  // operands (hi, lo of its rank block) and, for an interior block, its
-  // four of the step's eight row slabs.  Iterations past the last step
-  // re-read it (already cached) so that every iteration issues the same
-  // number of loads; rows past T read row T - 1.
+  // Loads of iteration k (step NQ k + qt) into slot k % R: this wave's B
+  // operands (hi, lo of its rank block) and, for an interior block, its NS
+  // of the step's eight row slabs.  Iterations past the last step re-read it
+  // (already cached) so that every iteration issues the same number of
+  // loads; rows past T read row T - 1.
   auto issue = [&](int k) {
-    const int st = 4 * k + qt;
+    const int st = NQ * k + qt;
     const int sc = st < nsteps ? st : nsteps - 1;
-    u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
+    u32x4* qs = smem + ((k % R) * kSlot + qt * kClass) * 64;
     if (has_rb) {
       const uint16_t* pb = planes + (int64_t)sc * bstride;
       acc_issue_slab(qs + (8 + 2 * rb) * 64, pb);
       acc_issue_slab(qs + (9 + 2 * rb) * 64, pb + 512);
     }
     if (!interior) return;
-    const int64_t t0 = (int64_t)kAccStep * sc + 8 * hw + 4 * rb;
+    const int64_t t0 = (int64_t)kAccStep * sc + 8 * hw + NS * rb;
     if ((int64_t)kAccStep * (sc + 1) <= T) {
-      acc_issue_rows4(qs + 4 * rb * 64, D + t0 * ldd + col, ldd);
+      acc_issue_rows<NS>(qs + NS * rb * 64, D + t0 * ldd + col, ldd);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NS; ++i) {
         const int64_t t = t0 + i < T ? t0 + i : T - 1;
-        acc_issue_slab(qs + (4 * rb + i) * 64, D + t * ldd + col);
+        acc_issue_slab(qs + (NS * rb + i) * 64, D + t * ldd + col);
       }
     }
   };
 
   if (interior) {
+    // Software-pipelined: iteration k's operands are in registers (a, bh,
+    // bl) before it starts; its hi-term MFMAs run while the LDS reads of
+    // iteration k + 1 are in flight.  Own loads in flight at the top of
+    // iteration k: iterations k+1 .. k+R-1 (2 + NS each, NS without a rank
+    // block); k + 1 has landed once (R - 2) iterations' loads remain.
+    constexpr int kWaitRb = (R - 2) * (2 + NS), kWaitNoRb = (R - 2) * NS;
+    // zero the rows of a step's block past T (last step only)
+    auto clip = [&](u32x4 (&row)[8], int s) __attribute__((always_inline)) {
+      if ((int64_t)kAccStep * (s + 1) > T) {
+        const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    u32x4 a[8], bh, bl;
 #pragma unroll
     for (int k = 0; k < R - 1; ++k) issue(k);
+    if (has_rb) wait_vmcnt<kWaitRb>();
+    else wait_vmcnt<kWaitNoRb>();
+    ring_barrier();
+    issue(R - 1);
+    if (has_rb) {
+      u32x4 row[8];
+      acc_read_step(lds_addr(smem + qt * kClass * 64 + lane),
+                    lds_addr(smem + (qt * kClass + 8 + 2 * rb) * 64 + lane), row, bh, bl);
+      clip(row, qt);
+      transpose8x8(row, a);
+    }
     for (int k = 0; k < Q; ++k) {
-      // Iteration k has landed once only the loads of iterations
-      // k+1 .. k+R-2 remain (six per iteration, four without a rank block).
-      static_assert(R == 3, "the wait counts assume a three-step ring");
-      if (has_rb) wait_vmcnt<6>();
-      else wait_vmcnt<4>();
-      ring_barrier();  // the partner's rows of iteration k have landed and
-                       // every wave is done with iteration k - 1's slot
-      issue(k + R - 1);
-      const int s = 4 * k + qt;
-      if (has_rb && s < nsteps) {
-        const u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
-        u32x4 row[8], a[8], bh, bl;
-        acc_read_step(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), row, bh, bl);
-        if ((int64_t)kAccStep * (s + 1) > T) {
-          const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
+      if (has_rb) wait_vmcnt<kWaitRb>();
+      else wait_vmcnt<kWaitNoRb>();
+      ring_barrier();  // every wave's loads of iteration k + 1 have landed and
+                       // every wave has read iteration k's slot
+      issue(k + R);
+      if (!has_rb) continue;
+      const bool live = NQ * k + qt < nsteps;  // uniform per wave
+      const u32x4* qs = smem + (((k + 1) % R) * kSlot + qt * kClass) * 64;
+      u32x4 rn[8], bhn, bln;
+      acc_read_issue(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), rn, bhn, bln);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-        transpose8x8(row, a);
-        acc_mfma_step(acc, a, bh, bl);
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bh), acc[e],
+                                                           0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      acc_read_wait(rn, bhn, bln);
+      clip(rn, NQ * (k + 1) + qt);
+      if (live) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e],
+                                                           0, 0, 0);
+      }
+      transpose8x8(rn, a);
+      bh = bhn;
+      bl = bln;
     }
   } else {
     // Block reaching past column d: the same barriers and B loads; rows by
@@ -544,9 +616,9 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
       wait_vmcnt<0>();
       ring_barrier();
       issue(k + R - 1);
-      const int s = 4 * k + qt;
+      const int s = NQ * k + qt;
       if (has_rb && s < nsteps) {
-        const u32x4* qs = smem + ((k % R) * kSlot + qt * kQuarter) * 64;
+        const u32x4* qs = smem + ((k % R) * kSlot + qt * kClass) * 64;
         const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
         u32x4 row[8], a[8], bh, bl;
 #pragma unroll
@@ -559,32 +631,12 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
   }
   wait_vmcnt<0>();  // no load may still target LDS past this point
 
-  // This thread's share of the block's S tile (256 rows x 32 RB ranks): rank
-  // j0 + lane of rows row0 + 8k, so a wave reads whole row segments.  The
-  // loads are issued now and complete while the quarter sums meet.
-  constexpr int TJ = 32 * RB;
-  constexpr int kRowsPerThread = kAccCols / kAccWaves;
   float* __restrict__ S = g.S[item];
   const int64_t r = g.r;
-  const int64_t row0 = c0 + wave;
-  const int64_t j = 32 * (int64_t)rg * RB + lane;
-  const bool jok = lane < TJ && j < r;
-  const int64_t jc = j < r ? j : r - 1;  // in-bounds address for idle lanes
-  int64_t rstride = kAccWaves * r;
-  float sv[kRowsPerThread];
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t row = row0 + kAccWaves * k < d ? row0 + kAccWaves * k : d - 1;
-    sv[k] = S[row * r + jc];
-  }
-  // Keep the addresses from being held live across the exchange below.
-  asm volatile("" : "+s"(rstride));
-  ring_barrier();  // every wave is done with the ring
-
-  // Quarter sums in accumulator order: element (e, j) of lane l at
+  // Class sums in accumulator order: element (e, j) of lane l at
   // [slot][(4e + j / 4) 64 + l] as float4, one 32 KiB slot per wave.
   f32x4* xr = reinterpret_cast<f32x4*>(smem);
-  auto put = [&](int slot) {
+  auto put = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -592,52 +644,125 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
         xr[(slot * 32 + 4 * e + v) * 64 + lane] =
             f32x4{acc[e][4 * v], acc[e][4 * v + 1], acc[e][4 * v + 2], acc[e][4 * v + 3]};
   };
-  auto add = [&](int slot) {
+  auto add_e = [&](int slot, int e) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int v = 0; v < 4; ++v) {
+      const f32x4 x = xr[(slot * 32 + 4 * e + v) * 64 + lane];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const f32x4 x = xr[(slot * 32 + 4 * e + v) * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[e][4 * v + i] += x[i];
-      }
+      for (int i = 0; i < 4; ++i) acc[e][4 * v + i] += x[i];
+    }
   };
-  // Q0 + Q1 and Q2 + Q3 (slots rb + 2 (qt >> 1)).
-  if (has_rb && (qt & 1)) put(rb + 2 * (qt >> 1));
-  wait_lgkmcnt0();
-  ring_barrier();
-  if (has_rb && !(qt & 1)) add(rb + 2 * (qt >> 1));
-  wait_lgkmcnt0();
-  ring_barrier();
-  // (Q0 + Q1) + (Q2 + Q3).
-  if (has_rb && qt == 2) put(rb);
-  wait_lgkmcnt0();
-  ring_barrier();
-  // The tile in LDS after the first 64 KiB, rows of TJ + 1 floats.
-  float* yt = reinterpret_cast<float*>(smem + 2 * 32 * 64);
-  constexpr int YS = TJ + 1;
-  if (has_rb && qt == 0) {
-    add(rb);
-    const int n = lane & 31;
+  auto add = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e) add_e(slot, e);
+  };
+
+  if constexpr (NQ == 4) {
+    // This thread's share of the block's S tile (256 rows x 32 RB ranks):
+    // rank lane of rows row0 + 8k, so a wave reads whole row segments.  The
+    // loads are issued now and complete while the class sums meet.
+    constexpr int TJ = 32 * RB;
+    constexpr int kRowsPerThread = kAccCols / kAccWaves;
+    const int64_t row0 = c0 + wave;
+    const int64_t j = lane;
+    const bool jok = lane < TJ && j < r;
+    const int64_t jc = j < r ? j : r - 1;  // in-bounds address for idle lanes
+    int64_t rstride = kAccWaves * r;
+    float sv[kRowsPerThread];
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int64_t row = row0 + kAccWaves * k < d ? row0 + kAccWaves * k : d - 1;
+      sv[k] = S[row * r + jc];
+    }
+    // Keep the addresses from being held live across the exchange below.
+    asm volatile("" : "+s"(rstride));
+    ring_barrier();  // every wave is done with the ring
+
+    // Q0 + Q1 and Q2 + Q3 (slots rb + 2 (qt >> 1)).
+    if (has_rb && (qt & 1)) put(rb + 2 * (qt >> 1));
+    wait_lgkmcnt0();
+    ring_barrier();
+    if (has_rb && !(qt & 1)) add(rb + 2 * (qt >> 1));
+    wait_lgkmcnt0();
+    ring_barrier();
+    // (Q0 + Q1) + (Q2 + Q3).
+    if (has_rb && qt == 2) put(rb);
+    wait_lgkmcnt0();
+    ring_barrier();
+    // The tile in LDS after the first 64 KiB, rows of TJ + 1 floats.
+    float* yt = reinterpret_cast<float*>(smem + 2 * 32 * 64);
+    constexpr int YS = TJ + 1;
+    if (has_rb && qt == 0) {
+      add(rb);
+      const int n = lane & 31;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 8 * v + 4 * hw + i;
+            yt[(8 * m + e) * YS + 32 * rb + n] = acc[e][4 * v + i];
+          }
+    }
+    wait_lgkmcnt0();
+    ring_barrier();
+    wait_vmcnt<0>();  // the S loads (long complete): no waits between the stores below
+    if (jok) {
+      float* p = S + row0 * r + j;
+#pragma unroll
+      for (int k = 0; k < kRowsPerThread; ++k) {
+        if (row0 + kAccWaves * k < d) *p = sv[k] + yt[(wave + kAccWaves * k) * YS + lane];
+        p += rstride;
+      }
+    }
+  } else {
+    if constexpr (NQ == 2) {
+      // H0 + H1: class 1 hands its sums to class 0 (four 32 KiB slots),
+      // which adds them instance by instance below.
+      ring_barrier();  // every wave is done with the ring
+      if (qt == 1) put(rb);
+      wait_lgkmcnt0();
+      ring_barrier();
+      if (qt != 0) return;
+    }
+    // S += the wave's 256 x 32 tile straight from the accumulators: for
+    // instance e and register 4v + i, the 32 lanes of a half hold 32
+    // consecutive ranks of row c0 + 8(8v + 4(l>>5) + i) + e.  The next
+    // instance's S values are loaded before this one's are stored.
+    const int j = 32 * rb + (lane & 31);
+    if (j >= r) return;
+    // The block's rows of S start at a wave-uniform base; lane offsets are
+    // 32-bit (256 rows x r <= 65536 floats).
+    float* __restrict__ Sb = S + c0 * r;
+    const uint32_t ur = (uint32_t)r;
+    const int nrows = d - c0 < kAccCols ? (int)(d - c0) : kAccCols;
+    float cur[16], nxt[16];
+    auto load = [&](int e, float (&dst)[16]) __attribute__((always_inline)) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = 8 * v + 4 * hw + i;
-          yt[(8 * m + e) * YS + 32 * rb + n] = acc[e][4 * v + i];
+          const int row = 8 * (8 * v + 4 * hw + i) + e;
+          dst[4 * v + i] = row < nrows ? Sb[(uint32_t)row * ur + (uint32_t)j] : 0.f;
         }
-  }
-  wait_lgkmcnt0();
-  ring_barrier();
-  wait_vmcnt<0>();  // the S loads (long complete): no waits between the stores below
-  if (jok) {
-    float* p = S + row0 * r + j;
+    };
+    load(0, cur);
 #pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) {
-      if (row0 + kAccWaves * k < d) *p = sv[k] + yt[(wave + kAccWaves * k) * YS + lane];
-      p += rstride;
+    for (int e = 0; e < 8; ++e) {
+      if (e < 7) load(e + 1, nxt);
+      if constexpr (NQ == 2) add_e(rb, e);  // class 1's sums, instance e
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * (8 * v + 4 * hw + i) + e;
+          if (row < nrows) Sb[(uint32_t)row * ur + (uint32_t)j] = cur[4 * v + i] + acc[e][4 * v + i];
+        }
+      if (e < 7) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
+      }
     }
   }
 }
@@ -664,7 +789,7 @@ __global__ void acc_f32_kernel(AccGroupArgs g) {
 
 int64_t acc_rank_pad(int64_t r) {
   const int64_t nrb = (r + 31) / 32;
-  return 32 * (nrb <= kAccGroupRB ? nrb : (nrb + kAccGroupRB - 1) / kAccGroupRB * kAccGroupRB);
+  return 32 * (nrb <= 2 ? nrb : nrb <= 4 ? 4 : (nrb + 7) / 8 * 8);
 }
 int64_t acc_token_pad(int64_t T) { return (T + kAccStep - 1) / kAccStep * kAccStep; }
 static int64_t acc_col_blocks(int64_t d) { return (d + kAccCols - 1) / kAccCols; }
@@ -727,8 +852,6 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   g.r = r;
   g.nsteps = (int)(acc_token_pad(T) / kAccStep);
   g.nrb = (int)(acc_rank_pad(r) / 32);
-  g.rb = g.nrb < kAccGroupRB ? g.nrb : kAccGroupRB;
-  g.ngroups = g.nrb / g.rb;
   for (int i = 0; i < n; ++i) {
     g.D[i] = items[i].D;
     g.XAt[i] = items[i].XAt;
@@ -762,12 +885,14 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
     if (e != hipSuccess) return e;
   }
   g.tile_begin[0] = 0;
-  for (int i = 0; i < n; ++i) g.tile_begin[i + 1] = g.tile_begin[i] + g.nq[i] * g.ngroups;
+  for (int i = 0; i < n; ++i) g.tile_begin[i + 1] = g.tile_begin[i] + g.nq[i];
   const int64_t tiles = g.tile_begin[n];
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  switch (g.rb) {
+  switch (g.nrb) {
     case 1: hipLaunchKernelGGL(acc_bf16_kernel<1>, grid, dim3(kAccWaves * 64), 0, s, g); break;
     case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, g); break;
+    case 4: hipLaunchKernelGGL(acc_bf16_kernel<4>, grid, dim3(kAccWaves * 64), 0, s, g); break;
+    case 8: hipLaunchKernelGGL(acc_bf16_kernel<8>, grid, dim3(kAccWaves * 64), 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

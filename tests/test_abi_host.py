@@ -47,6 +47,10 @@ def test_version_and_sizes(lib):
     assert B.accumulate_ws_bytes(4096, 3584, 64) == 64 * 4096 * 4
     assert B.accumulate_ws_bytes(1000, 300, 33) == 64 * 1008 * 4
     assert B.accumulate_ws_bytes(4096, 100, 100) == 128 * 4096 * 4
+    # ranks pad to 1, 2, 4 or 8 blocks of 32: r = 160 and 192 take 256
+    assert B.accumulate_ws_bytes(4096, 100, 160) == 256 * 4096 * 4
+    assert B.accumulate_ws_bytes(16, 100, 192) == 256 * 16 * 4
+    assert B.accumulate_ws_bytes(16, 100, 32) == 32 * 16 * 4
     assert B.accumulate_ws_bytes(0, 8, 8) == 0
     assert B.accumulate_ws_bytes(8, 0, 8) == 0
     assert B.rowadam_ws_bytes(0) == 0

@@ -114,7 +114,9 @@ def test_project_f32(T, k, r):
 
 @pytest.mark.parametrize("T,d,r,ldd", [(1000, 300, 64, 304), (512, 256, 8, 256), (4096, 512, 64, 512),
                                        (300, 1000, 256, 1000), (77, 24, 33, 24), (2048, 1536, 100, 1536),
-                                       (16, 8, 1, 8), (4500, 700, 40, 704), (32, 300, 64, 304)])
+                                       (16, 8, 1, 8), (4500, 700, 40, 704), (32, 300, 64, 304),
+                                       (1000, 1280, 256, 1280), (777, 768, 128, 768), (520, 600, 160, 608),
+                                       (40, 520, 96, 520), (2, 257, 256, 264)])
 def test_accumulate_bf16(T, d, r, ldd):
     say(f"accumulate bf16 T={T} d={d} r={r} ldd={ldd}")
     S0 = synth.fp32_matrix((d, r), 0.1, (12, d, r, 0, 5))
@@ -143,11 +145,10 @@ def test_accumulate_f32(T, d, r):
     assert relfro(S.cpu().numpy(), want) <= 1e-6
 
 
-@pytest.mark.parametrize("T", [1024, 4200])
-def test_accumulate_grouped_is_bit_identical_to_single_calls(T):
-    r = 64
+@pytest.mark.parametrize("T,r", [(1024, 64), (4200, 64), (1000, 256), (520, 128)])
+def test_accumulate_grouped_is_bit_identical_to_single_calls(T, r):
     shapes = [(3584, 0), (512, 1), (512, 2), (1000, 3), (2048, 4)]
-    say(f"accumulate grouped vs single T={T}")
+    say(f"accumulate grouped vs single T={T} r={r}")
     items, singles, xat = [], [], {}
     for d, i in shapes:
         bits, _ = bf16_inputs((T, d), 1e-3, (14, d, i, 0, 1))
@@ -451,15 +452,16 @@ def test_merge_fp32_unit_factor_and_values():
 # --------------------------------------------- full-size shapes (sampled)
 
 
-def test_full_size_layer_sampled():
-    """One 7B-shaped layer (q, k, v, o, gate, up, down; r = 64; T = 4096) through the entry
-    points and launch configuration the benchmark times: projections straight into packed
-    operands, one grouped packed accumulate, one grouped merge with the step size on the
-    device.  S is checked on sampled rows of every matrix against the oracle's X A^T and
-    D^T (X A^T); W on sampled rows of every matrix."""
-    w = synth.BY_NAME["qwen2.5-7b-set-r64"]
+@pytest.mark.parametrize("workload", ["qwen2.5-7b-set-r64", "dense-27b-set-r256"])
+def test_full_size_layer_sampled(workload):
+    """One full-size layer (q, k, v, o, gate, up, down; 7B shapes at r = 64, 27B shapes at
+    r = 256; T = 4096) through the entry points and launch configuration the benchmark
+    times: projections straight into packed operands, one grouped packed accumulate, one
+    grouped merge with the step size on the device.  S is checked on sampled rows of every
+    matrix against the oracle's X A^T and D^T (X A^T); W on sampled rows of every matrix."""
+    w = synth.BY_NAME[workload]
     T, r = w.T, w.r
-    say("full-size 7B layer, sampled (bench configuration)")
+    say(f"full-size layer of {workload}, sampled (bench configuration)")
     rs = np.random.default_rng(25)
     items, host = [], []
     for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
