@@ -68,17 +68,37 @@ __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t
 
 // Sixteen updated bf16 of one lane: W values w (two words), products
 // acc[0..15] of consecutive columns, element index e0 of the first (for the
-// stochastic-rounding draws).
+// stochastic-rounding draws).  aligned: e0 is a multiple of 16, so the
+// sixteen draws are exactly one generator block, element t taking bits
+// [16 (t & 3), +16) of word t >> 2.
 template <bool STOCH>
 __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const f32x16& acc,
-                                         float sc, KeyWords srk, uint64_t e0, u32x4& o0,
-                                         u32x4& o1) {
+                                         float sc, KeyWords srk, uint64_t e0, bool aligned,
+                                         u32x4& o0, u32x4& o1) {
+  uint32_t out[8];
+  if (STOCH && aligned) {
+    const Philox4 p = sr_block(srk, e0 >> 4);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
+      const uint32_t wbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
+      const float x = __builtin_fmaf(-sc, acc[t], bf16_bits_to_f32(wbits));
+      const uint32_t u = (uint32_t)(p.w[t >> 2] >> (16 * (t & 3))) & 0xFFFFu;
+      const uint32_t o = f32_to_bf16_sr(x, u);
+      if (t & 1)
+        out[t >> 1] |= o << 16;
+      else
+        out[t >> 1] = o;
+    }
+    o0 = u32x4{out[0], out[1], out[2], out[3]};
+    o1 = u32x4{out[4], out[5], out[6], out[7]};
+    return;
+  }
   Philox4 p0, p1;
   if constexpr (STOCH) {
     p0 = sr_block(srk, e0 >> 4);
     p1 = (((e0 + 15) >> 4) != (e0 >> 4)) ? sr_block(srk, (e0 + 15) >> 4) : p0;
   }
-  uint32_t out[8];
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
@@ -174,15 +194,17 @@ __device__ __forceinline__ void merge_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A block = 8 waves (two per SIMD) x E 32-column instances: columns
-// [cb BC, cb BC + BC), BC = 256 E, row bands [band_begin, band_end) of 32
-// rows.  KS = 16-rank
-// steps.  The signs of A for the block's columns are generated once into LDS
-// as bits and expanded into per-lane A operands; then each band computes
-// C = sigma^T U^T, updates and rounds.  Interior bands of column-interior
-// blocks stream through LDS (two band buffers for W, two for U, the next
-// band's loads in flight while one computes); the others take guarded
-// register loads and stores.
+// A block = 8 waves (two per SIMD) x E 32-column instances.  The work of a
+// launch is a list of units (matrix, column block of BC = 256 E columns,
+// 32-row band), ordered by matrix, then column block, then band; block b
+// takes units [b U / G, (b + 1) U / G) of the U units over G blocks, so the
+// blocks carry equal shares.  Its range splits into segments of one column
+// block each; for each, the signs of A for the block's columns are generated
+// into LDS as bits and expanded into per-lane A operands, then each band
+// computes C = sigma^T U^T (KS 16-rank steps), updates and rounds.  Interior
+// bands of column-interior blocks stream through LDS (a ring of W tiles and
+// U slabs, the next bands' loads in flight while one computes); the others
+// take guarded register loads and stores.
 constexpr int kMergeWaves = 8;
 
 struct MergeGroupArgs {
@@ -194,32 +216,20 @@ struct MergeGroupArgs {
   int64_t k[kMaxGroup];
   int64_t ldw[kMaxGroup];
   int64_t row0[kMaxGroup];
-  int64_t ncb[kMaxGroup];                 // column blocks of each matrix
-  int64_t block_begin[kMaxGroup + 1];     // first block of each matrix
+  int64_t unit_begin[kMaxGroup + 1];      // first unit of each matrix
+  // per > 0: block-per-run schedule instead of equal shares -- matrix i has
+  // blocks [block_begin[i], block_begin[i + 1]), block (cb, g) of it taking
+  // bands [g per, g per + per) of column block cb (cb fastest).
+  int64_t per;
+  int64_t block_begin[kMaxGroup + 1];
   int n;
   int64_t r;
-  int64_t per;                            // bands per block
   float scale_cr;
   const float* scale_dev;
 };
 
 template <int KS, int E, bool STOCH>
 __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGroupArgs g) {
-  // The matrix of this block (several share one launch).
-  if ((int64_t)blockIdx.x >= g.block_begin[g.n]) return;
-  int item = 0;
-  while ((int64_t)blockIdx.x >= g.block_begin[item + 1]) ++item;
-  const KeyArg key = g.key[item];
-  const KeyArg sr_key = g.sr_key[item];
-  uint16_t* __restrict__ W = g.W[item];
-  const float* __restrict__ U = g.U[item];
-  const int64_t d = g.d[item], k = g.k[item], ldw = g.ldw[item], row0 = g.row0[item];
-  const int64_t ncb = g.ncb[item];
-  const int64_t r = g.r;
-  const int64_t bands_per_block = g.per;
-  const float scale_cr = g.scale_cr;
-  const float* __restrict__ scale_dev = g.scale_dev;
-  const int64_t local = (int64_t)blockIdx.x - g.block_begin[item];
   constexpr int NWV = kMergeWaves;
   constexpr int BC = 32 * NWV * E;        // columns per block
   constexpr int NWd = BC / 32;            // sign words per rank
@@ -235,320 +245,358 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31;     // W row within the band (B and C layouts)
-  const int hw = lane >> 5;
-  const int64_t cb = local % ncb;
-  const int64_t bg = local / ncb;
-  const int64_t cblk = cb * BC;
-  const int64_t nbands = (d + 31) / 32;
-  const int64_t band_begin = bg * bands_per_block;
-  const int64_t band_end =
-      band_begin + bands_per_block < nbands ? band_begin + bands_per_block : nbands;
-  if (band_begin >= band_end) return;
+  const int64_t r = g.r;
+  const float scale_cr = g.scale_cr;
+  const float* __restrict__ scale_dev = g.scale_dev;
 
-  // Sign bits of ranks [0, 16 KS) for the block's columns: word w of rank j
-  // holds columns cblk + 32w + (0..31), bit set meaning -1.
-  uint32_t* sbits = reinterpret_cast<uint32_t*>(lds);
-  {
-    const KeyWords kw{key.k0, key.k1};
-    constexpr int NP = (BC + 255) / 256;  // Philox blocks per rank
-    for (int task = tid; task < 16 * KS * NP; task += NWV * 64) {
-      const int j = task / NP;
-      const int pb = task - j * NP;
-      const int64_t c256 = (cblk >> 8) + pb;
-      uint32_t words[8];
-      if (j < r && c256 * 256 < k) {
-        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)c256);
+  int64_t pos, pos_end;
+  if (g.per > 0) {
+    int it = 0;
+    while ((int64_t)blockIdx.x >= g.block_begin[it + 1]) ++it;
+    const int64_t nb = (g.d[it] + 31) / 32;
+    const int64_t ncb = (g.unit_begin[it + 1] - g.unit_begin[it]) / nb;
+    const int64_t local = (int64_t)blockIdx.x - g.block_begin[it];
+    const int64_t cb = local % ncb, bg = local / ncb;
+    pos = g.unit_begin[it] + cb * nb + bg * g.per;
+    pos_end = pos + (bg * g.per + g.per < nb ? g.per : nb - bg * g.per);
+  } else {
+    const int64_t total = g.unit_begin[g.n];
+    pos = (int64_t)blockIdx.x * total / (int64_t)gridDim.x;
+    pos_end = ((int64_t)blockIdx.x + 1) * total / (int64_t)gridDim.x;
+  }
+  for (bool first = true; pos < pos_end; first = false) {
+    // The lane index is opaque per segment, so that nothing derived from it
+    // is hoisted out of the segment loop and held in registers throughout.
+    int lane_o = tid & 63;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
+    const int n = lane & 31;     // W row within the band (B and C layouts)
+    const int hw = lane >> 5;
+    // The segment: one column block of one matrix, bands [band_begin, band_end).
+    int item = 0;
+    while (pos >= g.unit_begin[item + 1]) ++item;
+    const KeyArg key = g.key[item];
+    const KeyArg sr_key = g.sr_key[item];
+    uint16_t* __restrict__ W = g.W[item];
+    const float* __restrict__ U = g.U[item];
+    const int64_t d = g.d[item], k = g.k[item], ldw = g.ldw[item], row0 = g.row0[item];
+    const int64_t nbands = (d + 31) / 32;
+    const int64_t cb = (pos - g.unit_begin[item]) / nbands;
+    const int64_t cblk = cb * BC;
+    const int64_t band_begin = pos - g.unit_begin[item] - cb * nbands;
+    const int64_t seg_end = g.unit_begin[item] + (cb + 1) * nbands < pos_end
+                                ? g.unit_begin[item] + (cb + 1) * nbands
+                                : pos_end;
+    const int64_t band_end = band_begin + (seg_end - pos);
+    pos = seg_end;
+    if (!first) __syncthreads();  // the previous segment's LDS reads are done
+
+    // Sign bits of ranks [0, 16 KS) for the block's columns: word w of rank j
+    // holds columns cblk + 32w + (0..31), bit set meaning -1.
+    uint32_t* sbits = reinterpret_cast<uint32_t*>(lds);
+    {
+      const KeyWords kw{key.k0, key.k1};
+      constexpr int NP = (BC + 255) / 256;  // Philox blocks per rank
+      for (int task = tid; task < 16 * KS * NP; task += NWV * 64) {
+        const int j = task / NP;
+        const int pb = task - j * NP;
+        const int64_t c256 = (cblk >> 8) + pb;
+        uint32_t words[8];
+        if (j < r && c256 * 256 < k) {
+          const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)c256);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          words[2 * w] = (uint32_t)p.w[w];
-          words[2 * w + 1] = (uint32_t)(p.w[w] >> 32);
+          for (int w = 0; w < 4; ++w) {
+            words[2 * w] = (uint32_t)p.w[w];
+            words[2 * w + 1] = (uint32_t)(p.w[w] >> 32);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) words[w] = 0u;
         }
-      } else {
+        if constexpr (BC >= 256) {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) words[w] = 0u;
-      }
-      if constexpr (BC >= 256) {
+          for (int w = 0; w < 8; ++w) sbits[j * NWd + 8 * pb + w] = words[w];
+        } else {
+          const int off = (int)((cblk & 255) >> 5);  // 128-column block: half of the 256 bits
 #pragma unroll
-        for (int w = 0; w < 8; ++w) sbits[j * NWd + 8 * pb + w] = words[w];
-      } else {
-        const int off = (int)((cblk & 255) >> 5);  // 128-column block: half of the 256 bits
-#pragma unroll
-        for (int w = 0; w < NWd; ++w) sbits[j * NWd + w] = words[off + w];
+          for (int w = 0; w < NWd; ++w) sbits[j * NWd + w] = words[off + w];
+        }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // A operands: instance e holds, for MFMA row m = l & 31, column
-  // 32(E wave + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3) of the block and
-  // ranks 16s + 8(l >> 5) + i, i = 0..7.  Ranks >= r read as +1; their U
-  // terms are zero.
-  u32x4 afrag[E][KS];
-  {
-    const int m = lane & 31;
-    const int cm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+    // A operands: instance e holds, for MFMA row m = l & 31, column
+    // 32(E wave + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3) of the block and
+    // ranks 16s + 8(l >> 5) + i, i = 0..7.  Ranks >= r read as +1; their U
+    // terms are zero.
+    u32x4 afrag[E][KS];
+    {
+      const int m = lane & 31;
+      const int cm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int cl = 32 * (E * wave + e) + cm;
+      for (int e = 0; e < E; ++e) {
+        const int cl = 32 * (E * wave + e) + cm;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          uint32_t byte = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            byte |= ((sbits[(16 * s + 8 * hw + i) * NWd + (cl >> 5)] >> (cl & 31)) & 1u) << i;
+          afrag[e][s] = u32x4{
+              0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
+              0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
+              0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
+              0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+          if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __syncthreads();  // the sign bits are dead; the ring may be loaded
+
+    float sc = scale_cr;
+    if (scale_dev != nullptr) sc *= *scale_dev;
+    const KeyWords srk{sr_key.k0, sr_key.k1};
+    const int64_t cw = cblk + 32 * E * wave;   // this wave's first column
+    const bool col_interior = cblk + BC <= k;
+    const bool u_dma = (r & 3) == 0;
+    const bool r_full = (r & 15) == 0;
+    // Every lane's sixteen columns start at a multiple of 16, so with k a
+    // multiple of 16 each lane's draws are one whole generator block.
+    const bool sr_aligned = (k & 15) == 0;
+
+    // C of one band: acc[e] over all rank steps, B operands from bfrag(s).
+    auto mfma_band = [&](f32x16 (&acc)[E], auto&& bfrag) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        uint32_t byte = 0;
+        u32x4 bh, bl;
+        bfrag(s, bh, bl);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          byte |= ((sbits[(16 * s + 8 * hw + i) * NWd + (cl >> 5)] >> (cl & 31)) & 1u) << i;
-        afrag[e][s] = u32x4{
-            0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
-            0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
-            0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
-            0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+        for (int e = 0; e < E; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bh),
+                                                           acc[e], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bl),
+                                                           acc[e], 0, 0, 0);
+        // With many rank steps, keep each step's operand loads next to their
+        // use: hoisting them all would exceed the register file.
         if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  }
-  __syncthreads();  // the sign bits are dead; the ring may be loaded
-
-  float sc = scale_cr;
-  if (scale_dev != nullptr) sc *= *scale_dev;
-  const KeyWords srk{sr_key.k0, sr_key.k1};
-  const int64_t cw = cblk + 32 * E * wave;   // this wave's first column
-  const bool col_interior = cblk + BC <= k;
-  const bool u_dma = (r & 3) == 0;
-  const bool r_full = (r & 15) == 0;
-
-  // C of one band: acc[e] over all rank steps, B operands from bfrag(s).
-  auto mfma_band = [&](f32x16 (&acc)[E], auto&& bfrag) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 bh, bl;
-      bfrag(s, bh, bl);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bh),
-                                                         acc[e], 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bl),
-                                                         acc[e], 0, 0, 0);
-      // With many rank steps, keep each step's operand loads next to their
-      // use: hoisting them all would exceed the register file.
-      if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
-  // Four fp32 U values of rank slab li (step s = li >> 1, half q = li & 1)
-  // into the hi and lo operands of step s in bs; ranks >= r count as zero.
-  auto split_to_bs = [&](int li, const float (&xin)[4], int rr) __attribute__((always_inline)) {
-    const int s = li >> 1, q = li & 1;
-    const int j0 = 16 * s + 8 * hw + 4 * q;
-    float h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = xin[i];
-      if (!r_full && j0 + i >= rr) x = 0.f;
-      h[i] = (float)(__bf16)x;
-      l[i] = x - h[i];
-    }
-    const uint32_t hi0 = bf16_pair(h[0], h[1]), hi1 = bf16_pair(h[2], h[3]);
-    const uint32_t lo0 = bf16_pair(l[0], l[1]), lo1 = bf16_pair(l[2], l[3]);
-    const uint32_t ah = lds_u32(bs + s * 64 + lane) + 8 * q;
-    const uint32_t al = lds_u32(bs + (KS + s) * 64 + lane) + 8 * q;
-    asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3"
-                 :
-                 : "v"(ah), "v"(hi0 | ((uint64_t)hi1 << 32)), "v"(al),
-                   "v"(lo0 | ((uint64_t)lo1 << 32))
-                 : "memory");
-  };
-  // The band's hi and lo B operands of step s from bs.
-  auto bfrag_lds = [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
-    u32x4 hl[1];
-    lds_read_slabs<1>(lds_u32(bs + s * 64 + lane), hl);
-    bh = hl[0];
-    lds_read_slabs<1>(lds_u32(bs + (KS + s) * 64 + lane), hl);
-    bl = hl[0];
-  };
-
-  // Guarded path for one band (row or column edge): U through bs as in the
-  // streamed path, W by guarded register loads and stores.
-  auto edge_band = [&](int64_t band) __attribute__((always_inline)) {
-    const int64_t row = band * 32 + n;
-    merge_barrier();  // no wave still reads bs
-    {
-      // An opaque copy of r: the rank bounds are not hoisted out of the loop.
-      int rr = (int)r;
-      asm volatile("" : "+s"(rr));
-      for (int li = wave; li < 2 * KS; li += NWV) {
-        const int j0 = 16 * (li >> 1) + 8 * hw + 4 * (li & 1);
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          x[i] = (row < d && j0 + i < rr) ? U[row * r + j0 + i] : 0.f;
-        split_to_bs(li, x, rr);
-      }
-    }
-    lds_wait();
-    merge_barrier();  // the band's operands are split
-    f32x16 acc[E];
-    mfma_band(acc, bfrag_lds);
-    if (row >= d) return;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t c = cw + 32 * e + 16 * hw;
-      if (c >= k) continue;
-      u32x4 w0, w1, o0, o1;
-      load_w16(W, ldw, d, k, row, c, w0, w1);
-      update16<STOCH>(w0, w1, acc[e], sc, srk,
-                      (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)c, o0, o1);
-      if (c + 16 <= k) {
-        u32x4* dst = reinterpret_cast<u32x4*>(W + row * ldw + c);
-        dst[0] = o0;
-        dst[1] = o1;
-      } else {
-        for (int t = 0; t < 16 && c + t < k; ++t) {
-          const uint32_t word = (t < 8) ? o0[t >> 1] : o1[(t - 8) >> 1];
-          W[row * ldw + c + t] = (uint16_t)((t & 1) ? (word >> 16) : (word & 0xFFFFu));
-        }
-      }
-    }
-  };
-
-  // Interior bands: [band_begin, fast_end) when the block is column-interior
-  // and U rows are 16-byte aligned; the rest take the guarded path.
-  int64_t fast_end = band_begin;
-  if (col_interior && u_dma) {
-    fast_end = band_end;
-    if (fast_end * 32 > d) --fast_end;  // the partial last band of W
-  }
-
-  if (fast_end > band_begin) {
-    // Loads of band b into ring slot b % NR: W rows as whole 16E-chunk
-    // segments (lane L of a load covers row a = a0 + L / CH, LDS position
-    // L % CH, global chunk (L % CH) ^ (a & (CH - 1))), then U in operand
-    // order (load (s, q) gives lane L row L & 31, ranks 16s + 8(L>>5) + 4q
-    // .. +3).  Two bands are in flight while one computes.
-    constexpr int RPL = 64 / CH;              // W rows per 1 KiB load
-    constexpr int WL = 32 / RPL / NWV;        // W loads (and stores) per wave per band
-    constexpr int UL = (2 * KS + NWV - 1) / NWV;  // U loads per wave per band
-    constexpr int LB = WL + UL;               // loads per wave per band
-    static_assert(WL * RPL * NWV == 32, "W loads must cover the band");
-    auto slot_of = [&](int64_t band) __attribute__((always_inline)) {
-      return lds + (int)((band - band_begin) % NR) * SLOT;
     };
-    auto issue = [&](int64_t band) __attribute__((always_inline)) {
-      u32x4* wt = slot_of(band);
-      u32x4* ut = wt + WT;
+
+    u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
+    // Four fp32 U values of rank slab li (step s = li >> 1, half q = li & 1)
+    // into the hi and lo operands of step s in bs; ranks >= r count as zero.
+    auto split_to_bs = [&](int li, const float (&xin)[4], int rr) __attribute__((always_inline)) {
+      const int s = li >> 1, q = li & 1;
+      const int j0 = 16 * s + 8 * hw + 4 * q;
+      float h[4], l[4];
 #pragma unroll
-      for (int t = 0; t < WL; ++t) {
-        const int a = (wave * WL + t) * RPL + lane / CH;
-        const int pos = lane % CH;
-        const int chunk = pos ^ (a & (CH - 1));
-        dma16(W + (band * 32 + a) * ldw + cblk + 8 * chunk, wt + (wave * WL + t) * 64);
+      for (int i = 0; i < 4; ++i) {
+        float x = xin[i];
+        if (!r_full && j0 + i >= rr) x = 0.f;
+        h[i] = (float)(__bf16)x;
+        l[i] = x - h[i];
       }
-#pragma unroll
-      for (int t = 0; t < UL; ++t) {
-        int li = wave + NWV * t;
-        if (li > 2 * KS - 1) li = 2 * KS - 1;   // repeat a load: same bytes, same place
-        const int s = li >> 1, q = li & 1;
-        int64_t j = 16 * s + 8 * hw + 4 * q;
-        if (j + 4 > r) j = r - 4;                // ranks past r: any in-bounds chunk, zeroed later
-        const int64_t row = band * 32 + n;
-        dma16(U + row * r + j, ut + li * 64);
-      }
+      const uint32_t hi0 = bf16_pair(h[0], h[1]), hi1 = bf16_pair(h[2], h[3]);
+      const uint32_t lo0 = bf16_pair(l[0], l[1]), lo1 = bf16_pair(l[2], l[3]);
+      const uint32_t ah = lds_u32(bs + s * 64 + lane) + 8 * q;
+      const uint32_t al = lds_u32(bs + (KS + s) * 64 + lane) + 8 * q;
+      asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3"
+                   :
+                   : "v"(ah), "v"(hi0 | ((uint64_t)hi1 << 32)), "v"(al),
+                     "v"(lo0 | ((uint64_t)lo1 << 32))
+                   : "memory");
     };
-    // Wait until this wave's loads of band b have landed, given how many
-    // vector-memory operations it issued after them (see the loop).
-    auto wait_band = [&](int64_t band) __attribute__((always_inline)) {
-      const int64_t i = band - band_begin;
-      if constexpr (NR == 3) {
-        const bool more1 = band + 1 < fast_end;
-        if (i == 0) {
-          if (more1) merge_wait_vmcnt<LB>(); else merge_wait_vmcnt<0>();
-        } else if (i == 1) {
-          if (more1) merge_wait_vmcnt<LB + WL>(); else merge_wait_vmcnt<WL>();
-        } else {
-          if (more1) merge_wait_vmcnt<2 * WL + LB>(); else merge_wait_vmcnt<2 * WL>();
-        }
-      } else {
-        if (i == 0) merge_wait_vmcnt<0>(); else merge_wait_vmcnt<WL>();
-      }
+    // The band's hi and lo B operands of step s from bs.
+    auto bfrag_lds = [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+      u32x4 hl[1];
+      lds_read_slabs<1>(lds_u32(bs + s * 64 + lane), hl);
+      bh = hl[0];
+      lds_read_slabs<1>(lds_u32(bs + (KS + s) * 64 + lane), hl);
+      bl = hl[0];
     };
-#pragma unroll
-    for (int t = 0; t < NR - 1; ++t)
-      if (band_begin + t < fast_end) issue(band_begin + t);
-    for (int64_t band = band_begin; band < fast_end; ++band) {
-      // Issue order per wave: loads(b0) .. loads(b0 + NR - 2), then per band
-      // j: loads(j + NR - 1), stores(j).
-      wait_band(band);
-      merge_barrier();  // every wave's loads of this band have landed, and the
-                        // slot of band - 1 is no longer read
-      if (band + NR - 1 < fast_end) issue(band + NR - 1);
-      u32x4* wt = slot_of(band);
-      const u32x4* ut = wt + WT;
-      // Split U once per band: wave w converts fp32 slabs w, w + NWV, ...
-      // (step s, half q) into halves of the hi and lo operands of step s.
+
+    // Guarded path for one band (row or column edge): U through bs as in the
+    // streamed path, W by guarded register loads and stores.
+    auto edge_band = [&](int64_t band) __attribute__((always_inline)) {
+      const int64_t row = band * 32 + n;
+      merge_barrier();  // no wave still reads bs
       {
-        int rr = (int)r;  // opaque: the rank bounds are not hoisted
+        // An opaque copy of r: the rank bounds are not hoisted out of the loop.
+        int rr = (int)r;
         asm volatile("" : "+s"(rr));
         for (int li = wave; li < 2 * KS; li += NWV) {
-          u32x4 xv[1];
-          lds_read_slabs<1>(lds_u32(ut + li * 64 + lane), xv);
+          const int j0 = 16 * (li >> 1) + 8 * hw + 4 * (li & 1);
           float x[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t bits = xv[0][i];
-            x[i] = __builtin_bit_cast(float, bits);
-          }
+          for (int i = 0; i < 4; ++i)
+            x[i] = (row < d && j0 + i < rr) ? U[row * r + j0 + i] : 0.f;
           split_to_bs(li, x, rr);
         }
       }
       lds_wait();
       merge_barrier();  // the band's operands are split
-      // This lane's W chunks: columns 32e + 16hw .. +15 of row n are chunks
-      // cc, cc + 1 with cc = 4(E wave + e) + 2hw.
-      uint32_t wa[2 * E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int cc = 4 * (E * wave + e) + 2 * hw;
-        wa[2 * e] = lds_u32(wt + n * CH + (cc ^ (n & (CH - 1))));
-        wa[2 * e + 1] = lds_u32(wt + n * CH + ((cc + 1) ^ (n & (CH - 1))));
-      }
-      u32x4 wx[2 * E];
-      lds_read_at(wa, wx);
       f32x16 acc[E];
       mfma_band(acc, bfrag_lds);
-      const int64_t row = band * 32 + n;
+      if (row >= d) return;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        u32x4 o0, o1;
-        update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk,
-                        (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw),
-                        o0, o1);
-        lds_write16(wa[2 * e], o0);
-        lds_write16(wa[2 * e + 1], o1);
+        const int64_t c = cw + 32 * e + 16 * hw;
+        if (c >= k) continue;
+        u32x4 w0, w1, o0, o1;
+        load_w16(W, ldw, d, k, row, c, w0, w1);
+        update16<STOCH>(w0, w1, acc[e], sc, srk,
+                        (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)c, sr_aligned, o0, o1);
+        if (c + 16 <= k) {
+          u32x4* dst = reinterpret_cast<u32x4*>(W + row * ldw + c);
+          dst[0] = o0;
+          dst[1] = o1;
+        } else {
+          for (int t = 0; t < 16 && c + t < k; ++t) {
+            const uint32_t word = (t < 8) ? o0[t >> 1] : o1[(t - 8) >> 1];
+            W[row * ldw + c + t] = (uint16_t)((t & 1) ? (word >> 16) : (word & 0xFFFFu));
+          }
+        }
       }
-      lds_wait();
-      merge_barrier();  // the whole tile is updated
-      // Whole-row stores, in the load's lane order.
-      u32x4 ov[WL];
-      lds_read_slabs<WL>(lds_u32(wt + (wave * WL) * 64 + lane), ov);
-#pragma unroll
-      for (int t = 0; t < WL; ++t) {
-        const int a = (wave * WL + t) * RPL + lane / CH;
-        const int pos = lane % CH;
-        const int chunk = pos ^ (a & (CH - 1));
-        *reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk) = ov[t];
-      }
+    };
+
+    // Interior bands: [band_begin, fast_end) when the block is column-interior
+    // and U rows are 16-byte aligned; the rest take the guarded path.
+    int64_t fast_end = band_begin;
+    if (col_interior && u_dma) {
+      fast_end = band_end;
+      if (fast_end * 32 > d) --fast_end;  // the partial last band of W
     }
-    merge_wait_vmcnt<0>();
-  }
-  for (int64_t band = fast_end; band < band_end; ++band) edge_band(band);
+
+    if (fast_end > band_begin) {
+      // Loads of band b into ring slot b % NR: W rows as whole 16E-chunk
+      // segments (lane L of a load covers row a = a0 + L / CH, LDS position
+      // L % CH, global chunk (L % CH) ^ (a & (CH - 1))), then U in operand
+      // order (load (s, q) gives lane L row L & 31, ranks 16s + 8(L>>5) + 4q
+      // .. +3).  Two bands are in flight while one computes.
+      constexpr int RPL = 64 / CH;              // W rows per 1 KiB load
+      constexpr int WL = 32 / RPL / NWV;        // W loads (and stores) per wave per band
+      constexpr int UL = (2 * KS + NWV - 1) / NWV;  // U loads per wave per band
+      constexpr int LB = WL + UL;               // loads per wave per band
+      static_assert(WL * RPL * NWV == 32, "W loads must cover the band");
+      auto slot_of = [&](int64_t band) __attribute__((always_inline)) {
+        return lds + (int)((band - band_begin) % NR) * SLOT;
+      };
+      auto issue = [&](int64_t band) __attribute__((always_inline)) {
+        u32x4* wt = slot_of(band);
+        u32x4* ut = wt + WT;
+#pragma unroll
+        for (int t = 0; t < WL; ++t) {
+          const int a = (wave * WL + t) * RPL + lane / CH;
+          const int pos = lane % CH;
+          const int chunk = pos ^ (a & (CH - 1));
+          dma16(W + (band * 32 + a) * ldw + cblk + 8 * chunk, wt + (wave * WL + t) * 64);
+        }
+#pragma unroll
+        for (int t = 0; t < UL; ++t) {
+          int li = wave + NWV * t;
+          if (li > 2 * KS - 1) li = 2 * KS - 1;   // repeat a load: same bytes, same place
+          const int s = li >> 1, q = li & 1;
+          int64_t j = 16 * s + 8 * hw + 4 * q;
+          if (j + 4 > r) j = r - 4;                // ranks past r: any in-bounds chunk, zeroed later
+          const int64_t row = band * 32 + n;
+          dma16(U + row * r + j, ut + li * 64);
+        }
+      };
+      // Wait until this wave's loads of band b have landed, given how many
+      // vector-memory operations it issued after them (see the loop).
+      auto wait_band = [&](int64_t band) __attribute__((always_inline)) {
+        const int64_t i = band - band_begin;
+        if constexpr (NR == 3) {
+          const bool more1 = band + 1 < fast_end;
+          if (i == 0) {
+            if (more1) merge_wait_vmcnt<LB>(); else merge_wait_vmcnt<0>();
+          } else if (i == 1) {
+            if (more1) merge_wait_vmcnt<LB + WL>(); else merge_wait_vmcnt<WL>();
+          } else {
+            if (more1) merge_wait_vmcnt<2 * WL + LB>(); else merge_wait_vmcnt<2 * WL>();
+          }
+        } else {
+          if (i == 0) merge_wait_vmcnt<0>(); else merge_wait_vmcnt<WL>();
+        }
+      };
+#pragma unroll
+      for (int t = 0; t < NR - 1; ++t)
+        if (band_begin + t < fast_end) issue(band_begin + t);
+      for (int64_t band = band_begin; band < fast_end; ++band) {
+        // Issue order per wave: loads(b0) .. loads(b0 + NR - 2), then per band
+        // j: loads(j + NR - 1), stores(j).
+        wait_band(band);
+        merge_barrier();  // every wave's loads of this band have landed, and the
+                          // slot of band - 1 is no longer read
+        if (band + NR - 1 < fast_end) issue(band + NR - 1);
+        u32x4* wt = slot_of(band);
+        const u32x4* ut = wt + WT;
+        // Split U once per band: wave w converts fp32 slabs w, w + NWV, ...
+        // (step s, half q) into halves of the hi and lo operands of step s.
+        {
+          int rr = (int)r;  // opaque: the rank bounds are not hoisted
+          asm volatile("" : "+s"(rr));
+          for (int li = wave; li < 2 * KS; li += NWV) {
+            u32x4 xv[1];
+            lds_read_slabs<1>(lds_u32(ut + li * 64 + lane), xv);
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t bits = xv[0][i];
+              x[i] = __builtin_bit_cast(float, bits);
+            }
+            split_to_bs(li, x, rr);
+          }
+        }
+        lds_wait();
+        merge_barrier();  // the band's operands are split
+        // This lane's W chunks: columns 32e + 16hw .. +15 of row n are chunks
+        // cc, cc + 1 with cc = 4(E wave + e) + 2hw.
+        uint32_t wa[2 * E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int cc = 4 * (E * wave + e) + 2 * hw;
+          wa[2 * e] = lds_u32(wt + n * CH + (cc ^ (n & (CH - 1))));
+          wa[2 * e + 1] = lds_u32(wt + n * CH + ((cc + 1) ^ (n & (CH - 1))));
+        }
+        u32x4 wx[2 * E];
+        lds_read_at(wa, wx);
+        f32x16 acc[E];
+        mfma_band(acc, bfrag_lds);
+        const int64_t row = band * 32 + n;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          u32x4 o0, o1;
+          update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk,
+                          (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw),
+                          sr_aligned, o0, o1);
+          lds_write16(wa[2 * e], o0);
+          lds_write16(wa[2 * e + 1], o1);
+        }
+        lds_wait();
+        merge_barrier();  // the whole tile is updated
+        // Whole-row stores, in the load's lane order.
+        u32x4 ov[WL];
+        lds_read_slabs<WL>(lds_u32(wt + (wave * WL) * 64 + lane), ov);
+#pragma unroll
+        for (int t = 0; t < WL; ++t) {
+          const int a = (wave * WL + t) * RPL + lane / CH;
+          const int pos = lane % CH;
+          const int chunk = pos ^ (a & (CH - 1));
+          *reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk) = ov[t];
+        }
+      }
+      merge_wait_vmcnt<0>();
+    }
+    for (int64_t band = fast_end; band < band_end; ++band) edge_band(band);
+  }  // segments
 }
 
 // fp32 W: a block owns 16 rows x one 256-column Philox block; signs in LDS
@@ -614,7 +662,7 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   g.r = r;
   g.scale_cr = (float)(scale * cr);
   g.scale_dev = scale_dev;
-  int64_t units = 0, maxbands = 1;
+  g.unit_begin[0] = 0;
   for (int i = 0; i < n; ++i) {
     g.key[i] = items[i].key;
     g.sr_key[i] = items[i].sr_key;
@@ -624,32 +672,45 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     g.k[i] = items[i].k;
     g.ldw[i] = items[i].ldw;
     g.row0[i] = items[i].row0;
-    g.ncb[i] = (items[i].k + bc - 1) / bc;
+    const int64_t ncb = (items[i].k + bc - 1) / bc;
     const int64_t nb = (items[i].d + 31) / 32;
-    units += nb * g.ncb[i];
-    maxbands = std::max(maxbands, nb);
+    g.unit_begin[i + 1] = g.unit_begin[i] + ncb * nb;
   }
-  // At most one block per compute unit over the whole group (a second round
-  // of blocks would double the time of the matrices it holds), each a run of
-  // bands of one column block: the sign setup is amortised and the band ring
-  // stays full.
+  // At most one block per compute unit (a second round of blocks would
+  // double the time of the units it holds).  Equal shares balance the load
+  // but may split a column block's run of bands over two blocks (each
+  // then builds the block's A operands and fills its ring); runs of a fixed
+  // length per column block avoid that and are taken when their longest run
+  // is within 10% of an equal share.
   const int64_t cus = compute_units();
-  auto blocks_for = [&](int64_t p) {
+  const int64_t total = g.unit_begin[n];
+  if (total == 0) return hipSuccess;
+  int64_t blocks = total < cus ? total : cus;
+  const int64_t share = (total + blocks - 1) / blocks;
+  int64_t maxbands = 1;
+  for (int i = 0; i < n; ++i) maxbands = std::max(maxbands, (items[i].d + 31) / 32);
+  auto runs_for = [&](int64_t p) {
     int64_t b = 0;
-    for (int i = 0; i < n; ++i) b += g.ncb[i] * (((items[i].d + 31) / 32 + p - 1) / p);
+    for (int i = 0; i < n; ++i) {
+      const int64_t nb = (items[i].d + 31) / 32;
+      b += (g.unit_begin[i + 1] - g.unit_begin[i]) / (nb > 0 ? nb : 1) * ((nb + p - 1) / p);
+    }
     return b;
   };
-  int64_t per = (units + cus - 1) / cus;
-  if (per < 4) per = 4;
-  while (per < maxbands && blocks_for(per) > cus) ++per;
-  if (per > maxbands) per = maxbands;
-  g.per = per;
-  g.block_begin[0] = 0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t nb = (items[i].d + 31) / 32;
-    g.block_begin[i + 1] = g.block_begin[i] + g.ncb[i] * ((nb + per - 1) / per);
+  int64_t per = share;
+  while (per < maxbands && runs_for(per) > cus) ++per;
+  g.per = 0;
+  if (per * 10 <= share * 11) {
+    g.per = per;
+    g.block_begin[0] = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t nb = (items[i].d + 31) / 32;
+      const int64_t ncb = nb > 0 ? (g.unit_begin[i + 1] - g.unit_begin[i]) / nb : 0;
+      g.block_begin[i + 1] = g.block_begin[i] + ncb * ((nb + per - 1) / per);
+    }
+    blocks = g.block_begin[n];
   }
-  const dim3 grid((unsigned)g.block_begin[n]);
+  const dim3 grid((unsigned)blocks);
 #define LOGRA_MERGE_LAUNCH(KS, E)                                                               \
   if (stochastic)                                                                               \
     hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true>), grid, dim3(kMergeWaves * 64), 0, s, g); \

@@ -78,41 +78,46 @@ __global__ __launch_bounds__(256) void rowadam_rows_kernel(int64_t d, int64_t r,
   }
 }
 
-// One block: rho, then ||Ut||_F^2 = sum_i m_i / (sqrt(vh_i) + eps rho)^2 and
-// the norm-restoring ratio ||S||_F / ||Ut||_F.
-__global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nblocks,
-                                                           double eps, RowAdamWs ws) {
-  __shared__ double red[256];
-  __shared__ double tot[2];
-  if (threadIdx.x == 0) {
-    double a = 0.0, b = 0.0;
-    for (int64_t q = 0; q < nblocks; ++q) {
-      a += ws.partial[2 * q];
-      b += ws.partial[2 * q + 1];
-    }
-    tot[0] = a;  // ||S||_F^2
-    tot[1] = b;  // sum vh
-  }
-  __syncthreads();
-  const double erho = eps * sqrt(tot[1] / (double)d);
-  double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < d; i += 256) {
-    const double den = sqrt(ws.vh[i]) + erho;
-    if (den > 0.0) acc += ws.m[i] / (den * den);
-  }
-  red[threadIdx.x] = acc;
+// Sum of one value per thread over the block's 256 threads: a fixed tree,
+// every thread gets the total.
+__device__ double block_sum256(double x, double* red) {
+  __syncthreads();  // red may still be read by an earlier call
+  red[threadIdx.x] = x;
   __syncthreads();
   for (int w = 128; w >= 1; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
+  return red[0];
+}
+
+// One block: rho, then ||Ut||_F^2 = sum_i m_i / (sqrt(vh_i) + eps rho)^2 and
+// the norm-restoring ratio ||S||_F / ||Ut||_F.
+__global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nblocks,
+                                                           double eps, RowAdamWs ws) {
+  __shared__ double red[256];
+  // Per-block partial sums, thread t taking blocks t, t + 256, ...
+  double a = 0.0, b = 0.0;
+  for (int64_t q = threadIdx.x; q < nblocks; q += 256) {
+    a += ws.partial[2 * q];
+    b += ws.partial[2 * q + 1];
+  }
+  const double sum_m = block_sum256(a, red);   // ||S||_F^2
+  const double sum_vh = block_sum256(b, red);  // sum vh
+  const double erho = eps * sqrt(sum_vh / (double)d);
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < d; i += 256) {
+    const double den = sqrt(ws.vh[i]) + erho;
+    if (den > 0.0) acc += ws.m[i] / (den * den);
+  }
+  const double nu2 = block_sum256(acc, red);
   if (threadIdx.x == 0) {
-    const double nu2 = red[0];
     ws.scalars[0] = erho;
-    ws.scalars[1] = nu2 > 0.0 ? sqrt(tot[0] / nu2) : 0.0;
+    ws.scalars[1] = nu2 > 0.0 ? sqrt(sum_m / nu2) : 0.0;
   }
 }
 
+// Scaling pass: U = S * ratio / (sqrt(vh_i) + eps rho), row by row.
 __global__ __launch_bounds__(256) void rowadam_apply_kernel(int64_t d, int64_t r,
                                                             const float* S, float* U,
                                                             RowAdamWs ws) {

@@ -546,8 +546,35 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
     }
   };
 
-  if (interior) {
-    // Software-pipelined: iteration k's operands are in registers (a, bh,
+  if (interior && RB <= 2) {
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) issue(k);
+    for (int k = 0; k < Q; ++k) {
+      // Iteration k has landed once only the loads of iterations
+      // k+1 .. k+R-2 remain (2 + NS per iteration, NS without a rank block).
+      if (has_rb) wait_vmcnt<(R - 2) * (2 + NS)>();
+      else wait_vmcnt<(R - 2) * NS>();
+      ring_barrier();  // the other waves' rows of iteration k have landed and
+                       // every wave is done with iteration k - 1's slot
+      issue(k + R - 1);
+      const int s = NQ * k + qt;
+      if (has_rb && s < nsteps) {
+        const u32x4* qs = smem + ((k % R) * kSlot + qt * kClass) * 64;
+        u32x4 row[8], a[8], bh, bl;
+        acc_read_step(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), row, bh, bl);
+        if ((int64_t)kAccStep * (s + 1) > T) {
+          const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        transpose8x8(row, a);
+        acc_mfma_step(acc, a, bh, bl);
+      }
+    }
+  } else if (interior) {
+    // Four or eight rank blocks (each wave computes every step of its class)
+    // are software-pipelined: iteration k's operands are in registers (a, bh,
     // bl) before it starts; its hi-term MFMAs run while the LDS reads of
     // iteration k + 1 are in flight.  Own loads in flight at the top of
     // iteration k: iterations k+1 .. k+R-1 (2 + NS each, NS without a rank
