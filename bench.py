@@ -5,7 +5,8 @@ One step = one update over the whole layer set of the workload:
      the packed operand form the accumulate reads (XAt = X A^T)
   B. accumulate every sketch, every microbatch (grouped: the seven matrices
      of one layer and one microbatch per launch -- one kernel per launch)
-  C. RowAdam for every sketch, predicted-KL q over the context set, alpha on
+  C. RowAdam for every sketch (writing the update straight in the merge's
+     packed operand form), predicted-KL q over the context set, alpha on
      the device
   D. merge every matrix, W <- round(W - eta*alpha U A) (grouped: the seven
      matrices of one layer per launch)
@@ -225,7 +226,8 @@ def main():
           for i in range(nsets) for kind in w.shapes}
     W = {(l, kind): randn((d, k), 0.02) for (l, kind, mid, d, k) in mats}
     S = {(l, kind): torch.zeros((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
-    U = {(l, kind): torch.empty((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
+    UP = {(l, kind): torch.empty((B.packed_update_bytes(d, r),), dtype=torch.uint8, device=dev)
+          for (l, kind, mid, d, k) in mats}
     V = {(l, kind): torch.zeros((d,), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
     maxd = max(d for (_, _, _, d, _) in mats)
@@ -269,14 +271,14 @@ def main():
                 B.sketch_accumulate_grouped_packed([(D[(i, kind)], PL[(i, kind)], S[(l, kind)])
                                                     for (kind, d, k) in by_layer[l]], r)
         ev[2].record()
-        for key_ in S:                               # C: optimiser and step control
-            B.rowadam(S[key_], V[key_], t_step, w.beta, w.eps, U=U[key_], ws=ra_ws)
+        for key_ in S:                               # C: optimiser (U in the merge's packed form)
+            B.rowadam_packed(S[key_], V[key_], t_step, w.beta, w.eps, out=UP[key_], ws=ra_ws)
         B.predicted_kl_q(z, zd, w.tau, out=q, ws=kl_ws)
         B.step_alpha_dev(q, w.delta, w.alpha_max, out=alpha)
         ev[3].record()
         for l in range(layers):                      # D: merge (one launch per layer)
-            B.merge_grouped([(keys[(l, kind)], W[(l, kind)], U[(l, kind)]) for (kind, d, k) in by_layer[l]],
-                            w.eta, scale_dev=alpha, mode=rounding, sr_seed=w.sr_seed)
+            B.merge_grouped_packed([(keys[(l, kind)], W[(l, kind)], UP[(l, kind)]) for (kind, d, k) in by_layer[l]],
+                                   r, w.eta, scale_dev=alpha, mode=rounding, sr_seed=w.sr_seed)
         ev[4].record()
 
     def events():

@@ -315,6 +315,50 @@ LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int 
                                   const float* scale_dev, logra_round mode, uint64_t sr_seed,
                                   logra_stream stream);
 
+/* --------------------------------------------------------- packed update */
+
+/* Bytes of the packed update of d rows at rank r: U split into two bf16
+ * terms (hi = RNE(u), lo = RNE(u - hi)) in the merge's matrix-core operand
+ * order -- for each 32-row band g and 16-rank step s (steps padded to 1, 2,
+ * 4, 8 or 16), a 1 KiB hi operand then a 1 KiB lo operand in which 16-byte
+ * lane l holds rows 32g + (l & 31), ranks 16s + 8(l >> 5) .. +7; rows >= d
+ * and ranks >= r are zero.  The same bytes as fp32 U with rows padded to 32
+ * and ranks to 16, 32, 64, 128 or 256.  0 for invalid sizes. */
+LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r);
+
+/* Pack fp32 U [d x r] (contiguous) into the form above, so that a merge
+ * reads its operands as they are ([paper] §2.2: the update U is what the
+ * merge applies; the split is the hi + lo carrying of U in bf16 arithmetic).
+ * Errors: NULL pointers; d < 1, r < 1, r > LOGRA_MAX_RANK; packed_bytes too
+ * small; alignment; U overlapping the packed update. */
+LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_packed,
+                                size_t packed_bytes, logra_stream stream);
+
+/* logra_rowadam writing the packed update instead of fp32 U: the same fp32
+ * values as logra_rowadam's U, packed as by logra_pack_update, in one pass.
+ * Errors: as logra_rowadam; r > LOGRA_MAX_RANK; packed_bytes too small; the
+ * packed update overlapping S, v or the workspace. */
+LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                                   double beta, double eps, void* U_packed, size_t packed_bytes,
+                                   void* ws, size_t ws_bytes, logra_stream stream);
+
+typedef struct logra_merge_packed_desc {
+  logra_key key;          /* key of this matrix's A                          */
+  void* W;                /* [d x k] bf16, row-major, leading dimension ldw  */
+  int64_t d;
+  int64_t k;
+  int64_t ldw;
+  const void* U_packed;   /* logra_packed_update_bytes(d, r) bytes            */
+  int64_t row0;           /* global index of W's first row                    */
+} logra_merge_packed_desc;
+
+/* logra_merge_grouped with each U given as its packed update.  Same result
+ * bits as logra_merge_grouped with the fp32 U the update was packed from.
+ * Errors: as logra_merge_grouped. */
+LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_desc* descs, int n,
+                                         double scale, const float* scale_dev, logra_round mode,
+                                         uint64_t sr_seed, logra_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,11 @@ class MergeDesc(Structure):
                 ("U", c_void_p), ("row0", c_int64)]
 
 
+class MergePackedDesc(Structure):
+    _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
+                ("U_packed", c_void_p), ("row0", c_int64)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -68,6 +73,12 @@ SIGNATURES = {
     "logra_step_alpha_dev": (c_int, [c_void_p, c_float, c_float, c_void_p, c_void_p]),
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
+    "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_pack_update": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_rowadam_packed": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_double,
+                                     c_double, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+    "logra_merge_grouped_packed": (c_int, [c_int64, POINTER(MergePackedDesc), c_int, c_double,
+                                           c_void_p, c_int, c_uint64, c_void_p]),
     "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                             c_void_p, c_double, c_void_p, c_int, c_uint64, c_int64, c_void_p]),
 }
@@ -291,3 +302,47 @@ def merge_grouped(items, scale: float, scale_dev=None, mode: str = "nearest", sr
     m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
     _check(lib().logra_merge_grouped(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
                                      _stream(items[0][1], stream)))
+
+
+def packed_update_bytes(d: int, r: int) -> int:
+    return lib().logra_packed_update_bytes(d, r)
+
+
+def pack_update(U: torch.Tensor, out=None, stream=None):
+    """The merge's packed form of fp32 U [d x r] (a uint8 tensor)."""
+    d, r = U.shape
+    nb = packed_update_bytes(d, r)
+    P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=U.device)
+    _check(lib().logra_pack_update(d, r, _ptr(U), _ptr(P), P.numel() * P.element_size(),
+                                   _stream(U, stream)))
+    return P
+
+
+def rowadam_packed(S: torch.Tensor, v: torch.Tensor, t: int, beta: float, eps: float, out=None,
+                   ws=None, stream=None):
+    """RowAdam(S) written as the merge's packed update, v updated in place."""
+    d, r = S.shape
+    nb = packed_update_bytes(d, r)
+    P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=S.device)
+    if ws is None:
+        ws = workspace(rowadam_ws_bytes(d), S.device)
+    _check(lib().logra_rowadam_packed(d, r, _ptr(S), _ptr(v), t, beta, eps, _ptr(P),
+                                      P.numel() * P.element_size(), _ptr(ws), ws.numel(),
+                                      _stream(S, stream)))
+    return P
+
+
+def merge_grouped_packed(items, r: int, scale: float, scale_dev=None, mode: str = "nearest",
+                         sr_seed: int = 0, stream=None):
+    """items: sequence of (key, W, U_packed) or (key, W, U_packed, row0) with bf16 W; one launch."""
+    n = len(items)
+    descs = (MergePackedDesc * n)()
+    for i, it in enumerate(items):
+        k_, W, P = it[0], it[1], it[2]
+        row0 = it[3] if len(it) > 3 else 0
+        if P.numel() * P.element_size() < packed_update_bytes(W.shape[0], r):
+            raise ValueError("packed update too small for this W and r")
+        descs[i] = MergePackedDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), P.data_ptr(), row0)
+    m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
+    _check(lib().logra_merge_grouped_packed(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
+                                            _stream(items[0][1], stream)))

@@ -42,8 +42,10 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
                              bool packed, hipStream_t s);
 
 size_t rowadam_ws_bytes(int64_t d);
+// U (fp32) and/or U_packed (the merge's packed update) may be null.
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                          double beta, double eps, float* U, void* ws, hipStream_t s);
+                          double beta, double eps, float* U, void* U_packed, void* ws,
+                          hipStream_t s);
 
 size_t klq_ws_bytes(int64_t P, int64_t V);
 hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,
@@ -56,12 +58,17 @@ struct MergeItem {
   KeyArg sr_key;   // stochastic-rounding key of the matrix
   void* W;         // [d x k] bf16, leading dimension ldw
   int64_t d, k, ldw;
-  const float* U;  // [d x r] fp32
+  const void* U;   // [d x r] fp32, or the packed update (packed launches)
   int64_t row0;
 };
 // Several bf16 merges sharing r, the scale and the rounding mode in one launch.
 hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,
-                                const float* scale_dev, bool stochastic, hipStream_t s);
+                                const float* scale_dev, bool stochastic, bool packed,
+                                hipStream_t s);
+// 16-rank steps of the merge (1, 2, 4, 8 or 16) and the packed update's size.
+int merge_rank_steps(int64_t r);
+size_t packed_update_bytes(int64_t d, int64_t r);
+hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, void* packed, hipStream_t s);
 hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
                         int64_t ldw, const float* U, double scale, const float* scale_dev,
                         bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s);

@@ -211,7 +211,7 @@ struct MergeGroupArgs {
   KeyArg key[kMaxGroup];
   KeyArg sr_key[kMaxGroup];
   uint16_t* W[kMaxGroup];
-  const float* U[kMaxGroup];
+  const void* U[kMaxGroup];               // fp32 [d x r], or packed operands
   int64_t d[kMaxGroup];
   int64_t k[kMaxGroup];
   int64_t ldw[kMaxGroup];
@@ -228,7 +228,10 @@ struct MergeGroupArgs {
   const float* scale_dev;
 };
 
-template <int KS, int E, bool STOCH>
+// PACKED: U arrives already split in operand order (see the packed update
+// layout); the band's U slabs are then copied into the ring as they are,
+// with no split pass and no split buffer.
+template <int KS, int E, bool STOCH, bool PACKED>
 __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGroupArgs g) {
   constexpr int NWV = kMergeWaves;
   constexpr int BC = 32 * NWV * E;        // columns per block
@@ -236,12 +239,12 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   constexpr int CH = BC / 8;              // 16-byte chunks per tile row
   constexpr int WT = 32 * BC / 8;         // 16-byte chunks per W tile (32 rows)
   constexpr int UT = 32 * KS * 4;         // 16-byte chunks per U band (operand order)
-  constexpr int NR = KS >= 16 ? 2 : 3;    // bands in the LDS ring
-  constexpr int SLOT = WT + UT;           // one band: W tile, then fp32 U
-  // LDS: a ring of NR bands, then the band's U as bf16 hi/lo operands (KS
-  // hi slabs, KS lo slabs).  The sign bits live in the ring until the A
-  // operands are built.
-  __shared__ __align__(16) u32x4 lds[NR * SLOT + UT];
+  constexpr int NR = (KS >= 16 && !PACKED) ? 2 : 3;  // bands in the LDS ring
+  constexpr int SLOT = WT + UT;           // one band: W tile, then U (fp32 or packed)
+  // LDS: a ring of NR bands, then (fp32 U) the band's U as bf16 hi/lo
+  // operands (KS hi slabs, KS lo slabs).  The sign bits live in the ring
+  // until the A operands are built.
+  __shared__ __align__(16) u32x4 lds[NR * SLOT + (PACKED ? 0 : UT)];
   static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
@@ -279,7 +282,8 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     const KeyArg key = g.key[item];
     const KeyArg sr_key = g.sr_key[item];
     uint16_t* __restrict__ W = g.W[item];
-    const float* __restrict__ U = g.U[item];
+    const float* __restrict__ U = static_cast<const float*>(g.U[item]);
+    const uint16_t* __restrict__ Up = static_cast<const uint16_t*>(g.U[item]);
     const int64_t d = g.d[item], k = g.k[item], ldw = g.ldw[item], row0 = g.row0[item];
     const int64_t nbands = (d + 31) / 32;
     const int64_t cb = (pos - g.unit_begin[item]) / nbands;
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     const KeyWords srk{sr_key.k0, sr_key.k1};
     const int64_t cw = cblk + 32 * E * wave;   // this wave's first column
     const bool col_interior = cblk + BC <= k;
-    const bool u_dma = (r & 3) == 0;
+    const bool u_dma = PACKED || (r & 3) == 0;
     const bool r_full = (r & 15) == 0;
     // Every lane's sixteen columns start at a multiple of 16, so with k a
     // multiple of 16 each lane's draws are one whole generator block.
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       }
     };
 
-    u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs
+    u32x4* bs = lds + NR * SLOT;   // split U: KS hi slabs then KS lo slabs (fp32 U only)
     // Four fp32 U values of rank slab li (step s = li >> 1, half q = li & 1)
     // into the hi and lo operands of step s in bs; ranks >= r count as zero.
     auto split_to_bs = [&](int li, const float (&xin)[4], int rr) __attribute__((always_inline)) {
@@ -422,28 +426,37 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       bl = hl[0];
     };
 
-    // Guarded path for one band (row or column edge): U through bs as in the
-    // streamed path, W by guarded register loads and stores.
+    // Guarded path for one band (row or column edge): W by guarded register
+    // loads and stores; fp32 U split through bs as in the streamed path,
+    // packed U read straight from memory (its rows are padded to the band).
     auto edge_band = [&](int64_t band) __attribute__((always_inline)) {
       const int64_t row = band * 32 + n;
-      merge_barrier();  // no wave still reads bs
-      {
-        // An opaque copy of r: the rank bounds are not hoisted out of the loop.
-        int rr = (int)r;
-        asm volatile("" : "+s"(rr));
-        for (int li = wave; li < 2 * KS; li += NWV) {
-          const int j0 = 16 * (li >> 1) + 8 * hw + 4 * (li & 1);
-          float x[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            x[i] = (row < d && j0 + i < rr) ? U[row * r + j0 + i] : 0.f;
-          split_to_bs(li, x, rr);
-        }
-      }
-      lds_wait();
-      merge_barrier();  // the band's operands are split
       f32x16 acc[E];
-      mfma_band(acc, bfrag_lds);
+      if constexpr (PACKED) {
+        const uint16_t* ub = Up + band * KS * 1024 + lane * 8;
+        mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+          bh = *reinterpret_cast<const u32x4*>(ub + s * 1024);
+          bl = *reinterpret_cast<const u32x4*>(ub + s * 1024 + 512);
+        });
+      } else {
+        merge_barrier();  // no wave still reads bs
+        {
+          // An opaque copy of r: the rank bounds are not hoisted out of the loop.
+          int rr = (int)r;
+          asm volatile("" : "+s"(rr));
+          for (int li = wave; li < 2 * KS; li += NWV) {
+            const int j0 = 16 * (li >> 1) + 8 * hw + 4 * (li & 1);
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              x[i] = (row < d && j0 + i < rr) ? U[row * r + j0 + i] : 0.f;
+            split_to_bs(li, x, rr);
+          }
+        }
+        lds_wait();
+        merge_barrier();  // the band's operands are split
+        mfma_band(acc, bfrag_lds);
+      }
       if (row >= d) return;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -502,11 +515,16 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         for (int t = 0; t < UL; ++t) {
           int li = wave + NWV * t;
           if (li > 2 * KS - 1) li = 2 * KS - 1;   // repeat a load: same bytes, same place
-          const int s = li >> 1, q = li & 1;
-          int64_t j = 16 * s + 8 * hw + 4 * q;
-          if (j + 4 > r) j = r - 4;                // ranks past r: any in-bounds chunk, zeroed later
-          const int64_t row = band * 32 + n;
-          dma16(U + row * r + j, ut + li * 64);
+          if constexpr (PACKED) {
+            // slab li = 2s + (lo term) of the band, stored contiguously
+            dma16(Up + (band * 2 * KS + li) * 512 + lane * 8, ut + li * 64);
+          } else {
+            const int s = li >> 1, q = li & 1;
+            int64_t j = 16 * s + 8 * hw + 4 * q;
+            if (j + 4 > r) j = r - 4;              // ranks past r: any in-bounds chunk, zeroed later
+            const int64_t row = band * 32 + n;
+            dma16(U + row * r + j, ut + li * 64);
+          }
         }
       };
       // Wait until this wave's loads of band b have landed, given how many
@@ -540,7 +558,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         const u32x4* ut = wt + WT;
         // Split U once per band: wave w converts fp32 slabs w, w + NWV, ...
         // (step s, half q) into halves of the hi and lo operands of step s.
-        {
+        if constexpr (!PACKED) {
           int rr = (int)r;  // opaque: the rank bounds are not hoisted
           asm volatile("" : "+s"(rr));
           for (int li = wave; li < 2 * KS; li += NWV) {
@@ -554,9 +572,9 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
             }
             split_to_bs(li, x, rr);
           }
+          lds_wait();
+          merge_barrier();  // the band's operands are split
         }
-        lds_wait();
-        merge_barrier();  // the band's operands are split
         // This lane's W chunks: columns 32e + 16hw .. +15 of row n are chunks
         // cc, cc + 1 with cc = 4(E wave + e) + 2hw.
         uint32_t wa[2 * E];
@@ -569,7 +587,17 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         u32x4 wx[2 * E];
         lds_read_at(wa, wx);
         f32x16 acc[E];
-        mfma_band(acc, bfrag_lds);
+        if constexpr (PACKED) {
+          mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
+            u32x4 hl[1];
+            lds_read_slabs<1>(lds_u32(ut + (2 * s) * 64 + lane), hl);
+            bh = hl[0];
+            lds_read_slabs<1>(lds_u32(ut + (2 * s + 1) * 64 + lane), hl);
+            bl = hl[0];
+          });
+        } else {
+          mfma_band(acc, bfrag_lds);
+        }
         const int64_t row = band * 32 + n;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -650,11 +678,11 @@ static int64_t compute_units() {
 }
 
 hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,
-                                const float* scale_dev, bool stochastic, hipStream_t s) {
+                                const float* scale_dev, bool stochastic, bool packed,
+                                hipStream_t s) {
   if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
   const double cr = 1.0 / std::sqrt((double)r);
-  const int64_t ksteps = (r + 15) / 16;
-  const int ks = ksteps <= 1 ? 1 : ksteps <= 2 ? 2 : ksteps <= 4 ? 4 : ksteps <= 8 ? 8 : 16;
+  const int ks = merge_rank_steps(r);
   const int e = ks <= 4 ? 2 : 1;
   const int64_t bc = 32 * kMergeWaves * e;
   MergeGroupArgs g{};
@@ -711,11 +739,19 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     blocks = g.block_begin[n];
   }
   const dim3 grid((unsigned)blocks);
-#define LOGRA_MERGE_LAUNCH(KS, E)                                                               \
-  if (stochastic)                                                                               \
-    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true>), grid, dim3(kMergeWaves * 64), 0, s, g); \
-  else                                                                                          \
-    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false>), grid, dim3(kMergeWaves * 64), 0, s, g);
+#define LOGRA_MERGE_LAUNCH_P(KS, E, P)                                                      \
+  if (stochastic)                                                                           \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true, P>), grid, dim3(kMergeWaves * 64), 0, \
+                       s, g);                                                               \
+  else                                                                                      \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false, P>), grid, dim3(kMergeWaves * 64), 0, \
+                       s, g);
+#define LOGRA_MERGE_LAUNCH(KS, E)   \
+  if (packed) {                     \
+    LOGRA_MERGE_LAUNCH_P(KS, E, true) \
+  } else {                          \
+    LOGRA_MERGE_LAUNCH_P(KS, E, false) \
+  }
   switch (ks) {
     case 1: LOGRA_MERGE_LAUNCH(1, 2) break;
     case 2: LOGRA_MERGE_LAUNCH(2, 2) break;
@@ -725,6 +761,7 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     default: return hipErrorInvalidValue;
   }
 #undef LOGRA_MERGE_LAUNCH
+#undef LOGRA_MERGE_LAUNCH_P
   return hipGetLastError();
 }
 
@@ -739,7 +776,57 @@ hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bo
     return hipGetLastError();
   }
   const MergeItem it{key, sr_key, W, d, k, ldw, U, row0};
-  return launch_merge_grouped(&it, 1, r, scale, scale_dev, stochastic, s);
+  return launch_merge_grouped(&it, 1, r, scale, scale_dev, stochastic, false, s);
+}
+
+// Packed update: U [d x r] fp32 as the merge's B operands.  For 32-row band
+// g and 16-rank step s (steps padded to KS = 1, 2, 4, 8 or 16), a 1 KiB hi
+// slab then a 1 KiB lo slab, lane l holding rows 32g + (l & 31), ranks
+// 16s + 8(l >> 5) + i (i = 0..7) as bf16 hi = RNE(u), lo = RNE(u - hi);
+// rows >= d and ranks >= r are zero.
+int merge_rank_steps(int64_t r) {
+  const int64_t ksteps = (r + 15) / 16;
+  return ksteps <= 1 ? 1 : ksteps <= 2 ? 2 : ksteps <= 4 ? 4 : ksteps <= 8 ? 8 : 16;
+}
+size_t packed_update_bytes(int64_t d, int64_t r) {
+  return (size_t)((d + 31) / 32) * (size_t)merge_rank_steps(r) * 2048;
+}
+
+namespace {
+__global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, int ks,
+                                                          const float* __restrict__ U,
+                                                          uint16_t* __restrict__ P) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (band, step, lane)
+  const int lane = (int)(t & 63);
+  const int64_t bs = t >> 6;
+  const int64_t nb = (d + 31) / 32;
+  if (bs >= nb * ks) return;
+  const int64_t band = bs / ks;
+  const int s = (int)(bs - band * ks);
+  const int64_t row = band * 32 + (lane & 31);
+  const int64_t j0 = 16 * s + 8 * (lane >> 5);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (row < d && j0 + i < r) ? U[row * r + j0 + i] : 0.f;
+  u32x4 hv, lv;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float h0 = (float)(__bf16)x[2 * p], h1 = (float)(__bf16)x[2 * p + 1];
+    hv[p] = bf16_pair(h0, h1);
+    lv[p] = bf16_pair(x[2 * p] - h0, x[2 * p + 1] - h1);
+  }
+  uint16_t* dst = P + bs * 1024 + lane * 8;
+  *reinterpret_cast<u32x4*>(dst) = hv;
+  *reinterpret_cast<u32x4*>(dst + 512) = lv;
+}
+}  // namespace
+
+hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, void* packed, hipStream_t s) {
+  const int ks = merge_rank_steps(r);
+  const int64_t threads = (d + 31) / 32 * ks * 64;
+  hipLaunchKernelGGL(pack_update_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     d, r, ks, U, static_cast<uint16_t*>(packed));
+  return hipGetLastError();
 }
 
 }  // namespace logra

@@ -129,6 +129,48 @@ __global__ __launch_bounds__(256) void rowadam_apply_kernel(int64_t d, int64_t r
   U[idx] = (float)((double)S[idx] * f);
 }
 
+// The scaling pass writing the merge's packed update instead of fp32 U (the
+// same fp32 values, split into bf16 hi and lo terms in operand order): one
+// thread per (32-row band, 16-rank step, lane).
+__global__ __launch_bounds__(256) void rowadam_apply_packed_kernel(int64_t d, int64_t r, int ks,
+                                                                   const float* S,
+                                                                   uint16_t* P, RowAdamWs ws) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = (int)(t & 63);
+  const int64_t bs = t >> 6;
+  const int64_t nb = (d + 31) / 32;
+  if (bs >= nb * ks) return;
+  const int64_t band = bs / ks;
+  const int s = (int)(bs - band * ks);
+  const int64_t i = band * 32 + (lane & 31);
+  const int64_t j0 = 16 * s + 8 * (lane >> 5);
+  double f = 0.0;
+  if (i < d) {
+    const double den = sqrt(ws.vh[i]) + ws.scalars[0];
+    f = den > 0.0 ? ws.scalars[1] / den : 0.0;
+  }
+  float x[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    x[q] = (i < d && j0 + q < r) ? (float)((double)S[i * r + j0 + q] * f) : 0.f;
+  uint32_t hv[4], lv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const __bf16 h0 = (__bf16)x[2 * p], h1 = (__bf16)x[2 * p + 1];
+    const __bf16 l0 = (__bf16)(x[2 * p] - (float)h0), l1 = (__bf16)(x[2 * p + 1] - (float)h1);
+    hv[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    lv[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(P + bs * 1024 + lane * 8);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    dst[p] = hv[p];
+    dst[256 + p] = lv[p];
+  }
+}
+
 // -------------------------------------------------------- predicted KL q
 
 // Partial softmax moments of one chunk of one context, relative to the
@@ -267,7 +309,8 @@ size_t rowadam_ws_bytes(int64_t d) {
 }
 
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
-                          double beta, double eps, float* U, void* ws, hipStream_t s) {
+                          double beta, double eps, float* U, void* U_packed, void* ws,
+                          hipStream_t s) {
   const RowAdamWs w = rowadam_ws_layout(ws, d);
   const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
   const double b = beta;
@@ -279,10 +322,21 @@ hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_
   hipLaunchKernelGGL(rowadam_norm_kernel, dim3(1), dim3(256), 0, s, d, nb, eps, w);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = d * r;
-  hipLaunchKernelGGL(rowadam_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     d, r, S, U, w);
-  return hipGetLastError();
+  if (U != nullptr) {
+    const int64_t n = d * r;
+    hipLaunchKernelGGL(rowadam_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       d, r, S, U, w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (U_packed != nullptr) {
+    const int ks = merge_rank_steps(r);
+    const int64_t threads = (d + 31) / 32 * ks * 64;
+    hipLaunchKernelGGL(rowadam_apply_packed_kernel, dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, d, r, ks, S, static_cast<uint16_t*>(U_packed), w);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 size_t klq_ws_bytes(int64_t P, int64_t V) {

@@ -232,25 +232,68 @@ LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {
   return logra::rowadam_ws_bytes(d);
 }
 
+namespace {
+// RowAdam with U written as fp32 (U) or as the packed update (P, P_bytes).
+int rowadam_impl(const char* name, int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                 double beta, double eps, float* U, void* P, size_t P_bytes, void* ws,
+                 size_t ws_bytes, logra_stream stream) {
+  if (!S || !v || (!U && !P)) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
+  if (d < 1 || r < 1) return fail(LOGRA_ERR_SHAPE, "%s: need d, r >= 1", name);
+  if (P && bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "%s: need r <= %d", name, LOGRA_MAX_RANK);
+  if (t < 1) return fail(LOGRA_ERR_DOMAIN, "%s: t counts updates from 1", name);
+  if (!(beta >= 0.0 && beta < 1.0)) return fail(LOGRA_ERR_DOMAIN, "%s: beta must be in [0, 1)", name);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "%s: eps must be finite and >= 0", name);
+  const size_t need = logra::rowadam_ws_bytes(d);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
+  const size_t pneed = P ? logra::packed_update_bytes(d, r) : 0;
+  if (P && P_bytes < pneed) return fail(LOGRA_ERR_WORKSPACE, "%s: the packed update needs %zu bytes", name, pneed);
+  if (!aligned16(S) || (U && !aligned16(U)) || (P && !aligned16(P)) || !aligned16(v) || !aligned16(ws))
+    return fail(LOGRA_ERR_ALIGN, "%s: S, U, v and workspace must be 16-byte aligned", name);
+  const Range rs = range(S, (size_t)(d * r) * 4);
+  const Range ru = U ? range(U, (size_t)(d * r) * 4) : Range{0, 0};
+  const Range rp = P ? range(P, pneed) : Range{0, 0};
+  if (U && overlap(rs, ru) && rs.lo != ru.lo) return fail(LOGRA_ERR_ALIAS, "%s: U partially overlaps S", name);
+  if (P && (overlap(rp, rs) || overlap(rp, ru))) return fail(LOGRA_ERR_ALIAS, "%s: the packed update overlaps S or U", name);
+  const Range rv = range(v, (size_t)d * 4), rw = range(ws, need);
+  if (overlap(rv, rs) || overlap(rv, ru) || overlap(rw, rs) || overlap(rw, ru) || overlap(rw, rv) ||
+      overlap(rv, rp) || overlap(rw, rp))
+    return fail(LOGRA_ERR_ALIAS, "%s: v or workspace overlaps an operand", name);
+  return hip_status(logra::launch_rowadam(d, r, S, v, t, beta, eps, U, P, ws, static_cast<hipStream_t>(stream)),
+                    "rowadam launch");
+}
+}  // namespace
+
 LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
                             double beta, double eps, float* U, void* ws, size_t ws_bytes,
                             logra_stream stream) {
-  if (!S || !v || !U) return fail(LOGRA_ERR_NULL, "rowadam: NULL pointer");
-  if (d < 1 || r < 1) return fail(LOGRA_ERR_SHAPE, "rowadam: need d, r >= 1");
-  if (t < 1) return fail(LOGRA_ERR_DOMAIN, "rowadam: t counts updates from 1");
-  if (!(beta >= 0.0 && beta < 1.0)) return fail(LOGRA_ERR_DOMAIN, "rowadam: beta must be in [0, 1)");
-  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "rowadam: eps must be finite and >= 0");
-  const size_t need = logra::rowadam_ws_bytes(d);
-  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "rowadam: workspace of %zu bytes needed", need);
-  if (!aligned16(S) || !aligned16(U) || !aligned16(v) || !aligned16(ws))
-    return fail(LOGRA_ERR_ALIGN, "rowadam: S, U, v and workspace must be 16-byte aligned");
-  const Range rs = range(S, (size_t)(d * r) * 4), ru = range(U, (size_t)(d * r) * 4);
-  if (overlap(rs, ru) && rs.lo != ru.lo) return fail(LOGRA_ERR_ALIAS, "rowadam: U partially overlaps S");
-  const Range rv = range(v, (size_t)d * 4), rw = range(ws, need);
-  if (overlap(rv, rs) || overlap(rv, ru) || overlap(rw, rs) || overlap(rw, ru) || overlap(rw, rv))
-    return fail(LOGRA_ERR_ALIAS, "rowadam: v or workspace overlaps an operand");
-  return hip_status(logra::launch_rowadam(d, r, S, v, t, beta, eps, U, ws, static_cast<hipStream_t>(stream)),
-                    "rowadam launch");
+  if (!U) return fail(LOGRA_ERR_NULL, "rowadam: NULL pointer");
+  return rowadam_impl("rowadam", d, r, S, v, t, beta, eps, U, nullptr, 0, ws, ws_bytes, stream);
+}
+
+LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* v, int64_t t,
+                                   double beta, double eps, void* U_packed, size_t packed_bytes,
+                                   void* ws, size_t ws_bytes, logra_stream stream) {
+  if (!U_packed) return fail(LOGRA_ERR_NULL, "rowadam_packed: NULL pointer");
+  return rowadam_impl("rowadam_packed", d, r, S, v, t, beta, eps, nullptr, U_packed, packed_bytes, ws,
+                      ws_bytes, stream);
+}
+
+LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r) {
+  if (d < 1 || bad_rank(r)) return 0;
+  return logra::packed_update_bytes(d, r);
+}
+
+LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_packed,
+                                size_t packed_bytes, logra_stream stream) {
+  if (!U || !U_packed) return fail(LOGRA_ERR_NULL, "pack_update: NULL pointer");
+  if (d < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_update: need d >= 1, 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t need = logra::packed_update_bytes(d, r);
+  if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_update: the packed update needs %zu bytes", need);
+  if (!aligned16(U_packed)) return fail(LOGRA_ERR_ALIGN, "pack_update: the packed update must be 16-byte aligned");
+  if (overlap(range(U, (size_t)(d * r) * 4), range(U_packed, need)))
+    return fail(LOGRA_ERR_ALIAS, "pack_update: U overlaps the packed update");
+  return hip_status(logra::launch_pack_update(d, r, U, U_packed, static_cast<hipStream_t>(stream)),
+                    "pack_update launch");
 }
 
 LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V) {
@@ -290,37 +333,75 @@ LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_
                     "step_alpha_dev launch");
 }
 
+namespace {
+// One matrix of a grouped merge, U as fp32 or packed.
+struct MergeOperands {
+  const logra_key* key;
+  void* W;
+  int64_t d, k, ldw;
+  const void* U;
+  int64_t row0;
+};
+int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, int n, double scale,
+                       const float* scale_dev, logra_round mode, uint64_t sr_seed, bool packed,
+                       logra_stream stream) {
+  if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "%s: need 1 <= n <= %d", name, LOGRA_MAX_GROUP);
+  if (bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "%s: need 1 <= r <= %d", name, LOGRA_MAX_RANK);
+  if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "%s: unknown rounding mode", name);
+  if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "%s: scale must be finite", name);
+  auto u_range = [&](const MergeOperands& e) {
+    return range(e.U, packed ? logra::packed_update_bytes(e.d, r) : (size_t)(e.d * r) * 4);
+  };
+  logra::MergeItem items[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    const MergeOperands& e = ops[i];
+    if (!e.W || !e.U) return fail(LOGRA_ERR_NULL, "%s: NULL pointer in descriptor %d", name, i);
+    if (e.d < 1 || e.k < 1 || e.row0 < 0) return fail(LOGRA_ERR_SHAPE, "%s: need d, k >= 1 and row0 >= 0", name);
+    int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.k);
+    if (st) return st;
+    if (!aligned16(e.U)) return fail(LOGRA_ERR_ALIGN, "%s: U not 16-byte aligned", name);
+    const Range rw = range(e.W, extent(e.d, e.k, e.ldw, 2));
+    if (scale_dev && overlap(rw, range(scale_dev, 4))) return fail(LOGRA_ERR_ALIAS, "%s: W overlaps the device scale", name);
+    for (int j = 0; j <= i; ++j) {
+      if (overlap(rw, u_range(ops[j])) ||
+          (j < i && overlap(rw, range(ops[j].W, extent(ops[j].d, ops[j].k, ops[j].ldw, 2)))))
+        return fail(LOGRA_ERR_ALIAS, "%s: W of descriptor %d overlaps an operand of %d", name, i, j);
+      if (j < i && overlap(u_range(e), range(ops[j].W, extent(ops[j].d, ops[j].k, ops[j].ldw, 2))))
+        return fail(LOGRA_ERR_ALIAS, "%s: U of descriptor %d overlaps W of %d", name, i, j);
+    }
+    items[i] = logra::MergeItem{key_words(e.key->seed, e.key), key_words(sr_seed, e.key), e.W, e.d, e.k,
+                                e.ldw, e.U, e.row0};
+  }
+  return hip_status(logra::launch_merge_grouped(items, n, r, scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
+                                                packed, static_cast<hipStream_t>(stream)),
+                    "merge_grouped launch");
+}
+}  // namespace
+
 LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int n, double scale,
                                   const float* scale_dev, logra_round mode, uint64_t sr_seed,
                                   logra_stream stream) {
   if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
-  if (bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need 1 <= r <= %d", LOGRA_MAX_RANK);
-  if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "merge_grouped: unknown rounding mode");
-  if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "merge_grouped: scale must be finite");
-  logra::MergeItem items[LOGRA_MAX_GROUP];
-  for (int i = 0; i < n; ++i) {
-    const logra_merge_desc& e = descs[i];
-    if (!e.W || !e.U) return fail(LOGRA_ERR_NULL, "merge_grouped: NULL pointer in descriptor %d", i);
-    if (e.d < 1 || e.k < 1 || e.row0 < 0) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need d, k >= 1 and row0 >= 0");
-    int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.k);
-    if (st) return st;
-    if (!aligned16(e.U)) return fail(LOGRA_ERR_ALIGN, "merge_grouped: U not 16-byte aligned");
-    const Range rw = range(e.W, extent(e.d, e.k, e.ldw, 2));
-    if (scale_dev && overlap(rw, range(scale_dev, 4))) return fail(LOGRA_ERR_ALIAS, "merge_grouped: W overlaps the device scale");
-    for (int j = 0; j <= i; ++j) {
-      if (overlap(rw, range(descs[j].U, (size_t)(descs[j].d * r) * 4)) ||
-          (j < i && overlap(rw, range(descs[j].W, extent(descs[j].d, descs[j].k, descs[j].ldw, 2)))))
-        return fail(LOGRA_ERR_ALIAS, "merge_grouped: W of descriptor %d overlaps an operand of %d", i, j);
-      if (j < i && overlap(range(e.U, (size_t)(e.d * r) * 4), range(descs[j].W, extent(descs[j].d, descs[j].k, descs[j].ldw, 2))))
-        return fail(LOGRA_ERR_ALIAS, "merge_grouped: U of descriptor %d overlaps W of %d", i, j);
-    }
-    items[i] = logra::MergeItem{key_words(e.key.seed, &e.key), key_words(sr_seed, &e.key), e.W, e.d, e.k,
-                                e.ldw, e.U, e.row0};
-  }
-  return hip_status(logra::launch_merge_grouped(items, n, r, scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
-                                                static_cast<hipStream_t>(stream)),
-                    "merge_grouped launch");
+  MergeOperands ops[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i)
+    ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw, descs[i].U,
+                           descs[i].row0};
+  return merge_grouped_impl("merge_grouped", r, ops, n, scale, scale_dev, mode, sr_seed, false, stream);
+}
+
+LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_desc* descs, int n,
+                                         double scale, const float* scale_dev, logra_round mode,
+                                         uint64_t sr_seed, logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped_packed: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP)
+    return fail(LOGRA_ERR_SHAPE, "merge_grouped_packed: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  MergeOperands ops[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i)
+    ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw,
+                           descs[i].U_packed, descs[i].row0};
+  return merge_grouped_impl("merge_grouped_packed", r, ops, n, scale, scale_dev, mode, sr_seed, true,
+                            stream);
 }
 
 LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r, void* W,

@@ -207,3 +207,37 @@ def test_merge_validation(lib):
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp, 1.0, None, 7, 0, 0, None) == B.ERR_DOMAIN
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, A + 1024, 1.0, None, 0, 0, 0, None) == B.ERR_ALIAS
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, Bp + 8, 1.0, None, 0, 0, 0, None) == B.ERR_ALIGN
+
+
+def test_packed_update_sizes_and_validation(lib):
+    # rows padded to 32, ranks to 16-rank steps padded to 1, 2, 4, 8 or 16; 4 bytes per element
+    assert B.packed_update_bytes(4096, 64) == 4096 * 64 * 4
+    assert B.packed_update_bytes(100, 33) == 128 * 64 * 4
+    assert B.packed_update_bytes(1, 1) == 32 * 16 * 4
+    assert B.packed_update_bytes(17408, 160) == 17408 * 256 * 4
+    assert B.packed_update_bytes(0, 8) == 0 and B.packed_update_bytes(8, 257) == 0
+    nb = B.packed_update_bytes(64, 8)
+    f = lib.logra_pack_update
+    assert err(f, 64, 8, None, Bp, nb, None) == B.ERR_NULL
+    assert err(f, 64, 300, A, Bp, nb, None) == B.ERR_SHAPE
+    assert err(f, 64, 8, A, Bp, nb - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 64, 8, A, Bp + 8, nb, None) == B.ERR_ALIGN
+    assert err(f, 64, 8, A, A + 256, nb, None) == B.ERR_ALIAS            # packed inside U
+    g = lib.logra_rowadam_packed
+    ws = B.rowadam_ws_bytes(64)
+    assert err(g, 64, 8, A, Bp, 1, 0.95, 1e-8, None, nb, Dp, ws, None) == B.ERR_NULL
+    assert err(g, 64, 8, A, Bp, 1, 0.95, 1e-8, C, nb - 16, Dp, ws, None) == B.ERR_WORKSPACE
+    assert err(g, 64, 8, A, Bp, 1, 0.95, 1e-8, A + 64, nb, Dp, ws, None) == B.ERR_ALIAS    # packed in S
+    assert err(g, 64, 300, A, Bp, 1, 0.95, 1e-8, C, nb, Dp, ws, None) == B.ERR_SHAPE
+    m = lib.logra_merge_grouped_packed
+    d2 = (B.MergePackedDesc * 2)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp, 0),
+                                 B.MergePackedDesc(key(), A + 4096, 64, 64, 64, C, 0))
+    assert err(m, 64, d2, 2, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # W overlap
+    assert err(m, 64, None, 1, 1.0, None, 0, 0, None) == B.ERR_NULL
+    assert err(m, 300, d2, 1, 1.0, None, 0, 0, None) == B.ERR_SHAPE
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, A + 512, 0))
+    assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # packed U inside W
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), Bp, 64, 64, 64, Bp - 16, 0))
+    assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # packed U runs into W
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp + 8, 0))
+    assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN

@@ -382,6 +382,66 @@ def test_merge_grouped_equals_single_merges(r, mode):
         assert frac >= 0.9999 and exact >= 0.999
 
 
+def packed_update_reference(U: np.ndarray, r: int) -> np.ndarray:
+    """The documented packed-update layout built on the host: per 32-row band and 16-rank
+    step (steps padded to a power of two), a hi slab then a lo slab of 64 lanes x 8 bf16,
+    lane l holding row 32g + (l & 31), ranks 16s + 8(l >> 5) + i."""
+    d = U.shape[0]
+    ks = 1
+    while 16 * ks < r:
+        ks *= 2
+    nb = (d + 31) // 32
+    Up = np.zeros((nb * 32, 16 * ks), np.float32)
+    Up[:d, :r] = U
+    hi = torch.from_numpy(Up).to(torch.bfloat16)
+    lo = (torch.from_numpy(Up) - hi.float()).to(torch.bfloat16)
+    out = []
+    for t in (hi, lo):
+        bits = t.view(torch.int16).numpy().view(np.uint16).reshape(nb, 32, ks, 2, 8)
+        # [band, row, step, half, i] -> [band, step, half, row, i]
+        out.append(bits.transpose(0, 2, 3, 1, 4).reshape(nb, ks, 64, 8))
+    return np.stack(out, axis=2).reshape(-1)          # [band, step, hi/lo, lane, i]
+
+
+@pytest.mark.parametrize("d,r", [(100, 33), (64, 64), (1000, 256), (7, 1), (300, 130)])
+def test_pack_update_layout_and_rowadam_packed(d, r):
+    """pack_update writes the documented operand layout; rowadam_packed writes the packed form of
+    the U that rowadam computes (same v as well)."""
+    say(f"packed update d={d} r={r}")
+    U = synth.fp32_matrix((d, r), 1.0, (26, d, r, 0, 7))
+    P = B.pack_update(torch.from_numpy(U).to(DEV))
+    assert np.array_equal(P.cpu().numpy().view(np.uint16), packed_update_reference(U, r))
+    S = torch.from_numpy(synth.fp32_matrix((d, r), 0.3, (26, d, r, 0, 5))).to(DEV)
+    v0 = torch.from_numpy(np.abs(synth.fp32_matrix((d, 1), 0.1, (26, d, 0, 0, 6)))[:, 0].copy()).to(DEV)
+    v1, v2 = v0.clone(), v0.clone()
+    Uf = B.rowadam(S, v1, 3, 0.95, 1e-8)
+    Pk = B.rowadam_packed(S, v2, 3, 0.95, 1e-8)
+    assert torch.equal(v1.view(torch.int32), v2.view(torch.int32))
+    assert torch.equal(Pk, B.pack_update(Uf))
+
+
+@pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "stochastic"), (8, "nearest"),
+                                    (100, "nearest"), (256, "stochastic"), (256, "nearest")])
+def test_merge_grouped_packed_equals_fp32_update(r, mode):
+    """The merge from a packed update gives the bits of the merge from the fp32 U it was packed
+    from, over full, ragged-row, ragged-column and small matrices in one grouped launch."""
+    shapes = [(320, 1024), (100, 712), (64, 3584), (96, 512), (1000, 1280)]
+    say(f"merge grouped packed r={r} {mode}")
+    items_p, items_u = [], []
+    for i, (d, k) in enumerate(shapes):
+        wb, _ = bf16_inputs((d, k), 0.02, (27, d, k, i, 2))
+        U = torch.from_numpy(synth.fp32_matrix((d, r), 1.0, (27, d, r, i, 7))).to(DEV)
+        kk = B.key(13, 50 + i, 2)
+        W1 = bf16_dev(wb)
+        items_u.append((kk, W1, U))
+        items_p.append((kk, W1.clone(), B.pack_update(U)))
+    alpha = torch.tensor([0.75], dtype=torch.float32, device=DEV)
+    B.merge_grouped(items_u, 3e-4, scale_dev=alpha, mode=mode, sr_seed=9)
+    B.merge_grouped_packed(items_p, r, 3e-4, scale_dev=alpha, mode=mode, sr_seed=9)
+    for (_, W1, _), (_, W2, _) in zip(items_u, items_p):
+        assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+
+
 def test_merge_rollout_sync_invariant_and_row_blocks():
     """Two merges of equal W with equal (U, key, scale, mode, sr_seed) are bit-identical;
     merging a row block with its global row offset equals the same rows of the whole merge."""
@@ -457,8 +517,9 @@ def test_full_size_layer_sampled(workload):
     """One full-size layer (q, k, v, o, gate, up, down; 7B shapes at r = 64, 27B shapes at
     r = 256; T = 4096) through the entry points and launch configuration the benchmark
     times: projections straight into packed operands, one grouped packed accumulate, one
-    grouped merge with the step size on the device.  S is checked on sampled rows of every
-    matrix against the oracle's X A^T and D^T (X A^T); W on sampled rows of every matrix."""
+    grouped merge from packed updates with the step size on the device.  S is checked on
+    sampled rows of every matrix against the oracle's X A^T and D^T (X A^T); W on sampled
+    rows of every matrix."""
     w = synth.BY_NAME[workload]
     T, r = w.T, w.r
     say(f"full-size layer of {workload}, sampled (bench configuration)")
@@ -489,10 +550,11 @@ def test_full_size_layer_sampled(workload):
         U = synth.fp32_matrix((d, r), 1.0, (25, mid, 0, 0, 7))
         mitems.append((B.key(w.seed, mid, w.step), bf16_dev(wbits), torch.from_numpy(U).to(DEV)))
         mhost.append((mid, d, k, wbits, U))
+    packed = [B.pack_update(U) for (_, _, U) in mitems]
     for mode in ("nearest", "stochastic"):
         Ws = [W.clone() for (_, W, _) in mitems]
-        B.merge_grouped([(kk, W2, U) for (kk, _, U), W2 in zip(mitems, Ws)], 1e-3, scale_dev=alpha,
-                        mode=mode, sr_seed=w.sr_seed)
+        B.merge_grouped_packed([(kk, W2, P) for (kk, _, _), W2, P in zip(mitems, Ws, packed)], r, 1e-3,
+                               scale_dev=alpha, mode=mode, sr_seed=w.sr_seed)
         for (mid, d, k, wbits, U), W2 in zip(mhost, Ws):
             rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 16)]))
             A = oracle.regen_A(w.seed, mid, w.step, r, k)
