@@ -267,6 +267,37 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
  * (LOGRA_ERR_DOMAIN). */
 LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double* alpha);
 
+/* KL budget of update u (1-based) on a cosine schedule over H updates
+ * ([paper] App. D.1 "KL budget", Table 4: 2e-4 down to 2e-5 over H = 300):
+ *   delta_u = delta_min + (delta_max - delta_min)/2 * (1 + cos(pi (u-1)/(H-1)))
+ * for u <= H, held at delta_min afterwards ([paper] App. D.2: annealed over
+ * the horizon, then held constant).  Host, fp64.
+ * Errors: NULL delta_u; u < 1, H < 2; delta_min < 0, delta_max < delta_min
+ * or non-finite (LOGRA_ERR_DOMAIN). */
+LOGRA_API int logra_kl_budget(int64_t u, int64_t H, double delta_max, double delta_min,
+                              double* delta_u);
+
+/* Smoothed rollout-versus-trainer log-probability mismatch kappa ([summary]
+ * D.1: averaged over completed non-truncated responses, smoothed with weight
+ * 0.3, clamped below at zero).  valid = 0 until a first measurement. */
+typedef struct logra_mismatch_state {
+  double kappa;
+  int32_t valid;
+  int32_t reserved;
+} logra_mismatch_state;
+
+/* Fold one measurement into the state: kappa <- max(0, w m + (1 - w) kappa),
+ * or max(0, m) for the first one.  A NaN measurement (no valid measurement
+ * this update) leaves the state unchanged.  weight is 0.3 in the pages.
+ * Errors: NULL state; weight outside (0, 1]; infinite measurement. */
+LOGRA_API int logra_mismatch_update(logra_mismatch_state* state, double measurement, double weight);
+
+/* delta_eff = max(delta_u - kappa, 0.5 delta_u) ([paper] App. D.1, Table 4
+ * "budget floor 50%"); delta_u itself while the state holds no measurement.
+ * Errors: NULL pointers; delta_u < 0 or non-finite. */
+LOGRA_API int logra_effective_budget(double delta_u, const logra_mismatch_state* state,
+                                     double* delta_eff);
+
 /* Device form: *alpha_dev = min(alpha_max, sqrt(delta / *q_dev)) in fp32;
  * q = 0 gives alpha_max; q < 0 or NaN gives NaN (checked on the host by the
  * caller if needed).  Errors: NULL pointers; delta <= 0 or alpha_max <= 0. */

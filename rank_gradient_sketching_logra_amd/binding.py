@@ -46,6 +46,10 @@ class MergePackedDesc(Structure):
                 ("U_packed", c_void_p), ("row0", c_int64)]
 
 
+class MismatchState(Structure):
+    _fields_ = [("kappa", c_double), ("valid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -74,6 +78,9 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_kl_budget": (c_int, [c_int64, c_int64, c_double, c_double, POINTER(c_double)]),
+    "logra_mismatch_update": (c_int, [POINTER(MismatchState), c_double, c_double]),
+    "logra_effective_budget": (c_int, [c_double, POINTER(MismatchState), POINTER(c_double)]),
     "logra_pack_update": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_rowadam_packed": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_double,
                                      c_double, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
@@ -346,3 +353,22 @@ def merge_grouped_packed(items, r: int, scale: float, scale_dev=None, mode: str 
     m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
     _check(lib().logra_merge_grouped_packed(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
                                             _stream(items[0][1], stream)))
+
+
+def kl_budget(u: int, H: int, delta_max: float, delta_min: float) -> float:
+    out = c_double(0.0)
+    _check(lib().logra_kl_budget(u, H, delta_max, delta_min, ctypes.byref(out)))
+    return out.value
+
+
+def mismatch_update(state: MismatchState, measurement, weight: float = 0.3) -> MismatchState:
+    """Fold one mismatch measurement (None: no valid measurement) into state, in place."""
+    m = float("nan") if measurement is None else float(measurement)
+    _check(lib().logra_mismatch_update(ctypes.byref(state), m, weight))
+    return state
+
+
+def effective_budget(delta_u: float, state: MismatchState) -> float:
+    out = c_double(0.0)
+    _check(lib().logra_effective_budget(delta_u, ctypes.byref(state), ctypes.byref(out)))
+    return out.value

@@ -325,6 +325,47 @@ LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double*
   return ok();
 }
 
+LOGRA_API int logra_kl_budget(int64_t u, int64_t H, double delta_max, double delta_min,
+                              double* delta_u) {
+  if (!delta_u) return fail(LOGRA_ERR_NULL, "kl_budget: NULL output");
+  if (u < 1 || H < 2) return fail(LOGRA_ERR_DOMAIN, "kl_budget: need u >= 1 and H >= 2");
+  if (!std::isfinite(delta_max) || !std::isfinite(delta_min) || delta_min < 0.0 || delta_max < delta_min)
+    return fail(LOGRA_ERR_DOMAIN, "kl_budget: need 0 <= delta_min <= delta_max, finite");
+  if (u >= H) {
+    *delta_u = delta_min;
+    return ok();
+  }
+  const double pi = 3.14159265358979323846;
+  *delta_u = delta_min + 0.5 * (delta_max - delta_min) *
+                             (1.0 + std::cos(pi * (double)(u - 1) / (double)(H - 1)));
+  return ok();
+}
+
+LOGRA_API int logra_mismatch_update(logra_mismatch_state* state, double measurement, double weight) {
+  if (!state) return fail(LOGRA_ERR_NULL, "mismatch_update: NULL state");
+  if (!(weight > 0.0 && weight <= 1.0)) return fail(LOGRA_ERR_DOMAIN, "mismatch_update: weight must be in (0, 1]");
+  if (std::isinf(measurement)) return fail(LOGRA_ERR_DOMAIN, "mismatch_update: infinite measurement");
+  if (std::isnan(measurement)) return ok();  // no valid measurement this update
+  const double k = state->valid ? weight * measurement + (1.0 - weight) * state->kappa : measurement;
+  state->kappa = k > 0.0 ? k : 0.0;
+  state->valid = 1;
+  return ok();
+}
+
+LOGRA_API int logra_effective_budget(double delta_u, const logra_mismatch_state* state,
+                                     double* delta_eff) {
+  if (!state || !delta_eff) return fail(LOGRA_ERR_NULL, "effective_budget: NULL pointer");
+  if (!(delta_u >= 0.0) || !std::isfinite(delta_u)) return fail(LOGRA_ERR_DOMAIN, "effective_budget: delta_u must be finite and >= 0");
+  if (!state->valid) {
+    *delta_eff = delta_u;
+    return ok();
+  }
+  const double sub = delta_u - state->kappa;
+  const double floor = 0.5 * delta_u;
+  *delta_eff = sub > floor ? sub : floor;
+  return ok();
+}
+
 LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_max,
                                    float* alpha_dev, logra_stream stream) {
   if (!q_dev || !alpha_dev) return fail(LOGRA_ERR_NULL, "step_alpha_dev: NULL pointer");
