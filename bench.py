@@ -358,6 +358,23 @@ def main():
                                 "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
                                 "frac": round(fl / (avg_launch_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFS, 4),
                                 "flops_per_launch": fl})
+    # The reconstruction-cosine diagnostic on one dense gradient of the largest projection
+    # (outside the timed step; the method itself never forms G).
+    (_, dkind, dmid, dd, dk) = max(mats, key=lambda m: m[3] * m[4])
+    G = randn((dd, dk), 1e-2)
+    cws = B.workspace(B.reconstruction_cosine_ws_bytes(dd, dk, r), dev)
+    cout = torch.empty((4,), dtype=torch.float64, device=dev)
+    B.reconstruction_cosine(keys[(0, dkind)], G, r, out=cout, ws=cws)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        B.reconstruction_cosine(keys[(0, dkind)], G, r, out=cout, ws=cws)
+    c1.record()
+    torch.cuda.synchronize()
+    cus = c0.elapsed_time(c1) * 1e3 / 5
+    out["diagnostics"] = {"reconstruction_cosine": {
+        "matrix": f"{dkind} {dd}x{dk} bf16", "r": r, "cos": round(float(cout[0].item()), 6),
+        "us": round(cus, 1), "g_read_gbs": round(2 * dd * dk / (cus * 1e-6) / 1e9, 1)}}
     if not args.skip_cpu_baseline and layers == w.layers and w.name == DEFAULT_WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(w, rounding)
     print(json.dumps(out), flush=True)

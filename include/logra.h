@@ -137,6 +137,28 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
                                   const void* X, logra_dtype x_dtype, int64_t ldx,
                                   float* XAt, logra_stream stream);
 
+/* ------------------------------------------------------------ diagnostic */
+
+/* Workspace bytes of logra_reconstruction_cosine (0 for invalid sizes). */
+LOGRA_API size_t logra_reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r);
+
+/* How much of a dense gradient the sketch keeps: the Frobenius cosine
+ * between G [d x k] and its reconstruction (G A^T) A, A from `key` ([paper]
+ * App. D.3 "Reconstruction heatmaps"; Fig. 5 reports 0.046 at r = 4 up to
+ * 0.348 at r = 256 for Qwen2.5-1.5B gradients).  Written to out_dev (4
+ * doubles on the device): {cos, ||G||_F^2, ||G A^T||_F^2, ||(G A^T) A||_F^2}.
+ * Computed as ||S||^2 / (||G|| sqrt(sum_i S_i (A A^T) S_i^T)) with
+ * S = G A^T from the projection (bf16 G on matrix cores, fp32 G in fp64)
+ * and A A^T exact from the sign bits; sums in fp64, fixed order.  G is bf16
+ * or fp32 with leading dimension ldg >= k.  The dense G exists only for this
+ * diagnostic; the method never forms it.
+ * Errors: NULL pointers; d < 1, k < 1, r < 1, r > LOGRA_MAX_RANK, ldg < k;
+ * alignment; workspace too small; G, output and workspace overlapping. */
+LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64_t k, int64_t r,
+                                          const void* G, logra_dtype g_dtype, int64_t ldg,
+                                          double* out_dev, void* ws, size_t ws_bytes,
+                                          logra_stream stream);
+
 /* ---------------------------------------------------------------- sketch */
 
 /* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a

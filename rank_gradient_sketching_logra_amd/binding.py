@@ -78,6 +78,9 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_reconstruction_cosine_ws_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
+    "logra_reconstruction_cosine": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
+                                            c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_kl_budget": (c_int, [c_int64, c_int64, c_double, c_double, POINTER(c_double)]),
     "logra_mismatch_update": (c_int, [POINTER(MismatchState), c_double, c_double]),
     "logra_effective_budget": (c_int, [c_double, POINTER(MismatchState), POINTER(c_double)]),
@@ -372,3 +375,18 @@ def effective_budget(delta_u: float, state: MismatchState) -> float:
     out = c_double(0.0)
     _check(lib().logra_effective_budget(delta_u, ctypes.byref(state), ctypes.byref(out)))
     return out.value
+
+
+def reconstruction_cosine_ws_bytes(d: int, k: int, r: int) -> int:
+    return lib().logra_reconstruction_cosine_ws_bytes(d, k, r)
+
+
+def reconstruction_cosine(k_: Key, G: torch.Tensor, r: int, out=None, ws=None, stream=None):
+    """{cos(G, (G A^T) A), ||G||^2, ||G A^T||^2, ||G A^T A||^2} on the device (fp64 [4])."""
+    d, kk = G.shape
+    o = out if out is not None else torch.empty((4,), dtype=torch.float64, device=G.device)
+    if ws is None:
+        ws = workspace(reconstruction_cosine_ws_bytes(d, kk, r), G.device)
+    _check(lib().logra_reconstruction_cosine(ctypes.byref(k_), d, kk, r, _ptr(G), _dtype_code(G), _ld(G),
+                                             _ptr(o), _ptr(ws), ws.numel(), _stream(G, stream)))
+    return o

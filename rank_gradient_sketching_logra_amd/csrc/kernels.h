@@ -41,6 +41,13 @@ hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const voi
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
                              bool packed, hipStream_t s);
 
+// cos(G, (G A^T) A) and its parts {cos, ||G||^2, ||G A^T||^2, ||G A^T A||^2}
+// written to out (4 doubles on the device).
+size_t reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r);
+hipError_t launch_reconstruction_cosine(KeyArg key, int64_t d, int64_t k, int64_t r, const void* G,
+                                        bool bf16, int64_t ldg, double* out, void* ws,
+                                        hipStream_t s);
+
 size_t rowadam_ws_bytes(int64_t d);
 // U (fp32) and/or U_packed (the merge's packed update) may be null.
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,

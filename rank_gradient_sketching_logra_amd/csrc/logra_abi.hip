@@ -107,6 +107,33 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
                     "project_input launch");
 }
 
+LOGRA_API size_t logra_reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r) {
+  if (d < 1 || k < 1 || bad_rank(r)) return 0;
+  return logra::reconstruction_cosine_ws_bytes(d, k, r);
+}
+
+LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64_t k, int64_t r,
+                                          const void* G, logra_dtype g_dtype, int64_t ldg,
+                                          double* out_dev, void* ws, size_t ws_bytes,
+                                          logra_stream stream) {
+  if (!key || !G || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine: NULL pointer");
+  if (d < 1 || k < 1 || bad_rank(r))
+    return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  int st = check_matrix("reconstruction_cosine G", G, g_dtype, ldg, k);
+  if (st) return st;
+  const size_t need = logra::reconstruction_cosine_ws_bytes(d, k, r);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "reconstruction_cosine: workspace of %zu bytes needed", need);
+  if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(out_dev) & 7u) != 0)
+    return fail(LOGRA_ERR_ALIGN, "reconstruction_cosine: workspace 16-byte and output 8-byte aligned");
+  const Range rg = range(G, extent(d, k, ldg, elem_size(g_dtype))), rw = range(ws, need), ro = range(out_dev, 32);
+  if (overlap(rg, rw) || overlap(rg, ro) || overlap(rw, ro))
+    return fail(LOGRA_ERR_ALIAS, "reconstruction_cosine: G, output and workspace must not overlap");
+  return hip_status(logra::launch_reconstruction_cosine(key_words(key->seed, key), d, k, r, G,
+                                                        g_dtype == LOGRA_BF16, ldg, out_dev, ws,
+                                                        static_cast<hipStream_t>(stream)),
+                    "reconstruction_cosine launch");
+}
+
 LOGRA_API size_t logra_packed_input_bytes(int64_t T, int64_t r) {
   if (T < 1 || bad_rank(r)) return 0;
   return logra::acc_ws_bytes_per_item(T, 1, r);

@@ -241,3 +241,18 @@ def test_packed_update_sizes_and_validation(lib):
     assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # packed U runs into W
     d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp + 8, 0))
     assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
+
+
+def test_reconstruction_cosine_sizes_and_validation(lib):
+    assert B.reconstruction_cosine_ws_bytes(1000, 1536, 64) >= 1000 * 64 * 4 + 64 * 64 * 8
+    assert B.reconstruction_cosine_ws_bytes(0, 8, 8) == 0 and B.reconstruction_cosine_ws_bytes(8, 8, 300) == 0
+    f = lib.logra_reconstruction_cosine
+    k = ctypes.byref(key())
+    ws = B.reconstruction_cosine_ws_bytes(64, 64, 8)
+    assert err(f, k, 64, 64, 8, None, B.BF16, 64, C, Dp, ws, None) == B.ERR_NULL
+    assert err(f, k, 64, 64, 300, A, B.BF16, 64, C, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, k, 64, 64, 8, A, 7, 64, C, Dp, ws, None) == B.ERR_DTYPE
+    assert err(f, k, 64, 64, 8, A, B.BF16, 60, C, Dp, ws, None) == B.ERR_SHAPE        # ldg < k
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, C, Dp, ws - 8, None) == B.ERR_WORKSPACE
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, C + 4, Dp, ws, None) == B.ERR_ALIGN     # output
+    assert err(f, k, 64, 64, 8, A, B.BF16, 64, C, A + 512, ws, None) == B.ERR_ALIAS    # workspace in G

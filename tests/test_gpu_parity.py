@@ -509,6 +509,34 @@ def test_merge_fp32_unit_factor_and_values():
     assert np.max(np.abs(got.astype(np.float64) - want) / np.spacing(np.abs(want))) <= 1.0
 
 
+# ------------------------------------------------ reconstruction cosine
+
+
+@pytest.mark.parametrize("d,k,r,dtype,ld", [(64, 256, 8, "bf16", 256), (300, 712, 33, "bf16", 720),
+                                            (1000, 1536, 64, "bf16", 1536), (517, 1536, 256, "bf16", 1536),
+                                            (40, 300, 5, "f32", 304), (18944, 3584, 64, "bf16", 3584)])
+def test_reconstruction_cosine(d, k, r, dtype, ld):
+    """cos(G, (G A^T) A) and its parts against the oracle's direct definition ([paper] App. D.3);
+    the last case is a 7B gate-projection gradient at full size."""
+    say(f"reconstruction cosine d={d} k={k} r={r} {dtype}")
+    bits_or_x = synth.normal((d, ld), 0.01, (28, d, k, r, 1), dtype)
+    if dtype == "bf16":
+        G = bf16_dev(bits_or_x)[:, :k]
+        Gh = oracle.bf16_bits_to_f64(bits_or_x)[:, :k]
+    else:
+        G = torch.from_numpy(bits_or_x).to(DEV)[:, :k]
+        Gh = bits_or_x[:, :k].astype(np.float64)
+    out = B.reconstruction_cosine(B.key(4, 9, 1), G, r).cpu().numpy()
+    A = oracle.regen_A(4, 9, 1, r, k)
+    want = oracle.reconstruction_cosine(Gh, A)
+    S = Gh @ A.T
+    say(f"  cos {out[0]:.6f} oracle {want:.6f}")
+    assert out[0] == pytest.approx(want, rel=1e-5)
+    assert out[1] == pytest.approx((Gh * Gh).sum(), rel=1e-12)
+    assert out[2] == pytest.approx((S * S).sum(), rel=1e-5)
+    assert out[3] == pytest.approx(((S @ A) ** 2).sum(), rel=1e-5)
+
+
 # --------------------------------------------- full-size shapes (sampled)
 
 
