@@ -412,6 +412,56 @@ LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_des
                                          double scale, const float* scale_dev, logra_round mode,
                                          uint64_t sr_seed, logra_stream stream);
 
+/* ------------------------------------------------------ policy sync */
+
+/* What the trainer sends the rollout side for one matrix ([paper] §2.2
+ * "Memory and synchronization": the engine regenerates A from its seed and
+ * applies the received alpha*eta*U, O(d r) instead of the d k weights).  The
+ * payload is the packed update of fl32(s U), s the merge step size; both
+ * sides then merge from the same payload with scale 1, so their weights stay
+ * bit-identical.  Transport is the caller's: the header is plain data (host
+ * memory) and the payload payload_bytes of device memory. */
+#define LOGRA_SYNC_MAGIC 0x4C475253u  /* "LGRS" */
+#define LOGRA_SYNC_VERSION 1u
+typedef struct logra_sync_header {
+  uint32_t magic;          /* LOGRA_SYNC_MAGIC                               */
+  uint32_t version;        /* LOGRA_SYNC_VERSION                             */
+  logra_key key;           /* key of the matrix's A                          */
+  int64_t d, k, r;         /* W [d x k], rank r                              */
+  int32_t mode;            /* logra_round                                    */
+  int32_t reserved;
+  uint64_t sr_seed;        /* stochastic-rounding seed                       */
+  int64_t row0;            /* global index of the first row                  */
+  uint64_t payload_bytes;  /* logra_packed_update_bytes(d, r)                */
+} logra_sync_header;
+
+/* Build one matrix's payload: header filled on the host, payload (device,
+ * payload_bytes >= logra_packed_update_bytes(d, r)) = packed fl32(s U) with
+ * s = scale * (*scale_dev if scale_dev != NULL else 1).
+ * Errors: NULL pointers; d < 1, k < 1, r < 1, r > LOGRA_MAX_RANK, row0 < 0;
+ * unknown mode; non-finite scale; payload too small or misaligned; U
+ * overlapping the payload. */
+LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_t r,
+                              const float* U, double scale, const float* scale_dev,
+                              logra_round mode, uint64_t sr_seed, int64_t row0,
+                              logra_sync_header* header, void* payload, size_t payload_bytes,
+                              logra_stream stream);
+
+/* One matrix to apply: its header and payload, and the local bf16 W. */
+typedef struct logra_sync_desc {
+  const logra_sync_header* header;
+  const void* payload;
+  void* W;        /* [d x k] bf16, leading dimension ldw */
+  int64_t ldw;
+} logra_sync_desc;
+
+/* Apply n <= LOGRA_MAX_GROUP payloads sharing r, mode and sr_seed in one
+ * launch: W <- round(W - (P as U) A) with scale 1 -- the merge both sides run.
+ * Errors: NULL pointers; a bad magic or version, or a header whose
+ * payload_bytes does not match its d and r (LOGRA_ERR_DOMAIN); mixed r, mode
+ * or sr_seed; otherwise as logra_merge_grouped_packed. */
+LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

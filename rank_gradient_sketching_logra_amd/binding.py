@@ -50,6 +50,16 @@ class MismatchState(Structure):
     _fields_ = [("kappa", c_double), ("valid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class SyncHeader(Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("key", Key), ("d", c_int64),
+                ("k", c_int64), ("r", c_int64), ("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sr_seed", c_uint64), ("row0", c_int64), ("payload_bytes", c_uint64)]
+
+
+class SyncDesc(Structure):
+    _fields_ = [("header", POINTER(SyncHeader)), ("payload", c_void_p), ("W", c_void_p), ("ldw", c_int64)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -78,6 +88,10 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_sync_pack": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_double, c_void_p,
+                                c_int, c_uint64, c_int64, POINTER(SyncHeader), c_void_p, c_size_t,
+                                c_void_p]),
+    "logra_sync_apply": (c_int, [POINTER(SyncDesc), c_int, c_void_p]),
     "logra_reconstruction_cosine_ws_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
     "logra_reconstruction_cosine": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int,
                                             c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -390,3 +404,29 @@ def reconstruction_cosine(k_: Key, G: torch.Tensor, r: int, out=None, ws=None, s
     _check(lib().logra_reconstruction_cosine(ctypes.byref(k_), d, kk, r, _ptr(G), _dtype_code(G), _ld(G),
                                              _ptr(o), _ptr(ws), ws.numel(), _stream(G, stream)))
     return o
+
+
+def sync_pack(k_: Key, W_shape, U: torch.Tensor, scale: float, scale_dev=None, mode: str = "nearest",
+              sr_seed: int = 0, row0: int = 0, out=None, stream=None):
+    """(header, payload): what the trainer sends for one matrix -- the packed fl32(s U)."""
+    d, r = U.shape
+    kk = int(W_shape[1])
+    nb = packed_update_bytes(d, r)
+    P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=U.device)
+    h = SyncHeader()
+    m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
+    _check(lib().logra_sync_pack(ctypes.byref(k_), d, kk, r, _ptr(U), float(scale), _ptr(scale_dev), m,
+                                 sr_seed, row0, ctypes.byref(h), _ptr(P), P.numel() * P.element_size(),
+                                 _stream(U, stream)))
+    return h, P
+
+
+def sync_apply(items, stream=None):
+    """items: sequence of (header, payload, W); one grouped merge with scale 1."""
+    n = len(items)
+    descs = (SyncDesc * n)()
+    keep = []
+    for i, (h, P, W) in enumerate(items):
+        keep.append(h)
+        descs[i] = SyncDesc(ctypes.pointer(h), P.data_ptr(), W.data_ptr(), _ld(W))
+    _check(lib().logra_sync_apply(descs, n, _stream(items[0][2], stream)))

@@ -75,7 +75,9 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
 // 16-rank steps of the merge (1, 2, 4, 8 or 16) and the packed update's size.
 int merge_rank_steps(int64_t r);
 size_t packed_update_bytes(int64_t d, int64_t r);
-hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, void* packed, hipStream_t s);
+// packed = split(fl32(s U)), s = scale * (*scale_dev if given).
+hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, float scale,
+                              const float* scale_dev, void* packed, hipStream_t s);
 hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,
                         int64_t ldw, const float* U, double scale, const float* scale_dev,
                         bool stochastic, KeyArg sr_key, int64_t row0, hipStream_t s);

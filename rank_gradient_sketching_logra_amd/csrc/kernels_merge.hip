@@ -779,7 +779,8 @@ hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bo
   return launch_merge_grouped(&it, 1, r, scale, scale_dev, stochastic, false, s);
 }
 
-// Packed update: U [d x r] fp32 as the merge's B operands.  For 32-row band
+// Packed update: U [d x r] fp32 (times a scale, 1 for a plain update) as the
+// merge's B operands.  For 32-row band
 // g and 16-rank step s (steps padded to KS = 1, 2, 4, 8 or 16), a 1 KiB hi
 // slab then a 1 KiB lo slab, lane l holding rows 32g + (l & 31), ranks
 // 16s + 8(l >> 5) + i (i = 0..7) as bf16 hi = RNE(u), lo = RNE(u - hi);
@@ -793,7 +794,8 @@ size_t packed_update_bytes(int64_t d, int64_t r) {
 }
 
 namespace {
-__global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, int ks,
+__global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, int ks, float scale,
+                                                          const float* __restrict__ scale_dev,
                                                           const float* __restrict__ U,
                                                           uint16_t* __restrict__ P) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (band, step, lane)
@@ -805,9 +807,10 @@ __global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, 
   const int s = (int)(bs - band * ks);
   const int64_t row = band * 32 + (lane & 31);
   const int64_t j0 = 16 * s + 8 * (lane >> 5);
+  const float sc = scale_dev != nullptr ? scale * *scale_dev : scale;
   float x[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = (row < d && j0 + i < r) ? U[row * r + j0 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) x[i] = (row < d && j0 + i < r) ? sc * U[row * r + j0 + i] : 0.f;
   u32x4 hv, lv;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -821,11 +824,12 @@ __global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, 
 }
 }  // namespace
 
-hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, void* packed, hipStream_t s) {
+hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, float scale,
+                              const float* scale_dev, void* packed, hipStream_t s) {
   const int ks = merge_rank_steps(r);
   const int64_t threads = (d + 31) / 32 * ks * 64;
   hipLaunchKernelGGL(pack_update_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     d, r, ks, U, static_cast<uint16_t*>(packed));
+                     d, r, ks, scale, scale_dev, U, static_cast<uint16_t*>(packed));
   return hipGetLastError();
 }
 

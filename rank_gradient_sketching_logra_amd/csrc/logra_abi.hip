@@ -319,7 +319,7 @@ LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_pa
   if (!aligned16(U_packed)) return fail(LOGRA_ERR_ALIGN, "pack_update: the packed update must be 16-byte aligned");
   if (overlap(range(U, (size_t)(d * r) * 4), range(U_packed, need)))
     return fail(LOGRA_ERR_ALIAS, "pack_update: U overlaps the packed update");
-  return hip_status(logra::launch_pack_update(d, r, U, U_packed, static_cast<hipStream_t>(stream)),
+  return hip_status(logra::launch_pack_update(d, r, U, 1.0f, nullptr, U_packed, static_cast<hipStream_t>(stream)),
                     "pack_update launch");
 }
 
@@ -470,6 +470,57 @@ LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_des
                            descs[i].U_packed, descs[i].row0};
   return merge_grouped_impl("merge_grouped_packed", r, ops, n, scale, scale_dev, mode, sr_seed, true,
                             stream);
+}
+
+LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_t r,
+                              const float* U, double scale, const float* scale_dev,
+                              logra_round mode, uint64_t sr_seed, int64_t row0,
+                              logra_sync_header* header, void* payload, size_t payload_bytes,
+                              logra_stream stream) {
+  if (!key || !U || !header || !payload) return fail(LOGRA_ERR_NULL, "sync_pack: NULL pointer");
+  if (d < 1 || k < 1 || bad_rank(r) || row0 < 0)
+    return fail(LOGRA_ERR_SHAPE, "sync_pack: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
+  if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "sync_pack: unknown rounding mode");
+  if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "sync_pack: scale must be finite");
+  const size_t need = logra::packed_update_bytes(d, r);
+  if (payload_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "sync_pack: the payload needs %zu bytes", need);
+  if (!aligned16(payload)) return fail(LOGRA_ERR_ALIGN, "sync_pack: payload must be 16-byte aligned");
+  if (overlap(range(U, (size_t)(d * r) * 4), range(payload, need)))
+    return fail(LOGRA_ERR_ALIAS, "sync_pack: U overlaps the payload");
+  header->magic = LOGRA_SYNC_MAGIC;
+  header->version = LOGRA_SYNC_VERSION;
+  header->key = *key;
+  header->d = d;
+  header->k = k;
+  header->r = r;
+  header->mode = (int32_t)mode;
+  header->reserved = 0;
+  header->sr_seed = sr_seed;
+  header->row0 = row0;
+  header->payload_bytes = need;
+  return hip_status(logra::launch_pack_update(d, r, U, (float)scale, scale_dev, payload,
+                                              static_cast<hipStream_t>(stream)),
+                    "sync_pack launch");
+}
+
+LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "sync_apply: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sync_apply: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  MergeOperands ops[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    const logra_sync_header* h = descs[i].header;
+    if (!h || !descs[i].payload || !descs[i].W) return fail(LOGRA_ERR_NULL, "sync_apply: NULL pointer in descriptor %d", i);
+    if (h->magic != LOGRA_SYNC_MAGIC || h->version != LOGRA_SYNC_VERSION)
+      return fail(LOGRA_ERR_DOMAIN, "sync_apply: descriptor %d has no valid header", i);
+    if (h->d < 1 || h->k < 1 || bad_rank(h->r) || h->payload_bytes != logra::packed_update_bytes(h->d, h->r))
+      return fail(LOGRA_ERR_DOMAIN, "sync_apply: header %d sizes are inconsistent", i);
+    if (h->r != descs[0].header->r || h->mode != descs[0].header->mode || h->sr_seed != descs[0].header->sr_seed)
+      return fail(LOGRA_ERR_SHAPE, "sync_apply: descriptors must share r, mode and sr_seed");
+    ops[i] = MergeOperands{&h->key, descs[i].W, h->d, h->k, descs[i].ldw, descs[i].payload, h->row0};
+  }
+  const logra_sync_header* h0 = descs[0].header;
+  return merge_grouped_impl("sync_apply", h0->r, ops, n, 1.0, nullptr, (logra_round)h0->mode, h0->sr_seed,
+                            true, stream);
 }
 
 LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r, void* W,

@@ -256,3 +256,38 @@ def test_reconstruction_cosine_sizes_and_validation(lib):
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, C, Dp, ws - 8, None) == B.ERR_WORKSPACE
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, C + 4, Dp, ws, None) == B.ERR_ALIGN     # output
     assert err(f, k, 64, 64, 8, A, B.BF16, 64, C, A + 512, ws, None) == B.ERR_ALIAS    # workspace in G
+
+
+def test_sync_payload_validation(lib):
+    f = lib.logra_sync_pack
+    k = ctypes.byref(key())
+    nb = B.packed_update_bytes(64, 8)
+    h = B.SyncHeader()
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 0, 0, 0, None, Bp, nb, None) == B.ERR_NULL
+    assert err(f, k, 64, 128, 300, A, 1e-3, None, 0, 0, 0, ctypes.byref(h), Bp, nb, None) == B.ERR_SHAPE
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 0, 0, -1, ctypes.byref(h), Bp, nb, None) == B.ERR_SHAPE
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 3, 0, 0, ctypes.byref(h), Bp, nb, None) == B.ERR_DOMAIN
+    assert err(f, k, 64, 128, 8, A, float("nan"), None, 0, 0, 0, ctypes.byref(h), Bp, nb, None) == B.ERR_DOMAIN
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 0, 0, 0, ctypes.byref(h), Bp, nb - 1, None) == B.ERR_WORKSPACE
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 0, 0, 0, ctypes.byref(h), Bp + 8, nb, None) == B.ERR_ALIGN
+    assert err(f, k, 64, 128, 8, A, 1e-3, None, 0, 0, 0, ctypes.byref(h), A + 64, nb, None) == B.ERR_ALIAS
+    assert h.magic == 0                                   # no header written on failure
+
+    def header(d=64, kk=128, r=8, mode=0, seed=0, magic=0x4C475253, version=1, nbytes=None):
+        return B.SyncHeader(magic, version, key(), d, kk, r, mode, 0, seed, 0,
+                            B.packed_update_bytes(d, r) if nbytes is None else nbytes)
+    g = lib.logra_sync_apply
+
+    def descs(*hs):
+        arr = (B.SyncDesc * len(hs))()
+        for i, hh in enumerate(hs):
+            arr[i] = B.SyncDesc(ctypes.pointer(hh), Bp + 0x100000 * i, C + 0x100000 * i, hh.k)
+        return arr
+    h1, h2 = header(), header(magic=7)
+    assert err(g, descs(h1, h2), 2, None) == B.ERR_DOMAIN           # bad magic
+    assert err(g, descs(header(version=2)), 1, None) == B.ERR_DOMAIN
+    assert err(g, descs(header(nbytes=16)), 1, None) == B.ERR_DOMAIN  # sizes disagree
+    assert err(g, descs(header(), header(r=16)), 2, None) == B.ERR_SHAPE
+    assert err(g, descs(header(), header(mode=1)), 2, None) == B.ERR_SHAPE
+    assert err(g, descs(header()), 0, None) == B.ERR_SHAPE
+    assert err(g, None, 1, None) == B.ERR_NULL

@@ -442,6 +442,37 @@ def test_merge_grouped_packed_equals_fp32_update(r, mode):
         assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
 
 
+@pytest.mark.parametrize("r,mode", [(64, "stochastic"), (33, "nearest"), (256, "stochastic")])
+def test_sync_payload_trainer_and_rollout_agree(r, mode):
+    """Policy sync ([paper] §2.2): the trainer packs fl32(alpha eta U) once; its own merge from the
+    payload and the rollout side's sync_apply give identical weights, and both match the oracle's
+    merge with the same update to the merge bar."""
+    shapes = [(320, 1024), (100, 712), (64, 512)]
+    say(f"sync payload r={r} {mode}")
+    alpha = torch.tensor([0.6], dtype=torch.float32, device=DEV)
+    trainer, rollout, host = [], [], []
+    for i, (d, k) in enumerate(shapes):
+        wb, W64 = bf16_inputs((d, k), 0.02, (29, d, k, i, 2))
+        U = synth.fp32_matrix((d, r), 1.0, (29, d, r, i, 7))
+        kk = B.key(17, 60 + i, 4)
+        h, P = B.sync_pack(kk, (d, k), torch.from_numpy(U).to(DEV), 5e-4, scale_dev=alpha, mode=mode,
+                           sr_seed=3)
+        assert (h.magic, h.version, h.d, h.k, h.r, h.payload_bytes) == (0x4C475253, 1, d, k, r,
+                                                                        B.packed_update_bytes(d, r))
+        trainer.append((kk, bf16_dev(wb), P))
+        rollout.append((h, P, bf16_dev(wb)))
+        host.append((i, d, k, W64, U))
+    B.merge_grouped_packed(trainer, r, 1.0, mode=mode, sr_seed=3)
+    B.sync_apply(rollout)
+    for (_, W1, _), (_, _, W2), (i, d, k, W64, U) in zip(trainer, rollout, host):
+        assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+        A = oracle.regen_A(17, 60 + i, 4, r, k)
+        u = philox.sr_draws(3, 60 + i, 4, d, k) if mode == "stochastic" else None
+        want = oracle.merge(W64, U.astype(np.float64), A, 5e-4 * 0.6, w_dtype="bf16", mode=mode, u_draws=u)
+        frac, exact = ulp_check(bf16_host(W2), want)
+        assert frac >= 0.9999 and exact >= 0.999
+
+
 def test_merge_rollout_sync_invariant_and_row_blocks():
     """Two merges of equal W with equal (U, key, scale, mode, sr_seed) are bit-identical;
     merging a row block with its global row offset equals the same rows of the whole merge."""
