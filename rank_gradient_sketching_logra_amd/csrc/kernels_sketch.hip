@@ -88,40 +88,52 @@ __global__ void regen_A_kernel(KeyArg key, int64_t r, int64_t k, int int8_out, f
 
 // ------------------------------------------------------------- project
 
-// bf16 X: one block = 32 tokens x all ranks; the four waves take the
-// 256-column blocks of k round-robin, then add their partial tiles in a
-// fixed order.  NBT = padded rank / 32.
-template <int NBT>
-__global__ __launch_bounds__(256) void project_bf16_kernel(KeyArg key, int64_t T, int64_t k,
-                                                           int64_t r,
-                                                           const uint16_t* __restrict__ X,
-                                                           int64_t ldx, float cr,
-                                                           float* __restrict__ XAt,
-                                                           uint16_t* __restrict__ planes,
-                                                           int nrb, int nsteps) {
-  constexpr int NQ = (NBT + 1) / 2;
-  constexpr int RP = NBT * 32;
-  __shared__ __align__(16) float red[32][RP + 1];
+// bf16 X: one block = 16 tokens (one 16-token step of the packed form) x
+// all ranks.  Its eight waves take the 256-column blocks of k round-robin,
+// each with the loads of its next block in flight while it computes the
+// current one, then add their partial tiles in a fixed order.  The product is
+// v_mfma_f32_16x16x32_bf16: A lane l holds token t0 + (l & 15), columns
+// 32s + 8(l >> 4) .. +7 of the 256-column block (s = 0..7); B lane l holds
+// the signs of rank 16nb + (l & 15) for the same columns, expanded from the
+// Philox words of the lane that generated that rank; C lane l holds rank
+// 16nb + (l & 15) of tokens t0 + 4(l >> 4) + j in register j.  NB16 =
+// 16-rank blocks computed (>= r / 16).
+constexpr int kProjTokens = 16;
+constexpr int kProjWaves = 8;
+
+template <int NB16>
+__global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
+    KeyArg key, int64_t T, int64_t k, int64_t r, const uint16_t* __restrict__ X, int64_t ldx,
+    float cr, float* __restrict__ XAt, uint16_t* __restrict__ planes, int nrb, int nsteps) {
+  constexpr int NQ = (NB16 + 3) / 4;  // 64-rank groups, one Philox block per lane each
+  constexpr int RP = NB16 * 16;
+  __shared__ float red[kProjTokens][RP + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int64_t t0 = (int64_t)blockIdx.x * 32;
-  const int64_t trow = t0 + (lane & 31);
+  const int g4 = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kProjTokens;
+  const int64_t trow = t0 + (lane & 15);
   const KeyWords kw{key.k0, key.k1};
 
-  f32x16 acc[NBT];
+  f32x4 acc[NB16];
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[nb][e] = 0.f;
+  for (int nb = 0; nb < NB16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t nblk = (k + 255) >> 8;
-  for (int64_t b = wave; b < nblk; b += 4) {
+  u32x4 a[8];
+  auto load = [&](int64_t b, u32x4 (&dst)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dst[s] = load_bf16x8(X, ldx, trow, b * 256 + 32 * s + 8 * g4, T, k);
+  };
+  if (wave < nblk) load(wave, a);
+  for (int64_t b = wave; b < nblk; b += kProjWaves) {
+    u32x4 an[8];
+    if (b + kProjWaves < nblk) load(b + kProjWaves, an);
     uint32_t bits[NQ][8];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int64_t j = lane + 64 * q;
-      Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
+      const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
       const bool live = j < r;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -129,61 +141,57 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(KeyArg key, int64_t T
         bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
       }
     }
-    u32x4 a[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      a[s] = load_bf16x8(X, ldx, trow, b * 256 + 16 * s + 8 * half, T, k);
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-#pragma unroll
-      for (int nb = 0; nb < NBT; ++nb) {
-        const int src = (nb & 1) * 32 + (lane & 31);
-        const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 1][s >> 1], src, 64);
-        const uint32_t byte = (wv >> (16 * (s & 1) + 8 * half)) & 0xFFu;
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[s]),
-                                                          as_bf16x8(expand_signs(byte)),
-                                                          acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB16; ++nb) {
+        const int src = 16 * (nb & 3) + (lane & 15);
+        const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
+        const uint32_t byte = (wv >> (8 * g4)) & 0xFFu;
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]),
+                                                          as_bf16x8(expand_signs(byte)), acc[nb],
+                                                          0, 0, 0);
       }
+    }
+    if (b + kProjWaves < nblk) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) a[s] = an[s];
     }
   }
 
-  // Fixed-order reduction over the four waves: ((w0 + w1) + w2) + w3.
-  for (int w = 0; w < 4; ++w) {
+  // Fixed-order reduction over the eight waves: (((w0 + w1) + w2) + ...) + w7.
+  for (int w = 0; w < kProjWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int nb = 0; nb < NBT; ++nb)
+      for (int nb = 0; nb < NB16; ++nb)
 #pragma unroll
-        for (int reg = 0; reg < 16; ++reg) {
-          const int m = 8 * (reg >> 2) + 4 * half + (reg & 3);
-          const int n = nb * 32 + (lane & 31);
-          red[m][n] = (w == 0) ? acc[nb][reg] : red[m][n] + acc[nb][reg];
+        for (int j = 0; j < 4; ++j) {
+          const int m = 4 * g4 + j;
+          const int n = nb * 16 + (lane & 15);
+          red[m][n] = (w == 0) ? acc[nb][j] : red[m][n] + acc[nb][j];
         }
     }
     __syncthreads();
   }
   if (XAt) {
-    for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
+    for (int idx = threadIdx.x; idx < kProjTokens * r; idx += kProjWaves * 64) {
       const int m = idx / (int)r;
       const int j = idx - m * (int)r;
       const int64_t t = t0 + m;
       if (t < T) XAt[t * r + j] = red[m][j] * cr;
     }
   }
-  if (planes) {
-    // The block's two 16-token steps in the accumulate's operand order: one
-    // wave per (step, 32-rank block), lane l holding tokens 8(l>>5) + i of
-    // rank 32b + (l & 31) as hi and lo bf16 terms.  Rows past T are zero
-    // (X reads past T are zero); ranks past r are written as zero.
-    for (int c = wave; c < 2 * nrb; c += 4) {
-      const int sl = c / nrb;
-      const int b = c - sl * nrb;
-      const int64_t s = 2 * (int64_t)blockIdx.x + sl;
-      if (s >= nsteps) continue;
+  if (planes && blockIdx.x < nsteps) {
+    // This block's 16-token step in the accumulate's operand order: wave b
+    // writes 32-rank block b, lane l holding tokens 8(l>>5) + i of rank
+    // 32b + (l & 31) as hi and lo bf16 terms.  Rows past T are zero (X reads
+    // past T are zero); ranks past r are written as zero.
+    for (int b = wave; b < nrb; b += kProjWaves) {
       const int j = 32 * b + (lane & 31);
       float hv[8], lv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float v = j < r ? red[16 * sl + 8 * half + i][j] * cr : 0.f;
+        const float v = j < r ? red[8 * (lane >> 5) + i][j] * cr : 0.f;
         hv[i] = (float)(__bf16)v;
         lv[i] = v - hv[i];
       }
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(KeyArg key, int64_t T
         vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
       }
-      uint16_t* dst = planes + (s * nrb + b) * 1024 + lane * 8;
+      uint16_t* dst = planes + ((int64_t)blockIdx.x * nrb + b) * 1024 + lane * 8;
       *reinterpret_cast<u32x4*>(dst) = vh;
       *reinterpret_cast<u32x4*>(dst + 512) = vl;
     }
@@ -846,23 +854,25 @@ hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const voi
                        key, T, k, r, static_cast<const float*>(X), ldx, crd, XAt);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((T + 31) / 32));
+  const dim3 grid((unsigned)((T + kProjTokens - 1) / kProjTokens));
   const float cr = (float)crd;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
-  switch ((r + 31) / 32) {
-#define LOGRA_PROJ_CASE(NB)                                                                   \
-  case NB:                                                                                    \
-    hipLaunchKernelGGL(project_bf16_kernel<NB>, grid, dim3(256), 0, s, key, T, k, r, Xb, ldx, \
-                       cr, XAt, planes, nrb, nsteps);                                         \
+  const int64_t nb16 = (r + 15) / 16;
+  const int nb = nb16 <= 1 ? 1 : nb16 <= 2 ? 2 : nb16 <= 4 ? 4 : nb16 <= 6 ? 6 : nb16 <= 8 ? 8
+               : nb16 <= 12 ? 12 : 16;
+  switch (nb) {
+#define LOGRA_PROJ_CASE(NB)                                                                     \
+  case NB:                                                                                      \
+    hipLaunchKernelGGL(project_bf16_kernel<NB>, grid, dim3(kProjWaves * 64), 0, s, key, T, k, r, \
+                       Xb, ldx, cr, XAt, planes, nrb, nsteps);                                  \
     break;
     LOGRA_PROJ_CASE(1)
     LOGRA_PROJ_CASE(2)
-    LOGRA_PROJ_CASE(3)
     LOGRA_PROJ_CASE(4)
-    LOGRA_PROJ_CASE(5)
     LOGRA_PROJ_CASE(6)
-    LOGRA_PROJ_CASE(7)
     LOGRA_PROJ_CASE(8)
+    LOGRA_PROJ_CASE(12)
+    LOGRA_PROJ_CASE(16)
 #undef LOGRA_PROJ_CASE
     default:
       return hipErrorInvalidValue;
