@@ -568,23 +568,96 @@ def test_reconstruction_cosine(d, k, r, dtype, ld):
     assert out[3] == pytest.approx(((S @ A) ** 2).sum(), rel=1e-5)
 
 
+# ------------------------------------------------------ whole update
+
+
+@pytest.mark.parametrize("workload", ["single-256-r8-fp32", "single-4096-r64"])
+def test_whole_update_matches_oracle(workload):
+    """One whole update of a small workload, every step on the GPU through the C ABI: the
+    projection of each microbatch's input, the sketch over all microbatches, the optimiser
+    (SGD U = S, or RowAdam from v = 0 at t = 1), q and alpha where the workload has contexts,
+    and the merge -- against the oracle's chain on the same inputs ([paper] §2.1-2.3)."""
+    w = synth.BY_NAME[workload]
+    (layer, kind, mid, d, k) = w.matrices()[0]
+    T, r = w.T, w.r
+    bf16 = w.dtype == "bf16"
+    say(f"whole update of {workload}")
+    kk = B.key(w.seed, mid, w.step)
+    A = oracle.regen_A(w.seed, mid, w.step, r, k)
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    S_h = np.zeros((d, r))
+    for mb in range(w.microbatches):
+        xb = synth.layer_input(w, layer, kind, mb)
+        db = synth.output_grad(w, layer, kind, mb)
+        if bf16:
+            X, D = bf16_dev(xb), bf16_dev(db)
+            Xh, Dh = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(db)
+        else:
+            X, D = torch.from_numpy(xb).to(DEV), torch.from_numpy(db).to(DEV)
+            Xh, Dh = xb.astype(np.float64), db.astype(np.float64)
+        B.sketch_accumulate(D, B.project_input(kk, X, r), S)
+        S_h = oracle.accumulate(S_h, Dh, oracle.project(Xh, A))
+    assert relfro(S.cpu().numpy(), S_h) <= (5e-5 if bf16 else 1e-5)
+    if w.optimizer == "sgd":
+        U, U_h = S, S_h
+    else:
+        v = torch.zeros((d,), dtype=torch.float32, device=DEV)
+        U = B.rowadam(S, v, 1, w.beta, w.eps)
+        U_h, _ = oracle.rowadam(S_h, np.zeros(d), 1, w.beta, w.eps)
+        assert relfro(U.cpu().numpy(), U_h) <= 5e-5
+    alpha = w.alpha
+    if w.P:
+        zb, zdb = synth.kl_inputs(w)
+        zt = torch.from_numpy(zb).to(DEV) if not bf16 else bf16_dev(zb)
+        zdt = torch.from_numpy(zdb).to(DEV) if not bf16 else bf16_dev(zdb)
+        q = float(B.predicted_kl_q(zt, zdt, w.tau).item())
+        zh = zb.astype(np.float64) if not bf16 else oracle.bf16_bits_to_f64(zb)
+        zdh = zdb.astype(np.float64) if not bf16 else oracle.bf16_bits_to_f64(zdb)
+        q_h = oracle.predicted_kl_q(zh, zdh, w.tau)
+        assert q == pytest.approx(q_h, rel=1e-4)
+        assert B.step_alpha(q, w.delta, w.alpha_max) == pytest.approx(
+            oracle.step_alpha(q_h, w.delta, w.alpha_max), rel=1e-4)
+        if alpha is None:
+            alpha = oracle.step_alpha(q_h, w.delta, w.alpha_max)
+    wb = synth.weight(w, layer, kind)
+    W = bf16_dev(wb) if bf16 else torch.from_numpy(wb).to(DEV)
+    B.merge(kk, W, U, w.eta * alpha, mode=w.rounding, sr_seed=w.sr_seed)
+    Wh = oracle.bf16_bits_to_f64(wb) if bf16 else wb.astype(np.float64)
+    u = philox.sr_draws(w.sr_seed, mid, w.step, d, k) if w.rounding == "stochastic" else None
+    want = oracle.merge(Wh, U_h, A, w.eta * alpha, w_dtype=w.dtype, mode=w.rounding, u_draws=u)
+    if bf16:
+        frac, exact = ulp_check(bf16_host(W), want)
+        assert frac >= 0.9999 and exact >= 0.999
+    else:
+        # the chain: the applied update W' - W against the oracle's, relative Frobenius (the
+        # oracle's U is fp64, the GPU's fp32, so W' may differ by an ulp where the two round apart)
+        got = W.cpu().numpy().astype(np.float64)
+        assert relfro(got - Wh, want - Wh) <= 1e-5
+        # the merge alone: from the GPU's own U the oracle's W matches bit for bit
+        want_u = oracle.merge(Wh, U.cpu().numpy().astype(np.float64), A, w.eta * alpha, w_dtype="f32",
+                              mode="nearest")
+        assert (got == want_u).mean() >= 0.999
+
+
 # --------------------------------------------- full-size shapes (sampled)
 
 
-@pytest.mark.parametrize("workload", ["qwen2.5-7b-set-r64", "dense-27b-set-r256"])
-def test_full_size_layer_sampled(workload):
-    """One full-size layer (q, k, v, o, gate, up, down; 7B shapes at r = 64, 27B shapes at
-    r = 256; T = 4096) through the entry points and launch configuration the benchmark
-    times: projections straight into packed operands, one grouped packed accumulate, one
-    grouped merge from packed updates with the step size on the device.  S is checked on
-    sampled rows of every matrix against the oracle's X A^T and D^T (X A^T); W on sampled
-    rows of every matrix."""
+@pytest.mark.parametrize("workload,layer", [("qwen2.5-7b-set-r64", 0), ("qwen2.5-7b-set-r64", 27),
+                                            ("qwen2.5-1.5b-set-r64", 14), ("dense-27b-set-r256", 0),
+                                            ("dense-27b-set-r256", 63)])
+def test_full_size_layer_sampled(workload, layer):
+    """One full-size layer (q, k, v, o, gate, up, down; 1.5B and 7B shapes at r = 64, 27B
+    shapes at r = 256; T = 4096; first, middle or last layer, so each matrix has its own key)
+    through the entry points and launch configuration the benchmark times: projections
+    straight into packed operands, one grouped packed accumulate, one grouped merge from
+    packed updates with the step size on the device.  S is checked on sampled rows of every
+    matrix against the oracle's X A^T and D^T (X A^T); W on sampled rows of every matrix."""
     w = synth.BY_NAME[workload]
     T, r = w.T, w.r
-    say(f"full-size layer of {workload}, sampled (bench configuration)")
-    rs = np.random.default_rng(25)
+    say(f"full-size layer {layer} of {workload}, sampled (bench configuration)")
+    rs = np.random.default_rng(25 + layer)
     items, host = [], []
-    for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
+    for (layer, kind, mid, d, k) in w.matrices(layers=[layer]):
         xb = synth.layer_input(w, layer, kind, 0)
         db = synth.output_grad(w, layer, kind, 0)
         S0 = synth.fp32_matrix((d, r), 0.3, (25, mid, 0, 0, 5))
@@ -604,7 +677,7 @@ def test_full_size_layer_sampled(workload):
     # the layer's grouped merge, step size on the device
     alpha = torch.tensor([0.5], dtype=torch.float32, device=DEV)
     mitems, mhost = [], []
-    for (layer, kind, mid, d, k) in w.matrices(layers=[0]):
+    for (layer, kind, mid, d, k) in w.matrices(layers=[layer]):
         wbits = synth.weight(w, layer, kind)
         U = synth.fp32_matrix((d, r), 1.0, (25, mid, 0, 0, 7))
         mitems.append((B.key(w.seed, mid, w.step), bf16_dev(wbits), torch.from_numpy(U).to(DEV)))
