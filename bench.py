@@ -375,6 +375,17 @@ def main():
     out["diagnostics"] = {"reconstruction_cosine": {
         "matrix": f"{dkind} {dd}x{dk} bf16", "r": r, "cos": round(float(cout[0].item()), 6),
         "us": round(cus, 1), "g_read_gbs": round(2 * dd * dk / (cus * 1e-6) / 1e9, 1)}}
+    # The finite-difference check of the predicted KL at the step the update took.
+    a_dev = float(alpha.item())
+    ekl = B.exact_kl(z, zd, a_dev, w.tau)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    B.exact_kl(z, zd, a_dev, w.tau, out=ekl)
+    e1.record()
+    torch.cuda.synchronize()
+    out["diagnostics"]["exact_kl"] = {
+        "contexts": P, "vocab": Vv, "alpha": round(a_dev, 6), "predicted": float(a_dev * a_dev * q.item()),
+        "exact": float(ekl.item()), "us": round(e0.elapsed_time(e1) * 1e3, 1)}
     if not args.skip_cpu_baseline and layers == w.layers and w.name == DEFAULT_WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(w, rounding)
     print(json.dumps(out), flush=True)

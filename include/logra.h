@@ -283,6 +283,22 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
                                    logra_dtype dtype, float tau, float* q_dev,
                                    void* ws, size_t ws_bytes, logra_stream stream);
 
+/* Workspace bytes of logra_exact_kl for P contexts. */
+LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P);
+
+/* The finite-difference check of the predicted KL: the mean over the P
+ * contexts of KL(softmax(z_s/tau) || softmax((z_s + alpha zdot_s)/tau)),
+ * logits linear in the step ([paper] §2.3, Eq. 5 approximates it by
+ * alpha^2 q; App. A.1).  Written to out_dev (one double on the device).
+ * Evaluated per context as log E_p[exp(c (zdot - E_p[zdot]))], c = alpha/tau,
+ * through log1p/expm1 in fp64, so small steps keep their digits.  z, zdot as
+ * for logra_predicted_kl_q.
+ * Errors: NULL pointers; P < 1, V < 1; tau not finite and > 0; alpha not
+ * finite; workspace too small. */
+LOGRA_API int logra_exact_kl(int64_t P, int64_t V, const void* z, const void* zdot,
+                             logra_dtype dtype, double alpha, double tau, double* out_dev,
+                             void* ws, size_t ws_bytes, logra_stream stream);
+
 /* alpha = min(alpha_max, sqrt(delta / q)) on the host (fp64); q = 0 gives
  * alpha_max.  [paper] §2.3 and App. A.2 (root restored from alpha^2 q <= delta;
  * [zh], [ko]).  Errors: NULL alpha; q < 0 or NaN, delta <= 0, alpha_max <= 0

@@ -88,6 +88,9 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_exact_kl_ws_bytes": (c_size_t, [c_int64]),
+    "logra_exact_kl": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int, c_double, c_double, c_void_p,
+                               c_void_p, c_size_t, c_void_p]),
     "logra_sync_pack": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_double, c_void_p,
                                 c_int, c_uint64, c_int64, POINTER(SyncHeader), c_void_p, c_size_t,
                                 c_void_p]),
@@ -430,3 +433,19 @@ def sync_apply(items, stream=None):
         keep.append(h)
         descs[i] = SyncDesc(ctypes.pointer(h), P.data_ptr(), W.data_ptr(), _ld(W))
     _check(lib().logra_sync_apply(descs, n, _stream(items[0][2], stream)))
+
+
+def exact_kl_ws_bytes(P: int) -> int:
+    return lib().logra_exact_kl_ws_bytes(P)
+
+
+def exact_kl(z: torch.Tensor, zdot: torch.Tensor, alpha: float, tau: float, out=None, ws=None,
+             stream=None):
+    """Mean KL of a step alpha along zdot, on the device (one fp64 element)."""
+    P, V = z.shape
+    o = out if out is not None else torch.empty((1,), dtype=torch.float64, device=z.device)
+    if ws is None:
+        ws = workspace(exact_kl_ws_bytes(P), z.device)
+    _check(lib().logra_exact_kl(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), float(alpha), float(tau),
+                                _ptr(o), _ptr(ws), ws.numel(), _stream(z, stream)))
+    return o

@@ -54,6 +54,11 @@ hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_
                           double beta, double eps, float* U, void* U_packed, void* ws,
                           hipStream_t s);
 
+// Mean over P contexts of KL(softmax(z/tau) || softmax((z + alpha zdot)/tau)), fp64, to *out.
+size_t exact_kl_ws_bytes(int64_t P);
+hipError_t launch_exact_kl(int64_t P, int64_t V, const void* z, const void* zd, bool bf16,
+                           double alpha, double tau, double* out, void* ws, hipStream_t s);
+
 size_t klq_ws_bytes(int64_t P, int64_t V);
 hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,
                                  bool bf16, float tau, float* q, void* ws, hipStream_t s);

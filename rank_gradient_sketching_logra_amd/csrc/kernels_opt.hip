@@ -290,6 +290,72 @@ __global__ void step_alpha_kernel(const float* q, float delta, float amax, float
   *alpha = a;
 }
 
+// -------------------------------------------------- exact KL of a step
+
+// Per context s (one block): KL(p || p') with p = softmax(z/tau) and p' =
+// softmax((z + alpha zdot)/tau), logits linear in alpha.  With c = alpha/tau
+// and mu = E_p[zdot], KL = log E_p[exp(c (zdot - mu))] (the normalisers and
+// the linear term cancel), evaluated as log1p(E_p[expm1(c (zdot - mu))]) so
+// that a small step keeps its digits.  Three passes over the row in fp64:
+// max of z/tau, then the weights' sum and first moment, then the expm1
+// moment; fixed-tree block sums.
+__device__ double kl_block_sum(double x, double* red) {
+  __syncthreads();
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  return red[0];
+}
+__device__ double kl_block_max(double x, double* red) {
+  __syncthreads();
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  return red[0];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void exact_kl_rows_kernel(int64_t V, const void* z, const void* zd,
+                                                            double inv_tau, double c,
+                                                            double* __restrict__ kl) {
+  __shared__ double red[256];
+  const int64_t row = (int64_t)blockIdx.x * V;
+  double m = -INFINITY;
+  for (int64_t v = threadIdx.x; v < V; v += 256) m = fmax(m, (double)load_val<BF16>(z, row + v) * inv_tau);
+  m = kl_block_max(m, red);
+  double w = 0.0, wy = 0.0;
+  for (int64_t v = threadIdx.x; v < V; v += 256) {
+    const double e = exp((double)load_val<BF16>(z, row + v) * inv_tau - m);
+    w += e;
+    wy += e * (double)load_val<BF16>(zd, row + v);
+  }
+  const double W = kl_block_sum(w, red);
+  const double mu = kl_block_sum(wy, red) / W;
+  double g = 0.0;
+  for (int64_t v = threadIdx.x; v < V; v += 256) {
+    const double e = exp((double)load_val<BF16>(z, row + v) * inv_tau - m);
+    g += e * expm1(c * ((double)load_val<BF16>(zd, row + v) - mu));
+  }
+  const double G = kl_block_sum(g, red);
+  if (threadIdx.x == 0) kl[blockIdx.x] = log1p(G / W);
+}
+
+// Mean over contexts in a fixed tree.
+__global__ __launch_bounds__(256) void exact_kl_mean_kernel(int64_t P, const double* __restrict__ kl,
+                                                            double* __restrict__ out) {
+  __shared__ double red[256];
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < P; i += 256) a += kl[i];
+  const double t = kl_block_sum(a, red);
+  if (threadIdx.x == 0) *out = t / (double)P;
+}
+
 RowAdamWs rowadam_ws_layout(void* ws, int64_t d) {
   const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
   double* p = static_cast<double*>(ws);
@@ -359,6 +425,25 @@ hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void
   if (e != hipSuccess) return e;
   const double scale = 1.0 / (2.0 * (double)P * (double)tau * (double)tau);
   hipLaunchKernelGGL(klq_final_kernel, dim3(1), dim3(256), 0, s, P, part, scale, q);
+  return hipGetLastError();
+}
+
+size_t exact_kl_ws_bytes(int64_t P) { return (size_t)P * sizeof(double); }
+
+hipError_t launch_exact_kl(int64_t P, int64_t V, const void* z, const void* zd, bool bf16,
+                           double alpha, double tau, double* out, void* ws, hipStream_t s) {
+  double* kl = static_cast<double*>(ws);
+  const double inv_tau = 1.0 / tau;
+  const double c = alpha / tau;
+  if (bf16)
+    hipLaunchKernelGGL(exact_kl_rows_kernel<true>, dim3((unsigned)P), dim3(256), 0, s, V, z, zd,
+                       inv_tau, c, kl);
+  else
+    hipLaunchKernelGGL(exact_kl_rows_kernel<false>, dim3((unsigned)P), dim3(256), 0, s, V, z, zd,
+                       inv_tau, c, kl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(exact_kl_mean_kernel, dim3(1), dim3(256), 0, s, P, kl, out);
   return hipGetLastError();
 }
 

@@ -344,6 +344,29 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
                     "predicted_kl_q launch");
 }
 
+LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P) {
+  if (P < 1) return 0;
+  return logra::exact_kl_ws_bytes(P);
+}
+
+LOGRA_API int logra_exact_kl(int64_t P, int64_t V, const void* z, const void* zdot,
+                             logra_dtype dtype, double alpha, double tau, double* out_dev,
+                             void* ws, size_t ws_bytes, logra_stream stream) {
+  if (!z || !zdot || !out_dev) return fail(LOGRA_ERR_NULL, "exact_kl: NULL pointer");
+  if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "exact_kl: need P, V >= 1");
+  if (P > 2147483647) return fail(LOGRA_ERR_SHAPE, "exact_kl: too many contexts");
+  if (dtype != LOGRA_F32 && dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "exact_kl: dtype must be F32 or BF16");
+  if (!(tau > 0.0) || !std::isfinite(tau)) return fail(LOGRA_ERR_DOMAIN, "exact_kl: tau must be finite and > 0");
+  if (!std::isfinite(alpha)) return fail(LOGRA_ERR_DOMAIN, "exact_kl: alpha must be finite");
+  const size_t need = logra::exact_kl_ws_bytes(P);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "exact_kl: workspace of %zu bytes needed", need);
+  if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(out_dev) & 7u) != 0)
+    return fail(LOGRA_ERR_ALIGN, "exact_kl: workspace 16-byte and output 8-byte aligned");
+  return hip_status(logra::launch_exact_kl(P, V, z, zdot, dtype == LOGRA_BF16, alpha, tau, out_dev, ws,
+                                           static_cast<hipStream_t>(stream)),
+                    "exact_kl launch");
+}
+
 LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double* alpha) {
   if (!alpha) return fail(LOGRA_ERR_NULL, "step_alpha: NULL output");
   if (!(delta > 0.0) || !(alpha_max > 0.0)) return fail(LOGRA_ERR_DOMAIN, "step_alpha: delta and alpha_max must be > 0");

@@ -291,3 +291,16 @@ def test_sync_payload_validation(lib):
     assert err(g, descs(header(), header(mode=1)), 2, None) == B.ERR_SHAPE
     assert err(g, descs(header()), 0, None) == B.ERR_SHAPE
     assert err(g, None, 1, None) == B.ERR_NULL
+
+
+def test_exact_kl_validation(lib):
+    f = lib.logra_exact_kl
+    ws = B.exact_kl_ws_bytes(4)
+    assert ws == 4 * 8 and B.exact_kl_ws_bytes(0) == 0
+    assert err(f, 4, 512, None, Bp, B.BF16, 0.1, 1.0, C, Dp, ws, None) == B.ERR_NULL
+    assert err(f, 0, 512, A, Bp, B.BF16, 0.1, 1.0, C, Dp, ws, None) == B.ERR_SHAPE
+    assert err(f, 4, 512, A, Bp, 9, 0.1, 1.0, C, Dp, ws, None) == B.ERR_DTYPE
+    assert err(f, 4, 512, A, Bp, B.BF16, 0.1, 0.0, C, Dp, ws, None) == B.ERR_DOMAIN
+    assert err(f, 4, 512, A, Bp, B.BF16, float("inf"), 1.0, C, Dp, ws, None) == B.ERR_DOMAIN
+    assert err(f, 4, 512, A, Bp, B.BF16, 0.1, 1.0, C, Dp, ws - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 4, 512, A, Bp, B.BF16, 0.1, 1.0, C + 4, Dp, ws, None) == B.ERR_ALIGN

@@ -294,6 +294,29 @@ def test_predicted_kl_q(P, V, dtype, tau):
     assert abs(a - aw) <= 1e-4 * aw
 
 
+@pytest.mark.parametrize("P,V,dtype,tau", [(4, 512, "f32", 1.0), (64, 152064, "bf16", 1.0), (3, 1000, "bf16", 0.7)])
+def test_exact_kl_probe(P, V, dtype, tau):
+    """The finite-difference check: the mean exact KL of a step against the oracle's
+    (log-softmax difference in fp64), over small and large steps, and alpha^2 q -> KL as the
+    step shrinks, with q and the KL both from the GPU ([paper] §2.3 Eq. 5, App. A.1)."""
+    say(f"exact KL P={P} V={V} {dtype} tau={tau}")
+    zb = synth.normal((P, V), 4.0, (30, P, V, 0, 3), dtype)
+    zdb = synth.normal((P, V), 1.0, (30, P, V, 0, 4), dtype)
+    if dtype == "bf16":
+        z, zd = bf16_dev(zb), bf16_dev(zdb)
+        zh, zdh = oracle.bf16_bits_to_f64(zb), oracle.bf16_bits_to_f64(zdb)
+    else:
+        z, zd = torch.from_numpy(zb).to(DEV), torch.from_numpy(zdb).to(DEV)
+        zh, zdh = zb.astype(np.float64), zdb.astype(np.float64)
+    for a in (1e-3, 0.05, 1.0, 4.0):
+        got = float(B.exact_kl(z, zd, a, tau).item())
+        want = oracle.exact_kl_mean(zh, zdh, a, tau)
+        assert got == pytest.approx(want, rel=1e-6), a
+    q = float(B.predicted_kl_q(z, zd, tau).item())
+    a = 1e-3
+    assert float(B.exact_kl(z, zd, a, tau).item()) == pytest.approx(a * a * q, rel=2e-2)
+
+
 def test_predicted_kl_special_cases():
     say("predicted_kl_q special cases")
     P, V = 5, 3000
