@@ -375,6 +375,23 @@ def main():
     out["diagnostics"] = {"reconstruction_cosine": {
         "matrix": f"{dkind} {dd}x{dk} bf16", "r": r, "cos": round(float(cout[0].item()), 6),
         "us": round(cus, 1), "g_read_gbs": round(2 * dd * dk / (cus * 1e-6) / 1e9, 1)}}
+    # The merge phase in the other rounding mode (the metric uses the workload's own), on
+    # copies of the weights so the timed steps above are unaffected.
+    other = "stochastic" if rounding == "nearest" else "nearest"
+    Wc = {key_: t.clone() for key_, t in W.items()}
+    for rep in range(2):
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for l in range(layers):
+            B.merge_grouped_packed([(keys[(l, kind)], Wc[(l, kind)], UP[(l, kind)]) for (kind, d, k) in by_layer[l]],
+                                   r, w.eta, scale_dev=alpha, mode=other, sr_seed=w.sr_seed)
+        m1.record()
+        torch.cuda.synchronize()
+    other_ms = m0.elapsed_time(m1)
+    out["merge_other_rounding"] = {"rounding": other, "ms": round(other_ms, 3),
+                                   "gbs": round(merge_total / (other_ms * 1e-3) / 1e9, 1),
+                                   "pct_of_peak": round(100 * merge_total / (other_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    del Wc
     # The finite-difference check of the predicted KL at the step the update took.
     a_dev = float(alpha.item())
     ekl = B.exact_kl(z, zd, a_dev, w.tau)
