@@ -152,6 +152,19 @@ def regen_A(seed: int, matrix_id: int, step: int, r: int, k: int, kind: str = "f
     raise ValueError(kind)
 
 
+def gaussian_A(seed: int, matrix_id: int, step: int, r: int, k: int, kind: str = "f64"):
+    """Gaussian projection A [r x k] with entries z / sqrt(r), z standard normal
+    (the variant the pages ablate against Rademacher signs: [paper] §3.4.1 and
+    App. D.3; E[A^T A] = I as for the Rademacher A).  kind "f64" or "f32" (the
+    fp64 value rounded once)."""
+    a = philox.gaussian_normals(seed, matrix_id, step, r, k) / math.sqrt(r)
+    if kind == "f64":
+        return a
+    if kind == "f32":
+        return a.astype(np.float32)
+    raise ValueError(kind)
+
+
 # ---------------------------------------------------------------------------
 # The sketch path
 # ---------------------------------------------------------------------------

@@ -24,6 +24,10 @@ the layout is stated here and in ``include/logra.h``:
 * sign bits of A: one block per (row j, 256-column group b = l >> 8) with
   counter ``(j, b, 0, 0)``; column l uses bit ``l & 63`` of output word
   ``(l & 255) >> 6``; bit 1 means sigma = -1, bit 0 means sigma = +1;
+* Gaussian entries (the Gaussian projection variant): one block per (row j,
+  4-column group c = l >> 2) with counter ``(j, c, 2, 0)``; column l takes
+  Box-Muller pair ``(l & 3) >> 1`` of the four words, cosine for even l,
+  sine for odd l (see ``gaussian_normals``);
 * stochastic-rounding draws: key ``(sr_seed, (step << 32) | matrix_id)``;
   element e = (row0 + i) * k + l (logical index) uses counter
   ``(e >> 4, 0, 1, 0)`` and the 16 bits ``[16*(e & 3), +16)`` of output word
@@ -121,3 +125,31 @@ def sr_draws(sr_seed: int, matrix_id: int, step: int, d: int, k: int,
     lane = (e & np.uint64(15)).astype(np.int64)
     w = words[inv, lane >> 2]
     return ((w >> (np.uint64(16) * (e & np.uint64(3)))) & np.uint64(0xFFFF)).astype(np.uint32)
+
+
+def gaussian_normals(seed: int, matrix_id: int, step: int, r: int, k: int) -> np.ndarray:
+    """Standard normal entries z [r, k] (fp64) of the Gaussian projection variant.
+
+    Box-Muller (G. E. P. Box and M. E. Muller, "A Note on the Generation of
+    Random Normal Deviates", 1958) on the Philox stream: for row j and column
+    group c = l >> 2 the block with counter (j, c, 2, 0) gives words w0..w3,
+    uniforms u_i = ((w_i >> 11) + 1/2) 2^-53 in (0, 1), and
+    z_{4c} = sqrt(-2 ln u0) cos(2 pi u1), z_{4c+1} = sqrt(-2 ln u0) sin(2 pi u1),
+    z_{4c+2} = sqrt(-2 ln u2) cos(2 pi u3), z_{4c+3} = sqrt(-2 ln u2) sin(2 pi u3).
+    """
+    key = projection_key(seed, matrix_id, step)
+    ng = (k + 3) // 4
+    ctr = np.zeros((r, ng, 4), dtype=np.uint64)
+    ctr[..., 0] = np.arange(r, dtype=np.uint64)[:, None]
+    ctr[..., 1] = np.arange(ng, dtype=np.uint64)[None, :]
+    ctr[..., 2] = 2
+    words = philox4x64_10(ctr, key)                                 # [r, ng, 4]
+    u = ((words >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    rho0 = np.sqrt(-2.0 * np.log(u[..., 0]))
+    rho1 = np.sqrt(-2.0 * np.log(u[..., 2]))
+    z = np.empty((r, ng, 4))
+    z[..., 0] = rho0 * np.cos(2.0 * np.pi * u[..., 1])
+    z[..., 1] = rho0 * np.sin(2.0 * np.pi * u[..., 1])
+    z[..., 2] = rho1 * np.cos(2.0 * np.pi * u[..., 3])
+    z[..., 3] = rho1 * np.sin(2.0 * np.pi * u[..., 3])
+    return z.reshape(r, 4 * ng)[:, :k]

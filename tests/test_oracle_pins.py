@@ -163,6 +163,45 @@ def test_reconstruction_cosine_reproduces_paper_means():
         assert abs(np.mean(cos) - printed) < 0.004
 
 
+def test_gaussian_entries_are_standard_normal():
+    """N3: the Box-Muller entries of the Gaussian variant are N(0, 1) (Kolmogorov-Smirnov against
+    scipy's normal CDF, moments at their sampling error) and the two members of a pair, and
+    neighbouring pairs, are uncorrelated."""
+    from scipy import stats
+    z = oracle.philox.gaussian_normals(3, 1, 7, 256, 4096)          # 2^20 draws
+    n = z.size
+    assert abs(z.mean()) < 5.0 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 5.0 * math.sqrt(2.0 / n)
+    assert stats.kstest(z.ravel(), "norm").pvalue > 1e-3
+    zz = z.reshape(256, -1, 4)
+    for a, b in ((0, 1), (2, 3), (1, 2)):
+        c = np.corrcoef(zz[..., a].ravel(), zz[..., b].ravel())[0, 1]
+        assert abs(c) < 5.0 / math.sqrt(zz[..., a].size)
+
+
+def test_gaussian_projection_gram_and_cosine():
+    """N3 / P3: E[A^T A] = I for the Gaussian A too (the mean of S A over N draws converges to G
+    at sqrt((k+1)/(r N)), since E[(A^T A)^2] = ((k+r+1)/r) I), its reconstruction cosine follows
+    sqrt(r / (k + r + 1)), and at the 1.5B model's widths the Gaussian mean lies below the
+    Rademacher mean by less than the 2e-4 the pages print (tests/golden/reconstruction_cosine.json)."""
+    d, k, r, N = 12, 48, 4, 600
+    G = np.random.default_rng(0).standard_normal((d, k))
+    acc = np.zeros_like(G)
+    for n in range(N):
+        A = oracle.gaussian_A(2000 + n, 0, n, r, k)
+        acc += oracle.reconstruct(G @ A.T, A)
+    rel = np.linalg.norm(acc / N - G) / np.linalg.norm(G)
+    pred = math.sqrt((k + 1) / (r * N))
+    assert 0.85 * pred < rel < 1.15 * pred
+    G = np.random.default_rng(1).standard_normal((64, 1536))
+    cos = [oracle.reconstruction_cosine(G, oracle.gaussian_A(7, 0, s, 256, 1536)) for s in range(8)]
+    assert abs(np.mean(cos) - math.sqrt(256 / (1536 + 256 + 1))) < 0.002
+    g = golden("reconstruction_cosine.json")
+    widths = list(g["model_input_widths"].values())
+    gap = np.mean([math.sqrt(256 / (k + 255)) - math.sqrt(256 / (k + 257)) for k in widths])
+    assert 0 < gap < g["gaussian_decrease_below"]
+
+
 def test_sketch_memory_example():
     """P4: 4 d r bytes: 1 MiB at d = k = 4096, r = 64, against 64 MiB dense."""
     g = golden("sketch_memory.json")
