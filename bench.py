@@ -372,9 +372,16 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     cus = c0.elapsed_time(c1) * 1e3 / 5
+    # the same gradient under the Gaussian projection variant (the pages' ablation)
+    Ag = B.regen_A_gaussian(keys[(0, dkind)], r, dk, dev)
+    Agp = B.pack_projection(Ag)
+    gout = B.reconstruction_cosine_explicit(G, Ag, Agp, ws=cws)
+    torch.cuda.synchronize()
     out["diagnostics"] = {"reconstruction_cosine": {
         "matrix": f"{dkind} {dd}x{dk} bf16", "r": r, "cos": round(float(cout[0].item()), 6),
+        "cos_gaussian": round(float(gout[0].item()), 6),
         "us": round(cus, 1), "g_read_gbs": round(2 * dd * dk / (cus * 1e-6) / 1e9, 1)}}
+    del Ag, Agp
     # The merge phase in the other rounding mode (the metric uses the workload's own), on
     # copies of the weights so the timed steps above are unaffected.
     other = "stochastic" if rounding == "nearest" else "nearest"

@@ -159,6 +159,57 @@ LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64
                                           double* out_dev, void* ws, size_t ws_bytes,
                                           logra_stream stream);
 
+/* ------------------------------------------ Gaussian projection variant */
+
+/* The Gaussian projection the pages ablate against Rademacher signs
+ * ([paper] §3.4.1, App. D.3; Fig. 5: the mean reconstruction cosine drops by
+ * less than 2e-4): A[j][l] = fl32(z / sqrt(r)), z standard normal by
+ * Box-Muller (1958) on the same Philox stream -- for row j and 4-column group
+ * c = l >> 2 the block with counter (j, c, 2, 0) gives words w0..w3, uniforms
+ * u_i = ((w_i >> 11) + 1/2) 2^-53, and z = sqrt(-2 ln u0) cos(2 pi u1),
+ * sqrt(-2 ln u0) sin(2 pi u1), sqrt(-2 ln u2) cos(2 pi u3), sqrt(-2 ln u2)
+ * sin(2 pi u3) for columns 4c .. 4c + 3 (fp64, rounded once).  A [r x k] fp32
+ * row-major.  Unlike the signs, these entries are not exact in bf16, so
+ * projections with an explicit A carry it as bf16 hi + lo.
+ * Errors: NULL pointers; k < 1, r < 1, r > LOGRA_MAX_RANK; alignment. */
+LOGRA_API int logra_regen_A_gaussian(const logra_key* key, int64_t r, int64_t k, float* A,
+                                     logra_stream stream);
+
+/* Bytes of an explicit projection packed as the projection kernel's B
+ * operands: for each 256-column block, 32-column step and 16-rank block
+ * (rank blocks padded to 1, 2, 4, 6, 8, 12 or 16), a 1 KiB hi operand then a
+ * 1 KiB lo operand in which lane l holds rank 16nb + (l & 15), columns
+ * 256b + 32s + 8(l >> 4) .. +7.  0 for invalid sizes. */
+LOGRA_API size_t logra_projection_packed_bytes(int64_t r, int64_t k);
+
+/* Pack an explicit A [r x k] (fp32 row-major) into that form (hi = RNE(a),
+ * lo = RNE(a - hi); padding zero).
+ * Errors: NULL pointers; k < 1, r < 1, r > LOGRA_MAX_RANK; packed_bytes too
+ * small; alignment; A overlapping the packed output. */
+LOGRA_API int logra_pack_projection(int64_t r, int64_t k, const float* A, void* A_packed,
+                                    size_t packed_bytes, logra_stream stream);
+
+/* XAt = X A^T with an explicit projection (packed as above) instead of the
+ * key's signs, written as fp32 [T x r] (XAt) and/or in the accumulate's
+ * packed input form (planes, logra_packed_input_bytes(T, r) bytes); either
+ * may be NULL but not both.  X bf16.  [paper] §2.1.
+ * Errors: NULL pointers; T < 1, k < 1, r < 1, r > LOGRA_MAX_RANK, ldx < k;
+ * X not bf16; sizes; alignment; outputs overlapping an input or each other. */
+LOGRA_API int logra_project_input_explicit(int64_t T, int64_t k, int64_t r, const void* X,
+                                           logra_dtype x_dtype, int64_t ldx, const void* A_packed,
+                                           size_t packed_bytes, float* XAt, void* planes,
+                                           size_t planes_bytes, logra_stream stream);
+
+/* logra_reconstruction_cosine with an explicit projection: A (fp32) for the
+ * exact A A^T and A_packed (its packed form) for G A^T.  G bf16.  Same
+ * output and workspace as logra_reconstruction_cosine.
+ * Errors: as logra_reconstruction_cosine; G not bf16; packed_bytes too small. */
+LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t r, const void* G,
+                                                   logra_dtype g_dtype, int64_t ldg, const float* A,
+                                                   const void* A_packed, size_t packed_bytes,
+                                                   double* out_dev, void* ws, size_t ws_bytes,
+                                                   logra_stream stream);
+
 /* ---------------------------------------------------------------- sketch */
 
 /* Workspace bytes one logra_sketch_accumulate call (or one descriptor of a

@@ -88,6 +88,14 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_regen_A_gaussian": (c_int, [POINTER(Key), c_int64, c_int64, c_void_p, c_void_p]),
+    "logra_projection_packed_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_pack_projection": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_project_input_explicit": (c_int, [c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_void_p,
+                                             c_size_t, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_reconstruction_cosine_explicit": (c_int, [c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
+                                                     c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
+                                                     c_size_t, c_void_p]),
     "logra_exact_kl_ws_bytes": (c_size_t, [c_int64]),
     "logra_exact_kl": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int, c_double, c_double, c_void_p,
                                c_void_p, c_size_t, c_void_p]),
@@ -448,4 +456,51 @@ def exact_kl(z: torch.Tensor, zdot: torch.Tensor, alpha: float, tau: float, out=
         ws = workspace(exact_kl_ws_bytes(P), z.device)
     _check(lib().logra_exact_kl(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), float(alpha), float(tau),
                                 _ptr(o), _ptr(ws), ws.numel(), _stream(z, stream)))
+    return o
+
+
+def regen_A_gaussian(k_: Key, r: int, k: int, device="cuda", stream=None):
+    """The Gaussian projection variant A [r x k] (fp32) for key k_."""
+    A = torch.empty((r, k), dtype=torch.float32, device=device)
+    _check(lib().logra_regen_A_gaussian(ctypes.byref(k_), r, k, _ptr(A), _stream(A, stream)))
+    return A
+
+
+def projection_packed_bytes(r: int, k: int) -> int:
+    return lib().logra_projection_packed_bytes(r, k)
+
+
+def pack_projection(A: torch.Tensor, out=None, stream=None):
+    """An explicit fp32 A [r x k] in the projection kernel's operand form (uint8 tensor)."""
+    r, k = A.shape
+    nb = projection_packed_bytes(r, k)
+    P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=A.device)
+    _check(lib().logra_pack_projection(r, k, _ptr(A), _ptr(P), P.numel(), _stream(A, stream)))
+    return P
+
+
+def project_input_explicit(X: torch.Tensor, A_packed: torch.Tensor, r: int, planes=None, out=None,
+                           want_xat: bool = True, stream=None):
+    """X A^T with an explicit packed projection: returns (XAt or None, planes or None)."""
+    T, k = X.shape
+    XAt = out if out is not None else (torch.empty((T, r), dtype=torch.float32, device=X.device)
+                                       if want_xat else None)
+    pb = planes.numel() if planes is not None else 0
+    _check(lib().logra_project_input_explicit(T, k, r, _ptr(X), _dtype_code(X), _ld(X), _ptr(A_packed),
+                                              A_packed.numel(), _ptr(XAt), _ptr(planes), pb,
+                                              _stream(X, stream)))
+    return XAt, planes
+
+
+def reconstruction_cosine_explicit(G: torch.Tensor, A: torch.Tensor, A_packed: torch.Tensor, out=None,
+                                   ws=None, stream=None):
+    """reconstruction_cosine with an explicit projection A (fp32) and its packed form."""
+    d, kk = G.shape
+    r = A.shape[0]
+    o = out if out is not None else torch.empty((4,), dtype=torch.float64, device=G.device)
+    if ws is None:
+        ws = workspace(reconstruction_cosine_ws_bytes(d, kk, r), G.device)
+    _check(lib().logra_reconstruction_cosine_explicit(d, kk, r, _ptr(G), _dtype_code(G), _ld(G), _ptr(A),
+                                                      _ptr(A_packed), A_packed.numel(), _ptr(o), _ptr(ws),
+                                                      ws.numel(), _stream(G, stream)))
     return o

@@ -65,6 +65,23 @@ __device__ __forceinline__ Philox4 sigma_block(KeyWords key, uint64_t j, uint64_
   return philox4x64_10(j, b, 0, 0, key.k0, key.k1);
 }
 
+// Four standard normal entries of the Gaussian projection variant, columns
+// 4c .. 4c + 3 of row j: Box-Muller (Box and Muller, 1958) on the block with
+// counter (j, c, 2, 0), uniforms u_i = ((w_i >> 11) + 1/2) 2^-53, pairs
+// (u0, u1) and (u2, u3), cosine then sine; fp64.
+__device__ __forceinline__ void gaussian_block(KeyWords key, uint64_t j, uint64_t c, double (&z)[4]) {
+  const Philox4 p = philox4x64_10(j, c, 2, 0, key.k0, key.k1);
+  double u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = ((double)(p.w[i] >> 11) + 0.5) * 0x1.0p-53;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double rho0 = sqrt(-2.0 * log(u[0])), rho1 = sqrt(-2.0 * log(u[2]));
+  z[0] = rho0 * cos(two_pi * u[1]);
+  z[1] = rho0 * sin(two_pi * u[1]);
+  z[2] = rho1 * cos(two_pi * u[3]);
+  z[3] = rho1 * sin(two_pi * u[3]);
+}
+
 // 16 stochastic-rounding draws for flat elements [16*g, 16*g + 16): draw of
 // element e is bits [16*(e & 3), +16) of word (e & 15) >> 2.
 __device__ __forceinline__ Philox4 sr_block(KeyWords key, uint64_t g) {

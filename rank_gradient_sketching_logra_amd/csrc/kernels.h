@@ -34,9 +34,18 @@ size_t acc_ws_bytes_per_item(int64_t T, int64_t d, int64_t r);
 hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void* A,
                           hipStream_t s);
 // XAt may be null when planes is given (bf16 X only); planes, when not
-// null, receives the packed projected input the accumulate reads.
+// null, receives the packed projected input the accumulate reads.  A_packed,
+// when not null, is an explicit projection in the kernel's operand form (bf16
+// X only) used instead of the key's signs.
 hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const void* X,
-                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s);
+                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s,
+                          const void* A_packed = nullptr);
+// Gaussian projection variant A [r x k] fp32; explicit projections packed for
+// the projection kernel (projection_packed_bytes of them).
+hipError_t launch_regen_A_gaussian(KeyArg key, int64_t r, int64_t k, float* A, hipStream_t s);
+size_t projection_packed_bytes(int64_t r, int64_t k);
+hipError_t launch_pack_projection(int64_t r, int64_t k, const float* A, void* packed,
+                                  hipStream_t s);
 // packed: items' ws already hold the packed projected input (XAt unused).
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
                              bool packed, hipStream_t s);
@@ -44,9 +53,12 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
 // cos(G, (G A^T) A) and its parts {cos, ||G||^2, ||G A^T||^2, ||G A^T A||^2}
 // written to out (4 doubles on the device).
 size_t reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r);
+// With A (fp32 [r x k]) and A_packed (its projection operands) given, the
+// explicit projection is used instead of the key's signs (bf16 G only).
 hipError_t launch_reconstruction_cosine(KeyArg key, int64_t d, int64_t k, int64_t r, const void* G,
                                         bool bf16, int64_t ldg, double* out, void* ws,
-                                        hipStream_t s);
+                                        hipStream_t s, const float* A = nullptr,
+                                        const void* A_packed = nullptr);
 
 size_t rowadam_ws_bytes(int64_t d);
 // U (fp32) and/or U_packed (the merge's packed update) may be null.

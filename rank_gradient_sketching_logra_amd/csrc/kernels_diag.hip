@@ -49,6 +49,31 @@ __global__ __launch_bounds__(256) void sign_gram_kernel(int64_t r, int64_t k, in
   M[idx] = c2 * (double)(k - 2 * pop);
 }
 
+// M = A A^T [r x r] in fp64 from an explicit fp32 A [r x k]: one block per
+// 16 x 16 tile of M, the two 16-row slices of A staged through LDS 64
+// columns at a time; each thread sums one entry in column order.
+__global__ __launch_bounds__(256) void explicit_gram_kernel(int64_t r, int64_t k,
+                                                            const float* __restrict__ A,
+                                                            double* __restrict__ M) {
+  __shared__ float sa[16][65], sb[16][65];
+  const int tj = threadIdx.x >> 4, tl = threadIdx.x & 15;
+  const int64_t j0 = (int64_t)blockIdx.y * 16, l0 = (int64_t)blockIdx.x * 16;
+  double acc = 0.0;
+  for (int64_t c0 = 0; c0 < k; c0 += 64) {
+    for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+      const int row = idx >> 6, col = idx & 63;
+      const int64_t c = c0 + col;
+      sa[row][col] = (j0 + row < r && c < k) ? A[(j0 + row) * k + c] : 0.f;
+      sb[row][col] = (l0 + row < r && c < k) ? A[(l0 + row) * k + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int col = 0; col < 64; ++col) acc += (double)sa[tj][col] * (double)sb[tl][col];
+    __syncthreads();
+  }
+  if (j0 + tj < r && l0 + tl < r) M[(j0 + tj) * r + l0 + tl] = acc;
+}
+
 // Fixed-tree sum over the block's 256 threads (every thread gets the total).
 __device__ double cos_block_sum(double x, double* red) {
   __syncthreads();
@@ -187,18 +212,23 @@ size_t reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r) {
 
 hipError_t launch_reconstruction_cosine(KeyArg key, int64_t d, int64_t k, int64_t r, const void* G,
                                         bool bf16, int64_t ldg, double* out, void* ws,
-                                        hipStream_t s) {
+                                        hipStream_t s, const float* A, const void* A_packed) {
   const CosWs w = cos_ws_layout(ws, d, k, r);
-  hipError_t e = launch_project(key, d, k, r, G, bf16, ldg, w.S, nullptr, s);
+  hipError_t e = launch_project(key, d, k, r, G, bf16, ldg, w.S, nullptr, s, A_packed);
   if (e != hipSuccess) return e;
-  const int64_t nw = (k + 63) / 64;
-  hipLaunchKernelGGL(sign_words_kernel, dim3((unsigned)((r * nw + 255) / 256)), dim3(256), 0, s, key,
-                     r, k, nw, w.bits);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const double c = (double)(float)(1.0 / std::sqrt((double)r));
-  hipLaunchKernelGGL(sign_gram_kernel, dim3((unsigned)((r * r + 255) / 256)), dim3(256), 0, s, r, k,
-                     nw, c * c, w.bits, w.M);
+  if (A != nullptr) {
+    const dim3 g((unsigned)((r + 15) / 16), (unsigned)((r + 15) / 16));
+    hipLaunchKernelGGL(explicit_gram_kernel, g, dim3(256), 0, s, r, k, A, w.M);
+  } else {
+    const int64_t nw = (k + 63) / 64;
+    hipLaunchKernelGGL(sign_words_kernel, dim3((unsigned)((r * nw + 255) / 256)), dim3(256), 0, s,
+                       key, r, k, nw, w.bits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const double c = (double)(float)(1.0 / std::sqrt((double)r));
+    hipLaunchKernelGGL(sign_gram_kernel, dim3((unsigned)((r * r + 255) / 256)), dim3(256), 0, s, r,
+                       k, nw, c * c, w.bits, w.M);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nb = (d + kCosRows - 1) / kCosRows;

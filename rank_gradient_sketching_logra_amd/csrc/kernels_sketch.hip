@@ -86,6 +86,60 @@ __global__ void regen_A_kernel(KeyArg key, int64_t r, int64_t k, int int8_out, f
   }
 }
 
+// Gaussian projection variant: A[j][l] = fl32(z / sqrt(r)), z from
+// gaussian_block; one thread per row and 4-column group.
+__global__ void regen_A_gaussian_kernel(KeyArg key, int64_t r, int64_t k, float* __restrict__ A) {
+  const int64_t ng = (k + 3) >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= r * ng) return;
+  const int64_t j = idx / ng;
+  const int64_t c = idx - j * ng;
+  double z[4];
+  gaussian_block(KeyWords{key.k0, key.k1}, (uint64_t)j, (uint64_t)c, z);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t l = 4 * c + q;
+    if (l < k) A[j * k + l] = (float)(z[q] / sqrt((double)r));
+  }
+}
+
+// An explicit projection A [r x k] (fp32, row-major) as the projection
+// kernel's B operands: for 256-column block b, 32-column step s (8 per
+// block) and 16-rank block nb (NB16 of them), a 1 KiB hi slab then a 1 KiB lo
+// slab, lane l holding rank 16nb + (l & 15), columns 256b + 32s + 8(l >> 4)
+// .. +7 as bf16 hi = RNE(a), lo = RNE(a - hi); ranks >= r and columns >= k
+// are zero.  One thread per (b, s, nb, lane).
+__global__ __launch_bounds__(256) void pack_projection_kernel(int64_t r, int64_t k, int nb16,
+                                                              const float* __restrict__ A,
+                                                              uint16_t* __restrict__ P) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = (int)(t & 63);
+  const int64_t unit = t >> 6;                 // (b * 8 + s) * nb16 + nb
+  const int64_t nblk = (k + 255) >> 8;
+  if (unit >= nblk * 8 * nb16) return;
+  const int nb = (int)(unit % nb16);
+  const int64_t bs = unit / nb16;
+  const int64_t j = 16 * nb + (lane & 15);
+  const int64_t c0 = 32 * bs + 8 * (lane >> 4);  // 256 b + 32 s + 8 (l >> 4)
+  uint32_t hv[4], lv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float x[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t c = c0 + 2 * p + q;
+      x[q] = (j < r && c < k) ? A[j * k + c] : 0.f;
+    }
+    const __bf16 h0 = (__bf16)x[0], h1 = (__bf16)x[1];
+    const __bf16 l0 = (__bf16)(x[0] - (float)h0), l1 = (__bf16)(x[1] - (float)h1);
+    hv[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    lv[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  uint16_t* dst = P + (unit * 2) * 512 + lane * 8;
+  *reinterpret_cast<u32x4*>(dst) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+  *reinterpret_cast<u32x4*>(dst + 512) = u32x4{lv[0], lv[1], lv[2], lv[3]};
+}
+
 // ------------------------------------------------------------- project
 
 // bf16 X: one block = 16 tokens (one 16-token step of the packed form) x
@@ -101,10 +155,14 @@ __global__ void regen_A_kernel(KeyArg key, int64_t r, int64_t k, int int8_out, f
 constexpr int kProjTokens = 16;
 constexpr int kProjWaves = 8;
 
-template <int NB16>
+// EXPLICIT: the B operands come from an explicit projection packed as bf16
+// hi/lo operands (see pack_projection_kernel) instead of sign bits: two MFMAs
+// (hi, lo) per operand, no sign generation; cr is then 1.
+template <int NB16, bool EXPLICIT>
 __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
     KeyArg key, int64_t T, int64_t k, int64_t r, const uint16_t* __restrict__ X, int64_t ldx,
-    float cr, float* __restrict__ XAt, uint16_t* __restrict__ planes, int nrb, int nsteps) {
+    float cr, float* __restrict__ XAt, uint16_t* __restrict__ planes, int nrb, int nsteps,
+    const uint16_t* __restrict__ Ap) {
   constexpr int NQ = (NB16 + 3) / 4;  // 64-rank groups, one Philox block per lane each
   constexpr int RP = NB16 * 16;
   __shared__ float red[kProjTokens][RP + 1];
@@ -129,28 +187,44 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
   for (int64_t b = wave; b < nblk; b += kProjWaves) {
     u32x4 an[8];
     if (b + kProjWaves < nblk) load(b + kProjWaves, an);
-    uint32_t bits[NQ][8];
+    if constexpr (EXPLICIT) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int64_t j = lane + 64 * q;
-      const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
-      const bool live = j < r;
+      for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
-        bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+        for (int nb = 0; nb < NB16; ++nb) {
+          const uint16_t* ap = Ap + (((b * 8 + s) * NB16 + nb) * 2) * 512 + lane * 8;
+          const u32x4 bh = *reinterpret_cast<const u32x4*>(ap);
+          const u32x4 bl = *reinterpret_cast<const u32x4*>(ap + 512);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]), as_bf16x8(bh), acc[nb],
+                                                            0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]), as_bf16x8(bl), acc[nb],
+                                                            0, 0, 0);
+        }
       }
-    }
+    } else {
+      uint32_t bits[NQ][8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+      for (int q = 0; q < NQ; ++q) {
+        const int64_t j = lane + 64 * q;
+        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
+        const bool live = j < r;
 #pragma unroll
-      for (int nb = 0; nb < NB16; ++nb) {
-        const int src = 16 * (nb & 3) + (lane & 15);
-        const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
-        const uint32_t byte = (wv >> (8 * g4)) & 0xFFu;
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]),
-                                                          as_bf16x8(expand_signs(byte)), acc[nb],
-                                                          0, 0, 0);
+        for (int w = 0; w < 4; ++w) {
+          bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
+          bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int nb = 0; nb < NB16; ++nb) {
+          const int src = 16 * (nb & 3) + (lane & 15);
+          const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
+          const uint32_t byte = (wv >> (8 * g4)) & 0xFFu;
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]),
+                                                            as_bf16x8(expand_signs(byte)), acc[nb],
+                                                            0, 0, 0);
+        }
       }
     }
     if (b + kProjWaves < nblk) {
@@ -842,29 +916,59 @@ hipError_t launch_regen_A(KeyArg key, int64_t r, int64_t k, bool int8_out, void*
   return hipGetLastError();
 }
 
+// 16-rank blocks the projection kernel computes for rank r.
+int proj_nb16(int64_t r) {
+  const int64_t nb16 = (r + 15) / 16;
+  return nb16 <= 1 ? 1 : nb16 <= 2 ? 2 : nb16 <= 4 ? 4 : nb16 <= 6 ? 6 : nb16 <= 8 ? 8
+       : nb16 <= 12 ? 12 : 16;
+}
+
+size_t projection_packed_bytes(int64_t r, int64_t k) {
+  return (size_t)((k + 255) / 256) * 8 * (size_t)proj_nb16(r) * 2048;
+}
+
+hipError_t launch_regen_A_gaussian(KeyArg key, int64_t r, int64_t k, float* A, hipStream_t s) {
+  const int64_t n = r * ((k + 3) / 4);
+  hipLaunchKernelGGL(regen_A_gaussian_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     key, r, k, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_projection(int64_t r, int64_t k, const float* A, void* packed,
+                                  hipStream_t s) {
+  const int nb16 = proj_nb16(r);
+  const int64_t threads = (k + 255) / 256 * 8 * nb16 * 64;
+  hipLaunchKernelGGL(pack_projection_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, r, k, nb16, A, static_cast<uint16_t*>(packed));
+  return hipGetLastError();
+}
+
 hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const void* X,
-                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s) {
+                          bool bf16, int64_t ldx, float* XAt, uint16_t* planes, hipStream_t s,
+                          const void* A_packed) {
   const double crd = 1.0 / std::sqrt((double)r);
   const int nrb = (int)(acc_rank_pad(r) / 32);
   const int nsteps = (int)(acc_token_pad(T) / kAccStep);
   if (!bf16) {
-    if (planes) return hipErrorInvalidValue;
+    if (planes || A_packed) return hipErrorInvalidValue;
     const int64_t n = T * r;
     hipLaunchKernelGGL(project_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        key, T, k, r, static_cast<const float*>(X), ldx, crd, XAt);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((T + kProjTokens - 1) / kProjTokens));
-  const float cr = (float)crd;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
-  const int64_t nb16 = (r + 15) / 16;
-  const int nb = nb16 <= 1 ? 1 : nb16 <= 2 ? 2 : nb16 <= 4 ? 4 : nb16 <= 6 ? 6 : nb16 <= 8 ? 8
-               : nb16 <= 12 ? 12 : 16;
-  switch (nb) {
+  const uint16_t* Ap = static_cast<const uint16_t*>(A_packed);
+  const float cr = A_packed ? 1.0f : (float)crd;
+  switch (proj_nb16(r)) {
 #define LOGRA_PROJ_CASE(NB)                                                                     \
   case NB:                                                                                      \
-    hipLaunchKernelGGL(project_bf16_kernel<NB>, grid, dim3(kProjWaves * 64), 0, s, key, T, k, r, \
-                       Xb, ldx, cr, XAt, planes, nrb, nsteps);                                  \
+    if (Ap)                                                                                     \
+      hipLaunchKernelGGL((project_bf16_kernel<NB, true>), grid, dim3(kProjWaves * 64), 0, s, key, \
+                         T, k, r, Xb, ldx, cr, XAt, planes, nrb, nsteps, Ap);                   \
+    else                                                                                        \
+      hipLaunchKernelGGL((project_bf16_kernel<NB, false>), grid, dim3(kProjWaves * 64), 0, s,    \
+                         key, T, k, r, Xb, ldx, cr, XAt, planes, nrb, nsteps, Ap);              \
     break;
     LOGRA_PROJ_CASE(1)
     LOGRA_PROJ_CASE(2)

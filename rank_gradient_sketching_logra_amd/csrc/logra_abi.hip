@@ -107,6 +107,86 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
                     "project_input launch");
 }
 
+LOGRA_API int logra_regen_A_gaussian(const logra_key* key, int64_t r, int64_t k, float* A,
+                                     logra_stream stream) {
+  if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A_gaussian: NULL pointer");
+  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "regen_A_gaussian: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (!aligned16(A)) return fail(LOGRA_ERR_ALIGN, "regen_A_gaussian: A not 16-byte aligned");
+  return hip_status(logra::launch_regen_A_gaussian(key_words(key->seed, key), r, k, A,
+                                                   static_cast<hipStream_t>(stream)),
+                    "regen_A_gaussian launch");
+}
+
+LOGRA_API size_t logra_projection_packed_bytes(int64_t r, int64_t k) {
+  if (k < 1 || bad_rank(r)) return 0;
+  return logra::projection_packed_bytes(r, k);
+}
+
+LOGRA_API int logra_pack_projection(int64_t r, int64_t k, const float* A, void* A_packed,
+                                    size_t packed_bytes, logra_stream stream) {
+  if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_projection: NULL pointer");
+  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t need = logra::projection_packed_bytes(r, k);
+  if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_projection: %zu bytes needed", need);
+  if (!aligned16(A_packed)) return fail(LOGRA_ERR_ALIGN, "pack_projection: output not 16-byte aligned");
+  if (overlap(range(A, (size_t)(r * k) * 4), range(A_packed, need)))
+    return fail(LOGRA_ERR_ALIAS, "pack_projection: A overlaps the packed output");
+  return hip_status(logra::launch_pack_projection(r, k, A, A_packed, static_cast<hipStream_t>(stream)),
+                    "pack_projection launch");
+}
+
+LOGRA_API int logra_project_input_explicit(int64_t T, int64_t k, int64_t r, const void* X,
+                                           logra_dtype x_dtype, int64_t ldx, const void* A_packed,
+                                           size_t packed_bytes, float* XAt, void* planes,
+                                           size_t planes_bytes, logra_stream stream) {
+  if (!X || !A_packed || (!XAt && !planes)) return fail(LOGRA_ERR_NULL, "project_input_explicit: NULL pointer");
+  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_explicit: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_explicit: X must be bf16");
+  int st = check_matrix("project_input_explicit X", X, x_dtype, ldx, k);
+  if (st) return st;
+  const size_t aneed = logra::projection_packed_bytes(r, k);
+  if (packed_bytes < aneed) return fail(LOGRA_ERR_WORKSPACE, "project_input_explicit: the packed projection needs %zu bytes", aneed);
+  const size_t pneed = planes ? logra::acc_ws_bytes_per_item(T, 1, r) : 0;
+  if (planes && planes_bytes < pneed) return fail(LOGRA_ERR_WORKSPACE, "project_input_explicit: %zu bytes of packed output needed", pneed);
+  if (!aligned16(A_packed) || (planes && !aligned16(planes)) || (XAt && !aligned16(XAt)))
+    return fail(LOGRA_ERR_ALIGN, "project_input_explicit: operands must be 16-byte aligned");
+  const Range rx = range(X, extent(T, k, ldx, elem_size(x_dtype))), ra = range(A_packed, aneed);
+  const Range rp = planes ? range(planes, pneed) : Range{0, 0};
+  const Range ro = XAt ? range(XAt, (size_t)(T * r) * 4) : Range{0, 0};
+  if (overlap(rx, rp) || overlap(rx, ro) || overlap(rp, ro) || overlap(ra, rp) || overlap(ra, ro))
+    return fail(LOGRA_ERR_ALIAS, "project_input_explicit: outputs overlap an input or each other");
+  return hip_status(logra::launch_project(logra::KeyArg{0, 0}, T, k, r, X, true, ldx, XAt,
+                                          static_cast<uint16_t*>(planes), static_cast<hipStream_t>(stream),
+                                          A_packed),
+                    "project_input_explicit launch");
+}
+
+LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t r, const void* G,
+                                                   logra_dtype g_dtype, int64_t ldg, const float* A,
+                                                   const void* A_packed, size_t packed_bytes,
+                                                   double* out_dev, void* ws, size_t ws_bytes,
+                                                   logra_stream stream) {
+  if (!G || !A || !A_packed || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine_explicit: NULL pointer");
+  if (d < 1 || k < 1 || bad_rank(r))
+    return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine_explicit: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (g_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "reconstruction_cosine_explicit: G must be bf16");
+  int st = check_matrix("reconstruction_cosine_explicit G", G, g_dtype, ldg, k);
+  if (st) return st;
+  const size_t aneed = logra::projection_packed_bytes(r, k);
+  if (packed_bytes < aneed) return fail(LOGRA_ERR_WORKSPACE, "reconstruction_cosine_explicit: the packed projection needs %zu bytes", aneed);
+  const size_t need = logra::reconstruction_cosine_ws_bytes(d, k, r);
+  if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "reconstruction_cosine_explicit: workspace of %zu bytes needed", need);
+  if (!aligned16(ws) || !aligned16(A_packed) || (reinterpret_cast<uintptr_t>(out_dev) & 7u) != 0)
+    return fail(LOGRA_ERR_ALIGN, "reconstruction_cosine_explicit: workspace and packed projection 16-byte, output 8-byte aligned");
+  const Range rg = range(G, extent(d, k, ldg, 2)), rw = range(ws, need), ro = range(out_dev, 32);
+  if (overlap(rg, rw) || overlap(rg, ro) || overlap(rw, ro) || overlap(rw, range(A, (size_t)(r * k) * 4)) ||
+      overlap(rw, range(A_packed, aneed)))
+    return fail(LOGRA_ERR_ALIAS, "reconstruction_cosine_explicit: operands overlap");
+  return hip_status(logra::launch_reconstruction_cosine(logra::KeyArg{0, 0}, d, k, r, G, true, ldg, out_dev, ws,
+                                                        static_cast<hipStream_t>(stream), A, A_packed),
+                    "reconstruction_cosine_explicit launch");
+}
+
 LOGRA_API size_t logra_reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r) {
   if (d < 1 || k < 1 || bad_rank(r)) return 0;
   return logra::reconstruction_cosine_ws_bytes(d, k, r);

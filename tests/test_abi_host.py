@@ -304,3 +304,29 @@ def test_exact_kl_validation(lib):
     assert err(f, 4, 512, A, Bp, B.BF16, float("inf"), 1.0, C, Dp, ws, None) == B.ERR_DOMAIN
     assert err(f, 4, 512, A, Bp, B.BF16, 0.1, 1.0, C, Dp, ws - 1, None) == B.ERR_WORKSPACE
     assert err(f, 4, 512, A, Bp, B.BF16, 0.1, 1.0, C + 4, Dp, ws, None) == B.ERR_ALIGN
+
+
+def test_gaussian_projection_validation(lib):
+    k = ctypes.byref(key())
+    assert err(lib.logra_regen_A_gaussian, k, 8, 64, None, None) == B.ERR_NULL
+    assert err(lib.logra_regen_A_gaussian, k, 300, 64, A, None) == B.ERR_SHAPE
+    assert err(lib.logra_regen_A_gaussian, k, 8, 64, A + 4, None) == B.ERR_ALIGN
+    # 256-column blocks x 8 steps x 16-rank blocks (padded to 1, 2, 4, 6, 8, 12, 16) x 2 KiB
+    assert B.projection_packed_bytes(64, 3584) == 14 * 8 * 4 * 2048
+    assert B.projection_packed_bytes(100, 300) == 2 * 8 * 8 * 2048
+    assert B.projection_packed_bytes(0, 8) == 0
+    nb = B.projection_packed_bytes(8, 64)
+    f = lib.logra_pack_projection
+    assert err(f, 8, 64, None, Bp, nb, None) == B.ERR_NULL
+    assert err(f, 8, 64, A, Bp, nb - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 8, 64, A, A + 64, nb, None) == B.ERR_ALIAS
+    g = lib.logra_project_input_explicit
+    assert err(g, 16, 64, 8, A, B.BF16, 64, Bp, nb, None, None, 0, None) == B.ERR_NULL        # no output
+    assert err(g, 16, 64, 8, A, B.F32, 64, Bp, nb, C, None, 0, None) == B.ERR_DTYPE
+    assert err(g, 16, 64, 8, A, B.BF16, 64, Bp, nb - 16, C, None, 0, None) == B.ERR_WORKSPACE
+    assert err(g, 16, 64, 8, A, B.BF16, 64, Bp, nb, Bp + 64, None, 0, None) == B.ERR_ALIAS     # XAt in A
+    h = lib.logra_reconstruction_cosine_explicit
+    ws = B.reconstruction_cosine_ws_bytes(64, 64, 8)
+    assert err(h, 64, 64, 8, A, B.BF16, 64, None, Bp, nb, C, Dp, ws, None) == B.ERR_NULL
+    assert err(h, 64, 64, 8, A, B.F32, 64, C, Bp, nb, C + 0x100000, Dp, ws, None) == B.ERR_DTYPE
+    assert err(h, 64, 64, 8, A, B.BF16, 64, C, Bp, nb - 1, C + 0x100000, Dp, ws, None) == B.ERR_WORKSPACE

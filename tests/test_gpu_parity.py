@@ -591,6 +591,40 @@ def test_reconstruction_cosine(d, k, r, dtype, ld):
     assert out[3] == pytest.approx(((S @ A) ** 2).sum(), rel=1e-5)
 
 
+# ------------------------------------------------ Gaussian projection variant
+
+
+@pytest.mark.parametrize("r,k", [(64, 3584), (33, 700), (256, 1536), (5, 40)])
+def test_gaussian_projection(r, k):
+    """The Gaussian variant: A from Box-Muller on the Philox stream against the oracle's (device
+    and host libm may differ in the last fp64 bit, so fp32 A is compared within one ulp); the
+    projection with the packed explicit A against the oracle's X A^T; its packed output feeding
+    the accumulate; and the reconstruction cosine with Gaussian A against the oracle's."""
+    say(f"gaussian projection r={r} k={k}")
+    kk = B.key(6, 11, 2)
+    A = B.regen_A_gaussian(kk, r, k, DEV)
+    Ah = A.cpu().numpy()
+    want = oracle.gaussian_A(6, 11, 2, r, k, kind="f32")
+    assert np.all(np.abs(Ah.astype(np.float64) - want) <= np.spacing(np.abs(want)))
+    assert (Ah == want).mean() >= 0.999
+    A64 = oracle.gaussian_A(6, 11, 2, r, k)
+    Ap = B.pack_projection(A)
+    T, ld = 1000, (k + 7) // 8 * 8
+    xb, X = bf16_inputs((T, ld), 1.0, (31, T, k, r, 0))
+    planes = torch.empty((B.packed_input_bytes(T, r),), dtype=torch.uint8, device=DEV)
+    XAt, _ = B.project_input_explicit(bf16_dev(xb)[:, :k], Ap, r, planes=planes)
+    want_x = oracle.project(X[:, :k], A64)
+    assert relfro(XAt.cpu().numpy(), want_x) <= 1e-5
+    d, ldd = 300, 304
+    db, Dm = bf16_inputs((T, ldd), 1e-3, (31, T, d, r, 1))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    B.sketch_accumulate_grouped_packed([(bf16_dev(db)[:, :d], planes, S)], r)
+    assert relfro(S.cpu().numpy(), Dm[:, :d].T @ want_x) <= 5e-5
+    gb, Gh = bf16_inputs((512, ld), 0.01, (31, 512, k, r, 2))
+    out = B.reconstruction_cosine_explicit(bf16_dev(gb)[:, :k], A, Ap).cpu().numpy()
+    assert out[0] == pytest.approx(oracle.reconstruction_cosine(Gh[:, :k], A64), rel=1e-5)
+
+
 # ------------------------------------------------------ whole update
 
 
