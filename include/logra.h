@@ -479,6 +479,42 @@ LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_des
                                          double scale, const float* scale_dev, logra_round mode,
                                          uint64_t sr_seed, logra_stream stream);
 
+/* Bytes of an explicit projection packed as the merge's A operands (the
+ * merge's column order: column block cb of BC = 512 columns when the rank
+ * takes at most four 16-rank steps, else 256; for each wave w, instance e and
+ * rank step s, a 1 KiB hi then a 1 KiB lo operand in which lane l holds
+ * column BC cb + 32(E w + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3), m =
+ * l & 31, and ranks 16s + 8(l >> 5) .. +7).  0 for invalid sizes. */
+LOGRA_API size_t logra_merge_projection_packed_bytes(int64_t r, int64_t k);
+
+/* Pack an explicit A [r x k] (fp32 row-major, e.g. from logra_regen_A_gaussian)
+ * into that form (hi = RNE(a), lo = RNE(a - hi); padding zero).
+ * Errors: as logra_pack_projection. */
+LOGRA_API int logra_pack_merge_projection(int64_t r, int64_t k, const float* A, void* A_packed,
+                                          size_t packed_bytes, logra_stream stream);
+
+typedef struct logra_merge_explicit_desc {
+  logra_key key;          /* key of the matrix (stochastic-rounding draws only) */
+  void* W;                /* [d x k] bf16, leading dimension ldw                */
+  int64_t d;
+  int64_t k;
+  int64_t ldw;
+  const void* U_packed;   /* logra_packed_update_bytes(d, r) bytes             */
+  const void* A_packed;   /* logra_merge_projection_packed_bytes(r, k) bytes   */
+  int64_t row0;
+} logra_merge_explicit_desc;
+
+/* logra_merge_grouped_packed with an explicit projection (the Gaussian
+ * variant) instead of the key's signs: W <- round(W - s U A), s = scale *
+ * (*scale_dev if given) with A taken as given (no 1/sqrt(r) applied).  A and
+ * U both enter as bf16 hi + lo; the product keeps A hi x U hi, A hi x U lo
+ * and A lo x U hi (the dropped lo x lo term is below 2^-16 relative).
+ * Errors: as logra_merge_grouped_packed; NULL projection; misaligned or
+ * overlapping projection. */
+LOGRA_API int logra_merge_grouped_explicit(int64_t r, const logra_merge_explicit_desc* descs, int n,
+                                           double scale, const float* scale_dev, logra_round mode,
+                                           uint64_t sr_seed, logra_stream stream);
+
 /* ------------------------------------------------------ policy sync */
 
 /* What the trainer sends the rollout side for one matrix ([paper] §2.2

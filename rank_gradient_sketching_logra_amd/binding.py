@@ -60,6 +60,11 @@ class SyncDesc(Structure):
     _fields_ = [("header", POINTER(SyncHeader)), ("payload", c_void_p), ("W", c_void_p), ("ldw", c_int64)]
 
 
+class MergeExplicitDesc(Structure):
+    _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
+                ("U_packed", c_void_p), ("A_packed", c_void_p), ("row0", c_int64)]
+
+
 SIGNATURES = {
     "logra_version": (c_char_p, []),
     "logra_last_error": (c_char_p, []),
@@ -88,6 +93,10 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_merge_projection_packed_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_pack_merge_projection": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "logra_merge_grouped_explicit": (c_int, [c_int64, POINTER(MergeExplicitDesc), c_int, c_double, c_void_p,
+                                             c_int, c_uint64, c_void_p]),
     "logra_regen_A_gaussian": (c_int, [POINTER(Key), c_int64, c_int64, c_void_p, c_void_p]),
     "logra_projection_packed_bytes": (c_size_t, [c_int64, c_int64]),
     "logra_pack_projection": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -504,3 +513,31 @@ def reconstruction_cosine_explicit(G: torch.Tensor, A: torch.Tensor, A_packed: t
                                                       _ptr(A_packed), A_packed.numel(), _ptr(o), _ptr(ws),
                                                       ws.numel(), _stream(G, stream)))
     return o
+
+
+def merge_projection_packed_bytes(r: int, k: int) -> int:
+    return lib().logra_merge_projection_packed_bytes(r, k)
+
+
+def pack_merge_projection(A: torch.Tensor, out=None, stream=None):
+    """An explicit fp32 A [r x k] in the merge's operand order (uint8 tensor)."""
+    r, k = A.shape
+    nb = merge_projection_packed_bytes(r, k)
+    P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=A.device)
+    _check(lib().logra_pack_merge_projection(r, k, _ptr(A), _ptr(P), P.numel(), _stream(A, stream)))
+    return P
+
+
+def merge_grouped_explicit(items, r: int, scale: float, scale_dev=None, mode: str = "nearest",
+                           sr_seed: int = 0, stream=None):
+    """items: (key, W, U_packed, A_packed) or (key, W, U_packed, A_packed, row0); one launch."""
+    n = len(items)
+    descs = (MergeExplicitDesc * n)()
+    for i, it in enumerate(items):
+        k_, W, P, Ap = it[0], it[1], it[2], it[3]
+        row0 = it[4] if len(it) > 4 else 0
+        descs[i] = MergeExplicitDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), P.data_ptr(),
+                                     Ap.data_ptr(), row0)
+    m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
+    _check(lib().logra_merge_grouped_explicit(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
+                                              _stream(items[0][1], stream)))

@@ -84,6 +84,7 @@ struct MergeItem {
   int64_t d, k, ldw;
   const void* U;   // [d x r] fp32, or the packed update (packed launches)
   int64_t row0;
+  const void* A = nullptr;  // explicit projection in merge operand order (packed launches), or null
 };
 // Several bf16 merges sharing r, the scale and the rounding mode in one launch.
 hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,
@@ -93,6 +94,9 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
 int merge_rank_steps(int64_t r);
 size_t packed_update_bytes(int64_t d, int64_t r);
 // packed = split(fl32(s U)), s = scale * (*scale_dev if given).
+size_t merge_projection_packed_bytes(int64_t r, int64_t k);
+hipError_t launch_pack_merge_projection(int64_t r, int64_t k, const float* A, void* packed,
+                                        hipStream_t s);
 hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, float scale,
                               const float* scale_dev, void* packed, hipStream_t s);
 hipError_t launch_merge(KeyArg key, int64_t d, int64_t k, int64_t r, void* W, bool bf16,

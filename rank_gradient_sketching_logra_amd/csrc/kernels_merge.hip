@@ -212,6 +212,7 @@ struct MergeGroupArgs {
   KeyArg sr_key[kMaxGroup];
   uint16_t* W[kMaxGroup];
   const void* U[kMaxGroup];               // fp32 [d x r], or packed operands
+  const uint16_t* A[kMaxGroup];           // explicit projection in operand form, or null
   int64_t d[kMaxGroup];
   int64_t k[kMaxGroup];
   int64_t ldw[kMaxGroup];
@@ -231,7 +232,11 @@ struct MergeGroupArgs {
 // PACKED: U arrives already split in operand order (see the packed update
 // layout); the band's U slabs are then copied into the ring as they are,
 // with no split pass and no split buffer.
-template <int KS, int E, bool STOCH, bool PACKED>
+// EXPLICIT (with PACKED): the A operands come from an explicit projection
+// packed in the merge's operand order (bf16 hi and lo, see
+// pack_merge_projection_kernel) instead of sign bits; each rank step then
+// takes three MFMAs (A hi x U hi, A hi x U lo, A lo x U hi).
+template <int KS, int E, bool STOCH, bool PACKED, bool EXPLICIT = false>
 __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGroupArgs g) {
   constexpr int NWV = kMergeWaves;
   constexpr int BC = 32 * NWV * E;        // columns per block
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     // Sign bits of ranks [0, 16 KS) for the block's columns: word w of rank j
     // holds columns cblk + 32w + (0..31), bit set meaning -1.
     uint32_t* sbits = reinterpret_cast<uint32_t*>(lds);
-    {
+    if constexpr (!EXPLICIT) {
       const KeyWords kw{key.k0, key.k1};
       constexpr int NP = (BC + 255) / 256;  // Philox blocks per rank
       for (int task = tid; task < 16 * KS * NP; task += NWV * 64) {
@@ -335,7 +340,18 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     // ranks 16s + 8(l >> 5) + i, i = 0..7.  Ranks >= r read as +1; their U
     // terms are zero.
     u32x4 afrag[E][KS];
-    {
+    u32x4 alo[E][EXPLICIT ? KS : 1];
+    if constexpr (EXPLICIT) {
+      const uint16_t* __restrict__ Ap = g.A[item];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint16_t* p = Ap + (((((cb * NWV + wave) * E + e) * KS + s) * 2) * 512) + lane * 8;
+          afrag[e][s] = *reinterpret_cast<const u32x4*>(p);
+          alo[e][s] = *reinterpret_cast<const u32x4*>(p + 512);
+        }
+    } else {
       const int m = lane & 31;
       const int cm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
@@ -387,6 +403,12 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         for (int e = 0; e < E; ++e)
           acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bl),
                                                            acc[e], 0, 0, 0);
+        if constexpr (EXPLICIT) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(alo[e][s]), as_bf16x8(bh),
+                                                             acc[e], 0, 0, 0);
+        }
         // With many rank steps, keep each step's operand loads next to their
         // use: hoisting them all would exceed the register file.
         if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
@@ -688,7 +710,9 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   MergeGroupArgs g{};
   g.n = n;
   g.r = r;
-  g.scale_cr = (float)(scale * cr);
+  const bool explicit_a = items[0].A != nullptr;  // all or none (checked by the caller)
+  if (explicit_a && !packed) return hipErrorInvalidValue;
+  g.scale_cr = (float)(explicit_a ? scale : scale * cr);
   g.scale_dev = scale_dev;
   g.unit_begin[0] = 0;
   for (int i = 0; i < n; ++i) {
@@ -696,6 +720,7 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     g.sr_key[i] = items[i].sr_key;
     g.W[i] = static_cast<uint16_t*>(items[i].W);
     g.U[i] = items[i].U;
+    g.A[i] = static_cast<const uint16_t*>(items[i].A);
     g.d[i] = items[i].d;
     g.k[i] = items[i].k;
     g.ldw[i] = items[i].ldw;
@@ -746,11 +771,20 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   else                                                                                      \
     hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false, P>), grid, dim3(kMergeWaves * 64), 0, \
                        s, g);
-#define LOGRA_MERGE_LAUNCH(KS, E)   \
-  if (packed) {                     \
-    LOGRA_MERGE_LAUNCH_P(KS, E, true) \
-  } else {                          \
-    LOGRA_MERGE_LAUNCH_P(KS, E, false) \
+#define LOGRA_MERGE_LAUNCH_X(KS, E)                                                            \
+  if (stochastic)                                                                          \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true, true, true>), grid,                \
+                       dim3(kMergeWaves * 64), 0, s, g);                                  \
+  else                                                                                     \
+    hipLaunchKernelGGL((merge_bf16_kernel<KS, E, false, true, true>), grid,               \
+                       dim3(kMergeWaves * 64), 0, s, g);
+#define LOGRA_MERGE_LAUNCH(KS, E)        \
+  if (explicit_a) {                      \
+    LOGRA_MERGE_LAUNCH_X(KS, E)          \
+  } else if (packed) {                   \
+    LOGRA_MERGE_LAUNCH_P(KS, E, true)    \
+  } else {                               \
+    LOGRA_MERGE_LAUNCH_P(KS, E, false)   \
   }
   switch (ks) {
     case 1: LOGRA_MERGE_LAUNCH(1, 2) break;
@@ -762,6 +796,7 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   }
 #undef LOGRA_MERGE_LAUNCH
 #undef LOGRA_MERGE_LAUNCH_P
+#undef LOGRA_MERGE_LAUNCH_X
   return hipGetLastError();
 }
 
@@ -823,6 +858,69 @@ __global__ __launch_bounds__(256) void pack_update_kernel(int64_t d, int64_t r, 
   *reinterpret_cast<u32x4*>(dst + 512) = lv;
 }
 }  // namespace
+
+// An explicit projection A [r x k] (fp32 row-major) in the merge's A-operand
+// order: for column block cb (BC = 256 E columns, E = 2 when the merge takes
+// at most four 16-rank steps, else 1), wave w, instance e and rank step s, a
+// 1 KiB hi slab then a 1 KiB lo slab, lane l holding column
+// BC cb + 32(E w + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3) (m = l & 31)
+// and ranks 16s + 8(l >> 5) .. +7; ranks >= r and columns >= k are zero.
+size_t merge_projection_packed_bytes(int64_t r, int64_t k) {
+  const int ks = merge_rank_steps(r);
+  const int e = ks <= 4 ? 2 : 1;
+  const int64_t bc = 32 * kMergeWaves * e;
+  return (size_t)((k + bc - 1) / bc) * kMergeWaves * e * ks * 2048;
+}
+
+namespace {
+__global__ __launch_bounds__(256) void pack_merge_projection_kernel(int64_t r, int64_t k, int ks,
+                                                                    int ee,
+                                                                    const float* __restrict__ A,
+                                                                    uint16_t* __restrict__ P) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = (int)(t & 63);
+  const int64_t unit = t >> 6;  // (((cb * waves + w) * E + e) * KS + s)
+  const int64_t bc = 32 * kMergeWaves * ee;
+  const int64_t ncb = (k + bc - 1) / bc;
+  if (unit >= ncb * kMergeWaves * ee * ks) return;
+  const int s = (int)(unit % ks);
+  const int64_t u1 = unit / ks;
+  const int e = (int)(u1 % ee);
+  const int64_t u2 = u1 / ee;
+  const int w = (int)(u2 % kMergeWaves);
+  const int64_t cb = u2 / kMergeWaves;
+  const int m = lane & 31;
+  const int64_t col = cb * bc + 32 * (ee * w + e) + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int64_t j0 = 16 * s + 8 * (lane >> 5);
+  uint32_t hv[4], lv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float x[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t j = j0 + 2 * p + q;
+      x[q] = (j < r && col < k) ? A[j * k + col] : 0.f;
+    }
+    const float h0 = (float)(__bf16)x[0], h1 = (float)(__bf16)x[1];
+    hv[p] = bf16_pair(h0, h1);
+    lv[p] = bf16_pair(x[0] - h0, x[1] - h1);
+  }
+  uint16_t* dst = P + unit * 1024 + lane * 8;
+  *reinterpret_cast<u32x4*>(dst) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+  *reinterpret_cast<u32x4*>(dst + 512) = u32x4{lv[0], lv[1], lv[2], lv[3]};
+}
+}  // namespace
+
+hipError_t launch_pack_merge_projection(int64_t r, int64_t k, const float* A, void* packed,
+                                        hipStream_t s) {
+  const int ks = merge_rank_steps(r);
+  const int ee = ks <= 4 ? 2 : 1;
+  const int64_t bc = 32 * kMergeWaves * ee;
+  const int64_t threads = (k + bc - 1) / bc * kMergeWaves * ee * ks * 64;
+  hipLaunchKernelGGL(pack_merge_projection_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, s, r, k, ks, ee, A, static_cast<uint16_t*>(packed));
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_update(int64_t d, int64_t r, const float* U, float scale,
                               const float* scale_dev, void* packed, hipStream_t s) {

@@ -512,6 +512,7 @@ struct MergeOperands {
   int64_t d, k, ldw;
   const void* U;
   int64_t row0;
+  const void* A = nullptr;  // explicit projection (merge operand order), or null
 };
 int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, int n, double scale,
                        const float* scale_dev, logra_round mode, uint64_t sr_seed, bool packed,
@@ -540,8 +541,17 @@ int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, in
       if (j < i && overlap(u_range(e), range(ops[j].W, extent(ops[j].d, ops[j].k, ops[j].ldw, 2))))
         return fail(LOGRA_ERR_ALIAS, "%s: U of descriptor %d overlaps W of %d", name, i, j);
     }
+    if ((e.A != nullptr) != (ops[0].A != nullptr))
+      return fail(LOGRA_ERR_NULL, "%s: explicit projections for all descriptors or none", name);
+    if (e.A) {
+      const Range ra = range(e.A, logra::merge_projection_packed_bytes(r, e.k));
+      if (!aligned16(e.A)) return fail(LOGRA_ERR_ALIGN, "%s: projection %d not 16-byte aligned", name, i);
+      for (int j = 0; j <= i; ++j)
+        if (overlap(ra, range(ops[j].W, extent(ops[j].d, ops[j].k, ops[j].ldw, 2))))
+          return fail(LOGRA_ERR_ALIAS, "%s: projection %d overlaps a W", name, i);
+    }
     items[i] = logra::MergeItem{key_words(e.key->seed, e.key), key_words(sr_seed, e.key), e.W, e.d, e.k,
-                                e.ldw, e.U, e.row0};
+                                e.ldw, e.U, e.row0, e.A};
   }
   return hip_status(logra::launch_merge_grouped(items, n, r, scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
                                                 packed, static_cast<hipStream_t>(stream)),
@@ -572,6 +582,40 @@ LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_des
     ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw,
                            descs[i].U_packed, descs[i].row0};
   return merge_grouped_impl("merge_grouped_packed", r, ops, n, scale, scale_dev, mode, sr_seed, true,
+                            stream);
+}
+
+LOGRA_API size_t logra_merge_projection_packed_bytes(int64_t r, int64_t k) {
+  if (k < 1 || bad_rank(r)) return 0;
+  return logra::merge_projection_packed_bytes(r, k);
+}
+
+LOGRA_API int logra_pack_merge_projection(int64_t r, int64_t k, const float* A, void* A_packed,
+                                          size_t packed_bytes, logra_stream stream) {
+  if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_merge_projection: NULL pointer");
+  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_merge_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t need = logra::merge_projection_packed_bytes(r, k);
+  if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_merge_projection: %zu bytes needed", need);
+  if (!aligned16(A_packed)) return fail(LOGRA_ERR_ALIGN, "pack_merge_projection: output not 16-byte aligned");
+  if (overlap(range(A, (size_t)(r * k) * 4), range(A_packed, need)))
+    return fail(LOGRA_ERR_ALIAS, "pack_merge_projection: A overlaps the packed output");
+  return hip_status(logra::launch_pack_merge_projection(r, k, A, A_packed, static_cast<hipStream_t>(stream)),
+                    "pack_merge_projection launch");
+}
+
+LOGRA_API int logra_merge_grouped_explicit(int64_t r, const logra_merge_explicit_desc* descs, int n,
+                                           double scale, const float* scale_dev, logra_round mode,
+                                           uint64_t sr_seed, logra_stream stream) {
+  if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped_explicit: NULL descriptors");
+  if (n < 1 || n > LOGRA_MAX_GROUP)
+    return fail(LOGRA_ERR_SHAPE, "merge_grouped_explicit: need 1 <= n <= %d", LOGRA_MAX_GROUP);
+  MergeOperands ops[LOGRA_MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    if (!descs[i].A_packed) return fail(LOGRA_ERR_NULL, "merge_grouped_explicit: NULL projection in descriptor %d", i);
+    ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw,
+                           descs[i].U_packed, descs[i].row0, descs[i].A_packed};
+  }
+  return merge_grouped_impl("merge_grouped_explicit", r, ops, n, scale, scale_dev, mode, sr_seed, true,
                             stream);
 }
 

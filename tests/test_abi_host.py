@@ -330,3 +330,19 @@ def test_gaussian_projection_validation(lib):
     assert err(h, 64, 64, 8, A, B.BF16, 64, None, Bp, nb, C, Dp, ws, None) == B.ERR_NULL
     assert err(h, 64, 64, 8, A, B.F32, 64, C, Bp, nb, C + 0x100000, Dp, ws, None) == B.ERR_DTYPE
     assert err(h, 64, 64, 8, A, B.BF16, 64, C, Bp, nb - 1, C + 0x100000, Dp, ws, None) == B.ERR_WORKSPACE
+
+
+def test_merge_explicit_validation(lib):
+    assert B.merge_projection_packed_bytes(64, 3584) == 7 * 8 * 2 * 4 * 2048     # BC = 512, E = 2, KS = 4
+    assert B.merge_projection_packed_bytes(256, 5120) == 20 * 8 * 1 * 16 * 2048  # BC = 256, E = 1, KS = 16
+    assert B.merge_projection_packed_bytes(8, 0) == 0
+    nb = B.merge_projection_packed_bytes(8, 64)
+    assert err(lib.logra_pack_merge_projection, 8, 64, A, Bp, nb - 1, None) == B.ERR_WORKSPACE
+    assert err(lib.logra_pack_merge_projection, 8, 64, None, Bp, nb, None) == B.ERR_NULL
+    f = lib.logra_merge_grouped_explicit
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, None, 0))
+    assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_NULL
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C + 8, 0))
+    assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, A + 256, 0))
+    assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS       # projection inside W

@@ -625,6 +625,29 @@ def test_gaussian_projection(r, k):
     assert out[0] == pytest.approx(oracle.reconstruction_cosine(Gh[:, :k], A64), rel=1e-5)
 
 
+@pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "nearest"), (256, "stochastic")])
+def test_gaussian_merge(r, mode):
+    """The merge with the Gaussian projection (explicit A in the merge's operand order) against the
+    oracle's W - s U A with the same A, over full, ragged-row and ragged-column matrices."""
+    shapes = [(320, 1024), (100, 712), (64, 3584)]
+    say(f"gaussian merge r={r} {mode}")
+    items, host = [], []
+    for i, (d, k) in enumerate(shapes):
+        wb, W64 = bf16_inputs((d, k), 0.02, (32, d, k, i, 2))
+        U = synth.fp32_matrix((d, r), 1.0, (32, d, r, i, 7))
+        kk = B.key(8, 70 + i, 1)
+        A = B.regen_A_gaussian(kk, r, k, DEV)
+        items.append((kk, bf16_dev(wb), B.pack_update(torch.from_numpy(U).to(DEV)), B.pack_merge_projection(A)))
+        host.append((i, d, k, W64, U))
+    B.merge_grouped_explicit(items, r, 3e-4, mode=mode, sr_seed=4)
+    for (_, W, _, _), (i, d, k, W64, U) in zip(items, host):
+        A64 = oracle.gaussian_A(8, 70 + i, 1, r, k)
+        u = philox.sr_draws(4, 70 + i, 1, d, k) if mode == "stochastic" else None
+        want = oracle.merge(W64, U.astype(np.float64), A64, 3e-4, w_dtype="bf16", mode=mode, u_draws=u)
+        frac, exact = ulp_check(bf16_host(W), want)
+        assert frac >= 0.9999 and exact >= 0.999
+
+
 # ------------------------------------------------------ whole update
 
 
