@@ -3,8 +3,8 @@
 One step = one update over the whole layer set of the workload:
   A. project every selected matrix's input, every microbatch, straight into
      the packed operand form the accumulate reads (XAt = X A^T)
-  B. accumulate every sketch, every microbatch (grouped: the seven matrices
-     of one layer and one microbatch per launch -- one kernel per launch)
+  B. accumulate every sketch, every microbatch (one persistent launch per
+     microbatch over every matrix of every layer)
   C. RowAdam for every sketch (writing the update straight in the merge's
      packed operand form), predicted-KL q over the context set, alpha on
      the device
@@ -19,7 +19,7 @@ matrix) divided by their HIP-event time on the stream the kernels run on.
 Modes:
   (default)              the benchmark; prints one JSON line
   --counter-run          a short run for rocprofv3 --pmc: a plain copy of known
-                         size (the calibration) and two steps of two layers
+                         size (the calibration) and one step of the workload
   --summarize-traffic F W  read the FETCH_SIZE (F) and WRITE_SIZE (W) counter
                          CSVs of two --counter-run passes and print the
                          calibrated HBM bytes per accumulate launch
@@ -46,8 +46,8 @@ POOL_LIMIT_BYTES = 160e9  # distinct input sets up to this size, else a pool
 POOL_SETS = 17            # input sets in a pool (27B set: 17 x 0.74 GB)
 BALLAST_BYTES = {"dense-27b-set-r256": 10 * 10**9}
 DEFAULT_WORKLOAD = "qwen2.5-7b-set-r64"
-ACC_KERNEL = "acc_bf16_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "acc_bf16_kernel.qwen2.5-7b-set-r64.traffic.md")
+ACC_KERNEL = "acc_bf16_table_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "acc_bf16_table_kernel.qwen2.5-7b-set-r64.traffic.md")
 KERNEL_SOURCES = ["rank_gradient_sketching_logra_amd/csrc/kernels_sketch.hip",
                   "rank_gradient_sketching_logra_amd/csrc/kernels.h",
                   "rank_gradient_sketching_logra_amd/csrc/device_common.h"]
@@ -186,8 +186,7 @@ def main():
     rounding = args.rounding or w.rounding
     layers = args.layers or w.layers
     if args.counter_run:
-        layers = min(layers, 2)
-        args.steps, args.warmup = 2, 0
+        args.steps, args.warmup = 1, 0
     T, r, M = w.T, w.r, w.microbatches
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -232,6 +231,7 @@ def main():
     keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
     maxd = max(d for (_, _, _, d, _) in mats)
     ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
+    acc_ws = B.workspace(B.sketch_accumulate_table_ws_bytes(len(mats)), dev)
     # the rest of the model's weights, resident but untouched (27B set: the projections are
     # 43.6 GB of the model's ~54 GB)
     ballast = torch.empty((BALLAST_BYTES.get(w.name, 0),), dtype=torch.uint8, device=dev)
@@ -249,7 +249,7 @@ def main():
     acc_total = sum(acc_bytes(T, d, r) for (_, _, _, d, _) in mats) * M
     merge_total = sum(merge_bytes(d, k, r) for (_, _, _, d, k) in mats)
     proj_total = sum(project_bytes(T, k, r) for (_, _, _, d, k) in mats) * M
-    n_acc_launch = layers * M
+    n_acc_launch = M
     acc_per_launch = acc_total // n_acc_launch
     t_step = 0
 
@@ -266,10 +266,10 @@ def main():
                                            planes=PL[(sid[(l, mb)], kind)])
         ev[1].record()
         for mb in range(M):                          # B: backward-side sketch accumulation
-            for l in reversed(range(layers)):
-                i = sid[(l, mb)]
-                B.sketch_accumulate_grouped_packed([(D[(i, kind)], PL[(i, kind)], S[(l, kind)])
-                                                    for (kind, d, k) in by_layer[l]], r)
+            # one persistent launch per microbatch over every matrix of every layer
+            B.sketch_accumulate_table([(D[(sid[(l, mb)], kind)], PL[(sid[(l, mb)], kind)], S[(l, kind)])
+                                       for l in reversed(range(layers)) for (kind, d, k) in by_layer[l]],
+                                      r, ws=acc_ws)
         ev[2].record()
         for key_ in S:                               # C: optimiser (U in the merge's packed form)
             B.rowadam_packed(S[key_], V[key_], t_step, w.beta, w.eps, out=UP[key_], ws=ra_ws)

@@ -301,6 +301,24 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
                                                      const logra_acc_packed_desc* descs, int n,
                                                      logra_stream stream);
 
+/* Workspace bytes of logra_sketch_accumulate_table for n matrices (the
+ * matrix table the kernel reads). */
+LOGRA_API size_t logra_sketch_accumulate_table_ws_bytes(int n);
+
+/* logra_sketch_accumulate_grouped_packed over any number of matrices in one
+ * persistent launch (e.g. all projections of all layers for one
+ * microbatch): one block per compute unit takes the matrices' 256-column
+ * tiles in turn, so the compute units one layer's tiles leave idle and the
+ * ramp of separate launches are shared by the whole table.  Each tile is
+ * computed whole by one block in the documented summation order, so S has the
+ * same bits as with grouped or single calls.  The descriptor array is read on
+ * the host during the call and copied into the workspace on the stream.
+ * Errors: as logra_sketch_accumulate_grouped_packed for each descriptor;
+ * n < 1; workspace too small or misaligned; two sketches overlapping, or a
+ * sketch or the workspace overlapping another descriptor's operands. */
+LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_acc_packed_desc* descs,
+                                            int n, void* ws, size_t ws_bytes, logra_stream stream);
+
 /* ------------------------------------------------------------- optimiser */
 
 /* Workspace bytes logra_rowadam needs for d rows. */

@@ -93,6 +93,9 @@ SIGNATURES = {
     "logra_merge_grouped": (c_int, [c_int64, POINTER(MergeDesc), c_int, c_double, c_void_p, c_int,
                                     c_uint64, c_void_p]),
     "logra_packed_update_bytes": (c_size_t, [c_int64, c_int64]),
+    "logra_sketch_accumulate_table_ws_bytes": (c_size_t, [c_int]),
+    "logra_sketch_accumulate_table": (c_int, [c_int64, c_int64, POINTER(AccPackedDesc), c_int, c_void_p,
+                                              c_size_t, c_void_p]),
     "logra_merge_projection_packed_bytes": (c_size_t, [c_int64, c_int64]),
     "logra_pack_merge_projection": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_merge_grouped_explicit": (c_int, [c_int64, POINTER(MergeExplicitDesc), c_int, c_double, c_void_p,
@@ -541,3 +544,22 @@ def merge_grouped_explicit(items, r: int, scale: float, scale_dev=None, mode: st
     m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
     _check(lib().logra_merge_grouped_explicit(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
                                               _stream(items[0][1], stream)))
+
+
+def sketch_accumulate_table_ws_bytes(n: int) -> int:
+    return lib().logra_sketch_accumulate_table_ws_bytes(n)
+
+
+def sketch_accumulate_table(items, r: int, ws=None, stream=None):
+    """items: sequence of (D bf16 [T x d], packed planes, S) sharing T and r; one persistent launch."""
+    n = len(items)
+    T = items[0][0].shape[0]
+    descs = (AccPackedDesc * n)()
+    for i, (D, P, S) in enumerate(items):
+        if D.shape[0] != T:
+            raise ValueError("every D must have the same number of tokens")
+        descs[i] = AccPackedDesc(D.data_ptr(), P.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
+    if ws is None:
+        ws = workspace(sketch_accumulate_table_ws_bytes(n), items[0][0].device)
+    _check(lib().logra_sketch_accumulate_table(T, r, descs, n, _ptr(ws), ws.numel(),
+                                               _stream(items[0][0], stream)))

@@ -49,6 +49,14 @@ hipError_t launch_pack_projection(int64_t r, int64_t k, const float* A, void* pa
 // packed: items' ws already hold the packed projected input (XAt unused).
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,
                              bool packed, hipStream_t s);
+// Packed accumulate over any number of matrices in one persistent launch:
+// the matrix table (acc_table_ws_bytes(n) of device workspace) is copied in
+// from the host on the stream.
+size_t acc_table_ws_bytes(int n);
+hipError_t launch_accumulate_table(int64_t T, int64_t r, const AccItem* items, int n, void* ws,
+                                   hipStream_t s);
+// Compute units of the current device.
+int64_t compute_units();
 
 // cos(G, (G A^T) A) and its parts {cos, ||G||^2, ||G A^T||^2, ||G A^T A||^2}
 // written to out (4 doubles on the device).

@@ -686,7 +686,7 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(KeyArg key, int64_t d, i
 }  // namespace
 
 // Compute units of the current device (queried once per device).
-static int64_t compute_units() {
+int64_t compute_units() {
   static int64_t cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

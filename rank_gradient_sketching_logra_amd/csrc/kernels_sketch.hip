@@ -17,6 +17,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <vector>
+
 namespace logra {
 
 namespace {
@@ -562,38 +564,59 @@ struct AccShape {
 // single calls give the same bits.  Blocks that reach past column d take
 // guarded register loads; rows past T (last step only) are loaded from row
 // T - 1 and zeroed.
+}  // namespace
+
+// One matrix of a table-driven accumulate (device memory); entry n holds only
+// tile_begin = the total tile count.
+struct AccTableEntry {
+  const void* D;
+  const uint16_t* planes;
+  float* S;
+  int64_t d, ldd, tile_begin;
+};
+
+namespace {
+
+// One tile of the accumulate: 256 columns of one matrix, all ranks, all tokens.
+struct AccTile {
+  const uint16_t* D;       // bf16 [T x d], leading dimension ldd
+  const uint16_t* planes;  // packed projected input
+  float* S;                // [d x r]
+  int64_t d, ldd, q, T, r;
+  int nsteps, nrb;
+};
+
 template <int RB>
-__global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
+__device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
   using Sh = AccShape<RB>;
   constexpr int R = Sh::R, NQ = Sh::NQ, NS = Sh::NS, RBW = Sh::RBW;
   constexpr int kClass = Sh::kClass, kSlot = Sh::kSlot;
-  __shared__ __align__(16) u32x4 smem[Sh::kSmemKiB * 64];
 
-  const int64_t logical = xcd_logical_block();
-  if (logical >= g.tile_begin[g.n]) return;
-  int item = 0;
-  while (logical >= g.tile_begin[item + 1]) ++item;
-  const int64_t q = logical - g.tile_begin[item];
-  const uint16_t* __restrict__ D = static_cast<const uint16_t*>(g.D[item]);
-  const int64_t ldd = g.ldd[item];
-  const int64_t d = g.d[item];
-  const int64_t T = g.T;
+  const int64_t q = tile.q;
+  const uint16_t* __restrict__ D = tile.D;
+  const int64_t ldd = tile.ldd;
+  const int64_t d = tile.d;
+  const int64_t T = tile.T;
 
-  const int lane = threadIdx.x & 63;
+  // The lane index is opaque per tile, so that a loop over tiles does not
+  // hoist every lane-derived address out of it and hold them throughout.
+  int lane_o = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane_o));
+  const int lane = lane_o;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rb = wave % RBW;            // rank block of this wave
   const int qt = wave / RBW;            // token class
   const bool has_rb = rb < RB;          // uniform per wave
   const int hw = lane >> 5;
-  const int nsteps = g.nsteps;
+  const int nsteps = tile.nsteps;
   const int Q = (nsteps + NQ - 1) / NQ;  // iterations: steps NQ k + qt, k < Q
 
   const int64_t c0 = q * kAccCols;
   const int64_t col = c0 + 8 * (lane & 31);
   const bool interior = c0 + kAccCols <= d;  // uniform per block
   const bool col_full = col + 8 <= d;
-  const uint16_t* __restrict__ planes = g.planes[item] + (int64_t)rb * 1024 + lane * 8;
-  const int64_t bstride = (int64_t)g.nrb * 1024;
+  const uint16_t* __restrict__ planes = tile.planes + (int64_t)rb * 1024 + lane * 8;
+  const int64_t bstride = (int64_t)tile.nrb * 1024;
 
   f32x16 acc[8];
 #pragma unroll
@@ -740,8 +763,8 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
   }
   wait_vmcnt<0>();  // no load may still target LDS past this point
 
-  float* __restrict__ S = g.S[item];
-  const int64_t r = g.r;
+  float* __restrict__ S = tile.S;
+  const int64_t r = tile.r;
   // Class sums in accumulator order: element (e, j) of lane l at
   // [slot][(4e + j / 4) 64 + l] as float4, one 32 KiB slot per wave.
   f32x4* xr = reinterpret_cast<f32x4*>(smem);
@@ -873,6 +896,45 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
         for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
       }
     }
+  }
+}
+
+template <int RB>
+__global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
+  __shared__ __align__(16) u32x4 smem[AccShape<RB>::kSmemKiB * 64];
+  const int64_t logical = xcd_logical_block();
+  if (logical >= g.tile_begin[g.n]) return;
+  int item = 0;
+  while (logical >= g.tile_begin[item + 1]) ++item;
+  const AccTile tile{static_cast<const uint16_t*>(g.D[item]), g.planes[item], g.S[item], g.d[item],
+                     g.ldd[item], logical - g.tile_begin[item], g.T, g.r, g.nsteps, g.nrb};
+  acc_tile<RB>(tile, smem);
+}
+
+// Persistent form over a device-resident table of many matrices (e.g. every
+// projection of every layer for one microbatch): the grid is one block per
+// compute unit and block b takes tiles b, b + G, b + 2G, ... of the table's
+// tile list (matrix by matrix, column block by column block), so the compute
+// units left idle by one layer's tiles and the ramp of separate launches are
+// shared across the whole table.  Each tile is still computed whole by one
+// block, so the results are bit-identical to the per-layer launches.
+template <int RB>
+__global__ __launch_bounds__(512, 1) void acc_bf16_table_kernel(const AccTableEntry* __restrict__ tab,
+                                                                int n, int64_t T, int64_t r,
+                                                                int nsteps, int nrb) {
+  __shared__ __align__(16) u32x4 smem[AccShape<RB>::kSmemKiB * 64];
+  const int64_t total = tab[n].tile_begin;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    int lo = 0, hi = n - 1;  // the entry holding tile t: tile_begin[lo] <= t < tile_begin[lo + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tab[mid].tile_begin <= t) lo = mid; else hi = mid - 1;
+    }
+    const AccTableEntry& e = tab[lo];
+    const AccTile tile{static_cast<const uint16_t*>(e.D), e.planes, e.S, e.d, e.ldd,
+                       t - e.tile_begin, T, r, nsteps, nrb};
+    acc_tile<RB>(tile, smem);
+    __syncthreads();  // every wave is done with the LDS before the next tile's loads land
   }
 }
 
@@ -1034,6 +1096,39 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
     case 2: hipLaunchKernelGGL(acc_bf16_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, g); break;
     case 4: hipLaunchKernelGGL(acc_bf16_kernel<4>, grid, dim3(kAccWaves * 64), 0, s, g); break;
     case 8: hipLaunchKernelGGL(acc_bf16_kernel<8>, grid, dim3(kAccWaves * 64), 0, s, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t acc_table_ws_bytes(int n) { return round256((size_t)(n + 1) * sizeof(AccTableEntry)); }
+
+hipError_t launch_accumulate_table(int64_t T, int64_t r, const AccItem* items, int n, void* ws,
+                                   hipStream_t s) {
+  if (n < 1) return hipErrorInvalidValue;
+  std::vector<AccTableEntry> tab((size_t)n + 1);
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    tab[i] = AccTableEntry{items[i].D, static_cast<const uint16_t*>(items[i].ws), items[i].S,
+                           items[i].d, items[i].ldd, tiles};
+    tiles += acc_col_blocks(items[i].d);
+  }
+  tab[n] = AccTableEntry{nullptr, nullptr, nullptr, 0, 0, tiles};
+  // From pageable memory the copy is staged before the call returns, so the
+  // table may go out of scope right after.
+  hipError_t e = hipMemcpyAsync(ws, tab.data(), tab.size() * sizeof(AccTableEntry),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  const int nrb = (int)(acc_rank_pad(r) / 32);
+  const int nsteps = (int)(acc_token_pad(T) / kAccStep);
+  const int64_t cus = compute_units();
+  const dim3 grid((unsigned)(tiles < cus ? tiles : cus));
+  const AccTableEntry* t = static_cast<const AccTableEntry*>(ws);
+  switch (nrb) {
+    case 1: hipLaunchKernelGGL(acc_bf16_table_kernel<1>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
+    case 2: hipLaunchKernelGGL(acc_bf16_table_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
+    case 4: hipLaunchKernelGGL(acc_bf16_table_kernel<4>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
+    case 8: hipLaunchKernelGGL(acc_bf16_table_kernel<8>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

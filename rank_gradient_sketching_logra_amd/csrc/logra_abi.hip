@@ -1,7 +1,9 @@
 // C ABI entry points: host-side validation, then launches on the caller's
 // stream.  Nothing is launched when validation fails.  See include/logra.h
 // for the contract of every call.
+#include <algorithm>
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -332,6 +334,52 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
   }
   return hip_status(logra::launch_accumulate(T, r, true, items, n, true, static_cast<hipStream_t>(stream)),
                     "sketch_accumulate_grouped_packed launch");
+}
+
+LOGRA_API size_t logra_sketch_accumulate_table_ws_bytes(int n) {
+  if (n < 1) return 0;
+  return logra::acc_table_ws_bytes(n);
+}
+
+LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_acc_packed_desc* descs,
+                                            int n, void* ws, size_t ws_bytes, logra_stream stream) {
+  if (!descs || !ws) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer");
+  if (n < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need n >= 1");
+  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t tneed = logra::acc_table_ws_bytes(n);
+  if (ws_bytes < tneed) return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_table: workspace of %zu bytes needed", tneed);
+  if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_table: workspace not 16-byte aligned");
+  const size_t need = logra::acc_ws_bytes_per_item(T, 1, r);
+  const Range rws = range(ws, tneed);
+  std::vector<logra::AccItem> items((size_t)n);
+  std::vector<Range> rs((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const logra_acc_packed_desc& e = descs[i];
+    if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer in descriptor %d", i);
+    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: d must be >= 1");
+    int st = check_matrix("sketch_accumulate_table D", e.D, LOGRA_BF16, e.ldd, e.d);
+    if (st) return st;
+    if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_table: planes and S must be 16-byte aligned");
+    rs[i] = range(e.S, (size_t)(e.d * r) * 4);
+    if (overlap(rs[i], range(e.D, extent(T, e.d, e.ldd, 2))) || overlap(rs[i], range(e.planes, need)) ||
+        overlap(rws, rs[i]) || overlap(rws, range(e.D, extent(T, e.d, e.ldd, 2))) || overlap(rws, range(e.planes, need)))
+      return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_table: S or the workspace overlaps an operand of descriptor %d", i);
+    items[i] = logra::AccItem{e.D, nullptr, e.S, e.d, e.ldd, const_cast<uint16_t*>(e.planes)};
+  }
+  // Every sketch against every other matrix's operands (sorted by address, so
+  // the pairwise check stays cheap for whole-model tables).
+  std::vector<int> order((size_t)n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::sort(order.begin(), order.end(), [&](int a, int b) { return rs[a].lo < rs[b].lo; });
+  for (int i = 1; i < n; ++i)
+    if (overlap(rs[order[i - 1]], rs[order[i]])) return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_table: two sketches overlap");
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j)
+      if (i != j && (overlap(rs[i], range(descs[j].D, extent(T, descs[j].d, descs[j].ldd, 2))) ||
+                     overlap(rs[i], range(descs[j].planes, need))))
+        return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_table: sketch %d overlaps an operand of %d", i, j);
+  return hip_status(logra::launch_accumulate_table(T, r, items.data(), n, ws, static_cast<hipStream_t>(stream)),
+                    "sketch_accumulate_table launch");
 }
 
 LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {

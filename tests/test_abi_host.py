@@ -346,3 +346,20 @@ def test_merge_explicit_validation(lib):
     assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
     d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, A + 256, 0))
     assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS       # projection inside W
+
+
+def test_accumulate_table_validation(lib):
+    assert B.sketch_accumulate_table_ws_bytes(196) >= 197 * 48 and B.sketch_accumulate_table_ws_bytes(0) == 0
+    f = lib.logra_sketch_accumulate_table
+    ws = B.sketch_accumulate_table_ws_bytes(2)
+    W = 0x20000000
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64))
+    assert err(f, 128, 64, d2, 2, W, ws, None) == B.ERR_ALIAS            # sketches overlap
+    assert err(f, 128, 64, d2, 0, W, ws, None) == B.ERR_SHAPE
+    assert err(f, 128, 64, d2, 2, W, ws - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 128, 64, d2, 2, None, ws, None) == B.ERR_NULL
+    assert err(f, 128, 300, d2, 1, W, ws, None) == B.ERR_SHAPE
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(C + 1024, Bp, Dp, 64, 64))
+    assert err(f, 128, 64, d2, 2, W, ws, None) == B.ERR_ALIAS            # sketch 0 inside D of 1
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64))
+    assert err(f, 128, 64, d1, 1, C + 64, ws, None) == B.ERR_ALIAS       # workspace inside S

@@ -169,6 +169,40 @@ def test_accumulate_grouped_is_bit_identical_to_single_calls(T, r):
         assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
 
 
+@pytest.mark.parametrize("T,r", [(1000, 64), (4096, 33), (520, 256), (777, 100)])
+def test_accumulate_table_equals_grouped_calls(T, r):
+    """One persistent launch over a table of many matrices (three 'layers' of mixed widths,
+    including a ragged edge tile) gives the bits of the per-layer grouped packed launches, and
+    matches the oracle."""
+    shapes = [(640, 0), (256, 1), (1000, 2), (2048, 3), (512, 4), (300, 5), (768, 6), (256, 7), (1536, 8)]
+    say(f"accumulate table T={T} r={r}")
+    planes = []
+    for g in range(3):
+        xb = synth.normal((T, 64), 1.0, (33, T, g, 0, 9), "bf16")
+        planes.append(B.project_input_packed(B.key(2, g, 1), bf16_dev(xb), r))
+    items_t, items_g, host = [], [], []
+    for d, i in shapes:
+        ld = (d + 7) // 8 * 8
+        db, Dm = bf16_inputs((T, ld), 1e-3, (33, T, d, i, 1))
+        D = bf16_dev(db)[:, :d]
+        S0 = synth.fp32_matrix((d, r), 0.1, (33, d, r, i, 5))
+        P = planes[i // 3]
+        items_t.append((D, P, torch.from_numpy(S0.copy()).to(DEV)))
+        items_g.append((D, P, torch.from_numpy(S0.copy()).to(DEV)))
+        host.append((Dm[:, :d], S0))
+    B.sketch_accumulate_table(items_t, r)
+    for g in range(3):
+        B.sketch_accumulate_grouped_packed(items_g[3 * g:3 * g + 3], r)
+    for (_, _, St), (_, _, Sg) in zip(items_t, items_g):
+        assert torch.equal(St.view(torch.int32), Sg.view(torch.int32))
+    # the oracle, through the projection the packed planes hold
+    for g in range(3):
+        X = oracle.bf16_bits_to_f64(synth.normal((T, 64), 1.0, (33, T, g, 0, 9), "bf16"))
+        XAt = oracle.project(X, oracle.regen_A(2, g, 1, r, 64))
+        for (_, _, St), (Dm, S0) in list(zip(items_t, host))[3 * g:3 * g + 3]:
+            assert relfro(St.cpu().numpy(), S0 + Dm.T @ XAt) <= 5e-5
+
+
 @pytest.mark.parametrize("T,r", [(1000, 64), (4096, 33), (48, 256)])
 def test_packed_projection_feeds_accumulate(T, r):
     """project_input_packed + accumulate_grouped_packed: the same XAt bits as project_input,
