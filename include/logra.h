@@ -302,17 +302,22 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
                                                      logra_stream stream);
 
 /* Workspace bytes of logra_sketch_accumulate_table for n matrices (the
- * matrix table the kernel reads). */
+ * matrix table the kernel reads and eight tile counters). */
 LOGRA_API size_t logra_sketch_accumulate_table_ws_bytes(int n);
 
 /* logra_sketch_accumulate_grouped_packed over any number of matrices in one
  * persistent launch (e.g. all projections of all layers for one
- * microbatch): one block per compute unit takes the matrices' 256-column
- * tiles in turn, so the compute units one layer's tiles leave idle and the
- * ramp of separate launches are shared by the whole table.  Each tile is
- * computed whole by one block in the documented summation order, so S has the
- * same bits as with grouped or single calls.  The descriptor array is read on
- * the host during the call and copied into the workspace on the stream.
+ * microbatch).  The matrices' 256-column tiles, in descriptor order, are cut
+ * into eight contiguous ranges, one per XCD; the blocks resident on an XCD
+ * take its range's tiles in turn from a counter in the workspace, so the
+ * tiles of one matrix run close together on one XCD and share its L2 copy of
+ * the packed input, and the compute units one layer's tiles leave idle and
+ * the ramp of separate launches are shared by the whole table.  Each tile is
+ * computed whole by one block in the documented summation order, so S has
+ * the same bits as with grouped or single calls.  The descriptor array is
+ * read on the host during the call and copied, with the zeroed counters,
+ * into the workspace on the stream; calls that share a workspace must not
+ * overlap in time.
  * Errors: as logra_sketch_accumulate_grouped_packed for each descriptor;
  * n < 1; workspace too small or misaligned; two sketches overlapping, or a
  * sketch or the workspace overlapping another descriptor's operands. */

@@ -912,19 +912,41 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
 }
 
 // Persistent form over a device-resident table of many matrices (e.g. every
-// projection of every layer for one microbatch): the grid is one block per
-// compute unit and block b takes tiles b, b + G, b + 2G, ... of the table's
-// tile list (matrix by matrix, column block by column block), so the compute
-// units left idle by one layer's tiles and the ramp of separate launches are
-// shared across the whole table.  Each tile is still computed whole by one
-// block, so the results are bit-identical to the per-layer launches.
+// projection of every layer for one microbatch): the grid is a whole number
+// of blocks per XCD, at most one block per compute unit.  The table's tile
+// list (matrix by matrix, column block by column block) is cut into eight
+// contiguous ranges, one per XCD (blocks are dispatched round-robin over the
+// XCDs), and the blocks of an XCD take its range's tiles in order from a
+// counter of their own.  The column tiles of one matrix so run close together
+// in time on one XCD and read its packed input from that XCD's L2, and the
+// compute units left idle by one layer's tiles and the ramp of separate
+// launches are shared across the whole table.  Each tile is still computed
+// whole by one block, so the results are bit-identical to the per-layer
+// launches; which block runs a tile changes nothing.
 template <int RB>
 __global__ __launch_bounds__(512, 1) void acc_bf16_table_kernel(const AccTableEntry* __restrict__ tab,
-                                                                int n, int64_t T, int64_t r,
-                                                                int nsteps, int nrb) {
+                                                                unsigned* __restrict__ next, int n,
+                                                                int64_t T, int64_t r, int nsteps,
+                                                                int nrb) {
   __shared__ __align__(16) u32x4 smem[AccShape<RB>::kSmemKiB * 64];
+  __shared__ unsigned claimed[2];
   const int64_t total = tab[n].tile_begin;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  const int xcd = (int)(blockIdx.x & 7);
+  const int64_t per = gridDim.x >> 3;  // blocks per XCD
+  const int64_t begin = total * xcd / 8, end = total * (xcd + 1) / 8;
+  int64_t t = begin + (blockIdx.x >> 3);
+  for (int it = 0; t < end; ++it) {
+    // Claim the block's following tile now; the index is needed only when
+    // this tile is done, so the atomic's latency is hidden behind it.
+    // The address is made opaque per lane (lane_o is 0 here): with a uniform
+    // address the compiler turns the atomic into a wave-wide form whose
+    // result is broadcast, and waits for it, right away.
+    unsigned c = 0;
+    if (threadIdx.x == 0) {
+      int lane_o = (int)threadIdx.x;
+      asm volatile("" : "+v"(lane_o));
+      c = atomicAdd(next + xcd + lane_o, 1u);
+    }
     int lo = 0, hi = n - 1;  // the entry holding tile t: tile_begin[lo] <= t < tile_begin[lo + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -934,7 +956,11 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_table_kernel(const AccTableEn
     const AccTile tile{static_cast<const uint16_t*>(e.D), e.planes, e.S, e.d, e.ldd,
                        t - e.tile_begin, T, r, nsteps, nrb};
     acc_tile<RB>(tile, smem);
-    __syncthreads();  // every wave is done with the LDS before the next tile's loads land
+    // Slot it & 1 is written again two tiles on, after a barrier every
+    // thread reaches only once it has read the slot here.
+    if (threadIdx.x == 0) claimed[it & 1] = c;
+    __syncthreads();  // also: every wave is done with the LDS before the next tile's loads land
+    t = begin + per + (int64_t)claimed[it & 1];
   }
 }
 
@@ -1101,12 +1127,16 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
   return hipGetLastError();
 }
 
-size_t acc_table_ws_bytes(int n) { return round256((size_t)(n + 1) * sizeof(AccTableEntry)); }
+// Workspace: the n + 1 table entries, then one more entry's room holding the
+// eight per-XCD tile counters.
+static_assert(sizeof(AccTableEntry) >= 8 * sizeof(unsigned), "counters fit one entry");
+size_t acc_table_ws_bytes(int n) { return round256((size_t)(n + 2) * sizeof(AccTableEntry)); }
 
 hipError_t launch_accumulate_table(int64_t T, int64_t r, const AccItem* items, int n, void* ws,
                                    hipStream_t s) {
   if (n < 1) return hipErrorInvalidValue;
-  std::vector<AccTableEntry> tab((size_t)n + 1);
+  // The table and the zeroed counters (entry n + 1) go over in one copy.
+  std::vector<AccTableEntry> tab((size_t)n + 2, AccTableEntry{nullptr, nullptr, nullptr, 0, 0, 0});
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     tab[i] = AccTableEntry{items[i].D, static_cast<const uint16_t*>(items[i].ws), items[i].S,
@@ -1121,14 +1151,18 @@ hipError_t launch_accumulate_table(int64_t T, int64_t r, const AccItem* items, i
   if (e != hipSuccess) return e;
   const int nrb = (int)(acc_rank_pad(r) / 32);
   const int nsteps = (int)(acc_token_pad(T) / kAccStep);
-  const int64_t cus = compute_units();
-  const dim3 grid((unsigned)(tiles < cus ? tiles : cus));
+  // Blocks per XCD: enough for every tile of the largest range, at most the
+  // XCD's share of the compute units.
+  const int64_t cus_per_xcd = compute_units() / 8 > 0 ? compute_units() / 8 : 1;
+  const int64_t range = (tiles + 7) / 8;
+  const dim3 grid((unsigned)(8 * (range < cus_per_xcd ? range : cus_per_xcd)));
   const AccTableEntry* t = static_cast<const AccTableEntry*>(ws);
+  unsigned* next = reinterpret_cast<unsigned*>(static_cast<AccTableEntry*>(ws) + n + 1);
   switch (nrb) {
-    case 1: hipLaunchKernelGGL(acc_bf16_table_kernel<1>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
-    case 2: hipLaunchKernelGGL(acc_bf16_table_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
-    case 4: hipLaunchKernelGGL(acc_bf16_table_kernel<4>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
-    case 8: hipLaunchKernelGGL(acc_bf16_table_kernel<8>, grid, dim3(kAccWaves * 64), 0, s, t, n, T, r, nsteps, nrb); break;
+    case 1: hipLaunchKernelGGL(acc_bf16_table_kernel<1>, grid, dim3(kAccWaves * 64), 0, s, t, next, n, T, r, nsteps, nrb); break;
+    case 2: hipLaunchKernelGGL(acc_bf16_table_kernel<2>, grid, dim3(kAccWaves * 64), 0, s, t, next, n, T, r, nsteps, nrb); break;
+    case 4: hipLaunchKernelGGL(acc_bf16_table_kernel<4>, grid, dim3(kAccWaves * 64), 0, s, t, next, n, T, r, nsteps, nrb); break;
+    case 8: hipLaunchKernelGGL(acc_bf16_table_kernel<8>, grid, dim3(kAccWaves * 64), 0, s, t, next, n, T, r, nsteps, nrb); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -349,7 +349,7 @@ def test_merge_explicit_validation(lib):
 
 
 def test_accumulate_table_validation(lib):
-    assert B.sketch_accumulate_table_ws_bytes(196) >= 197 * 48 and B.sketch_accumulate_table_ws_bytes(0) == 0
+    assert B.sketch_accumulate_table_ws_bytes(196) >= 198 * 48 and B.sketch_accumulate_table_ws_bytes(0) == 0
     f = lib.logra_sketch_accumulate_table
     ws = B.sketch_accumulate_table_ws_bytes(2)
     W = 0x20000000

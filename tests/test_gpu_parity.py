@@ -203,6 +203,38 @@ def test_accumulate_table_equals_grouped_calls(T, r):
             assert relfro(St.cpu().numpy(), S0 + Dm.T @ XAt) <= 5e-5
 
 
+@pytest.mark.parametrize("T,r", [(48, 64), (200, 256)])
+def test_accumulate_table_many_tiles_per_block(T, r):
+    """A table of more tiles than the grid has blocks, so every block claims several tiles in
+    turn from its XCD's range: twice in a row on one workspace (the counters start again from
+    zero), the same bits as one grouped launch per matrix, and the oracle on two matrices."""
+    widths = [4096 + 256 * (i % 5) - 37 * (i % 3) for i in range(24)]  # 16..20 tiles each
+    say(f"accumulate table, many tiles T={T} r={r} tiles={sum((d + 255) // 256 for d in widths)}")
+    xb = synth.normal((T, 64), 1.0, (34, T, r, 0, 9), "bf16")
+    P = B.project_input_packed(B.key(2, 5, 1), bf16_dev(xb), r)
+    items_t, items_g, host = [], [], []
+    for i, d in enumerate(widths):
+        ld = (d + 7) // 8 * 8
+        db, Dm = bf16_inputs((T, ld), 1e-3, (34, T, d, i, 1))
+        D = bf16_dev(db)[:, :d]
+        S0 = synth.fp32_matrix((d, r), 0.1, (34, d, r, i, 5))
+        items_t.append((D, P, torch.from_numpy(S0.copy()).to(DEV)))
+        items_g.append((D, P, torch.from_numpy(S0.copy()).to(DEV)))
+        host.append((Dm[:, :d], S0))
+    ws = B.workspace(B.sketch_accumulate_table_ws_bytes(len(widths)), DEV)
+    for _ in range(2):
+        B.sketch_accumulate_table(items_t, r, ws=ws)
+        for it in items_g:
+            B.sketch_accumulate_grouped_packed([it], r)
+    for (_, _, St), (_, _, Sg) in zip(items_t, items_g):
+        assert torch.equal(St.view(torch.int32), Sg.view(torch.int32))
+    X = oracle.bf16_bits_to_f64(xb)
+    XAt = oracle.project(X, oracle.regen_A(2, 5, 1, r, 64))
+    for i in (0, len(widths) - 1):
+        Dm, S0 = host[i]
+        assert relfro(items_t[i][2].cpu().numpy(), S0 + 2.0 * (Dm.T @ XAt)) <= 5e-5
+
+
 @pytest.mark.parametrize("T,r", [(1000, 64), (4096, 33), (48, 256)])
 def test_packed_projection_feeds_accumulate(T, r):
     """project_input_packed + accumulate_grouped_packed: the same XAt bits as project_input,
