@@ -2,7 +2,8 @@
 
 One step = one update over the whole layer set of the workload:
   A. project every selected matrix's input, every microbatch, straight into
-     the packed operand form the accumulate reads (XAt = X A^T)
+     the packed operand form the accumulate reads (XAt = X A^T; one
+     persistent launch per microbatch over every matrix of every layer)
   B. accumulate every sketch, every microbatch (one persistent launch per
      microbatch over every matrix of every layer)
   C. RowAdam for every sketch (writing the update straight in the merge's
@@ -232,6 +233,7 @@ def main():
     maxd = max(d for (_, _, _, d, _) in mats)
     ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
     acc_ws = B.workspace(B.sketch_accumulate_table_ws_bytes(len(mats)), dev)
+    proj_ws = B.workspace(B.project_input_table_ws_bytes(len(mats)), dev)
     # the rest of the model's weights, resident but untouched (27B set: the projections are
     # 43.6 GB of the model's ~54 GB)
     ballast = torch.empty((BALLAST_BYTES.get(w.name, 0),), dtype=torch.uint8, device=dev)
@@ -260,10 +262,11 @@ def main():
             s.zero_()
         ev[0].record()
         for mb in range(M):                          # A: forward-side projections
-            for l in range(layers):
-                for (kind, d, k) in by_layer[l]:
-                    B.project_input_packed(keys[(l, kind)], X[(sid[(l, mb)], shared[kind])], r,
-                                           planes=PL[(sid[(l, mb)], kind)])
+            # one persistent launch per microbatch over every matrix of every layer
+            B.project_input_table([(keys[(l, kind)], X[(sid[(l, mb)], shared[kind])], None,
+                                    PL[(sid[(l, mb)], kind)])
+                                   for l in range(layers) for (kind, d, k) in by_layer[l]],
+                                  r, ws=proj_ws)
         ev[1].record()
         for mb in range(M):                          # B: backward-side sketch accumulation
             # one persistent launch per microbatch over every matrix of every layer

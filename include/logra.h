@@ -239,6 +239,44 @@ LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r,
                                       logra_stream stream);
 
 /* One matrix of a grouped accumulate. */
+/* One projection of logra_project_input_table. */
+typedef struct logra_project_desc {
+  logra_key key;     /* key of this projection's A                          */
+  const void* X;     /* [T x k] bf16, row-major, leading dimension ldx      */
+  int64_t k;
+  int64_t ldx;
+  float* XAt;        /* [T x r] fp32 contiguous, or NULL                    */
+  void* planes;      /* logra_packed_input_bytes(T, r) bytes, or NULL       */
+} logra_project_desc;
+
+#define LOGRA_MAX_PROJECT_TABLE 1024
+
+/* Workspace bytes of logra_project_input_table for n projections (the table
+ * the kernel reads and an item counter); 0 for n out of range. */
+LOGRA_API size_t logra_project_input_table_ws_bytes(int n);
+
+/* logra_project_input_packed for up to LOGRA_MAX_PROJECT_TABLE projections
+ * sharing T and r (e.g. every projection of every layer for one microbatch)
+ * in one persistent launch ([paper] Sec. 2.1; [rgc] "How it works").  Each
+ * descriptor gets XAt (fp32) and/or its packed planes.  The work items are
+ * (projection, 16-token step) in descriptor order; each wave of the grid
+ * computes one item whole (all k columns, all ranks) and takes the next
+ * unclaimed one from a counter in the workspace, so projections of any width
+ * mix without idle compute units.  Summation order: for each token and rank,
+ * the 256-column blocks in ascending order, each block's 32-column MFMA
+ * steps in order; deterministic, and equal to logra_project_input_packed's
+ * result up to the last bits (that call adds its column blocks in eight
+ * interleaved partial sums).  Several descriptors may share one X.  The
+ * descriptor array is read on the host during the call and copied, with the
+ * zeroed counter, into the workspace on the stream; calls that share a
+ * workspace must not overlap in time.
+ * Errors: NULL pointers or a descriptor without outputs; T < 1, k < 1, r out
+ * of range, ldx < k, n out of range; alignment (X rows, outputs 16 bytes);
+ * workspace too small; two outputs overlapping, or an output or the
+ * workspace overlapping any X. */
+LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_project_desc* descs,
+                                        int n, void* ws, size_t ws_bytes, logra_stream stream);
+
 typedef struct logra_acc_desc {
   const void* D;       /* [T x d], row-major, leading dimension ldd */
   const float* XAt;    /* [T x r] fp32 contiguous                    */

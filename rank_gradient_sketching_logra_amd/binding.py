@@ -31,6 +31,11 @@ class AccDesc(Structure):
     _fields_ = [("D", c_void_p), ("XAt", c_void_p), ("S", c_void_p), ("d", c_int64), ("ldd", c_int64)]
 
 
+class ProjectDesc(Structure):
+    _fields_ = [("key", Key), ("X", c_void_p), ("k", c_int64), ("ldx", c_int64), ("XAt", c_void_p),
+                ("planes", c_void_p)]
+
+
 class AccPackedDesc(Structure):
     _fields_ = [("D", c_void_p), ("planes", c_void_p), ("S", c_void_p), ("d", c_int64),
                 ("ldd", c_int64)]
@@ -96,6 +101,9 @@ SIGNATURES = {
     "logra_sketch_accumulate_table_ws_bytes": (c_size_t, [c_int]),
     "logra_sketch_accumulate_table": (c_int, [c_int64, c_int64, POINTER(AccPackedDesc), c_int, c_void_p,
                                               c_size_t, c_void_p]),
+    "logra_project_input_table_ws_bytes": (c_size_t, [c_int]),
+    "logra_project_input_table": (c_int, [c_int64, c_int64, POINTER(ProjectDesc), c_int, c_void_p, c_size_t,
+                                          c_void_p]),
     "logra_merge_projection_packed_bytes": (c_size_t, [c_int64, c_int64]),
     "logra_pack_merge_projection": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_merge_grouped_explicit": (c_int, [c_int64, POINTER(MergeExplicitDesc), c_int, c_double, c_void_p,
@@ -227,6 +235,27 @@ def project_input_packed(k_: Key, X: torch.Tensor, r: int, planes=None, out=None
     _check(lib().logra_project_input_packed(ctypes.byref(k_), T, k, r, _ptr(X), _dtype_code(X), _ld(X),
                                             _ptr(out), _ptr(planes), planes.numel(), _stream(X, stream)))
     return planes
+
+
+def project_input_table_ws_bytes(n: int) -> int:
+    return lib().logra_project_input_table_ws_bytes(n)
+
+
+def project_input_table(items, r: int, ws=None, stream=None):
+    """items: sequence of (key, X bf16 [T x k], XAt fp32 [T x r] or None, planes or None) sharing
+    T and r; one persistent launch writes every given output."""
+    n = len(items)
+    T = items[0][1].shape[0]
+    descs = (ProjectDesc * n)()
+    for i, (k_, X, XAt, P) in enumerate(items):
+        if X.shape[0] != T:
+            raise ValueError("every X must have the same number of tokens")
+        descs[i] = ProjectDesc(k_, X.data_ptr(), X.shape[1], _ld(X),
+                               None if XAt is None else XAt.data_ptr(),
+                               None if P is None else P.data_ptr())
+    if ws is None:
+        ws = workspace(project_input_table_ws_bytes(n), items[0][1].device)
+    _check(lib().logra_project_input_table(T, r, descs, n, _ptr(ws), ws.numel(), _stream(items[0][1], stream)))
 
 
 def sketch_accumulate_grouped_packed(items, r: int, stream=None):

@@ -55,6 +55,21 @@ hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* ite
 size_t acc_table_ws_bytes(int n);
 hipError_t launch_accumulate_table(int64_t T, int64_t r, const AccItem* items, int n, void* ws,
                                    hipStream_t s);
+// Table-driven bf16 projection: any number (<= proj_table_max()) of
+// projections sharing T and r in one persistent launch; the table
+// (proj_table_ws_bytes(n) of device workspace) is copied in from the host on
+// the stream.  Each item writes XAt and/or planes (either may be null).
+struct ProjItem {
+  const void* X;   // [T x k] bf16
+  int64_t ldx, k;
+  KeyArg key;
+  float* XAt;
+  uint16_t* planes;
+};
+int proj_table_max();
+size_t proj_table_ws_bytes(int n);
+hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int n, void* ws,
+                                hipStream_t s);
 // Compute units of the current device.
 int64_t compute_units();
 

@@ -29,13 +29,70 @@ __device__ __forceinline__ uint64_t pick_word(const Philox4& p, int i) {
   return (i & 2) ? b : a;
 }
 
-// Eight bf16 values +-1 from the low 8 bits of b (bit i set -> element i is -1).
-__device__ __forceinline__ u32x4 expand_signs(uint32_t b) {
+// Eight bf16 values +-1 for the projection's paired column order: dword p
+// takes its low element's sign from bit 15 - p of w and its high element's
+// from bit 31 - p (bit set -> -1).  Two VALU operations per dword.
+// (x & m) | c in one v_and_or_b32: the compiler splits it in two when m and
+// c are literals, which that encoding cannot carry, so they are passed in
+// registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(m), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ u32x4 expand_sign_pairs(uint32_t w) {
+  const uint32_t m = 0x80008000u, one = 0x3F803F80u;
   u32x4 v;
-  v[0] = 0x3F803F80u | ((b << 15) & 0x8000u) | ((b << 30) & 0x80000000u);
-  v[1] = 0x3F803F80u | ((b << 13) & 0x8000u) | ((b << 28) & 0x80000000u);
-  v[2] = 0x3F803F80u | ((b << 11) & 0x8000u) | ((b << 26) & 0x80000000u);
-  v[3] = 0x3F803F80u | ((b << 9) & 0x8000u) | ((b << 24) & 0x80000000u);
+  v[0] = and_or(w, m, one);
+  v[1] = and_or(w << 1, m, one);
+  v[2] = and_or(w << 2, m, one);
+  v[3] = and_or(w << 3, m, one);
+  return v;
+}
+
+// Four consecutive bf16 of row `row` from column `col` as two words; zero
+// outside [0, nrows) x [0, ncols).  col is a multiple of 4 and rows start
+// 16-byte aligned, so the whole run is one 8-byte load.
+__device__ __forceinline__ void load_bf16x4(const uint16_t* __restrict__ base, int64_t ld,
+                                            int64_t row, int64_t col, int64_t nrows,
+                                            int64_t ncols, uint32_t& w0, uint32_t& w1) {
+  w0 = 0u;
+  w1 = 0u;
+  if (row >= nrows || col >= ncols) return;
+  const uint16_t* p = base + row * ld + col;
+  if (col + 4 <= ncols) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w0 = v.x;
+    w1 = v.y;
+    return;
+  }
+  uint32_t e[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = (col + i < ncols) ? p[i] : 0u;
+  w0 = e[0] | (e[1] << 16);
+  w1 = e[2] | (e[3] << 16);
+}
+
+// X operand of one projection MFMA in the paired column order: for lane
+// group g = lane >> 4 and the 32 columns from c32, element 2p holds column
+// c32 + 15 - 4g - p and element 2p + 1 column c32 + 31 - 4g - p.  Their
+// signs are bits 15 - 4g - p and 31 - 4g - p of the columns' 32-bit Philox
+// half-word w, which expand_sign_pairs(w << 4g) places in the same elements.
+// Any order of the 32 columns within one MFMA gives the same sum over them
+// up to rounding; this one makes the sign expansion two operations per pair.
+__device__ __forceinline__ u32x4 load_x_paired(const uint16_t* __restrict__ base, int64_t ld,
+                                               int64_t row, int64_t c32, int g, int64_t nrows,
+                                               int64_t ncols) {
+  uint32_t l0, l1, h0, h1;
+  const int64_t c = c32 + 12 - 4 * g;  // runs c .. c+3 and c+16 .. c+19
+  load_bf16x4(base, ld, row, c, nrows, ncols, l0, l1);
+  load_bf16x4(base, ld, row, c + 16, nrows, ncols, h0, h1);
+  u32x4 v;
+  v[0] = __builtin_amdgcn_perm(h1, l1, 0x07060302u);  // columns c+3, c+19
+  v[1] = __builtin_amdgcn_perm(h1, l1, 0x05040100u);  // c+2, c+18
+  v[2] = __builtin_amdgcn_perm(h0, l0, 0x07060302u);  // c+1, c+17
+  v[3] = __builtin_amdgcn_perm(h0, l0, 0x05040100u);  // c, c+16
   return v;
 }
 
@@ -148,14 +205,17 @@ __global__ __launch_bounds__(256) void pack_projection_kernel(int64_t r, int64_t
 // all ranks.  Its eight waves take the 256-column blocks of k round-robin,
 // each with the loads of its next block in flight while it computes the
 // current one, then add their partial tiles in a fixed order.  The product is
-// v_mfma_f32_16x16x32_bf16: A lane l holds token t0 + (l & 15), columns
-// 32s + 8(l >> 4) .. +7 of the 256-column block (s = 0..7); B lane l holds
-// the signs of rank 16nb + (l & 15) for the same columns, expanded from the
-// Philox words of the lane that generated that rank; C lane l holds rank
+// v_mfma_f32_16x16x32_bf16: A lane l holds token t0 + (l & 15) and eight of
+// the columns 32s .. 32s + 31 of the 256-column block (s = 0..7) in the
+// paired order of load_x_paired (the explicit-projection path: columns
+// 32s + 8(l >> 4) .. +7); B lane l holds the signs of rank 16nb + (l & 15)
+// for the same columns, expanded from the Philox words of the lane that
+// generated that rank; C lane l holds rank
 // 16nb + (l & 15) of tokens t0 + 4(l >> 4) + j in register j.  NB16 =
 // 16-rank blocks computed (>= r / 16).
 constexpr int kProjTokens = 16;
 constexpr int kProjWaves = 8;
+constexpr int kProjTableMax = 1024;  // projections in one table launch
 
 // EXPLICIT: the B operands come from an explicit projection packed as bf16
 // hi/lo operands (see pack_projection_kernel) instead of sign bits: two MFMAs
@@ -183,7 +243,9 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
   u32x4 a[8];
   auto load = [&](int64_t b, u32x4 (&dst)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = load_bf16x8(X, ldx, trow, b * 256 + 32 * s + 8 * g4, T, k);
+    for (int s = 0; s < 8; ++s)
+      dst[s] = EXPLICIT ? load_bf16x8(X, ldx, trow, b * 256 + 32 * s + 8 * g4, T, k)
+                        : load_x_paired(X, ldx, trow, b * 256 + 32 * s, g4, T, k);
   };
   if (wave < nblk) load(wave, a);
   for (int64_t b = wave; b < nblk; b += kProjWaves) {
@@ -222,10 +284,8 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
         for (int nb = 0; nb < NB16; ++nb) {
           const int src = 16 * (nb & 3) + (lane & 15);
           const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
-          const uint32_t byte = (wv >> (8 * g4)) & 0xFFu;
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]),
-                                                            as_bf16x8(expand_signs(byte)), acc[nb],
-                                                            0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(a[s]), as_bf16x8(expand_sign_pairs(wv << (4 * g4))), acc[nb], 0, 0, 0);
         }
       }
     }
@@ -283,6 +343,168 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
       *reinterpret_cast<u32x4*>(dst) = vh;
       *reinterpret_cast<u32x4*>(dst + 512) = vl;
     }
+  }
+}
+
+}  // namespace
+
+// One projection of a table-driven projection (device memory); entry n holds
+// only item_begin = the total number of 16-token items.
+struct ProjTableEntry {
+  const uint16_t* X;   // bf16 [T x k], leading dimension ldx
+  float* XAt;          // fp32 [T x r] or null
+  uint16_t* planes;    // packed projected input or null
+  uint64_t k0, k1;     // key words of this projection's A
+  int64_t ldx, k, item_begin;
+};
+
+namespace {
+
+constexpr int kPtWaves = 4;  // waves per block of the table projection
+
+// Persistent projection over a device-resident table of projections (e.g.
+// every projection of every layer for one microbatch).  The work items are
+// (projection, 16-token step) in table order; each wave takes one item at a
+// time and computes it whole -- all k columns, all ranks -- so no two waves
+// share a result and nothing is exchanged between waves.  Wave w of block b
+// starts at item 4b + w and then takes the next unclaimed item from a
+// counter, so items are handed out in order and the fast waves take more.
+// Per item: for each 256-column block in order, the next block's X loads in
+// flight, the signs of the lane's rank (one Philox block per 64 ranks)
+// expanded in the paired column order, eight 16x16x32 MFMA steps; the sums
+// run over the column blocks in ascending order in one accumulator.  The
+// tile then goes through the wave's own LDS rows to the fp32 output and/or
+// the accumulate's packed operand form, as in project_bf16_kernel.  The
+// column blocks' partial sums are added in another order than in
+// project_bf16_kernel, so the two differ in the last bits; each is
+// deterministic.
+template <int NB16>
+__global__ __launch_bounds__(kPtWaves * 64)
+__attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void project_table_kernel(
+    const ProjTableEntry* __restrict__ tab, unsigned* __restrict__ next, int n, int64_t T,
+    int64_t r, float cr, int nrb) {
+  constexpr int NQ = (NB16 + 3) / 4;
+  constexpr int RP = NB16 * 16;
+  __shared__ int64_t begin_s[kProjTableMax + 1];
+  __shared__ float red[kPtWaves][kProjTokens][RP + 1];
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) begin_s[i] = tab[i].item_begin;
+  __syncthreads();  // the only block-wide barrier: waves run independently below
+  const int64_t total = begin_s[n];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t grid_waves = (int64_t)gridDim.x * kPtWaves;
+  int64_t item = (int64_t)blockIdx.x * kPtWaves + wave;
+  while (item < total) {
+    // The lane index is opaque per item, so that lane-derived addresses are
+    // not hoisted out of the item loop and held in registers throughout.
+    int lane_o = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
+    const int g4 = lane >> 4;
+    float (*rw)[RP + 1] = red[wave];
+    // Claim the wave's following item now; the value is needed only when
+    // this one is done.  The address is opaque per lane so that the atomic is
+    // not turned into a wave-wide form that waits for its result at once.
+    unsigned claim = 0;
+    if (lane == 0) {
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      claim = atomicAdd(next + lane_o, 1u);
+    }
+    int lo = 0, hi = n - 1;  // the entry holding the item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (begin_s[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const ProjTableEntry& e = tab[lo];
+    const uint16_t* __restrict__ X = e.X;
+    const int64_t ldx = e.ldx, k = e.k;
+    const KeyWords kw{e.k0, e.k1};
+    const int64_t st = item - begin_s[lo];
+    const int64_t t0 = st * kProjTokens;
+    const int64_t trow = t0 + (lane & 15);
+
+    f32x4 acc[NB16];
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t nblk = (k + 255) >> 8;
+    auto load = [&](int64_t b, u32x4 (&dst)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) dst[s] = load_x_paired(X, ldx, trow, b * 256 + 32 * s, g4, T, k);
+    };
+    u32x4 a[8];
+    load(0, a);
+    for (int64_t b = 0; b < nblk; ++b) {
+      u32x4 an[8];
+      if (b + 1 < nblk) load(b + 1, an);
+      uint32_t bits[NQ][8];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int64_t j = lane + 64 * q;
+        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
+        const bool live = j < r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
+          bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int nb = 0; nb < NB16; ++nb) {
+          const int src = 16 * (nb & 3) + (lane & 15);
+          const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(a[s]), as_bf16x8(expand_sign_pairs(wv << (4 * g4))), acc[nb], 0, 0, 0);
+        }
+      }
+      if (b + 1 < nblk) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) a[s] = an[s];
+      }
+    }
+
+    // The wave's tile through its own LDS rows (a wave's LDS accesses take
+    // effect in program order, so no barrier is needed).
+#pragma unroll
+    for (int nb = 0; nb < NB16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[nb][j];
+    asm volatile("" ::: "memory");
+    if (e.XAt) {
+      float* __restrict__ XAt = e.XAt;
+      for (int idx = lane; idx < kProjTokens * r; idx += 64) {
+        const int m = idx / (int)r;
+        const int j = idx - m * (int)r;
+        const int64_t t = t0 + m;
+        if (t < T) XAt[t * r + j] = rw[m][j] * cr;
+      }
+    }
+    if (e.planes) {
+      for (int b = 0; b < nrb; ++b) {
+        const int j = 32 * b + (lane & 31);
+        float hv[8], lv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float v = j < r ? rw[8 * (lane >> 5) + i][j] * cr : 0.f;
+          hv[i] = (float)(__bf16)v;
+          lv[i] = v - hv[i];
+        }
+        u32x4 vh, vl;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          vh[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p + 1]) << 16);
+          vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
+        }
+        uint16_t* dst = e.planes + (st * nrb + b) * 1024 + lane * 8;
+        *reinterpret_cast<u32x4*>(dst) = vh;
+        *reinterpret_cast<u32x4*>(dst + 512) = vl;
+      }
+    }
+    asm volatile("" ::: "memory");  // this item's LDS reads before the next item's writes
+    item = grid_waves + (int64_t)__builtin_amdgcn_readfirstlane(claim);
   }
 }
 
@@ -1070,6 +1292,61 @@ hipError_t launch_project(KeyArg key, int64_t T, int64_t k, int64_t r, const voi
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+int proj_table_max() { return kProjTableMax; }
+
+// Workspace: the n + 1 table entries, then one more entry's room holding the
+// item counter.
+size_t proj_table_ws_bytes(int n) { return round256((size_t)(n + 2) * sizeof(ProjTableEntry)); }
+
+template <int NB>
+static hipError_t launch_project_table_nb(const ProjTableEntry* t, unsigned* next, int n,
+                                          int64_t T, int64_t r, float cr, int nrb,
+                                          hipStream_t s) {
+  static int per_cu = 0;  // resident blocks per compute unit, from the occupancy query
+  if (per_cu == 0) {
+    int b = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, project_table_kernel<NB>,
+                                                                kPtWaves * 64, 0);
+    if (e != hipSuccess) return e;
+    per_cu = b > 0 ? b : 1;
+  }
+  const dim3 grid((unsigned)(per_cu * compute_units()));
+  hipLaunchKernelGGL(project_table_kernel<NB>, grid, dim3(kPtWaves * 64), 0, s, t, next, n, T,
+                     r, cr, nrb);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int n, void* ws,
+                                hipStream_t s) {
+  if (n < 1 || n > kProjTableMax) return hipErrorInvalidValue;
+  std::vector<ProjTableEntry> tab((size_t)n + 2,
+                                  ProjTableEntry{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0});
+  const int64_t per = (T + kProjTokens - 1) / kProjTokens;  // items per projection
+  for (int i = 0; i < n; ++i)
+    tab[i] = ProjTableEntry{static_cast<const uint16_t*>(items[i].X), items[i].XAt,
+                            items[i].planes, items[i].key.k0, items[i].key.k1, items[i].ldx,
+                            items[i].k, per * i};
+  tab[n].item_begin = per * n;
+  // From pageable memory the copy is staged before the call returns.
+  hipError_t e = hipMemcpyAsync(ws, tab.data(), tab.size() * sizeof(ProjTableEntry),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  const ProjTableEntry* t = static_cast<const ProjTableEntry*>(ws);
+  unsigned* next = reinterpret_cast<unsigned*>(static_cast<ProjTableEntry*>(ws) + n + 1);
+  const float cr = (float)(1.0 / std::sqrt((double)r));
+  const int nrb = (int)(acc_rank_pad(r) / 32);
+  switch (proj_nb16(r)) {
+    case 1: return launch_project_table_nb<1>(t, next, n, T, r, cr, nrb, s);
+    case 2: return launch_project_table_nb<2>(t, next, n, T, r, cr, nrb, s);
+    case 4: return launch_project_table_nb<4>(t, next, n, T, r, cr, nrb, s);
+    case 6: return launch_project_table_nb<6>(t, next, n, T, r, cr, nrb, s);
+    case 8: return launch_project_table_nb<8>(t, next, n, T, r, cr, nrb, s);
+    case 12: return launch_project_table_nb<12>(t, next, n, T, r, cr, nrb, s);
+    case 16: return launch_project_table_nb<16>(t, next, n, T, r, cr, nrb, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_accumulate(int64_t T, int64_t r, bool bf16, const AccItem* items, int n,

@@ -242,6 +242,53 @@ LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_
                     "project_input_packed launch");
 }
 
+LOGRA_API size_t logra_project_input_table_ws_bytes(int n) {
+  if (n < 1 || n > LOGRA_MAX_PROJECT_TABLE) return 0;
+  return logra::proj_table_ws_bytes(n);
+}
+
+LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_project_desc* descs,
+                                        int n, void* ws, size_t ws_bytes, logra_stream stream) {
+  static_assert(LOGRA_MAX_PROJECT_TABLE <= 1024, "the kernel's table limit");
+  if (!descs || !ws) return fail(LOGRA_ERR_NULL, "project_input_table: NULL pointer");
+  if (n < 1 || n > LOGRA_MAX_PROJECT_TABLE) return fail(LOGRA_ERR_SHAPE, "project_input_table: need 1 <= n <= %d", LOGRA_MAX_PROJECT_TABLE);
+  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  const size_t tneed = logra::proj_table_ws_bytes(n);
+  if (ws_bytes < tneed) return fail(LOGRA_ERR_WORKSPACE, "project_input_table: workspace of %zu bytes needed", tneed);
+  if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "project_input_table: workspace not 16-byte aligned");
+  const size_t pneed = logra::acc_ws_bytes_per_item(T, 1, r);
+  const size_t xat_bytes = (size_t)(T * r) * 4;
+  std::vector<logra::ProjItem> items((size_t)n);
+  std::vector<Range> xs((size_t)n), outs;
+  outs.reserve(2 * (size_t)n + 1);
+  outs.push_back(range(ws, tneed));
+  for (int i = 0; i < n; ++i) {
+    const logra_project_desc& e = descs[i];
+    if (!e.X) return fail(LOGRA_ERR_NULL, "project_input_table: NULL X in descriptor %d", i);
+    if (!e.XAt && !e.planes) return fail(LOGRA_ERR_NULL, "project_input_table: descriptor %d has no output", i);
+    if (e.k < 1) return fail(LOGRA_ERR_SHAPE, "project_input_table: k must be >= 1");
+    int st = check_matrix("project_input_table X", e.X, LOGRA_BF16, e.ldx, e.k);
+    if (st) return st;
+    if ((e.XAt && !aligned16(e.XAt)) || (e.planes && !aligned16(e.planes)))
+      return fail(LOGRA_ERR_ALIGN, "project_input_table: outputs must be 16-byte aligned");
+    xs[i] = range(e.X, extent(T, e.k, e.ldx, 2));
+    if (e.XAt) outs.push_back(range(e.XAt, xat_bytes));
+    if (e.planes) outs.push_back(range(e.planes, pneed));
+    items[i] = logra::ProjItem{e.X, e.ldx, e.k, key_words(e.key.seed, &e.key), e.XAt,
+                               static_cast<uint16_t*>(e.planes)};
+  }
+  // Outputs (and the workspace) against each other, sorted by address, then
+  // against every input; inputs may be shared.
+  std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (overlap(outs[i - 1], outs[i])) return fail(LOGRA_ERR_ALIAS, "project_input_table: two outputs (or an output and the workspace) overlap");
+  for (const Range& o : outs)
+    for (int j = 0; j < n; ++j)
+      if (overlap(o, xs[j])) return fail(LOGRA_ERR_ALIAS, "project_input_table: an output or the workspace overlaps the X of descriptor %d", j);
+  return hip_status(logra::launch_project_table(T, r, items.data(), n, ws, static_cast<hipStream_t>(stream)),
+                    "project_input_table launch");
+}
+
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r) {
   if (T < 1 || d < 1 || bad_rank(r)) return 0;
   return logra::acc_ws_bytes_per_item(T, d, r);

@@ -363,3 +363,37 @@ def test_accumulate_table_validation(lib):
     assert err(f, 128, 64, d2, 2, W, ws, None) == B.ERR_ALIAS            # sketch 0 inside D of 1
     d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64))
     assert err(f, 128, 64, d1, 1, C + 64, ws, None) == B.ERR_ALIAS       # workspace inside S
+
+
+def test_project_table_validation(lib):
+    """Host-side checks of the table projection; nothing is launched."""
+    assert B.project_input_table_ws_bytes(196) >= 198 * 64
+    assert B.project_input_table_ws_bytes(0) == 0 and B.project_input_table_ws_bytes(1025) == 0
+    f = lib.logra_project_input_table
+    ws = B.project_input_table_ws_bytes(2)
+    W = 0x20000000
+    k0 = B.key(1, 2, 3)
+    P = B.packed_input_bytes(64, 64)
+
+    def descs(*rows):
+        return (B.ProjectDesc * len(rows))(*[B.ProjectDesc(k0, *row) for row in rows])
+
+    good = descs((A, 256, 256, None, C), (A, 256, 256, None, C + P))       # one X shared
+    assert err(f, 64, 64, good, 2, W, ws - 1, None) == B.ERR_WORKSPACE
+    assert err(f, 64, 64, good, 0, W, ws, None) == B.ERR_SHAPE
+    assert err(f, 64, 64, good, 1025, W, ws, None) == B.ERR_SHAPE
+    assert err(f, 64, 300, good, 2, W, ws, None) == B.ERR_SHAPE
+    assert err(f, 64, 64, good, 2, None, ws, None) == B.ERR_NULL
+    assert err(f, 64, 64, descs((A, 256, 256, None, None)), 1, W, ws, None) == B.ERR_NULL  # no output
+    assert err(f, 64, 64, descs((0, 256, 256, None, C)), 1, W, ws, None) == B.ERR_NULL
+    assert err(f, 64, 64, descs((A, 256, 200, None, C)), 1, W, ws, None) == B.ERR_SHAPE    # ldx < k
+    assert err(f, 64, 64, descs((A, 256, 256, None, C + 8)), 1, W, ws, None) == B.ERR_ALIGN
+    assert err(f, 64, 64, descs((A + 8, 256, 256, None, C)), 1, W, ws, None) == B.ERR_ALIGN
+    overl = descs((A, 256, 256, None, C), (A, 256, 256, None, C + P - 256))
+    assert err(f, 64, 64, overl, 2, W, ws, None) == B.ERR_ALIAS                # planes overlap
+    xat = descs((A, 256, 256, C, C + 64 * 64 * 4 - 16))
+    assert err(f, 64, 64, xat, 1, W, ws, None) == B.ERR_ALIAS                  # XAt meets planes
+    into_x = descs((A, 256, 256, None, C), (C + 2 * P, 256, 256, None, A + 4096))
+    assert err(f, 64, 64, into_x, 2, W, ws, None) == B.ERR_ALIAS               # planes inside X of 0
+    assert err(f, 64, 64, good, 2, A + 1024, ws, None) == B.ERR_ALIAS          # workspace inside X
+    assert err(f, 64, 64, good, 2, C + 16, ws, None) == B.ERR_ALIAS            # workspace meets planes

@@ -77,7 +77,8 @@ def test_regen_A_bit_exact(r, k):
 
 
 @pytest.mark.parametrize("T,k,r,ldx", [(64, 256, 64, 256), (1000, 712, 33, 720), (96, 3584, 256, 3584),
-                                       (37, 40, 1, 48), (512, 1536, 64, 1536)])
+                                       (37, 40, 1, 48), (512, 1536, 64, 1536), (50, 1001, 64, 1008),
+                                       (20, 259, 96, 264)])
 def test_project_bf16(T, k, r, ldx):
     say(f"project bf16 T={T} k={k} r={r} ldx={ldx}")
     bits, X = bf16_inputs((T, ldx), 1.0, (9, T, k, r, 0))
@@ -264,6 +265,82 @@ def test_packed_projection_feeds_accumulate(T, r):
     for (_, _, Sp), (_, _, Su), want in zip(items_p, items_u, wants):
         assert torch.equal(Sp.view(torch.int32), Su.view(torch.int32))
         assert relfro(Sp.cpu().numpy(), want) <= 5e-5
+
+
+@pytest.mark.parametrize("T,r", [(1000, 64), (48, 256), (200, 33)])
+def test_project_table(T, r):
+    """One table launch over projections of mixed widths (ragged k, padded rows, one X shared by
+    two projections, entries with only XAt or only planes): XAt within 1e-5 of the oracle and
+    within fp32 rounding of the single-call projection; the planes give the S bits of the
+    table's own XAt through the unpacked accumulate, and S within tolerance of the oracle; a
+    second call on the same workspace gives the same bits."""
+    widths = [(256, 256), (712, 720), (1001, 1008), (3584, 3584), (40, 48)]
+    say(f"project table T={T} r={r}")
+    xs = []
+    for i, (k, ld) in enumerate(widths):
+        xb, X = bf16_inputs((T, ld), 1.0, (35, T, k, i, 0))
+        xs.append((bf16_dev(xb)[:, :k], X[:, :k]))
+    # (input, matrix id, XAt wanted, planes wanted); input 0 is shared by two projections
+    spec = [(0, 1, True, True), (1, 2, True, True), (2, 3, True, False), (3, 4, True, True),
+            (4, 5, True, True), (0, 6, False, True)]
+    nb = B.packed_input_bytes(T, r)
+
+    def outputs():
+        return [(torch.full((T, r), float("nan"), device=DEV) if want_x else None,
+                 torch.zeros((nb,), dtype=torch.uint8, device=DEV) if want_p else None)
+                for (_, _, want_x, want_p) in spec]
+
+    ws = B.workspace(B.project_input_table_ws_bytes(len(spec)), DEV)
+    runs = []
+    for _ in range(2):
+        outs = outputs()
+        B.project_input_table([(B.key(8, mid, 2), xs[xi][0], xo, po)
+                               for (xi, mid, _, _), (xo, po) in zip(spec, outs)], r, ws=ws)
+        runs.append(outs)
+    for (xa, pa), (xb_, pb) in zip(*runs):
+        if xa is not None:
+            assert torch.equal(xa.view(torch.int32), xb_.view(torch.int32))
+        if pa is not None:
+            assert torch.equal(pa, pb)
+    d = 300
+    db, Dm = bf16_inputs((T, 304), 1e-3, (35, T, d, 0, 1))
+    D = bf16_dev(db)[:, :d]
+    S0 = synth.fp32_matrix((d, r), 0.1, (35, d, r, 0, 5))
+    for (xi, mid, _, _), (xo, po) in zip(spec, runs[0]):
+        Xd, X = xs[xi]
+        A = oracle.regen_A(8, mid, 2, r, X.shape[1])
+        if xo is not None:
+            assert relfro(xo.cpu().numpy(), oracle.project(X, A)) <= 1e-5
+            assert relfro(xo.cpu().numpy(), B.project_input(B.key(8, mid, 2), Xd, r).cpu().numpy()) <= 1e-6
+        if po is not None:
+            Sp = torch.from_numpy(S0.copy()).to(DEV)
+            B.sketch_accumulate_grouped_packed([(D, po, Sp)], r)
+            assert relfro(Sp.cpu().numpy(), S0 + oracle.dense_gradient(Dm[:, :d], X) @ A.T) <= 5e-5
+            if xo is not None:
+                Su = torch.from_numpy(S0.copy()).to(DEV)
+                B.sketch_accumulate_grouped([(D, xo, Su)])
+                assert torch.equal(Sp.view(torch.int32), Su.view(torch.int32))
+
+
+def test_project_table_many_items_per_wave():
+    """More 16-token items than the grid has waves, so every wave claims several in turn:
+    every XAt within fp32 rounding of the single-call projection, two against the oracle."""
+    T, r = 4096, 64
+    ks = [256, 512, 300] * 8
+    say(f"project table, many items: {len(ks) * T // 16} items")
+    xs = []
+    for i, k in enumerate(ks):
+        ld = (k + 7) // 8 * 8
+        xb, X = bf16_inputs((T, ld), 1.0, (36, T, k, i, 0))
+        xs.append((bf16_dev(xb)[:, :k], X[:, :k]))
+    outs = [torch.full((T, r), float("nan"), device=DEV) for _ in ks]
+    B.project_input_table([(B.key(9, i, 1), xs[i][0], outs[i], None) for i in range(len(ks))], r)
+    for i in range(len(ks)):
+        single = B.project_input(B.key(9, i, 1), xs[i][0], r)
+        assert relfro(outs[i].cpu().numpy(), single.cpu().numpy()) <= 1e-6
+    for i in (0, len(ks) - 1):
+        want = oracle.project(xs[i][1], oracle.regen_A(9, i, 1, r, ks[i]))
+        assert relfro(outs[i].cpu().numpy(), want) <= 1e-5
 
 
 def test_accumulate_deterministic_and_zero_d_is_noop():
