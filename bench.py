@@ -213,17 +213,18 @@ def main():
     shared = {"q": "att", "k": "att", "v": "att", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
     xw = {"att": w.shapes["q"][1], "o": w.shapes["o"][1], "mlp": w.shapes["gate"][1], "down": w.shapes["down"][1]}
     pbytes = B.packed_input_bytes(T, r)
-    # One input set (X, D and packed planes of every matrix) per (layer, microbatch).  When
-    # the distinct sets would not fit beside the weights, the step rotates through a pool of
-    # sets, consecutive launches on consecutive sets, the pool far larger than the 256 MB
-    # Infinity Cache.
-    set_bytes = T * 2 * (sum(xw.values()) + sum(d for (_, d) in w.shapes.values())) + len(w.shapes) * pbytes
+    # One input set (X and D of every matrix) per (layer, microbatch).  When the distinct
+    # sets would not fit beside the weights, the step rotates through a pool of sets,
+    # consecutive launches on consecutive sets, the pool far larger than the 256 MB Infinity
+    # Cache.  The packed projected inputs are outputs of the projection phase and inputs of
+    # the accumulate phase, so every (layer, microbatch, matrix) has its own.
+    set_bytes = T * 2 * (sum(xw.values()) + sum(d for (_, d) in w.shapes.values()))
     nsets = layers * M if layers * M * set_bytes <= POOL_LIMIT_BYTES else POOL_SETS
     sid = {(l, mb): (mb * layers + l) % nsets for l in range(layers) for mb in range(M)}
     X = {(i, s): randn((T, xw[s]), 1.0) for i in range(nsets) for s in xw}
     D = {(i, kind): randn((T, d), 1e-3) for i in range(nsets) for kind, (d, k) in w.shapes.items()}
-    PL = {(i, kind): torch.empty((pbytes,), dtype=torch.uint8, device=dev)
-          for i in range(nsets) for kind in w.shapes}
+    PL = {(l, mb, kind): torch.empty((pbytes,), dtype=torch.uint8, device=dev)
+          for l in range(layers) for mb in range(M) for kind in w.shapes}
     W = {(l, kind): randn((d, k), 0.02) for (l, kind, mid, d, k) in mats}
     S = {(l, kind): torch.zeros((d, r), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     UP = {(l, kind): torch.empty((B.packed_update_bytes(d, r),), dtype=torch.uint8, device=dev)
@@ -264,13 +265,13 @@ def main():
         for mb in range(M):                          # A: forward-side projections
             # one persistent launch per microbatch over every matrix of every layer
             B.project_input_table([(keys[(l, kind)], X[(sid[(l, mb)], shared[kind])], None,
-                                    PL[(sid[(l, mb)], kind)])
+                                    PL[(l, mb, kind)])
                                    for l in range(layers) for (kind, d, k) in by_layer[l]],
                                   r, ws=proj_ws)
         ev[1].record()
         for mb in range(M):                          # B: backward-side sketch accumulation
             # one persistent launch per microbatch over every matrix of every layer
-            B.sketch_accumulate_table([(D[(sid[(l, mb)], kind)], PL[(sid[(l, mb)], kind)], S[(l, kind)])
+            B.sketch_accumulate_table([(D[(sid[(l, mb)], kind)], PL[(l, mb, kind)], S[(l, kind)])
                                        for l in reversed(range(layers)) for (kind, d, k) in by_layer[l]],
                                       r, ws=acc_ws)
         ev[2].record()
