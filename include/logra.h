@@ -44,14 +44,16 @@
  *
  * Generator (this library's choice -- the pages fix only that A is
  * regenerated from a seed and metadata, [paper] §2.2 "Memory and
- * synchronization"): Philox4x64-10 (Salmon et al., SC'11).
+ * synchronization"): the Philox family (Salmon et al., SC'11).
  *   key of a projection      = (seed, (step << 32) | matrix_id)
  *   sign of A[j, l]          = bit (l & 63) of word ((l & 255) >> 6) of
- *                              Philox(counter = (j, l >> 8, 0, 0)); 1 -> -1
+ *                              Philox4x64-10(counter = (j, l >> 8, 0, 0)); 1 -> -1
  *   stochastic-rounding draw = for element e = (row0 + i) * k + l of W, the
- *                              16 bits [16*(e & 3), +16) of word ((e & 15) >> 2)
- *                              of Philox(counter = (e >> 4, 0, 1, 0)) under key
- *                              (sr_seed, (step << 32) | matrix_id)
+ *                              16 bits [16*(e & 1), +16) of word ((e & 7) >> 1)
+ *                              of Philox4x32-10 with 32-bit counter words
+ *                              (g & 0xFFFFFFFF, g >> 32, matrix_id, step),
+ *                              g = e >> 3, under the 32-bit key words
+ *                              (sr_seed & 0xFFFFFFFF, sr_seed >> 32)
  */
 #ifndef LOGRA_H_
 #define LOGRA_H_

@@ -1,19 +1,21 @@
-"""Philox4x64-10 counter-based generator, written from its published definition.
+"""Philox4x64-10 and Philox4x32-10 counter-based generators, written from their
+published definition.
 
 TEST INFRASTRUCTURE ONLY: part of the CPU oracle.  Only tests, the smoke check
 and the benchmark's CPU-baseline leg may import this package.
 
-Source of the generator: J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
+Source of the generators: J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
 "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11 -- the Philox family,
-instance N=4 words of W=64 bits, R=10 rounds.  One round maps the counter
-(x0, x1, x2, x3) under the round key (k0, k1) to
+instances N=4 words of W=64 bits and of W=32 bits, R=10 rounds.  One round
+maps the counter (x0, x1, x2, x3) under the round key (k0, k1) to
 
     (hi(M1*x2) ^ x1 ^ k0,  lo(M1*x2),  hi(M0*x0) ^ x3 ^ k1,  lo(M0*x0))
 
-where hi/lo are the upper/lower 64 bits of the 128-bit product; between
-rounds the key advances by the Weyl constants (golden ratio and sqrt(3)-1 in
-64-bit fixed point).  The result is pinned bit-for-bit against numpy's
-independent ``numpy.random.Philox`` (also 4x64-10) in the tests.
+where hi/lo are the upper/lower W bits of the 2W-bit product; between rounds
+the key advances by the Weyl constants (golden ratio and sqrt(3)-1 in W-bit
+fixed point).  The 4x64 instance is pinned bit-for-bit against numpy's
+independent ``numpy.random.Philox`` in the tests, the 4x32 instance against
+the known-answer vectors published with the generators.
 
 The pages fix only that the projection is regenerated "from its seed and
 metadata" (LoGRA paper text, paperpeel.com, §2.2 "Memory and
@@ -21,17 +23,20 @@ synchronization").  Which generator and which bits is this library's choice;
 the layout is stated here and in ``include/logra.h``:
 
 * key of a projection: ``(seed, (step << 32) | matrix_id)``;
-* sign bits of A: one block per (row j, 256-column group b = l >> 8) with
-  counter ``(j, b, 0, 0)``; column l uses bit ``l & 63`` of output word
-  ``(l & 255) >> 6``; bit 1 means sigma = -1, bit 0 means sigma = +1;
-* Gaussian entries (the Gaussian projection variant): one block per (row j,
-  4-column group c = l >> 2) with counter ``(j, c, 2, 0)``; column l takes
-  Box-Muller pair ``(l & 3) >> 1`` of the four words, cosine for even l,
-  sine for odd l (see ``gaussian_normals``);
-* stochastic-rounding draws: key ``(sr_seed, (step << 32) | matrix_id)``;
-  element e = (row0 + i) * k + l (logical index) uses counter
-  ``(e >> 4, 0, 1, 0)`` and the 16 bits ``[16*(e & 3), +16)`` of output word
-  ``(e & 15) >> 2``.
+* sign bits of A (Philox4x64-10): one block per (row j, 256-column group
+  b = l >> 8) with counter ``(j, b, 0, 0)``; column l uses bit ``l & 63`` of
+  output word ``(l & 255) >> 6``; bit 1 means sigma = -1, bit 0 means +1;
+* Gaussian entries (the Gaussian projection variant, Philox4x64-10): one
+  block per (row j, 4-column group c = l >> 2) with counter ``(j, c, 2, 0)``;
+  column l takes Box-Muller pair ``(l & 3) >> 1`` of the four words, cosine
+  for even l, sine for odd l (see ``gaussian_normals``);
+* stochastic-rounding draws (Philox4x32-10, a quarter of the 4x64 instance's
+  multiplies per draw): element e = (row0 + i) * k + l (logical index) of
+  the matrix with projection key ``(sr_seed, (step << 32) | matrix_id)``
+  uses the block with 32-bit counter words
+  ``(g & 0xFFFFFFFF, g >> 32, matrix_id, step)``, g = e >> 3, under the
+  32-bit key words ``(sr_seed & 0xFFFFFFFF, sr_seed >> 32)``, and takes the
+  16 bits ``[16*(e & 1), +16)`` of output word ``(e & 7) >> 1``.
 """
 from __future__ import annotations
 
@@ -88,6 +93,35 @@ def philox4x64_10(ctr, key):
     return np.stack([x0, x1, x2, x3], axis=-1)
 
 
+# Multipliers and Weyl increments of Philox4x32 (Salmon et al., SC'11).
+PHILOX32_M0 = np.uint64(0xD2511F53)
+PHILOX32_M1 = np.uint64(0xCD9E8D57)
+PHILOX32_W0 = np.uint64(0x9E3779B9)
+PHILOX32_W1 = np.uint64(0xBB67AE85)
+
+
+def philox4x32_10(ctr, key):
+    """Apply Philox4x32-10 to 32-bit counter words ``ctr`` (shape [..., 4]) under the
+    32-bit key words ``key`` = (k0, k1).  Words are carried in uint64 arrays (the
+    32x32-bit products fit exactly); returns uint64 words below 2**32."""
+    x = np.array(ctr, dtype=np.uint64, copy=True)
+    if x.shape[-1] != 4:
+        raise ValueError("counter must have 4 words")
+    if np.any(x > MASK32):
+        raise ValueError("counter words must fit 32 bits")
+    k0 = np.asarray(key[0], dtype=np.uint64) & MASK32
+    k1 = np.asarray(key[1], dtype=np.uint64) & MASK32
+    x0, x1, x2, x3 = x[..., 0], x[..., 1], x[..., 2], x[..., 3]
+    for rnd in range(ROUNDS):
+        if rnd:
+            k0 = (k0 + PHILOX32_W0) & MASK32
+            k1 = (k1 + PHILOX32_W1) & MASK32
+        p0 = x0 * PHILOX32_M0
+        p1 = x2 * PHILOX32_M1
+        x0, x1, x2, x3 = (p1 >> SHIFT32) ^ x1 ^ k0, p1 & MASK32, (p0 >> SHIFT32) ^ x3 ^ k1, p0 & MASK32
+    return np.stack([x0, x1, x2, x3], axis=-1)
+
+
 def projection_key(seed: int, matrix_id: int, step: int):
     """Key words of one projection matrix A: (seed, step<<32 | matrix_id)."""
     if not (0 <= matrix_id < 2**32 and 0 <= step < 2**32 and 0 <= seed < 2**64):
@@ -112,19 +146,23 @@ def sign_bits(seed: int, matrix_id: int, step: int, r: int, k: int) -> np.ndarra
 
 def sr_draws(sr_seed: int, matrix_id: int, step: int, d: int, k: int,
              row0: int = 0) -> np.ndarray:
-    """16-bit stochastic-rounding draws u as uint32 array [d, k]."""
-    key = projection_key(sr_seed, matrix_id, step)
+    """16-bit stochastic-rounding draws u as uint32 array [d, k] (Philox4x32-10)."""
+    if not (0 <= matrix_id < 2**32 and 0 <= step < 2**32 and 0 <= sr_seed < 2**64):
+        raise ValueError("sr_seed must fit 64 bits, matrix_id and step 32 bits")
     e = ((np.arange(d, dtype=np.uint64)[:, None] + np.uint64(row0)) * np.uint64(k)
          + np.arange(k, dtype=np.uint64)[None, :])
-    blocks, inv = np.unique(e >> np.uint64(4), return_inverse=True)
+    blocks, inv = np.unique(e >> np.uint64(3), return_inverse=True)
     ctr = np.zeros((blocks.size, 4), dtype=np.uint64)
-    ctr[:, 0] = blocks
-    ctr[:, 2] = 1
-    words = philox4x64_10(ctr, key)                     # [nblocks, 4]
+    ctr[:, 0] = blocks & MASK32
+    ctr[:, 1] = blocks >> SHIFT32
+    ctr[:, 2] = matrix_id
+    ctr[:, 3] = step
+    key = (np.uint64(sr_seed) & MASK32, np.uint64(sr_seed) >> SHIFT32)
+    words = philox4x32_10(ctr, key)                     # [nblocks, 4]
     inv = inv.reshape(e.shape)
-    lane = (e & np.uint64(15)).astype(np.int64)
-    w = words[inv, lane >> 2]
-    return ((w >> (np.uint64(16) * (e & np.uint64(3)))) & np.uint64(0xFFFF)).astype(np.uint32)
+    lane = (e & np.uint64(7)).astype(np.int64)
+    w = words[inv, lane >> 1]
+    return ((w >> (np.uint64(16) * (e & np.uint64(1)))) & np.uint64(0xFFFF)).astype(np.uint32)
 
 
 def gaussian_normals(seed: int, matrix_id: int, step: int, r: int, k: int) -> np.ndarray:

@@ -1,8 +1,10 @@
 // Device-side building blocks shared by the LoGRA kernels (gfx950 / CDNA4).
 //
-// - Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
-//   Easy as 1, 2, 3", SC'11): the counter-based generator that regenerates
-//   the Rademacher projection and the stochastic-rounding draws.
+// - Philox4x64-10 and Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+//   Random Numbers: As Easy as 1, 2, 3", SC'11): the counter-based generators
+//   that regenerate the Rademacher projection (4x64) and the
+//   stochastic-rounding draws (4x32: two 32x32-bit products per round instead
+//   of two 64x64-bit ones, about a quarter of the multiplies per draw).
 // - bf16 rounding: nearest-even and deterministic stochastic rounding of an
 //   fp32 value.  Stochastic rounding moves to the far bf16 neighbour with
 //   probability equal to the fraction of the gap ("Randomized Gradient
@@ -82,10 +84,50 @@ __device__ __forceinline__ void gaussian_block(KeyWords key, uint64_t j, uint64_
   z[3] = rho1 * sin(two_pi * u[3]);
 }
 
-// 16 stochastic-rounding draws for flat elements [16*g, 16*g + 16): draw of
-// element e is bits [16*(e & 3), +16) of word (e & 15) >> 2.
-__device__ __forceinline__ Philox4 sr_block(KeyWords key, uint64_t g) {
-  return philox4x64_10(g, 0, 1, 0, key.k0, key.k1);
+// Multipliers and Weyl key increments of Philox4x32 (SC'11).
+constexpr uint32_t kPhilox32M0 = 0xD2511F53u;
+constexpr uint32_t kPhilox32M1 = 0xCD9E8D57u;
+constexpr uint32_t kPhilox32W0 = 0x9E3779B9u;
+constexpr uint32_t kPhilox32W1 = 0xBB67AE85u;
+
+struct Philox4x32 {
+  uint32_t w[4];
+};
+
+// Ten rounds of the same structure on 32-bit words: each 32x32-bit product
+// gives hi and lo in one multiply-add.
+__device__ __forceinline__ Philox4x32 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                    uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)c0 * kPhilox32M0;
+    const uint64_t p1 = (uint64_t)c2 * kPhilox32M1;
+    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c1 = (uint32_t)p1;
+    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c3 = (uint32_t)p0;
+    k0 += kPhilox32W0;
+    k1 += kPhilox32W1;
+  }
+  Philox4x32 out;
+  out.w[0] = c0;
+  out.w[1] = c1;
+  out.w[2] = c2;
+  out.w[3] = c3;
+  return out;
+}
+
+// 8 stochastic-rounding draws for flat elements [8*g, 8*g + 8) of the matrix
+// whose key is (sr_seed, step << 32 | matrix_id): the Philox4x32-10 block
+// with counter (g lo, g hi, matrix_id, step) under key (sr_seed lo, sr_seed
+// hi); the draw of element e is bits [16*(e & 1), +16) of word (e & 7) >> 1.
+__device__ __forceinline__ Philox4x32 sr_block(KeyWords key, uint64_t g) {
+  return philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), (uint32_t)key.k1,
+                       (uint32_t)(key.k1 >> 32), (uint32_t)key.k0, (uint32_t)(key.k0 >> 32));
+}
+
+__device__ __forceinline__ uint32_t sr_draw(const Philox4x32& p, uint64_t e) {
+  return (p.w[(e & 7) >> 1] >> (16 * (e & 1))) & 0xFFFFu;
 }
 
 // ------------------------------------------------------------- bf16 bits

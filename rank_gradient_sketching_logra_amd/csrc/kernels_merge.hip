@@ -22,23 +22,13 @@
 // runs over rank steps in ascending order, hi then lo, whatever the row or
 // block position, so a merge of a row block equals the same rows of a
 // whole-matrix merge; the sixteen stochastic-rounding draws of a lane's
-// elements come from one Philox block when k is a multiple of 16.
+// elements come from two Philox4x32 blocks when k is a multiple of 16.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace logra {
 
 namespace {
-
-__device__ __forceinline__ uint64_t pick_word_m(const Philox4& p, int i) {
-  const uint64_t a = (i & 1) ? p.w[1] : p.w[0];
-  const uint64_t b = (i & 1) ? p.w[3] : p.w[2];
-  return (i & 2) ? b : a;
-}
-
-__device__ __forceinline__ uint32_t sr_draw(const Philox4& p, uint64_t e) {
-  return (uint32_t)(pick_word_m(p, (int)((e & 15) >> 2)) >> (16 * (e & 3))) & 0xFFFFu;
-}
 
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
@@ -69,53 +59,54 @@ __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t
 // Sixteen updated bf16 of one lane: W values w (two words), products
 // acc[0..15] of consecutive columns, element index e0 of the first (for the
 // stochastic-rounding draws).  aligned: e0 is a multiple of 16, so the
-// sixteen draws are exactly one generator block, element t taking bits
-// [16 (t & 3), +16) of word t >> 2.
+// sixteen draws are exactly two generator blocks, element t taking bits
+// [16 (t & 1), +16) of word (t & 7) >> 1 of block t >> 3.
 template <bool STOCH>
 __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const f32x16& acc,
                                          float sc, KeyWords srk, uint64_t e0, bool aligned,
                                          u32x4& o0, u32x4& o1) {
   uint32_t out[8];
-  if (STOCH && aligned) {
-    const Philox4 p = sr_block(srk, e0 >> 4);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
-      const uint32_t wbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
-      const float x = __builtin_fmaf(-sc, acc[t], bf16_bits_to_f32(wbits));
-      const uint32_t u = (uint32_t)(p.w[t >> 2] >> (16 * (t & 3))) & 0xFFFFu;
-      const uint32_t o = f32_to_bf16_sr(x, u);
-      if (t & 1)
-        out[t >> 1] |= o << 16;
-      else
-        out[t >> 1] = o;
-    }
-    o0 = u32x4{out[0], out[1], out[2], out[3]};
-    o1 = u32x4{out[4], out[5], out[6], out[7]};
-    return;
-  }
-  Philox4 p0, p1;
-  if constexpr (STOCH) {
-    p0 = sr_block(srk, e0 >> 4);
-    p1 = (((e0 + 15) >> 4) != (e0 >> 4)) ? sr_block(srk, (e0 + 15) >> 4) : p0;
-  }
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  auto value = [&](int t) __attribute__((always_inline)) {
     const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
     const uint32_t wbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
-    const float x = __builtin_fmaf(-sc, acc[t], bf16_bits_to_f32(wbits));
-    uint32_t o;
-    if constexpr (STOCH) {
-      const uint64_t ee = e0 + t;
-      const uint32_t u = ((ee >> 4) == (e0 >> 4)) ? sr_draw(p0, ee) : sr_draw(p1, ee);
-      o = f32_to_bf16_sr(x, u);
-    } else {
-      o = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
-    }
+    return __builtin_fmaf(-sc, acc[t], bf16_bits_to_f32(wbits));
+  };
+  auto put = [&](int t, uint32_t o) __attribute__((always_inline)) {
     if (t & 1)
-      out[t >> 1] |= o << 16;
+      out[t >> 1] = (out[t >> 1] & 0xFFFFu) | (o << 16);
     else
-      out[t >> 1] = o;
+      out[t >> 1] = (out[t >> 1] & 0xFFFF0000u) | o;
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = 0u;
+  if constexpr (!STOCH) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) put(t, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)value(t)));
+  } else if (aligned) {
+    // One block per eight elements, generated and used in turn so that only
+    // one block's words are live at a time.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
+#pragma unroll
+      for (int t = 8 * h; t < 8 * h + 8; ++t)
+        put(t, f32_to_bf16_sr(value(t), (p.w[(t & 7) >> 1] >> (16 * (t & 1))) & 0xFFFFu));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // Elements e0 .. e0 + 15 lie in blocks g0, g0 + 1 and, when e0 is not a
+    // multiple of 8, g0 + 2; each block rounds the elements it covers.
+    const uint64_t g0 = e0 >> 3;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const Philox4x32 p = sr_block(srk, g0 + (uint64_t)b);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint64_t ee = e0 + (uint64_t)t;
+        if ((ee >> 3) - g0 == (uint64_t)b) put(t, f32_to_bf16_sr(value(t), sr_draw(p, ee)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   o0 = u32x4{out[0], out[1], out[2], out[3]};
   o1 = u32x4{out[4], out[5], out[6], out[7]};
@@ -244,8 +235,9 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   constexpr int CH = BC / 8;              // 16-byte chunks per tile row
   constexpr int WT = 32 * BC / 8;         // 16-byte chunks per W tile (32 rows)
   constexpr int UT = 32 * KS * 4;         // 16-byte chunks per U band (operand order)
-  constexpr int NR = (KS >= 16 && !PACKED) ? 2 : 3;  // bands in the LDS ring
   constexpr int SLOT = WT + UT;           // one band: W tile, then U (fp32 or packed)
+  // bands in the LDS ring: three when they fit in the 160 KiB, else two
+  constexpr int NR = (3 * SLOT + (PACKED ? 0 : UT)) * 16 <= 160 * 1024 ? 3 : 2;
   // LDS: a ring of NR bands, then (fp32 U) the band's U as bf16 hi/lo
   // operands (KS hi slabs, KS lo slabs).  The sign bits live in the ring
   // until the A operands are built.

@@ -267,6 +267,46 @@ def test_packed_projection_feeds_accumulate(T, r):
         assert relfro(Sp.cpu().numpy(), want) <= 5e-5
 
 
+@pytest.mark.parametrize("T,k,r", [(777, 64, 100), (48, 312, 256), (777, 312, 8), (1000, 64, 33)])
+def test_packed_planes_layout_against_oracle(T, k, r):
+    """The packed projected input decoded by its documented layout (per 16-token step and
+    32-rank block a hi operand then a lo operand; lane l holding tokens 8(l >> 5) + i of rank
+    32b + (l & 31)): hi + lo is the oracle's X A^T, and the padding (ranks past r, tokens past
+    T) is exactly zero.  Run twice, on a fresh output and on one filled with NaN, so no part
+    of the output may be left unwritten."""
+    say(f"packed planes layout T={T} k={k} r={r}")
+    xb, X = bf16_inputs((T, k), 1.0, (35, T, k, r, 0))
+    want = oracle.project(X, oracle.regen_A(4, 2, 1, r, k))
+    nrb = {1: 1, 2: 2}.get((r + 31) // 32, 4 if (r + 31) // 32 <= 4 else 8)
+    nsteps = (T + 15) // 16
+    pad = np.zeros((16 * nsteps, 32 * nrb))
+    pad[:T, :r] = want
+    full = np.zeros((nsteps, nrb, 64, 8))
+    for lane in range(64):
+        for i in range(8):
+            full[:, :, lane, i] = pad[8 * (lane >> 5) + i::16, :].reshape(nsteps, nrb, 32)[:, :, lane & 31]
+    for fill in (None, float("nan")):
+        planes = None
+        if fill is not None:
+            planes = torch.full((B.packed_input_bytes(T, r) // 2,), fill, dtype=torch.bfloat16, device=DEV).view(torch.uint8)
+        planes = B.project_input_packed(B.key(4, 2, 1), bf16_dev(xb), r, planes=planes)
+        u = planes.cpu().numpy().view(np.uint16)[: nsteps * nrb * 1024].reshape(nsteps, nrb, 2, 64, 8)
+        dec = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        got = dec[:, :, 0] + dec[:, :, 1]
+        assert np.isfinite(got).all()
+        live = np.zeros_like(full, dtype=bool)
+        live_pad = np.zeros_like(pad, dtype=bool)
+        live_pad[:T, :r] = True
+        for lane in range(64):
+            for i in range(8):
+                live[:, :, lane, i] = live_pad[8 * (lane >> 5) + i::16, :].reshape(nsteps, nrb, 32)[:, :, lane & 31]
+        assert np.all(dec[:, :, 0][~live] == 0) and np.all(dec[:, :, 1][~live] == 0)
+        assert relfro(got, full) <= 2e-5
+        # hi is the nearest bf16 of the sum: |lo| at most half an ulp of hi
+        hi = dec[:, :, 0]
+        assert np.all(np.abs(dec[:, :, 1]) <= np.abs(hi) * 2.0 ** -8 + 1e-30)
+
+
 @pytest.mark.parametrize("T,r", [(1000, 64), (48, 256), (200, 33)])
 def test_project_table(T, r):
     """One table launch over projections of mixed widths (ragged k, padded rows, one X shared by

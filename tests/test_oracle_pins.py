@@ -3,7 +3,8 @@
 Each test ties one oracle function to something other than itself: values
 printed on the pages (fixtures under tests/golden/, each with its citation),
 closed forms, invariants, brute force on tiny inputs, or an independent
-library routine (numpy's Philox, torch's fp32->bf16 conversion, BLAS ger).
+library routine (numpy's Philox, torch's fp32->bf16 conversion, BLAS ger), or
+published known-answer vectors (Philox4x32-10).
 """
 import json
 import math
@@ -73,18 +74,75 @@ def test_sign_bit_layout_against_numpy():
                 assert bits[j, l] == want
 
 
-def test_sr_draw_layout_against_numpy():
-    """SR draws: element e = (row0+i)*k + l takes bits [16*(e&3), +16) of word (e&15)>>2
-    of the block with counter (e >> 4, 0, 1, 0) under key (sr_seed, step<<32 | id)."""
-    sr_seed, mid, step, d, k, row0 = 9, 11, 2, 3, 37, 5
+# Known-answer vectors of Philox4x32-10 published with the generators (Salmon et al.,
+# SC'11, Random123 distribution): (counter words, key words) -> output words.
+PHILOX4X32_10_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX4X32_10_KAT)
+def test_philox4x32_matches_known_answers(ctr, key, want):
+    """Oracle Philox4x32-10 (the stochastic-rounding stream) == the published known answers."""
+    got = philox.philox4x32_10(np.array(ctr, dtype=np.uint64), key)
+    assert [int(x) for x in got] == list(want)
+    # batched: the same block anywhere in a batch
+    batch = np.array([ctr, (1, 2, 3, 4), ctr], dtype=np.uint64)
+    gb = philox.philox4x32_10(batch, key)
+    assert [int(x) for x in gb[0]] == list(want) and [int(x) for x in gb[2]] == list(want)
+
+
+def _scalar_philox4x32_10(ctr, key):
+    """Plain-integer Philox4x32-10, one block, from the round definition."""
+    m0, m1, w0, w1, mask = 0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE85, 0xFFFFFFFF
+    x, k0, k1 = list(ctr), key[0], key[1]
+    for rnd in range(10):
+        if rnd:
+            k0, k1 = (k0 + w0) & mask, (k1 + w1) & mask
+        p0, p1 = m0 * x[0], m1 * x[2]
+        x = [(p1 >> 32) ^ x[1] ^ k0, p1 & mask, (p0 >> 32) ^ x[3] ^ k1, p0 & mask]
+    return x
+
+
+def test_scalar_philox4x32_matches_known_answers():
+    for ctr, key, want in PHILOX4X32_10_KAT:
+        assert _scalar_philox4x32_10(ctr, key) == list(want)
+
+
+@pytest.mark.parametrize("sr_seed,mid,step,d,k,row0", [
+    (9, 11, 2, 3, 37, 5),
+    (2**40 + 3, 2**32 - 1, 7, 2, 21, 2**31),   # 64-bit seed, block index past 2**32
+])
+def test_sr_draw_layout(sr_seed, mid, step, d, k, row0):
+    """SR draws: element e = (row0+i)*k + l takes bits [16*(e&1), +16) of word (e&7)>>1
+    of the Philox4x32-10 block with counter (g lo, g hi, matrix_id, step), g = e >> 3,
+    under key (sr_seed lo, sr_seed hi)."""
     u = philox.sr_draws(sr_seed, mid, step, d, k, row0=row0)
-    key = (sr_seed, (step << 32) | mid)
+    key = (sr_seed & 0xFFFFFFFF, sr_seed >> 32)
     for i in range(d):
         for l in range(k):
             e = (row0 + i) * k + l
-            blk = _numpy_philox_block((e >> 4, 0, 1, 0), key)
-            want = (int(blk[(e & 15) >> 2]) >> (16 * (e & 3))) & 0xFFFF
+            g = e >> 3
+            blk = _scalar_philox4x32_10((g & 0xFFFFFFFF, g >> 32, mid, step), key)
+            want = (blk[(e & 7) >> 1] >> (16 * (e & 1))) & 0xFFFF
             assert u[i, l] == want
+
+
+def test_sr_draws_uniform_and_keyed():
+    """The 16-bit draws are uniform (mean and variance of U{0..65535}) and change with
+    the seed, the matrix id and the step."""
+    u = philox.sr_draws(1, 0, 0, 256, 1024).astype(np.float64)
+    n = u.size
+    assert abs(u.mean() - 32767.5) < 4 * 18918.6 / np.sqrt(n)
+    assert abs(u.var() / (65536.0**2 - 1) * 12 - 1) < 0.01
+    for other in (philox.sr_draws(2, 0, 0, 256, 1024), philox.sr_draws(1, 1, 0, 256, 1024),
+                  philox.sr_draws(1, 0, 1, 256, 1024)):
+        assert np.mean(other == u) < 1e-3
 
 
 def test_signs_are_balanced_and_independent_of_other_keys():
