@@ -168,6 +168,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight bf16 values +-1 (an MFMA operand of signs) in a paired order: dword
+// p takes its low element's sign from bit 15 - p of w and its high element's
+// from bit 31 - p (bit set -> -1).  Two VALU operations per dword.
+// (x & m) | c is one v_and_or_b32 only when m and c sit in registers (that
+// encoding carries no two literals), so the constants are passed through an
+// empty asm statement that makes them opaque.  The instruction itself is left
+// to the compiler: it then knows a VALU op writes the register and inserts the
+// wait states the matrix core needs before reading it as an operand (an
+// and_or written in inline assembly is invisible to that hazard check, and the
+// MFMA read a stale register).
+__device__ __forceinline__ u32x4 expand_sign_pairs(uint32_t w) {
+  uint32_t m = 0x80008000u, one = 0x3F803F80u;
+  asm("" : "+v"(m), "+v"(one));
+  u32x4 v;
+  v[0] = (w & m) | one;
+  v[1] = ((w << 1) & m) | one;
+  v[2] = ((w << 2) & m) | one;
+  v[3] = ((w << 3) & m) | one;
+  return v;
+}
+
 // Split an fp32 value into bf16 hi + bf16 lo with hi = RNE(x) and
 // lo = RNE(x - hi); hi + lo carries ~16 significant bits.
 __device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {

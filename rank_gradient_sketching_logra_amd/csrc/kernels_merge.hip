@@ -330,9 +330,15 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
     // A operands: instance e holds, for MFMA row m = l & 31, column
     // 32(E wave + e) + 16((m >> 2) & 1) + 4(m >> 3) + (m & 3) of the block and
     // ranks 16s + 8(l >> 5) + i, i = 0..7.  Ranks >= r read as +1; their U
-    // terms are zero.
-    u32x4 afrag[E][KS];
+    // terms are zero.  At 256 ranks the E KS operands would not fit in the
+    // register file beside the rest, so they are held as sign bits instead,
+    // four operands per word (operand q of a word: the signs of ranks 2p and
+    // 2p + 1 at bits 15 - 4q - p and 31 - 4q - p), and expanded at each use.
+    constexpr bool SBITS = !EXPLICIT && KS == 16;
+    constexpr int NAW = SBITS ? (E * KS + 3) / 4 : 1;
+    u32x4 afrag[E][SBITS ? 1 : KS];
     u32x4 alo[E][EXPLICIT ? KS : 1];
+    uint32_t awords[NAW];
     if constexpr (EXPLICIT) {
       const uint16_t* __restrict__ Ap = g.A[item];
 #pragma unroll
@@ -347,23 +353,47 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       const int m = lane & 31;
       const int cm = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
+      for (int w = 0; w < NAW; ++w) awords[w] = 0u;
+#pragma unroll
       for (int e = 0; e < E; ++e) {
         const int cl = 32 * (E * wave + e) + cm;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
+          // An opaque base per step, so that the step's eight reads are not
+          // hoisted with every other step's and held at once.
+          int base = (16 * s + 8 * hw) * NWd + (cl >> 5);
+          if constexpr (SBITS) asm volatile("" : "+v"(base));
           uint32_t byte = 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            byte |= ((sbits[(16 * s + 8 * hw + i) * NWd + (cl >> 5)] >> (cl & 31)) & 1u) << i;
-          afrag[e][s] = u32x4{
-              0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
-              0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
-              0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
-              0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+          for (int i = 0; i < 8; ++i) byte |= ((sbits[base + i * NWd] >> (cl & 31)) & 1u) << i;
+          if constexpr (SBITS) {
+            const int o = e * KS + s, q = o & 3;
+            uint32_t w = 0;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp)
+              w |= (((byte >> (2 * pp)) & 1u) << (15 - 4 * q - pp)) |
+                   (((byte >> (2 * pp + 1)) & 1u) << (31 - 4 * q - pp));
+            awords[o >> 2] |= w;
+          } else {
+            afrag[e][s] = u32x4{
+                0x3F803F80u | ((byte << 15) & 0x8000u) | ((byte << 30) & 0x80000000u),
+                0x3F803F80u | ((byte << 13) & 0x8000u) | ((byte << 28) & 0x80000000u),
+                0x3F803F80u | ((byte << 11) & 0x8000u) | ((byte << 26) & 0x80000000u),
+                0x3F803F80u | ((byte << 9) & 0x8000u) | ((byte << 24) & 0x80000000u)};
+          }
           if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
+    // The A operand of instance e, rank step s.
+    auto aop = [&](int e, int s) __attribute__((always_inline)) {
+      if constexpr (SBITS) {
+        const int o = e * KS + s;
+        return expand_sign_pairs(awords[o >> 2] << (4 * (o & 3)));
+      } else {
+        return afrag[e][s];
+      }
+    };
     __syncthreads();  // the sign bits are dead; the ring may be loaded
 
     float sc = scale_cr;
@@ -389,11 +419,11 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         bfrag(s, bh, bl);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bh),
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop(e, s)), as_bf16x8(bh),
                                                            acc[e], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(afrag[e][s]), as_bf16x8(bl),
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop(e, s)), as_bf16x8(bl),
                                                            acc[e], 0, 0, 0);
         if constexpr (EXPLICIT) {
 #pragma unroll
@@ -403,6 +433,41 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         }
         // With many rank steps, keep each step's operand loads next to their
         // use: hoisting them all would exceed the register file.
+        if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // C of one band from packed U slabs in LDS (slab 2s the hi term, 2s + 1
+    // the lo term of step s, 1 KiB apart): the slabs of G steps are read in
+    // one group and waited for once, so a band takes KS / G LDS round trips.
+    auto mfma_band_packed = [&](f32x16 (&acc)[E], const u32x4* ut) __attribute__((always_inline)) {
+      constexpr int G = KS < 4 ? KS : (KS == 16 && E == 2) ? 2 : 4;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
+#pragma unroll
+      for (int s0 = 0; s0 < KS; s0 += G) {
+        u32x4 x[2 * G];
+        lds_read_slabs<2 * G>(lds_u32(ut + (2 * s0) * 64 + lane), x);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const int s = s0 + i;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop(e, s)), as_bf16x8(x[2 * i]),
+                                                             acc[e], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop(e, s)),
+                                                             as_bf16x8(x[2 * i + 1]), acc[e], 0, 0, 0);
+          if constexpr (EXPLICIT) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(alo[e][s]),
+                                                               as_bf16x8(x[2 * i]), acc[e], 0, 0, 0);
+          }
+        }
         if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -602,13 +667,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         lds_read_at(wa, wx);
         f32x16 acc[E];
         if constexpr (PACKED) {
-          mfma_band(acc, [&](int s, u32x4& bh, u32x4& bl) __attribute__((always_inline)) {
-            u32x4 hl[1];
-            lds_read_slabs<1>(lds_u32(ut + (2 * s) * 64 + lane), hl);
-            bh = hl[0];
-            lds_read_slabs<1>(lds_u32(ut + (2 * s + 1) * 64 + lane), hl);
-            bl = hl[0];
-          });
+          mfma_band_packed(acc, ut);
         } else {
           mfma_band(acc, bfrag_lds);
         }
@@ -697,12 +756,13 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
   const double cr = 1.0 / std::sqrt((double)r);
   const int ks = merge_rank_steps(r);
-  const int e = ks <= 4 ? 2 : 1;
+  const bool explicit_a = items[0].A != nullptr;  // all or none (checked by the caller)
+  // 32-column instances per wave (must match the kernel instantiated below)
+  const int e = (ks <= 4 || (ks == 16 && !explicit_a)) ? 2 : 1;
   const int64_t bc = 32 * kMergeWaves * e;
   MergeGroupArgs g{};
   g.n = n;
   g.r = r;
-  const bool explicit_a = items[0].A != nullptr;  // all or none (checked by the caller)
   if (explicit_a && !packed) return hipErrorInvalidValue;
   g.scale_cr = (float)(explicit_a ? scale : scale * cr);
   g.scale_dev = scale_dev;
@@ -783,7 +843,15 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     case 2: LOGRA_MERGE_LAUNCH(2, 2) break;
     case 4: LOGRA_MERGE_LAUNCH(4, 2) break;
     case 8: LOGRA_MERGE_LAUNCH(8, 1) break;
-    case 16: LOGRA_MERGE_LAUNCH(16, 1) break;
+    case 16:
+      if (explicit_a) {
+        LOGRA_MERGE_LAUNCH_X(16, 1)
+      } else if (packed) {
+        LOGRA_MERGE_LAUNCH_P(16, 2, true)
+      } else {
+        LOGRA_MERGE_LAUNCH_P(16, 2, false)
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
 #undef LOGRA_MERGE_LAUNCH

@@ -29,27 +29,6 @@ __device__ __forceinline__ uint64_t pick_word(const Philox4& p, int i) {
   return (i & 2) ? b : a;
 }
 
-// Eight bf16 values +-1 for the projection's paired column order: dword p
-// takes its low element's sign from bit 15 - p of w and its high element's
-// from bit 31 - p (bit set -> -1).  Two VALU operations per dword.
-// (x & m) | c is one v_and_or_b32 only when m and c sit in registers (that
-// encoding carries no two literals), so the constants are passed through an
-// empty asm statement that makes them opaque.  The instruction itself is left
-// to the compiler: it then knows a VALU op writes the register and inserts the
-// wait states the matrix core needs before reading it as an operand (an
-// and_or written in inline assembly is invisible to that hazard check, and the
-// MFMA read a stale register).
-__device__ __forceinline__ u32x4 expand_sign_pairs(uint32_t w) {
-  uint32_t m = 0x80008000u, one = 0x3F803F80u;
-  asm("" : "+v"(m), "+v"(one));
-  u32x4 v;
-  v[0] = (w & m) | one;
-  v[1] = ((w << 1) & m) | one;
-  v[2] = ((w << 2) & m) | one;
-  v[3] = ((w << 3) & m) | one;
-  return v;
-}
-
 // Four consecutive bf16 of row `row` from column `col` as two words; zero
 // outside [0, nrows) x [0, ncols).  col is a multiple of 4 and rows start
 // 16-byte aligned, so the whole run is one 8-byte load.
