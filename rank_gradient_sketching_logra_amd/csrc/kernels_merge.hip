@@ -197,6 +197,7 @@ __device__ __forceinline__ void merge_barrier() {
 // U slabs, the next bands' loads in flight while one computes); the others
 // take guarded register loads and stores.
 constexpr int kMergeWaves = 8;
+constexpr int kMergeRunSlack = 110;
 
 struct MergeGroupArgs {
   KeyArg key[kMaxGroup];
@@ -214,6 +215,7 @@ struct MergeGroupArgs {
   // bands [g per, g per + per) of column block cb (cb fastest).
   int64_t per;
   int64_t block_begin[kMaxGroup + 1];
+  int64_t nblocks;  // blocks with work; the grid is padded to a multiple of 8
   int n;
   int64_t r;
   float scale_cr;
@@ -250,20 +252,28 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   const float scale_cr = g.scale_cr;
   const float* __restrict__ scale_dev = g.scale_dev;
 
+  // Logical block index: blocks are dispatched round-robin over the 8 XCDs,
+  // so logical blocks x nxb .. (x + 1) nxb - 1 run on XCD x.  The column
+  // blocks of one band run (consecutive logical blocks) then share that
+  // XCD's L2 copy of the run's packed U instead of each fetching it.
+  const int64_t nxb = gridDim.x >> 3;
+  const int64_t lb = (int64_t)(blockIdx.x & 7) * nxb + (int64_t)(blockIdx.x >> 3);
+  if (lb >= g.nblocks) return;  // padding (uniform per block, before any barrier)
+
   int64_t pos, pos_end;
   if (g.per > 0) {
     int it = 0;
-    while ((int64_t)blockIdx.x >= g.block_begin[it + 1]) ++it;
+    while (lb >= g.block_begin[it + 1]) ++it;
     const int64_t nb = (g.d[it] + 31) / 32;
     const int64_t ncb = (g.unit_begin[it + 1] - g.unit_begin[it]) / nb;
-    const int64_t local = (int64_t)blockIdx.x - g.block_begin[it];
+    const int64_t local = lb - g.block_begin[it];
     const int64_t cb = local % ncb, bg = local / ncb;
     pos = g.unit_begin[it] + cb * nb + bg * g.per;
     pos_end = pos + (bg * g.per + g.per < nb ? g.per : nb - bg * g.per);
   } else {
     const int64_t total = g.unit_begin[g.n];
-    pos = (int64_t)blockIdx.x * total / (int64_t)gridDim.x;
-    pos_end = ((int64_t)blockIdx.x + 1) * total / (int64_t)gridDim.x;
+    pos = lb * total / g.nblocks;
+    pos_end = (lb + 1) * total / g.nblocks;
   }
   for (bool first = true; pos < pos_end; first = false) {
     // The lane index is opaque per segment, so that nothing derived from it
@@ -784,9 +794,12 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   // At most one block per compute unit (a second round of blocks would
   // double the time of the units it holds).  Equal shares balance the load
   // but may split a column block's run of bands over two blocks (each
-  // then builds the block's A operands and fills its ring); runs of a fixed
-  // length per column block avoid that and are taken when their longest run
-  // is within 10% of an equal share.
+  // then builds the block's A operands and fills its ring), and the blocks
+  // running at one time hold different bands, so each fetches its own
+  // packed U.  Runs of a fixed length per column block avoid both -- the
+  // column blocks of a run are consecutive logical blocks on one XCD, so
+  // they read the run's U bands from that XCD's L2 -- and are taken when
+  // their longest run is within kMergeRunSlack percent of an equal share.
   const int64_t cus = compute_units();
   const int64_t total = g.unit_begin[n];
   if (total == 0) return hipSuccess;
@@ -805,7 +818,7 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   int64_t per = share;
   while (per < maxbands && runs_for(per) > cus) ++per;
   g.per = 0;
-  if (per * 10 <= share * 11) {
+  if (per * 100 <= share * kMergeRunSlack) {
     g.per = per;
     g.block_begin[0] = 0;
     for (int i = 0; i < n; ++i) {
@@ -815,7 +828,8 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
     }
     blocks = g.block_begin[n];
   }
-  const dim3 grid((unsigned)blocks);
+  g.nblocks = blocks;
+  const dim3 grid((unsigned)((blocks + 7) / 8 * 8));
 #define LOGRA_MERGE_LAUNCH_P(KS, E, P)                                                      \
   if (stochastic)                                                                           \
     hipLaunchKernelGGL((merge_bf16_kernel<KS, E, true, P>), grid, dim3(kMergeWaves * 64), 0, \
