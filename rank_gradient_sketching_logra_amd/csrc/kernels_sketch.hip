@@ -326,14 +326,20 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
 
 }  // namespace
 
-// One projection of a table-driven projection (device memory); entry n holds
-// only item_begin = the total number of 16-token items.
+// Projections that read one input X, up to this many to an entry (at most
+// 64 ranks; one above).
+constexpr int kProjFuse = 3;
+
+// One entry of a table-driven projection (device memory): np projections of
+// the same input X, each with its own A and outputs; entry n holds only
+// item_begin = the total number of 16-token items.
 struct ProjTableEntry {
-  const uint16_t* X;   // bf16 [T x k], leading dimension ldx
-  float* XAt;          // fp32 [T x r] or null
-  uint16_t* planes;    // packed projected input or null
-  uint64_t k0, k1;     // key words of this projection's A
+  const uint16_t* X;              // bf16 [T x k], leading dimension ldx
+  float* XAt[kProjFuse];          // fp32 [T x r] or null
+  uint16_t* planes[kProjFuse];    // packed projected input or null
+  uint64_t k0[kProjFuse], k1[kProjFuse];  // key words of each projection's A
   int64_t ldx, k, item_begin;
+  int np;
 };
 
 namespace {
@@ -342,7 +348,9 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 
 // Persistent projection over a device-resident table of projections (e.g.
 // every projection of every layer for one microbatch).  The work items are
-// (projection, 16-token step) in table order; each wave takes one item at a
+// (entry, 16-token step) in table order, an entry being up to NPF
+// projections of one input (q, k and v of a layer; gate and up), so X is read
+// once for all of them; each wave takes one item at a
 // time and computes it whole -- all k columns, all ranks -- so no two waves
 // share a result and nothing is exchanged between waves.  Wave w of block b
 // starts at item 4b + w and then takes the next unclaimed item from a
@@ -358,11 +366,12 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // deterministic.
 template <int NB16>
 __global__ __launch_bounds__(kPtWaves * 64)
-__attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void project_table_kernel(
+__attribute__((amdgpu_waves_per_eu(NB16 <= 4 ? 3 : 2))) void project_table_kernel(
     const ProjTableEntry* __restrict__ tab, unsigned* __restrict__ next, int n, int64_t T,
     int64_t r, float cr, int nrb) {
   constexpr int NQ = (NB16 + 3) / 4;
   constexpr int RP = NB16 * 16;
+  constexpr int NPF = NB16 <= 4 ? kProjFuse : 1;  // projections an entry may hold
   __shared__ int64_t begin_s[kProjTableMax + 1];
   __shared__ float red[kPtWaves][kProjTokens][RP + 1];
   for (int i = threadIdx.x; i <= n; i += blockDim.x) begin_s[i] = tab[i].item_begin;
@@ -396,14 +405,16 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void p
     const ProjTableEntry& e = tab[lo];
     const uint16_t* __restrict__ X = e.X;
     const int64_t ldx = e.ldx, k = e.k;
-    const KeyWords kw{e.k0, e.k1};
+    const int np = e.np;
     const int64_t st = item - begin_s[lo];
     const int64_t t0 = st * kProjTokens;
     const int64_t trow = t0 + (lane & 15);
 
-    f32x4 acc[NB16];
+    f32x4 acc[NPF][NB16];
 #pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pj = 0; pj < NPF; ++pj)
+#pragma unroll
+      for (int nb = 0; nb < NB16; ++nb) acc[pj][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t nblk = (k + 255) >> 8;
     auto load = [&](int64_t b, u32x4 (&dst)[8]) __attribute__((always_inline)) {
 #pragma unroll
@@ -414,26 +425,31 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void p
     for (int64_t b = 0; b < nblk; ++b) {
       u32x4 an[8];
       if (b + 1 < nblk) load(b + 1, an);
-      uint32_t bits[NQ][8];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int64_t j = lane + 64 * q;
-        const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
-        const bool live = j < r;
+      for (int pj = 0; pj < NPF; ++pj) {
+        if (pj >= np) break;  // uniform per wave
+        const KeyWords kw{e.k0[pj], e.k1[pj]};
+        uint32_t bits[NQ][8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
-          bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+        for (int q = 0; q < NQ; ++q) {
+          const int64_t j = lane + 64 * q;
+          const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
+          const bool live = j < r;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
+            bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+          }
         }
-      }
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s) {
 #pragma unroll
-        for (int nb = 0; nb < NB16; ++nb) {
-          const int src = 16 * (nb & 3) + (lane & 15);
-          const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(a[s]), as_bf16x8(expand_sign_pairs(wv << (4 * g4))), acc[nb], 0, 0, 0);
+          for (int nb = 0; nb < NB16; ++nb) {
+            const int src = 16 * (nb & 3) + (lane & 15);
+            const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
+            acc[pj][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(a[s]), as_bf16x8(expand_sign_pairs(wv << (4 * g4))), acc[pj][nb], 0, 0, 0);
+          }
         }
       }
       if (b + 1 < nblk) {
@@ -442,15 +458,18 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void p
       }
     }
 
-    // The wave's tile through its own LDS rows (a wave's LDS accesses take
-    // effect in program order, so no barrier is needed).
+    // Each projection's tile through the wave's own LDS rows (a wave's LDS
+    // accesses take effect in program order, so no barrier is needed).
+#pragma unroll
+    for (int pj = 0; pj < NPF; ++pj) {
+    if (pj >= np) break;  // uniform per wave
 #pragma unroll
     for (int nb = 0; nb < NB16; ++nb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[nb][j];
+      for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[pj][nb][j];
     asm volatile("" ::: "memory");
-    if (e.XAt) {
-      float* __restrict__ XAt = e.XAt;
+    if (e.XAt[pj]) {
+      float* __restrict__ XAt = e.XAt[pj];
       for (int idx = lane; idx < kProjTokens * r; idx += 64) {
         const int m = idx / (int)r;
         const int j = idx - m * (int)r;
@@ -458,7 +477,7 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void p
         if (t < T) XAt[t * r + j] = rw[m][j] * cr;
       }
     }
-    if (e.planes) {
+    if (e.planes[pj]) {
       for (int b = 0; b < nrb; ++b) {
         const int j = 32 * b + (lane & 31);
         float hv[8], lv[8];
@@ -476,12 +495,13 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 2 ? 4 : (NB16 <= 4 ? 3 : 2)))) void p
           vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
         }
-        uint16_t* dst = e.planes + (st * nrb + b) * 1024 + lane * 8;
+        uint16_t* dst = e.planes[pj] + (st * nrb + b) * 1024 + lane * 8;
         *reinterpret_cast<u32x4*>(dst) = vh;
         *reinterpret_cast<u32x4*>(dst + 512) = vl;
       }
     }
-    asm volatile("" ::: "memory");  // this item's LDS reads before the next item's writes
+    asm volatile("" ::: "memory");  // this tile's LDS reads before the next tile's writes
+    }
     item = grid_waves + (int64_t)__builtin_amdgcn_readfirstlane(claim);
   }
 }
@@ -1299,14 +1319,39 @@ static hipError_t launch_project_table_nb(const ProjTableEntry* t, unsigned* nex
 hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int n, void* ws,
                                 hipStream_t s) {
   if (n < 1 || n > kProjTableMax) return hipErrorInvalidValue;
-  std::vector<ProjTableEntry> tab((size_t)n + 2,
-                                  ProjTableEntry{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0});
-  const int64_t per = (T + kProjTokens - 1) / kProjTokens;  // items per projection
-  for (int i = 0; i < n; ++i)
-    tab[i] = ProjTableEntry{static_cast<const uint16_t*>(items[i].X), items[i].XAt,
-                            items[i].planes, items[i].key.k0, items[i].key.k1, items[i].ldx,
-                            items[i].k, per * i};
-  tab[n].item_begin = per * n;
+  std::vector<ProjTableEntry> tab((size_t)n + 2, ProjTableEntry{});
+  const int64_t per = (T + kProjTokens - 1) / kProjTokens;  // items per entry
+  // Consecutive projections of one input (same X, k and leading dimension)
+  // share an entry, up to kProjFuse of them at <= 64 ranks: X is read once for
+  // all.  Each projection's sums are formed as they would be alone, so the
+  // outputs do not depend on the grouping.
+  const int fuse = proj_nb16(r) <= 4 ? kProjFuse : 1;
+  int ne = 0;
+  for (int i = 0; i < n; ++i) {
+    ProjTableEntry* cur = ne > 0 ? &tab[ne - 1] : nullptr;
+    if (cur && cur->np < fuse && cur->X == items[i].X && cur->k == items[i].k &&
+        cur->ldx == items[i].ldx) {
+      cur->XAt[cur->np] = items[i].XAt;
+      cur->planes[cur->np] = items[i].planes;
+      cur->k0[cur->np] = items[i].key.k0;
+      cur->k1[cur->np] = items[i].key.k1;
+      ++cur->np;
+      continue;
+    }
+    ProjTableEntry& t = tab[ne];
+    t.X = static_cast<const uint16_t*>(items[i].X);
+    t.XAt[0] = items[i].XAt;
+    t.planes[0] = items[i].planes;
+    t.k0[0] = items[i].key.k0;
+    t.k1[0] = items[i].key.k1;
+    t.ldx = items[i].ldx;
+    t.k = items[i].k;
+    t.item_begin = per * ne;
+    t.np = 1;
+    ++ne;
+  }
+  tab[ne].item_begin = per * ne;
+  n = ne;
   // From pageable memory the copy is staged before the call returns.
   hipError_t e = hipMemcpyAsync(ws, tab.data(), tab.size() * sizeof(ProjTableEntry),
                                 hipMemcpyHostToDevice, s);

@@ -362,6 +362,40 @@ def test_project_table(T, r):
                 assert torch.equal(Sp.view(torch.int32), Su.view(torch.int32))
 
 
+@pytest.mark.parametrize("T,r", [(1000, 64), (777, 33), (200, 100)])
+def test_project_table_fused_inputs(T, r):
+    """Consecutive projections of one input (q, k, v; gate, up; four in a row, one more than an
+    entry holds) are projected together, reading the input once: the same XAt and packed bits
+    as the same table with every input a distinct copy, and within 1e-5 of the oracle."""
+    say(f"project table fused T={T} r={r}")
+    widths = [(512, 512), (300, 304), (3584, 3584)]
+    xs = []
+    for i, (k, ld) in enumerate(widths):
+        xb, X = bf16_inputs((T, ld), 1.0, (37, T, k, i, 0))
+        xs.append((bf16_dev(xb), X[:, :k], k))
+    order = [0, 0, 0, 1, 2, 2, 1, 0, 0, 0, 0, 2]   # input of each projection, in table order
+    nb = B.packed_input_bytes(T, r)
+
+    def run(inputs):
+        outs = [(torch.full((T, r), float("nan"), device=DEV),
+                 torch.full((nb // 2,), float("nan"), dtype=torch.bfloat16, device=DEV).view(torch.uint8))
+                for _ in order]
+        B.project_input_table([(B.key(10, j, 3), inputs[j], xo, po)
+                               for j, (xo, po) in enumerate(outs)], r)
+        return outs
+
+    fused = run([xs[i][0][:, :xs[i][2]] for i in order])
+    # distinct copies (padded rows kept): nothing to share
+    alone = run([xs[i][0].clone()[:, :xs[i][2]] for i in order])
+    for (xf, pf), (xa, pa) in zip(fused, alone):
+        assert torch.equal(xf.view(torch.int32), xa.view(torch.int32))
+        assert torch.equal(pf, pa)
+    for j in (0, 2, 5, 10):
+        X = xs[order[j]][1]
+        want = oracle.project(X, oracle.regen_A(10, j, 3, r, X.shape[1]))
+        assert relfro(fused[j][0].cpu().numpy(), want) <= 1e-5
+
+
 def test_project_table_many_items_per_wave():
     """More 16-token items than the grid has waves, so every wave claims several in turn:
     every XAt within fp32 rounding of the single-call projection, two against the oracle."""
