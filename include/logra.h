@@ -46,8 +46,11 @@
  * regenerated from a seed and metadata, [paper] §2.2 "Memory and
  * synchronization"): the Philox family (Salmon et al., SC'11).
  *   key of a projection      = (seed, (step << 32) | matrix_id)
- *   sign of A[j, l]          = bit (l & 63) of word ((l & 255) >> 6) of
- *                              Philox4x64-10(counter = (j, l >> 8, 0, 0)); 1 -> -1
+ *   sign of A[j, l]          = bit (l & 31) of word ((l & 127) >> 5) of
+ *                              Philox4x32-10 with 32-bit counter words
+ *                              (l >> 7, j | 2^31, matrix_id, step) under the
+ *                              32-bit key words (seed & 0xFFFFFFFF, seed >> 32);
+ *                              1 -> -1
  *   stochastic-rounding draw = for element e = (row0 + i) * k + l of W, the
  *                              16 bits [16*(e & 1), +16) of word ((e & 7) >> 1)
  *                              of Philox4x32-10 with 32-bit counter words

@@ -23,9 +23,12 @@ synchronization").  Which generator and which bits is this library's choice;
 the layout is stated here and in ``include/logra.h``:
 
 * key of a projection: ``(seed, (step << 32) | matrix_id)``;
-* sign bits of A (Philox4x64-10): one block per (row j, 256-column group
-  b = l >> 8) with counter ``(j, b, 0, 0)``; column l uses bit ``l & 63`` of
-  output word ``(l & 255) >> 6``; bit 1 means sigma = -1, bit 0 means +1;
+* sign bits of A (Philox4x32-10): one block per (row j, 128-column group
+  c = l >> 7) with 32-bit counter words ``(c, j | 2**31, matrix_id, step)``
+  under the 32-bit key words ``(seed & 0xFFFFFFFF, seed >> 32)``; column l
+  uses bit ``l & 31`` of output word ``(l & 127) >> 5``; bit 1 means
+  sigma = -1, bit 0 means +1 (the top bit of counter word 1 keeps these
+  blocks apart from the rounding draws' under an equal seed);
 * Gaussian entries (the Gaussian projection variant, Philox4x64-10): one
   block per (row j, 4-column group c = l >> 2) with counter ``(j, c, 2, 0)``;
   column l takes Box-Muller pair ``(l & 3) >> 1`` of the four words, cosine
@@ -130,18 +133,21 @@ def projection_key(seed: int, matrix_id: int, step: int):
 
 
 def sign_bits(seed: int, matrix_id: int, step: int, r: int, k: int) -> np.ndarray:
-    """Sign bits of A as a uint8 array [r, k]: 1 means sigma = -1."""
-    key = projection_key(seed, matrix_id, step)
-    nblk = (k + 255) // 256
-    j = np.arange(r, dtype=np.uint64)[:, None]
-    b = np.arange(nblk, dtype=np.uint64)[None, :]
+    """Sign bits of A as a uint8 array [r, k]: 1 means sigma = -1 (Philox4x32-10)."""
+    projection_key(seed, matrix_id, step)   # range checks
+    if r > 2**31:
+        raise ValueError("r must be below 2**31")
+    nblk = (k + 127) // 128
     ctr = np.zeros((r, nblk, 4), dtype=np.uint64)
-    ctr[..., 0] = j
-    ctr[..., 1] = b
-    words = philox4x64_10(ctr, key)                     # [r, nblk, 4]
+    ctr[..., 0] = np.arange(nblk, dtype=np.uint64)[None, :]
+    ctr[..., 1] = np.arange(r, dtype=np.uint64)[:, None] | np.uint64(2**31)
+    ctr[..., 2] = matrix_id
+    ctr[..., 3] = step
+    key = (np.uint64(seed) & MASK32, np.uint64(seed) >> SHIFT32)
+    words = philox4x32_10(ctr, key)                     # [r, nblk, 4]
     l = np.arange(k)
-    w = words[:, l >> 8, (l & 255) >> 6]                # [r, k]
-    return ((w >> (l & 63).astype(np.uint64)) & np.uint64(1)).astype(np.uint8)
+    w = words[:, l >> 7, (l & 127) >> 5]                # [r, k]
+    return ((w >> (l & 31).astype(np.uint64)) & np.uint64(1)).astype(np.uint8)
 
 
 def sr_draws(sr_seed: int, matrix_id: int, step: int, d: int, k: int,

@@ -2,9 +2,10 @@
 //
 // - Philox4x64-10 and Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 //   Random Numbers: As Easy as 1, 2, 3", SC'11): the counter-based generators
-//   that regenerate the Rademacher projection (4x64) and the
+//   that regenerate the Rademacher projection's signs and the
 //   stochastic-rounding draws (4x32: two 32x32-bit products per round instead
-//   of two 64x64-bit ones, about a quarter of the multiplies per draw).
+//   of two 64x64-bit ones, about a quarter of the multiplies per bit) and the
+//   Gaussian projection variant's entries (4x64).
 // - bf16 rounding: nearest-even and deterministic stochastic rounding of an
 //   fp32 value.  Stochastic rounding moves to the far bf16 neighbour with
 //   probability equal to the fraction of the gap ("Randomized Gradient
@@ -61,12 +62,6 @@ struct KeyWords {
   uint64_t k0, k1;
 };
 
-// 256 sign bits of row j, columns [256*b, 256*b + 256) of sigma.
-// Bit l & 255 of the result (word (l & 255) >> 6, bit l & 63) set means -1.
-__device__ __forceinline__ Philox4 sigma_block(KeyWords key, uint64_t j, uint64_t b) {
-  return philox4x64_10(j, b, 0, 0, key.k0, key.k1);
-}
-
 // Four standard normal entries of the Gaussian projection variant, columns
 // 4c .. 4c + 3 of row j: Box-Muller (Box and Muller, 1958) on the block with
 // counter (j, c, 2, 0), uniforms u_i = ((w_i >> 11) + 1/2) 2^-53, pairs
@@ -114,6 +109,26 @@ __device__ __forceinline__ Philox4x32 philox4x32_10(uint32_t c0, uint32_t c1, ui
   out.w[1] = c1;
   out.w[2] = c2;
   out.w[3] = c3;
+  return out;
+}
+
+// 256 sign bits of row j, columns [256*b, 256*b + 256) of sigma, as four
+// 64-bit words: bit l & 255 (word (l & 255) >> 6, bit l & 63) set means -1.
+// They are two Philox4x32-10 blocks, one per 128-column group c = l >> 7,
+// with counter (c, j | 2^31, matrix_id, step) under key (seed lo, seed hi);
+// column l is bit l & 31 of the block's word (l & 127) >> 5, so 64-bit word i
+// is words 2(i & 1) (low half) and 2(i & 1) + 1 (high half) of block 2b + (i >> 1).
+__device__ __forceinline__ Philox4 sigma_block(KeyWords key, uint64_t j, uint64_t b) {
+  const uint32_t c1 = (uint32_t)j | 0x80000000u;
+  const uint32_t mid = (uint32_t)key.k1, step = (uint32_t)(key.k1 >> 32);
+  const uint32_t s0 = (uint32_t)key.k0, s1 = (uint32_t)(key.k0 >> 32);
+  const Philox4x32 lo = philox4x32_10((uint32_t)(2 * b), c1, mid, step, s0, s1);
+  const Philox4x32 hi = philox4x32_10((uint32_t)(2 * b + 1), c1, mid, step, s0, s1);
+  Philox4 out;
+  out.w[0] = (uint64_t)lo.w[0] | ((uint64_t)lo.w[1] << 32);
+  out.w[1] = (uint64_t)lo.w[2] | ((uint64_t)lo.w[3] << 32);
+  out.w[2] = (uint64_t)hi.w[0] | ((uint64_t)hi.w[1] << 32);
+  out.w[3] = (uint64_t)hi.w[2] | ((uint64_t)hi.w[3] << 32);
   return out;
 }
 

@@ -60,18 +60,19 @@ def test_philox_batched_matches_numpy():
         assert np.array_equal(got[i], _numpy_philox_block(ctrs[i], (int(key[0]), int(key[1]))))
 
 
-def test_sign_bit_layout_against_numpy():
-    """Sign bits of A: row j, column l is bit (l & 63) of word (l & 255) >> 6 of the
-    block with counter (j, l >> 8, 0, 0) under key (seed, step<<32 | id)."""
-    seed, mid, step, r, k = 77, 5, 3, 5, 700
-    bits = philox.sign_bits(seed, mid, step, r, k)
-    key = (seed, (step << 32) | mid)
-    for j in range(r):
-        for b in range((k + 255) // 256):
-            blk = _numpy_philox_block((j, b, 0, 0), key)
-            for l in range(256 * b, min(k, 256 * b + 256)):
-                want = (int(blk[(l & 255) >> 6]) >> (l & 63)) & 1
-                assert bits[j, l] == want
+def test_sign_bit_layout():
+    """Sign bits of A: row j, column l is bit (l & 31) of word (l & 127) >> 5 of the
+    Philox4x32-10 block with counter (l >> 7, j | 2**31, matrix id, step) under key
+    (seed lo, seed hi), re-derived with the plain-integer generator (pinned by the
+    published known answers below)."""
+    for seed, mid, step, r, k in [(77, 5, 3, 5, 700), (2**40 + 9, 2**32 - 1, 2**32 - 1, 3, 260)]:
+        bits = philox.sign_bits(seed, mid, step, r, k)
+        key = (seed & 0xFFFFFFFF, seed >> 32)
+        for j in range(r):
+            for c in range((k + 127) // 128):
+                blk = _scalar_philox4x32_10((c, j | 2**31, mid, step), key)
+                for l in range(128 * c, min(k, 128 * c + 128)):
+                    assert bits[j, l] == (blk[(l & 127) >> 5] >> (l & 31)) & 1
 
 
 # Known-answer vectors of Philox4x32-10 published with the generators (Salmon et al.,
