@@ -6,7 +6,7 @@ One step = one update over the whole layer set of the workload:
      persistent launch per microbatch over every matrix of every layer)
   B. accumulate every sketch, every microbatch (one persistent launch per
      microbatch over every matrix of every layer)
-  C. RowAdam for every sketch (writing the update straight in the merge's
+  C. RowAdam for every sketch in one grouped call (writing the update straight in the merge's
      packed operand form), predicted-KL q over the context set, alpha on
      the device
   D. merge every matrix, W <- round(W - eta*alpha U A) (grouped: the seven
@@ -231,8 +231,7 @@ def main():
           for (l, kind, mid, d, k) in mats}
     V = {(l, kind): torch.zeros((d,), dtype=torch.float32, device=dev) for (l, kind, mid, d, k) in mats}
     keys = {(l, kind): B.key(w.seed, mid, w.step) for (l, kind, mid, d, k) in mats}
-    maxd = max(d for (_, _, _, d, _) in mats)
-    ra_ws = B.workspace(B.rowadam_ws_bytes(maxd), dev)
+    ra_ws = B.workspace(B.rowadam_grouped_ws_bytes(len(mats), sum(d for (_, _, _, d, _) in mats)), dev)
     acc_ws = B.workspace(B.sketch_accumulate_table_ws_bytes(len(mats)), dev)
     proj_ws = B.workspace(B.project_input_table_ws_bytes(len(mats)), dev)
     # the rest of the model's weights, resident but untouched (27B set: the projections are
@@ -275,8 +274,9 @@ def main():
                                        for l in reversed(range(layers)) for (kind, d, k) in by_layer[l]],
                                       r, ws=acc_ws)
         ev[2].record()
-        for key_ in S:                               # C: optimiser (U in the merge's packed form)
-            B.rowadam_packed(S[key_], V[key_], t_step, w.beta, w.eps, out=UP[key_], ws=ra_ws)
+        # C: optimiser (U in the merge's packed form), every sketch in one grouped call
+        B.rowadam_packed_grouped([(S[key_], V[key_], UP[key_]) for key_ in S], r, t_step, w.beta,
+                                 w.eps, ws=ra_ws)
         B.predicted_kl_q(z, zd, w.tau, out=q, ws=kl_ws)
         B.step_alpha_dev(q, w.delta, w.alpha_max, out=alpha)
         ev[3].record()

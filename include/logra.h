@@ -528,6 +528,32 @@ LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* 
                                    double beta, double eps, void* U_packed, size_t packed_bytes,
                                    void* ws, size_t ws_bytes, logra_stream stream);
 
+/* One sketch of a grouped RowAdam. */
+typedef struct logra_rowadam_desc {
+  const float* S;         /* [d x r] fp32 sketch, contiguous                   */
+  float* v;               /* [d] fp32 row second moments, updated in place     */
+  void* U_packed;         /* packed update output (logra_packed_update_bytes)  */
+  size_t packed_bytes;    /* bytes available at U_packed                       */
+  int64_t d;              /* rows                                              */
+} logra_rowadam_desc;
+
+/* Workspace bytes logra_rowadam_packed_grouped needs for n sketches of
+ * total_rows rows in all (0 if n < 1 or total_rows < n). */
+LOGRA_API size_t logra_rowadam_grouped_ws_bytes(int n, int64_t total_rows);
+
+/* logra_rowadam_packed for n sketches sharing r, t, beta and eps in three
+ * launches instead of 3n (one RowAdam per selected matrix of a model, [summary]
+ * "B. RowAdam": the statistics are per matrix).  Every sketch's results (v and
+ * the packed update) are bit-identical to its own logra_rowadam_packed call.
+ * The workspace holds a copy of the descriptor table and each sketch's
+ * statistics.  Errors: as logra_rowadam_packed for each descriptor; n < 1 or
+ * n > LOGRA_MAX_ROWADAM_GROUP; an output (v, packed update, workspace)
+ * overlapping another output or any sketch. */
+#define LOGRA_MAX_ROWADAM_GROUP 65536
+LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* descs, int n,
+                                           int64_t t, double beta, double eps, void* ws,
+                                           size_t ws_bytes, logra_stream stream);
+
 typedef struct logra_merge_packed_desc {
   logra_key key;          /* key of this matrix's A                          */
   void* W;                /* [d x k] bf16, row-major, leading dimension ldw  */

@@ -65,6 +65,11 @@ class SyncDesc(Structure):
     _fields_ = [("header", POINTER(SyncHeader)), ("payload", c_void_p), ("W", c_void_p), ("ldw", c_int64)]
 
 
+class RowAdamDesc(Structure):
+    _fields_ = [("S", c_void_p), ("v", c_void_p), ("U_packed", c_void_p), ("packed_bytes", c_size_t),
+                ("d", c_int64)]
+
+
 class MergeExplicitDesc(Structure):
     _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
                 ("U_packed", c_void_p), ("A_packed", c_void_p), ("row0", c_int64)]
@@ -132,6 +137,9 @@ SIGNATURES = {
     "logra_pack_update": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "logra_rowadam_packed": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int64, c_double,
                                      c_double, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+    "logra_rowadam_grouped_ws_bytes": (c_size_t, [c_int, c_int64]),
+    "logra_rowadam_packed_grouped": (c_int, [c_int64, POINTER(RowAdamDesc), c_int, c_int64, c_double,
+                                             c_double, c_void_p, c_size_t, c_void_p]),
     "logra_merge_grouped_packed": (c_int, [c_int64, POINTER(MergePackedDesc), c_int, c_double,
                                            c_void_p, c_int, c_uint64, c_void_p]),
     "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
@@ -406,6 +414,28 @@ def rowadam_packed(S: torch.Tensor, v: torch.Tensor, t: int, beta: float, eps: f
                                       P.numel() * P.element_size(), _ptr(ws), ws.numel(),
                                       _stream(S, stream)))
     return P
+
+
+def rowadam_grouped_ws_bytes(n: int, total_rows: int) -> int:
+    return lib().logra_rowadam_grouped_ws_bytes(n, total_rows)
+
+
+def rowadam_packed_grouped(items, r: int, t: int, beta: float, eps: float, ws=None, stream=None):
+    """items: sequence of (S fp32 [d x r], v fp32 [d], P packed update) sharing r; RowAdam of
+    every sketch in three launches, each result as its own rowadam_packed call."""
+    n = len(items)
+    descs = (RowAdamDesc * n)()
+    rows = 0
+    for i, (S, v, P) in enumerate(items):
+        if S.shape[1] != r or v.shape[0] != S.shape[0]:
+            raise ValueError("S must be [d x r] and v [d]")
+        descs[i] = RowAdamDesc(S.data_ptr(), v.data_ptr(), P.data_ptr(), P.numel() * P.element_size(),
+                               S.shape[0])
+        rows += S.shape[0]
+    if ws is None:
+        ws = workspace(rowadam_grouped_ws_bytes(n, rows), items[0][0].device)
+    _check(lib().logra_rowadam_packed_grouped(r, descs, n, t, beta, eps, _ptr(ws), ws.numel(),
+                                              _stream(items[0][0], stream)))
 
 
 def merge_grouped_packed(items, r: int, scale: float, scale_dev=None, mode: str = "nearest",

@@ -84,6 +84,16 @@ hipError_t launch_reconstruction_cosine(KeyArg key, int64_t d, int64_t k, int64_
                                         const void* A_packed = nullptr);
 
 size_t rowadam_ws_bytes(int64_t d);
+// One sketch of a grouped RowAdam writing packed updates.
+struct RowAdamItem {
+  const float* S;
+  float* v;
+  void* P;
+  int64_t d;
+};
+size_t rowadam_grouped_ws_bytes(int n, int64_t total_rows);
+hipError_t launch_rowadam_packed_grouped(const RowAdamItem* items, int n, int64_t r, int64_t t,
+                                         double beta, double eps, void* ws, hipStream_t s);
 // U (fp32) and/or U_packed (the merge's packed update) may be null.
 hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
                           double beta, double eps, float* U, void* U_packed, void* ws,

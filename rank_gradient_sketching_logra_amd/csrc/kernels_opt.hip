@@ -13,6 +13,9 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <cmath>
+#include <vector>
+
 namespace logra {
 
 namespace {
@@ -28,6 +31,16 @@ struct RowAdamWs {
   double* scalars;  // [4]: eps*rho, norm ratio, -, -
 };
 
+// One sketch of a grouped RowAdam (device table; entry n holds only the
+// totals rb_begin and ap_begin).
+struct RowAdamEntry {
+  const float* S;
+  float* v;
+  uint16_t* P;
+  int64_t d, rb_begin, ap_begin;
+  RowAdamWs ws;
+};
+
 __device__ __forceinline__ double wave_sum(double x) {
   // Butterfly over the 64 lanes (fixed pattern, every lane gets the total).
 #pragma unroll
@@ -35,14 +48,16 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-__global__ __launch_bounds__(256) void rowadam_rows_kernel(int64_t d, int64_t r,
-                                                           const float* __restrict__ S,
-                                                           float* __restrict__ v, double beta,
-                                                           double bias_corr, RowAdamWs ws) {
+// One block's 16 rows (block index blk of the matrix): energies, the
+// second-moment update, and the block's partial sums.
+__device__ __forceinline__ void rowadam_rows_block(int64_t blk, int64_t d, int64_t r,
+                                                   const float* __restrict__ S,
+                                                   float* __restrict__ v, double beta,
+                                                   double bias_corr, const RowAdamWs& ws) {
   __shared__ double sm[kRowsPerBlock], svh[kRowsPerBlock];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
+  const int64_t base = blk * kRowsPerBlock;
   for (int q = wave; q < kRowsPerBlock; q += 4) {
     const int64_t i = base + q;
     double m = 0.0, vh = 0.0;
@@ -73,9 +88,16 @@ __global__ __launch_bounds__(256) void rowadam_rows_kernel(int64_t d, int64_t r,
       a += sm[q];
       b += svh[q];
     }
-    ws.partial[2 * blockIdx.x] = a;
-    ws.partial[2 * blockIdx.x + 1] = b;
+    ws.partial[2 * blk] = a;
+    ws.partial[2 * blk + 1] = b;
   }
+}
+
+__global__ __launch_bounds__(256) void rowadam_rows_kernel(int64_t d, int64_t r,
+                                                           const float* __restrict__ S,
+                                                           float* __restrict__ v, double beta,
+                                                           double bias_corr, RowAdamWs ws) {
+  rowadam_rows_block(blockIdx.x, d, r, S, v, beta, bias_corr, ws);
 }
 
 // Sum of one value per thread over the block's 256 threads: a fixed tree,
@@ -93,8 +115,8 @@ __device__ double block_sum256(double x, double* red) {
 
 // One block: rho, then ||Ut||_F^2 = sum_i m_i / (sqrt(vh_i) + eps rho)^2 and
 // the norm-restoring ratio ||S||_F / ||Ut||_F.
-__global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nblocks,
-                                                           double eps, RowAdamWs ws) {
+__device__ __forceinline__ void rowadam_norm_block(int64_t d, int64_t nblocks, double eps,
+                                                   const RowAdamWs& ws) {
   __shared__ double red[256];
   // Per-block partial sums, thread t taking blocks t, t + 256, ...
   double a = 0.0, b = 0.0;
@@ -117,6 +139,11 @@ __global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nb
   }
 }
 
+__global__ __launch_bounds__(256) void rowadam_norm_kernel(int64_t d, int64_t nblocks,
+                                                           double eps, RowAdamWs ws) {
+  rowadam_norm_block(d, nblocks, eps, ws);
+}
+
 // Scaling pass: U = S * ratio / (sqrt(vh_i) + eps rho), row by row.
 __global__ __launch_bounds__(256) void rowadam_apply_kernel(int64_t d, int64_t r,
                                                             const float* S, float* U,
@@ -132,10 +159,9 @@ __global__ __launch_bounds__(256) void rowadam_apply_kernel(int64_t d, int64_t r
 // The scaling pass writing the merge's packed update instead of fp32 U (the
 // same fp32 values, split into bf16 hi and lo terms in operand order): one
 // thread per (32-row band, 16-rank step, lane).
-__global__ __launch_bounds__(256) void rowadam_apply_packed_kernel(int64_t d, int64_t r, int ks,
-                                                                   const float* S,
-                                                                   uint16_t* P, RowAdamWs ws) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void rowadam_apply_packed_thread(int64_t t, int64_t d, int64_t r, int ks,
+                                                            const float* S, uint16_t* P,
+                                                            const RowAdamWs& ws) {
   const int lane = (int)(t & 63);
   const int64_t bs = t >> 6;
   const int64_t nb = (d + 31) / 32;
@@ -169,6 +195,51 @@ __global__ __launch_bounds__(256) void rowadam_apply_packed_kernel(int64_t d, in
     dst[p] = hv[p];
     dst[256 + p] = lv[p];
   }
+}
+
+__global__ __launch_bounds__(256) void rowadam_apply_packed_kernel(int64_t d, int64_t r, int ks,
+                                                                   const float* S,
+                                                                   uint16_t* P, RowAdamWs ws) {
+  rowadam_apply_packed_thread((int64_t)blockIdx.x * 256 + threadIdx.x, d, r, ks, S, P, ws);
+}
+
+// Grouped RowAdam over many sketches (device table): entry e's row blocks are
+// blocks [rb_begin, rb_begin of e + 1) of the rows launch, its norm is block
+// e of the norm launch, and its (band, step) units of the packed scaling pass
+// are [ap_begin, ap_begin of e + 1).  Each sketch's arithmetic is that of
+// the single call, so the results are bit-identical.
+__device__ __forceinline__ int rowadam_entry(const RowAdamEntry* __restrict__ tab, int n,
+                                             int64_t x, bool by_rows) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((by_rows ? tab[mid].rb_begin : tab[mid].ap_begin) <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void rowadam_rows_grouped_kernel(const RowAdamEntry* __restrict__ tab,
+                                                                   int n, int64_t r, double beta,
+                                                                   double bias_corr) {
+  const int e = rowadam_entry(tab, n, blockIdx.x, true);
+  const RowAdamEntry& t = tab[e];
+  rowadam_rows_block((int64_t)blockIdx.x - t.rb_begin, t.d, r, t.S, t.v, beta, bias_corr, t.ws);
+}
+
+__global__ __launch_bounds__(256) void rowadam_norm_grouped_kernel(const RowAdamEntry* __restrict__ tab,
+                                                                   double eps) {
+  const RowAdamEntry& t = tab[blockIdx.x];
+  rowadam_norm_block(t.d, (t.d + kRowsPerBlock - 1) / kRowsPerBlock, eps, t.ws);
+}
+
+__global__ __launch_bounds__(256) void rowadam_apply_packed_grouped_kernel(
+    const RowAdamEntry* __restrict__ tab, int n, int64_t total, int64_t r, int ks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t unit = t >> 6;
+  if (unit >= total) return;
+  const int e = rowadam_entry(tab, n, unit, false);
+  const RowAdamEntry& x = tab[e];
+  rowadam_apply_packed_thread(t - x.ap_begin * 64, x.d, r, ks, x.S, x.P, x.ws);
 }
 
 // -------------------------------------------------------- predicted KL q
@@ -403,6 +474,55 @@ hipError_t launch_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_
     e = hipGetLastError();
   }
   return e;
+}
+
+size_t rowadam_grouped_ws_bytes(int n, int64_t total_rows) {
+  // the table, then per sketch its m, vh, partial sums and scalars (at most
+  // total_rows / 16 + n row blocks in all)
+  const size_t tab = ((size_t)(n + 1) * sizeof(RowAdamEntry) + 255) / 256 * 256;
+  const int64_t nb = total_rows / kRowsPerBlock + n;
+  return tab + (size_t)(2 * total_rows + 2 * nb + 4 * n) * sizeof(double);
+}
+
+hipError_t launch_rowadam_packed_grouped(const RowAdamItem* items, int n, int64_t r, int64_t t,
+                                         double beta, double eps, void* ws, hipStream_t s) {
+  if (n < 1) return hipErrorInvalidValue;
+  std::vector<RowAdamEntry> tab((size_t)n + 1, RowAdamEntry{});
+  const size_t tab_bytes = ((size_t)(n + 1) * sizeof(RowAdamEntry) + 255) / 256 * 256;
+  double* area = reinterpret_cast<double*>(static_cast<char*>(ws) + tab_bytes);
+  const int ks = merge_rank_steps(r);
+  int64_t rb = 0, ap = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t d = items[i].d;
+    const int64_t nb = (d + kRowsPerBlock - 1) / kRowsPerBlock;
+    RowAdamEntry& e = tab[i];
+    e.S = items[i].S;
+    e.v = items[i].v;
+    e.P = static_cast<uint16_t*>(items[i].P);
+    e.d = d;
+    e.rb_begin = rb;
+    e.ap_begin = ap;
+    e.ws = rowadam_ws_layout(area, d);
+    area += 2 * d + 2 * nb + 4;
+    rb += nb;
+    ap += (d + 31) / 32 * ks;
+  }
+  tab[n].rb_begin = rb;
+  tab[n].ap_begin = ap;
+  // From pageable memory the copy is staged before the call returns.
+  hipError_t e = hipMemcpyAsync(ws, tab.data(), tab.size() * sizeof(RowAdamEntry),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  const RowAdamEntry* dtab = static_cast<const RowAdamEntry*>(ws);
+  const double bias = 1.0 - std::pow(beta, (double)t);
+  hipLaunchKernelGGL(rowadam_rows_grouped_kernel, dim3((unsigned)rb), dim3(256), 0, s, dtab, n, r,
+                     beta, bias);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(rowadam_norm_grouped_kernel, dim3((unsigned)n), dim3(256), 0, s, dtab, eps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(rowadam_apply_packed_grouped_kernel, dim3((unsigned)((ap * 64 + 255) / 256)),
+                     dim3(256), 0, s, dtab, n, ap, r, ks);
+  return hipGetLastError();
 }
 
 size_t klq_ws_bytes(int64_t P, int64_t V) {

@@ -480,6 +480,65 @@ LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* 
                       ws_bytes, stream);
 }
 
+LOGRA_API size_t logra_rowadam_grouped_ws_bytes(int n, int64_t total_rows) {
+  if (n < 1 || n > LOGRA_MAX_ROWADAM_GROUP || total_rows < n) return 0;
+  return logra::rowadam_grouped_ws_bytes(n, total_rows);
+}
+
+LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* descs, int n,
+                                           int64_t t, double beta, double eps, void* ws,
+                                           size_t ws_bytes, logra_stream stream) {
+  static const char* name = "rowadam_packed_grouped";
+  if (!descs || !ws) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
+  if (n < 1 || n > LOGRA_MAX_ROWADAM_GROUP) return fail(LOGRA_ERR_SHAPE, "%s: need 1 <= n <= %d", name, LOGRA_MAX_ROWADAM_GROUP);
+  if (r < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "%s: need 1 <= r <= %d", name, LOGRA_MAX_RANK);
+  if (t < 1) return fail(LOGRA_ERR_DOMAIN, "%s: t counts updates from 1", name);
+  if (!(beta >= 0.0 && beta < 1.0)) return fail(LOGRA_ERR_DOMAIN, "%s: beta must be in [0, 1)", name);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(LOGRA_ERR_DOMAIN, "%s: eps must be finite and >= 0", name);
+  if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "%s: workspace not 16-byte aligned", name);
+  int64_t rows = 0;
+  std::vector<logra::RowAdamItem> items((size_t)n);
+  std::vector<Range> ins((size_t)n), outs;
+  outs.reserve(2 * (size_t)n + 1);
+  for (int i = 0; i < n; ++i) {
+    const logra_rowadam_desc& e = descs[i];
+    if (!e.S || !e.v || !e.U_packed) return fail(LOGRA_ERR_NULL, "%s: NULL pointer in descriptor %d", name, i);
+    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "%s: descriptor %d needs d >= 1", name, i);
+    const size_t pneed = logra::packed_update_bytes(e.d, r);
+    if (e.packed_bytes < pneed) return fail(LOGRA_ERR_WORKSPACE, "%s: descriptor %d: the packed update needs %zu bytes", name, i, pneed);
+    if (!aligned16(e.S) || !aligned16(e.v) || !aligned16(e.U_packed))
+      return fail(LOGRA_ERR_ALIGN, "%s: descriptor %d: S, v and the packed update must be 16-byte aligned", name, i);
+    ins[i] = range(e.S, (size_t)(e.d * r) * 4);
+    outs.push_back(range(e.v, (size_t)e.d * 4));
+    outs.push_back(range(e.U_packed, pneed));
+    items[i] = logra::RowAdamItem{e.S, e.v, e.U_packed, e.d};
+    rows += e.d;
+  }
+  const size_t need = logra::rowadam_grouped_ws_bytes(n, rows);
+  if (ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", name, need);
+  outs.push_back(range(ws, need));
+  std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (overlap(outs[i - 1], outs[i])) return fail(LOGRA_ERR_ALIAS, "%s: two outputs (or an output and the workspace) overlap", name);
+  // Every output against every sketch: with the sketches sorted by start and
+  // the running maximum of their ends, an output [lo, hi) meets a sketch iff
+  // some sketch starting before hi ends after lo.
+  std::vector<Range> sin = ins;
+  std::sort(sin.begin(), sin.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  std::vector<uintptr_t> maxhi(sin.size());
+  for (size_t q = 0; q < sin.size(); ++q) maxhi[q] = q ? std::max(maxhi[q - 1], sin[q].hi) : sin[q].hi;
+  for (const Range& o : outs) {
+    const size_t m = (size_t)(std::lower_bound(sin.begin(), sin.end(), o.hi,
+                                               [](const Range& a, uintptr_t x) { return a.lo < x; }) -
+                              sin.begin());
+    if (m > 0 && maxhi[m - 1] > o.lo)
+      return fail(LOGRA_ERR_ALIAS, "%s: an output or the workspace overlaps a sketch", name);
+  }
+  return hip_status(logra::launch_rowadam_packed_grouped(items.data(), n, r, t, beta, eps, ws,
+                                                         static_cast<hipStream_t>(stream)),
+                    "rowadam_packed_grouped launch");
+}
+
 LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r) {
   if (d < 1 || bad_rank(r)) return 0;
   return logra::packed_update_bytes(d, r);

@@ -183,6 +183,38 @@ def test_rowadam_validation(lib):
     assert err(f, 64, 8, A, A + 64, 1, 0.95, 1e-8, C, Dp, ws, None) == B.ERR_ALIAS     # v inside S
 
 
+def test_rowadam_grouped_validation(lib):
+    f = lib.logra_rowadam_packed_grouped
+    r = 64
+    pb = B.packed_update_bytes(64, r)
+    E = 0x10000000
+
+    def descs(*rows):
+        arr = (B.RowAdamDesc * len(rows))()
+        for i, row in enumerate(rows):
+            arr[i] = B.RowAdamDesc(*row)
+        return arr
+
+    good = [(A, Bp, C, pb, 64), (A + 64 * r * 4, Bp + 256, C + pb, pb, 64)]
+    ws = B.rowadam_grouped_ws_bytes(2, 128)
+    assert ws > 0 and B.rowadam_grouped_ws_bytes(0, 10) == 0 and B.rowadam_grouped_ws_bytes(3, 2) == 0
+    assert err(f, r, None, 2, 1, 0.95, 1e-8, E, ws, None) == B.ERR_NULL
+    assert err(f, r, descs(*good), 0, 1, 0.95, 1e-8, E, ws, None) == B.ERR_SHAPE
+    assert err(f, 300, descs(*good), 2, 1, 0.95, 1e-8, E, ws, None) == B.ERR_SHAPE      # r above the maximum
+    assert err(f, r, descs(*good), 2, 0, 0.95, 1e-8, E, ws, None) == B.ERR_DOMAIN       # t < 1
+    assert err(f, r, descs(*good), 2, 1, 1.0, 1e-8, E, ws, None) == B.ERR_DOMAIN        # beta
+    assert err(f, r, descs(*good), 2, 1, 0.95, 1e-8, E, ws - 8, None) == B.ERR_WORKSPACE
+    assert err(f, r, descs(good[0], (A, Bp + 256, C + pb, pb - 16, 64)), 2, 1, 0.95, 1e-8, E, ws,
+               None) == B.ERR_WORKSPACE                                                  # packed bytes
+    assert err(f, r, descs(good[0], (A, Bp + 8, C + pb, pb, 64)), 2, 1, 0.95, 1e-8, E, ws,
+               None) == B.ERR_ALIGN
+    assert err(f, r, descs(good[0], (A, Bp + 128, C + pb, pb, 64)), 2, 1, 0.95, 1e-8, E, ws,
+               None) == B.ERR_ALIAS                                                      # two v overlap
+    assert err(f, r, descs(good[0], (A + 64 * r * 4, Bp + 256, A + 1024, pb, 64)), 2, 1, 0.95, 1e-8,
+               E, ws, None) == B.ERR_ALIAS                                               # output in a sketch
+    assert err(f, r, descs(*good), 2, 1, 0.95, 1e-8, C + 64, ws, None) == B.ERR_ALIAS    # workspace
+
+
 def test_predicted_kl_validation(lib):
     f = lib.logra_predicted_kl_q
     ws = B.predicted_kl_q_ws_bytes(4, 512)

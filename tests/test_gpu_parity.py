@@ -660,6 +660,40 @@ def test_pack_update_layout_and_rowadam_packed(d, r):
     assert torch.equal(Pk, B.pack_update(Uf))
 
 
+@pytest.mark.parametrize("r", [64, 100, 256])
+def test_rowadam_packed_grouped_equals_single_calls(r):
+    """One grouped RowAdam over sketches of mixed heights gives every sketch the v and packed
+    update bits of its own rowadam_packed call, and U within 1e-6 of the oracle."""
+    ds = [3584, 512, 17, 1000, 33, 18944]
+    say(f"rowadam grouped r={r}")
+    t, beta, eps = 3, 0.95, 1e-8
+    items, singles, host = [], [], []
+    for i, d in enumerate(ds):
+        S = torch.from_numpy(synth.fp32_matrix((d, r), 0.1, (38, d, r, i, 0))).to(DEV)
+        v0 = np.abs(synth.fp32_matrix((d, 1), 0.01, (38, d, r, i, 1)))[:, 0].astype(np.float32)
+        nb = B.packed_update_bytes(d, r)
+        P1 = torch.full((nb // 4,), float("nan"), device=DEV).view(torch.uint8)
+        P2 = torch.full((nb // 4,), float("nan"), device=DEV).view(torch.uint8)
+        v1, v2 = torch.from_numpy(v0.copy()).to(DEV), torch.from_numpy(v0.copy()).to(DEV)
+        items.append((S, v1, P1))
+        singles.append((S, v2, P2))
+        host.append((S.cpu().numpy(), v0))
+    B.rowadam_packed_grouped(items, r, t, beta, eps)
+    for S, v2, P2 in singles:
+        B.rowadam_packed(S, v2, t, beta, eps, out=P2)
+    for (_, v1, P1), (_, v2, P2) in zip(items, singles):
+        assert torch.equal(v1.view(torch.int32), v2.view(torch.int32))
+        assert torch.equal(P1, P2)
+    # the oracle, through the fp32 U of a single call on the first and last sketch
+    for i in (0, len(ds) - 1):
+        S_h, v0 = host[i]
+        U = torch.empty((ds[i], r), dtype=torch.float32, device=DEV)
+        B.rowadam(torch.from_numpy(S_h).to(DEV), torch.from_numpy(v0.copy()).to(DEV), t, beta, eps, U=U)
+        want, _ = oracle.rowadam(S_h.astype(np.float64), v0.astype(np.float64), t, beta, eps)
+        assert relfro(U.cpu().numpy(), want) <= 1e-6
+        assert torch.equal(items[i][2], B.pack_update(U))
+
+
 @pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "stochastic"), (8, "nearest"),
                                     (100, "nearest"), (256, "stochastic"), (256, "nearest")])
 def test_merge_grouped_packed_equals_fp32_update(r, mode):
