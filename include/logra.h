@@ -271,7 +271,10 @@ LOGRA_API size_t logra_project_input_table_ws_bytes(int n);
  * the 256-column blocks in ascending order, each block's 32-column MFMA
  * steps in order; deterministic, and equal to logra_project_input_packed's
  * result up to the last bits (that call adds its column blocks in eight
- * interleaved partial sums).  Several descriptors may share one X.  The
+ * interleaved partial sums).  Several descriptors may share one X;
+ * consecutive descriptors with the same X, k and ldx (up to three, at
+ * r <= 64) are projected together, reading X once, with each projection's
+ * sums formed as they would be alone (the same bits either way).  The
  * descriptor array is read on the host during the call and copied, with the
  * zeroed counter, into the workspace on the stream; calls that share a
  * workspace must not overlap in time.
