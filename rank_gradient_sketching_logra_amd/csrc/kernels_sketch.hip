@@ -17,6 +17,7 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace logra {
@@ -332,7 +333,7 @@ constexpr int kProjFuse = 3;
 
 // One entry of a table-driven projection (device memory): np projections of
 // the same input X, each with its own A and outputs; entry n holds only
-// item_begin = the total number of 16-token items.
+// item_begin = the total number of work items.
 struct ProjTableEntry {
   const uint16_t* X;              // bf16 [T x k], leading dimension ldx
   float* XAt[kProjFuse];          // fp32 [T x r] or null
@@ -348,30 +349,38 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 
 // Persistent projection over a device-resident table of projections (e.g.
 // every projection of every layer for one microbatch).  The work items are
-// (entry, 16-token step) in table order, an entry being up to NPF
-// projections of one input (q, k and v of a layer; gate and up), so X is read
-// once for all of them; each wave takes one item at a
+// (entry, TS consecutive 16-token steps) in table order, an entry being up to
+// NPF projections of one input (q, k and v of a layer; gate and up), so X is
+// read once for all of them; each wave takes one item at a
 // time and computes it whole -- all k columns, all ranks -- so no two waves
-// share a result and nothing is exchanged between waves.  Wave w of block b
+// share a result and nothing is exchanged between waves.  At <= 64 ranks an
+// item holds two token steps, which share each expanded sign operand (the
+// generation, the lane exchange and the expansion are VALU work that does not
+// depend on the tokens).  Wave w of block b
 // starts at item 4b + w and then takes the next unclaimed item from a
 // counter, so items are handed out in order and the fast waves take more.
 // Per item: for each 256-column block in order, the next block's X loads in
 // flight, the signs of the lane's rank (one Philox block per 64 ranks)
-// expanded in the paired column order, eight 16x16x32 MFMA steps; the sums
+// expanded in the paired column order, eight 16x16x32 MFMA steps per token
+// step; the sums
 // run over the column blocks in ascending order in one accumulator.  The
 // tile then goes through the wave's own LDS rows to the fp32 output and/or
 // the accumulate's packed operand form, as in project_bf16_kernel.  The
 // column blocks' partial sums are added in another order than in
 // project_bf16_kernel, so the two differ in the last bits; each is
 // deterministic.
+// Token steps per work item of the table projection.
+__host__ __device__ constexpr int proj_table_steps(int nb16) { return nb16 <= 4 ? 2 : 1; }
+
 template <int NB16>
 __global__ __launch_bounds__(kPtWaves * 64)
-__attribute__((amdgpu_waves_per_eu(NB16 <= 4 ? 3 : 2))) void project_table_kernel(
+__attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
     const ProjTableEntry* __restrict__ tab, unsigned* __restrict__ next, int n, int64_t T,
     int64_t r, float cr, int nrb) {
   constexpr int NQ = (NB16 + 3) / 4;
   constexpr int RP = NB16 * 16;
   constexpr int NPF = NB16 <= 4 ? kProjFuse : 1;  // projections an entry may hold
+  constexpr int TS = proj_table_steps(NB16);
   __shared__ int64_t begin_s[kProjTableMax + 1];
   __shared__ float red[kPtWaves][kProjTokens][RP + 1];
   for (int i = threadIdx.x; i <= n; i += blockDim.x) begin_s[i] = tab[i].item_begin;
@@ -406,25 +415,39 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 4 ? 3 : 2))) void project_table_kerne
     const uint16_t* __restrict__ X = e.X;
     const int64_t ldx = e.ldx, k = e.k;
     const int np = e.np;
-    const int64_t st = item - begin_s[lo];
-    const int64_t t0 = st * kProjTokens;
-    const int64_t trow = t0 + (lane & 15);
+    const int64_t st0 = (item - begin_s[lo]) * TS;  // the item's first token step
+    const int64_t trow = st0 * kProjTokens + (lane & 15);
 
-    f32x4 acc[NPF][NB16];
+    f32x4 acc[TS][NPF][NB16];
 #pragma unroll
-    for (int pj = 0; pj < NPF; ++pj)
+    for (int h = 0; h < TS; ++h)
 #pragma unroll
-      for (int nb = 0; nb < NB16; ++nb) acc[pj][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pj = 0; pj < NPF; ++pj)
+#pragma unroll
+        for (int nb = 0; nb < NB16; ++nb) acc[h][pj][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t nblk = (k + 255) >> 8;
-    auto load = [&](int64_t b, u32x4 (&dst)[8]) __attribute__((always_inline)) {
+    // Rows at or beyond T load as zeros (a last step past T is never stored).
+    auto load = [&](int64_t b, u32x4 (&dst)[TS][8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dst[s] = load_x_paired(X, ldx, trow, b * 256 + 32 * s, g4, T, k);
+      for (int h = 0; h < TS; ++h)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          dst[h][s] = load_x_paired(X, ldx, trow + h * kProjTokens, b * 256 + 32 * s, g4, T, k);
     };
-    u32x4 a[8];
-    load(0, a);
+    // One token step: the next block's X loads are in flight during this
+    // block's work.  Two: the block's own loads are issued first and are in
+    // flight while the first projection's signs are generated (registers for
+    // a second set are not there).
+    constexpr bool kAhead = TS == 1;
+    u32x4 a[TS][8];
+    if constexpr (kAhead) load(0, a);
     for (int64_t b = 0; b < nblk; ++b) {
-      u32x4 an[8];
-      if (b + 1 < nblk) load(b + 1, an);
+      u32x4 an[TS][8];
+      if constexpr (kAhead) {
+        if (b + 1 < nblk) load(b + 1, an);
+      } else {
+        load(b, a);
+      }
 #pragma unroll
       for (int pj = 0; pj < NPF; ++pj) {
         if (pj >= np) break;  // uniform per wave
@@ -447,26 +470,37 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 4 ? 3 : 2))) void project_table_kerne
           for (int nb = 0; nb < NB16; ++nb) {
             const int src = 16 * (nb & 3) + (lane & 15);
             const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
-            acc[pj][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(a[s]), as_bf16x8(expand_sign_pairs(wv << (4 * g4))), acc[pj][nb], 0, 0, 0);
+            const bf16x8 sg = as_bf16x8(expand_sign_pairs(wv << (4 * g4)));
+#pragma unroll
+            for (int h = 0; h < TS; ++h)
+              acc[h][pj][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[h][s]), sg,
+                                                                       acc[h][pj][nb], 0, 0, 0);
           }
         }
       }
-      if (b + 1 < nblk) {
+      if (kAhead && b + 1 < nblk) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) a[s] = an[s];
+        for (int h = 0; h < TS; ++h)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) a[h][s] = an[h][s];
       }
     }
 
     // Each projection's tile through the wave's own LDS rows (a wave's LDS
-    // accesses take effect in program order, so no barrier is needed).
+    // accesses take effect in program order, so no barrier is needed), one
+    // token step at a time.
+#pragma unroll
+    for (int h = 0; h < TS; ++h) {
+    const int64_t st = st0 + h;
+    const int64_t t0 = st * kProjTokens;
+    if (t0 >= T) break;  // uniform per wave
 #pragma unroll
     for (int pj = 0; pj < NPF; ++pj) {
     if (pj >= np) break;  // uniform per wave
 #pragma unroll
     for (int nb = 0; nb < NB16; ++nb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[pj][nb][j];
+      for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[h][pj][nb][j];
     asm volatile("" ::: "memory");
     if (e.XAt[pj]) {
       float* __restrict__ XAt = e.XAt[pj];
@@ -501,6 +535,7 @@ __attribute__((amdgpu_waves_per_eu(NB16 <= 4 ? 3 : 2))) void project_table_kerne
       }
     }
     asm volatile("" ::: "memory");  // this tile's LDS reads before the next tile's writes
+    }
     }
     item = grid_waves + (int64_t)__builtin_amdgcn_readfirstlane(claim);
   }
@@ -1320,7 +1355,8 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
                                 hipStream_t s) {
   if (n < 1 || n > kProjTableMax) return hipErrorInvalidValue;
   std::vector<ProjTableEntry> tab((size_t)n + 2, ProjTableEntry{});
-  const int64_t per = (T + kProjTokens - 1) / kProjTokens;  // items per entry
+  const int64_t per_tokens = (int64_t)kProjTokens * proj_table_steps(proj_nb16(r));
+  const int64_t per = (T + per_tokens - 1) / per_tokens;  // items per entry
   // Consecutive projections of one input (same X, k and leading dimension)
   // share an entry, up to kProjFuse of them at <= 64 ranks: X is read once for
   // all.  Each projection's sums are formed as they would be alone, so the
@@ -1350,6 +1386,11 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
     t.np = 1;
     ++ne;
   }
+  // Entries with the widest inputs first: work is claimed in table order, so
+  // the launch ends on the shortest items and its tail is short.
+  std::stable_sort(tab.begin(), tab.begin() + ne,
+                   [](const ProjTableEntry& a, const ProjTableEntry& b) { return a.k > b.k; });
+  for (int i = 0; i < ne; ++i) tab[i].item_begin = per * i;
   tab[ne].item_begin = per * ne;
   n = ne;
   // From pageable memory the copy is staged before the call returns.
