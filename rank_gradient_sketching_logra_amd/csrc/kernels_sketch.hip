@@ -370,7 +370,7 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // project_bf16_kernel, so the two differ in the last bits; each is
 // deterministic.
 // Token steps per work item of the table projection.
-__host__ __device__ constexpr int proj_table_steps(int nb16) { return nb16 <= 4 ? 2 : 1; }
+__host__ __device__ constexpr int proj_table_steps(int nb16) { return 2; }
 
 template <int NB16>
 __global__ __launch_bounds__(kPtWaves * 64)
@@ -452,29 +452,31 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
       for (int pj = 0; pj < NPF; ++pj) {
         if (pj >= np) break;  // uniform per wave
         const KeyWords kw{e.k0[pj], e.k1[pj]};
-        uint32_t bits[NQ][8];
+        // One 64-rank quarter at a time: its signs, then its MFMAs (each
+        // accumulator still takes the eight column steps in order).
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const int64_t j = lane + 64 * q;
           const Philox4 p = sigma_block(kw, (uint64_t)j, (uint64_t)b);
           const bool live = j < r;
+          uint32_t bits[8];
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            bits[q][2 * w] = live ? (uint32_t)p.w[w] : 0u;
-            bits[q][2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+            bits[2 * w] = live ? (uint32_t)p.w[w] : 0u;
+            bits[2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
           }
-        }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+          for (int s = 0; s < 8; ++s) {
 #pragma unroll
-          for (int nb = 0; nb < NB16; ++nb) {
-            const int src = 16 * (nb & 3) + (lane & 15);
-            const uint32_t wv = (uint32_t)__shfl((int)bits[nb >> 2][s], src, 64);
-            const bf16x8 sg = as_bf16x8(expand_sign_pairs(wv << (4 * g4)));
+            for (int nb = 4 * q; nb < 4 * q + 4 && nb < NB16; ++nb) {
+              const int src = 16 * (nb & 3) + (lane & 15);
+              const uint32_t wv = (uint32_t)__shfl((int)bits[s], src, 64);
+              const bf16x8 sg = as_bf16x8(expand_sign_pairs(wv << (4 * g4)));
 #pragma unroll
-            for (int h = 0; h < TS; ++h)
-              acc[h][pj][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[h][s]), sg,
-                                                                       acc[h][pj][nb], 0, 0, 0);
+              for (int h = 0; h < TS; ++h)
+                acc[h][pj][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(a[h][s]), sg, acc[h][pj][nb], 0, 0, 0);
+            }
           }
         }
       }
