@@ -264,10 +264,11 @@ LOGRA_API size_t logra_project_input_table_ws_bytes(int n);
  * sharing T and r (e.g. every projection of every layer for one microbatch)
  * in one persistent launch ([paper] Sec. 2.1; [rgc] "How it works").  Each
  * descriptor gets XAt (fp32) and/or its packed planes.  The work items are
- * (projection, 16-token step) in descriptor order; each wave of the grid
- * computes one item whole (all k columns, all ranks) and takes the next
- * unclaimed one from a counter in the workspace, so projections of any width
- * mix without idle compute units.  Summation order: for each token and rank,
+ * (projection group, two 16-token steps), the groups ordered widest X first
+ * (so the launch ends on its shortest items); each wave of the grid computes
+ * one item whole (all k columns, all ranks) and takes the next unclaimed one
+ * from a counter in the workspace, so projections of any width mix without
+ * idle compute units.  The outputs do not depend on the order.  Summation order: for each token and rank,
  * the 256-column blocks in ascending order, each block's 32-column MFMA
  * steps in order; deterministic, and equal to logra_project_input_packed's
  * result up to the last bits (that call adds its column blocks in eight

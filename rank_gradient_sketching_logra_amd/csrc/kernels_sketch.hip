@@ -353,10 +353,10 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // NPF projections of one input (q, k and v of a layer; gate and up), so X is
 // read once for all of them; each wave takes one item at a
 // time and computes it whole -- all k columns, all ranks -- so no two waves
-// share a result and nothing is exchanged between waves.  At <= 64 ranks an
-// item holds two token steps, which share each expanded sign operand (the
-// generation, the lane exchange and the expansion are VALU work that does not
-// depend on the tokens).  Wave w of block b
+// share a result and nothing is exchanged between waves.  An item holds two
+// token steps, which share each expanded sign operand (the generation, the
+// lane exchange and the expansion are VALU work that does not depend on the
+// tokens).  Wave w of block b
 // starts at item 4b + w and then takes the next unclaimed item from a
 // counter, so items are handed out in order and the fast waves take more.
 // Per item: for each 256-column block in order, the next block's X loads in
@@ -370,7 +370,7 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // project_bf16_kernel, so the two differ in the last bits; each is
 // deterministic.
 // Token steps per work item of the table projection.
-__host__ __device__ constexpr int proj_table_steps(int nb16) { return 2; }
+constexpr int kProjTableSteps = 2;
 
 template <int NB16>
 __global__ __launch_bounds__(kPtWaves * 64)
@@ -380,7 +380,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
   constexpr int NQ = (NB16 + 3) / 4;
   constexpr int RP = NB16 * 16;
   constexpr int NPF = NB16 <= 4 ? kProjFuse : 1;  // projections an entry may hold
-  constexpr int TS = proj_table_steps(NB16);
+  constexpr int TS = kProjTableSteps;
   __shared__ int64_t begin_s[kProjTableMax + 1];
   __shared__ float red[kPtWaves][kProjTokens][RP + 1];
   for (int i = threadIdx.x; i <= n; i += blockDim.x) begin_s[i] = tab[i].item_begin;
@@ -434,10 +434,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
         for (int s = 0; s < 8; ++s)
           dst[h][s] = load_x_paired(X, ldx, trow + h * kProjTokens, b * 256 + 32 * s, g4, T, k);
     };
-    // One token step: the next block's X loads are in flight during this
-    // block's work.  Two: the block's own loads are issued first and are in
-    // flight while the first projection's signs are generated (registers for
-    // a second set are not there).
+    // With one token step per item the next block's X loads would be in
+    // flight during this block's work; with two the block's own loads are
+    // issued first and are in flight while the first projection's signs are
+    // generated (registers for a second set are not there).
     constexpr bool kAhead = TS == 1;
     u32x4 a[TS][8];
     if constexpr (kAhead) load(0, a);
@@ -1357,7 +1357,7 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
                                 hipStream_t s) {
   if (n < 1 || n > kProjTableMax) return hipErrorInvalidValue;
   std::vector<ProjTableEntry> tab((size_t)n + 2, ProjTableEntry{});
-  const int64_t per_tokens = (int64_t)kProjTokens * proj_table_steps(proj_nb16(r));
+  const int64_t per_tokens = (int64_t)kProjTokens * kProjTableSteps;
   const int64_t per = (T + per_tokens - 1) / per_tokens;  // items per entry
   // Consecutive projections of one input (same X, k and leading dimension)
   // share an entry, up to kProjFuse of them at <= 64 ranks: X is read once for

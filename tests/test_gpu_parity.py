@@ -397,11 +397,12 @@ def test_project_table_fused_inputs(T, r):
 
 
 def test_project_table_many_items_per_wave():
-    """More 16-token items than the grid has waves, so every wave claims several in turn:
-    every XAt within fp32 rounding of the single-call projection, two against the oracle."""
+    """More work items (two 16-token steps each) than the grid has waves, so every wave claims
+    several in turn: every XAt within fp32 rounding of the single-call projection, two against
+    the oracle."""
     T, r = 4096, 64
-    ks = [256, 512, 300] * 8
-    say(f"project table, many items: {len(ks) * T // 16} items")
+    ks = [256, 512, 300] * 12
+    say(f"project table, many items: {len(ks) * T // 32} items")
     xs = []
     for i, k in enumerate(ks):
         ld = (k + 7) // 8 * 8
