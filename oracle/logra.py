@@ -19,10 +19,12 @@ Sources (cited by page title and section):
   [summary] paperlayer.ai section summary of the paper, "B. RowAdam" and
             "D.1 Main mathematical-reasoning experiments".
 
-Arithmetic is fp64 on the exactly decoded bf16/fp32 inputs.  Where the kernel
-must make an integer decision in its own precision (rounding the merged weight
-to bf16), the oracle forms the fp64 value, rounds it once to fp32 and takes
-the decision there, as the library does.
+Arithmetic is fp64 on the exactly decoded bf16/fp32 inputs.  The merged
+weight is formed in fp64 and rounded once, straight to the weight's type
+(nearest-even, or stochastically with the fraction of the gap taken from the
+fp64 value); the library forms it in fp32 first, which may move a result by
+one bf16 unit where the value sits within fp32 rounding of a tie or a
+stochastic threshold -- inside the merge's 1-ulp contract.
 
 Parity status of every function is stated in its docstring; all are pinned by
 the CPU tests except the placement of RowAdam's relative epsilon, whose
@@ -99,13 +101,75 @@ def f32_to_bf16_stochastic(x32: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 
 def ulp_bf16(x: np.ndarray) -> np.ndarray:
-    """Spacing of bf16 at |x| (the larger of the two spacings at a binade edge)."""
-    x = np.abs(np.asarray(x, dtype=np.float64))
-    tiny = 2.0 ** -133                              # bf16 subnormal spacing
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
-    sp = np.where(x >= 2.0 ** -126, 2.0 ** (e - 7), tiny)
-    return sp
+    """Spacing of consecutive bf16 values at |x|.
+
+    bf16 keeps 8 significant bits, so in the binade [2^e, 2^(e+1)) (e >= -126)
+    the spacing is 2^(e-7); below 2^-126 (subnormals, and zero) it is 2^-133.
+    At a power of two the spacing above it, the larger one, is returned.  The
+    binade is read with frexp, which is exact (a logarithm can round a value
+    just below a power of two up into the next binade).  Non-finite inputs
+    give NaN.
+    """
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    finite = np.isfinite(ax)
+    _, e = np.frexp(np.where(finite, ax, 0.0))      # ax = m 2^e, m in [0.5, 1)
+    sp = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    sp = np.where(ax < 2.0 ** -126, 2.0 ** -133, sp)
+    return np.where(finite, sp, np.nan)
+
+
+def _bf16_neighbours(x: np.ndarray):
+    """For finite fp64 x: the bf16 bit patterns a (nearer zero) and b (next away from
+    zero, infinity past the largest finite value) around x, and the fraction
+    f = (|x| - |a|) / (|b| - |a|) of the gap, all exact in fp64."""
+    ax = np.minimum(np.abs(x), 2.0 ** 128)         # at 2^128 and above: a = infinity
+    gap = ulp_bf16(ax)
+    a = np.floor(ax / gap) * gap                    # truncation to the bf16 grid (exact)
+    f = np.where(ax < 2.0 ** 128, (ax - a) / gap, 0.0)
+    with np.errstate(over="ignore"):
+        a_mag = (a.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint32)
+    sign = np.where(np.signbit(x), np.uint32(0x8000), np.uint32(0))
+    a_bits = a_mag | sign
+    b_bits = (a_mag + np.uint32(1)) | sign          # 0x7F7F + 1 = 0x7F80, infinity
+    return a_bits, b_bits, f
+
+
+def f64_to_bf16_rne(x64: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 once, nearest with ties to even; uint16 bits.
+
+    The result is the bf16 neighbour of x nearer to it; at exactly half the gap
+    the neighbour whose last significand bit is 0.  Values from half a gap past
+    the largest finite bf16 round to infinity; +-0 keep their sign; NaN gives a
+    quiet NaN.
+    """
+    x = np.asarray(x64, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    a_bits, b_bits, f = _bf16_neighbours(xf)
+    up = (f > 0.5) | ((f == 0.5) & ((a_bits & np.uint32(1)) == 1))
+    out = np.where(up, b_bits, a_bits)
+    inf_bits = np.where(np.signbit(x), np.uint32(0xFF80), np.uint32(0x7F80))
+    nan_bits = np.where(np.signbit(x), np.uint32(0xFFC0), np.uint32(0x7FC0))
+    out = np.where(np.isinf(x), inf_bits, out)
+    out = np.where(np.isnan(x), nan_bits, out)
+    return out.astype(np.uint16)
+
+
+def f64_to_bf16_stochastic(x64: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Stochastic rounding of fp64 values to bf16 with 16-bit draws ``u``; uint16 bits.
+
+    [rgc] "How it works": the far neighbour b is taken with probability equal
+    to the fraction f of the gap that x has crossed: b iff
+    floor(f * 2^16) + u >= 2^16, else the neighbour a nearer zero.  f comes
+    from the fp64 value itself.  Non-finite inputs round to nearest.
+    """
+    x = np.asarray(x64, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    a_bits, b_bits, f = _bf16_neighbours(xf)
+    take_b = (np.floor(f * 65536.0) + np.asarray(u, dtype=np.float64)) >= 65536.0
+    out = np.where(take_b, b_bits, a_bits).astype(np.uint16)
+    return np.where(finite, out, f64_to_bf16_rne(x)).astype(np.uint16)
 
 
 # ---------------------------------------------------------------------------
@@ -329,25 +393,25 @@ def merge(W: np.ndarray, U: np.ndarray, A: np.ndarray, scale: float, *,
     A regenerated from its seed (scale = 1 there).  [rgc] "How it works":
     bf16 weights kept without an fp32 copy, updated with stochastic rounding.
 
-    The update is formed in fp64 and rounded once to fp32; bf16 weights are
-    then rounded to nearest-even or stochastically with ``u_draws``.
+    The updated weight is formed in fp64 and rounded once, straight to the
+    weight's type: to fp32 (nearest) for ``w_dtype == "f32"``, to bf16
+    nearest-even or stochastically with ``u_draws`` for ``"bf16"``.
     ``W`` holds the decoded weights (fp64); the result is fp32 values for
-    ``w_dtype == "f32"`` and uint16 bf16 bits for ``"bf16"``.
+    ``"f32"`` and uint16 bf16 bits for ``"bf16"``.
     """
     x64 = np.asarray(W, np.float64) - float(scale) * (np.asarray(U, np.float64) @ np.asarray(A, np.float64))
-    x32 = x64.astype(np.float32)
     if w_dtype == "f32":
         if mode != "nearest":
             raise ValueError("stochastic rounding is defined for bf16 weights only")
-        return x32
+        return x64.astype(np.float32)
     if w_dtype != "bf16":
         raise ValueError(w_dtype)
     if mode == "nearest":
-        return f32_to_bf16_rne(x32)
+        return f64_to_bf16_rne(x64)
     if mode == "stochastic":
         if u_draws is None:
             raise ValueError("stochastic rounding needs draws")
-        return f32_to_bf16_stochastic(x32, u_draws)
+        return f64_to_bf16_stochastic(x64, u_draws)
     raise ValueError(mode)
 
 

@@ -402,6 +402,34 @@ def test_predicted_kl_matches_exact_kl_as_alpha_vanishes():
         assert 5 < gaps[0] / gaps[1] < 20 and 5 < gaps[1] / gaps[2] < 20   # first order
 
 
+def test_exact_kl_direction_from_the_third_cumulant():
+    """The exact KL is D_KL(pi_theta || pi_theta+alpha D) ([paper] §2.3: the average KL from
+    the current policy to the stepped one).  With c = alpha / tau and K(c) the cumulant
+    generating function of zdot under p, that KL is K(c) - c E_p[zdot] = c^2 k2 / 2 +
+    c^3 k3 / 6 + O(c^4), while the reverse direction gives c^2 k2 / 2 + c^3 k3 / 3.  Both
+    share the alpha^2 q limit, so the alpha^3 term, with k3 the third central moment of zdot
+    under p, decides the direction: (KL / alpha^2 - q) / alpha -> mean_s k3 / (6 tau^3)."""
+    rs = np.random.default_rng(33)
+    P, V = 6, 300
+    z = rs.standard_normal((P, V))
+    zd = rs.exponential(1.0, (P, V)) ** 1.5           # skewed, so k3 is far from zero
+    for tau in (1.0, 0.6):
+        p = np.exp(z / tau - (z / tau).max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        mu = (p * zd).sum(axis=1, keepdims=True)
+        k3 = (p * (zd - mu) ** 3).sum(axis=1)
+        forward = k3.mean() / (6 * tau ** 3)
+        reverse = k3.mean() / (3 * tau ** 3)
+        assert forward > 0.05
+        q = oracle.predicted_kl_q(z, zd, tau)
+        errs = []
+        for a in (1e-2, 3e-3, 1e-3):
+            third = (oracle.exact_kl_mean(z, zd, a, tau) / a ** 2 - q) / a
+            errs.append(abs(third - forward) / forward)
+            assert abs(third - reverse) / reverse > 0.4
+        assert errs[2] < 2e-2 and errs[2] < errs[1] < errs[0]
+
+
 def test_predicted_kl_special_cases():
     """P7: constant zdot -> q = 0 (softmax is shift invariant); uniform p -> population
     variance of zdot / (2 tau^2); two tokens -> p1 p2 (zd1 - zd2)^2 / (2 tau^2)."""
@@ -482,6 +510,99 @@ def test_stochastic_rounding_definition():
                                         np.array([0, 65535], dtype=np.uint32))
     assert np.isinf(oracle.bf16_bits_to_f64(out)[1])
     assert oracle.bf16_bits_to_f64(out)[0] == float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])
+
+
+def _torch_bf16_values(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns with torch's own bfloat16 type (independent of the oracle)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def test_ulp_bf16_matches_bit_increments():
+    """The unit every merge tolerance is measured in: for every finite bf16 value b (both
+    signs), ulp_bf16 at b and anywhere in (b, next) equals the distance to the bit-incremented
+    value as torch decodes it -- binade edges, subnormals and zero included; at the largest
+    finite value (whose increment is infinity) it equals the distance to the value below."""
+    bits = np.arange(0, 0x7F7F, dtype=np.uint16)              # 0 .. one below the largest finite
+    lo = _torch_bf16_values(bits)
+    hi = _torch_bf16_values(bits + np.uint16(1))
+    gap = hi - lo
+    assert np.all(gap > 0)
+    for sign in (1.0, -1.0):
+        assert np.array_equal(oracle.ulp_bf16(sign * lo), gap)
+        mid = lo + 0.5 * gap
+        assert np.array_equal(oracle.ulp_bf16(sign * mid), gap)
+        below_next = np.nextafter(hi, 0.0)                     # fp64 just under the next bf16
+        assert np.array_equal(oracle.ulp_bf16(sign * below_next), gap)
+    top = _torch_bf16_values(np.array([0x7F7E, 0x7F7F], dtype=np.uint16))
+    assert oracle.ulp_bf16(top[1]) == top[1] - top[0] == 2.0 ** 120
+    # a few fixed points: 1 (spacing above), the smallest normal, a subnormal, zero
+    assert oracle.ulp_bf16(1.0) == 2.0 ** -7 and oracle.ulp_bf16(np.nextafter(1.0, 0)) == 2.0 ** -8
+    assert oracle.ulp_bf16(2.0 ** -126) == 2.0 ** -133 == oracle.ulp_bf16(3 * 2.0 ** -133) == oracle.ulp_bf16(0.0)
+    assert np.isnan(oracle.ulp_bf16(np.inf))
+
+
+def test_fp64_nearest_rounding_is_the_nearest_bf16():
+    """The merge's nearest rounding from fp64: on fp32-representable inputs it agrees with
+    torch's fp32 -> bf16 conversion (ties and edges included); on general fp64 inputs the
+    result is, by brute force, the nearest of torch's bf16 values around x (ties to the even
+    pattern); and it rounds once, where fp64 -> fp32 -> bf16 would round twice."""
+    import torch
+    rs = np.random.default_rng(31)
+    x32 = (rs.standard_normal(100000) * 3).astype(np.float32)
+    u = x32.view(np.uint32).copy()
+    u[:2000] = (u[:2000] & 0xFFFF0000) | 0x8000
+    u[2000:4000] = (u[2000:4000] & 0xFFFF0000) | 0x7FFF
+    x32 = np.concatenate([u.view(np.float32), np.array(
+        [0.0, -0.0, 1e-40, -3e-39, 3.4e38, -3.39e38, np.inf, -np.inf, np.float32(2 ** -133)], np.float32)])
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_rne(x32.astype(np.float64)), want)
+    # general fp64 values: brute-force nearest among the candidates around torch's rounding
+    x = np.concatenate([rs.standard_normal(50000) * 10.0 ** rs.integers(-40, 38, 50000),
+                        rs.standard_normal(2000) * 2.0 ** -128])
+    t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    sgn, mag = t & np.uint16(0x8000), (t & np.uint16(0x7FFF)).astype(np.int32)
+    cands = np.stack([sgn | np.maximum(mag - 1, 0), t, sgn | (mag + 1)]).astype(np.uint16)
+    vals = _torch_bf16_values(cands.ravel()).reshape(cands.shape)
+    dist = np.abs(vals - x[None, :])
+    best = dist.min(axis=0)
+    got = oracle.f64_to_bf16_rne(x)
+    gval = _torch_bf16_values(got)
+    assert np.array_equal(np.abs(gval - x), best)
+    ties = (dist == best[None, :]).sum(axis=0) > 1
+    assert np.all((got[ties] & 1) == 0)
+    # one rounding: 1 + 2^-8 + 2^-30 is above the midpoint 1 + 2^-8, so it rounds up to
+    # 1 + 2^-7; through fp32 it would first become the midpoint and then tie to 1
+    assert _torch_bf16_values(oracle.f64_to_bf16_rne(np.array([1 + 2 ** -8 + 2 ** -30])))[0] == 1 + 2 ** -7
+    assert _torch_bf16_values(oracle.f64_to_bf16_rne(np.array([-(1 + 2 ** -8 - 2 ** -40)])))[0] == -1.0
+    assert np.isinf(_torch_bf16_values(oracle.f64_to_bf16_rne(np.array([1e300, 2.0 ** 128])))).all()
+
+
+def test_fp64_stochastic_rounding_takes_the_fraction_from_fp64():
+    """Stochastic rounding of fp64 values ([rgc] 'How it works'): the result is one of the two
+    bf16 neighbours; over all 2^16 draws the far one is taken exactly floor(f 2^16) times,
+    with f the fraction of the gap computed from the fp64 value (not from an fp32 rounding of
+    it); so the mean over the draws is within gap / 2^16 of x."""
+    allu = np.arange(65536, dtype=np.uint32)
+    rs = np.random.default_rng(32)
+    for x in np.concatenate([rs.standard_normal(40) * 10.0 ** rs.integers(-30, 30, 40), [3e-39, -7e-40]]):
+        out = oracle.f64_to_bf16_stochastic(np.full(65536, x), allu)
+        vals = _torch_bf16_values(out)
+        nb = np.unique(vals)
+        assert len(nb) <= 2 and nb.min() <= x <= nb.max()
+        gap = oracle.ulp_bf16(x)
+        assert abs(vals.mean() - x) <= gap / 65536 * (1 + 1e-9)
+    # f = 1/4 + 2^-20 of the gap above 1: the far neighbour 16384 times of 65536; an fp32
+    # rounding of x would keep only 16 bits of f and could not tell 1/4 + 2^-20 from 1/4 + 0
+    for frac, count in ((0.25, 16384), (0.25 + 2 ** -20, 16384), (0.25 + 2 ** -16, 16385), (1 - 2 ** -30, 65535)):
+        x = 1.0 + 2 ** -7 * frac
+        out = oracle.f64_to_bf16_stochastic(np.full(65536, x), allu)
+        assert int((_torch_bf16_values(out) > 1.0).sum()) == count
+    # bf16 values stay unchanged whatever the draw
+    b = _torch_bf16_values(rs.integers(0, 0x7F7F, 1000).astype(np.uint16))
+    out = oracle.f64_to_bf16_stochastic(b, rs.integers(0, 65536, 1000).astype(np.uint32))
+    assert np.array_equal(_torch_bf16_values(out), b)
 
 
 def test_merge_zero_update_keeps_weights():
