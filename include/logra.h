@@ -82,7 +82,9 @@ typedef enum logra_status {
   LOGRA_ERR_ALIAS = 5,     /* output overlaps an input it must not overlap      */
   LOGRA_ERR_DOMAIN = 6,    /* scalar out of its domain (q<0, NaN, delta<=0, ...) */
   LOGRA_ERR_HIP = 7,       /* the HIP runtime reported an error                  */
-  LOGRA_ERR_WORKSPACE = 8  /* workspace missing or too small                     */
+  LOGRA_ERR_WORKSPACE = 8, /* workspace or packed buffer missing or too small    */
+  LOGRA_ERR_HOST = 9        /* host-side failure inside the call (out of host
+                               memory); nothing was launched                     */
 } logra_status;
 
 typedef enum logra_dtype {
@@ -251,7 +253,9 @@ typedef struct logra_project_desc {
   int64_t k;
   int64_t ldx;
   float* XAt;        /* [T x r] fp32 contiguous, or NULL                    */
-  void* planes;      /* logra_packed_input_bytes(T, r) bytes, or NULL       */
+  void* planes;      /* packed projected input, or NULL                     */
+  size_t planes_bytes; /* bytes available at planes: at least
+                          logra_packed_input_bytes(T, r) when planes is set */
 } logra_project_desc;
 
 #define LOGRA_MAX_PROJECT_TABLE 1024
@@ -337,12 +341,15 @@ typedef struct logra_acc_packed_desc {
   float* S;                 /* [d x r] fp32 contiguous                         */
   int64_t d;
   int64_t ldd;
+  size_t planes_bytes;      /* bytes available at planes: at least
+                               logra_packed_input_bytes(T, r)                 */
 } logra_acc_packed_desc;
 
 /* logra_sketch_accumulate_grouped for bf16 D with the projected inputs
  * already packed (by logra_project_input_packed): the same result bits, one
  * kernel, no workspace.  Several descriptors may share one packed input.
  * Errors: NULL pointers; T < 1, d < 1, r out of range, ldd < d; alignment;
+ * planes_bytes below logra_packed_input_bytes(T, r) (LOGRA_ERR_WORKSPACE);
  * S overlapping D, a packed input or another S; n out of range. */
 LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
                                                      const logra_acc_packed_desc* descs, int n,
@@ -564,13 +571,16 @@ typedef struct logra_merge_packed_desc {
   int64_t d;
   int64_t k;
   int64_t ldw;
-  const void* U_packed;   /* logra_packed_update_bytes(d, r) bytes            */
+  const void* U_packed;   /* packed update of this matrix                     */
   int64_t row0;           /* global index of W's first row                    */
+  size_t packed_bytes;    /* bytes available at U_packed: at least
+                             logra_packed_update_bytes(d, r)                  */
 } logra_merge_packed_desc;
 
 /* logra_merge_grouped with each U given as its packed update.  Same result
  * bits as logra_merge_grouped with the fp32 U the update was packed from.
- * Errors: as logra_merge_grouped. */
+ * Errors: as logra_merge_grouped; packed_bytes below
+ * logra_packed_update_bytes(d, r) (LOGRA_ERR_WORKSPACE). */
 LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_desc* descs, int n,
                                          double scale, const float* scale_dev, logra_round mode,
                                          uint64_t sr_seed, logra_stream stream);
@@ -595,9 +605,11 @@ typedef struct logra_merge_explicit_desc {
   int64_t d;
   int64_t k;
   int64_t ldw;
-  const void* U_packed;   /* logra_packed_update_bytes(d, r) bytes             */
-  const void* A_packed;   /* logra_merge_projection_packed_bytes(r, k) bytes   */
+  const void* U_packed;   /* packed update of this matrix                      */
+  const void* A_packed;   /* the projection in the merge's operand order       */
   int64_t row0;
+  size_t packed_bytes;    /* bytes at U_packed: >= logra_packed_update_bytes(d, r) */
+  size_t A_packed_bytes;  /* bytes at A_packed: >= logra_merge_projection_packed_bytes(r, k) */
 } logra_merge_explicit_desc;
 
 /* logra_merge_grouped_packed with an explicit projection (the Gaussian

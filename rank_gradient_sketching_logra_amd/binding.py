@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogra.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_ALIAS, ERR_DOMAIN, ERR_HIP, ERR_WORKSPACE = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_ALIAS, ERR_DOMAIN, ERR_HIP, ERR_WORKSPACE, ERR_HOST = range(10)
 F32, BF16, I8 = 0, 1, 2
 ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
 MAX_RANK = 256
@@ -33,12 +33,12 @@ class AccDesc(Structure):
 
 class ProjectDesc(Structure):
     _fields_ = [("key", Key), ("X", c_void_p), ("k", c_int64), ("ldx", c_int64), ("XAt", c_void_p),
-                ("planes", c_void_p)]
+                ("planes", c_void_p), ("planes_bytes", c_size_t)]
 
 
 class AccPackedDesc(Structure):
     _fields_ = [("D", c_void_p), ("planes", c_void_p), ("S", c_void_p), ("d", c_int64),
-                ("ldd", c_int64)]
+                ("ldd", c_int64), ("planes_bytes", c_size_t)]
 
 
 class MergeDesc(Structure):
@@ -48,7 +48,7 @@ class MergeDesc(Structure):
 
 class MergePackedDesc(Structure):
     _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
-                ("U_packed", c_void_p), ("row0", c_int64)]
+                ("U_packed", c_void_p), ("row0", c_int64), ("packed_bytes", c_size_t)]
 
 
 class MismatchState(Structure):
@@ -72,7 +72,8 @@ class RowAdamDesc(Structure):
 
 class MergeExplicitDesc(Structure):
     _fields_ = [("key", Key), ("W", c_void_p), ("d", c_int64), ("k", c_int64), ("ldw", c_int64),
-                ("U_packed", c_void_p), ("A_packed", c_void_p), ("row0", c_int64)]
+                ("U_packed", c_void_p), ("A_packed", c_void_p), ("row0", c_int64),
+                ("packed_bytes", c_size_t), ("A_packed_bytes", c_size_t)]
 
 
 SIGNATURES = {
@@ -201,6 +202,32 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_dtype(name: str, t: torch.Tensor, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _need_sketch(name: str, S: torch.Tensor, d: int, r: int):
+    """S (or U): fp32, contiguous, [d x r]."""
+    if S.dtype != torch.float32 or not S.is_contiguous() or tuple(S.shape) != (d, r):
+        raise ValueError(f"{name} must be a contiguous fp32 [{d} x {r}] tensor, got "
+                         f"{S.dtype} {tuple(S.shape)}{'' if S.is_contiguous() else ' (not contiguous)'}")
+
+
+def _scratch(nbytes: int, device, stream=None) -> torch.Tensor:
+    """An internal workspace for one call.  It is allocated on the current stream; when the
+    call runs on another stream, the allocator is told so (record_stream), so the memory is
+    not handed out again before that stream has finished with it."""
+    ws = workspace(nbytes, device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def key(seed: int, matrix_id: int, step: int) -> Key:
     return Key(seed, matrix_id, step)
 
@@ -258,11 +285,14 @@ def project_input_table(items, r: int, ws=None, stream=None):
     for i, (k_, X, XAt, P) in enumerate(items):
         if X.shape[0] != T:
             raise ValueError("every X must have the same number of tokens")
+        _need_dtype("X", X, torch.bfloat16)
+        if XAt is not None:
+            _need_sketch("XAt", XAt, T, r)
         descs[i] = ProjectDesc(k_, X.data_ptr(), X.shape[1], _ld(X),
                                None if XAt is None else XAt.data_ptr(),
-                               None if P is None else P.data_ptr())
+                               None if P is None else P.data_ptr(), 0 if P is None else _nbytes(P))
     if ws is None:
-        ws = workspace(project_input_table_ws_bytes(n), items[0][1].device)
+        ws = _scratch(project_input_table_ws_bytes(n), items[0][1].device, stream)
     _check(lib().logra_project_input_table(T, r, descs, n, _ptr(ws), ws.numel(), _stream(items[0][1], stream)))
 
 
@@ -272,9 +302,12 @@ def sketch_accumulate_grouped_packed(items, r: int, stream=None):
     T = items[0][0].shape[0]
     descs = (AccPackedDesc * n)()
     for i, (D, planes, S) in enumerate(items):
-        if S.shape[1] != r:
-            raise ValueError("S must be [d x r]")
-        descs[i] = AccPackedDesc(D.data_ptr(), planes.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
+        if D.shape[0] != T:
+            raise ValueError("every D must have the same number of tokens")
+        _need_dtype("D", D, torch.bfloat16)
+        _need_sketch("S", S, D.shape[1], r)
+        descs[i] = AccPackedDesc(D.data_ptr(), planes.data_ptr(), S.data_ptr(), D.shape[1], _ld(D),
+                                 _nbytes(planes))
     _check(lib().logra_sketch_accumulate_grouped_packed(T, r, descs, n, _stream(items[0][0], stream)))
 
 
@@ -296,7 +329,7 @@ def sketch_accumulate(D: torch.Tensor, XAt: torch.Tensor, S: torch.Tensor, ws=No
     T, d = D.shape
     r = S.shape[1]
     if ws is None:
-        ws = workspace(accumulate_ws_bytes(T, d, r), D.device)
+        ws = _scratch(accumulate_ws_bytes(T, d, r), D.device, stream)
     _check(lib().logra_sketch_accumulate(T, d, r, _ptr(D), _dtype_code(D), _ld(D), _ptr(XAt),
                                          _ptr(S), _ptr(ws), ws.numel(), _stream(D, stream)))
     return S
@@ -311,8 +344,8 @@ def sketch_accumulate_grouped(items, ws=None, stream=None):
     for i, (D, XAt, S) in enumerate(items):
         descs[i] = AccDesc(D.data_ptr(), XAt.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
     if ws is None:
-        ws = workspace(accumulate_grouped_ws_bytes(T, [D.shape[1] for (D, _, _) in items], r),
-                       items[0][0].device)
+        ws = _scratch(accumulate_grouped_ws_bytes(T, [D.shape[1] for (D, _, _) in items], r),
+                      items[0][0].device, stream)
     _check(lib().logra_sketch_accumulate_grouped(T, r, _dtype_code(items[0][0]), descs, n, _ptr(ws),
                                                  ws.numel(), _stream(items[0][0], stream)))
 
@@ -327,7 +360,7 @@ def rowadam(S: torch.Tensor, v: torch.Tensor, t: int, beta: float, eps: float, U
     d, r = S.shape
     U = U if U is not None else torch.empty_like(S)
     if ws is None:
-        ws = workspace(rowadam_ws_bytes(d), S.device)
+        ws = _scratch(rowadam_ws_bytes(d), S.device, stream)
     _check(lib().logra_rowadam(d, r, _ptr(S), _ptr(v), t, beta, eps, _ptr(U), _ptr(ws), ws.numel(),
                                _stream(S, stream)))
     return U
@@ -342,7 +375,7 @@ def predicted_kl_q(z: torch.Tensor, zdot: torch.Tensor, tau: float, out=None, ws
     P, V = z.shape
     q = out if out is not None else torch.empty((1,), dtype=torch.float32, device=z.device)
     if ws is None:
-        ws = workspace(predicted_kl_q_ws_bytes(P, V), z.device)
+        ws = _scratch(predicted_kl_q_ws_bytes(P, V), z.device, stream)
     _check(lib().logra_predicted_kl_q(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), tau, _ptr(q),
                                       _ptr(ws), ws.numel(), _stream(z, stream)))
     return q
@@ -409,7 +442,7 @@ def rowadam_packed(S: torch.Tensor, v: torch.Tensor, t: int, beta: float, eps: f
     nb = packed_update_bytes(d, r)
     P = out if out is not None else torch.empty((nb,), dtype=torch.uint8, device=S.device)
     if ws is None:
-        ws = workspace(rowadam_ws_bytes(d), S.device)
+        ws = _scratch(rowadam_ws_bytes(d), S.device, stream)
     _check(lib().logra_rowadam_packed(d, r, _ptr(S), _ptr(v), t, beta, eps, _ptr(P),
                                       P.numel() * P.element_size(), _ptr(ws), ws.numel(),
                                       _stream(S, stream)))
@@ -433,7 +466,7 @@ def rowadam_packed_grouped(items, r: int, t: int, beta: float, eps: float, ws=No
                                S.shape[0])
         rows += S.shape[0]
     if ws is None:
-        ws = workspace(rowadam_grouped_ws_bytes(n, rows), items[0][0].device)
+        ws = _scratch(rowadam_grouped_ws_bytes(n, rows), items[0][0].device, stream)
     _check(lib().logra_rowadam_packed_grouped(r, descs, n, t, beta, eps, _ptr(ws), ws.numel(),
                                               _stream(items[0][0], stream)))
 
@@ -446,9 +479,9 @@ def merge_grouped_packed(items, r: int, scale: float, scale_dev=None, mode: str 
     for i, it in enumerate(items):
         k_, W, P = it[0], it[1], it[2]
         row0 = it[3] if len(it) > 3 else 0
-        if P.numel() * P.element_size() < packed_update_bytes(W.shape[0], r):
-            raise ValueError("packed update too small for this W and r")
-        descs[i] = MergePackedDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), P.data_ptr(), row0)
+        _need_dtype("W", W, torch.bfloat16)
+        descs[i] = MergePackedDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), P.data_ptr(), row0,
+                                   _nbytes(P))
     m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
     _check(lib().logra_merge_grouped_packed(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
                                             _stream(items[0][1], stream)))
@@ -482,7 +515,7 @@ def reconstruction_cosine(k_: Key, G: torch.Tensor, r: int, out=None, ws=None, s
     d, kk = G.shape
     o = out if out is not None else torch.empty((4,), dtype=torch.float64, device=G.device)
     if ws is None:
-        ws = workspace(reconstruction_cosine_ws_bytes(d, kk, r), G.device)
+        ws = _scratch(reconstruction_cosine_ws_bytes(d, kk, r), G.device, stream)
     _check(lib().logra_reconstruction_cosine(ctypes.byref(k_), d, kk, r, _ptr(G), _dtype_code(G), _ld(G),
                                              _ptr(o), _ptr(ws), ws.numel(), _stream(G, stream)))
     return o
@@ -524,7 +557,7 @@ def exact_kl(z: torch.Tensor, zdot: torch.Tensor, alpha: float, tau: float, out=
     P, V = z.shape
     o = out if out is not None else torch.empty((1,), dtype=torch.float64, device=z.device)
     if ws is None:
-        ws = workspace(exact_kl_ws_bytes(P), z.device)
+        ws = _scratch(exact_kl_ws_bytes(P), z.device, stream)
     _check(lib().logra_exact_kl(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), float(alpha), float(tau),
                                 _ptr(o), _ptr(ws), ws.numel(), _stream(z, stream)))
     return o
@@ -570,7 +603,7 @@ def reconstruction_cosine_explicit(G: torch.Tensor, A: torch.Tensor, A_packed: t
     r = A.shape[0]
     o = out if out is not None else torch.empty((4,), dtype=torch.float64, device=G.device)
     if ws is None:
-        ws = workspace(reconstruction_cosine_ws_bytes(d, kk, r), G.device)
+        ws = _scratch(reconstruction_cosine_ws_bytes(d, kk, r), G.device, stream)
     _check(lib().logra_reconstruction_cosine_explicit(d, kk, r, _ptr(G), _dtype_code(G), _ld(G), _ptr(A),
                                                       _ptr(A_packed), A_packed.numel(), _ptr(o), _ptr(ws),
                                                       ws.numel(), _stream(G, stream)))
@@ -598,8 +631,9 @@ def merge_grouped_explicit(items, r: int, scale: float, scale_dev=None, mode: st
     for i, it in enumerate(items):
         k_, W, P, Ap = it[0], it[1], it[2], it[3]
         row0 = it[4] if len(it) > 4 else 0
+        _need_dtype("W", W, torch.bfloat16)
         descs[i] = MergeExplicitDesc(k_, W.data_ptr(), W.shape[0], W.shape[1], _ld(W), P.data_ptr(),
-                                     Ap.data_ptr(), row0)
+                                     Ap.data_ptr(), row0, _nbytes(P), _nbytes(Ap))
     m = ROUND_NEAREST if mode == "nearest" else ROUND_STOCHASTIC if mode == "stochastic" else -1
     _check(lib().logra_merge_grouped_explicit(r, descs, n, scale, _ptr(scale_dev), m, sr_seed,
                                               _stream(items[0][1], stream)))
@@ -617,8 +651,10 @@ def sketch_accumulate_table(items, r: int, ws=None, stream=None):
     for i, (D, P, S) in enumerate(items):
         if D.shape[0] != T:
             raise ValueError("every D must have the same number of tokens")
-        descs[i] = AccPackedDesc(D.data_ptr(), P.data_ptr(), S.data_ptr(), D.shape[1], _ld(D))
+        _need_dtype("D", D, torch.bfloat16)
+        _need_sketch("S", S, D.shape[1], r)
+        descs[i] = AccPackedDesc(D.data_ptr(), P.data_ptr(), S.data_ptr(), D.shape[1], _ld(D), _nbytes(P))
     if ws is None:
-        ws = workspace(sketch_accumulate_table_ws_bytes(n), items[0][0].device)
+        ws = _scratch(sketch_accumulate_table_ws_bytes(n), items[0][0].device, stream)
     _check(lib().logra_sketch_accumulate_table(T, r, descs, n, _ptr(ws), ws.numel(),
                                                _stream(items[0][0], stream)))

@@ -7,29 +7,46 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <string>
+#include <exception>
+#include <new>
 
 #include "../../include/logra.h"
 #include "kernels.h"
 
 namespace {
 
-thread_local std::string g_last_error;
+// The calling thread's last error message.  A fixed buffer: recording an
+// error allocates nothing, so it cannot itself fail inside the guard below.
+thread_local char g_last_error[512];
 
 int fail(int status, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return status;
 }
 
 int ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return LOGRA_OK;
 }
+
+// Every int-returning entry point runs its body inside LOGRA_TRY ...
+// LOGRA_CATCH, so no C++ exception (std::bad_alloc from a descriptor table,
+// say) crosses the C ABI: it becomes LOGRA_ERR_HOST with a message.
+#define LOGRA_TRY try {
+#define LOGRA_CATCH(name)                                                                  \
+  }                                                                                        \
+  catch (const std::bad_alloc&) {                                                          \
+    return fail(LOGRA_ERR_HOST, "%s: out of host memory", name);                           \
+  }                                                                                        \
+  catch (const std::exception& ex) {                                                       \
+    return fail(LOGRA_ERR_HOST, "%s: host-side exception: %s", name, ex.what());          \
+  }                                                                                        \
+  catch (...) {                                                                            \
+    return fail(LOGRA_ERR_HOST, "%s: unknown host-side exception", name);                  \
+  }
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -77,7 +94,7 @@ extern "C" {
 
 LOGRA_API const char* logra_version(void) { return "logra-mi355x 0.1.0 (gfx950)"; }
 
-LOGRA_API const char* logra_last_error(void) { return g_last_error.c_str(); }
+LOGRA_API const char* logra_last_error(void) { return g_last_error; }
 
 LOGRA_API int64_t logra_sketch_bytes(int64_t d, int64_t r) {
   if (d < 0 || r < 0) return -1;
@@ -86,17 +103,20 @@ LOGRA_API int64_t logra_sketch_bytes(int64_t d, int64_t r) {
 
 LOGRA_API int logra_regen_A(const logra_key* key, int64_t r, int64_t k, logra_dtype out,
                             void* A, logra_stream stream) {
+  LOGRA_TRY
   if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A: NULL key or output");
   if (bad_rank(r) || k < 1) return fail(LOGRA_ERR_SHAPE, "regen_A: need 1 <= r <= %d and k >= 1", LOGRA_MAX_RANK);
   if (out != LOGRA_I8 && out != LOGRA_F32) return fail(LOGRA_ERR_DTYPE, "regen_A: output must be I8 or F32");
   return hip_status(logra::launch_regen_A(key_words(key->seed, key), r, k, out == LOGRA_I8, A,
                                           static_cast<hipStream_t>(stream)),
                     "regen_A launch");
+  LOGRA_CATCH("regen_A")
 }
 
 LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, int64_t r,
                                   const void* X, logra_dtype x_dtype, int64_t ldx, float* XAt,
                                   logra_stream stream) {
+  LOGRA_TRY
   if (!key || !X || !XAt) return fail(LOGRA_ERR_NULL, "project_input: NULL pointer");
   if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   int st = check_matrix("project_input X", X, x_dtype, ldx, k);
@@ -107,16 +127,19 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
   return hip_status(logra::launch_project(key_words(key->seed, key), T, k, r, X, x_dtype == LOGRA_BF16,
                                           ldx, XAt, nullptr, static_cast<hipStream_t>(stream)),
                     "project_input launch");
+  LOGRA_CATCH("project_input")
 }
 
 LOGRA_API int logra_regen_A_gaussian(const logra_key* key, int64_t r, int64_t k, float* A,
                                      logra_stream stream) {
+  LOGRA_TRY
   if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A_gaussian: NULL pointer");
   if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "regen_A_gaussian: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (!aligned16(A)) return fail(LOGRA_ERR_ALIGN, "regen_A_gaussian: A not 16-byte aligned");
   return hip_status(logra::launch_regen_A_gaussian(key_words(key->seed, key), r, k, A,
                                                    static_cast<hipStream_t>(stream)),
                     "regen_A_gaussian launch");
+  LOGRA_CATCH("regen_A_gaussian")
 }
 
 LOGRA_API size_t logra_projection_packed_bytes(int64_t r, int64_t k) {
@@ -126,6 +149,7 @@ LOGRA_API size_t logra_projection_packed_bytes(int64_t r, int64_t k) {
 
 LOGRA_API int logra_pack_projection(int64_t r, int64_t k, const float* A, void* A_packed,
                                     size_t packed_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_projection: NULL pointer");
   if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::projection_packed_bytes(r, k);
@@ -135,12 +159,14 @@ LOGRA_API int logra_pack_projection(int64_t r, int64_t k, const float* A, void* 
     return fail(LOGRA_ERR_ALIAS, "pack_projection: A overlaps the packed output");
   return hip_status(logra::launch_pack_projection(r, k, A, A_packed, static_cast<hipStream_t>(stream)),
                     "pack_projection launch");
+  LOGRA_CATCH("pack_projection")
 }
 
 LOGRA_API int logra_project_input_explicit(int64_t T, int64_t k, int64_t r, const void* X,
                                            logra_dtype x_dtype, int64_t ldx, const void* A_packed,
                                            size_t packed_bytes, float* XAt, void* planes,
                                            size_t planes_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!X || !A_packed || (!XAt && !planes)) return fail(LOGRA_ERR_NULL, "project_input_explicit: NULL pointer");
   if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_explicit: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_explicit: X must be bf16");
@@ -161,6 +187,7 @@ LOGRA_API int logra_project_input_explicit(int64_t T, int64_t k, int64_t r, cons
                                           static_cast<uint16_t*>(planes), static_cast<hipStream_t>(stream),
                                           A_packed),
                     "project_input_explicit launch");
+  LOGRA_CATCH("project_input_explicit")
 }
 
 LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t r, const void* G,
@@ -168,6 +195,7 @@ LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t
                                                    const void* A_packed, size_t packed_bytes,
                                                    double* out_dev, void* ws, size_t ws_bytes,
                                                    logra_stream stream) {
+  LOGRA_TRY
   if (!G || !A || !A_packed || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine_explicit: NULL pointer");
   if (d < 1 || k < 1 || bad_rank(r))
     return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine_explicit: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
@@ -187,6 +215,7 @@ LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t
   return hip_status(logra::launch_reconstruction_cosine(logra::KeyArg{0, 0}, d, k, r, G, true, ldg, out_dev, ws,
                                                         static_cast<hipStream_t>(stream), A, A_packed),
                     "reconstruction_cosine_explicit launch");
+  LOGRA_CATCH("reconstruction_cosine_explicit")
 }
 
 LOGRA_API size_t logra_reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r) {
@@ -198,6 +227,7 @@ LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64
                                           const void* G, logra_dtype g_dtype, int64_t ldg,
                                           double* out_dev, void* ws, size_t ws_bytes,
                                           logra_stream stream) {
+  LOGRA_TRY
   if (!key || !G || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine: NULL pointer");
   if (d < 1 || k < 1 || bad_rank(r))
     return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
@@ -214,6 +244,7 @@ LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64
                                                         g_dtype == LOGRA_BF16, ldg, out_dev, ws,
                                                         static_cast<hipStream_t>(stream)),
                     "reconstruction_cosine launch");
+  LOGRA_CATCH("reconstruction_cosine")
 }
 
 LOGRA_API size_t logra_packed_input_bytes(int64_t T, int64_t r) {
@@ -225,6 +256,7 @@ LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_
                                          const void* X, logra_dtype x_dtype, int64_t ldx,
                                          float* XAt, void* planes, size_t planes_bytes,
                                          logra_stream stream) {
+  LOGRA_TRY
   if (!key || !X || !planes) return fail(LOGRA_ERR_NULL, "project_input_packed: NULL pointer");
   if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_packed: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_packed: X must be bf16");
@@ -240,6 +272,7 @@ LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_
   return hip_status(logra::launch_project(key_words(key->seed, key), T, k, r, X, true, ldx, XAt,
                                           static_cast<uint16_t*>(planes), static_cast<hipStream_t>(stream)),
                     "project_input_packed launch");
+  LOGRA_CATCH("project_input_packed")
 }
 
 LOGRA_API size_t logra_project_input_table_ws_bytes(int n) {
@@ -249,6 +282,7 @@ LOGRA_API size_t logra_project_input_table_ws_bytes(int n) {
 
 LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_project_desc* descs,
                                         int n, void* ws, size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   static_assert(LOGRA_MAX_PROJECT_TABLE <= 1024, "the kernel's table limit");
   if (!descs || !ws) return fail(LOGRA_ERR_NULL, "project_input_table: NULL pointer");
   if (n < 1 || n > LOGRA_MAX_PROJECT_TABLE) return fail(LOGRA_ERR_SHAPE, "project_input_table: need 1 <= n <= %d", LOGRA_MAX_PROJECT_TABLE);
@@ -267,6 +301,8 @@ LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_projec
     if (!e.X) return fail(LOGRA_ERR_NULL, "project_input_table: NULL X in descriptor %d", i);
     if (!e.XAt && !e.planes) return fail(LOGRA_ERR_NULL, "project_input_table: descriptor %d has no output", i);
     if (e.k < 1) return fail(LOGRA_ERR_SHAPE, "project_input_table: k must be >= 1");
+    if (e.planes && e.planes_bytes < pneed)
+      return fail(LOGRA_ERR_WORKSPACE, "project_input_table: descriptor %d: the packed input needs %zu bytes", i, pneed);
     int st = check_matrix("project_input_table X", e.X, LOGRA_BF16, e.ldx, e.k);
     if (st) return st;
     if ((e.XAt && !aligned16(e.XAt)) || (e.planes && !aligned16(e.planes)))
@@ -287,6 +323,7 @@ LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_projec
       if (overlap(o, xs[j])) return fail(LOGRA_ERR_ALIAS, "project_input_table: an output or the workspace overlaps the X of descriptor %d", j);
   return hip_status(logra::launch_project_table(T, r, items.data(), n, ws, static_cast<hipStream_t>(stream)),
                     "project_input_table launch");
+  LOGRA_CATCH("project_input_table")
 }
 
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r) {
@@ -320,6 +357,7 @@ static int check_acc_item(const char* name, int64_t T, int64_t r, logra_dtype dt
 LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r, const void* D,
                                       logra_dtype d_dtype, int64_t ldd, const float* XAt,
                                       float* S, void* ws, size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   int st = check_acc_item("sketch_accumulate", T, r, d_dtype, D, d, ldd, XAt, S, ws, ws_bytes);
   if (st) return st;
@@ -327,11 +365,13 @@ LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r, const voi
   return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, &it, 1, false,
                                              static_cast<hipStream_t>(stream)),
                     "sketch_accumulate launch");
+  LOGRA_CATCH("sketch_accumulate")
 }
 
 LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype d_dtype,
                                               const logra_acc_desc* descs, int n, void* ws,
                                               size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
@@ -354,11 +394,13 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
   return hip_status(logra::launch_accumulate(T, r, d_dtype == LOGRA_BF16, items, n, false,
                                              static_cast<hipStream_t>(stream)),
                     "sketch_accumulate_grouped launch");
+  LOGRA_CATCH("sketch_accumulate_grouped")
 }
 
 LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
                                                      const logra_acc_packed_desc* descs, int n,
                                                      logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
@@ -368,6 +410,8 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
     const logra_acc_packed_desc& e = descs[i];
     if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL pointer in descriptor %d", i);
     if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: d must be >= 1");
+    if (e.planes_bytes < need)
+      return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_grouped_packed: descriptor %d: the packed input needs %zu bytes", i, need);
     int st = check_matrix("sketch_accumulate_grouped_packed D", e.D, LOGRA_BF16, e.ldd, e.d);
     if (st) return st;
     if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_grouped_packed: planes and S must be 16-byte aligned");
@@ -381,6 +425,7 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
   }
   return hip_status(logra::launch_accumulate(T, r, true, items, n, true, static_cast<hipStream_t>(stream)),
                     "sketch_accumulate_grouped_packed launch");
+  LOGRA_CATCH("sketch_accumulate_grouped_packed")
 }
 
 LOGRA_API size_t logra_sketch_accumulate_table_ws_bytes(int n) {
@@ -390,6 +435,7 @@ LOGRA_API size_t logra_sketch_accumulate_table_ws_bytes(int n) {
 
 LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_acc_packed_desc* descs,
                                             int n, void* ws, size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!descs || !ws) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer");
   if (n < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need n >= 1");
   if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
@@ -404,6 +450,8 @@ LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_ac
     const logra_acc_packed_desc& e = descs[i];
     if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer in descriptor %d", i);
     if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: d must be >= 1");
+    if (e.planes_bytes < need)
+      return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_table: descriptor %d: the packed input needs %zu bytes", i, need);
     int st = check_matrix("sketch_accumulate_table D", e.D, LOGRA_BF16, e.ldd, e.d);
     if (st) return st;
     if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_table: planes and S must be 16-byte aligned");
@@ -427,6 +475,7 @@ LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_ac
         return fail(LOGRA_ERR_ALIAS, "sketch_accumulate_table: sketch %d overlaps an operand of %d", i, j);
   return hip_status(logra::launch_accumulate_table(T, r, items.data(), n, ws, static_cast<hipStream_t>(stream)),
                     "sketch_accumulate_table launch");
+  LOGRA_CATCH("sketch_accumulate_table")
 }
 
 LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {
@@ -468,16 +517,20 @@ int rowadam_impl(const char* name, int64_t d, int64_t r, const float* S, float* 
 LOGRA_API int logra_rowadam(int64_t d, int64_t r, const float* S, float* v, int64_t t,
                             double beta, double eps, float* U, void* ws, size_t ws_bytes,
                             logra_stream stream) {
+  LOGRA_TRY
   if (!U) return fail(LOGRA_ERR_NULL, "rowadam: NULL pointer");
   return rowadam_impl("rowadam", d, r, S, v, t, beta, eps, U, nullptr, 0, ws, ws_bytes, stream);
+  LOGRA_CATCH("rowadam")
 }
 
 LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* v, int64_t t,
                                    double beta, double eps, void* U_packed, size_t packed_bytes,
                                    void* ws, size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!U_packed) return fail(LOGRA_ERR_NULL, "rowadam_packed: NULL pointer");
   return rowadam_impl("rowadam_packed", d, r, S, v, t, beta, eps, nullptr, U_packed, packed_bytes, ws,
                       ws_bytes, stream);
+  LOGRA_CATCH("rowadam_packed")
 }
 
 LOGRA_API size_t logra_rowadam_grouped_ws_bytes(int n, int64_t total_rows) {
@@ -488,6 +541,7 @@ LOGRA_API size_t logra_rowadam_grouped_ws_bytes(int n, int64_t total_rows) {
 LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* descs, int n,
                                            int64_t t, double beta, double eps, void* ws,
                                            size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   static const char* name = "rowadam_packed_grouped";
   if (!descs || !ws) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
   if (n < 1 || n > LOGRA_MAX_ROWADAM_GROUP) return fail(LOGRA_ERR_SHAPE, "%s: need 1 <= n <= %d", name, LOGRA_MAX_ROWADAM_GROUP);
@@ -537,6 +591,7 @@ LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* 
   return hip_status(logra::launch_rowadam_packed_grouped(items.data(), n, r, t, beta, eps, ws,
                                                          static_cast<hipStream_t>(stream)),
                     "rowadam_packed_grouped launch");
+  LOGRA_CATCH("rowadam_packed_grouped")
 }
 
 LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r) {
@@ -546,6 +601,7 @@ LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r) {
 
 LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_packed,
                                 size_t packed_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!U || !U_packed) return fail(LOGRA_ERR_NULL, "pack_update: NULL pointer");
   if (d < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_update: need d >= 1, 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::packed_update_bytes(d, r);
@@ -555,6 +611,7 @@ LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_pa
     return fail(LOGRA_ERR_ALIAS, "pack_update: U overlaps the packed update");
   return hip_status(logra::launch_pack_update(d, r, U, 1.0f, nullptr, U_packed, static_cast<hipStream_t>(stream)),
                     "pack_update launch");
+  LOGRA_CATCH("pack_update")
 }
 
 LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V) {
@@ -565,6 +622,7 @@ LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V) {
 LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zdot,
                                    logra_dtype dtype, float tau, float* q_dev, void* ws,
                                    size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!z || !zdot || !q_dev) return fail(LOGRA_ERR_NULL, "predicted_kl_q: NULL pointer");
   if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: need P, V >= 1");
   if (P > 65535) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: at most 65535 contexts per call");
@@ -576,6 +634,7 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
   return hip_status(logra::launch_predicted_kl_q(P, V, z, zdot, dtype == LOGRA_BF16, tau, q_dev, ws,
                                                  static_cast<hipStream_t>(stream)),
                     "predicted_kl_q launch");
+  LOGRA_CATCH("predicted_kl_q")
 }
 
 LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P) {
@@ -586,6 +645,7 @@ LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P) {
 LOGRA_API int logra_exact_kl(int64_t P, int64_t V, const void* z, const void* zdot,
                              logra_dtype dtype, double alpha, double tau, double* out_dev,
                              void* ws, size_t ws_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!z || !zdot || !out_dev) return fail(LOGRA_ERR_NULL, "exact_kl: NULL pointer");
   if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "exact_kl: need P, V >= 1");
   if (P > 2147483647) return fail(LOGRA_ERR_SHAPE, "exact_kl: too many contexts");
@@ -599,18 +659,22 @@ LOGRA_API int logra_exact_kl(int64_t P, int64_t V, const void* z, const void* zd
   return hip_status(logra::launch_exact_kl(P, V, z, zdot, dtype == LOGRA_BF16, alpha, tau, out_dev, ws,
                                            static_cast<hipStream_t>(stream)),
                     "exact_kl launch");
+  LOGRA_CATCH("exact_kl")
 }
 
 LOGRA_API int logra_step_alpha(double q, double delta, double alpha_max, double* alpha) {
+  LOGRA_TRY
   if (!alpha) return fail(LOGRA_ERR_NULL, "step_alpha: NULL output");
   if (!(delta > 0.0) || !(alpha_max > 0.0)) return fail(LOGRA_ERR_DOMAIN, "step_alpha: delta and alpha_max must be > 0");
   if (std::isnan(q) || q < 0.0) return fail(LOGRA_ERR_DOMAIN, "step_alpha: q must be >= 0");
   *alpha = q == 0.0 ? alpha_max : std::fmin(alpha_max, std::sqrt(delta / q));
   return ok();
+  LOGRA_CATCH("step_alpha")
 }
 
 LOGRA_API int logra_kl_budget(int64_t u, int64_t H, double delta_max, double delta_min,
                               double* delta_u) {
+  LOGRA_TRY
   if (!delta_u) return fail(LOGRA_ERR_NULL, "kl_budget: NULL output");
   if (u < 1 || H < 2) return fail(LOGRA_ERR_DOMAIN, "kl_budget: need u >= 1 and H >= 2");
   if (!std::isfinite(delta_max) || !std::isfinite(delta_min) || delta_min < 0.0 || delta_max < delta_min)
@@ -623,9 +687,11 @@ LOGRA_API int logra_kl_budget(int64_t u, int64_t H, double delta_max, double del
   *delta_u = delta_min + 0.5 * (delta_max - delta_min) *
                              (1.0 + std::cos(pi * (double)(u - 1) / (double)(H - 1)));
   return ok();
+  LOGRA_CATCH("kl_budget")
 }
 
 LOGRA_API int logra_mismatch_update(logra_mismatch_state* state, double measurement, double weight) {
+  LOGRA_TRY
   if (!state) return fail(LOGRA_ERR_NULL, "mismatch_update: NULL state");
   if (!(weight > 0.0 && weight <= 1.0)) return fail(LOGRA_ERR_DOMAIN, "mismatch_update: weight must be in (0, 1]");
   if (std::isinf(measurement)) return fail(LOGRA_ERR_DOMAIN, "mismatch_update: infinite measurement");
@@ -634,10 +700,12 @@ LOGRA_API int logra_mismatch_update(logra_mismatch_state* state, double measurem
   state->kappa = k > 0.0 ? k : 0.0;
   state->valid = 1;
   return ok();
+  LOGRA_CATCH("mismatch_update")
 }
 
 LOGRA_API int logra_effective_budget(double delta_u, const logra_mismatch_state* state,
                                      double* delta_eff) {
+  LOGRA_TRY
   if (!state || !delta_eff) return fail(LOGRA_ERR_NULL, "effective_budget: NULL pointer");
   if (!(delta_u >= 0.0) || !std::isfinite(delta_u)) return fail(LOGRA_ERR_DOMAIN, "effective_budget: delta_u must be finite and >= 0");
   if (!state->valid) {
@@ -648,14 +716,17 @@ LOGRA_API int logra_effective_budget(double delta_u, const logra_mismatch_state*
   const double floor = 0.5 * delta_u;
   *delta_eff = sub > floor ? sub : floor;
   return ok();
+  LOGRA_CATCH("effective_budget")
 }
 
 LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_max,
                                    float* alpha_dev, logra_stream stream) {
+  LOGRA_TRY
   if (!q_dev || !alpha_dev) return fail(LOGRA_ERR_NULL, "step_alpha_dev: NULL pointer");
   if (!(delta > 0.f) || !(alpha_max > 0.f)) return fail(LOGRA_ERR_DOMAIN, "step_alpha_dev: delta and alpha_max must be > 0");
   return hip_status(logra::launch_step_alpha(q_dev, delta, alpha_max, alpha_dev, static_cast<hipStream_t>(stream)),
                     "step_alpha_dev launch");
+  LOGRA_CATCH("step_alpha_dev")
 }
 
 namespace {
@@ -667,6 +738,8 @@ struct MergeOperands {
   const void* U;
   int64_t row0;
   const void* A = nullptr;  // explicit projection (merge operand order), or null
+  size_t U_bytes = 0;       // bytes available at a packed U (unused for fp32 U)
+  size_t A_bytes = 0;       // bytes available at A
 };
 int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, int n, double scale,
                        const float* scale_dev, logra_round mode, uint64_t sr_seed, bool packed,
@@ -686,6 +759,9 @@ int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, in
     int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.k);
     if (st) return st;
     if (!aligned16(e.U)) return fail(LOGRA_ERR_ALIGN, "%s: U not 16-byte aligned", name);
+    if (packed && e.U_bytes < logra::packed_update_bytes(e.d, r))
+      return fail(LOGRA_ERR_WORKSPACE, "%s: descriptor %d: the packed update needs %zu bytes", name, i,
+                  logra::packed_update_bytes(e.d, r));
     const Range rw = range(e.W, extent(e.d, e.k, e.ldw, 2));
     if (scale_dev && overlap(rw, range(scale_dev, 4))) return fail(LOGRA_ERR_ALIAS, "%s: W overlaps the device scale", name);
     for (int j = 0; j <= i; ++j) {
@@ -698,6 +774,9 @@ int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, in
     if ((e.A != nullptr) != (ops[0].A != nullptr))
       return fail(LOGRA_ERR_NULL, "%s: explicit projections for all descriptors or none", name);
     if (e.A) {
+      if (e.A_bytes < logra::merge_projection_packed_bytes(r, e.k))
+        return fail(LOGRA_ERR_WORKSPACE, "%s: descriptor %d: the packed projection needs %zu bytes", name, i,
+                    logra::merge_projection_packed_bytes(r, e.k));
       const Range ra = range(e.A, logra::merge_projection_packed_bytes(r, e.k));
       if (!aligned16(e.A)) return fail(LOGRA_ERR_ALIGN, "%s: projection %d not 16-byte aligned", name, i);
       for (int j = 0; j <= i; ++j)
@@ -716,6 +795,7 @@ int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, in
 LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int n, double scale,
                                   const float* scale_dev, logra_round mode, uint64_t sr_seed,
                                   logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "merge_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   MergeOperands ops[LOGRA_MAX_GROUP];
@@ -723,20 +803,23 @@ LOGRA_API int logra_merge_grouped(int64_t r, const logra_merge_desc* descs, int 
     ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw, descs[i].U,
                            descs[i].row0};
   return merge_grouped_impl("merge_grouped", r, ops, n, scale, scale_dev, mode, sr_seed, false, stream);
+  LOGRA_CATCH("merge_grouped")
 }
 
 LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_desc* descs, int n,
                                          double scale, const float* scale_dev, logra_round mode,
                                          uint64_t sr_seed, logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped_packed: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP)
     return fail(LOGRA_ERR_SHAPE, "merge_grouped_packed: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   MergeOperands ops[LOGRA_MAX_GROUP];
   for (int i = 0; i < n; ++i)
     ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw,
-                           descs[i].U_packed, descs[i].row0};
+                           descs[i].U_packed, descs[i].row0, nullptr, descs[i].packed_bytes};
   return merge_grouped_impl("merge_grouped_packed", r, ops, n, scale, scale_dev, mode, sr_seed, true,
                             stream);
+  LOGRA_CATCH("merge_grouped_packed")
 }
 
 LOGRA_API size_t logra_merge_projection_packed_bytes(int64_t r, int64_t k) {
@@ -746,6 +829,7 @@ LOGRA_API size_t logra_merge_projection_packed_bytes(int64_t r, int64_t k) {
 
 LOGRA_API int logra_pack_merge_projection(int64_t r, int64_t k, const float* A, void* A_packed,
                                           size_t packed_bytes, logra_stream stream) {
+  LOGRA_TRY
   if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_merge_projection: NULL pointer");
   if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_merge_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::merge_projection_packed_bytes(r, k);
@@ -755,11 +839,13 @@ LOGRA_API int logra_pack_merge_projection(int64_t r, int64_t k, const float* A, 
     return fail(LOGRA_ERR_ALIAS, "pack_merge_projection: A overlaps the packed output");
   return hip_status(logra::launch_pack_merge_projection(r, k, A, A_packed, static_cast<hipStream_t>(stream)),
                     "pack_merge_projection launch");
+  LOGRA_CATCH("pack_merge_projection")
 }
 
 LOGRA_API int logra_merge_grouped_explicit(int64_t r, const logra_merge_explicit_desc* descs, int n,
                                            double scale, const float* scale_dev, logra_round mode,
                                            uint64_t sr_seed, logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "merge_grouped_explicit: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP)
     return fail(LOGRA_ERR_SHAPE, "merge_grouped_explicit: need 1 <= n <= %d", LOGRA_MAX_GROUP);
@@ -767,10 +853,12 @@ LOGRA_API int logra_merge_grouped_explicit(int64_t r, const logra_merge_explicit
   for (int i = 0; i < n; ++i) {
     if (!descs[i].A_packed) return fail(LOGRA_ERR_NULL, "merge_grouped_explicit: NULL projection in descriptor %d", i);
     ops[i] = MergeOperands{&descs[i].key, descs[i].W, descs[i].d, descs[i].k, descs[i].ldw,
-                           descs[i].U_packed, descs[i].row0, descs[i].A_packed};
+                           descs[i].U_packed, descs[i].row0, descs[i].A_packed, descs[i].packed_bytes,
+                           descs[i].A_packed_bytes};
   }
   return merge_grouped_impl("merge_grouped_explicit", r, ops, n, scale, scale_dev, mode, sr_seed, true,
                             stream);
+  LOGRA_CATCH("merge_grouped_explicit")
 }
 
 LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_t r,
@@ -778,6 +866,7 @@ LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_
                               logra_round mode, uint64_t sr_seed, int64_t row0,
                               logra_sync_header* header, void* payload, size_t payload_bytes,
                               logra_stream stream) {
+  LOGRA_TRY
   if (!key || !U || !header || !payload) return fail(LOGRA_ERR_NULL, "sync_pack: NULL pointer");
   if (d < 1 || k < 1 || bad_rank(r) || row0 < 0)
     return fail(LOGRA_ERR_SHAPE, "sync_pack: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
@@ -802,9 +891,11 @@ LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_
   return hip_status(logra::launch_pack_update(d, r, U, (float)scale, scale_dev, payload,
                                               static_cast<hipStream_t>(stream)),
                     "sync_pack launch");
+  LOGRA_CATCH("sync_pack")
 }
 
 LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream stream) {
+  LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "sync_apply: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sync_apply: need 1 <= n <= %d", LOGRA_MAX_GROUP);
   MergeOperands ops[LOGRA_MAX_GROUP];
@@ -817,17 +908,20 @@ LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream
       return fail(LOGRA_ERR_DOMAIN, "sync_apply: header %d sizes are inconsistent", i);
     if (h->r != descs[0].header->r || h->mode != descs[0].header->mode || h->sr_seed != descs[0].header->sr_seed)
       return fail(LOGRA_ERR_SHAPE, "sync_apply: descriptors must share r, mode and sr_seed");
-    ops[i] = MergeOperands{&h->key, descs[i].W, h->d, h->k, descs[i].ldw, descs[i].payload, h->row0};
+    ops[i] = MergeOperands{&h->key, descs[i].W, h->d, h->k, descs[i].ldw, descs[i].payload, h->row0, nullptr,
+                           (size_t)h->payload_bytes};
   }
   const logra_sync_header* h0 = descs[0].header;
   return merge_grouped_impl("sync_apply", h0->r, ops, n, 1.0, nullptr, (logra_round)h0->mode, h0->sr_seed,
                             true, stream);
+  LOGRA_CATCH("sync_apply")
 }
 
 LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r, void* W,
                           logra_dtype w_dtype, int64_t ldw, const float* U, double scale,
                           const float* scale_dev, logra_round mode, uint64_t sr_seed,
                           int64_t row0, logra_stream stream) {
+  LOGRA_TRY
   if (!key || !W || !U) return fail(LOGRA_ERR_NULL, "merge: NULL pointer");
   if (d < 1 || k < 1 || bad_rank(r) || row0 < 0) return fail(LOGRA_ERR_SHAPE, "merge: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
   int st = check_matrix("merge W", W, w_dtype, ldw, k);
@@ -844,6 +938,7 @@ LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r,
                                         scale, scale_dev, mode == LOGRA_ROUND_STOCHASTIC,
                                         key_words(sr_seed, key), row0, static_cast<hipStream_t>(stream)),
                     "merge launch");
+  LOGRA_CATCH("merge")
 }
 
 }  // extern "C"

@@ -73,6 +73,10 @@ C = 0x8000000
 Dp = 0xC000000
 
 
+PIN = 128 * 64 * 4        # packed projected input of T = 128 tokens at r = 64
+PUP = 64 * 64 * 4         # packed update of d = 64 rows at r = 64 (or fewer ranks)
+
+
 def key():
     return B.Key(1, 0, 0)
 
@@ -142,14 +146,14 @@ def test_packed_sizes_and_validation(lib):
     assert err(f, k, 16, 64, 8, A, B.BF16, 64, None, A + 256, nb, None) == B.ERR_ALIAS     # planes in X
     assert err(f, k, 16, 64, 8, A, B.BF16, 64, Bp + 16, Bp, nb, None) == B.ERR_ALIAS       # XAt in planes
     g = lib.logra_sketch_accumulate_grouped_packed
-    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64))
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64, PIN), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64, PIN))
     assert err(g, 128, 64, d2, 2, None) == B.ERR_ALIAS                                     # sketches overlap
     assert err(g, 128, 64, d2, 0, None) == B.ERR_SHAPE
     assert err(g, 128, 300, d2, 1, None) == B.ERR_SHAPE
     assert err(g, 128, 64, None, 1, None) == B.ERR_NULL
-    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, Bp + 64, 64, 64))
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, Bp + 64, 64, 64, PIN))
     assert err(g, 128, 64, d1, 1, None) == B.ERR_ALIAS                                     # S in planes
-    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp + 4, C, 64, 64))
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp + 4, C, 64, 64, PIN))
     assert err(g, 128, 64, d1, 1, None) == B.ERR_ALIGN
 
 
@@ -262,16 +266,16 @@ def test_packed_update_sizes_and_validation(lib):
     assert err(g, 64, 8, A, Bp, 1, 0.95, 1e-8, A + 64, nb, Dp, ws, None) == B.ERR_ALIAS    # packed in S
     assert err(g, 64, 300, A, Bp, 1, 0.95, 1e-8, C, nb, Dp, ws, None) == B.ERR_SHAPE
     m = lib.logra_merge_grouped_packed
-    d2 = (B.MergePackedDesc * 2)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp, 0),
-                                 B.MergePackedDesc(key(), A + 4096, 64, 64, 64, C, 0))
+    d2 = (B.MergePackedDesc * 2)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp, 0, PUP),
+                                 B.MergePackedDesc(key(), A + 4096, 64, 64, 64, C, 0, PUP))
     assert err(m, 64, d2, 2, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # W overlap
     assert err(m, 64, None, 1, 1.0, None, 0, 0, None) == B.ERR_NULL
     assert err(m, 300, d2, 1, 1.0, None, 0, 0, None) == B.ERR_SHAPE
-    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, A + 512, 0))
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, A + 512, 0, PUP))
     assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # packed U inside W
-    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), Bp, 64, 64, 64, Bp - 16, 0))
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), Bp, 64, 64, 64, Bp - 16, 0, PUP))
     assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS        # packed U runs into W
-    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp + 8, 0))
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp + 8, 0, PUP))
     assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
 
 
@@ -372,11 +376,11 @@ def test_merge_explicit_validation(lib):
     assert err(lib.logra_pack_merge_projection, 8, 64, A, Bp, nb - 1, None) == B.ERR_WORKSPACE
     assert err(lib.logra_pack_merge_projection, 8, 64, None, Bp, nb, None) == B.ERR_NULL
     f = lib.logra_merge_grouped_explicit
-    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, None, 0))
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, None, 0, PUP, 1 << 20))
     assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_NULL
-    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C + 8, 0))
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C + 8, 0, PUP, 1 << 20))
     assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIGN
-    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, A + 256, 0))
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, A + 256, 0, PUP, 1 << 20))
     assert err(f, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_ALIAS       # projection inside W
 
 
@@ -385,15 +389,15 @@ def test_accumulate_table_validation(lib):
     f = lib.logra_sketch_accumulate_table
     ws = B.sketch_accumulate_table_ws_bytes(2)
     W = 0x20000000
-    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64))
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64, PIN), B.AccPackedDesc(A + 65536, Bp, C + 64, 64, 64, PIN))
     assert err(f, 128, 64, d2, 2, W, ws, None) == B.ERR_ALIAS            # sketches overlap
     assert err(f, 128, 64, d2, 0, W, ws, None) == B.ERR_SHAPE
     assert err(f, 128, 64, d2, 2, W, ws - 1, None) == B.ERR_WORKSPACE
     assert err(f, 128, 64, d2, 2, None, ws, None) == B.ERR_NULL
     assert err(f, 128, 300, d2, 1, W, ws, None) == B.ERR_SHAPE
-    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64), B.AccPackedDesc(C + 1024, Bp, Dp, 64, 64))
+    d2 = (B.AccPackedDesc * 2)(B.AccPackedDesc(A, Bp, C, 64, 64, PIN), B.AccPackedDesc(C + 1024, Bp, Dp, 64, 64, PIN))
     assert err(f, 128, 64, d2, 2, W, ws, None) == B.ERR_ALIAS            # sketch 0 inside D of 1
-    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64))
+    d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64, PIN))
     assert err(f, 128, 64, d1, 1, C + 64, ws, None) == B.ERR_ALIAS       # workspace inside S
 
 
@@ -408,7 +412,7 @@ def test_project_table_validation(lib):
     P = B.packed_input_bytes(64, 64)
 
     def descs(*rows):
-        return (B.ProjectDesc * len(rows))(*[B.ProjectDesc(k0, *row) for row in rows])
+        return (B.ProjectDesc * len(rows))(*[B.ProjectDesc(k0, *row, P) for row in rows])
 
     good = descs((A, 256, 256, None, C), (A, 256, 256, None, C + P))       # one X shared
     assert err(f, 64, 64, good, 2, W, ws - 1, None) == B.ERR_WORKSPACE
@@ -429,3 +433,39 @@ def test_project_table_validation(lib):
     assert err(f, 64, 64, into_x, 2, W, ws, None) == B.ERR_ALIAS               # planes inside X of 0
     assert err(f, 64, 64, good, 2, A + 1024, ws, None) == B.ERR_ALIAS          # workspace inside X
     assert err(f, 64, 64, good, 2, C + 16, ws, None) == B.ERR_ALIAS            # workspace meets planes
+
+
+def test_packed_buffer_sizes_are_checked(lib):
+    """Every descriptor that points at a packed buffer carries its size, and a buffer smaller
+    than the layout needs is rejected before anything is launched (a short buffer would be
+    read past its end)."""
+    W = 0x20000000
+    # accumulate: table and grouped packed, planes one 16-byte chunk short
+    f = lib.logra_sketch_accumulate_table
+    ws = B.sketch_accumulate_table_ws_bytes(1)
+    for pb, want in ((PIN - 16, B.ERR_WORKSPACE), (0, B.ERR_WORKSPACE)):
+        d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64, pb))
+        assert err(f, 128, 64, d1, 1, W, ws, None) == want
+        assert err(lib.logra_sketch_accumulate_grouped_packed, 128, 64, d1, 1, None) == want
+        assert "packed input" in lib.logra_last_error().decode()
+    # planes sized for fewer tokens or a lower rank than the call's
+    small_T = B.packed_input_bytes(64, 64)
+    small_r = B.packed_input_bytes(128, 32)
+    for pb in (small_T, small_r):
+        d1 = (B.AccPackedDesc * 1)(B.AccPackedDesc(A, Bp, C, 64, 64, pb))
+        assert err(f, 128, 64, d1, 1, W, ws, None) == B.ERR_WORKSPACE
+    # table projection: planes too small for T x r
+    g = lib.logra_project_input_table
+    pws = B.project_input_table_ws_bytes(1)
+    d = (B.ProjectDesc * 1)(B.ProjectDesc(B.key(1, 2, 3), A, 256, 256, None, C, B.packed_input_bytes(64, 64) - 16))
+    assert err(g, 64, 64, d, 1, W, pws, None) == B.ERR_WORKSPACE
+    # merges: packed update and explicit projection too small
+    m = lib.logra_merge_grouped_packed
+    d1 = (B.MergePackedDesc * 1)(B.MergePackedDesc(key(), A, 64, 64, 64, Bp, 0, PUP - 16))
+    assert err(m, 64, d1, 1, 1.0, None, 0, 0, None) == B.ERR_WORKSPACE
+    x = lib.logra_merge_grouped_explicit
+    need = B.merge_projection_packed_bytes(8, 64)
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C, 0, PUP, need - 16))
+    assert err(x, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_WORKSPACE
+    d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C, 0, 16, need))
+    assert err(x, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_WORKSPACE
