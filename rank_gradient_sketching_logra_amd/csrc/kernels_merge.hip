@@ -26,6 +26,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <atomic>
+
 namespace logra {
 
 namespace {
@@ -746,18 +748,21 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(KeyArg key, int64_t d, i
 
 }  // namespace
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; concurrent
+// first calls may both query, and store the same value).
 int64_t compute_units() {
-  static int64_t cached[64] = {0};
+  static std::atomic<int64_t> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
+  int64_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
       n = 256;
-    cached[dev] = n;
+    v = n;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double scale,

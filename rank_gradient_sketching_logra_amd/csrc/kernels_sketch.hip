@@ -18,6 +18,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 namespace logra {
@@ -1339,13 +1340,17 @@ template <int NB>
 static hipError_t launch_project_table_nb(const ProjTableEntry* t, unsigned* next, int n,
                                           int64_t T, int64_t r, float cr, int nrb,
                                           hipStream_t s) {
-  static int per_cu = 0;  // resident blocks per compute unit, from the occupancy query
+  // resident blocks per compute unit, from the occupancy query (once; concurrent
+  // first calls store the same value)
+  static std::atomic<int> cached_per_cu{0};
+  int per_cu = cached_per_cu.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int b = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, project_table_kernel<NB>,
                                                                 kPtWaves * 64, 0);
     if (e != hipSuccess) return e;
     per_cu = b > 0 ? b : 1;
+    cached_per_cu.store(per_cu, std::memory_order_relaxed);
   }
   const dim3 grid((unsigned)(per_cu * compute_units()));
   hipLaunchKernelGGL(project_table_kernel<NB>, grid, dim3(kPtWaves * 64), 0, s, t, next, n, T,

@@ -74,14 +74,24 @@ size_t extent(int64_t rows, int64_t cols, int64_t ld, size_t es) {
 
 bool bad_rank(int64_t r) { return r < 1 || r > LOGRA_MAX_RANK; }
 
+// Bounds that keep every byte count the validation forms (extents, T * r * 4,
+// d * k * 2, ...) far inside int64_t / size_t: a dimension or leading
+// dimension is at most 2^40 elements and one matrix at most 2^50 elements.
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+constexpr int64_t kMaxElems = int64_t(1) << 50;
+bool bad_dim(int64_t x) { return x < 1 || x > kMaxDim; }
+
 logra::KeyArg key_words(uint64_t seed, const logra_key* key) {
   return logra::KeyArg{seed, ((uint64_t)key->step << 32) | (uint64_t)key->matrix_id};
 }
 
 // A matrix operand (X, D or W): dtype, alignment of base and rows.
-int check_matrix(const char* name, const void* p, logra_dtype t, int64_t ld, int64_t cols) {
+int check_matrix(const char* name, const void* p, logra_dtype t, int64_t ld, int64_t rows, int64_t cols) {
   if (t != LOGRA_F32 && t != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "%s: dtype must be F32 or BF16", name);
   if (ld < cols) return fail(LOGRA_ERR_SHAPE, "%s: leading dimension %lld < %lld", name, (long long)ld, (long long)cols);
+  if (bad_dim(rows) || bad_dim(cols) || ld > kMaxDim || rows > kMaxElems / ld)
+    return fail(LOGRA_ERR_SHAPE, "%s: %lld x %lld (leading dimension %lld) is out of range", name, (long long)rows,
+                (long long)cols, (long long)ld);
   if (!aligned16(p)) return fail(LOGRA_ERR_ALIGN, "%s: base pointer not 16-byte aligned", name);
   if ((ld * (int64_t)elem_size(t)) % 16 != 0)
     return fail(LOGRA_ERR_ALIGN, "%s: rows not 16-byte aligned (leading dimension %lld)", name, (long long)ld);
@@ -105,7 +115,7 @@ LOGRA_API int logra_regen_A(const logra_key* key, int64_t r, int64_t k, logra_dt
                             void* A, logra_stream stream) {
   LOGRA_TRY
   if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A: NULL key or output");
-  if (bad_rank(r) || k < 1) return fail(LOGRA_ERR_SHAPE, "regen_A: need 1 <= r <= %d and k >= 1", LOGRA_MAX_RANK);
+  if (bad_rank(r) || bad_dim(k)) return fail(LOGRA_ERR_SHAPE, "regen_A: need 1 <= r <= %d and k >= 1", LOGRA_MAX_RANK);
   if (out != LOGRA_I8 && out != LOGRA_F32) return fail(LOGRA_ERR_DTYPE, "regen_A: output must be I8 or F32");
   return hip_status(logra::launch_regen_A(key_words(key->seed, key), r, k, out == LOGRA_I8, A,
                                           static_cast<hipStream_t>(stream)),
@@ -118,8 +128,8 @@ LOGRA_API int logra_project_input(const logra_key* key, int64_t T, int64_t k, in
                                   logra_stream stream) {
   LOGRA_TRY
   if (!key || !X || !XAt) return fail(LOGRA_ERR_NULL, "project_input: NULL pointer");
-  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
-  int st = check_matrix("project_input X", X, x_dtype, ldx, k);
+  if (bad_dim(T) || bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  int st = check_matrix("project_input X", X, x_dtype, ldx, T, k);
   if (st) return st;
   if (!aligned16(XAt)) return fail(LOGRA_ERR_ALIGN, "project_input: XAt not 16-byte aligned");
   if (overlap(range(X, extent(T, k, ldx, elem_size(x_dtype))), range(XAt, (size_t)(T * r) * 4)))
@@ -134,7 +144,7 @@ LOGRA_API int logra_regen_A_gaussian(const logra_key* key, int64_t r, int64_t k,
                                      logra_stream stream) {
   LOGRA_TRY
   if (!key || !A) return fail(LOGRA_ERR_NULL, "regen_A_gaussian: NULL pointer");
-  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "regen_A_gaussian: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "regen_A_gaussian: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (!aligned16(A)) return fail(LOGRA_ERR_ALIGN, "regen_A_gaussian: A not 16-byte aligned");
   return hip_status(logra::launch_regen_A_gaussian(key_words(key->seed, key), r, k, A,
                                                    static_cast<hipStream_t>(stream)),
@@ -143,7 +153,7 @@ LOGRA_API int logra_regen_A_gaussian(const logra_key* key, int64_t r, int64_t k,
 }
 
 LOGRA_API size_t logra_projection_packed_bytes(int64_t r, int64_t k) {
-  if (k < 1 || bad_rank(r)) return 0;
+  if (bad_dim(k) || bad_rank(r)) return 0;
   return logra::projection_packed_bytes(r, k);
 }
 
@@ -151,7 +161,7 @@ LOGRA_API int logra_pack_projection(int64_t r, int64_t k, const float* A, void* 
                                     size_t packed_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_projection: NULL pointer");
-  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::projection_packed_bytes(r, k);
   if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_projection: %zu bytes needed", need);
   if (!aligned16(A_packed)) return fail(LOGRA_ERR_ALIGN, "pack_projection: output not 16-byte aligned");
@@ -168,9 +178,9 @@ LOGRA_API int logra_project_input_explicit(int64_t T, int64_t k, int64_t r, cons
                                            size_t planes_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!X || !A_packed || (!XAt && !planes)) return fail(LOGRA_ERR_NULL, "project_input_explicit: NULL pointer");
-  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_explicit: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_explicit: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_explicit: X must be bf16");
-  int st = check_matrix("project_input_explicit X", X, x_dtype, ldx, k);
+  int st = check_matrix("project_input_explicit X", X, x_dtype, ldx, T, k);
   if (st) return st;
   const size_t aneed = logra::projection_packed_bytes(r, k);
   if (packed_bytes < aneed) return fail(LOGRA_ERR_WORKSPACE, "project_input_explicit: the packed projection needs %zu bytes", aneed);
@@ -197,10 +207,10 @@ LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t
                                                    logra_stream stream) {
   LOGRA_TRY
   if (!G || !A || !A_packed || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine_explicit: NULL pointer");
-  if (d < 1 || k < 1 || bad_rank(r))
+  if (bad_dim(d) || bad_dim(k) || bad_rank(r))
     return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine_explicit: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (g_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "reconstruction_cosine_explicit: G must be bf16");
-  int st = check_matrix("reconstruction_cosine_explicit G", G, g_dtype, ldg, k);
+  int st = check_matrix("reconstruction_cosine_explicit G", G, g_dtype, ldg, d, k);
   if (st) return st;
   const size_t aneed = logra::projection_packed_bytes(r, k);
   if (packed_bytes < aneed) return fail(LOGRA_ERR_WORKSPACE, "reconstruction_cosine_explicit: the packed projection needs %zu bytes", aneed);
@@ -219,7 +229,7 @@ LOGRA_API int logra_reconstruction_cosine_explicit(int64_t d, int64_t k, int64_t
 }
 
 LOGRA_API size_t logra_reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r) {
-  if (d < 1 || k < 1 || bad_rank(r)) return 0;
+  if (bad_dim(d) || bad_dim(k) || bad_rank(r)) return 0;
   return logra::reconstruction_cosine_ws_bytes(d, k, r);
 }
 
@@ -229,9 +239,9 @@ LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64
                                           logra_stream stream) {
   LOGRA_TRY
   if (!key || !G || !out_dev) return fail(LOGRA_ERR_NULL, "reconstruction_cosine: NULL pointer");
-  if (d < 1 || k < 1 || bad_rank(r))
+  if (bad_dim(d) || bad_dim(k) || bad_rank(r))
     return fail(LOGRA_ERR_SHAPE, "reconstruction_cosine: need d, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
-  int st = check_matrix("reconstruction_cosine G", G, g_dtype, ldg, k);
+  int st = check_matrix("reconstruction_cosine G", G, g_dtype, ldg, d, k);
   if (st) return st;
   const size_t need = logra::reconstruction_cosine_ws_bytes(d, k, r);
   if (!ws || ws_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "reconstruction_cosine: workspace of %zu bytes needed", need);
@@ -248,7 +258,7 @@ LOGRA_API int logra_reconstruction_cosine(const logra_key* key, int64_t d, int64
 }
 
 LOGRA_API size_t logra_packed_input_bytes(int64_t T, int64_t r) {
-  if (T < 1 || bad_rank(r)) return 0;
+  if (bad_dim(T) || bad_rank(r)) return 0;
   return logra::acc_ws_bytes_per_item(T, 1, r);
 }
 
@@ -258,9 +268,9 @@ LOGRA_API int logra_project_input_packed(const logra_key* key, int64_t T, int64_
                                          logra_stream stream) {
   LOGRA_TRY
   if (!key || !X || !planes) return fail(LOGRA_ERR_NULL, "project_input_packed: NULL pointer");
-  if (T < 1 || k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_packed: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_packed: need T, k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   if (x_dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "project_input_packed: X must be bf16");
-  int st = check_matrix("project_input_packed X", X, x_dtype, ldx, k);
+  int st = check_matrix("project_input_packed X", X, x_dtype, ldx, T, k);
   if (st) return st;
   const size_t need = logra::acc_ws_bytes_per_item(T, 1, r);
   if (planes_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "project_input_packed: %zu bytes of packed output needed", need);
@@ -286,7 +296,7 @@ LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_projec
   static_assert(LOGRA_MAX_PROJECT_TABLE <= 1024, "the kernel's table limit");
   if (!descs || !ws) return fail(LOGRA_ERR_NULL, "project_input_table: NULL pointer");
   if (n < 1 || n > LOGRA_MAX_PROJECT_TABLE) return fail(LOGRA_ERR_SHAPE, "project_input_table: need 1 <= n <= %d", LOGRA_MAX_PROJECT_TABLE);
-  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "project_input_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t tneed = logra::proj_table_ws_bytes(n);
   if (ws_bytes < tneed) return fail(LOGRA_ERR_WORKSPACE, "project_input_table: workspace of %zu bytes needed", tneed);
   if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "project_input_table: workspace not 16-byte aligned");
@@ -300,10 +310,10 @@ LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_projec
     const logra_project_desc& e = descs[i];
     if (!e.X) return fail(LOGRA_ERR_NULL, "project_input_table: NULL X in descriptor %d", i);
     if (!e.XAt && !e.planes) return fail(LOGRA_ERR_NULL, "project_input_table: descriptor %d has no output", i);
-    if (e.k < 1) return fail(LOGRA_ERR_SHAPE, "project_input_table: k must be >= 1");
+    if (bad_dim(e.k)) return fail(LOGRA_ERR_SHAPE, "project_input_table: k must be >= 1");
     if (e.planes && e.planes_bytes < pneed)
       return fail(LOGRA_ERR_WORKSPACE, "project_input_table: descriptor %d: the packed input needs %zu bytes", i, pneed);
-    int st = check_matrix("project_input_table X", e.X, LOGRA_BF16, e.ldx, e.k);
+    int st = check_matrix("project_input_table X", e.X, LOGRA_BF16, e.ldx, T, e.k);
     if (st) return st;
     if ((e.XAt && !aligned16(e.XAt)) || (e.planes && !aligned16(e.planes)))
       return fail(LOGRA_ERR_ALIGN, "project_input_table: outputs must be 16-byte aligned");
@@ -327,7 +337,7 @@ LOGRA_API int logra_project_input_table(int64_t T, int64_t r, const logra_projec
 }
 
 LOGRA_API size_t logra_sketch_accumulate_ws_bytes(int64_t T, int64_t d, int64_t r) {
-  if (T < 1 || d < 1 || bad_rank(r)) return 0;
+  if (bad_dim(T) || bad_dim(d) || bad_rank(r)) return 0;
   return logra::acc_ws_bytes_per_item(T, d, r);
 }
 
@@ -335,8 +345,8 @@ static int check_acc_item(const char* name, int64_t T, int64_t r, logra_dtype dt
                           int64_t d, int64_t ldd, const float* XAt, const float* S, void* ws,
                           size_t ws_bytes) {
   if (!D || !XAt || !S) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
-  if (d < 1) return fail(LOGRA_ERR_SHAPE, "%s: d must be >= 1", name);
-  int st = check_matrix(name, D, dt, ldd, d);
+  if (bad_dim(d)) return fail(LOGRA_ERR_SHAPE, "%s: d must be >= 1", name);
+  int st = check_matrix(name, D, dt, ldd, T, d);
   if (st) return st;
   if (!aligned16(XAt) || !aligned16(S)) return fail(LOGRA_ERR_ALIGN, "%s: XAt and S must be 16-byte aligned", name);
   const Range rs = range(S, (size_t)(d * r) * 4);
@@ -358,7 +368,7 @@ LOGRA_API int logra_sketch_accumulate(int64_t T, int64_t d, int64_t r, const voi
                                       logra_dtype d_dtype, int64_t ldd, const float* XAt,
                                       float* S, void* ws, size_t ws_bytes, logra_stream stream) {
   LOGRA_TRY
-  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   int st = check_acc_item("sketch_accumulate", T, r, d_dtype, D, d, ldd, XAt, S, ws, ws_bytes);
   if (st) return st;
   logra::AccItem it{D, XAt, S, d, ldd, ws};
@@ -374,7 +384,7 @@ LOGRA_API int logra_sketch_accumulate_grouped(int64_t T, int64_t r, logra_dtype 
   LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need 1 <= n <= %d", LOGRA_MAX_GROUP);
-  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   logra::AccItem items[LOGRA_MAX_GROUP];
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
@@ -403,16 +413,16 @@ LOGRA_API int logra_sketch_accumulate_grouped_packed(int64_t T, int64_t r,
   LOGRA_TRY
   if (!descs) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL descriptors");
   if (n < 1 || n > LOGRA_MAX_GROUP) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need 1 <= n <= %d", LOGRA_MAX_GROUP);
-  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::acc_ws_bytes_per_item(T, 1, r);
   logra::AccItem items[LOGRA_MAX_GROUP];
   for (int i = 0; i < n; ++i) {
     const logra_acc_packed_desc& e = descs[i];
     if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_grouped_packed: NULL pointer in descriptor %d", i);
-    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: d must be >= 1");
+    if (bad_dim(e.d)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_grouped_packed: d must be >= 1");
     if (e.planes_bytes < need)
       return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_grouped_packed: descriptor %d: the packed input needs %zu bytes", i, need);
-    int st = check_matrix("sketch_accumulate_grouped_packed D", e.D, LOGRA_BF16, e.ldd, e.d);
+    int st = check_matrix("sketch_accumulate_grouped_packed D", e.D, LOGRA_BF16, e.ldd, T, e.d);
     if (st) return st;
     if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_grouped_packed: planes and S must be 16-byte aligned");
     const Range rs = range(e.S, (size_t)(e.d * r) * 4);
@@ -438,7 +448,7 @@ LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_ac
   LOGRA_TRY
   if (!descs || !ws) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer");
   if (n < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need n >= 1");
-  if (T < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(T) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: need T >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t tneed = logra::acc_table_ws_bytes(n);
   if (ws_bytes < tneed) return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_table: workspace of %zu bytes needed", tneed);
   if (!aligned16(ws)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_table: workspace not 16-byte aligned");
@@ -449,10 +459,10 @@ LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_ac
   for (int i = 0; i < n; ++i) {
     const logra_acc_packed_desc& e = descs[i];
     if (!e.D || !e.planes || !e.S) return fail(LOGRA_ERR_NULL, "sketch_accumulate_table: NULL pointer in descriptor %d", i);
-    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: d must be >= 1");
+    if (bad_dim(e.d)) return fail(LOGRA_ERR_SHAPE, "sketch_accumulate_table: d must be >= 1");
     if (e.planes_bytes < need)
       return fail(LOGRA_ERR_WORKSPACE, "sketch_accumulate_table: descriptor %d: the packed input needs %zu bytes", i, need);
-    int st = check_matrix("sketch_accumulate_table D", e.D, LOGRA_BF16, e.ldd, e.d);
+    int st = check_matrix("sketch_accumulate_table D", e.D, LOGRA_BF16, e.ldd, T, e.d);
     if (st) return st;
     if (!aligned16(e.planes) || !aligned16(e.S)) return fail(LOGRA_ERR_ALIGN, "sketch_accumulate_table: planes and S must be 16-byte aligned");
     rs[i] = range(e.S, (size_t)(e.d * r) * 4);
@@ -479,7 +489,7 @@ LOGRA_API int logra_sketch_accumulate_table(int64_t T, int64_t r, const logra_ac
 }
 
 LOGRA_API size_t logra_rowadam_ws_bytes(int64_t d) {
-  if (d < 1) return 0;
+  if (bad_dim(d)) return 0;
   return logra::rowadam_ws_bytes(d);
 }
 
@@ -489,7 +499,7 @@ int rowadam_impl(const char* name, int64_t d, int64_t r, const float* S, float* 
                  double beta, double eps, float* U, void* P, size_t P_bytes, void* ws,
                  size_t ws_bytes, logra_stream stream) {
   if (!S || !v || (!U && !P)) return fail(LOGRA_ERR_NULL, "%s: NULL pointer", name);
-  if (d < 1 || r < 1) return fail(LOGRA_ERR_SHAPE, "%s: need d, r >= 1", name);
+  if (bad_dim(d) || bad_dim(r) || d > kMaxElems / r) return fail(LOGRA_ERR_SHAPE, "%s: d x r out of range", name);
   if (P && bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "%s: need r <= %d", name, LOGRA_MAX_RANK);
   if (t < 1) return fail(LOGRA_ERR_DOMAIN, "%s: t counts updates from 1", name);
   if (!(beta >= 0.0 && beta < 1.0)) return fail(LOGRA_ERR_DOMAIN, "%s: beta must be in [0, 1)", name);
@@ -534,7 +544,7 @@ LOGRA_API int logra_rowadam_packed(int64_t d, int64_t r, const float* S, float* 
 }
 
 LOGRA_API size_t logra_rowadam_grouped_ws_bytes(int n, int64_t total_rows) {
-  if (n < 1 || n > LOGRA_MAX_ROWADAM_GROUP || total_rows < n) return 0;
+  if (n < 1 || n > LOGRA_MAX_ROWADAM_GROUP || total_rows < n || total_rows > kMaxElems) return 0;
   return logra::rowadam_grouped_ws_bytes(n, total_rows);
 }
 
@@ -557,7 +567,7 @@ LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* 
   for (int i = 0; i < n; ++i) {
     const logra_rowadam_desc& e = descs[i];
     if (!e.S || !e.v || !e.U_packed) return fail(LOGRA_ERR_NULL, "%s: NULL pointer in descriptor %d", name, i);
-    if (e.d < 1) return fail(LOGRA_ERR_SHAPE, "%s: descriptor %d needs d >= 1", name, i);
+    if (bad_dim(e.d)) return fail(LOGRA_ERR_SHAPE, "%s: descriptor %d needs d >= 1", name, i);
     const size_t pneed = logra::packed_update_bytes(e.d, r);
     if (e.packed_bytes < pneed) return fail(LOGRA_ERR_WORKSPACE, "%s: descriptor %d: the packed update needs %zu bytes", name, i, pneed);
     if (!aligned16(e.S) || !aligned16(e.v) || !aligned16(e.U_packed))
@@ -595,7 +605,7 @@ LOGRA_API int logra_rowadam_packed_grouped(int64_t r, const logra_rowadam_desc* 
 }
 
 LOGRA_API size_t logra_packed_update_bytes(int64_t d, int64_t r) {
-  if (d < 1 || bad_rank(r)) return 0;
+  if (bad_dim(d) || bad_rank(r)) return 0;
   return logra::packed_update_bytes(d, r);
 }
 
@@ -603,7 +613,7 @@ LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_pa
                                 size_t packed_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!U || !U_packed) return fail(LOGRA_ERR_NULL, "pack_update: NULL pointer");
-  if (d < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_update: need d >= 1, 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(d) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_update: need d >= 1, 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::packed_update_bytes(d, r);
   if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_update: the packed update needs %zu bytes", need);
   if (!aligned16(U_packed)) return fail(LOGRA_ERR_ALIGN, "pack_update: the packed update must be 16-byte aligned");
@@ -615,7 +625,7 @@ LOGRA_API int logra_pack_update(int64_t d, int64_t r, const float* U, void* U_pa
 }
 
 LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V) {
-  if (P < 1 || V < 1) return 0;
+  if (bad_dim(P) || bad_dim(V)) return 0;
   return logra::klq_ws_bytes(P, V);
 }
 
@@ -624,7 +634,7 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
                                    size_t ws_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!z || !zdot || !q_dev) return fail(LOGRA_ERR_NULL, "predicted_kl_q: NULL pointer");
-  if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: need P, V >= 1");
+  if (bad_dim(P) || bad_dim(V)) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: need P, V >= 1");
   if (P > 65535) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q: at most 65535 contexts per call");
   if (dtype != LOGRA_F32 && dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "predicted_kl_q: dtype must be F32 or BF16");
   if (!(tau > 0.f) || !std::isfinite(tau)) return fail(LOGRA_ERR_DOMAIN, "predicted_kl_q: tau must be finite and > 0");
@@ -638,7 +648,7 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
 }
 
 LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P) {
-  if (P < 1) return 0;
+  if (bad_dim(P)) return 0;
   return logra::exact_kl_ws_bytes(P);
 }
 
@@ -647,7 +657,7 @@ LOGRA_API int logra_exact_kl(int64_t P, int64_t V, const void* z, const void* zd
                              void* ws, size_t ws_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!z || !zdot || !out_dev) return fail(LOGRA_ERR_NULL, "exact_kl: NULL pointer");
-  if (P < 1 || V < 1) return fail(LOGRA_ERR_SHAPE, "exact_kl: need P, V >= 1");
+  if (bad_dim(P) || bad_dim(V)) return fail(LOGRA_ERR_SHAPE, "exact_kl: need P, V >= 1");
   if (P > 2147483647) return fail(LOGRA_ERR_SHAPE, "exact_kl: too many contexts");
   if (dtype != LOGRA_F32 && dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "exact_kl: dtype must be F32 or BF16");
   if (!(tau > 0.0) || !std::isfinite(tau)) return fail(LOGRA_ERR_DOMAIN, "exact_kl: tau must be finite and > 0");
@@ -755,8 +765,8 @@ int merge_grouped_impl(const char* name, int64_t r, const MergeOperands* ops, in
   for (int i = 0; i < n; ++i) {
     const MergeOperands& e = ops[i];
     if (!e.W || !e.U) return fail(LOGRA_ERR_NULL, "%s: NULL pointer in descriptor %d", name, i);
-    if (e.d < 1 || e.k < 1 || e.row0 < 0) return fail(LOGRA_ERR_SHAPE, "%s: need d, k >= 1 and row0 >= 0", name);
-    int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.k);
+    if (bad_dim(e.d) || bad_dim(e.k) || e.row0 < 0 || e.row0 > kMaxElems) return fail(LOGRA_ERR_SHAPE, "%s: need d, k >= 1 and row0 >= 0", name);
+    int st = check_matrix("merge_grouped W", e.W, LOGRA_BF16, e.ldw, e.d, e.k);
     if (st) return st;
     if (!aligned16(e.U)) return fail(LOGRA_ERR_ALIGN, "%s: U not 16-byte aligned", name);
     if (packed && e.U_bytes < logra::packed_update_bytes(e.d, r))
@@ -823,7 +833,7 @@ LOGRA_API int logra_merge_grouped_packed(int64_t r, const logra_merge_packed_des
 }
 
 LOGRA_API size_t logra_merge_projection_packed_bytes(int64_t r, int64_t k) {
-  if (k < 1 || bad_rank(r)) return 0;
+  if (bad_dim(k) || bad_rank(r)) return 0;
   return logra::merge_projection_packed_bytes(r, k);
 }
 
@@ -831,7 +841,7 @@ LOGRA_API int logra_pack_merge_projection(int64_t r, int64_t k, const float* A, 
                                           size_t packed_bytes, logra_stream stream) {
   LOGRA_TRY
   if (!A || !A_packed) return fail(LOGRA_ERR_NULL, "pack_merge_projection: NULL pointer");
-  if (k < 1 || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_merge_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
+  if (bad_dim(k) || bad_rank(r)) return fail(LOGRA_ERR_SHAPE, "pack_merge_projection: need k >= 1 and 1 <= r <= %d", LOGRA_MAX_RANK);
   const size_t need = logra::merge_projection_packed_bytes(r, k);
   if (packed_bytes < need) return fail(LOGRA_ERR_WORKSPACE, "pack_merge_projection: %zu bytes needed", need);
   if (!aligned16(A_packed)) return fail(LOGRA_ERR_ALIGN, "pack_merge_projection: output not 16-byte aligned");
@@ -868,7 +878,7 @@ LOGRA_API int logra_sync_pack(const logra_key* key, int64_t d, int64_t k, int64_
                               logra_stream stream) {
   LOGRA_TRY
   if (!key || !U || !header || !payload) return fail(LOGRA_ERR_NULL, "sync_pack: NULL pointer");
-  if (d < 1 || k < 1 || bad_rank(r) || row0 < 0)
+  if (bad_dim(d) || bad_dim(k) || bad_rank(r) || row0 < 0 || row0 > kMaxElems)
     return fail(LOGRA_ERR_SHAPE, "sync_pack: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
   if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "sync_pack: unknown rounding mode");
   if (!std::isfinite(scale)) return fail(LOGRA_ERR_DOMAIN, "sync_pack: scale must be finite");
@@ -904,7 +914,7 @@ LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream
     if (!h || !descs[i].payload || !descs[i].W) return fail(LOGRA_ERR_NULL, "sync_apply: NULL pointer in descriptor %d", i);
     if (h->magic != LOGRA_SYNC_MAGIC || h->version != LOGRA_SYNC_VERSION)
       return fail(LOGRA_ERR_DOMAIN, "sync_apply: descriptor %d has no valid header", i);
-    if (h->d < 1 || h->k < 1 || bad_rank(h->r) || h->payload_bytes != logra::packed_update_bytes(h->d, h->r))
+    if (bad_dim(h->d) || bad_dim(h->k) || bad_rank(h->r) || h->payload_bytes != logra::packed_update_bytes(h->d, h->r))
       return fail(LOGRA_ERR_DOMAIN, "sync_apply: header %d sizes are inconsistent", i);
     if (h->r != descs[0].header->r || h->mode != descs[0].header->mode || h->sr_seed != descs[0].header->sr_seed)
       return fail(LOGRA_ERR_SHAPE, "sync_apply: descriptors must share r, mode and sr_seed");
@@ -923,8 +933,8 @@ LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r,
                           int64_t row0, logra_stream stream) {
   LOGRA_TRY
   if (!key || !W || !U) return fail(LOGRA_ERR_NULL, "merge: NULL pointer");
-  if (d < 1 || k < 1 || bad_rank(r) || row0 < 0) return fail(LOGRA_ERR_SHAPE, "merge: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
-  int st = check_matrix("merge W", W, w_dtype, ldw, k);
+  if (bad_dim(d) || bad_dim(k) || bad_rank(r) || row0 < 0 || row0 > kMaxElems) return fail(LOGRA_ERR_SHAPE, "merge: need d, k >= 1, 1 <= r <= %d, row0 >= 0", LOGRA_MAX_RANK);
+  int st = check_matrix("merge W", W, w_dtype, ldw, d, k);
   if (st) return st;
   if (mode != LOGRA_ROUND_NEAREST && mode != LOGRA_ROUND_STOCHASTIC) return fail(LOGRA_ERR_DOMAIN, "merge: unknown rounding mode");
   if (w_dtype == LOGRA_F32 && mode == LOGRA_ROUND_STOCHASTIC)
