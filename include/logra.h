@@ -673,6 +673,27 @@ typedef struct logra_sync_desc {
  * or sr_seed; otherwise as logra_merge_grouped_packed. */
 LOGRA_API int logra_sync_apply(const logra_sync_desc* descs, int n, logra_stream stream);
 
+/* ------------------------------------------------- measurement helper */
+
+typedef enum logra_probe {
+  LOGRA_PROBE_READ = 0,  /* read src                    */
+  LOGRA_PROBE_COPY = 1   /* copy src to dst             */
+} logra_probe;
+
+/* Not a step of the method: a streaming read of `bytes` of src, or a copy of
+ * them to dst, with 16-byte accesses spread over every compute unit
+ * (blocks_per_cu blocks of 256 threads per unit, grid-strided, non-temporal).
+ * Timed by the caller, it gives the read and copy ceilings the kernels are
+ * measured against, and a transfer of known size to calibrate HBM byte
+ * counters with.  READ writes 4 KiB of fold values to dst (their values are
+ * meaningless).  bytes must be a positive multiple of 16; blocks_per_cu in
+ * [1, 32].
+ * Errors: NULL pointers; bytes not a positive multiple of 16 or above 2^50;
+ * blocks_per_cu out of range; unknown mode; src or dst not 16-byte aligned;
+ * src and dst overlapping. */
+LOGRA_API int logra_bandwidth_probe(logra_probe mode, const void* src, void* dst, size_t bytes,
+                                    int blocks_per_cu, logra_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

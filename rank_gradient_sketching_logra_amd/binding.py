@@ -145,6 +145,7 @@ SIGNATURES = {
                                            c_void_p, c_int, c_uint64, c_void_p]),
     "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                             c_void_p, c_double, c_void_p, c_int, c_uint64, c_int64, c_void_p]),
+    "logra_bandwidth_probe": (c_int, [c_int, c_void_p, c_void_p, c_size_t, c_int, c_void_p]),
 }
 
 _lib_handle = None
@@ -658,3 +659,18 @@ def sketch_accumulate_table(items, r: int, ws=None, stream=None):
         ws = _scratch(sketch_accumulate_table_ws_bytes(n), items[0][0].device, stream)
     _check(lib().logra_sketch_accumulate_table(T, r, descs, n, _ptr(ws), ws.numel(),
                                                _stream(items[0][0], stream)))
+
+
+PROBE_READ, PROBE_COPY = 0, 1
+
+
+def bandwidth_probe(mode: str, src: torch.Tensor, dst: torch.Tensor, blocks_per_cu: int = 4, stream=None):
+    """Stream src ("read"; dst takes 4 KiB of fold values) or copy it into dst ("copy"): the
+    measurement helper, not a step of the method."""
+    m = PROBE_READ if mode == "read" else PROBE_COPY if mode == "copy" else -1
+    nbytes = _nbytes(src)
+    if mode == "read" and _nbytes(dst) < 4096:
+        raise ValueError("the read probe writes 4 KiB to dst")
+    if mode == "copy" and _nbytes(dst) < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check(lib().logra_bandwidth_probe(m, _ptr(src), _ptr(dst), nbytes, blocks_per_cu, _stream(src, stream)))

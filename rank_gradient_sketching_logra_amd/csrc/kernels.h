@@ -73,6 +73,12 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
 // Compute units of the current device.
 int64_t compute_units();
 
+// Streaming probe: read `bytes` of src (one 16-byte word per block into dst's
+// 256 slots) or copy them to dst; blocks_per_cu blocks of 256 threads per
+// compute unit.
+hipError_t launch_probe(bool copy, const void* src, void* dst, int64_t bytes, int blocks_per_cu,
+                        hipStream_t s);
+
 // cos(G, (G A^T) A) and its parts {cos, ||G||^2, ||G A^T||^2, ||G A^T A||^2}
 // written to out (4 doubles on the device).
 size_t reconstruction_cosine_ws_bytes(int64_t d, int64_t k, int64_t r);

@@ -951,4 +951,21 @@ LOGRA_API int logra_merge(const logra_key* key, int64_t d, int64_t k, int64_t r,
   LOGRA_CATCH("merge")
 }
 
+LOGRA_API int logra_bandwidth_probe(logra_probe mode, const void* src, void* dst, size_t bytes,
+                                    int blocks_per_cu, logra_stream stream) {
+  LOGRA_TRY
+  if (!src || !dst) return fail(LOGRA_ERR_NULL, "bandwidth_probe: NULL pointer");
+  if (mode != LOGRA_PROBE_READ && mode != LOGRA_PROBE_COPY) return fail(LOGRA_ERR_DOMAIN, "bandwidth_probe: unknown mode");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 50))
+    return fail(LOGRA_ERR_SHAPE, "bandwidth_probe: bytes must be a positive multiple of 16, at most 2^50");
+  if (blocks_per_cu < 1 || blocks_per_cu > 32) return fail(LOGRA_ERR_SHAPE, "bandwidth_probe: need 1 <= blocks_per_cu <= 32");
+  if (!aligned16(src) || !aligned16(dst)) return fail(LOGRA_ERR_ALIGN, "bandwidth_probe: src and dst must be 16-byte aligned");
+  const size_t dbytes = mode == LOGRA_PROBE_COPY ? bytes : 4096;
+  if (overlap(range(src, bytes), range(dst, dbytes))) return fail(LOGRA_ERR_ALIAS, "bandwidth_probe: src and dst overlap");
+  return hip_status(logra::launch_probe(mode == LOGRA_PROBE_COPY, src, dst, (int64_t)bytes, blocks_per_cu,
+                                        static_cast<hipStream_t>(stream)),
+                    "bandwidth_probe launch");
+  LOGRA_CATCH("bandwidth_probe")
+}
+
 }  // extern "C"

@@ -469,3 +469,16 @@ def test_packed_buffer_sizes_are_checked(lib):
     assert err(x, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_WORKSPACE
     d1 = (B.MergeExplicitDesc * 1)(B.MergeExplicitDesc(key(), A, 64, 64, 64, Bp, C, 0, 16, need))
     assert err(x, 8, d1, 1, 1.0, None, 0, 0, None) == B.ERR_WORKSPACE
+
+
+def test_bandwidth_probe_validation(lib):
+    f = lib.logra_bandwidth_probe
+    assert err(f, 0, None, Bp, 1 << 20, 4, None) == B.ERR_NULL
+    assert err(f, 2, A, Bp, 1 << 20, 4, None) == B.ERR_DOMAIN             # unknown mode
+    assert err(f, 0, A, Bp, 0, 4, None) == B.ERR_SHAPE
+    assert err(f, 0, A, Bp, 1000, 4, None) == B.ERR_SHAPE                 # not a multiple of 16
+    assert err(f, 0, A, Bp, 1 << 20, 0, None) == B.ERR_SHAPE
+    assert err(f, 0, A, Bp, 1 << 20, 33, None) == B.ERR_SHAPE
+    assert err(f, 1, A + 8, Bp, 1 << 20, 4, None) == B.ERR_ALIGN
+    assert err(f, 1, A, A + (1 << 19), 1 << 20, 4, None) == B.ERR_ALIAS   # copy onto itself
+    assert err(f, 0, A, A + 4096, 1 << 20, 4, None) == B.ERR_ALIAS        # fold slots inside src

@@ -19,7 +19,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "rank_gradient_sketching_logra_amd", "csrc")
 OUT = os.path.join(ROOT, "_build", "sanitize")
-SOURCES = ["logra_abi.hip", "kernels_sketch.hip", "kernels_merge.hip", "kernels_opt.hip", "kernels_diag.hip"]
+SOURCES = ["logra_abi.hip", "kernels_sketch.hip", "kernels_merge.hip", "kernels_opt.hip", "kernels_diag.hip",
+           "kernels_probe.hip"]
 DRIVER = os.path.join(ROOT, "tests", "abi_sanitize", "abi_driver.cpp")
 HIPCC = "/opt/rocm/bin/hipcc"
 # sanitizers on the host side only (the device side is not compiled at all here)

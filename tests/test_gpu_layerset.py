@@ -1,0 +1,204 @@
+"""GPU parity of whole updates over full-size layer sets, through the call sequence the
+benchmark times (rank_gradient_sketching_logra_amd.update): table projections of every
+matrix of every layer with fused shared-input entries and widest-first items, table
+accumulates with the layers reversed and per-XCD tile claiming, one grouped RowAdam into
+packed updates, q and alpha on the device, and one grouped merge per layer.
+
+Every layer of the set takes part in every launch, so the launches have the benchmark's
+shape.  Layers {0, L/2, L-1} carry seeded host inputs and are checked against the oracle
+("LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient Sketches", §2.1-2.3):
+S and U in full (relative Frobenius error and the largest per-row relative error), q and
+alpha, and sampled rows of every merged weight.  The other layers carry device-random
+inputs of the same shapes; they are not checked.  Two microbatches per update.
+
+Bounds: S and U relative Frobenius <= 5e-5 and every row <= 2e-4 (the contract is 2e-3);
+q and alpha <= 1e-4 relative; merged W within 1 bf16 ulp of the oracle on >= 99.99% of
+the sampled elements and identical on >= 99.9%.  The merge is checked twice: with the
+step the update computes (alpha from q), and again with alpha = 1, where the update is a
+few bf16 units of W and every rounding decision is exercised.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import philox
+from rank_gradient_sketching_logra_amd import binding as B
+from rank_gradient_sketching_logra_amd import synth
+from rank_gradient_sketching_logra_amd import update as UPD
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MICROBATCHES = 2
+# the synthetic input each shared layer input is drawn as
+INPUT_KIND = {"att": "q", "o": "o", "mlp": "gate", "down": "down"}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def relfro(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / (nb if nb > 0 else 1.0))
+
+
+def row_rel_max(a, b):
+    """Largest relative error of one row (rows of b that are zero are skipped)."""
+    num = np.linalg.norm(np.asarray(a, np.float64) - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    keep = den > 0
+    return float((num[keep] / den[keep]).max()) if keep.any() else 0.0
+
+
+def decode_packed_update(P: torch.Tensor, d: int, r: int) -> np.ndarray:
+    """U from the merge's packed update: per 32-row band and 16-rank step a hi then a lo slab of
+    64 lanes x 8 bf16, lane l holding row 32g + (l & 31), ranks 16s + 8(l >> 5) + i; U = hi + lo."""
+    ks = 1
+    while 16 * ks < r:
+        ks *= 2
+    nb = (d + 31) // 32
+    bits = P.cpu().numpy().view(np.uint16)[: nb * ks * 2 * 64 * 8].reshape(nb, ks, 2, 2, 32, 8)
+    vals = oracle.bf16_bits_to_f64(bits)
+    u = vals[:, :, 0] + vals[:, :, 1]                       # [band, step, half, row, i]
+    u = u.transpose(0, 3, 1, 2, 4).reshape(nb * 32, ks * 16)
+    return u[:d, :r]
+
+
+def ulp_check(got_bits, want_bits):
+    g = oracle.bf16_bits_to_f64(got_bits)
+    wv = oracle.bf16_bits_to_f64(want_bits)
+    return (np.abs(g - wv) <= oracle.ulp_bf16(wv)).mean(), (got_bits == want_bits).mean()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("workload", ["qwen2.5-7b-set-r64", "qwen2.5-1.5b-set-r64", "dense-27b-set-r256"])
+def test_layer_set_update_through_the_benchmark_sequence(workload):
+    w = synth.BY_NAME[workload]
+    L, T, r, M = w.layers, w.T, w.r, MICROBATCHES
+    kinds = tuple(w.kinds)
+    layers = list(range(L))
+    sampled = sorted({0, L // 2, L - 1})
+    say(f"{workload}: {L} layers, r={r}, T={T} x {M} microbatches; checked layers {sampled}")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4321)
+
+    def rnd(shape, std):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        t.normal_(0.0, std, generator=gen)
+        return t
+
+    width = {grp: w.shapes[kd][1] for grp, kd in INPUT_KIND.items()}
+    fill_x = {grp: rnd((T, width[grp]), 1.0) for grp in INPUT_KIND}
+    fill_d = {kd: rnd((T, d), 1e-3) for kd, (d, k) in w.shapes.items()}
+    Xh, Dh, X, D = {}, {}, {}, {}
+    for l in sampled:
+        for mb in range(M):
+            for grp, kd in INPUT_KIND.items():
+                Xh[(l, grp, mb)] = synth.layer_input(w, l, kd, mb)
+                X[(l, grp, mb)] = bf16_dev(Xh[(l, grp, mb)])
+            for kd in kinds:
+                Dh[(l, kd, mb)] = synth.output_grad(w, l, kd, mb)
+                D[(l, kd, mb)] = bf16_dev(Dh[(l, kd, mb)])
+    say("  inputs ready")
+
+    def x_of(mb):
+        return lambda l, kd: X.get((l, UPD.SHARED_INPUT[kd], mb), fill_x[UPD.SHARED_INPUT[kd]])
+
+    def d_of(mb):
+        return lambda l, kd: D.get((l, kd, mb), fill_d[kd])
+
+    pbytes = B.packed_input_bytes(T, r)
+    PL = {(l, kd, mb): torch.empty((pbytes,), dtype=torch.uint8, device=DEV)
+          for l in layers for kd in kinds for mb in range(M)}
+    S = {(l, kd): torch.zeros((w.shapes[kd][0], r), dtype=torch.float32, device=DEV) for l in layers for kd in kinds}
+    V = {(l, kd): torch.zeros((w.shapes[kd][0],), dtype=torch.float32, device=DEV) for l in layers for kd in kinds}
+    UPK = {(l, kd): torch.empty((B.packed_update_bytes(w.shapes[kd][0], r),), dtype=torch.uint8, device=DEV)
+           for l in layers for kd in kinds}
+    keys = {(l, kd): B.key(w.seed, 7 * l + synth.KINDS.index(kd), w.step) for l in layers for kd in kinds}
+    n = L * len(kinds)
+    proj_ws = B.workspace(B.project_input_table_ws_bytes(n), DEV)
+    acc_ws = B.workspace(B.sketch_accumulate_table_ws_bytes(n), DEV)
+    ra_ws = B.workspace(B.rowadam_grouped_ws_bytes(n, sum(s.shape[0] for s in S.values())), DEV)
+    key_of = lambda l, kd: keys[(l, kd)]
+    for mb in range(M):
+        UPD.project(layers, kinds, key_of, x_of(mb), lambda l, kd, mb=mb: PL[(l, kd, mb)], r, proj_ws)
+    for mb in range(M):
+        UPD.accumulate(layers, kinds, d_of(mb), lambda l, kd, mb=mb: PL[(l, kd, mb)], lambda l, kd: S[(l, kd)],
+                       r, acc_ws)
+    UPD.optimise([(S[key_], V[key_], UPK[key_]) for key_ in S], r, 1, w.beta, w.eps, ra_ws)
+    alpha = None
+    if w.P:
+        zb, zdb = synth.kl_inputs(w)
+        q = torch.empty((1,), dtype=torch.float32, device=DEV)
+        alpha = torch.empty((1,), dtype=torch.float32, device=DEV)
+        UPD.step_size(bf16_dev(zb), bf16_dev(zdb), w.tau, w.delta, w.alpha_max, q, alpha,
+                      B.workspace(B.predicted_kl_q_ws_bytes(w.P, w.V), DEV))
+    Wd = {}
+    for l in layers:
+        for kd in kinds:
+            d, k = w.shapes[kd]
+            Wd[(l, kd)] = bf16_dev(synth.weight(w, l, kd)) if l in sampled else rnd((d, k), 0.02)
+    W0 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
+    UPD.merge(layers, kinds, key_of, lambda l, kd: Wd[(l, kd)], lambda l, kd: UPK[(l, kd)], r, w.eta, alpha,
+              w.rounding, w.sr_seed)
+    W1 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
+    UPD.merge(layers, kinds, key_of, lambda l, kd: Wd[(l, kd)], lambda l, kd: UPK[(l, kd)], r, w.eta, None,
+              w.rounding, w.sr_seed)
+    W2 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
+    torch.cuda.synchronize()
+    say("  GPU update done")
+
+    # q and alpha against the oracle
+    a_dev = 1.0
+    if w.P:
+        q_h = oracle.predicted_kl_q(oracle.bf16_bits_to_f64(zb), oracle.bf16_bits_to_f64(zdb), w.tau)
+        a_h = oracle.step_alpha(q_h, w.delta, w.alpha_max)
+        say(f"  q {q.item():.7g} (oracle {q_h:.7g}), alpha {alpha.item():.7g} (oracle {a_h:.7g}), P={w.P} V={w.V}")
+        assert q.item() == pytest.approx(q_h, rel=1e-4)
+        assert alpha.item() == pytest.approx(a_h, rel=1e-4)
+        a_dev = float(alpha.item())
+
+    rs = np.random.default_rng(7)
+    for l in sampled:
+        # the oracle's projected inputs of this layer, one per (shared input, microbatch) and matrix
+        for kd in kinds:
+            mid = 7 * l + synth.KINDS.index(kd)
+            d, k = w.shapes[kd]
+            A = oracle.regen_A(w.seed, mid, w.step, r, k)
+            S_h = np.zeros((d, r))
+            for mb in range(M):
+                XAt = oracle.project(oracle.bf16_bits_to_f64(Xh[(l, UPD.SHARED_INPUT[kd], mb)]), A)
+                S_h = oracle.accumulate(S_h, oracle.bf16_bits_to_f64(Dh[(l, kd, mb)]), XAt)
+            S_g = S[(l, kd)].cpu().numpy()
+            e_s, e_sr = relfro(S_g, S_h), row_rel_max(S_g, S_h)
+            U_h, _ = oracle.rowadam(S_h, np.zeros(d), 1, w.beta, w.eps)
+            U_g = decode_packed_update(UPK[(l, kd)], d, r)
+            e_u, e_ur = relfro(U_g, U_h), row_rel_max(U_g, U_h)
+            rows = np.unique(np.concatenate([[0, d - 1], rs.integers(0, d, 24)]))
+            u = (np.concatenate([philox.sr_draws(w.sr_seed, mid, w.step, 1, k, row0=int(i)) for i in rows])
+                 if w.rounding == "stochastic" else None)
+            Ar = A
+            want1 = oracle.merge(oracle.bf16_bits_to_f64(W0[(l, kd)][rows]), U_h[rows], Ar, w.eta * a_dev,
+                                 w_dtype="bf16", mode=w.rounding, u_draws=u)
+            f1, x1 = ulp_check(W1[(l, kd)][rows], want1)
+            want2 = oracle.merge(oracle.bf16_bits_to_f64(W1[(l, kd)][rows]), U_h[rows], Ar, w.eta,
+                                 w_dtype="bf16", mode=w.rounding, u_draws=u)
+            f2, x2 = ulp_check(W2[(l, kd)][rows], want2)
+            changed = float((W2[(l, kd)][rows] != W1[(l, kd)][rows]).mean())
+            say(f"  layer {l} {kd:4s} {d}x{k}: S fro {e_s:.2e} row {e_sr:.2e}; U fro {e_u:.2e} row {e_ur:.2e}; "
+                f"W step 1 ulp {f1:.5f} same {x1:.5f}; W alpha=1 ulp {f2:.5f} same {x2:.5f} (changed {changed:.3f})")
+            assert e_s <= 5e-5 and e_sr <= 2e-4
+            assert e_u <= 5e-5 and e_ur <= 2e-4
+            assert f1 >= 0.9999 and x1 >= 0.999
+            assert f2 >= 0.9999 and x2 >= 0.999
+            assert changed > 0.5          # the alpha = 1 step moves most weights

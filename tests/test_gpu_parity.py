@@ -980,10 +980,11 @@ def test_whole_update_matches_oracle(workload):
 def test_full_size_layer_sampled(workload, layer):
     """One full-size layer (q, k, v, o, gate, up, down; 1.5B and 7B shapes at r = 64, 27B
     shapes at r = 256; T = 4096; first, middle or last layer, so each matrix has its own key)
-    through the entry points and launch configuration the benchmark times: projections
-    straight into packed operands, one grouped packed accumulate, one grouped merge from
-    packed updates with the step size on the device.  S is checked on sampled rows of every
-    matrix against the oracle's X A^T and D^T (X A^T); W on sampled rows of every matrix."""
+    through the single-layer entry points: projections straight into packed operands, one
+    grouped packed accumulate, one grouped merge from packed updates with the step size on
+    the device.  (The table launches the benchmark times are checked at full size in
+    test_gpu_layerset.py.)  S is checked on sampled rows of every matrix against the
+    oracle's X A^T and D^T (X A^T); W on sampled rows of every matrix."""
     w = synth.BY_NAME[workload]
     T, r = w.T, w.r
     say(f"full-size layer {layer} of {workload}, sampled (bench configuration)")
