@@ -201,7 +201,7 @@ def measure_ceilings(B, torch, dev):
     dst = torch.empty((half,), dtype=torch.uint8, device=dev)
     best = {"read": (0.0, 0), "copy": (0.0, 0)}
     for mode in ("read", "copy"):
-        for bpc in (2, 4, 8):
+        for bpc in (1, 2, 4, 8):
             a = src if mode == "read" else src[:half]
             o = sink if mode == "read" else dst
             B.bandwidth_probe(mode, a, o, bpc)
@@ -218,7 +218,7 @@ def measure_ceilings(B, torch, dev):
     del src, dst, sink
     return {"read_gbs": round(best["read"][0], 1), "copy_gbs": round(best["copy"][0], 1),
             "read_blocks_per_cu": best["read"][1], "copy_blocks_per_cu": best["copy"][1],
-            "bytes": PROBE_BYTES, "probe": "logra_bandwidth_probe (16-byte non-temporal accesses, grid-strided)"}
+            "bytes": PROBE_BYTES, "probe": "logra_bandwidth_probe (16-byte accesses, non-temporal loads, grid-strided)"}
 
 
 def roofline(name, per_launch_bytes, per_launch_flops, launch_us):

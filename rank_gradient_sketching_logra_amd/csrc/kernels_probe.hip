@@ -45,6 +45,7 @@ __global__ void __launch_bounds__(kProbeThreads) probe_read_kernel(const u32x4* 
   }
 }
 
+// Copy: non-temporal loads, plain stores (the faster pair on this part).
 __global__ void __launch_bounds__(kProbeThreads) probe_copy_kernel(const u32x4* __restrict__ src,
                                                                   u32x4* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(kProbeThreads) probe_copy_kernel(const u32x4* 
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+    for (int u = 0; u < kProbeUnroll; ++u) dst[i + u * stride] = v[u];
   }
   for (; i < n16; i += stride) dst[i] = src[i];
 }
