@@ -411,6 +411,22 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
                                    logra_dtype dtype, float tau, float* q_dev,
                                    void* ws, size_t ws_bytes, logra_stream stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): logra_predicted_kl_q
+ * with no workspace argument, the same result bits.  The partial moments go to
+ * a scratch array the library holds on each GPU (LOGRA_NOALLOC_MAX_CONTEXTS
+ * contexts, 512 bytes each: 2 MiB per GPU, held until the process ends); its
+ * device address is looked up once per device, on the first call there.  The
+ * call allocates nothing.  Calls on one GPU share that array, so calls that
+ * overlap in time on one GPU (on two streams, or from two threads) race;
+ * calls in one stream, or on different GPUs, do not.
+ * Errors: as logra_predicted_kl_q; P > LOGRA_NOALLOC_MAX_CONTEXTS
+ * (LOGRA_ERR_SHAPE); the scratch address unavailable (LOGRA_ERR_HIP). */
+#define LOGRA_NOALLOC_MAX_CONTEXTS 4096
+LOGRA_API int logra_predicted_kl_q_noalloc(int64_t P, int64_t V, const void* z, const void* zdot,
+                                           logra_dtype dtype, float tau, float* q_dev,
+                                           logra_stream stream);
+
 /* Workspace bytes of logra_exact_kl for P contexts. */
 LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P);
 
@@ -682,7 +698,8 @@ typedef enum logra_probe {
 
 /* Not a step of the method: a streaming read of `bytes` of src, or a copy of
  * them to dst, with 16-byte accesses spread over every compute unit
- * (blocks_per_cu blocks of 256 threads per unit, grid-strided, non-temporal).
+ * (blocks_per_cu blocks of 256 threads per unit, grid-strided, non-temporal
+ * loads).
  * Timed by the caller, it gives the read and copy ceilings the kernels are
  * measured against, and a transfer of known size to calibrate HBM byte
  * counters with.  READ writes 4 KiB of fold values to dst (their values are

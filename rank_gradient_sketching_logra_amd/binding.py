@@ -146,6 +146,8 @@ SIGNATURES = {
     "logra_merge": (c_int, [POINTER(Key), c_int64, c_int64, c_int64, c_void_p, c_int, c_int64,
                             c_void_p, c_double, c_void_p, c_int, c_uint64, c_int64, c_void_p]),
     "logra_bandwidth_probe": (c_int, [c_int, c_void_p, c_void_p, c_size_t, c_int, c_void_p]),
+    "logra_predicted_kl_q_noalloc": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_int, c_float,
+                                             c_void_p, c_void_p]),
 }
 
 _lib_handle = None
@@ -380,6 +382,21 @@ def predicted_kl_q(z: torch.Tensor, zdot: torch.Tensor, tau: float, out=None, ws
     _check(lib().logra_predicted_kl_q(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), tau, _ptr(q),
                                       _ptr(ws), ws.numel(), _stream(z, stream)))
     return q
+
+
+NOALLOC_MAX_CONTEXTS = 4096
+
+
+def predicted_kl_q_noalloc(z: torch.Tensor, zdot: torch.Tensor, tau: float, out: torch.Tensor,
+                           stream=None):
+    """q on the device with no workspace: the library's per-GPU scratch holds the partials (for
+    callers that cannot allocate).  out is the caller's one-element fp32 tensor; nothing is
+    allocated here."""
+    P, V = z.shape
+    _need_dtype("zdot", zdot, z.dtype)
+    _check(lib().logra_predicted_kl_q_noalloc(P, V, _ptr(z), _ptr(zdot), _dtype_code(z), tau, _ptr(out),
+                                              _stream(z, stream)))
+    return out
 
 
 def step_alpha(q: float, delta: float, alpha_max: float) -> float:

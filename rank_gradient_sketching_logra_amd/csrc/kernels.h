@@ -111,6 +111,11 @@ hipError_t launch_exact_kl(int64_t P, int64_t V, const void* z, const void* zd, 
                            double alpha, double tau, double* out, void* ws, hipStream_t s);
 
 size_t klq_ws_bytes(int64_t P, int64_t V);
+// The same q with the partials in the library's per-GPU scratch array (no
+// workspace, no allocation); at most noalloc_max_contexts() contexts.
+int64_t noalloc_max_contexts();
+hipError_t launch_predicted_kl_q_noalloc(int64_t P, int64_t V, const void* z, const void* zd,
+                                         bool bf16, float tau, float* q, hipStream_t s);
 hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zd,
                                  bool bf16, float tau, float* q, void* ws, hipStream_t s);
 hipError_t launch_step_alpha(const float* q, float delta, float amax, float* alpha,

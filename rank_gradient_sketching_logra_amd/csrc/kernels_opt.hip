@@ -13,6 +13,7 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <atomic>
 #include <cmath>
 #include <vector>
 
@@ -546,6 +547,46 @@ hipError_t launch_predicted_kl_q(int64_t P, int64_t V, const void* z, const void
   const double scale = 1.0 / (2.0 * (double)P * (double)tau * (double)tau);
   hipLaunchKernelGGL(klq_final_kernel, dim3(1), dim3(256), 0, s, P, part, scale, q);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free q: the per-chunk partial moments of up to
+// kNoAllocMaxContexts contexts.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` is only a stand-in for
+// the symbol: the device address comes from hipGetSymbolAddress, per device.
+constexpr int64_t kNoAllocMaxContexts = 4096;
+static __device__ __align__(256) double scratch[kNoAllocMaxContexts * kKlqChunks * 4];
+
+int64_t noalloc_max_contexts() { return kNoAllocMaxContexts; }
+
+// The current device's address of `scratch`, looked up once per device (a
+// concurrent first call on the same device looks it up too and stores the
+// same address).
+static hipError_t scratch_address(void** out) {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_predicted_kl_q_noalloc(int64_t P, int64_t V, const void* z, const void* zd,
+                                         bool bf16, float tau, float* q, hipStream_t s) {
+  if (P < 1 || P > kNoAllocMaxContexts) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // Every partial the final pass reads is written by this call's first pass
+  // (P x kKlqChunks entries), so nothing needs clearing.
+  return launch_predicted_kl_q(P, V, z, zd, bf16, tau, q, ws, s);
 }
 
 size_t exact_kl_ws_bytes(int64_t P) { return (size_t)P * sizeof(double); }

@@ -647,6 +647,24 @@ LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const vo
   LOGRA_CATCH("predicted_kl_q")
 }
 
+LOGRA_API int logra_predicted_kl_q_noalloc(int64_t P, int64_t V, const void* z, const void* zdot,
+                                           logra_dtype dtype, float tau, float* q_dev,
+                                           logra_stream stream) {
+  LOGRA_TRY
+  static_assert(LOGRA_NOALLOC_MAX_CONTEXTS == 4096, "the scratch array's size");
+  if (!z || !zdot || !q_dev) return fail(LOGRA_ERR_NULL, "predicted_kl_q_noalloc: NULL pointer");
+  if (bad_dim(P) || bad_dim(V)) return fail(LOGRA_ERR_SHAPE, "predicted_kl_q_noalloc: need P, V >= 1");
+  if (P > logra::noalloc_max_contexts())
+    return fail(LOGRA_ERR_SHAPE, "predicted_kl_q_noalloc: at most %d contexts per call", LOGRA_NOALLOC_MAX_CONTEXTS);
+  if (dtype != LOGRA_F32 && dtype != LOGRA_BF16) return fail(LOGRA_ERR_DTYPE, "predicted_kl_q_noalloc: dtype must be F32 or BF16");
+  if (!(tau > 0.f) || !std::isfinite(tau)) return fail(LOGRA_ERR_DOMAIN, "predicted_kl_q_noalloc: tau must be finite and > 0");
+  if (!aligned16(z) || !aligned16(zdot)) return fail(LOGRA_ERR_ALIGN, "predicted_kl_q_noalloc: z and zdot must be 16-byte aligned");
+  return hip_status(logra::launch_predicted_kl_q_noalloc(P, V, z, zdot, dtype == LOGRA_BF16, tau, q_dev,
+                                                         static_cast<hipStream_t>(stream)),
+                    "predicted_kl_q_noalloc launch");
+  LOGRA_CATCH("predicted_kl_q_noalloc")
+}
+
 LOGRA_API size_t logra_exact_kl_ws_bytes(int64_t P) {
   if (bad_dim(P)) return 0;
   return logra::exact_kl_ws_bytes(P);

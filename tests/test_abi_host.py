@@ -482,3 +482,16 @@ def test_bandwidth_probe_validation(lib):
     assert err(f, 1, A + 8, Bp, 1 << 20, 4, None) == B.ERR_ALIGN
     assert err(f, 1, A, A + (1 << 19), 1 << 20, 4, None) == B.ERR_ALIAS   # copy onto itself
     assert err(f, 0, A, A + 4096, 1 << 20, 4, None) == B.ERR_ALIAS        # fold slots inside src
+
+
+def test_predicted_kl_noalloc_validation(lib):
+    """The allocation-free q takes no workspace and rejects more contexts than its scratch holds."""
+    f = lib.logra_predicted_kl_q_noalloc
+    assert err(f, 4, 512, None, Bp, B.BF16, 1.0, C, None) == B.ERR_NULL
+    assert err(f, 0, 512, A, Bp, B.BF16, 1.0, C, None) == B.ERR_SHAPE
+    assert err(f, B.NOALLOC_MAX_CONTEXTS + 1, 8, A, Bp, B.BF16, 1.0, C, None) == B.ERR_SHAPE
+    assert err(f, 4, 512, A, Bp, B.I8, 1.0, C, None) == B.ERR_DTYPE
+    assert err(f, 4, 512, A, Bp, B.BF16, 0.0, C, None) == B.ERR_DOMAIN
+    assert err(f, 4, 512, A + 8, Bp, B.BF16, 1.0, C, None) == B.ERR_ALIGN
+    assert "contexts" in (lib.logra_predicted_kl_q_noalloc(B.NOALLOC_MAX_CONTEXTS + 1, 8, A, Bp, B.BF16, 1.0, C,
+                                                           None) and lib.logra_last_error().decode())
