@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="use fewer layers (profiling runs only)")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
+                    help="per-dispatch means of every counter in a rocprofv3 --pmc csv, for the "
+                         "accumulate and merge kernels")
     return ap.parse_args()
 
 
@@ -147,6 +150,30 @@ def summarize_traffic(fetch_csv, write_csv, workload):
                     "fetch_calibration": round(ffac, 4), "write_calibration": round(wfac, 4),
                     "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
                     "dispatches": len(f[kernel]), "kernel_sources": kernel_source_hash(kernel)})
+    return out
+
+
+def summarize_counters(path):
+    """Mean per dispatch of every counter in one rocprofv3 counter csv, with the mean dispatch
+    duration, for the accumulate and the merge kernels (the counters summed over the dimensions
+    rocprofv3 reports them in)."""
+    per = {}
+    for row in csv.DictReader(open(path)):
+        key = next((k for k in (ACC_KERNEL, MERGE_KERNEL) if k in row["Kernel_Name"]), None)
+        if key is None:
+            continue
+        d = per.setdefault(key, {}).setdefault(row["Dispatch_Id"], {"counters": {}})
+        d["ns"] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        c = d["counters"]
+        c[row["Counter_Name"]] = c.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    out = []
+    for kernel, disp in per.items():
+        n = len(disp)
+        names = sorted({c for d in disp.values() for c in d["counters"]})
+        out.append({"kernel": kernel, "dispatches": n,
+                    "mean_us": round(sum(d["ns"] for d in disp.values()) / n / 1e3, 2),
+                    "mean": {c: sum(d["counters"].get(c, 0.0) for d in disp.values()) / n for c in names},
+                    "kernel_sources": kernel_source_hash(kernel)})
     return out
 
 
@@ -241,6 +268,10 @@ def main():
     if args.summarize_traffic:
         for t in summarize_traffic(*args.summarize_traffic, args.workload):
             print("traffic-json: " + json.dumps(t))
+        return
+    if args.summarize_counters:
+        for t in summarize_counters(args.summarize_counters):
+            print("counters-json: " + json.dumps(t))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
