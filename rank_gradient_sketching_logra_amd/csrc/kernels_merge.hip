@@ -32,6 +32,9 @@ namespace logra {
 
 namespace {
 
+// Two bf16 bit patterns, the operand and result type of v_cvt_sr_bf16_f32.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
@@ -85,15 +88,37 @@ __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const
 #pragma unroll
     for (int t = 0; t < 16; ++t) put(t, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)value(t)));
   } else if (aligned) {
-    // One block per eight elements, generated and used in turn so that only
-    // one block's words are live at a time.
+    // v_cvt_sr_bf16_f32 adds the high 16 bits of its second operand to the
+    // discarded half of the fp32 pattern and truncates: the rule above for
+    // every non-NaN value (infinity stays infinity, overflow lands on it).  So
+    // an odd element takes its generator word as it is (its draw is the high
+    // half) and an even one the word shifted up by 16; the two results of a
+    // pair fill the halves of one output word.  NaN is the one case the
+    // instruction rounds differently: the sum of the sixteen values is NaN
+    // whenever one of them is, and only then do the NaN elements take the
+    // quiet NaN of their sign.
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] = value(t);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
 #pragma unroll
-      for (int t = 8 * h; t < 8 * h + 8; ++t)
-        put(t, f32_to_bf16_sr(value(t), (p.w[(t & 7) >> 1] >> (16 * (t & 1))) & 0xFFFFu));
-      __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < 4; ++q) {
+        // both halves are written, so pk may start as any value
+        s16x2 pk = __builtin_bit_cast(s16x2, p.w[q] << 16);
+        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q], p.w[q] << 16, false);
+        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q + 1], p.w[q], true);
+        out[4 * h + q] = __builtin_bit_cast(uint32_t, pk);
+      }
+    }
+    float sum = v[0];
+#pragma unroll
+    for (int t = 1; t < 16; ++t) sum += v[t];
+    if (__builtin_isnan(sum)) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (__builtin_isnan(v[t])) put(t, f32_to_bf16_rne(v[t]));
     }
   } else {
     // Elements e0 .. e0 + 15 lie in blocks g0, g0 + 1 and, when e0 is not a
