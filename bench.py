@@ -53,6 +53,10 @@ POOL_LIMIT_BYTES = 160e9  # distinct input sets up to this size, else a pool
 POOL_SETS = 17            # input sets in a pool (27B set: 17 x 0.74 GB)
 BALLAST_BYTES = {"dense-27b-set-r256": 10 * 10**9}
 DEFAULT_WORKLOAD = "qwen2.5-7b-set-r64"
+# Microbatches per projection and accumulate launch.  Two at r = 64: the inputs of a pair of
+# microbatches are stored together, so each tile's fixed cost (ring fill, class-sum exchange,
+# S read and write) is paid once per pair.  One at r = 256, where pairing saved 2.5%.
+PER_LAUNCH = {"qwen2.5-7b-set-r64": 2, "qwen2.5-1.5b-set-r64": 2}
 ACC_KERNEL = "acc_bf16_table_kernel"
 MERGE_KERNEL = "merge_bf16_kernel"
 CALIB_KERNEL = "probe_copy_kernel"
@@ -74,6 +78,9 @@ def parse():
     ap.add_argument("--rounding", default=None, choices=[None, "nearest", "stochastic"])
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="use fewer layers (profiling runs only)")
+    ap.add_argument("--microbatches-per-launch", type=int, default=None,
+                    help="microbatches whose inputs are stored together and projected and "
+                         "accumulated by one launch each (default: per workload)")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
@@ -102,22 +109,24 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, workload):
+def read_traffic(kernel, workload, tokens_per_launch):
     """Calibrated HBM bytes per launch of `kernel` from the committed counter summary, or None
-    when it is missing or was taken on other kernel sources."""
+    when it is missing, was taken on other kernel sources or (the accumulate) on launches of
+    another token count."""
     try:
         with open(os.path.join(ROOT, TRAFFIC_FILES[kernel].format(w=workload))) as fh:
             for line in fh:
                 if line.startswith("traffic-json: "):
                     t = json.loads(line[len("traffic-json: "):])
-                    if t.get("kernel_sources") == kernel_source_hash(kernel):
+                    if t.get("kernel_sources") == kernel_source_hash(kernel) and (
+                            kernel != ACC_KERNEL or t.get("tokens_per_launch") == tokens_per_launch):
                         return t
     except OSError:
         pass
     return None
 
 
-def summarize_traffic(fetch_csv, write_csv, workload):
+def summarize_traffic(fetch_csv, write_csv, workload, tokens_per_launch):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the calibration copy, the accumulate and
     the merge; each counter is scaled by bytes-moved / counter-reading of the copy.  Returns
     one summary per kernel."""
@@ -149,7 +158,8 @@ def summarize_traffic(fetch_csv, write_csv, workload):
                     "traffic_bytes_per_launch": round(fk + wk),
                     "fetch_calibration": round(ffac, 4), "write_calibration": round(wfac, 4),
                     "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
-                    "dispatches": len(f[kernel]), "kernel_sources": kernel_source_hash(kernel)})
+                    "dispatches": len(f[kernel]), "kernel_sources": kernel_source_hash(kernel),
+                    "tokens_per_launch": tokens_per_launch})
     return out
 
 
@@ -266,7 +276,10 @@ def roofline(name, per_launch_bytes, per_launch_flops, launch_us):
 def main():
     args = parse()
     if args.summarize_traffic:
-        for t in summarize_traffic(*args.summarize_traffic, args.workload):
+        from rank_gradient_sketching_logra_amd import synth
+        w = synth.BY_NAME[args.workload]
+        tpl = w.T * (args.microbatches_per_launch or PER_LAUNCH.get(w.name, 1))
+        for t in summarize_traffic(*args.summarize_traffic, args.workload, tpl):
             print("traffic-json: " + json.dumps(t))
         return
     if args.summarize_counters:
@@ -288,6 +301,15 @@ def main():
     if args.counter_run:
         args.steps, args.warmup = 1, 0
     T, r, M = w.T, w.r, w.microbatches
+    # G microbatches per launch: their inputs are stored as one [G T x width] block per matrix,
+    # so one launch of G T tokens projects or accumulates them all (S is read and written
+    # once per G microbatches).  From here on T and M count tokens per launch and launches.
+    G = args.microbatches_per_launch or PER_LAUNCH.get(w.name, 1)
+    if G < 1 or M % G:
+        print(f"--microbatches-per-launch must divide the {M} microbatches", file=sys.stderr)
+        sys.exit(2)
+    T_mb = T
+    T, M = G * T, M // G
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
@@ -404,8 +426,8 @@ def main():
               if w.name == DEFAULT_WORKLOAD else
               f"sketch-accumulate + merge HBM GB/s (% of peak), {w.name}")
     full = layers == w.layers
-    acc_traffic = read_traffic(ACC_KERNEL, w.name) if full else None
-    merge_traffic = read_traffic(MERGE_KERNEL, w.name) if full else None
+    acc_traffic = read_traffic(ACC_KERNEL, w.name, T) if full else None
+    merge_traffic = read_traffic(MERGE_KERNEL, w.name, T) if full else None
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -419,8 +441,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian inputs of the workload's shapes, resident in HBM)",
-        "config": {"workload": w.name, "layers": layers, "matrices": len(mats), "r": r, "T": T,
-                   "microbatches": M, "rounding": rounding, "optimizer": w.optimizer,
+        "config": {"workload": w.name, "layers": layers, "matrices": len(mats), "r": r, "T": T_mb,
+                   "microbatches": M * G, "microbatches_per_launch": G, "rounding": rounding, "optimizer": w.optimizer,
                    "contexts": P, "vocab": Vv, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2)},
     }
     # Roofline of the dominant kernel (the accumulate) from the method's own work per launch

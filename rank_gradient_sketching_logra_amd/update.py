@@ -9,13 +9,15 @@ For every selected matrix of every layer and every microbatch ("LoGRA: Scaling
 LLM Reinforcement Learning with Low-Rank Gradient Sketches", §2.1-2.3):
 
   project     XAt = X A^T, written in the accumulate's packed operand form;
-              one persistent launch per microbatch over all matrices of all
+              one persistent launch per microbatch (or per group of
+              microbatches whose inputs are stored one after another, which
+              is one launch over their tokens) over all matrices of all
               layers, layers ascending and each layer's matrices in
               q, k, v, o, gate, up, down order, so the matrices that share an
               input (q, k, v; gate, up) are neighbours and are projected
               together, reading their input once
-  accumulate  S += D^T XAt; one persistent launch per microbatch over all
-              matrices, layers in reverse (the order a backward pass
+  accumulate  S += D^T XAt; one persistent launch per microbatch (or group)
+              over all matrices, layers in reverse (the order a backward pass
               produces their derivatives)
   optimise    RowAdam of every sketch in one grouped call, writing the update
               in the merge's packed operand form
