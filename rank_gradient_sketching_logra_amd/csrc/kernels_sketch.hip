@@ -658,17 +658,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) with the other counters unconstrained.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Transpose a lane's 8 x 8 block of bf16 (row[i] = eight columns of token
-// i): a[e] = the eight tokens of column e, as one MFMA operand.  Each output
-// word takes one 16-bit half from each of two rows (one byte permute).
+// Transpose of a lane's 8 x 8 block of bf16 (row[i] = eight columns of token
+// i), one operand: the eight tokens of column e, as one MFMA operand.  Each
+// output word takes one 16-bit half from each of two rows (one byte permute).
+__device__ __forceinline__ u32x4 transpose8x8_e(const u32x4 (&row)[8], int e) {
+  const int q = e >> 1;
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 a;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) a[p] = __builtin_amdgcn_perm(row[2 * p + 1][q], row[2 * p][q], sel);
+  return a;
+}
+// The whole transpose: a[e] for e = 0..7.
 __device__ __forceinline__ void transpose8x8(const u32x4 (&row)[8], u32x4 (&a)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) a[e][p] = __builtin_amdgcn_perm(row[2 * p + 1][q], row[2 * p][q], sel);
-  }
+  for (int e = 0; e < 8; ++e) a[e] = transpose8x8_e(row, e);
 }
 
 // 32-bit LDS address of a shared-memory object.
@@ -973,7 +977,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
                        // every wave has read iteration k's slot
       issue(k + R);
       if (!has_rb) continue;
-      const bool live = NQ * k + qt < nsteps;  // uniform per wave
+      const bool live = NQ == 1 || NQ * k + qt < nsteps;  // uniform per wave (always with one class)
       const u32x4* qs = smem + (((k + 1) % R) * kSlot + qt * kClass) * 64;
       u32x4 rn[8], bhn, bln;
       acc_read_issue(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), rn, bhn, bln);
@@ -987,13 +991,30 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
       __builtin_amdgcn_sched_barrier(0);
       acc_read_wait(rn, bhn, bln);
       clip(rn, NQ * (k + 1) + qt);
-      if (live) {
+      if constexpr (NQ == 1) {
+        // Each lo-term MFMA is followed by the transpose that overwrites its
+        // A operand with the next step's: the VALU work of one instance runs
+        // while the matrix core works on another.
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e) {
           acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e],
                                                            0, 0, 0);
+          a[e] = transpose8x8_e(rn, e);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      } else {
+        if (live) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e],
+                                                             0, 0, 0);
+        }
+        transpose8x8(rn, a);
       }
-      transpose8x8(rn, a);
       bh = bhn;
       bl = bln;
     }
