@@ -40,11 +40,16 @@ __device__ __forceinline__ void load_bf16x4(const uint16_t* __restrict__ base, i
   w0 = 0u;
   w1 = 0u;
   if (row >= nrows || col >= ncols) return;
-  const uint16_t* p = base + row * ld + col;
+  // X is device memory: read through the global address space, so the loads
+  // count on the vector-memory counter only (a flat load also counts on the
+  // LDS counter, and every wait for an LDS access would then wait for it).
+  typedef __attribute__((address_space(1))) const uint16_t gu16;
+  typedef __attribute__((address_space(1))) const u32x2 gu2;
+  gu16* p = (gu16*)base + row * ld + col;
   if (col + 4 <= ncols) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w0 = v.x;
-    w1 = v.y;
+    const u32x2 v = *(gu2*)p;
+    w0 = v[0];
+    w1 = v[1];
     return;
   }
   uint32_t e[4];
@@ -73,6 +78,35 @@ __device__ __forceinline__ u32x4 load_x_paired(const uint16_t* __restrict__ base
   v[1] = __builtin_amdgcn_perm(h1, l1, 0x05040100u);  // c+2, c+18
   v[2] = __builtin_amdgcn_perm(h0, l0, 0x07060302u);  // c+1, c+17
   v[3] = __builtin_amdgcn_perm(h0, l0, 0x05040100u);  // c, c+16
+  return v;
+}
+
+// The operand of load_x_paired in two steps, for ncols a multiple of 4 (each
+// group of four columns is wholly inside or outside the matrix): the four
+// words of the two 8-byte loads (a group outside reads eight zero bytes), and
+// later their permutation into the paired order.  Nothing follows a load
+// before the permutation, so the loads can be in flight until the operand is
+// used.
+__device__ const u32x2 kZeroX = {0u, 0u};
+__device__ __forceinline__ u32x4 load_x_raw(const uint16_t* __restrict__ base, int64_t ld,
+                                            int64_t row, int64_t c32, int g, int64_t nrows,
+                                            int64_t ncols) {
+  typedef __attribute__((address_space(1))) const uint16_t gu16;
+  typedef __attribute__((address_space(1))) const u32x2 gu2;
+  const int64_t c = c32 + 12 - 4 * g;  // runs c .. c+3 and c+16 .. c+19
+  const bool okr = row < nrows;
+  gu2* zero = (gu2*)&kZeroX;
+  gu2* pl = okr && c < ncols ? (gu2*)((gu16*)base + row * ld + c) : zero;
+  gu2* ph = okr && c + 16 < ncols ? (gu2*)((gu16*)base + row * ld + c + 16) : zero;
+  const u32x2 l = *pl, h = *ph;
+  return u32x4{l[0], l[1], h[0], h[1]};
+}
+__device__ __forceinline__ u32x4 x_paired_from_raw(u32x4 w) {
+  u32x4 v;
+  v[0] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);  // columns c+3, c+19
+  v[1] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);  // c+2, c+18
+  v[2] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);  // c+1, c+17
+  v[3] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);  // c, c+16
   return v;
 }
 
@@ -541,6 +575,192 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
     }
     }
     item = grid_waves + (int64_t)__builtin_amdgcn_readfirstlane(claim);
+  }
+}
+
+// Block-wide projection for more than 64 ranks (one projection per entry).
+// A work item is (entry, 256 consecutive tokens); the eight waves of the
+// block take two 16-token steps each, so the signs of every 256-column block
+// are generated once per 256 tokens and shared by the block, instead of once
+// per two steps as in project_table_kernel, where their generation and
+// expansion outweighed the matrix work.  The chunks c = (column block b,
+// 32-column step s) run in order with one block barrier each; iteration c
+//   generates column block b + 1's sign words when s = 0 (one Philox4x32-10
+//   per thread: the low or high half of sigma_block for one rank),
+//   expands chunk c + 1's words into MFMA operands (two per thread),
+//   loads the inputs of chunk c + 3 (a ring of four chunks in registers),
+//   and runs chunk c's MFMAs with the operands from LDS,
+// in double-buffered LDS areas, each written one barrier or more after its
+// last read.  Every accumulator takes the same MFMAs with the same operands
+// in the same order as in project_table_kernel ((b, s) ascending), so the
+// outputs are identical.
+constexpr int kPbWaves = 8;
+constexpr int kPbSteps = 2;                                        // token steps per wave
+constexpr int kPbTokens = kPbWaves * kPbSteps * kProjTokens;       // tokens per item
+constexpr int kPbAhead = 3;                                        // chunks of inputs in flight
+
+template <int NB16>
+__global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
+    const ProjTableEntry* __restrict__ tab, unsigned* __restrict__ next, int n, int64_t T,
+    int64_t r, float cr, int nrb) {
+  static_assert(NB16 >= 5 && NB16 <= 16, "more than 64 ranks, at most 256");
+  constexpr int RP = NB16 * 16;
+  constexpr int TS = kPbSteps;
+  constexpr int XR = kPbAhead + 1;  // input ring slots
+  // sign words [buffer][rank][word]; operands [buffer][rank block][lane]
+  constexpr int kWordsBytes = 2 * RP * 8 * 4;
+  constexpr int kOpsBytes = 2 * NB16 * 64 * 16;
+  constexpr int kRedBytes = kPbWaves * kProjTokens * (RP + 1) * 4;  // the epilogue's rows
+  constexpr int kLds = kWordsBytes + kOpsBytes > kRedBytes ? kWordsBytes + kOpsBytes : kRedBytes;
+  __shared__ __align__(16) unsigned char lds[kLds];
+  __shared__ int64_t begin_s[kProjTableMax + 1];
+  __shared__ unsigned claim_s;
+  uint32_t (*words)[RP][8] = reinterpret_cast<uint32_t (*)[RP][8]>(lds);
+  u32x4 (*ops)[NB16][64] = reinterpret_cast<u32x4 (*)[NB16][64]>(lds + kWordsBytes);
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) begin_s[i] = tab[i].item_begin;
+  __syncthreads();
+  const int64_t total = begin_s[n];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t item = blockIdx.x;
+  while (item < total) {  // uniform per block
+    int lane_o = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
+    const int g4 = lane >> 4;
+    if (threadIdx.x == 0) claim_s = atomicAdd(next, 1u);  // read after the item's last barrier
+    int lo = 0, hi = n - 1;  // the entry holding the item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (begin_s[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const ProjTableEntry& e = tab[lo];
+    const uint16_t* __restrict__ X = e.X;
+    const int64_t ldx = e.ldx, k = e.k;
+    const uint32_t s0 = (uint32_t)e.k0[0], s1 = (uint32_t)(e.k0[0] >> 32);
+    const uint32_t mid = (uint32_t)e.k1[0], stp = (uint32_t)(e.k1[0] >> 32);
+    const int64_t st0 = (item - begin_s[lo]) * (kPbWaves * TS) + wave * TS;  // the wave's first step
+    const int64_t trow = st0 * kProjTokens + (lane & 15);
+    const int64_t nblk = (k + 255) >> 8;
+    const int64_t nch = nblk * 8;
+    // Column block b's sign words: thread t computes half t & 1 of
+    // sigma_block for rank t >> 1 (words 0..3 the low half, 4..7 the high).
+    auto gen = [&](int64_t b) __attribute__((always_inline)) {
+      const int j = (int)(threadIdx.x >> 1), half = (int)(threadIdx.x & 1);
+      if (j < RP) {
+        const Philox4x32 p =
+            philox4x32_10((uint32_t)(2 * b + half), (uint32_t)j | 0x80000000u, mid, stp, s0, s1);
+        const bool live = j < r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) words[b & 1][j][4 * half + i] = live ? p.w[i] : 0u;
+      }
+    };
+    // Chunk c's operands: rank blocks 2w and 2w + 1 of wave w, the lane's rank
+    // 16 nb + (l & 15) holding the step's 32 columns in the paired order.
+    auto expand = [&](int64_t c) __attribute__((always_inline)) {
+      const int64_t b = c >> 3;
+      const int s = (int)(c & 7);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int nb = 2 * wave + i;
+        if (nb < NB16) {  // uniform
+          const uint32_t wv = words[b & 1][16 * nb + (lane & 15)][s];
+          ops[c & 1][nb][lane] = expand_sign_pairs(wv << (4 * g4));
+        }
+      }
+    };
+    auto load_chunk = [&](int64_t c, u32x4 (&x)[TS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < TS; ++h)
+        x[h] = load_x_raw(X, ldx, trow + h * kProjTokens, (c >> 3) * 256 + 32 * (c & 7), g4, T, k);
+    };
+    f32x4 acc[TS][NB16];
+#pragma unroll
+    for (int h = 0; h < TS; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB16; ++nb) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Loaded words of chunk c in slot c % XR.  Every wave loads and computes
+    // every chunk with no branch around the loads (loads in branches are
+    // waited for in full): a wave past T loads zeros and its sums are never
+    // stored, and loads past the last chunk repeat it and are not used.
+    u32x4 xr[XR][TS];
+#pragma unroll
+    for (int c = 0; c < kPbAhead; ++c) load_chunk(c < nch ? c : nch - 1, xr[c]);
+    gen(0);
+    __syncthreads();
+    expand(0);
+    __syncthreads();
+    for (int64_t b = 0; b < nblk; ++b) {
+      // the step is a constant in each copy of the body, and so is every
+      // ring slot
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int64_t c = 8 * b + s;
+        if (s == 0 && b + 1 < nblk) gen(b + 1);
+        if (c + 1 < nch) expand(c + 1);
+        load_chunk(c + kPbAhead < nch ? c + kPbAhead : nch - 1, xr[(s + kPbAhead) % XR]);
+        u32x4 xp[TS];
+#pragma unroll
+        for (int h = 0; h < TS; ++h) xp[h] = x_paired_from_raw(xr[s % XR][h]);
+#pragma unroll
+        for (int nb = 0; nb < NB16; ++nb) {
+          const u32x4 op = ops[c & 1][nb][lane];
+#pragma unroll
+          for (int h = 0; h < TS; ++h)
+            acc[h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xp[h]), as_bf16x8(op),
+                                                                 acc[h][nb], 0, 0, 0);
+        }
+        __syncthreads();
+      }
+    }
+    // Each wave's tile through its own LDS rows, as in project_table_kernel.
+    float (*rw)[RP + 1] = reinterpret_cast<float (*)[RP + 1]>(lds) + wave * kProjTokens;
+#pragma unroll
+    for (int h = 0; h < TS; ++h) {
+      const int64_t st = st0 + h;
+      const int64_t t0 = st * kProjTokens;
+      if (t0 >= T) break;  // uniform per wave
+#pragma unroll
+      for (int nb = 0; nb < NB16; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rw[4 * g4 + j][nb * 16 + (lane & 15)] = acc[h][nb][j];
+      asm volatile("" ::: "memory");
+      if (e.XAt[0]) {
+        float* __restrict__ XAt = e.XAt[0];
+        for (int idx = lane; idx < kProjTokens * r; idx += 64) {
+          const int m = idx / (int)r;
+          const int j = idx - m * (int)r;
+          const int64_t t = t0 + m;
+          if (t < T) XAt[t * r + j] = rw[m][j] * cr;
+        }
+      }
+      if (e.planes[0]) {
+        for (int bb = 0; bb < nrb; ++bb) {
+          const int j = 32 * bb + (lane & 31);
+          float hv[8], lv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = j < r ? rw[8 * (lane >> 5) + i][j] * cr : 0.f;
+            hv[i] = (float)(__bf16)v;
+            lv[i] = v - hv[i];
+          }
+          u32x4 vh, vl;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            vh[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2 * p + 1]) << 16);
+            vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
+          }
+          uint16_t* dst = e.planes[0] + (st * nrb + bb) * 1024 + lane * 8;
+          *reinterpret_cast<u32x4*>(dst) = vh;
+          *reinterpret_cast<u32x4*>(dst + 512) = vl;
+        }
+      }
+      asm volatile("" ::: "memory");  // this step's LDS reads before the next step's writes
+    }
+    __syncthreads();  // the rows are read; the next item's words may be written
+    item = (int64_t)gridDim.x + (int64_t)claim_s;
+    __syncthreads();  // every thread has read claim_s before the next item rewrites it
   }
 }
 
@@ -1383,7 +1603,11 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
                                 hipStream_t s) {
   if (n < 1 || n > kProjTableMax) return hipErrorInvalidValue;
   std::vector<ProjTableEntry> tab((size_t)n + 2, ProjTableEntry{});
-  const int64_t per_tokens = (int64_t)kProjTokens * kProjTableSteps;
+  // Above 64 ranks a block takes 256 tokens of one projection at a time
+  // (project_blocked_kernel); otherwise a wave takes two token steps.
+  bool blocked = proj_nb16(r) > 4;
+  for (int i = 0; i < n && blocked; ++i) blocked = items[i].k % 4 == 0;  // its loads need it
+  const int64_t per_tokens = blocked ? (int64_t)kPbTokens : (int64_t)kProjTokens * kProjTableSteps;
   const int64_t per = (T + per_tokens - 1) / per_tokens;  // items per entry
   // Consecutive projections of one input (same X, k and leading dimension)
   // share an entry, up to kProjFuse of them at <= 64 ranks: X is read once for
@@ -1429,6 +1653,22 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
   unsigned* next = reinterpret_cast<unsigned*>(static_cast<ProjTableEntry*>(ws) + n + 1);
   const float cr = (float)(1.0 / std::sqrt((double)r));
   const int nrb = (int)(acc_rank_pad(r) / 32);
+  if (blocked) {
+    const dim3 grid((unsigned)compute_units());  // one block per compute unit (its LDS)
+    switch (proj_nb16(r)) {
+#define LOGRA_PROJ_BLOCKED(NB)                                                                  \
+  case NB:                                                                                      \
+    hipLaunchKernelGGL(project_blocked_kernel<NB>, grid, dim3(kPbWaves * 64), 0, s, t, next, n, T, \
+                       r, cr, nrb);                                                             \
+    return hipGetLastError();
+      LOGRA_PROJ_BLOCKED(6)
+      LOGRA_PROJ_BLOCKED(8)
+      LOGRA_PROJ_BLOCKED(12)
+      LOGRA_PROJ_BLOCKED(16)
+#undef LOGRA_PROJ_BLOCKED
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (proj_nb16(r)) {
     case 1: return launch_project_table_nb<1>(t, next, n, T, r, cr, nrb, s);
     case 2: return launch_project_table_nb<2>(t, next, n, T, r, cr, nrb, s);
