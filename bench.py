@@ -57,6 +57,10 @@ DEFAULT_WORKLOAD = "qwen2.5-7b-set-r64"
 # microbatches are stored together, so each tile's fixed cost (ring fill, class-sum exchange,
 # S read and write) is paid once per pair.  One at r = 256, where pairing saved 2.5%.
 PER_LAUNCH = {"qwen2.5-7b-set-r64": 2, "qwen2.5-1.5b-set-r64": 2}
+# Layers per grouped merge launch (at most 16 matrices a launch): two layers halve the
+# launches and give each block twice the units over which to spread its start (sign
+# generation, ring fill).
+MERGE_PER_LAUNCH = {"qwen2.5-7b-set-r64": 2, "qwen2.5-1.5b-set-r64": 2, "dense-27b-set-r256": 2}
 ACC_KERNEL = "acc_bf16_table_kernel"
 MERGE_KERNEL = "merge_bf16_kernel"
 CALIB_KERNEL = "probe_copy_kernel"
@@ -81,6 +85,8 @@ def parse():
     ap.add_argument("--microbatches-per-launch", type=int, default=None,
                     help="microbatches whose inputs are stored together and projected and "
                          "accumulated by one launch each (default: per workload)")
+    ap.add_argument("--merge-layers-per-launch", type=int, default=None,
+                    help="layers per grouped merge launch (default: per workload)")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
@@ -109,24 +115,25 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, workload, tokens_per_launch):
+def read_traffic(kernel, workload, tokens_per_launch, layers_per_launch):
     """Calibrated HBM bytes per launch of `kernel` from the committed counter summary, or None
-    when it is missing, was taken on other kernel sources or (the accumulate) on launches of
-    another token count."""
+    when it is missing, was taken on other kernel sources or on launches of another size (the
+    accumulate's tokens, the merge's layers)."""
     try:
         with open(os.path.join(ROOT, TRAFFIC_FILES[kernel].format(w=workload))) as fh:
             for line in fh:
                 if line.startswith("traffic-json: "):
                     t = json.loads(line[len("traffic-json: "):])
-                    if t.get("kernel_sources") == kernel_source_hash(kernel) and (
-                            kernel != ACC_KERNEL or t.get("tokens_per_launch") == tokens_per_launch):
+                    same = (t.get("tokens_per_launch") == tokens_per_launch if kernel == ACC_KERNEL
+                            else t.get("layers_per_launch", 1) == layers_per_launch)
+                    if t.get("kernel_sources") == kernel_source_hash(kernel) and same:
                         return t
     except OSError:
         pass
     return None
 
 
-def summarize_traffic(fetch_csv, write_csv, workload, tokens_per_launch):
+def summarize_traffic(fetch_csv, write_csv, workload, tokens_per_launch, layers_per_launch):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the calibration copy, the accumulate and
     the merge; each counter is scaled by bytes-moved / counter-reading of the copy.  Returns
     one summary per kernel."""
@@ -159,7 +166,8 @@ def summarize_traffic(fetch_csv, write_csv, workload, tokens_per_launch):
                     "fetch_calibration": round(ffac, 4), "write_calibration": round(wfac, 4),
                     "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
                     "dispatches": len(f[kernel]), "kernel_sources": kernel_source_hash(kernel),
-                    "tokens_per_launch": tokens_per_launch})
+                    **({"tokens_per_launch": tokens_per_launch} if kernel == ACC_KERNEL
+                       else {"layers_per_launch": layers_per_launch})})
     return out
 
 
@@ -279,7 +287,8 @@ def main():
         from rank_gradient_sketching_logra_amd import synth
         w = synth.BY_NAME[args.workload]
         tpl = w.T * (args.microbatches_per_launch or PER_LAUNCH.get(w.name, 1))
-        for t in summarize_traffic(*args.summarize_traffic, args.workload, tpl):
+        mpl = args.merge_layers_per_launch or MERGE_PER_LAUNCH.get(w.name, 1)
+        for t in summarize_traffic(*args.summarize_traffic, args.workload, tpl, mpl):
             print("traffic-json: " + json.dumps(t))
         return
     if args.summarize_counters:
@@ -310,6 +319,10 @@ def main():
         sys.exit(2)
     T_mb = T
     T, M = G * T, M // G
+    ML = args.merge_layers_per_launch or MERGE_PER_LAUNCH.get(w.name, 1)
+    if ML < 1 or ML * len(w.kinds) > 16:
+        print("--merge-layers-per-launch: at most 16 matrices per launch", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
@@ -393,7 +406,7 @@ def main():
         U.step_size(z, zd, w.tau, w.delta, w.alpha_max, q, alpha, kl_ws)
         ev[3].record()
         U.merge(layer_list, kinds, lambda l, kd: keys[(l, kd)], lambda l, kd: W[(l, kd)],   # D: merge
-                lambda l, kd: UP[(l, kd)], r, w.eta, alpha, rounding, w.sr_seed)
+                lambda l, kd: UP[(l, kd)], r, w.eta, alpha, rounding, w.sr_seed, per_launch=ML)
         ev[4].record()
 
     def events():
@@ -421,13 +434,14 @@ def main():
     merge_gbs = merge_total / (merge_ms * 1e-3) / 1e9
     proj_gbs = proj_total / (med[0] * 1e-3) / 1e9
     acc_launch_us = acc_ms * 1e3 / M
-    merge_launch_us = merge_ms * 1e3 / layers
+    merge_launches = (layers + ML - 1) // ML
+    merge_launch_us = merge_ms * 1e3 / merge_launches
     metric = ("sketch-accumulate + merge HBM GB/s (% of peak), Qwen-7B layer set, r=64"
               if w.name == DEFAULT_WORKLOAD else
               f"sketch-accumulate + merge HBM GB/s (% of peak), {w.name}")
     full = layers == w.layers
-    acc_traffic = read_traffic(ACC_KERNEL, w.name, T) if full else None
-    merge_traffic = read_traffic(MERGE_KERNEL, w.name, T) if full else None
+    acc_traffic = read_traffic(ACC_KERNEL, w.name, T, ML) if full else None
+    merge_traffic = read_traffic(MERGE_KERNEL, w.name, T, ML) if full else None
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -442,7 +456,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian inputs of the workload's shapes, resident in HBM)",
         "config": {"workload": w.name, "layers": layers, "matrices": len(mats), "r": r, "T": T_mb,
-                   "microbatches": M * G, "microbatches_per_launch": G, "rounding": rounding, "optimizer": w.optimizer,
+                   "microbatches": M * G, "microbatches_per_launch": G, "merge_layers_per_launch": ML,
+                   "rounding": rounding, "optimizer": w.optimizer,
                    "contexts": P, "vocab": Vv, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2)},
     }
     # Roofline of the dominant kernel (the accumulate) from the method's own work per launch
@@ -456,9 +471,10 @@ def main():
     # beside the roofline, not used for it.
     rf["mfma_executed_tflops"] = round(2 * (acc_flops // M) / (acc_launch_us * 1e-6) / 1e12, 1)
     out["roofline"] = rf
-    mrf = roofline(MERGE_KERNEL, merge_total // layers, merge_flops // layers, merge_launch_us)
+    mrf = roofline(MERGE_KERNEL, merge_total // merge_launches, merge_flops // merge_launches,
+                   merge_launch_us)
     mrf.update({"traffic": merge_traffic["traffic_bytes_per_launch"] if merge_traffic else None,
-                "bytes_per_launch": merge_total // layers, "launches": layers * K,
+                "bytes_per_launch": merge_total // merge_launches, "launches": merge_launches * K,
                 "median_launch_us": round(merge_launch_us, 3)})
     out["roofline_merge"] = mrf
     out["phases_ms"] = {"project": round(med[0], 3), "accumulate": round(acc_ms, 3),
@@ -517,7 +533,7 @@ def main():
         m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         m0.record()
         U.merge(layer_list, kinds, lambda l, kd: keys[(l, kd)], lambda l, kd: Wc[(l, kd)],
-                lambda l, kd: UP[(l, kd)], r, w.eta, alpha, other, w.sr_seed)
+                lambda l, kd: UP[(l, kd)], r, w.eta, alpha, other, w.sr_seed, per_launch=ML)
         m1.record()
         torch.cuda.synchronize()
         if rep:

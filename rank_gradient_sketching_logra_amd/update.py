@@ -23,7 +23,8 @@ LLM Reinforcement Learning with Low-Rank Gradient Sketches", §2.1-2.3):
               in the merge's packed operand form
   step size   q over the context set and alpha = min(alpha_max, sqrt(delta/q)),
               both on the device
-  merge       W <- round(W - eta alpha U A); one grouped launch per layer
+  merge       W <- round(W - eta alpha U A); one grouped launch per layer (or per
+              group of layers)
 
 Accessors are callables: key(l, kind), x(l, kind) and so on return the key or
 tensor of matrix `kind` of layer `l` (for the microbatch being processed).
@@ -61,9 +62,11 @@ def step_size(z, zdot, tau, delta, alpha_max, q, alpha, ws, stream=None):
     B.step_alpha_dev(q, delta, alpha_max, out=alpha, stream=stream)
 
 
-def merge(layers, kinds, key, w, up, r, eta, alpha, mode, sr_seed, stream=None):
-    """W <- round(W - eta * alpha * U A) for every matrix, one grouped launch per layer;
-    alpha is a one-element device tensor (or None for alpha = 1)."""
-    for l in layers:
-        B.merge_grouped_packed([(key(l, kd), w(l, kd), up(l, kd)) for kd in kinds], r, eta,
-                               scale_dev=alpha, mode=mode, sr_seed=sr_seed, stream=stream)
+def merge(layers, kinds, key, w, up, r, eta, alpha, mode, sr_seed, stream=None, per_launch=1):
+    """W <- round(W - eta * alpha * U A) for every matrix, one grouped launch per `per_launch`
+    layers; alpha is a one-element device tensor (or None for alpha = 1)."""
+    layers = list(layers)
+    for i in range(0, len(layers), per_launch):
+        B.merge_grouped_packed([(key(l, kd), w(l, kd), up(l, kd)) for l in layers[i:i + per_launch]
+                                for kd in kinds], r, eta, scale_dev=alpha, mode=mode, sr_seed=sr_seed,
+                               stream=stream)

@@ -11,7 +11,7 @@ S and U in full (relative Frobenius error and the largest per-row relative error
 alpha, and sampled rows of every merged weight.  The other layers carry device-random
 inputs of the same shapes; they are not checked.  Two microbatches per update, either
 launched one at a time or, as the benchmark runs the 7B and 27B sets, stored together and
-projected and accumulated by one launch of 2T tokens.
+projected and accumulated by one launch of 2T tokens.  The merges take two layers per launch.
 
 Bounds: S and U relative Frobenius <= 5e-5 and every row <= 2e-4 (the contract is 2e-3);
 q and alpha <= 1e-4 relative; merged W within 1 bf16 ulp of the oracle on >= 99.99% of
@@ -33,6 +33,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 MICROBATCHES = 2
+MERGE_LAYERS = 2  # layers per grouped merge launch, as the benchmark runs them
 # the synthetic input each shared layer input is drawn as
 INPUT_KIND = {"att": "q", "o": "o", "mlp": "gate", "down": "down"}
 
@@ -159,10 +160,10 @@ def test_layer_set_update_through_the_benchmark_sequence(workload, per_launch):
             Wd[(l, kd)] = bf16_dev(synth.weight(w, l, kd)) if l in sampled else rnd((d, k), 0.02)
     W0 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
     UPD.merge(layers, kinds, key_of, lambda l, kd: Wd[(l, kd)], lambda l, kd: UPK[(l, kd)], r, w.eta, alpha,
-              w.rounding, w.sr_seed)
+              w.rounding, w.sr_seed, per_launch=MERGE_LAYERS)
     W1 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
     UPD.merge(layers, kinds, key_of, lambda l, kd: Wd[(l, kd)], lambda l, kd: UPK[(l, kd)], r, w.eta, None,
-              w.rounding, w.sr_seed)
+              w.rounding, w.sr_seed, per_launch=MERGE_LAYERS)
     W2 = {(l, kd): bf16_host(Wd[(l, kd)]) for l in sampled for kd in kinds}
     torch.cuda.synchronize()
     say("  GPU update done")
