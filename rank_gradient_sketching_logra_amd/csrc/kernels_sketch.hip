@@ -800,6 +800,7 @@ __global__ void project_f32_kernel(KeyArg key, int64_t T, int64_t k, int64_t r,
 constexpr int kAccStep = 16;        // tokens per MFMA step
 constexpr int kAccCols = 256;       // columns of D per block: 32 lanes x 8
 constexpr int kAccWaves = 8;        // waves per block: rank blocks x token classes
+constexpr int kAccBAhead = 2;       // 256 ranks: steps the B operands are loaded ahead
 
 struct AccGroupArgs {
   const void* D[kMaxGroup];
@@ -952,6 +953,30 @@ __device__ __forceinline__ void acc_read_wait(u32x4 (&row)[8], u32x4& bh, u32x4&
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(row[0]), "+v"(row[1]), "+v"(row[2]), "+v"(row[3]), "+v"(row[4]),
                  "+v"(row[5]), "+v"(row[6]), "+v"(row[7]), "+v"(bh), "+v"(bl)
+               :
+               : "memory");
+}
+
+// The eight row slabs only, issued; valid after acc_read_rows_wait().
+__device__ __forceinline__ void acc_read_rows_issue(uint32_t ad, u32x4 (&row)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168"
+      : "=&v"(row[0]), "=&v"(row[1]), "=&v"(row[2]), "=&v"(row[3]), "=&v"(row[4]),
+        "=&v"(row[5]), "=&v"(row[6]), "=&v"(row[7])
+      : "v"(ad)
+      : "memory");
+}
+__device__ __forceinline__ void acc_read_rows_wait(u32x4 (&row)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(row[0]), "+v"(row[1]), "+v"(row[2]), "+v"(row[3]), "+v"(row[4]),
+                 "+v"(row[5]), "+v"(row[6]), "+v"(row[7])
                :
                : "memory");
 }
@@ -1158,6 +1183,101 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
         transpose8x8(row, a);
         acc_mfma_step(acc, a, bh, bl);
       }
+    }
+  } else if (RB == 8 && interior) {
+    if constexpr (RB == 8) {
+      // Eight rank blocks: a wave's B operands (its rank block's packed
+      // input, which no other wave reads) are loaded straight into registers
+      // P steps ahead, and only the D rows, which all eight waves read, pass
+      // through the LDS ring (P + 2 slots of eight slabs).  Iteration k
+      // issues B(k + P) and then D(k + P + 2) into the slot D(k) left.
+      // Loads complete in issue order, so once no more than the loads issued
+      // after iteration k - P's B loads remain (its D load and three per
+      // later iteration), B(k) and D(k + 1) (issued in iteration k - P - 1)
+      // have landed.  Iteration k's operands A (the transposed rows) are in
+      // registers before it starts; its hi-term MFMAs run while the LDS reads
+      // of step k + 1 are in flight.
+      constexpr int P = kAccBAhead, NB = P + 1, RD = P + 2;
+      typedef __attribute__((address_space(1))) const u32x4 gb4;
+      typedef __attribute__((address_space(1))) const uint16_t gb16;
+      auto clip = [&](u32x4 (&row)[8], int s) __attribute__((always_inline)) {
+        if ((int64_t)kAccStep * (s + 1) > T) {
+          const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (t0 + i >= T) row[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      };
+      u32x4 bh[NB], bl[NB], a[8];
+      auto load_b = [&](int st, u32x4& h, u32x4& l) __attribute__((always_inline)) {
+        const int sc = st < nsteps ? st : nsteps - 1;
+        const gb4* p = (const gb4*)((const gb16*)planes + (int64_t)sc * bstride);
+        h = p[0];
+        l = p[64];
+      };
+      auto issue_d = [&](int st) __attribute__((always_inline)) {
+        const int sc = st < nsteps ? st : nsteps - 1;
+        const int64_t t0 = (int64_t)kAccStep * sc + 8 * hw + rb;
+        const int64_t t = t0 < T ? t0 : T - 1;
+        acc_issue_slab(smem + ((st % RD) * 8 + rb) * 64, D + t * ldd + col);
+      };
+#pragma unroll
+      for (int j = 0; j < RD - P; ++j) issue_d(j);
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        load_b(j, bh[j], bl[j]);
+        issue_d(j + RD - P);
+      }
+      wait_vmcnt<RD - P - 1 + 3 * P>();  // D(0) has landed
+      ring_barrier();
+      {
+        u32x4 row[8];
+        acc_read_rows_issue(lds_addr(smem + lane), row);
+        acc_read_rows_wait(row);
+        clip(row, 0);
+        transpose8x8(row, a);
+      }
+      auto iter = [&](int k, auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        wait_vmcnt<1 + 3 * (P - 1)>();
+        ring_barrier();  // every wave's D(k + 1) has landed and every wave
+                         // has read D(k)'s slot
+        load_b(k + P, bh[(u + P) % NB], bl[(u + P) % NB]);
+        issue_d(k + RD);
+        u32x4 rn[8];
+        acc_read_rows_issue(lds_addr(smem + ((k + 1) % RD) * 8 * 64 + lane), rn);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bh[u]),
+                                                           acc[e], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        acc_read_rows_wait(rn);
+        clip(rn, k + 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl[u]),
+                                                           acc[e], 0, 0, 0);
+          a[e] = transpose8x8_e(rn, e);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      static_assert(NB == 3, "the unrolled ring below has three entries");
+      int k = 0;
+      for (; k + NB <= Q; k += NB) {
+        iter(k, I0{});
+        iter(k + 1, I1{});
+        iter(k + 2, I2{});
+      }
+      if (k < Q) iter(k, I0{});
+      if (k + 1 < Q) iter(k + 1, I1{});
     }
   } else if (interior) {
     // Four or eight rank blocks (each wave computes every step of its class)
