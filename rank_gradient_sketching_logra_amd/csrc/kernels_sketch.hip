@@ -81,33 +81,33 @@ __device__ __forceinline__ u32x4 load_x_paired(const uint16_t* __restrict__ base
   return v;
 }
 
-// The operand of load_x_paired in two steps, for ncols a multiple of 4 (each
-// group of four columns is wholly inside or outside the matrix): the four
-// words of the two 8-byte loads (a group outside reads eight zero bytes), and
-// later their permutation into the paired order.  Nothing follows a load
-// before the permutation, so the loads can be in flight until the operand is
-// used.
-__device__ const u32x2 kZeroX = {0u, 0u};
-__device__ __forceinline__ u32x4 load_x_raw(const uint16_t* __restrict__ base, int64_t ld,
-                                            int64_t row, int64_t c32, int g, int64_t nrows,
-                                            int64_t ncols) {
+// Eight consecutive columns of one row of X as one 16-byte load, for ncols a
+// multiple of 8 and rows 16-byte aligned (each group of eight columns lies
+// wholly inside or outside the matrix; a group outside, or a row past nrows,
+// reads sixteen zero bytes).
+__device__ const u32x4 kZeroX8 = {0u, 0u, 0u, 0u};
+__device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ base, int64_t ld,
+                                         int64_t row, int64_t col, int64_t nrows,
+                                         int64_t ncols) {
   typedef __attribute__((address_space(1))) const uint16_t gu16;
-  typedef __attribute__((address_space(1))) const u32x2 gu2;
-  const int64_t c = c32 + 12 - 4 * g;  // runs c .. c+3 and c+16 .. c+19
-  const bool okr = row < nrows;
-  gu2* zero = (gu2*)&kZeroX;
-  gu2* pl = okr && c < ncols ? (gu2*)((gu16*)base + row * ld + c) : zero;
-  gu2* ph = okr && c + 16 < ncols ? (gu2*)((gu16*)base + row * ld + c + 16) : zero;
-  const u32x2 l = *pl, h = *ph;
-  return u32x4{l[0], l[1], h[0], h[1]};
+  typedef __attribute__((address_space(1))) const u32x4 gu4;
+  const bool ok = row < nrows && col < ncols;
+  return *(ok ? (gu4*)((gu16*)base + row * ld + col) : (gu4*)&kZeroX8);
 }
-__device__ __forceinline__ u32x4 x_paired_from_raw(u32x4 w) {
-  u32x4 v;
-  v[0] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);  // columns c+3, c+19
-  v[1] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);  // c+2, c+18
-  v[2] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);  // c+1, c+17
-  v[3] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);  // c, c+16
-  return v;
+// Bits 0, 2, .., 30 of x in bits 0 .. 15.
+__device__ __forceinline__ uint32_t even_bits(uint32_t x) {
+  x &= 0x55555555u;
+  x = (x | (x >> 1)) & 0x33333333u;
+  x = (x | (x >> 2)) & 0x0F0F0F0Fu;
+  x = (x | (x >> 4)) & 0x00FF00FFu;
+  return (x | (x >> 8)) & 0x0000FFFFu;
+}
+// The sign word of 32 columns (bit j: column j) rearranged for operands in
+// the consecutive column order: bit 15 - i takes column 2i and bit 31 - i
+// column 2i + 1, so that expand_sign_pairs(w << 4g) gives the signs of
+// columns 8g .. 8g + 7 in element order, matching one 16-byte load of X.
+__device__ __forceinline__ uint32_t sign_word_consecutive(uint32_t w) {
+  return __builtin_bitreverse32(even_bits(w >> 1) | (even_bits(w) << 16));
 }
 
 // Eight consecutive bf16 of row `row` starting at column `col`; zero outside
@@ -607,6 +607,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
   constexpr int RP = NB16 * 16;
   constexpr int TS = kPbSteps;
   constexpr int XR = kPbAhead + 1;  // input ring slots
+  static_assert(8 % XR == 0, "chunk c sits in slot s % XR, s = c mod 8: XR must divide 8");
   // sign words [buffer][rank][word]; operands [buffer][rank block][lane]
   constexpr int kWordsBytes = 2 * RP * 8 * 4;
   constexpr int kOpsBytes = 2 * NB16 * 64 * 16;
@@ -655,7 +656,8 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
       }
     };
     // Chunk c's operands: rank blocks 2w and 2w + 1 of wave w, the lane's rank
-    // 16 nb + (l & 15) holding the step's 32 columns in the paired order.
+    // 16 nb + (l & 15) holding the step's 32 columns in the consecutive order
+    // (lane group g: columns 8g .. 8g + 7), as the X operand holds them.
     auto expand = [&](int64_t c) __attribute__((always_inline)) {
       const int64_t b = c >> 3;
       const int s = (int)(c & 7);
@@ -664,14 +666,14 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
         const int nb = 2 * wave + i;
         if (nb < NB16) {  // uniform
           const uint32_t wv = words[b & 1][16 * nb + (lane & 15)][s];
-          ops[c & 1][nb][lane] = expand_sign_pairs(wv << (4 * g4));
+          ops[c & 1][nb][lane] = expand_sign_pairs(sign_word_consecutive(wv) << (4 * g4));
         }
       }
     };
     auto load_chunk = [&](int64_t c, u32x4 (&x)[TS]) __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < TS; ++h)
-        x[h] = load_x_raw(X, ldx, trow + h * kProjTokens, (c >> 3) * 256 + 32 * (c & 7), g4, T, k);
+        x[h] = load_x8(X, ldx, trow + h * kProjTokens, (c >> 3) * 256 + 32 * (c & 7) + 8 * g4, T, k);
     };
     f32x4 acc[TS][NB16];
 #pragma unroll
@@ -698,16 +700,13 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
         if (s == 0 && b + 1 < nblk) gen(b + 1);
         if (c + 1 < nch) expand(c + 1);
         load_chunk(c + kPbAhead < nch ? c + kPbAhead : nch - 1, xr[(s + kPbAhead) % XR]);
-        u32x4 xp[TS];
-#pragma unroll
-        for (int h = 0; h < TS; ++h) xp[h] = x_paired_from_raw(xr[s % XR][h]);
 #pragma unroll
         for (int nb = 0; nb < NB16; ++nb) {
           const u32x4 op = ops[c & 1][nb][lane];
 #pragma unroll
           for (int h = 0; h < TS; ++h)
-            acc[h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xp[h]), as_bf16x8(op),
-                                                                 acc[h][nb], 0, 0, 0);
+            acc[h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xr[s % XR][h]),
+                                                                 as_bf16x8(op), acc[h][nb], 0, 0, 0);
         }
         __syncthreads();
       }
@@ -1726,7 +1725,7 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
   // Above 64 ranks a block takes 256 tokens of one projection at a time
   // (project_blocked_kernel); otherwise a wave takes two token steps.
   bool blocked = proj_nb16(r) > 4;
-  for (int i = 0; i < n && blocked; ++i) blocked = items[i].k % 4 == 0;  // its loads need it
+  for (int i = 0; i < n && blocked; ++i) blocked = items[i].k % 8 == 0;  // its 16-byte loads need it
   const int64_t per_tokens = blocked ? (int64_t)kPbTokens : (int64_t)kProjTokens * kProjTableSteps;
   const int64_t per = (T + per_tokens - 1) / per_tokens;  // items per entry
   // Consecutive projections of one input (same X, k and leading dimension)
