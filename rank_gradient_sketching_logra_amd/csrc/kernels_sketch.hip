@@ -1279,8 +1279,8 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
       if (k + 1 < Q) iter(k + 1, I1{});
     }
   } else if (interior) {
-    // Four or eight rank blocks (each wave computes every step of its class)
-    // are software-pipelined: iteration k's operands are in registers (a, bh,
+    // Four rank blocks (each wave computes every step of its class) are
+    // software-pipelined: iteration k's operands are in registers (a, bh,
     // bl) before it starts; its hi-term MFMAs run while the LDS reads of
     // iteration k + 1 are in flight.  Own loads in flight at the top of
     // iteration k: iterations k+1 .. k+R-1 (2 + NS each, NS without a rank
@@ -1316,7 +1316,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
                        // every wave has read iteration k's slot
       issue(k + R);
       if (!has_rb) continue;
-      const bool live = NQ == 1 || NQ * k + qt < nsteps;  // uniform per wave (always with one class)
+      const bool live = NQ * k + qt < nsteps;  // uniform per wave
       const u32x4* qs = smem + (((k + 1) % R) * kSlot + qt * kClass) * 64;
       u32x4 rn[8], bhn, bln;
       acc_read_issue(lds_addr(qs + lane), lds_addr(qs + (8 + 2 * rb) * 64 + lane), rn, bhn, bln);
@@ -1330,30 +1330,13 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
       __builtin_amdgcn_sched_barrier(0);
       acc_read_wait(rn, bhn, bln);
       clip(rn, NQ * (k + 1) + qt);
-      if constexpr (NQ == 1) {
-        // Each lo-term MFMA is followed by the transpose that overwrites its
-        // A operand with the next step's: the VALU work of one instance runs
-        // while the matrix core works on another.
+      if (live) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e],
-                                                           0, 0, 0);
-          a[e] = transpose8x8_e(rn, e);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-      } else {
-        if (live) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e],
-                                                             0, 0, 0);
-        }
-        transpose8x8(rn, a);
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[e]), as_bf16x8(bl), acc[e], 0,
+                                                           0, 0);
       }
+      transpose8x8(rn, a);
       bh = bhn;
       bl = bln;
     }
