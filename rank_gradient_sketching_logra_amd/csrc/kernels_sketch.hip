@@ -1092,8 +1092,10 @@ struct AccTile {
   int nsteps, nrb;
 };
 
-template <int RB>
-__device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
+// loop_done() runs once the tile's loads have all landed, before the class
+// sums meet and S is updated.
+template <int RB, typename LoopDone>
+__device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem, LoopDone&& loop_done) {
   using Sh = AccShape<RB>;
   constexpr int R = Sh::R, NQ = Sh::NQ, NS = Sh::NS, RBW = Sh::RBW;
   constexpr int kClass = Sh::kClass, kSlot = Sh::kSlot;
@@ -1363,8 +1365,13 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
     }
   }
   wait_vmcnt<0>();  // no load may still target LDS past this point
+  loop_done();
 
-  float* __restrict__ S = tile.S;
+  // S through the global address space: flat accesses also count on the LDS
+  // counter, so every wait for an LDS access below would wait for them too
+  // (with flat stores, each row's store would wait for the one before).
+  typedef __attribute__((address_space(1))) float gf32;
+  gf32* __restrict__ S = (gf32*)tile.S;
   const int64_t r = tile.r;
   // Class sums in accumulator order: element (e, j) of lane l at
   // [slot][(4e + j / 4) 64 + l] as float4, one 32 KiB slot per wave.
@@ -1442,7 +1449,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
     ring_barrier();
     wait_vmcnt<0>();  // the S loads (long complete): no waits between the stores below
     if (jok) {
-      float* p = S + row0 * r + j;
+      gf32* p = S + row0 * r + j;
 #pragma unroll
       for (int k = 0; k < kRowsPerThread; ++k) {
         if (row0 + kAccWaves * k < d) *p = sv[k] + yt[(wave + kAccWaves * k) * YS + lane];
@@ -1467,7 +1474,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem) {
     if (j >= r) return;
     // The block's rows of S start at a wave-uniform base; lane offsets are
     // 32-bit (256 rows x r <= 65536 floats).
-    float* __restrict__ Sb = S + c0 * r;
+    gf32* __restrict__ Sb = S + c0 * r;
     const uint32_t ur = (uint32_t)r;
     const int nrows = d - c0 < kAccCols ? (int)(d - c0) : kAccCols;
     float cur[16], nxt[16];
@@ -1509,7 +1516,7 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_kernel(AccGroupArgs g) {
   while (logical >= g.tile_begin[item + 1]) ++item;
   const AccTile tile{static_cast<const uint16_t*>(g.D[item]), g.planes[item], g.S[item], g.d[item],
                      g.ldd[item], logical - g.tile_begin[item], g.T, g.r, g.nsteps, g.nrb};
-  acc_tile<RB>(tile, smem);
+  acc_tile<RB>(tile, smem, [] {});
 }
 
 // Persistent form over a device-resident table of many matrices (e.g. every
@@ -1556,11 +1563,19 @@ __global__ __launch_bounds__(512, 1) void acc_bf16_table_kernel(const AccTableEn
     const AccTableEntry& e = tab[lo];
     const AccTile tile{static_cast<const uint16_t*>(e.D), e.planes, e.S, e.d, e.ldd,
                        t - e.tile_begin, T, r, nsteps, nrb};
-    acc_tile<RB>(tile, smem);
-    // Slot it & 1 is written again two tiles on, after a barrier every
-    // thread reaches only once it has read the slot here.
-    if (threadIdx.x == 0) claimed[it & 1] = c;
-    __syncthreads();  // also: every wave is done with the LDS before the next tile's loads land
+    // The claim is stored once the tile's loads have landed (the atomic has
+    // returned by then, so its wait costs nothing).  Slot it & 1 is written
+    // again two tiles on, after a barrier every thread reaches only once it
+    // has read the slot here.
+    acc_tile<RB>(tile, smem, [&] {
+      if (threadIdx.x == 0) claimed[it & 1] = c;
+    });
+    // Every wave is done with the LDS before the next tile's loads land.  The
+    // tile's S stores need not have completed: the next tile touches other
+    // rows of S, and its waits by count only grow more conservative while
+    // stores are outstanding.
+    wait_lgkmcnt0();
+    ring_barrier();
     t = begin + per + (int64_t)claimed[it & 1];
   }
 }
