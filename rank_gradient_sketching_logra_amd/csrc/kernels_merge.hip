@@ -237,10 +237,14 @@ struct MergeGroupArgs {
   int64_t ldw[kMaxGroup];
   int64_t row0[kMaxGroup];
   int64_t unit_begin[kMaxGroup + 1];      // first unit of each matrix
-  // per > 0: block-per-run schedule instead of equal shares -- matrix i has
-  // blocks [block_begin[i], block_begin[i + 1]), block (cb, g) of it taking
-  // bands [g per, g per + per) of column block cb (cb fastest).
-  int64_t per;
+  // runs: block-per-run schedule instead of equal shares -- matrix i has
+  // blocks [block_begin[i], block_begin[i + 1]).  With pack[i] > 1 block j
+  // of it takes every band of column blocks [j pack, (j + 1) pack); else
+  // block (cb, g) of it (cb fastest) takes bands [g nb / m, (g + 1) nb / m)
+  // of column block cb, m = nruns[i] runs of nearly equal length.
+  int runs;
+  int nruns[kMaxGroup];
+  int pack[kMaxGroup];
   int64_t block_begin[kMaxGroup + 1];
   int64_t nblocks;  // blocks with work; the grid is padded to a multiple of 8
   int n;
@@ -288,15 +292,23 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   if (lb >= g.nblocks) return;  // padding (uniform per block, before any barrier)
 
   int64_t pos, pos_end;
-  if (g.per > 0) {
+  if (g.runs) {
     int it = 0;
     while (lb >= g.block_begin[it + 1]) ++it;
     const int64_t nb = (g.d[it] + 31) / 32;
     const int64_t ncb = (g.unit_begin[it + 1] - g.unit_begin[it]) / nb;
     const int64_t local = lb - g.block_begin[it];
-    const int64_t cb = local % ncb, bg = local / ncb;
-    pos = g.unit_begin[it] + cb * nb + bg * g.per;
-    pos_end = pos + (bg * g.per + g.per < nb ? g.per : nb - bg * g.per);
+    if (g.pack[it] > 1) {
+      const int64_t cb0 = local * g.pack[it];
+      const int64_t cb1 = cb0 + g.pack[it] < ncb ? cb0 + g.pack[it] : ncb;
+      pos = g.unit_begin[it] + cb0 * nb;
+      pos_end = g.unit_begin[it] + cb1 * nb;
+    } else {
+      const int64_t m = g.nruns[it];
+      const int64_t cb = local % ncb, bg = local / ncb;
+      pos = g.unit_begin[it] + cb * nb + bg * nb / m;
+      pos_end = g.unit_begin[it] + cb * nb + (bg + 1) * nb / m;
+    }
   } else {
     const int64_t total = g.unit_begin[g.n];
     pos = lb * total / g.nblocks;
@@ -826,37 +838,52 @@ hipError_t launch_merge_grouped(const MergeItem* items, int n, int64_t r, double
   // but may split a column block's run of bands over two blocks (each
   // then builds the block's A operands and fills its ring), and the blocks
   // running at one time hold different bands, so each fetches its own
-  // packed U.  Runs of a fixed length per column block avoid both -- the
-  // column blocks of a run are consecutive logical blocks on one XCD, so
-  // they read the run's U bands from that XCD's L2 -- and are taken when
-  // their longest run is within kMergeRunSlack percent of an equal share.
+  // packed U.  Runs avoid both: the column blocks of one band range are
+  // consecutive logical blocks on one XCD, so they read the range's U from
+  // that XCD's L2.  Each matrix takes m runs of nearly equal length per
+  // column block, or, when its column blocks are short, several whole
+  // column blocks per block; the run length L starts at the equal share
+  // and grows until the runs fit the compute units.  The runs are taken
+  // when the longest is within kMergeRunSlack percent of the equal share.
   const int64_t cus = compute_units();
   const int64_t total = g.unit_begin[n];
   if (total == 0) return hipSuccess;
   int64_t blocks = total < cus ? total : cus;
   const int64_t share = (total + blocks - 1) / blocks;
-  int64_t maxbands = 1;
-  for (int i = 0; i < n; ++i) maxbands = std::max(maxbands, (items[i].d + 31) / 32);
-  auto runs_for = [&](int64_t p) {
-    int64_t b = 0;
-    for (int i = 0; i < n; ++i) {
-      const int64_t nb = (items[i].d + 31) / 32;
-      b += (g.unit_begin[i + 1] - g.unit_begin[i]) / (nb > 0 ? nb : 1) * ((nb + p - 1) / p);
-    }
-    return b;
-  };
-  int64_t per = share;
-  while (per < maxbands && runs_for(per) > cus) ++per;
-  g.per = 0;
-  if (per * 100 <= share * kMergeRunSlack) {
-    g.per = per;
-    g.block_begin[0] = 0;
+  g.runs = 0;
+  for (int64_t L = share; L <= 2 * share; ++L) {
+    int64_t nblk = 0, worst = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t nb = (items[i].d + 31) / 32;
       const int64_t ncb = nb > 0 ? (g.unit_begin[i + 1] - g.unit_begin[i]) / nb : 0;
-      g.block_begin[i + 1] = g.block_begin[i] + ncb * ((nb + per - 1) / per);
+      if (2 * nb <= L) {
+        const int64_t c = std::min<int64_t>(std::max<int64_t>(L / nb, 1), std::max<int64_t>(ncb, 1));
+        g.pack[i] = (int)c;
+        g.nruns[i] = 1;
+        nblk += (ncb + c - 1) / c;
+        worst = std::max(worst, c * nb);
+      } else {
+        const int64_t m = (nb + L - 1) / L;
+        g.pack[i] = 1;
+        g.nruns[i] = (int)m;
+        nblk += ncb * m;
+        worst = std::max(worst, (nb + m - 1) / m);
+      }
     }
-    blocks = g.block_begin[n];
+    if (nblk <= cus) {
+      if (worst * 100 <= share * kMergeRunSlack) {
+        g.runs = 1;
+        g.block_begin[0] = 0;
+        for (int i = 0; i < n; ++i) {
+          const int64_t nb = (items[i].d + 31) / 32;
+          const int64_t ncb = nb > 0 ? (g.unit_begin[i + 1] - g.unit_begin[i]) / nb : 0;
+          g.block_begin[i + 1] = g.block_begin[i] +
+                                 (g.pack[i] > 1 ? (ncb + g.pack[i] - 1) / g.pack[i] : ncb * g.nruns[i]);
+        }
+        blocks = g.block_begin[n];
+      }
+      break;
+    }
   }
   g.nblocks = blocks;
   const dim3 grid((unsigned)((blocks + 7) / 8 * 8));
