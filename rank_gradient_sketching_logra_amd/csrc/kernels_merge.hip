@@ -150,6 +150,12 @@ __device__ __forceinline__ void merge_wait_vmcnt() {
 __device__ __forceinline__ void dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
+// The same with the non-temporal hint (cache policy NT), for W: each of its
+// lines is read once and written once, so it should not displace the packed
+// update that the column blocks of a run share in L2.
+__device__ __forceinline__ void dma16_nt(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 2);
+}
 
 // LDS accesses of the streamed tiles are written as statements the compiler
 // cannot order against the direct loads still in flight (it would otherwise
@@ -637,7 +643,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
           const int a = (wave * WL + t) * RPL + lane / CH;
           const int pos = lane % CH;
           const int chunk = pos ^ (a & (CH - 1));
-          dma16(W + (band * 32 + a) * ldw + cblk + 8 * chunk, wt + (wave * WL + t) * 64);
+          dma16_nt(W + (band * 32 + a) * ldw + cblk + 8 * chunk, wt + (wave * WL + t) * 64);
         }
 #pragma unroll
         for (int t = 0; t < UL; ++t) {
@@ -732,7 +738,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         }
         lds_wait();
         merge_barrier();  // the whole tile is updated
-        // Whole-row stores, in the load's lane order.
+        // Whole-row stores, in the load's lane order, non-temporal as the loads.
         u32x4 ov[WL];
         lds_read_slabs<WL>(lds_u32(wt + (wave * WL) * 64 + lane), ov);
 #pragma unroll
@@ -740,7 +746,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
           const int a = (wave * WL + t) * RPL + lane / CH;
           const int pos = lane % CH;
           const int chunk = pos ^ (a & (CH - 1));
-          *reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk) = ov[t];
+          __builtin_nontemporal_store(ov[t], reinterpret_cast<u32x4*>(W + (band * 32 + a) * ldw + cblk + 8 * chunk));
         }
       }
       merge_wait_vmcnt<0>();

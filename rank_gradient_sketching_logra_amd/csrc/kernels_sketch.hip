@@ -354,8 +354,8 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_bf16_kernel(
                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
       }
       uint16_t* dst = planes + ((int64_t)blockIdx.x * nrb + b) * 1024 + lane * 8;
-      *reinterpret_cast<u32x4*>(dst) = vh;
-      *reinterpret_cast<u32x4*>(dst + 512) = vl;
+      __builtin_nontemporal_store(vh, reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(vl, reinterpret_cast<u32x4*>(dst + 512));
     }
   }
 }
@@ -545,7 +545,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
         const int m = idx / (int)r;
         const int j = idx - m * (int)r;
         const int64_t t = t0 + m;
-        if (t < T) XAt[t * r + j] = rw[m][j] * cr;
+        if (t < T) __builtin_nontemporal_store(rw[m][j] * cr, XAt + t * r + j);
       }
     }
     if (e.planes[pj]) {
@@ -566,9 +566,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
           vl[p] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
         }
+        // non-temporal: the planes are read by a later launch, not from L2
         uint16_t* dst = e.planes[pj] + (st * nrb + b) * 1024 + lane * 8;
-        *reinterpret_cast<u32x4*>(dst) = vh;
-        *reinterpret_cast<u32x4*>(dst + 512) = vl;
+        __builtin_nontemporal_store(vh, reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(vl, reinterpret_cast<u32x4*>(dst + 512));
       }
     }
     asm volatile("" ::: "memory");  // this tile's LDS reads before the next tile's writes
@@ -729,7 +730,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
           const int m = idx / (int)r;
           const int j = idx - m * (int)r;
           const int64_t t = t0 + m;
-          if (t < T) XAt[t * r + j] = rw[m][j] * cr;
+          if (t < T) __builtin_nontemporal_store(rw[m][j] * cr, XAt + t * r + j);
         }
       }
       if (e.planes[0]) {
@@ -751,8 +752,8 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void project_blocked_kernel(
                     ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lv[2 * p + 1]) << 16);
           }
           uint16_t* dst = e.planes[0] + (st * nrb + bb) * 1024 + lane * 8;
-          *reinterpret_cast<u32x4*>(dst) = vh;
-          *reinterpret_cast<u32x4*>(dst + 512) = vl;
+          __builtin_nontemporal_store(vh, reinterpret_cast<u32x4*>(dst));
+          __builtin_nontemporal_store(vl, reinterpret_cast<u32x4*>(dst + 512));
         }
       }
       asm volatile("" ::: "memory");  // this step's LDS reads before the next step's writes
@@ -849,8 +850,8 @@ __global__ __launch_bounds__(256) void acc_pack_kernel(AccGroupArgs g) {
     vl[p] = pack_bf16x2(l[2 * p], l[2 * p + 1]);
   }
   uint16_t* dst = g.planes[item] + chunk * 1024 + lane * 8;
-  *reinterpret_cast<u32x4*>(dst) = vh;
-  *reinterpret_cast<u32x4*>(dst + 512) = vl;
+  __builtin_nontemporal_store(vh, reinterpret_cast<u32x4*>(dst));
+  __builtin_nontemporal_store(vl, reinterpret_cast<u32x4*>(dst + 512));
 }
 
 // Eight bf16 of row t of D from column col; zero outside the matrix.
@@ -1003,17 +1004,23 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // Direct global->LDS loads of N 1 KiB row slabs at dst: rows prow,
-// prow + ldd, ...; lane l's 16 bytes land at byte 16 l of each.
+// prow + ldd, ...; lane l's 16 bytes land at byte 16 l of each.  D is read
+// once, so its loads carry the non-temporal hint (cache policy NT) and do not
+// displace the packed input, which the column tiles of a matrix share in L2.
 template <int N>
 __device__ __forceinline__ void acc_issue_rows(u32x4* dst, const uint16_t* prow, int64_t ldd) {
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_global_load_lds(prow + i * ldd, dst + i * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(prow + i * ldd, dst + i * 64, 16, 0, 2);
 }
 
 // Direct global->LDS load of one 1 KiB slab from p to dst.
 __device__ __forceinline__ void acc_issue_slab(u32x4* dst, const uint16_t* p) {
   __builtin_amdgcn_global_load_lds(p, dst, 16, 0, 0);
+}
+// The same with the non-temporal hint, for slabs of D.
+__device__ __forceinline__ void acc_issue_slab_nt(u32x4* dst, const uint16_t* p) {
+  __builtin_amdgcn_global_load_lds(p, dst, 16, 0, 2);
 }
 
 // acc[e] += A_e B over one 16-token step, hi term then lo term.
@@ -1154,7 +1161,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem, LoopD
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int64_t t = t0 + i < T ? t0 + i : T - 1;
-        acc_issue_slab(qs + (NS * rb + i) * 64, D + t * ldd + col);
+        acc_issue_slab_nt(qs + (NS * rb + i) * 64, D + t * ldd + col);
       }
     }
   };
@@ -1220,7 +1227,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem, LoopD
         const int sc = st < nsteps ? st : nsteps - 1;
         const int64_t t0 = (int64_t)kAccStep * sc + 8 * hw + rb;
         const int64_t t = t0 < T ? t0 : T - 1;
-        acc_issue_slab(smem + ((st % RD) * 8 + rb) * 64, D + t * ldd + col);
+        acc_issue_slab_nt(smem + ((st % RD) * 8 + rb) * 64, D + t * ldd + col);
       };
 #pragma unroll
       for (int j = 0; j < RD - P; ++j) issue_d(j);
