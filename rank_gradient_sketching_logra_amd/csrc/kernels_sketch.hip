@@ -396,8 +396,9 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // counter, so items are handed out in order and the fast waves take more.
 // Per item: for each 256-column block in order, the next block's X loads in
 // flight, the signs of the lane's rank (one Philox block per 64 ranks)
-// expanded in the paired column order, eight 16x16x32 MFMA steps per token
-// step; the sums
+// expanded in the paired column order (X16: the inputs as 16-byte loads of
+// eight consecutive columns, the sign words rearranged to match), eight
+// 16x16x32 MFMA steps per token step; the sums
 // run over the column blocks in ascending order in one accumulator.  The
 // tile then goes through the wave's own LDS rows to the fp32 output and/or
 // the accumulate's packed operand form, as in project_bf16_kernel.  The
@@ -407,7 +408,7 @@ constexpr int kPtWaves = 4;  // waves per block of the table projection
 // Token steps per work item of the table projection.
 constexpr int kProjTableSteps = 2;
 
-template <int NB16>
+template <int NB16, bool X16>
 __global__ __launch_bounds__(kPtWaves * 64)
 __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
     const ProjTableEntry* __restrict__ tab, unsigned* __restrict__ next, int n, int64_t T,
@@ -467,7 +468,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
       for (int h = 0; h < TS; ++h)
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-          dst[h][s] = load_x_paired(X, ldx, trow + h * kProjTokens, b * 256 + 32 * s, g4, T, k);
+          dst[h][s] = X16 ? load_x8(X, ldx, trow + h * kProjTokens, b * 256 + 32 * s + 8 * g4, T, k)
+                          : load_x_paired(X, ldx, trow + h * kProjTokens, b * 256 + 32 * s, g4, T, k);
     };
     // With one token step per item the next block's X loads would be in
     // flight during this block's work; with two the block's own loads are
@@ -499,6 +501,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void project_table_kernel(
           for (int w = 0; w < 4; ++w) {
             bits[2 * w] = live ? (uint32_t)p.w[w] : 0u;
             bits[2 * w + 1] = live ? (uint32_t)(p.w[w] >> 32) : 0u;
+          }
+          if constexpr (X16) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) bits[w] = sign_word_consecutive(bits[w]);
           }
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
@@ -1701,7 +1707,7 @@ int proj_table_max() { return kProjTableMax; }
 // item counter.
 size_t proj_table_ws_bytes(int n) { return round256((size_t)(n + 2) * sizeof(ProjTableEntry)); }
 
-template <int NB>
+template <int NB, bool X16 = false>
 static hipError_t launch_project_table_nb(const ProjTableEntry* t, unsigned* next, int n,
                                           int64_t T, int64_t r, float cr, int nrb,
                                           hipStream_t s) {
@@ -1711,15 +1717,15 @@ static hipError_t launch_project_table_nb(const ProjTableEntry* t, unsigned* nex
   int per_cu = cached_per_cu.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int b = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, project_table_kernel<NB>,
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, project_table_kernel<NB, X16>,
                                                                 kPtWaves * 64, 0);
     if (e != hipSuccess) return e;
     per_cu = b > 0 ? b : 1;
     cached_per_cu.store(per_cu, std::memory_order_relaxed);
   }
   const dim3 grid((unsigned)(per_cu * compute_units()));
-  hipLaunchKernelGGL(project_table_kernel<NB>, grid, dim3(kPtWaves * 64), 0, s, t, next, n, T,
-                     r, cr, nrb);
+  hipLaunchKernelGGL((project_table_kernel<NB, X16>), grid, dim3(kPtWaves * 64), 0, s, t, next, n,
+                     T, r, cr, nrb);
   return hipGetLastError();
 }
 
@@ -1791,6 +1797,19 @@ hipError_t launch_project_table(int64_t T, int64_t r, const ProjItem* items, int
       LOGRA_PROJ_BLOCKED(16)
 #undef LOGRA_PROJ_BLOCKED
       default: return hipErrorInvalidValue;
+    }
+  }
+  // Up to 64 ranks, when every k is a multiple of 8, the inputs are loaded 16
+  // bytes at a time (eight consecutive columns) and the sign words rearranged
+  // to match, as in the block form.
+  bool x16 = true;
+  for (int i = 0; i < n && x16; ++i) x16 = items[i].k % 8 == 0;
+  if (x16) {
+    switch (proj_nb16(r)) {
+      case 1: return launch_project_table_nb<1, true>(t, next, n, T, r, cr, nrb, s);
+      case 2: return launch_project_table_nb<2, true>(t, next, n, T, r, cr, nrb, s);
+      case 4: return launch_project_table_nb<4, true>(t, next, n, T, r, cr, nrb, s);
+      default: break;
     }
   }
   switch (proj_nb16(r)) {
