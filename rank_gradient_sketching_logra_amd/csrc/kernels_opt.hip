@@ -177,9 +177,22 @@ __device__ __forceinline__ void rowadam_apply_packed_thread(int64_t t, int64_t d
     f = den > 0.0 ? ws.scalars[1] / den : 0.0;
   }
   float x[8];
+  if (i < d && j0 + 8 <= r && (r & 3) == 0) {
+    // the row's eight values as two 16-byte loads (rows of S are 16-byte
+    // aligned when r is a multiple of 4); S is read once here
+    typedef __attribute__((address_space(1))) const f32x4 gf4;
+    const gf4* ps = (const gf4*)(S + i * r + j0);
+    const f32x4 a = __builtin_nontemporal_load(ps), b = __builtin_nontemporal_load(ps + 1);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    x[q] = (i < d && j0 + q < r) ? (float)((double)S[i * r + j0 + q] * f) : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      x[q] = (float)((double)a[q] * f);
+      x[4 + q] = (float)((double)b[q] * f);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      x[q] = (i < d && j0 + q < r) ? (float)((double)S[i * r + j0 + q] * f) : 0.f;
+  }
   uint32_t hv[4], lv[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -190,12 +203,10 @@ __device__ __forceinline__ void rowadam_apply_packed_thread(int64_t t, int64_t d
     lv[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
             ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(P + bs * 1024 + lane * 8);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    dst[p] = hv[p];
-    dst[256 + p] = lv[p];
-  }
+  // one 16-byte store per term, non-temporal: the merge reads them in a later launch
+  u32x4* dst = reinterpret_cast<u32x4*>(P + bs * 1024 + lane * 8);
+  __builtin_nontemporal_store(u32x4{hv[0], hv[1], hv[2], hv[3]}, dst);
+  __builtin_nontemporal_store(u32x4{lv[0], lv[1], lv[2], lv[3]}, dst + 64);
 }
 
 __global__ __launch_bounds__(256) void rowadam_apply_packed_kernel(int64_t d, int64_t r, int ks,
