@@ -396,6 +396,41 @@ def test_project_table_fused_inputs(T, r):
         assert relfro(fused[j][0].cpu().numpy(), want) <= 1e-5
 
 
+@pytest.mark.parametrize("T,r", [(1000, 64), (777, 33), (40, 8)])
+def test_project_table_sixteen_byte_inputs(T, r):
+    """Up to 64 ranks, a table whose every k is a multiple of 8 loads its inputs 16 bytes at a
+    time and rearranges the sign words to match (k from 8 to 3584, one input shared by
+    consecutive projections, ragged T): XAt within 1e-5 of the oracle and within fp32 rounding
+    of the single-call projection, and the planes give the S bits of the table's own XAt
+    through the unpacked accumulate."""
+    say(f"project table, 16-byte inputs T={T} r={r}")
+    widths = [(512, 512), (3584, 3584), (40, 48), (1000, 1000), (8, 8)]
+    xs = []
+    for i, (k, ld) in enumerate(widths):
+        xb, X = bf16_inputs((T, ld), 1.0, (39, T, k, i, 0))
+        xs.append((bf16_dev(xb)[:, :k], X[:, :k]))
+    order = [0, 0, 0, 1, 2, 3, 3, 4]   # input of each projection, in table order
+    nb = B.packed_input_bytes(T, r)
+    outs = [(torch.full((T, r), float("nan"), device=DEV), torch.zeros((nb,), dtype=torch.uint8, device=DEV))
+            for _ in order]
+    B.project_input_table([(B.key(11, j, 4), xs[xi][0], xo, po)
+                           for j, (xi, (xo, po)) in enumerate(zip(order, outs))], r)
+    d = 200
+    db, _ = bf16_inputs((T, d), 1e-3, (39, T, d, 0, 1))
+    D = bf16_dev(db)
+    S0 = synth.fp32_matrix((d, r), 0.1, (39, d, r, 0, 5))
+    for j, xi in enumerate(order):
+        Xd, X = xs[xi]
+        xo, po = outs[j]
+        assert relfro(xo.cpu().numpy(), oracle.project(X, oracle.regen_A(11, j, 4, r, X.shape[1]))) <= 1e-5
+        assert relfro(xo.cpu().numpy(), B.project_input(B.key(11, j, 4), Xd, r).cpu().numpy()) <= 1e-6
+        Sp = torch.from_numpy(S0.copy()).to(DEV)
+        B.sketch_accumulate_grouped_packed([(D, po, Sp)], r)
+        Su = torch.from_numpy(S0.copy()).to(DEV)
+        B.sketch_accumulate_grouped([(D, xo, Su)])
+        assert torch.equal(Sp.view(torch.int32), Su.view(torch.int32))
+
+
 def test_project_table_many_items_per_wave():
     """More work items (two 16-token steps each) than the grid has waves, so every wave claims
     several in turn: every XAt within fp32 rounding of the single-call projection, two against
