@@ -142,7 +142,15 @@ __device__ __forceinline__ Philox4x32 sr_block(KeyWords key, uint64_t g) {
 }
 
 __device__ __forceinline__ uint32_t sr_draw(const Philox4x32& p, uint64_t e) {
-  return (p.w[(e & 7) >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  // The word is picked by selects on register values, not by indexing: an
+  // indexed pick (which the compiler also forms from selects of the array's
+  // elements) puts the block in private or LDS memory and makes the kernel
+  // wait for it.
+  uint32_t w0 = p.w[0], w1 = p.w[1], w2 = p.w[2], w3 = p.w[3];
+  asm("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+  const uint32_t i = (uint32_t)(e & 7) >> 1;
+  const uint32_t w = (i & 2) ? ((i & 1) ? w3 : w2) : ((i & 1) ? w1 : w0);
+  return (w >> (16 * (uint32_t)(e & 1))) & 0xFFFFu;
 }
 
 // ------------------------------------------------------------- bf16 bits

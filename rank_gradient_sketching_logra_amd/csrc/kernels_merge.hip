@@ -65,11 +65,12 @@ __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t
 // acc[0..15] of consecutive columns, element index e0 of the first (for the
 // stochastic-rounding draws).  aligned: e0 is a multiple of 16, so the
 // sixteen draws are exactly two generator blocks, element t taking bits
-// [16 (t & 1), +16) of word (t & 7) >> 1 of block t >> 3.
-template <bool STOCH>
+// [16 (t & 1), +16) of word (t & 7) >> 1 of block t >> 3.  PRE (aligned
+// only): the two blocks were generated earlier by the caller, in pre.
+template <bool STOCH, bool PRE = false>
 __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const f32x16& acc,
                                          float sc, KeyWords srk, uint64_t e0, bool aligned,
-                                         u32x4& o0, u32x4& o1) {
+                                         u32x4& o0, u32x4& o1, const u32x4* pre = nullptr) {
   uint32_t out[8];
   auto value = [&](int t) __attribute__((always_inline)) {
     const uint32_t word = (t < 8) ? w0[t >> 1] : w1[(t - 8) >> 1];
@@ -102,13 +103,21 @@ __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const
     for (int t = 0; t < 16; ++t) v[t] = value(t);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
+      uint32_t pw[4];
+      if constexpr (PRE) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pw[q] = pre[h][q];
+      } else {
+        const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pw[q] = p.w[q];
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // both halves are written, so pk may start as any value
-        s16x2 pk = __builtin_bit_cast(s16x2, p.w[q] << 16);
-        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q], p.w[q] << 16, false);
-        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q + 1], p.w[q], true);
+        s16x2 pk = __builtin_bit_cast(s16x2, pw[q] << 16);
+        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q], pw[q] << 16, false);
+        pk = __builtin_amdgcn_cvt_sr_bf16_f32(pk, v[8 * h + 2 * q + 1], pw[q], true);
         out[4 * h + q] = __builtin_bit_cast(uint32_t, pk);
       }
     }
@@ -281,6 +290,11 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   // operands (KS hi slabs, KS lo slabs).  The sign bits live in the ring
   // until the A operands are built.
   __shared__ __align__(16) u32x4 lds[NR * SLOT + (PACKED ? 0 : UT)];
+  // With many rank steps (the MFMA chain long against the rounding), the
+  // stochastic-rounding draws of a band are generated inside the chain and
+  // parked here until the rounding: two generator blocks per instance.
+  constexpr bool kDrawsInChain = STOCH && PACKED && !EXPLICIT && KS >= 8;
+  __shared__ __align__(16) u32x4 draws[kDrawsInChain ? NWV * 2 * E * 64 : 1];
   static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
@@ -492,11 +506,16 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       }
     };
 
+    constexpr int kPackedGroup = KS < 4 ? KS : (KS == 16 && E == 2) ? 2 : 4;
     // C of one band from packed U slabs in LDS (slab 2s the hi term, 2s + 1
     // the lo term of step s, 1 KiB apart): the slabs of G steps are read in
     // one group and waited for once, so a band takes KS / G LDS round trips.
-    auto mfma_band_packed = [&](f32x16 (&acc)[E], const u32x4* ut) __attribute__((always_inline)) {
-      constexpr int G = KS < 4 ? KS : (KS == 16 && E == 2) ? 2 : 4;
+    // after_group(i) runs after the MFMAs of group i, in the same scheduling
+    // region, so independent vector work placed there issues while the
+    // matrix cores are busy.
+    auto mfma_band_packed = [&](f32x16 (&acc)[E], const u32x4* ut, auto&& after_group)
+                                __attribute__((always_inline)) {
+      constexpr int G = kPackedGroup;
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
@@ -523,6 +542,7 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
                                                                as_bf16x8(x[2 * i]), acc[e], 0, 0, 0);
           }
         }
+        after_group(s0 / G);
         if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -718,21 +738,49 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
           wa[2 * e] = lds_u32(wt + n * CH + (cc ^ (n & (CH - 1))));
           wa[2 * e + 1] = lds_u32(wt + n * CH + ((cc + 1) ^ (n & (CH - 1))));
         }
+        const int64_t row = band * 32 + n;
+        // The draws (aligned k) are generated one block after each of the
+        // first 2E groups of the chain; they depend only on the element
+        // index, not on the products.
+        static_assert(!kDrawsInChain || KS / kPackedGroup >= 2 * E, "one draw block per group");
+        // The W values are read before the chain, or, with the draws in it,
+        // after it (the draws take their registers meanwhile).
         u32x4 wx[2 * E];
-        lds_read_at(wa, wx);
+        if constexpr (!kDrawsInChain) lds_read_at(wa, wx);
         f32x16 acc[E];
+        u32x4 pre[E][2];
         if constexpr (PACKED) {
-          mfma_band_packed(acc, ut);
+          mfma_band_packed(acc, ut, [&](int grp) __attribute__((always_inline)) {
+            if constexpr (kDrawsInChain) {
+              if (grp < 2 * E) {
+                const int e = grp >> 1, h = grp & 1;
+                const uint64_t e0 =
+                    (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw);
+                const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
+                lds_write16(lds_u32(draws + (wave * 2 * E + grp) * 64 + lane),
+                            u32x4{p.w[0], p.w[1], p.w[2], p.w[3]});
+              }
+            }
+          });
         } else {
           mfma_band(acc, bfrag_lds);
         }
-        const int64_t row = band * 32 + n;
+        if constexpr (kDrawsInChain) {
+          lds_read_at(wa, wx);
+          u32x4 dv[2 * E];
+          lds_read_slabs<2 * E>(lds_u32(draws + (wave * 2 * E) * 64 + lane), dv);
+#pragma unroll
+          for (int b = 0; b < 2 * E; ++b) pre[b >> 1][b & 1] = dv[b];
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           u32x4 o0, o1;
-          update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk,
-                          (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw),
-                          sr_aligned, o0, o1);
+          const uint64_t e0 = (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw);
+          if (kDrawsInChain && sr_aligned)
+            update16<STOCH, kDrawsInChain>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk, e0, true, o0, o1,
+                                           pre[e]);
+          else
+            update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk, e0, sr_aligned, o0, o1);
           lds_write16(wa[2 * e], o0);
           lds_write16(wa[2 * e + 1], o1);
         }
