@@ -1214,8 +1214,12 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem, LoopD
       constexpr int P = kAccBAhead, NB = P + 1, RD = P + 2;
       typedef __attribute__((address_space(1))) const u32x4 gb4;
       typedef __attribute__((address_space(1))) const uint16_t gb16;
+      // Only a ragged last step has rows past T.  The empty volatile asm
+      // keeps this a branch: flattened into selects it costs every step
+      // some forty vector instructions while the matrix cores wait.
       auto clip = [&](u32x4 (&row)[8], int s) __attribute__((always_inline)) {
-        if ((int64_t)kAccStep * (s + 1) > T) {
+        if (__builtin_expect((int64_t)kAccStep * (s + 1) > T, 0)) {
+          asm volatile("");
           const int64_t t0 = (int64_t)kAccStep * s + 8 * hw;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
