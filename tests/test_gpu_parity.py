@@ -752,7 +752,8 @@ def test_merge_grouped_packed_equals_fp32_update(r, mode):
         assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
 
 
-@pytest.mark.parametrize("r,mode", [(64, "stochastic"), (33, "nearest"), (256, "stochastic")])
+@pytest.mark.parametrize("r,mode", [(64, "stochastic"), (33, "nearest"), (100, "stochastic"),
+                                    (256, "stochastic")])
 def test_sync_payload_trainer_and_rollout_agree(r, mode):
     """Policy sync ([paper] §2.2): the trainer packs fl32(alpha eta U) once; its own merge from the
     payload and the rollout side's sync_apply give identical weights, and both match the oracle's
