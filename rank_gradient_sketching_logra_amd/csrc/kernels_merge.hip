@@ -202,6 +202,22 @@ __device__ __forceinline__ void lds_read_slabs(uint32_t a, u32x4 (&x)[N]) {
         : "memory");
   }
 }
+// The same N reads, issued only; the registers are valid after
+// lds_wait_slabs() (the outputs stay tied to the wait, so they are neither
+// read nor reused before it).
+template <int N>
+__device__ __forceinline__ void lds_issue_slabs(uint32_t a, u32x4 (&x)[N]) {
+  static_assert(N == 4, "slab count");
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(a) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_slabs(u32x4 (&x)[N]) {
+  static_assert(N == 4, "slab count");
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : : "memory");
+}
 // 16-byte reads at two or four arbitrary addresses.
 __device__ __forceinline__ void lds_read_at(const uint32_t (&a)[2], u32x4 (&x)[2]) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
@@ -520,10 +536,21 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
       for (int e = 0; e < E; ++e)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[e][i] = 0.f;
+      // With several groups, group g + 1's slabs are read while group g's
+      // MFMAs run (two register sets).
+      constexpr bool kAhead = KS / G >= 2 && 2 * G == 4;
+      u32x4 x[2 * G];
+      if constexpr (kAhead) lds_read_slabs<2 * G>(lds_u32(ut + lane), x);
 #pragma unroll
       for (int s0 = 0; s0 < KS; s0 += G) {
-        u32x4 x[2 * G];
-        lds_read_slabs<2 * G>(lds_u32(ut + (2 * s0) * 64 + lane), x);
+        u32x4 xn[2 * G];
+        const bool more = kAhead && s0 + G < KS;  // a constant once unrolled
+        if constexpr (kAhead) {
+          if (more) lds_issue_slabs<2 * G>(lds_u32(ut + (2 * (s0 + G)) * 64 + lane), xn);
+          __builtin_amdgcn_sched_barrier(0);  // the reads go out before this group's MFMAs
+        } else {
+          lds_read_slabs<2 * G>(lds_u32(ut + (2 * s0) * 64 + lane), x);
+        }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           const int s = s0 + i;
@@ -543,6 +570,14 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
           }
         }
         after_group(s0 / G);
+        if constexpr (kAhead) {
+          if (more) {
+            __builtin_amdgcn_sched_barrier(0);  // and are waited for after them
+            lds_wait_slabs<2 * G>(xn);
+#pragma unroll
+            for (int i = 0; i < 2 * G; ++i) x[i] = xn[i];
+          }
+        }
         if constexpr (KS > 8) __builtin_amdgcn_sched_barrier(0);
       }
     };
