@@ -61,6 +61,16 @@ __device__ __forceinline__ void load_w16(const uint16_t* __restrict__ W, int64_t
   }
 }
 
+// Whether any of sixteen values is NaN: their sum is NaN whenever one of
+// them is (and also for +inf beside -inf, which only costs a pass that finds
+// nothing).  Timed faster than unordered compares of pairs.
+__device__ __forceinline__ bool any_nan16(const float (&v)[16]) {
+  float sum = v[0];
+#pragma unroll
+  for (int t = 1; t < 16; ++t) sum += v[t];
+  return __builtin_isnan(sum);
+}
+
 // Sixteen updated bf16 of one lane: W values w (two words), products
 // acc[0..15] of consecutive columns, element index e0 of the first (for the
 // stochastic-rounding draws).  aligned: e0 is a multiple of 16, so the
@@ -86,8 +96,18 @@ __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = 0u;
   if constexpr (!STOCH) {
+    // The hardware conversion keeps a NaN's (quieted) payload; a NaN is
+    // returned as the quiet NaN of its sign, as in the stochastic path.
+    float v[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) put(t, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)value(t)));
+    for (int t = 0; t < 16; ++t) v[t] = value(t);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) put(t, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t]));
+    if (any_nan16(v)) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (__builtin_isnan(v[t])) put(t, f32_to_bf16_rne(v[t]));
+    }
   } else if (aligned) {
     // v_cvt_sr_bf16_f32 adds the high 16 bits of its second operand to the
     // discarded half of the fp32 pattern and truncates: the rule above for
@@ -95,9 +115,8 @@ __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const
     // an odd element takes its generator word as it is (its draw is the high
     // half) and an even one the word shifted up by 16; the two results of a
     // pair fill the halves of one output word.  NaN is the one case the
-    // instruction rounds differently: the sum of the sixteen values is NaN
-    // whenever one of them is, and only then do the NaN elements take the
-    // quiet NaN of their sign.
+    // instruction rounds differently: when any of the sixteen values is NaN,
+    // the NaN elements take the quiet NaN of their sign.
     float v[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) v[t] = value(t);
@@ -121,10 +140,7 @@ __device__ __forceinline__ void update16(const u32x4& w0, const u32x4& w1, const
         out[4 * h + q] = __builtin_bit_cast(uint32_t, pk);
       }
     }
-    float sum = v[0];
-#pragma unroll
-    for (int t = 1; t < 16; ++t) sum += v[t];
-    if (__builtin_isnan(sum)) {
+    if (any_nan16(v)) {
 #pragma unroll
       for (int t = 0; t < 16; ++t)
         if (__builtin_isnan(v[t])) put(t, f32_to_bf16_rne(v[t]));

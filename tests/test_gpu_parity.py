@@ -629,6 +629,39 @@ def test_merge_bf16(d, k, r, mode, ldw):
     assert exact >= 0.999
 
 
+@pytest.mark.parametrize("r,mode,k", [(64, "nearest", 512), (64, "stochastic", 512), (64, "stochastic", 520),
+                                      (256, "nearest", 1024), (256, "stochastic", 1024)])
+def test_merge_special_values(r, mode, k):
+    """NaN (quiet and signalling, both signs) and infinities in W through the packed merge the
+    benchmark times and the fp32-U merge: a NaN becomes the quiet NaN of its sign and an
+    infinity stays itself, bit for bit as the oracle rounds them, and every other element meets
+    the merge bar.  k = 520 takes the stochastic path for k not a multiple of 16; 256 ranks the
+    path whose draws are generated inside the MFMA chain."""
+    d = 96
+    say(f"merge special values r={r} {mode} k={k}")
+    wbits = synth.normal((d, k), 0.02, (41, d, k, r, 2), "bf16").copy()
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x7F81, 0xFFA5], np.uint16)
+    ii, jj = np.nonzero((np.arange(d)[:, None] * 7 + np.arange(k)[None, :] * 13) % 89 == 0)
+    wbits[ii, jj] = specials[np.arange(len(ii)) % len(specials)]
+    special = np.zeros((d, k), bool)
+    special[ii, jj] = True
+    U = synth.fp32_matrix((d, r), 1.0, (41, d, r, 0, 7))
+    kk = B.key(2, 9, 1)
+    A = oracle.regen_A(2, 9, 1, r, k)
+    u = philox.sr_draws(4, 9, 1, d, k) if mode == "stochastic" else None
+    want = oracle.merge(oracle.bf16_bits_to_f64(wbits), U.astype(np.float64), A, 3e-4, w_dtype="bf16",
+                        mode=mode, u_draws=u)
+    W1, W2 = bf16_dev(wbits), bf16_dev(wbits)
+    Ud = torch.from_numpy(U).to(DEV)
+    B.merge_grouped_packed([(kk, W1, B.pack_update(Ud))], r, 3e-4, mode=mode, sr_seed=4)
+    B.merge(kk, W2, Ud, 3e-4, mode=mode, sr_seed=4)
+    assert torch.equal(W1.view(torch.int16), W2.view(torch.int16))
+    got = bf16_host(W1)
+    assert np.array_equal(got[special], want[special])
+    frac, exact = ulp_check(got[~special], want[~special])
+    assert frac >= 0.9999 and exact >= 0.999
+
+
 @pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "nearest"), (256, "stochastic")])
 def test_merge_grouped_equals_single_merges(r, mode):
     """One grouped launch over matrices of mixed shapes (full, ragged column and row edges, small)
