@@ -46,7 +46,8 @@ from . import philox
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Decode bf16 bit patterns (uint16) to fp64: a bf16 is the top half of an fp32."""
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return u32.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # a signalling NaN widens to a quiet NaN of its sign
+        return u32.view(np.float32).astype(np.float64)
 
 
 def f32_to_bf16_rne(x32: np.ndarray) -> np.ndarray:
