@@ -494,7 +494,8 @@ LOGRA_API int logra_step_alpha_dev(const float* q_dev, float delta, float alpha_
  * is the received alpha*eta*U and scale = 1 ([paper] §2.2 "Memory and
  * synchronization").  W is bf16 (mode NEAREST or STOCHASTIC) or fp32 (NEAREST
  * only), leading dimension ldw >= k.  U [d x r] fp32 contiguous.  The update
- * is formed in fp32 and rounded once to W's type.  row0 is the global index
+ * is formed in fp32 and rounded once to W's type; for bf16 W a NaN becomes
+ * the quiet NaN of its sign and an infinity stays itself.  row0 is the global index
  * of W's first row (for row-sharded merges: stochastic-rounding draws are
  * indexed by (row0 + i) * k + l, so a merge of a row block equals the same
  * rows of a whole-matrix merge).  Two merges of equal W with equal
