@@ -1216,7 +1216,7 @@ __device__ __forceinline__ void acc_tile(const AccTile& tile, u32x4* smem, LoopD
       typedef __attribute__((address_space(1))) const uint16_t gb16;
       // Only a ragged last step has rows past T.  The empty volatile asm
       // keeps this a branch: flattened into selects it costs every step
-      // some forty vector instructions while the matrix cores wait.
+      // some forty vector instructions.
       auto clip = [&](u32x4 (&row)[8], int s) __attribute__((always_inline)) {
         if (__builtin_expect((int64_t)kAccStep * (s + 1) > T, 0)) {
           asm volatile("");
