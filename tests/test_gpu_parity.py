@@ -969,6 +969,34 @@ def test_gaussian_merge(r, mode):
         assert frac >= 0.9999 and exact >= 0.999
 
 
+@pytest.mark.parametrize("mode", ["nearest", "stochastic"])
+def test_gaussian_merge_special_values(mode):
+    """NaN and infinities in W through the merge with an explicit (Gaussian) projection: a NaN
+    becomes the quiet NaN of its sign and an infinity stays itself, bit for bit as the oracle
+    rounds them; every other element meets the merge bar."""
+    d, k, r = 96, 512, 64
+    say(f"gaussian merge special values {mode}")
+    wbits = synth.normal((d, k), 0.02, (43, d, k, r, 2), "bf16").copy()
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x7F81, 0xFFA5], np.uint16)
+    ii, jj = np.nonzero((np.arange(d)[:, None] * 5 + np.arange(k)[None, :] * 11) % 83 == 0)
+    wbits[ii, jj] = specials[np.arange(len(ii)) % len(specials)]
+    special = np.zeros((d, k), bool)
+    special[ii, jj] = True
+    U = synth.fp32_matrix((d, r), 1.0, (43, d, r, 0, 7))
+    kk = B.key(8, 77, 1)
+    A = B.regen_A_gaussian(kk, r, k, DEV)
+    W = bf16_dev(wbits)
+    B.merge_grouped_explicit([(kk, W, B.pack_update(torch.from_numpy(U).to(DEV)), B.pack_merge_projection(A))],
+                             r, 3e-4, mode=mode, sr_seed=4)
+    u = philox.sr_draws(4, 77, 1, d, k) if mode == "stochastic" else None
+    want = oracle.merge(oracle.bf16_bits_to_f64(wbits), U.astype(np.float64), oracle.gaussian_A(8, 77, 1, r, k),
+                        3e-4, w_dtype="bf16", mode=mode, u_draws=u)
+    got = bf16_host(W)
+    assert np.array_equal(got[special], want[special])
+    frac, exact = ulp_check(got[~special], want[~special])
+    assert frac >= 0.9999 and exact >= 0.999
+
+
 # ------------------------------------------------------ whole update
 
 
