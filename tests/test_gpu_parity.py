@@ -884,6 +884,35 @@ def test_merge_fp32_unit_factor_and_values():
     assert np.max(np.abs(got.astype(np.float64) - want) / np.spacing(np.abs(want))) <= 1.0
 
 
+def test_merge_fp32_special_values():
+    """fp32 W with NaN (quiet and signalling, both signs) and infinities: each infinity stays
+    itself, each NaN stays a NaN of its sign, and every other element matches the oracle's fp32
+    rounding as in the test above."""
+    d, k, r = 96, 512, 8
+    say("merge fp32 special values")
+    W0 = synth.normal((d, k), 0.02, (25, 0, 0, 0, 2), "f32").copy()
+    specials = np.array([0x7FC00000, 0xFFC00000, 0x7F800000, 0xFF800000, 0x7F800123, 0xFFA00001],
+                        np.uint32).view(np.float32)
+    ii, jj = np.nonzero((np.arange(d)[:, None] * 7 + np.arange(k)[None, :] * 13) % 89 == 0)
+    W0[ii, jj] = specials[np.arange(len(ii)) % len(specials)]
+    special = np.zeros((d, k), bool)
+    special[ii, jj] = True
+    U0 = synth.fp32_matrix((d, r), 1.0, (25, 0, 0, 0, 7))
+    W = torch.from_numpy(W0.copy()).to(DEV)
+    B.merge(B.key(1, 0, 0), W, torch.from_numpy(U0).to(DEV), 1e-3)
+    with np.errstate(invalid="ignore"):
+        want = oracle.merge(W0.astype(np.float64), U0.astype(np.float64), oracle.regen_A(1, 0, 0, r, k), 1e-3,
+                            w_dtype="f32")
+    got = W.cpu().numpy()
+    nan = special & np.isnan(W0)
+    assert np.all(np.isnan(got[nan])) and np.array_equal(np.signbit(got[nan]), np.signbit(W0[nan]))
+    inf = special & np.isinf(W0)
+    assert np.array_equal(got[inf], W0[inf])
+    rest = ~special
+    assert (got[rest] == want[rest]).mean() >= 0.999
+    assert np.max(np.abs(got[rest].astype(np.float64) - want[rest]) / np.spacing(np.abs(want[rest]))) <= 1.0
+
+
 # ------------------------------------------------ reconstruction cosine
 
 
