@@ -404,7 +404,9 @@ LOGRA_API size_t logra_predicted_kl_q_ws_bytes(int64_t P, int64_t V);
 
 /* q = 1/(2 P tau^2) * sum_s Var_{v ~ softmax(z_s/tau)}[zdot_s,v], written to
  * q_dev (one float on the device).  z, zdot [P x V] row-major contiguous,
- * bf16 or fp32 (same dtype).  [paper] §2.3 (Eq. 6), App. A.1.
+ * bf16 or fp32 (same dtype).  A logit of -inf marks a masked entry
+ * (probability 0); each context needs at least one finite logit.  zdot must
+ * be finite.  [paper] §2.3 (Eq. 6), App. A.1.
  * Errors: NULL pointers; P < 1, V < 1; tau not finite and > 0; workspace too
  * small. */
 LOGRA_API int logra_predicted_kl_q(int64_t P, int64_t V, const void* z, const void* zdot,

@@ -302,6 +302,9 @@ __global__ __launch_bounds__(kKlqThreads) void klq_partial_kernel(int64_t V, con
       y[e] = ok ? load_val<BF16>(zd, row + v0 + e) - c : 0.f;
       gm = fmaxf(gm, l[e]);
     }
+    // Eight masked entries (logit -inf, weight 0) add nothing; skipped, they
+    // cannot turn into exp(-inf - (-inf)) = NaN before the first finite one.
+    if (gm == -INFINITY) continue;
     if (gm > mo.m) {
       const float f = __expf(mo.m - gm);
       mo.w *= f;

@@ -581,6 +581,38 @@ def test_predicted_kl_special_cases():
     assert abs(qu - zd.astype(np.float64).var() / 8.0) <= 1e-5 * qu
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_predicted_kl_masked_vocabulary(dtype):
+    """Masked vocabulary entries (logit -inf, so probability 0): scattered, a whole leading range
+    (several chunks with no finite logit, the case that must not become NaN), and a context with
+    a single finite logit (variance 0).  q matches the oracle, through the workspace call and the
+    allocation-free one."""
+    P, V = 6, 5000
+    say(f"predicted_kl_q masked vocabulary {dtype}")
+    z = synth.normal((P, V), 4.0, (21, P, V, 0, 3), "f32").copy()
+    zd = synth.normal((P, V), 1.0, (21, P, V, 0, 4), "f32")
+    rs = np.random.default_rng(5)
+    z[0, rs.random(V) < 0.3] = -np.inf
+    z[1, :1800] = -np.inf
+    z[2, :] = -np.inf
+    z[2, 1234] = 1.5
+    z[3, V - 700:] = -np.inf
+    if dtype == "bf16":
+        zb = torch.from_numpy(z).to(torch.bfloat16)
+        zdb = torch.from_numpy(zd).to(torch.bfloat16)
+        zh, zdh = zb.float().numpy(), zdb.float().numpy()
+        zdev, zddev = zb.to(DEV), zdb.to(DEV)
+    else:
+        zh, zdh = z, zd
+        zdev, zddev = torch.from_numpy(z).to(DEV), torch.from_numpy(zd).to(DEV)
+    want = oracle.predicted_kl_q(zh.astype(np.float64), zdh.astype(np.float64), 1.0)
+    got = B.predicted_kl_q(zdev, zddev, 1.0).item()
+    assert math.isfinite(got) and got == pytest.approx(want, rel=1e-4)
+    q = torch.empty((1,), dtype=torch.float32, device=DEV)
+    B.predicted_kl_q_noalloc(zdev, zddev, 1.0, q)
+    assert q.item() == got
+
+
 def test_step_alpha_device_edges():
     say("step_alpha_dev edges")
     q = torch.tensor([0.0, 8e-3, -1.0], device=DEV)
