@@ -694,6 +694,37 @@ def test_merge_special_values(r, mode, k):
     assert frac >= 0.9999 and exact >= 0.999
 
 
+@pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (256, "stochastic")])
+def test_merge_overflow(r, mode):
+    """Weights near the largest finite bf16 and an update of the same size: values past the
+    largest finite bf16 go to the infinity of their sign (stochastically: with the probability
+    of their fraction of the last gap), as the oracle rounds them; the finite results meet the
+    merge bar."""
+    d, k = 64, 512
+    say(f"merge overflow r={r} {mode}")
+    sign = np.where(synth.normal((d, k), 1.0, (45, d, k, r, 1), "f32") < 0, -1.0, 1.0)
+    W64 = sign * 3.0e38
+    wbits = oracle.f64_to_bf16_rne(W64)
+    U = synth.fp32_matrix((d, r), 1.0, (45, d, r, 0, 7))
+    kk = B.key(3, 11, 1)
+    A = oracle.regen_A(3, 11, 1, r, k)
+    u = philox.sr_draws(4, 11, 1, d, k) if mode == "stochastic" else None
+    want = oracle.merge(oracle.bf16_bits_to_f64(wbits), U.astype(np.float64), A, 1e38, w_dtype="bf16",
+                        mode=mode, u_draws=u)
+    W = bf16_dev(wbits)
+    B.merge_grouped_packed([(kk, W, B.pack_update(torch.from_numpy(U).to(DEV)))], r, 1e38, mode=mode,
+                           sr_seed=4)
+    got = bf16_host(W)
+    inf = np.isinf(oracle.bf16_bits_to_f64(want))
+    say(f"  {inf.mean():.3f} of the results overflow")
+    assert 0.05 < inf.mean() < 0.95
+    # where the oracle overflows: the same infinity, but for the rare element whose fp32 update
+    # (rounded once before the bf16 rounding) falls on the other side of the last decision
+    assert (got[inf] == want[inf]).mean() >= 0.999
+    frac, exact = ulp_check(got[~inf], want[~inf])
+    assert frac >= 0.9999 and exact >= 0.999
+
+
 @pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "nearest"), (256, "stochastic")])
 def test_merge_grouped_equals_single_merges(r, mode):
     """One grouped launch over matrices of mixed shapes (full, ragged column and row edges, small)
