@@ -453,6 +453,33 @@ def test_project_table_many_items_per_wave():
         assert relfro(outs[i].cpu().numpy(), want) <= 1e-5
 
 
+@pytest.mark.parametrize("r", [64, 256])
+def test_accumulate_nan_in_d_stays_in_its_row(r):
+    """A NaN in D at (token t, column c) makes row c of S NaN, as D^T X A^T does, and leaves
+    every other row within tolerance of the oracle: through the table projection's packed
+    planes and the table accumulate the benchmark times."""
+    T, k, d = 300, 256, 512
+    say(f"accumulate with a NaN in D r={r}")
+    xb, X = bf16_inputs((T, k), 1.0, (47, T, k, r, 0))
+    db, Dm = bf16_inputs((T, d), 1e-3, (47, T, d, r, 1))
+    db = db.copy()
+    db[5, 7] = 0x7FC0
+    db[200, 300] = 0xFFC0
+    kk = B.key(6, 3, 1)
+    P = torch.zeros((B.packed_input_bytes(T, r),), dtype=torch.uint8, device=DEV)
+    B.project_input_table([(kk, bf16_dev(xb), None, P)], r)
+    S0 = synth.fp32_matrix((d, r), 0.1, (47, d, r, 0, 5))
+    S = torch.from_numpy(S0.copy()).to(DEV)
+    B.sketch_accumulate_table([(bf16_dev(db), P, S)], r)
+    got = S.cpu().numpy()
+    bad = np.zeros(d, bool)
+    bad[[7, 300]] = True
+    assert np.isnan(got[bad]).all()
+    assert np.isfinite(got[~bad]).all()
+    want = S0.astype(np.float64) + oracle.dense_gradient(Dm, X) @ oracle.regen_A(6, 3, 1, r, k).T
+    assert relfro(got[~bad], want[~bad]) <= 5e-5
+
+
 def test_accumulate_deterministic_and_zero_d_is_noop():
     T, d, r = 2048, 2000, 64
     say("accumulate determinism")
