@@ -78,7 +78,7 @@ def test_regen_A_bit_exact(r, k):
 
 @pytest.mark.parametrize("T,k,r,ldx", [(64, 256, 64, 256), (1000, 712, 33, 720), (96, 3584, 256, 3584),
                                        (37, 40, 1, 48), (512, 1536, 64, 1536), (50, 1001, 64, 1008),
-                                       (20, 259, 96, 264)])
+                                       (20, 259, 96, 264), (1, 300, 64, 304), (3, 5120, 256, 5120)])
 def test_project_bf16(T, k, r, ldx):
     say(f"project bf16 T={T} k={k} r={r} ldx={ldx}")
     bits, X = bf16_inputs((T, ldx), 1.0, (9, T, k, r, 0))
@@ -307,7 +307,7 @@ def test_packed_planes_layout_against_oracle(T, k, r):
         assert np.all(np.abs(dec[:, :, 1]) <= np.abs(hi) * 2.0 ** -8 + 1e-30)
 
 
-@pytest.mark.parametrize("T,r", [(1000, 64), (48, 256), (200, 33)])
+@pytest.mark.parametrize("T,r", [(1000, 64), (48, 256), (200, 33), (1, 64), (5, 256)])
 def test_project_table(T, r):
     """One table launch over projections of mixed widths (ragged k, padded rows, one X shared by
     two projections, entries with only XAt or only planes): XAt within 1e-5 of the oracle and
