@@ -256,11 +256,16 @@ __global__ __launch_bounds__(256) void rowadam_apply_packed_grouped_kernel(
 
 // -------------------------------------------------------- predicted KL q
 
-// Partial softmax moments of one chunk of one context, relative to the
-// running maximum m of z/tau and to a per-context shift c of zdot:
-//   w = sum exp(l - m), s1 = sum exp(l - m)(zd - c), s2 = sum exp(l - m)(zd - c)^2.
+// Softmax-weighted moments of zdot over part of one context, relative to
+// the part's largest logit m = max z/tau: w = sum exp(l - m), the weighted
+// mean of zdot - c, and M2 = sum exp(l - m) (zdot - c - mean)^2, with c a
+// zdot value of the part (each thread's first).  They are updated one value
+// at a time (Welford) and merged pairwise (Chan, Golub and LeVeque), so the
+// variance never comes from a difference of large sums, and the shift keeps
+// an offset common to the context out of the fp32 means: neither a common
+// offset of zdot nor a few outlying entries cost precision.
 struct Moments {
-  float m, w, s1, s2;
+  float m, w, mean, M2, c;
 };
 
 __device__ __forceinline__ Moments combine(Moments a, Moments b) {
@@ -268,7 +273,11 @@ __device__ __forceinline__ Moments combine(Moments a, Moments b) {
   if (a.w == 0.f && a.m == -INFINITY) return b;
   const float m = fmaxf(a.m, b.m);
   const float fa = __expf(a.m - m), fb = __expf(b.m - m);
-  return Moments{m, a.w * fa + b.w * fb, a.s1 * fa + b.s1 * fb, a.s2 * fa + b.s2 * fb};
+  const float wa = a.w * fa, wb = b.w * fb;
+  const float w = wa + wb;  // >= 1: the part holding the larger maximum has weight >= 1
+  const float delta = (b.mean - a.mean) + (b.c - a.c);
+  return Moments{m, w, a.mean + delta * (wb / w),
+                 a.M2 * fa + b.M2 * fb + delta * delta * (wa * (wb / w)), a.c};
 }
 
 constexpr int kKlqThreads = 256;
@@ -290,8 +299,9 @@ __global__ __launch_bounds__(kKlqThreads) void klq_partial_kernel(int64_t V, con
   const int64_t lo = blockIdx.x * chunk;
   const int64_t hi = lo + chunk < V ? lo + chunk : V;
   const int64_t row = s * V;
-  const float c = load_val<BF16>(zd, row);  // shift: zdot of the first vocabulary entry
-  Moments mo{-INFINITY, 0.f, 0.f, 0.f};
+  const int64_t first = lo + (int64_t)threadIdx.x * 8;
+  const float c = first < hi ? load_val<BF16>(zd, row + first) : 0.f;
+  Moments mo{-INFINITY, 0.f, 0.f, 0.f, c};
   for (int64_t v0 = lo + (int64_t)threadIdx.x * 8; v0 < hi; v0 += (int64_t)kKlqThreads * 8) {
     float l[8], y[8];
     float gm = -INFINITY;
@@ -306,18 +316,21 @@ __global__ __launch_bounds__(kKlqThreads) void klq_partial_kernel(int64_t V, con
     // cannot turn into exp(-inf - (-inf)) = NaN before the first finite one.
     if (gm == -INFINITY) continue;
     if (gm > mo.m) {
-      const float f = __expf(mo.m - gm);
+      const float f = __expf(mo.m - gm);  // the mean is unchanged by a common factor
       mo.w *= f;
-      mo.s1 *= f;
-      mo.s2 *= f;
+      mo.M2 *= f;
       mo.m = gm;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = __expf(l[e] - mo.m);
-      mo.w += p;
-      mo.s1 += p * y[e];
-      mo.s2 += p * y[e] * y[e];
+      if (p > 0.f) {  // masked entries (and weights below the fp32 range) add nothing
+        const float w = mo.w + p;
+        const float dy = y[e] - mo.mean;
+        mo.mean += dy * (p / w);
+        mo.M2 += p * dy * (y[e] - mo.mean);
+        mo.w = w;
+      }
     }
   }
   red[threadIdx.x] = mo;
@@ -330,8 +343,8 @@ __global__ __launch_bounds__(kKlqThreads) void klq_partial_kernel(int64_t V, con
     double* o = part + (s * kKlqChunks + blockIdx.x) * 4;
     o[0] = red[0].m;
     o[1] = red[0].w;
-    o[2] = red[0].s1;
-    o[3] = red[0].s2;
+    o[2] = (double)red[0].mean + (double)red[0].c;  // the mean of zdot itself
+    o[3] = red[0].M2;
   }
 }
 
@@ -342,21 +355,22 @@ __global__ __launch_bounds__(256) void klq_final_kernel(int64_t P, const double*
   __shared__ double red[256];
   double acc = 0.0;
   for (int64_t s = threadIdx.x; s < P; s += 256) {
-    double m = -INFINITY, w = 0.0, s1 = 0.0, s2 = 0.0;
+    // The chunks' moments merged in order, as in combine() but in fp64.
+    double m = -INFINITY, w = 0.0, mean = 0.0, M2 = 0.0;
     for (int c = 0; c < kKlqChunks; ++c) {
       const double* o = part + (s * kKlqChunks + c) * 4;
       if (o[1] == 0.0 && o[0] == -INFINITY) continue;
       const double mm = o[0] > m ? o[0] : m;
       const double fa = exp(m - mm), fb = exp(o[0] - mm);
-      w = w * fa + o[1] * fb;
-      s1 = s1 * fa + o[2] * fb;
-      s2 = s2 * fa + o[3] * fb;
+      const double wa = w * fa, wb = o[1] * fb;
+      const double wn = wa + wb;
+      const double delta = o[2] - mean;
+      mean += delta * (wb / wn);
+      M2 = M2 * fa + o[3] * fb + delta * delta * (wa * (wb / wn));
+      w = wn;
       m = mm;
     }
-    const double mean = s1 / w;
-    double var = s2 / w - mean * mean;
-    if (var < 0.0) var = 0.0;
-    acc += var;
+    acc += M2 / w;
   }
   red[threadIdx.x] = acc;
   __syncthreads();

@@ -608,6 +608,26 @@ def test_predicted_kl_special_cases():
     assert abs(qu - zd.astype(np.float64).var() / 8.0) <= 1e-5 * qu
 
 
+@pytest.mark.parametrize("kind", ["first", "common", "scattered"])
+def test_predicted_kl_zdot_offsets(kind):
+    """q is a variance, so it must not lose precision when zdot carries a large offset: on the
+    first entry of each context, on every entry, or on a few scattered entries.  q within 1e-5
+    of the oracle in each case."""
+    P, V = 8, 20000
+    say(f"predicted_kl_q with zdot offsets ({kind})")
+    z = synth.normal((P, V), 4.0, (22, P, V, 0, 3), "f32")
+    zd = synth.normal((P, V), 1.0, (22, P, V, 0, 4), "f32").copy()
+    if kind == "first":
+        zd[:, 0] += 1000.0
+    elif kind == "common":
+        zd += 10000.0
+    else:
+        zd[:, ::997] += 300.0
+    want = oracle.predicted_kl_q(z.astype(np.float64), zd.astype(np.float64), 1.0)
+    got = B.predicted_kl_q(torch.from_numpy(z).to(DEV), torch.from_numpy(zd).to(DEV), 1.0).item()
+    assert got == pytest.approx(want, rel=1e-5)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_predicted_kl_masked_vocabulary(dtype):
     """Masked vocabulary entries (logit -inf, so probability 0): scattered, a whole leading range
