@@ -358,7 +358,10 @@ def exact_kl_mean(z: np.ndarray, zdot: np.ndarray, alpha: float, tau: float) -> 
     """
     lp = _log_softmax(np.asarray(z, np.float64) / tau)
     lq = _log_softmax((np.asarray(z, np.float64) + alpha * np.asarray(zdot, np.float64)) / tau)
-    return float((np.exp(lp) * (lp - lq)).sum(axis=1).mean())
+    # an entry of probability 0 (logit -inf, masked) adds 0 log 0 = 0 to the sum
+    with np.errstate(invalid="ignore"):
+        terms = np.where(np.isneginf(lp), 0.0, np.exp(lp) * (lp - lq))
+    return float(terms.sum(axis=1).mean())
 
 
 def step_alpha(q: float, delta: float, alpha_max: float) -> float:

@@ -633,7 +633,7 @@ def test_predicted_kl_masked_vocabulary(dtype):
     """Masked vocabulary entries (logit -inf, so probability 0): scattered, a whole leading range
     (several chunks with no finite logit, the case that must not become NaN), and a context with
     a single finite logit (variance 0).  q matches the oracle, through the workspace call and the
-    allocation-free one."""
+    allocation-free one, and so does the exact KL of two steps."""
     P, V = 6, 5000
     say(f"predicted_kl_q masked vocabulary {dtype}")
     z = synth.normal((P, V), 4.0, (21, P, V, 0, 3), "f32").copy()
@@ -658,6 +658,11 @@ def test_predicted_kl_masked_vocabulary(dtype):
     q = torch.empty((1,), dtype=torch.float32, device=DEV)
     B.predicted_kl_q_noalloc(zdev, zddev, 1.0, q)
     assert q.item() == got
+    for a in (1e-3, 0.5):
+        kl = float(B.exact_kl(zdev, zddev, a, 1.0).item())
+        assert math.isfinite(kl)
+        assert kl == pytest.approx(oracle.exact_kl_mean(zh.astype(np.float64), zdh.astype(np.float64), a, 1.0),
+                                   rel=1e-6)
 
 
 def test_step_alpha_device_edges():

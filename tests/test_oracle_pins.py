@@ -445,6 +445,28 @@ def test_predicted_kl_special_cases():
     assert oracle.predicted_kl_q(z2, zd2, 1.0) == pytest.approx(want, rel=1e-12)
 
 
+def test_masked_logits_are_removed_entries():
+    """A logit of -inf is an entry of probability 0: q and the exact KL over a vocabulary with
+    masked entries equal q and the KL over the vocabulary with those entries left out (0 log 0
+    taken as 0), whatever their zdot."""
+    rs = np.random.default_rng(12)
+    P, V = 5, 80
+    z = rs.standard_normal((P, V)) * 2
+    zd = rs.standard_normal((P, V))
+    keep = rs.random((P, V)) > 0.4
+    keep[:, 0] = True
+    keep[4, 1:] = False                                # a context with one live entry
+    zm = np.where(keep, z, -np.inf)
+    zdm = np.where(keep, zd, 1e6)                      # masked zdot must not matter
+    q_rows, kl_rows = [], []
+    for s in range(P):
+        q_rows.append(oracle.predicted_kl_q(z[s:s + 1, keep[s]], zd[s:s + 1, keep[s]], 0.8))
+        kl_rows.append(oracle.exact_kl_mean(z[s:s + 1, keep[s]], zd[s:s + 1, keep[s]], 0.3, 0.8))
+    assert q_rows[4] == 0.0 and kl_rows[4] == pytest.approx(0.0, abs=1e-15)
+    assert oracle.predicted_kl_q(zm, zdm, 0.8) == pytest.approx(np.mean(q_rows), rel=1e-12)
+    assert oracle.exact_kl_mean(zm, zdm, 0.3, 0.8) == pytest.approx(np.mean(kl_rows), rel=1e-12)
+
+
 def test_step_rule_printed_cases():
     """P5 (tests/golden/step_rule.json): q = 4 delta halves the step; alpha is capped."""
     g = golden("step_rule.json")
