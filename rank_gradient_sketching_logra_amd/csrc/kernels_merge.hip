@@ -327,6 +327,10 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
   // parked here until the rounding: two generator blocks per instance.
   constexpr bool kDrawsInChain = STOCH && PACKED && !EXPLICIT && KS >= 8;
   __shared__ __align__(16) u32x4 draws[kDrawsInChain ? NWV * 2 * E * 64 : 1];
+  // With fewer rank steps the draws stay in registers: they are generated
+  // after the chain's MFMAs are issued, in the same scheduling region, so
+  // the generator's vector work issues while the matrix cores run.
+  constexpr bool kDrawsInRegs = STOCH && PACKED && !EXPLICIT && !kDrawsInChain;
   static_assert(16 * KS * NWd <= 4 * WT, "sign bits must fit in one W tile");
 
   const int tid = threadIdx.x;
@@ -802,6 +806,20 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         u32x4 pre[E][2];
         if constexpr (PACKED) {
           mfma_band_packed(acc, ut, [&](int grp) __attribute__((always_inline)) {
+            if constexpr (kDrawsInRegs) {
+              if (grp == 0) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                  const uint64_t e0 =
+                      (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw);
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    const Philox4x32 p = sr_block(srk, (e0 >> 3) + h);
+                    pre[e][h] = u32x4{p.w[0], p.w[1], p.w[2], p.w[3]};
+                  }
+                }
+              }
+            }
             if constexpr (kDrawsInChain) {
               if (grp < 2 * E) {
                 const int e = grp >> 1, h = grp & 1;
@@ -827,9 +845,9 @@ __global__ __launch_bounds__(kMergeWaves * 64, 1) void merge_bf16_kernel(MergeGr
         for (int e = 0; e < E; ++e) {
           u32x4 o0, o1;
           const uint64_t e0 = (uint64_t)(row0 + row) * (uint64_t)k + (uint64_t)(cw + 32 * e + 16 * hw);
-          if (kDrawsInChain && sr_aligned)
-            update16<STOCH, kDrawsInChain>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk, e0, true, o0, o1,
-                                           pre[e]);
+          if ((kDrawsInChain || kDrawsInRegs) && sr_aligned)
+            update16<STOCH, kDrawsInChain || kDrawsInRegs>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk, e0,
+                                                           true, o0, o1, pre[e]);
           else
             update16<STOCH>(wx[2 * e], wx[2 * e + 1], acc[e], sc, srk, e0, sr_aligned, o0, o1);
           lds_write16(wa[2 * e], o0);
