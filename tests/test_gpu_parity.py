@@ -879,7 +879,8 @@ def test_rowadam_packed_grouped_equals_single_calls(r):
 
 
 @pytest.mark.parametrize("r,mode", [(64, "nearest"), (64, "stochastic"), (33, "stochastic"), (8, "nearest"),
-                                    (100, "nearest"), (256, "stochastic"), (256, "nearest")])
+                                    (8, "stochastic"), (20, "stochastic"), (100, "nearest"),
+                                    (128, "stochastic"), (256, "stochastic"), (256, "nearest")])
 def test_merge_grouped_packed_equals_fp32_update(r, mode):
     """The merge from a packed update gives the bits of the merge from the fp32 U it was packed
     from, over full, ragged-row, ragged-column and small matrices in one grouped launch."""
@@ -901,7 +902,7 @@ def test_merge_grouped_packed_equals_fp32_update(r, mode):
 
 
 @pytest.mark.parametrize("r,mode", [(64, "stochastic"), (33, "nearest"), (100, "stochastic"),
-                                    (256, "stochastic")])
+                                    (256, "stochastic"), (16, "stochastic"), (32, "stochastic")])
 def test_sync_payload_trainer_and_rollout_agree(r, mode):
     """Policy sync ([paper] §2.2): the trainer packs fl32(alpha eta U) once; its own merge from the
     payload and the rollout side's sync_apply give identical weights, and both match the oracle's
