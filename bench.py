@@ -53,10 +53,11 @@ POOL_LIMIT_BYTES = 160e9  # distinct input sets up to this size, else a pool
 POOL_SETS = 17            # input sets in a pool (27B set: 17 x 0.74 GB)
 BALLAST_BYTES = {"dense-27b-set-r256": 10 * 10**9}
 DEFAULT_WORKLOAD = "qwen2.5-7b-set-r64"
-# Microbatches per projection and accumulate launch.  Two at r = 64: the inputs of a pair of
-# microbatches are stored together, so each tile's fixed cost (ring fill, class-sum exchange,
-# S read and write) is paid once per pair.  One at r = 256, where pairing saved 2.5%.
-PER_LAUNCH = {"qwen2.5-7b-set-r64": 2, "qwen2.5-1.5b-set-r64": 2}
+# Microbatches per projection and accumulate launch.  Several at r = 64 (four on the 7B set,
+# two on the 1.5B set): their inputs are stored together, so each tile's fixed cost (ring fill,
+# class-sum exchange, S read and write) is paid once per launch.  One at r = 256, where pairing
+# saved 2.5%.
+PER_LAUNCH = {"qwen2.5-7b-set-r64": 4, "qwen2.5-1.5b-set-r64": 2}
 # Layers per grouped merge launch (at most 16 matrices a launch): two layers halve the
 # launches and give each block twice the units over which to spread its start (sign
 # generation, ring fill).
